@@ -1,0 +1,278 @@
+/*
+ * sa.h -- C ABI of the query-dependent sparse-attention library (libsa.so),
+ * written for AMD Instinct MI355X (gfx950).
+ *
+ * The library computes one hot path:
+ *   1. an indexer scores every cached key cheaply -- either a low-rank (r = 16)
+ *      projection of pre-RoPE queries and keys ("Full Attention Strikes Back",
+ *      method section 2; one head-collapsed channel per key/value group,
+ *      "Oracle-Guided Sparse Prefill", section 2.2), or a second-order Taylor
+ *      score of 64-token pages from their mean and diagonal variance ("SPLA",
+ *      section 2.1);
+ *   2. a support set is chosen by dynamic top-p attention mass with a
+ *      sort-free histogram threshold, or by top-k ("Full Attention Strikes
+ *      Back", method sections 3 and 5);
+ *   3. exact softmax attention runs over the selected keys/values only, one
+ *      support per key/value group shared by its query heads, per query in
+ *      decode and per block of b_sel queries in causal prefill
+ *      ("Oracle-Guided Sparse Prefill", section 2.1).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers unless marked "host".  The caller owns every
+ *    buffer; the library never allocates or frees memory.  Scratch memory is
+ *    passed in as a workspace whose size comes from sa_workspace_size().
+ *  - A workspace must be zero-filled once before its first use; every call
+ *    leaves the parts it relies on zero again.  Calls that share a workspace
+ *    must be ordered (same stream, or synchronised).
+ *  - Every call is asynchronous on the given HIP stream (NULL = default
+ *    stream) and never synchronises the host.
+ *  - Arguments are checked on the host before anything is launched; a failed
+ *    check returns an error code, launches nothing and writes nothing.
+ *    sa_last_error() then gives a message (per calling thread).  A failed
+ *    launch returns SA_ERR_HIP.
+ *  - Layouts are row-major, rightmost index fastest.  Grouped-query attention:
+ *    with G = n_q_heads / n_kv_heads, query head h uses key/value group h / G.
+ *  - Paged caches: a pool holds n_pool_pages pages, each [n_kv_heads][page][w]
+ *    for a row width w (head_dim for keys/values, idx_rank for indexer keys,
+ *    2 * head_dim for page statistics: mean then variance).  Token t of
+ *    sequence b lives in pool page page_table[b][t / page], slot t % page.
+ *    seq_lens[b] must lie in [0, max_len] and every page id a sequence uses in
+ *    [0, n_pool_pages); kernels clamp both into range rather than fault, so a
+ *    violation gives wrong values, never an out-of-bounds access.
+ *  - Support lists: idx[row][cap] int32, ascending token indices padded with -1,
+ *    count[row] the number of valid entries; row = b * n_kv_heads + g for decode
+ *    and blk * n_kv_heads + g for prefill.
+ *  - Results are deterministic: identical inputs give bit-identical outputs.
+ *  - Supported shapes: head_dim 64 or 128, idx_rank 16, page 64,
+ *    G in {1, 2, 4, 8, 16}.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARGUMENT = 1, /* null pointer, bad size or parameter        */
+  SA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (shape, dtype)   */
+  SA_ERR_CAPACITY = 3,         /* cap below the worst-case support size      */
+  SA_ERR_WORKSPACE = 4,        /* workspace missing or smaller than required */
+  SA_ERR_HIP = 5               /* a HIP launch failed                        */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Host-side problem description. */
+typedef struct {
+  int32_t batch;        /* B sequences (1 for prefill)                          */
+  int32_t n_q_heads;    /* H_q                                                  */
+  int32_t n_kv_heads;   /* H_kv, divides H_q                                    */
+  int32_t head_dim;     /* d                                                    */
+  int32_t idx_rank;     /* r of the indexer projection                          */
+  int32_t page_size;    /* tokens per page                                      */
+  int32_t max_pages;    /* columns of page_table                                */
+  int32_t max_len;      /* host bound on seq_lens[b]; <= max_pages * page_size  */
+  int64_t n_pool_pages; /* pages in every pool                                  */
+} sa_shape;
+
+/* Device-side paging of the caches. */
+typedef struct {
+  const int32_t* page_table; /* [batch][max_pages] */
+  const int32_t* seq_lens;   /* [batch]; unused by the prefill calls */
+} sa_pages;
+
+/* Operation ids for sa_workspace_size(). */
+typedef enum {
+  SA_OP_INDEX_SCORES = 0,
+  SA_OP_SELECT = 1,          /* param = max candidates per row (tokens or pages) */
+  SA_OP_SPARSE_DECODE = 2,   /* param = cap of the support lists                 */
+  SA_OP_PREFILL_SELECT = 3,  /* param = n_tokens of the prefill                  */
+  SA_OP_DECODE_STEP = 4      /* param = cap                                      */
+} sa_op;
+
+/* Bytes of workspace the operation needs for this shape (0 if none).  A
+ * workspace sized for the maximum over the operations a caller uses may be
+ * shared by them (calls ordered on one stream). */
+size_t sa_workspace_size(sa_op op, const sa_shape* shape, int64_t param);
+
+/* ---------------------------------------------------------------------------
+ * Cache maintenance (off the per-step path)
+ * ------------------------------------------------------------------------- */
+
+/* Indexer keys of newly appended tokens ("Full Attention Strikes Back",
+ * method section 2: the low-rank projector acts on keys before RoPE):
+ *   kidx_pool[slot[t] / page][g][slot[t] % page][:] = W_k[g]^T k_pre[t][g][:]
+ * k_pre [T][n_kv_heads][head_dim], w_k [n_kv_heads][head_dim][idx_rank],
+ * kidx_pool [n_pool_pages][n_kv_heads][page][idx_rank], all of dtype;
+ * slot [T] int64 pool token rows (page id * page_size + slot in page).
+ * fp32 accumulation, one rounding to dtype on store. */
+sa_status sa_index_append(const sa_shape* shape, const void* k_pre, const void* w_k,
+                          sa_dtype dtype, const int64_t* slot, int32_t T,
+                          void* kidx_pool, hipStream_t stream);
+
+/* Page statistics for the Taylor page score ("SPLA", section 2.1, diagonal
+ * covariance): for each listed pool page and group, the mean and the
+ * population variance (divide by n) over the first n_valid[i] tokens:
+ *   stats_pool[pages[i]][g][0][:] = mean,  stats_pool[pages[i]][g][1][:] = var
+ * k_pool [n_pool_pages][n_kv_heads][page][head_dim]; pages, n_valid [n] int32
+ * (n_valid in [1, page]); stats_pool [n_pool_pages][n_kv_heads][2][head_dim];
+ * k_pool and stats_pool of dtype.  fp32 accumulation (two passes). */
+sa_status sa_page_stats(const sa_shape* shape, const void* k_pool, sa_dtype dtype,
+                        const int32_t* pages, const int32_t* n_valid, int32_t n,
+                        void* stats_pool, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode: indexer scores
+ * ------------------------------------------------------------------------- */
+
+/* Token indexer scores ("Full Attention Strikes Back", method section 2;
+ * head-collapsed channel, "Oracle-Guided Sparse Prefill", section 2.2):
+ *   q_c[b][g] = s_idx * mean_{h in g} W_q[h]^T q[b][h]
+ *   x[(b * n_kv_heads + g) * ldx + j] = q_c[b][g] . Kidx[b][g][j],  j < seq_lens[b]
+ * q [batch][n_q_heads][head_dim], w_q [n_q_heads][head_dim][idx_rank],
+ * kidx_pool [n_pool_pages][n_kv_heads][page][idx_rank], all of dtype;
+ * x fp32 with row stride ldx >= max_len (entries j >= seq_lens[b] untouched).
+ * fp32 arithmetic. */
+sa_status sa_index_scores(const sa_shape* shape, const sa_pages* pages, const void* q,
+                          const void* w_q, const void* kidx_pool, sa_dtype dtype,
+                          float s_idx, float* x, int64_t ldx, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Taylor page scores ("SPLA", section 2.1): for page p of sequence b with
+ * n = min(page, seq_lens[b] - p * page) valid tokens, q'_h = s_att * q[b][h]:
+ *   x[(b * n_kv_heads + g) * ldx + p] =
+ *       mean_{h in g} [ q'_h . mean_p + log(1 + 0.5 * sum_i q'_{h,i}^2 var_{p,i}) ]
+ *       + log(n / page)
+ * (the log of exp(q.kbar)(1 + q^T diag(var) q / 2), averaged over the group's
+ * heads; the last term keeps a partial page's estimate of its total mass).
+ * q [batch][n_q_heads][head_dim] and stats_pool of dtype; x fp32, ldx >=
+ * max_pages. */
+sa_status sa_page_scores(const sa_shape* shape, const sa_pages* pages, const void* q,
+                         const void* stats_pool, sa_dtype dtype, float s_att, float* x,
+                         int64_t ldx, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Support selection (sort-free histogram threshold)
+ * ------------------------------------------------------------------------- */
+
+/* Dynamic top-p support ("Full Attention Strikes Back", method sections 3 and
+ * 5) over the token scores x (rows b * n_kv_heads + g, stride ldx, n = seq_lens[b]
+ * candidates): with masses P_j = exp(x_j - max x) / sum exp(x - max x), rank
+ * the candidates by (x descending, index ascending) and keep the shortest
+ * prefix whose mass reaches p (>= p); p >= 1 keeps all.  The sink tokens
+ * [0, n_sink) and the window [n - n_window, n) are then added (attention sink
+ * and sliding window, method section 1).  Output: idx[row][cap] ascending,
+ * -1 padded; count[row].  cap >= max_len.  The threshold is found by a radix
+ * histogram over order-preserving keys of the fp32 scores, with masses summed
+ * in 2^-40 fixed point, so the result does not depend on scheduling. */
+sa_status sa_select_topp(const sa_shape* shape, const sa_pages* pages, const float* x,
+                         int64_t ldx, float p, int32_t n_sink, int32_t n_window,
+                         int32_t* idx, int32_t* count, int32_t cap, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* Static top-k support ("Full Attention Strikes Back", method section 3;
+ * "Oracle-Guided Sparse Prefill", section 2.2): the first min(k, n) candidates
+ * of the same ranking.  unit = 1: candidates are tokens (n = seq_lens[b]), and
+ * the sink/window tokens are added as for top-p; cap >= min(k, max_len) +
+ * n_sink + n_window (or max_len if smaller).  unit = page_size: candidates are
+ * pages (n = ceil(seq_lens[b] / page)), each selected page expands to its
+ * tokens; n_sink and n_window must be 0; cap >= k * page_size (or max_len if
+ * smaller). */
+sa_status sa_select_topk(const sa_shape* shape, const sa_pages* pages, const float* x,
+                         int64_t ldx, int32_t k, int32_t unit, int32_t n_sink,
+                         int32_t n_window, int32_t* idx, int32_t* count, int32_t cap,
+                         void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Decode: exact attention over the support
+ * ------------------------------------------------------------------------- */
+
+/* Split-KV sparse decode ("Oracle-Guided Sparse Prefill", section 2.1:
+ * attention recomputed with the original q, k, v restricted to the support):
+ * for every query head h of group g of sequence b, over the listed tokens
+ * S = idx[b * n_kv_heads + g][0 .. count)
+ *   out[b][h] = sum_{j in S} softmax_S(s_att * q[b][h] . k_j) v_j
+ *   lse[b][h] = log sum_{j in S} exp(s_att * q[b][h] . k_j)   (lse may be NULL)
+ * An empty support gives out = 0 and lse = -inf.  q, k_pool, v_pool of dtype;
+ * out [batch][n_q_heads][head_dim] of out_dtype; lse fp32.  List entries must
+ * be in [0, seq_lens[b]).  fp32 accumulation. */
+sa_status sa_sparse_decode(const sa_shape* shape, const sa_pages* pages, const void* q,
+                           const void* k_pool, const void* v_pool, sa_dtype dtype,
+                           const int32_t* idx, const int32_t* count, int32_t cap,
+                           float s_att, void* out, sa_dtype out_dtype, float* lse,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* One whole decode step: sa_index_scores, then sa_select_topp (p in (0, 1])
+ * or, if top_k > 0, sa_select_topk with unit 1, then sa_sparse_decode.  The
+ * scores x ([batch * n_kv_heads][ldx] fp32), idx and count are outputs too. */
+sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const void* q,
+                         const void* w_q, const void* kidx_pool, const void* k_pool,
+                         const void* v_pool, sa_dtype dtype, float s_idx, float s_att,
+                         float p, int32_t top_k, int32_t n_sink, int32_t n_window,
+                         float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
+                         void* out, sa_dtype out_dtype, float* lse, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Causal prefill with supports shared by blocks of b_sel queries
+ * ------------------------------------------------------------------------- */
+
+/* Block supports ("Oracle-Guided Sparse Prefill", sections 2.1 and 2.2): for
+ * query block blk = rows [blk * b_sel, min(n_tokens, (blk + 1) * b_sel)) and
+ * group g,
+ *   q_c = s_idx * mean_{i in blk, h in g} W_q[h]^T q[i][h]
+ * scores x_j = q_c . Kidx[g][j] over the keys of earlier blocks,
+ * j < blk * b_sel, and keeps the top k of them (all when there are at most k)
+ * ranked as in sa_select_topk.  Output idx[blk * n_kv_heads + g][cap]
+ * ascending, -1 padded, count likewise; cap >= min(k, n_tokens).  The block's
+ * own keys are not listed: sa_sparse_prefill always attends to them causally.
+ * q [n_tokens][n_q_heads][head_dim], w_q, kidx_pool of dtype; page_table row 0
+ * of pages maps the single sequence. */
+sa_status sa_select_prefill_topk(const sa_shape* shape, const sa_pages* pages,
+                                 int32_t n_tokens, const void* q, const void* w_q,
+                                 const void* kidx_pool, sa_dtype dtype, float s_idx,
+                                 int32_t b_sel, int32_t k, int32_t* idx, int32_t* count,
+                                 int32_t cap, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Block-sparse causal prefill attention ("Oracle-Guided Sparse Prefill",
+ * section 2.1): row i of block blk, head h of group g attends to the listed
+ * keys S = idx[blk * n_kv_heads + g][0 .. count) plus the block's own keys
+ * j in [blk * b_sel, i]:
+ *   out[i][h] = sum_j softmax(s_att * q[i][h] . k_j) v_j,  lse[i][h] likewise.
+ * Listed keys must precede the block.  q [n_tokens][n_q_heads][head_dim],
+ * k_pool, v_pool of dtype (SA_BF16 only); out [n_tokens][n_q_heads][head_dim]
+ * of out_dtype; lse [n_tokens][n_q_heads] fp32 or NULL.  b_sel must be 64.
+ * bf16 matrix-core products with fp32 accumulation and fp32 softmax. */
+sa_status sa_sparse_prefill(const sa_shape* shape, const sa_pages* pages, int32_t n_tokens,
+                            const void* q, const void* k_pool, const void* v_pool,
+                            sa_dtype dtype, const int32_t* idx, const int32_t* count,
+                            int32_t cap, int32_t b_sel, float s_att, void* out,
+                            sa_dtype out_dtype, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Diagnostics
+ * ------------------------------------------------------------------------- */
+
+/* Static name of a status code. */
+const char* sa_status_string(sa_status status);
+
+/* Message of the last non-OK return on the calling thread ("" if none). */
+const char* sa_last_error(void);
+
+/* Library version string. */
+const char* sa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

@@ -1,0 +1,46 @@
+"""Float64 CPU oracle for query-dependent sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+link this package: only ``tests/``, the smoke check in ``__graft_entry__`` and
+the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the
+HIP library (no kernels, headers, helpers, tables or constants) and imports
+nothing from it.
+
+Every function computes the plain definition of one step, in numpy float64,
+one row at a time, and cites the page and section it follows.  Where the pages
+leave a step open, the docstring states the reading taken.
+
+Parity status of each function (what pins it, from the tests in
+``tests/test_oracle_pins.py``):
+
+* ``round_to_bf16``      pinned: bit-equal to torch's fp32->bf16 rounding on
+                         fp32-representable inputs, hand-made halfway cases.
+* ``indexer_keys``, ``collapse_query``, ``token_scores``
+                         pinned: brute-force loops on tiny inputs, group
+                         semantics (a needle seen only by one group), linearity.
+* ``page_stats``         pinned: closed forms (constant page, +/- pairs,
+                         arithmetic progression).
+* ``page_scores``        pinned: constant page equals the exact mean of
+                         exp-scores; O(sigma^4) decay on axis-pair pages;
+                         diagonal-vs-full covariance gap; Gaussian closed form.
+* ``select_topp``/``select_topk``
+                         pinned: hand-made dyadic distributions
+                         (tests/golden/topp_dyadic.txt), brute-force subset
+                         enumeration, p=1 / k>=n give everything.
+* ``with_sink_window``, ``expand_pages``
+                         pinned: hand-made cases.
+* ``attend``             pinned: torch scaled_dot_product_attention in float64,
+                         single-key support, key/value permutation invariance.
+* ``prefill_*``          pinned: early blocks equal dense causal attention
+                         (torch SDPA, is_causal), segment permutation
+                         invariance, query covariance.
+
+Parity unpinned (our readings, fixed only by our own written definitions, no
+worked example on the pages): the indexer scale ``s_idx``, the mean over a
+group's heads (and over a query block) of the projected query, the union of
+the always-kept sink/window tokens after selection, the log-domain mean over a
+group's heads of the page score, and the partial-page term log(n/page).
+"""
+
+from .sparse_attention import *  # noqa: F401,F403
+from .sparse_attention import __all__  # noqa: F401

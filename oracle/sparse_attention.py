@@ -1,0 +1,381 @@
+"""Plain float64 definitions of every step of query-dependent sparse attention.
+
+Test infrastructure only (see the package docstring).  All arrays are numpy;
+inputs are converted to float64 exactly (bf16 and fp32 values are exactly
+representable in float64).  Loops stay simple so each step can be read
+against the pages:
+
+* "Full Attention Strikes Back" (RTPurbo) -- method section 1 (local heads keep
+  an attention sink and a sliding window), section 2 (a low-rank r=16 projector
+  applied to queries and keys before RoPE scores every cached token), section 3
+  (dynamic top-p: take tokens until the accumulated attention mass of the
+  low-rank scores reaches p; static top-k as the alternative).
+* "Oracle-Guided Sparse Prefill for Full/GQA layers" -- section 2.1 (top-k
+  support, attention recomputed with the original q, k, v restricted to the
+  support; support shared by a block of b_sel = 64 consecutive queries) and
+  section 2.2 (one head-collapsed scoring channel shared by the heads; the
+  budget k is a runtime knob).
+* "SPLA: Block Sparse Plus Linear Attention" -- section 2.1 (block score from a
+  second-order Taylor expansion around the block mean, exp(q.kbar) times
+  (1 + q^T Cov(k) q / 2), with the covariance replaced by its diagonal).
+* "Sparser Block-Sparse Attention via Token Permutation" (PBS-Attn) -- section 1
+  (attention output is invariant to a joint permutation of key/value pairs and
+  covariant with a permutation of the queries).
+
+Group convention (grouped-query attention): with G = H_q / H_kv, query head h
+belongs to key/value group g = h // G.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "f64",
+    "round_to_bf16",
+    "indexer_keys",
+    "collapse_query",
+    "token_scores",
+    "page_stats",
+    "page_scores",
+    "taylor_page_score",
+    "candidate_order",
+    "softmax_mass",
+    "select_topp",
+    "prefix_reaching",
+    "select_topk",
+    "with_sink_window",
+    "expand_pages",
+    "attend",
+    "decode_row",
+    "decode_row_pages",
+    "prefill_block_rows",
+    "prefill_block_query",
+    "prefill_block_support",
+    "prefill_block_attend",
+    "group_of_head",
+    "heads_of_group",
+]
+
+
+def f64(a) -> np.ndarray:
+    """Exact conversion of an array (fp32 or bf16-valued fp32) to float64."""
+    return np.asarray(a, dtype=np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bfloat16 value, ties to even.
+
+    bfloat16 keeps 8 significant bits (1 implicit + 7 stored) and the float32
+    exponent range; its smallest subnormal step is 2**-133.  The value is
+    returned as float64.  Used to model a bf16 store of a float64 result.
+    """
+    x = f64(x)
+    out = np.zeros_like(x)
+    nz = x != 0
+    _, e = np.frexp(x[nz])  # |x| = m * 2**e with 0.5 <= m < 1
+    step_exp = np.maximum(e - 8, -133)  # spacing of bf16 values near x
+    q = np.rint(np.ldexp(x[nz], -step_exp))  # np.rint: half to even
+    out[nz] = np.ldexp(q, step_exp)
+    return out
+
+
+def group_of_head(h: int, n_q_heads: int, n_kv_heads: int) -> int:
+    return h // (n_q_heads // n_kv_heads)
+
+
+def heads_of_group(g: int, n_q_heads: int, n_kv_heads: int) -> list:
+    G = n_q_heads // n_kv_heads
+    return list(range(g * G, (g + 1) * G))
+
+
+# ---------------------------------------------------------------------------
+# Indexer (RTPurbo section 2; Oracle-Guided Sparse Prefill section 2.2)
+# ---------------------------------------------------------------------------
+
+
+def indexer_keys(k_pre, w_k) -> np.ndarray:
+    """Low-rank indexer keys: row j is W_k^T k_j (k taken before RoPE).
+
+    k_pre: [T, d], w_k: [d, r]  ->  [T, r]
+    """
+    return f64(k_pre) @ f64(w_k)
+
+
+def collapse_query(q_heads, w_q_heads, s_idx: float) -> np.ndarray:
+    """Head-collapsed indexer query of one group.
+
+    Each head's pre-RoPE query is projected to rank r, q~_h = W_q[h]^T q_h,
+    and the group keeps one scoring channel: the mean of q~_h over its heads,
+    times the indexer scale s_idx.  Averaging the projected queries equals
+    averaging the heads' low-rank logits (reading: the mean over the group's
+    heads is how one shared channel serves them).
+
+    q_heads: [G, d], w_q_heads: [G, d, r]  ->  [r]
+    """
+    q_heads, w_q_heads = f64(q_heads), f64(w_q_heads)
+    G = q_heads.shape[0]
+    acc = np.zeros(w_q_heads.shape[2])
+    for h in range(G):
+        acc += w_q_heads[h].T @ q_heads[h]
+    return s_idx * acc / G
+
+
+def token_scores(q_c, ktil) -> np.ndarray:
+    """Indexer score of every cached token: x_j = q_c . K~_j.
+
+    q_c: [r], ktil: [L, r]  ->  [L]
+    """
+    return f64(ktil) @ f64(q_c)
+
+
+# ---------------------------------------------------------------------------
+# Page statistics and the Taylor page score (SPLA section 2.1)
+# ---------------------------------------------------------------------------
+
+
+def page_stats(k, page_size: int = 64):
+    """Per-page mean and diagonal (population) variance of the keys.
+
+    k: [L, d] -> mean [P, d], var [P, d], n [P] with P = ceil(L / page_size);
+    the last page may hold fewer than page_size tokens.  Variance divides by
+    the number of tokens in the page (reading: the statistic of the block's
+    own tokens, not an estimate of a wider population).
+    """
+    k = f64(k)
+    L, d = k.shape
+    P = (L + page_size - 1) // page_size
+    mean = np.zeros((P, d))
+    var = np.zeros((P, d))
+    n = np.zeros(P, dtype=np.int64)
+    for p in range(P):
+        rows = k[p * page_size : min(L, (p + 1) * page_size)]
+        n[p] = rows.shape[0]
+        mu = rows.sum(axis=0) / n[p]
+        dev = rows - mu
+        mean[p] = mu
+        var[p] = (dev * dev).sum(axis=0) / n[p]
+    return mean, var, n
+
+
+def taylor_page_score(qp, mean_p, var_p) -> float:
+    """The printed block score exp(q.kbar) * (1 + q^T diag(var) q / 2).
+
+    qp is the already-scaled query (s_att * q).  Diagonal covariance as the
+    page prescribes to avoid O(d^2) storage.
+    """
+    qp, mean_p, var_p = f64(qp), f64(mean_p), f64(var_p)
+    return math.exp(float(qp @ mean_p)) * (1.0 + 0.5 * float((qp * qp) @ var_p))
+
+
+def page_scores(q_heads, mean, var, n_valid, s_att: float, page_size: int = 64):
+    """Group page score x_p used for page selection.
+
+    For head h with scaled query q'_h = s_att * q_h the log of the Taylor
+    block score is  l_{h,p} = q'_h . kbar_p + log(1 + 0.5 * sum_i q'_{h,i}^2 var_{p,i}),
+    plus log(n_p / page_size) for a partial page, so that the score keeps
+    estimating the block's total exp-mass.  The group's score is the mean of
+    l_{h,p} over its heads (reading: the log-domain analogue of the
+    head-collapsed channel).  Ranking by the log score equals ranking by the
+    score itself and cannot overflow.
+
+    q_heads: [G, d], mean/var: [P, d], n_valid: [P] -> [P]
+    """
+    q_heads, mean, var = f64(q_heads), f64(mean), f64(var)
+    qp = s_att * q_heads                      # [G, d]
+    first = qp @ mean.T                       # [G, P]  q'_h . kbar_p
+    second = np.log1p(0.5 * ((qp * qp) @ var.T))  # [G, P]
+    ell = first + second
+    partial = np.log(np.asarray(n_valid, dtype=np.float64) / page_size)
+    return ell.mean(axis=0) + partial
+
+
+# ---------------------------------------------------------------------------
+# Support selection (RTPurbo section 3; Oracle-Guided Sparse Prefill 2.1/2.2)
+# ---------------------------------------------------------------------------
+
+
+def candidate_order(x) -> np.ndarray:
+    """Candidates ranked by score descending; equal scores by index ascending."""
+    x = f64(x)
+    idx = np.arange(x.shape[0])
+    return np.lexsort((idx, -x))
+
+
+def softmax_mass(x) -> np.ndarray:
+    """Attention mass of each candidate under the indexer scores."""
+    x = f64(x)
+    w = np.exp(x - x.max())
+    return w / w.sum()
+
+
+def select_topp(x, p: float) -> np.ndarray:
+    """Dynamic top-p support: the shortest prefix of the candidate order whose
+    accumulated mass reaches p (cumulative >= p).  p >= 1 keeps every
+    candidate, as does a prefix sum that never reaches p in floating point.
+    Returns the selected indices in ascending order.
+    """
+    x = f64(x)
+    n = x.shape[0]
+    if n == 0:
+        return np.zeros(0, dtype=np.int64)
+    if not p > 0:
+        raise ValueError("p must be in (0, 1]")
+    if p >= 1.0:
+        return np.arange(n)
+    order = candidate_order(x)
+    take = prefix_reaching(softmax_mass(x)[order], p)
+    return np.sort(order[:take])
+
+
+def prefix_reaching(mass_in_order, p: float) -> int:
+    """Length of the shortest prefix of the ordered masses whose running sum
+    is >= p (all of them if the sum never gets there)."""
+    n = len(mass_in_order)
+    cum = 0.0
+    for i in range(n):
+        cum += float(mass_in_order[i])
+        if cum >= p:
+            return i + 1
+    return n
+
+
+def select_topk(x, k: int) -> np.ndarray:
+    """Static top-k support: the first min(k, n) candidates of the order,
+    returned in ascending index order."""
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    order = candidate_order(x)
+    return np.sort(order[: min(k, order.shape[0])])
+
+
+def with_sink_window(S, L: int, n_sink: int, n_window: int) -> np.ndarray:
+    """Union of a support with the always-kept attention-sink tokens [0, n_sink)
+    and the sliding window [L - n_window, L) (reading: the local tokens are
+    added after selection and do not take part in the mass count)."""
+    keep = set(int(j) for j in S)
+    keep.update(range(0, min(n_sink, L)))
+    keep.update(range(max(0, L - n_window), L))
+    return np.array(sorted(keep), dtype=np.int64)
+
+
+def expand_pages(pages, L: int, page_size: int = 64) -> np.ndarray:
+    """Token indices of the selected pages (the last page may be partial)."""
+    out = []
+    for p in sorted(int(q) for q in pages):
+        out.extend(range(p * page_size, min(L, (p + 1) * page_size)))
+    return np.array(out, dtype=np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Exact attention over the support (Oracle-Guided Sparse Prefill 2.1)
+# ---------------------------------------------------------------------------
+
+
+def attend(q_heads, K, V, s_att: float):
+    """Softmax attention of each query head over the given keys/values,
+    renormalised over them (the support).
+
+    q_heads: [G, d], K/V: [n, d]  ->  o [G, d], lse [G]
+    lse_h = log sum_j exp(s_att * q_h . k_j).
+    """
+    q_heads, K, V = f64(q_heads), f64(K), f64(V)
+    G = q_heads.shape[0]
+    o = np.zeros((G, V.shape[1]))
+    lse = np.zeros(G)
+    for h in range(G):
+        logits = s_att * (K @ q_heads[h])
+        m = logits.max()
+        w = np.exp(logits - m)
+        l = w.sum()
+        o[h] = (w @ V) / l
+        lse[h] = m + math.log(l)
+    return o, lse
+
+
+def decode_row(q_heads, w_q_heads, ktil, K, V, *, s_idx, s_att, p=None, k=None,
+               n_sink=0, n_window=0):
+    """One decode step of one key/value group: indexer scores, top-p (or
+    top-k) support, sink/window union, exact attention over the support."""
+    L = K.shape[0]
+    q_c = collapse_query(q_heads, w_q_heads, s_idx)
+    x = token_scores(q_c, ktil)
+    if (p is None) == (k is None):
+        raise ValueError("give exactly one of p, k")
+    S = select_topp(x, p) if p is not None else select_topk(x, k)
+    S = with_sink_window(S, L, n_sink, n_window)
+    o, lse = attend(q_heads, f64(K)[S], f64(V)[S], s_att)
+    return {"q_c": q_c, "x": x, "S": S, "o": o, "lse": lse}
+
+
+def decode_row_pages(q_heads, mean, var, n_valid, K, V, *, s_att, k_pages,
+                     page_size=64):
+    """Page-granular decode of one group: Taylor page scores, top-k pages,
+    expansion to tokens, exact attention over those tokens."""
+    L = K.shape[0]
+    x = page_scores(q_heads, mean, var, n_valid, s_att, page_size)
+    pages = select_topk(x, k_pages)
+    S = expand_pages(pages, L, page_size)
+    o, lse = attend(q_heads, f64(K)[S], f64(V)[S], s_att)
+    return {"x": x, "pages": pages, "S": S, "o": o, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# Causal prefill with a support shared by a block of b_sel queries
+# (Oracle-Guided Sparse Prefill 2.1 granularity, 2.2 inference)
+# ---------------------------------------------------------------------------
+
+
+def prefill_block_rows(blk: int, b_sel: int, N: int) -> range:
+    return range(blk * b_sel, min(N, (blk + 1) * b_sel))
+
+
+def prefill_block_query(Q_blk, w_q_heads, s_idx: float) -> np.ndarray:
+    """Indexer query shared by a query block and a group: the mean over the
+    block's queries and the group's heads of W_q[h]^T q_{i,h}, times s_idx.
+
+    Q_blk: [n_rows, G, d], w_q_heads: [G, d, r] -> [r]
+    """
+    Q_blk, w_q_heads = f64(Q_blk), f64(w_q_heads)
+    n_rows, G, _ = Q_blk.shape
+    acc = np.zeros(w_q_heads.shape[2])
+    for i in range(n_rows):
+        for h in range(G):
+            acc += w_q_heads[h].T @ Q_blk[i, h]
+    return s_idx * acc / (n_rows * G)
+
+
+def prefill_block_support(q_c, ktil, blk: int, b_sel: int, k: int) -> np.ndarray:
+    """Shared support of query block blk: top-k of the indexer scores over the
+    keys of all earlier blocks, j < b_sel * blk (all of them when there are at
+    most k).  The block's own (diagonal) keys are always attended, causally,
+    and are not part of this list."""
+    n_cand = blk * b_sel
+    if n_cand == 0:
+        return np.zeros(0, dtype=np.int64)
+    x = token_scores(q_c, f64(ktil)[:n_cand])
+    return select_topk(x, k)
+
+
+def prefill_block_attend(Q_blk, K, V, S, blk: int, b_sel: int, s_att: float):
+    """Exact attention of each row of a query block: keys are the shared
+    support S plus the block's own keys up to and including the row's
+    position.
+
+    Q_blk: [n_rows, G, d], K/V: [N, d] (keys of the group) -> o [n_rows, G, d],
+    lse [n_rows, G]
+    """
+    Q_blk, K, V = f64(Q_blk), f64(K), f64(V)
+    n_rows, G, d = Q_blk.shape
+    base = blk * b_sel
+    o = np.zeros((n_rows, G, d))
+    lse = np.zeros((n_rows, G))
+    S = [int(j) for j in S]
+    for i in range(n_rows):
+        keys = S + list(range(base, base + i + 1))
+        oi, li = attend(Q_blk[i], K[keys], V[keys], s_att)
+        o[i] = oi
+        lse[i] = li
+    return o, lse

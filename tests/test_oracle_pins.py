@@ -1,0 +1,508 @@
+"""Pins of the float64 oracle to facts fixed outside the oracle itself:
+hand-made distributions, brute force on tiny inputs, closed forms, library
+routines (torch scaled_dot_product_attention in float64), and the invariants
+the pages state.  CPU only."""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding helper
+# ---------------------------------------------------------------------------
+
+
+def test_round_to_bf16_matches_torch_on_fp32_values():
+    rng = _rng(0)
+    x32 = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(3.0),
+        (rng.standard_normal(2000) * 1e-30).astype(np.float32),
+        (rng.standard_normal(2000) * 1e30).astype(np.float32),
+    ])
+    ref = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.round_to_bf16(x32.astype(np.float64)), ref)
+
+
+def test_round_to_bf16_halfway_cases():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to even -> 1.
+    assert O.round_to_bf16(np.array([1 + 2.0 ** -8]))[0] == 1.0
+    # 1 + 3*2^-8 lies halfway between 1+2^-7 (odd) and 1+2^-6 (even) -> 1+2^-6.
+    assert O.round_to_bf16(np.array([1 + 3 * 2.0 ** -8]))[0] == 1 + 2.0 ** -6
+    # just above halfway rounds up
+    assert O.round_to_bf16(np.array([1 + 2.0 ** -8 + 2.0 ** -30]))[0] == 1 + 2.0 ** -7
+    assert O.round_to_bf16(np.array([-1 - 2.0 ** -8 - 2.0 ** -30]))[0] == -1 - 2.0 ** -7
+    assert O.round_to_bf16(np.array([0.0]))[0] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Selection rule: golden dyadic cases, brute force
+# ---------------------------------------------------------------------------
+
+
+def _golden_cases():
+    cases = []
+    with open(os.path.join(GOLDEN, "topp_dyadic.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            kind, masses, param, expect = [s.strip() for s in line.split("|")]
+            cases.append((kind, np.array([float(v) for v in masses.split()]),
+                          float(param), [int(v) for v in expect.split()]))
+    return cases
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: f"{c[0]}-{c[2]}-{len(c[1])}")
+def test_golden_dyadic_rule(case):
+    kind, masses, param, expect = case
+    order = O.candidate_order(masses)  # order of masses == order of log-scores
+    if kind == "topp":
+        take = O.prefix_reaching(masses[order], param) if param < 1 else len(masses)
+        got = sorted(order[:take].tolist())
+    else:
+        got = sorted(order[: min(int(param), len(masses))].tolist())
+    assert got == expect
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: f"{c[0]}-{c[2]}-{len(c[1])}")
+def test_golden_through_scores(case):
+    """The score-level entry points reproduce the golden sets when scores are
+    log-masses, except where p sits exactly on a running sum (there rounding
+    of exp/log may decide, and the mass-level test above already pins it)."""
+    kind, masses, param, expect = case
+    x = np.log(masses)
+    if kind == "topk":
+        assert O.select_topk(x, int(param)).tolist() == expect
+        return
+    cums = np.cumsum(np.sort(masses)[::-1])
+    if param < 1 and np.any(np.abs(cums - param) < 1e-12):
+        pytest.skip("p on an exact running sum")
+    assert O.select_topp(x, param).tolist() == expect
+
+
+def test_softmax_mass_closed_form_and_shift():
+    x = np.log(np.array([1.0, 2.0, 5.0]))
+    np.testing.assert_allclose(O.softmax_mass(x), [1 / 8, 2 / 8, 5 / 8], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(O.softmax_mass(x + 700.0), [1 / 8, 2 / 8, 5 / 8], atol=1e-15)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_topp_brute_force(seed):
+    rng = _rng(100 + seed)
+    n = int(rng.integers(1, 11))
+    x = rng.standard_normal(n) * 2.0
+    w = np.exp(x)
+    for p in (0.3, 0.5, 0.77, 0.9, 0.99):
+        S = O.select_topp(x, p)
+        # brute force: minimum cardinality among subsets reaching p, then max mass
+        best = None
+        for c in range(1, n + 1):
+            feas = []
+            for sub in itertools.combinations(range(n), c):
+                m = math.fsum(w[list(sub)]) / math.fsum(w)
+                if m >= p:
+                    feas.append((m, sub))
+            if feas:
+                best = (c, max(feas)[1])
+                break
+        assert best is not None
+        assert len(S) == best[0]
+        assert sorted(S.tolist()) == sorted(best[1])
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_topk_brute_force(seed):
+    rng = _rng(200 + seed)
+    n = int(rng.integers(1, 11))
+    x = rng.standard_normal(n)
+    for k in range(1, n + 2):
+        S = O.select_topk(x, k)
+        c = min(k, n)
+        best = max(itertools.combinations(range(n), c), key=lambda s: math.fsum(x[list(s)]))
+        assert sorted(S.tolist()) == sorted(best)
+
+
+def test_ties_take_lower_index_and_all_at_p1():
+    x = np.array([1.0, 3.0, 3.0, 3.0, 0.0])
+    assert O.select_topk(x, 2).tolist() == [1, 2]
+    assert O.select_topp(x, 1.0).tolist() == [0, 1, 2, 3, 4]
+    # three tied maxima carry most of the mass; p just above 2/3 of their sum
+    w = np.exp(x - 3.0)
+    p = (2 * w[1]) / w.sum() + 1e-9
+    assert O.select_topp(x, p).tolist() == [1, 2, 3]
+    with pytest.raises(ValueError):
+        O.select_topp(x, 0.0)
+    with pytest.raises(ValueError):
+        O.select_topk(x, 0)
+
+
+def test_sink_window_and_page_expansion():
+    S = np.array([10, 50, 97])
+    assert O.with_sink_window(S, 100, 4, 5).tolist() == [0, 1, 2, 3, 10, 50, 95, 96, 97, 98, 99]
+    assert O.with_sink_window(np.array([], dtype=int), 3, 4, 512).tolist() == [0, 1, 2]
+    assert O.expand_pages([2, 0], 150, 64).tolist() == list(range(0, 64)) + list(range(128, 150))
+
+
+# ---------------------------------------------------------------------------
+# Indexer
+# ---------------------------------------------------------------------------
+
+
+def test_indexer_coordinate_projector_reduces_to_plain_dot():
+    """With W = [I_r; 0] the low-rank channel is the first r coordinates, so
+    the score is s_idx * (mean_h q_h[:r]) . k_j[:r]."""
+    rng = _rng(1)
+    d, r, G, L = 32, 16, 4, 50
+    W = np.zeros((d, r))
+    W[:r, :r] = np.eye(r)
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((L, d))
+    s = 0.37
+    x = O.token_scores(O.collapse_query(q, np.stack([W] * G), s), O.indexer_keys(K, W))
+    expect = np.array([s * sum(q[:, i].mean() * K[j, i] for i in range(r)) for j in range(L)])
+    np.testing.assert_allclose(x, expect, rtol=1e-13, atol=1e-13)
+
+
+def test_indexer_collapse_is_mean_of_head_logits():
+    rng = _rng(2)
+    d, r, G, L = 64, 16, 8, 40
+    Wq = rng.standard_normal((G, d, r)) / 8
+    Wk = rng.standard_normal((d, r)) / 8
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((L, d))
+    kt = O.indexer_keys(K, Wk)
+    x = O.token_scores(O.collapse_query(q, Wq, 1.5), kt)
+    per_head = np.stack([O.token_scores(O.collapse_query(q[h:h + 1], Wq[h:h + 1], 1.5), kt)
+                         for h in range(G)])
+    np.testing.assert_allclose(x, per_head.mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_indexer_group_semantics():
+    """Two groups whose heads point at different planted keys: each group's
+    top-1 is its own key, and the sign is right (aligned keys score high)."""
+    rng = _rng(3)
+    d, r, H_q, H_kv, L = 32, 16, 8, 2, 64
+    G = H_q // H_kv
+    W = rng.standard_normal((H_kv, d, r)) / math.sqrt(d)
+    K = rng.standard_normal((L, H_kv, d)) * 0.1
+    q = rng.standard_normal((H_q, d)) * 0.1
+    targets = {0: 5, 1: 41}
+    for g, j in targets.items():
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        for h in O.heads_of_group(g, H_q, H_kv):
+            q[h] += 3 * u
+        K[j, g] += 4 * u
+        K[targets[1 - g], g] -= 4 * u  # the other group's needle is anti-aligned here
+    for g, j in targets.items():
+        hs = O.heads_of_group(g, H_q, H_kv)
+        qc = O.collapse_query(q[hs], np.stack([W[g]] * G), 1.0)
+        x = O.token_scores(qc, O.indexer_keys(K[:, g], W[g]))
+        assert O.select_topk(x, 1).tolist() == [j]
+        assert int(np.argmin(x)) == targets[1 - g]
+
+
+# ---------------------------------------------------------------------------
+# Page statistics and the Taylor page score
+# ---------------------------------------------------------------------------
+
+
+def test_page_stats_closed_forms():
+    d = 8
+    # page 0: constant rows; page 1: +/- sigma pairs around m; page 2: arithmetic
+    # progression 0..63 in every dim; page 3 (partial, 10 rows): 0..9
+    c = np.arange(d, dtype=float)
+    m = np.linspace(-1, 1, d)
+    sig = 0.75
+    p1 = np.concatenate([m + sig * np.ones(d)] * 32 + [m - sig * np.ones(d)] * 32).reshape(64, d)
+    p2 = np.repeat(np.arange(64, dtype=float)[:, None], d, axis=1)
+    p3 = np.repeat(np.arange(10, dtype=float)[:, None], d, axis=1)
+    K = np.concatenate([np.tile(c, (64, 1)), p1, p2, p3])
+    mean, var, n = O.page_stats(K, 64)
+    assert n.tolist() == [64, 64, 64, 10]
+    np.testing.assert_allclose(mean[0], c, atol=0)
+    np.testing.assert_allclose(var[0], 0, atol=0)
+    np.testing.assert_allclose(mean[1], m, atol=1e-15)
+    np.testing.assert_allclose(var[1], sig ** 2, rtol=1e-14)
+    np.testing.assert_allclose(mean[2], 31.5, rtol=1e-15)
+    np.testing.assert_allclose(var[2], (64 ** 2 - 1) / 12, rtol=1e-14)
+    np.testing.assert_allclose(mean[3], 4.5, rtol=1e-15)
+    np.testing.assert_allclose(var[3], (10 ** 2 - 1) / 12, rtol=1e-14)
+
+
+def _axis_pair_page(kbar, sig, rng, npairs=32):
+    """64 keys kbar +/- sig*z*e_a (pairs along coordinate axes): the empirical
+    mean is exactly kbar and the empirical covariance exactly diagonal."""
+    d = kbar.shape[0]
+    rows = []
+    for _ in range(npairs):
+        a = int(rng.integers(d))
+        z = float(rng.standard_normal())
+        e = np.zeros(d)
+        e[a] = sig * z
+        rows += [kbar + e, kbar - e]
+    return np.array(rows)
+
+
+def test_taylor_constant_page_is_exact():
+    rng = _rng(4)
+    d = 16
+    kb = rng.standard_normal(d)
+    page = np.tile(kb, (64, 1))
+    q = rng.standard_normal(d) * 0.3
+    mean, var, _ = O.page_stats(page, 64)
+    exact = np.mean(np.exp(page @ q))
+    assert O.taylor_page_score(q, mean[0], var[0]) == pytest.approx(exact, rel=1e-14)
+
+
+def test_taylor_axis_pairs_fourth_order_decay():
+    """On axis-pair pages the Taylor score misses only 4th and higher moments:
+    relative error ~ sigma^4 (log-log slope 4)."""
+    rng = _rng(5)
+    d = 16
+    kb = rng.standard_normal(d) * 0.2
+    q = rng.standard_normal(d) * 0.5
+    base = _axis_pair_page(kb, 1.0, _rng(6)) - kb  # unit-scale deviations
+    errs = []
+    sigmas = [0.4, 0.2, 0.1, 0.05, 0.025]
+    for s in sigmas:
+        page = kb + s * base
+        mean, var, _ = O.page_stats(page, 64)
+        exact = np.mean(np.exp(page @ q))
+        errs.append(abs(O.taylor_page_score(q, mean[0], var[0]) - exact) / exact)
+    slopes = np.diff(np.log(errs)) / np.diff(np.log(sigmas))
+    assert np.all(np.abs(slopes - 4.0) < 0.15), slopes
+
+
+def test_taylor_diagonal_leaves_offdiagonal_term():
+    """On general random pages the diagonal approximation leaves the
+    off-diagonal covariance term, so the error is far larger than on
+    axis-pair pages of the same scale (pins the diagonal, not the full
+    covariance, being used)."""
+    rng = _rng(7)
+    d = 16
+    q = rng.standard_normal(d) * 0.5
+    kb = rng.standard_normal(d) * 0.2
+    for s in (0.1, 0.025):
+        gen = kb + s * rng.standard_normal((64, d))
+        ax = kb + s * (_axis_pair_page(kb, 1.0, _rng(8)) - kb)
+        errs = []
+        for page in (gen, ax):
+            mean, var, _ = O.page_stats(page, 64)
+            exact = np.mean(np.exp(page @ q))
+            errs.append(abs(O.taylor_page_score(q, mean[0], var[0]) - exact) / exact)
+        assert errs[0] > 50 * errs[1]
+
+
+def test_taylor_gaussian_closed_form():
+    """For k ~ N(mu, diag(s2)), E exp(q.k) = exp(q.mu + q^T S q / 2); the
+    Taylor score is its first-order expansion in t = q^T S q, so the relative
+    gap approaches t^2/8."""
+    rng = _rng(9)
+    d = 16
+    mu = rng.standard_normal(d) * 0.3
+    s2 = rng.uniform(0.5, 1.5, d)
+    for scale in (0.1, 0.05, 0.02):
+        q = rng.standard_normal(d) * scale
+        t = float((q * q) @ s2)
+        exact = math.exp(float(q @ mu) + 0.5 * t)
+        gap = (exact - O.taylor_page_score(q, mu, s2)) / exact
+        assert gap == pytest.approx(t * t / 8, rel=0.05)
+
+
+def test_page_scores_is_mean_of_log_taylor_scores():
+    rng = _rng(10)
+    d, G, P = 16, 4, 6
+    q = rng.standard_normal((G, d))
+    mean = rng.standard_normal((P, d))
+    var = rng.uniform(0, 2, (P, d))
+    n = np.array([64] * 5 + [20])
+    s = 0.25
+    x = O.page_scores(q, mean, var, n, s, 64)
+    for p in range(P):
+        logs = [math.log(O.taylor_page_score(s * q[h], mean[p], var[p])) for h in range(G)]
+        assert x[p] == pytest.approx(np.mean(logs) + math.log(n[p] / 64), abs=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Attention over the support
+# ---------------------------------------------------------------------------
+
+
+def _sdpa(q, K, V, scale, causal=False):
+    """torch SDPA in float64 on CPU (math backend), the library reference."""
+    qt = torch.from_numpy(np.ascontiguousarray(q, dtype=np.float64))
+    Kt = torch.from_numpy(np.ascontiguousarray(K, dtype=np.float64))
+    Vt = torch.from_numpy(np.ascontiguousarray(V, dtype=np.float64))
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, Kt, Vt, scale=scale, is_causal=causal)
+    return out.numpy()
+
+
+def test_dense_special_case_matches_sdpa():
+    """p = 1 or k >= L (no sink/window) select every key, and the sparse
+    decode equals dense attention."""
+    rng = _rng(11)
+    G, d, L, r = 4, 32, 200, 16
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((L, d))
+    V = rng.standard_normal((L, d))
+    Wq = rng.standard_normal((G, d, r)) / math.sqrt(d)
+    Wk = rng.standard_normal((d, r)) / math.sqrt(d)
+    kt = O.indexer_keys(K, Wk)
+    s = 1 / math.sqrt(d)
+    ref = _sdpa(q[None, :, None, :], K[None, None], V[None, None], s)[0, :, 0]
+    for kw in ({"p": 1.0}, {"k": L}, {"k": L + 7}):
+        out = O.decode_row(q, Wq, kt, K, V, s_idx=1.0, s_att=s, **kw)
+        assert out["S"].tolist() == list(range(L))
+        np.testing.assert_allclose(out["o"], ref, rtol=0, atol=1e-12)
+    # lse against a direct logsumexp of the full logits
+    o, lse = O.attend(q, K, V, s)
+    logits = s * q @ K.T
+    np.testing.assert_allclose(lse, np.log(np.exp(logits).sum(axis=1)), rtol=1e-13)
+
+
+def test_single_key_support_returns_its_value():
+    rng = _rng(12)
+    q = rng.standard_normal((3, 16))
+    K = rng.standard_normal((1, 16))
+    V = rng.standard_normal((1, 16))
+    o, lse = O.attend(q, K, V, 0.25)
+    for h in range(3):
+        np.testing.assert_array_equal(o[h], V[0])
+    np.testing.assert_allclose(lse, 0.25 * q @ K[0], rtol=1e-15)
+
+
+def test_gqa_heads_equal_single_head_attention():
+    rng = _rng(13)
+    q = rng.standard_normal((8, 32))
+    K = rng.standard_normal((70, 32))
+    V = rng.standard_normal((70, 32))
+    o, lse = O.attend(q, K, V, 0.2)
+    for h in range(8):
+        oh, lh = O.attend(q[h:h + 1], K, V, 0.2)
+        np.testing.assert_array_equal(oh[0], o[h])
+        assert lh[0] == lse[h]
+
+
+def test_kv_permutation_invariance_decode():
+    """Jointly permuting (k_j, v_j, K~_j) leaves the output unchanged and maps
+    the support through the permutation (scores have no ties here)."""
+    rng = _rng(14)
+    G, d, L, r = 4, 32, 300, 16
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((L, d))
+    V = rng.standard_normal((L, d))
+    W = rng.standard_normal((d, r)) / math.sqrt(d)
+    Wq = np.stack([W] * G)
+    kt = O.indexer_keys(K, W)
+    perm = rng.permutation(L)
+    for kw in ({"p": 0.8}, {"k": 40}):
+        a = O.decode_row(q, Wq, kt, K, V, s_idx=2.0, s_att=0.2, **kw)
+        b = O.decode_row(q, Wq, kt[perm], K[perm], V[perm], s_idx=2.0, s_att=0.2, **kw)
+        assert sorted(perm[b["S"]].tolist()) == a["S"].tolist()
+        np.testing.assert_allclose(b["o"], a["o"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(b["lse"], a["lse"], rtol=0, atol=1e-12)
+
+
+def test_head_permutation_covariance_decode():
+    rng = _rng(15)
+    G, d, L, r = 4, 16, 100, 16
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((L, d))
+    V = rng.standard_normal((L, d))
+    W = rng.standard_normal((d, r)) / 4
+    Wq = np.stack([W] * G)
+    kt = O.indexer_keys(K, W)
+    perm = rng.permutation(G)
+    a = O.decode_row(q, Wq, kt, K, V, s_idx=1.0, s_att=0.25, p=0.9)
+    b = O.decode_row(q[perm], Wq[perm], kt, K, V, s_idx=1.0, s_att=0.25, p=0.9)
+    assert a["S"].tolist() == b["S"].tolist()
+    np.testing.assert_allclose(b["o"], a["o"][perm], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Causal prefill with block-shared supports
+# ---------------------------------------------------------------------------
+
+
+def _prefill_case(seed, N=320, G=2, d=16, r=16):
+    rng = _rng(seed)
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    W = rng.standard_normal((d, r)) / math.sqrt(d)
+    return Q, K, V, np.stack([W] * G), O.indexer_keys(K, W)
+
+
+def test_early_prefill_blocks_equal_dense_causal():
+    """While b_sel * blk <= k every earlier key is kept, so each row equals
+    dense causal attention."""
+    b_sel, k = 32, 96
+    Q, K, V, Wq, kt = _prefill_case(16, N=224)
+    s = 0.25
+    N, G, d = Q.shape
+    ref = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], V[None, None], s, causal=True)[0]
+    for blk in range(0, k // b_sel + 1):
+        rows = O.prefill_block_rows(blk, b_sel, N)
+        qc = O.prefill_block_query(Q[rows.start:rows.stop], Wq, 1.0)
+        S = O.prefill_block_support(qc, kt, blk, b_sel, k)
+        assert S.tolist() == list(range(blk * b_sel))
+        o, _ = O.prefill_block_attend(Q[rows.start:rows.stop], K, V, S, blk, b_sel, s)
+        np.testing.assert_allclose(o, np.transpose(ref[:, rows.start:rows.stop], (1, 0, 2)),
+                                   rtol=0, atol=1e-12)
+
+
+def test_prefill_segment_permutation_invariance():
+    """Permuting the keys strictly before the block (one segment, pairing of
+    k, v and K~ kept) leaves the block's outputs unchanged."""
+    b_sel, k, blk = 32, 40, 6
+    Q, K, V, Wq, kt = _prefill_case(17)
+    rng = _rng(18)
+    base = blk * b_sel
+    perm = np.concatenate([rng.permutation(base), np.arange(base, K.shape[0])])
+    rows = O.prefill_block_rows(blk, b_sel, K.shape[0])
+    Qb = Q[rows.start:rows.stop]
+    qc = O.prefill_block_query(Qb, Wq, 1.0)
+    S1 = O.prefill_block_support(qc, kt, blk, b_sel, k)
+    S2 = O.prefill_block_support(qc, kt[perm], blk, b_sel, k)
+    assert sorted(perm[S2].tolist()) == S1.tolist()
+    o1, l1 = O.prefill_block_attend(Qb, K, V, S1, blk, b_sel, 0.25)
+    o2, l2 = O.prefill_block_attend(Qb, K[perm], V[perm], S2, blk, b_sel, 0.25)
+    np.testing.assert_allclose(o2, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, rtol=0, atol=1e-12)
+
+
+def test_prefill_block_query_permutation_invariant():
+    Q, K, V, Wq, kt = _prefill_case(19)
+    rng = _rng(20)
+    Qb = Q[64:96]
+    a = O.prefill_block_query(Qb, Wq, 0.7)
+    b = O.prefill_block_query(Qb[rng.permutation(32)], Wq, 0.7)
+    c = O.prefill_block_query(Qb[:, ::-1], Wq[::-1], 0.7)
+    np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(a, c, rtol=1e-13, atol=1e-14)
+
+
+def test_prefill_support_excludes_own_block_and_is_topk():
+    b_sel, k, blk = 32, 20, 5
+    Q, K, V, Wq, kt = _prefill_case(21)
+    rows = O.prefill_block_rows(blk, b_sel, K.shape[0])
+    qc = O.prefill_block_query(Q[rows.start:rows.stop], Wq, 1.0)
+    S = O.prefill_block_support(qc, kt, blk, b_sel, k)
+    assert len(S) == k and S.max() < blk * b_sel
+    x = kt[: blk * b_sel] @ qc
+    assert x[S].min() > np.delete(x, S).max()
