@@ -1,0 +1,345 @@
+"""Throughput of the sparse-attention hot path on one MI355X.
+
+    python bench.py [--workload decode64k|decode1m|batched|prefill128k]
+                    [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+A step is one pass of the whole path over one batch of synthetic input
+(inputs already resident in GPU memory):
+  decode64k : indexer scores + top-p(0.9) select (+4 sink, +512 window) +
+              split-KV sparse decode; B=1, 32/4 heads, d=128, L=65536, bf16
+  decode1m  : Taylor page scores + top-32 pages + sparse decode; L=2^20
+  batched   : as decode64k for 32 sequences of 16K-128K tokens, 32/8 heads
+  prefill128k: block top-k(2048) selection + block-sparse causal prefill
+Prints one JSON line.  The value is the algorithmic HBM bytes of the step
+(indexer keys or page statistics, plus the selected K/V rows) per second for
+the decode workloads, and selected-block FLOP/s for prefill.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("sparse decode µs/step + HBM GB/s at 64K/1M; sparse prefill TFLOP/s at 128K")
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode64k",
+                    choices=["decode64k", "decode1m", "batched", "prefill128k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--warm", action="store_true",
+                    help="reuse one input replica every step (cache-warm)")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+
+def _events():
+    import torch
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_loop(fn, n, warmup=3, reps=1):
+    """Average device milliseconds per call of fn(i).
+
+    The calls fn(0) .. fn(reps-1) (one per input replica) are captured once
+    into a HIP graph on a side stream (every library call launches on the
+    current stream), and the graph is replayed until n calls have run, timed
+    with HIP events on that stream: the figure excludes Python and launch
+    overhead between calls, not the gaps between kernels inside a call."""
+    import torch
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(max(warmup, 1)):
+            fn(i % reps)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(reps):
+            fn(i)
+    torch.cuda.synchronize()
+    n_rep = max(1, math.ceil(n / reps))
+    with torch.cuda.stream(s):
+        for _ in range(max(1, warmup // reps)):
+            g.replay()
+        a, b = _events()
+        a.record(s)
+        for _ in range(n_rep):
+            g.replay()
+        b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (n_rep * reps)
+
+
+def fill_kidx(ops, shape, inp, kidx_pool):
+    """Indexer keys of every pool row through sa_index_append (cache
+    maintenance, outside the timed region)."""
+    import torch
+    P, Hkv, page, d = inp.k_pool.shape
+    step = max(1, (1 << 26) // (page * Hkv * d))
+    for p0 in range(0, P, step):
+        p1 = min(P, p0 + step)
+        k_pre = inp.k_pool[p0:p1].permute(0, 2, 1, 3).reshape(-1, Hkv, d).contiguous()
+        slot = torch.arange(p0 * page, p1 * page, device=k_pre.device, dtype=torch.int64)
+        ops.sa_index_append(shape, k_pre, inp.w_k, slot, kidx_pool)
+
+
+def cpu_threads_info():
+    return len(os.sched_getaffinity(0))
+
+
+# ---------------------------------------------------------------------------
+# decode workloads
+# ---------------------------------------------------------------------------
+
+
+def bench_decode(args, name):
+    import numpy as np
+    import torch
+
+    import synth
+    from dynamic_sparse_attention_02_amd import _lib as L
+    from dynamic_sparse_attention_02_amd import ops
+
+    dev = "cuda"
+    if name == "decode64k":
+        inp = synth.make_decode64k(device="cpu").to(dev)  # CPU draw keeps the budget fixed
+    elif name == "batched":
+        inp = synth.make_batched_decode(device=dev)
+    else:
+        inp = synth.make_decode1m(device=dev)
+    B, Hq, Hkv, d = inp.B, inp.H_q, inp.H_kv, inp.d
+    rows = B * Hkv
+    Lmax = max(inp.seq_lens)
+    shape = ops.make_shape(batch=B, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                           max_pages=inp.max_pages, max_len=Lmax, n_pool_pages=inp.n_pages)
+    lens = inp.seq_lens_tensor()
+    pages = ops.make_pages(inp.page_table, lens)
+    page_mode = name == "decode1m"
+    sel = inp.select
+    n_sink, n_window = sel.get("n_sink", 0), sel.get("n_window", 0)
+
+    if page_mode:
+        stats = torch.empty((inp.n_pages, Hkv, 2, d), dtype=inp.dtype, device=dev)
+        pid = torch.arange(inp.n_pages, dtype=torch.int32, device=dev)
+        nval = torch.full((inp.n_pages,), 64, dtype=torch.int32, device=dev)
+        ops.sa_page_stats(shape, inp.k_pool, pid, nval, stats)
+        cache_a = stats
+        k_pages = sel["k_pages"]
+        cap = k_pages * 64
+        n_cand = inp.max_pages
+        x = torch.empty((rows, n_cand), dtype=torch.float32, device=dev)
+        per_row_index_bytes = [math.ceil(L / 64) * 2 * d * 2 for L in inp.seq_lens]
+    else:
+        kidx = torch.zeros((inp.n_pages, Hkv, 64, 16), dtype=inp.dtype, device=dev)
+        fill_kidx(ops, shape, inp, kidx)
+        cache_a = kidx
+        cap = Lmax
+        x = torch.empty((rows, Lmax), dtype=torch.float32, device=dev)
+        per_row_index_bytes = [L * 16 * 2 for L in inp.seq_lens]
+    idx = torch.empty((rows, cap), dtype=torch.int32, device=dev)
+    count = torch.empty((rows,), dtype=torch.int32, device=dev)
+    out = torch.empty((B, Hq, d), dtype=inp.dtype, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    ws_sel = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SELECT, shape, x.shape[1]))
+    ws_dec = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SPARSE_DECODE, shape, cap))
+    ws_idx = ops.alloc_workspace(ops.workspace_size(L.SA_OP_INDEX_SCORES, shape, 0))
+
+    # bytes a step must touch (index part: all of it; K/V: the selected rows)
+    def run_select(rep):
+        a, kp, vp = rep
+        if page_mode:
+            ops.sa_page_scores(shape, pages, inp.q, a, inp.s_att, x)
+            ops.sa_select_topk(shape, pages, x, k_pages, 64, 0, 0, idx, count, ws_sel)
+        else:
+            ops.sa_index_scores(shape, pages, inp.q, inp.w_q, a, inp.s_idx, x, ws_idx)
+            ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
+
+    def run_step(rep):
+        run_select(rep)
+        ops.sa_sparse_decode(shape, pages, inp.q, rep[1], rep[2], idx, count, inp.s_att, out, lse,
+                             ws_dec)
+
+    base = (cache_a, inp.k_pool, inp.v_pool)
+    run_step(base)
+    torch.cuda.synchronize()
+    counts = count.cpu().numpy().astype(np.int64)
+    kv_bytes = int(counts.sum()) * 2 * d * 2
+    index_bytes = int(sum(per_row_index_bytes[b] for b in range(B) for _ in range(Hkv)))
+    step_bytes = index_bytes + kv_bytes
+
+    # input replicas so that a step does not find the previous step's rows in
+    # the 256 MB last-level cache
+    R = 1 if args.warm else max(1, min(32, math.ceil(4 * MALL_BYTES / step_bytes)))
+    reps = [base] + [tuple(t.clone() for t in base) for _ in range(R - 1)]
+    torch.cuda.synchronize()
+
+    ms = time_loop(lambda i: run_step(reps[i]), args.steps, warmup=args.warmup, reps=R)
+    # the graph replays must reproduce an eager step bit for bit
+    torch.cuda.synchronize()
+    g_out, g_idx, g_cnt = out.clone(), idx.clone(), count.clone()
+    run_step(reps[R - 1])
+    torch.cuda.synchronize()
+    assert torch.equal(g_cnt, count) and torch.equal(g_idx, idx) and torch.equal(g_out, out), \
+        "graph replay differs from the eager step"
+    # per-component times (same rotation), for the breakdown and the roofline
+    if page_mode:
+        t_index = time_loop(lambda i: ops.sa_page_scores(shape, pages, inp.q, reps[i][0],
+                                                         inp.s_att, x), args.steps, reps=R)
+    else:
+        t_index = time_loop(lambda i: ops.sa_index_scores(shape, pages, inp.q, inp.w_q,
+                                                          reps[i][0], inp.s_idx, x, ws_idx),
+                            args.steps, reps=R)
+    run_select(base)
+    t_select = time_loop(lambda i: (ops.sa_select_topk(shape, pages, x, k_pages, 64, 0, 0, idx,
+                                                       count, ws_sel) if page_mode else
+                                    ops.sa_select_topp(shape, pages, x, sel["p"], n_sink,
+                                                       n_window, idx, count, ws_sel)), args.steps)
+    t_decode = time_loop(lambda i: ops.sa_sparse_decode(shape, pages, inp.q, reps[i][1],
+                                                        reps[i][2], idx, count, inp.s_att,
+                                                        out, lse, ws_dec), args.steps, reps=R)
+    comp = {"index_scores" if not page_mode else "page_scores": (t_index, index_bytes),
+            "select": (t_select, 0), "sparse_decode": (t_decode, kv_bytes)}
+    dom = max((k for k in comp if comp[k][1] > 0), key=lambda k: comp[k][0])
+    dom_ms, dom_bytes = comp[dom]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "context": (Lmax if B == 1 else
+                                                              [min(inp.seq_lens), Lmax]),
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "selection": ("top-%d pages (Taylor page score)" % sel["k_pages"]
+                                 if page_mode else
+                                 f"top-p {sel['p']} + sink {n_sink} + window {n_window}"),
+                   "input_replicas": R},
+        "step_bytes": step_bytes,
+        "index_bytes": index_bytes,
+        "kv_bytes": kv_bytes,
+        "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
+        "breakdown_ms": {k: round(v[0], 5) for k, v in comp.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_decode(inp, cache_a if not page_mode else None,
+                                                  step_bytes, args.cpu_seconds, page_mode,
+                                                  stats if page_mode else None)
+    return res
+
+
+def cpu_baseline_decode(inp, kidx, step_bytes, seconds, page_mode, stats):
+    """The float64 oracle on the host cores, on a bounded sample of the same
+    step: whole (b, g) rows, repeated until ~seconds of CPU work."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    rows = [(b, g) for b in range(inp.B) for g in range(inp.H_kv)]
+    data = []
+    for b, g in rows[: min(len(rows), 8)]:
+        hs = inp.heads(g)
+        q = inp.q[b, hs].double().cpu().numpy()
+        K = inp.seq_keys(b, g).double().cpu().numpy()
+        V = inp.seq_values(b, g).double().cpu().numpy()
+        if page_mode:
+            L = inp.seq_lens[b]
+            npg = (L + 63) // 64
+            st = stats[inp.page_table[b, :npg].long(), g].reshape(npg, -1)
+            st = st.double().cpu().numpy()
+            n = np.array([min(64, L - 64 * p) for p in range(st.shape[0])])
+            data.append((q, st[:, :inp.d], st[:, inp.d:], n, K, V))
+        else:
+            kt = inp.seq_rows(kidx, b, g).double().cpu().numpy()
+            data.append((q, inp.w_q[hs].double().cpu().numpy(), kt, K, V, inp.seq_lens[b]))
+    sel = inp.select
+    done_bytes = 0.0
+    t0 = time.perf_counter()
+    n_rows = 0
+    with threadpool_limits(limits=1):
+        while True:
+            for item in data:
+                if page_mode:
+                    q, mu, var, n, K, V = item
+                    r = O.decode_row_pages(q, mu, var, n, K, V, s_att=inp.s_att,
+                                           k_pages=sel["k_pages"])
+                    done_bytes += mu.shape[0] * 2 * inp.d * 2 + len(r["S"]) * 2 * inp.d * 2
+                else:
+                    q, wq, kt, K, V, L = item
+                    r = O.decode_row(q, wq, kt, K, V, s_idx=inp.s_idx, s_att=inp.s_att,
+                                     p=float(np.float32(sel["p"])), n_sink=sel["n_sink"],
+                                     n_window=sel["n_window"])
+                    done_bytes += L * 16 * 2 + len(r["S"]) * 2 * inp.d * 2
+                n_rows += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": round(done_bytes / el / 1e9, 5), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"{n_rows} (sequence, group) rows of the same step, float64 numpy, "
+                      f"{el:.1f} s", "host_threads_available": cpu_threads_info()}
+
+
+def bench_prefill(args):
+    raise SystemExit("prefill128k: not built yet")
+
+
+# ---------------------------------------------------------------------------
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    import dynamic_sparse_attention_02_amd as pkg
+    pkg.load_library()
+    if args.workload == "prefill128k":
+        res = bench_prefill(args)
+    else:
+        res = bench_decode(args, args.workload)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,849 @@
+// Sort-free support selection by a radix histogram over order-preserving keys
+// of the fp32 scores ("Full Attention Strikes Back", method section 5: a
+// histogram threshold instead of a sort; section 3: dynamic top-p by attention
+// mass, or static top-k).
+//
+// Rows (one per (sequence, key/value group)) are split into chunks of kChunk
+// candidates, one block per chunk.  A key is the score's bit pattern mapped so
+// that unsigned order equals float order; it is resolved 12 + 12 + 8 bits at a
+// time.  Each level builds a per-block LDS histogram of the current digit
+// (count, and for top-p the mass exp(x - max) in 2^-40 fixed point, so sums are
+// exact integers whatever the order of the atomics), flushes its non-empty
+// bins to a global per-row histogram, and the last block of the row to arrive
+// finds the digit where the running count (top-k) or mass (top-p) crosses the
+// target.  Ties on the final key are taken lowest index first.  Compaction
+// then writes the ascending index list, unioned with the always-kept sink and
+// window tokens (method section 1), or expands selected pages to tokens.
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunk = 8192;                  // candidates per block
+constexpr int kPer = kChunk / kThreads;       // candidates per thread
+constexpr int kBins = 4096;                   // 12-bit digits
+constexpr int kCoarse = kBins / 64;           // 64-bin groups (two-step resolve)
+constexpr double kFix = 1099511627776.0;      // 2^40 fixed-point unit of mass
+
+enum : uint32_t { kSearching = 0, kTakeGE = 1, kTakeTies = 2 };
+
+struct RowState {
+  uint32_t mode;     // kSearching / kTakeGE (key >= thr) / kTakeTies
+  uint32_t prefix;   // resolved high bits of the threshold key
+  uint32_t thr;      // threshold key
+  uint32_t n_eq;     // kTakeTies: keys == thr to take (lowest index first)
+  uint32_t need;     // top-k: candidates still needed inside the prefix bin
+  uint32_t maxkey;   // top-p: key of the row maximum
+  uint32_t arrive;   // arrival counter of the current level (reset by resolver)
+  uint32_t n_cand;
+  uint64_t rem;      // top-p: mass still needed inside the prefix bin
+  uint64_t total;    // top-p: total mass of the row
+};
+static_assert(sizeof(RowState) == 48, "layout");
+
+struct WsLayout {
+  RowState* state;
+  uint32_t* chunkmax;  // [rows][nchunk]
+  uint32_t* cnt_eq;    // [rows][nchunk]
+  uint32_t* cnt_out;   // [rows][nchunk]
+  uint32_t* hcnt;      // [2][rows][kBins]
+  uint64_t* hmass;     // [2][rows][kBins]
+  uint32_t* ccnt;      // [2][rows][kCoarse] sums of 64 consecutive bins
+  uint64_t* cmass;     // [2][rows][kCoarse]
+};
+
+__host__ __device__ inline int nchunk_of(int32_t max_cand) {
+  return (max_cand + kChunk - 1) / kChunk;
+}
+
+WsLayout carve(void* ws, int32_t rows, int32_t max_cand) {
+  const int nch = nchunk_of(max_cand);
+  char* p = (char*)ws;
+  WsLayout w;
+  w.state = (RowState*)p;            p += align_up(sizeof(RowState) * rows, 256);
+  w.chunkmax = (uint32_t*)p;         p += align_up(sizeof(uint32_t) * rows * nch, 256);
+  w.cnt_eq = (uint32_t*)p;           p += align_up(sizeof(uint32_t) * rows * nch, 256);
+  w.cnt_out = (uint32_t*)p;          p += align_up(sizeof(uint32_t) * rows * nch, 256);
+  w.hcnt = (uint32_t*)p;             p += align_up(sizeof(uint32_t) * 2 * rows * kBins, 256);
+  w.hmass = (uint64_t*)p;            p += align_up(sizeof(uint64_t) * 2 * rows * kBins, 256);
+  w.ccnt = (uint32_t*)p;             p += align_up(sizeof(uint32_t) * 2 * rows * kCoarse, 256);
+  w.cmass = (uint64_t*)p;
+  return w;
+}
+
+__device__ __forceinline__ int32_t n_cand_of(const SelectArgs& a, int row) {
+  const int b = row / a.Hkv;
+  const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
+  return a.unit == 1 ? L : (L + a.unit - 1) / a.unit;
+}
+
+// Exclusive block scan (kThreads threads) of an unsigned value.
+template <typename U>
+__device__ __forceinline__ U block_excl_scan(U v, U* lds4, U& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  U inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    U y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) lds4[w] = inc;
+  __syncthreads();
+  U off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    U s = lds4[i];
+    if (i < w) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - v;
+}
+
+__device__ __forceinline__ uint64_t mass_fixed(float x, float mx) {
+  const float e = __expf(x - mx);  // in (0, 1]
+  return (uint64_t)(e * 1099511627776.0f);
+}
+
+// ---------------------------------------------------------------------------
+// Init: per-chunk maximum key, zero level-1 histogram, row state.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_sel_init(SelectArgs a, WsLayout w, int nch) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int32_t n = n_cand_of(a, row);
+  const float* xr = a.x + (int64_t)row * a.ldx;
+  uint32_t mk = 0;
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t j = c * kChunk + i * kThreads + threadIdx.x;
+    if (j < n) {
+      uint32_t k = score_key(xr[j]);
+      mk = k > mk ? k : mk;
+    }
+  }
+  mk = wave_max_u32(mk);
+  __shared__ uint32_t red[kWaves];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mk;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t m = 0;
+    for (int i = 0; i < kWaves; ++i) m = red[i] > m ? red[i] : m;
+    w.chunkmax[(int64_t)row * nch + c] = m;
+  }
+  // zero histogram buffer 0 of the row (bins spread over the row's chunks)
+  uint32_t* hc = w.hcnt + (int64_t)row * kBins;
+  uint64_t* hm = w.hmass + (int64_t)row * kBins;
+  for (int i = c * kThreads + threadIdx.x; i < kBins; i += nch * kThreads) {
+    hc[i] = 0;
+    hm[i] = 0;
+  }
+  if (c == 0 && threadIdx.x < kCoarse) {
+    w.ccnt[(int64_t)row * kCoarse + threadIdx.x] = 0;
+    w.cmass[(int64_t)row * kCoarse + threadIdx.x] = 0;
+  }
+  if (c == 0 && threadIdx.x == 0) {
+    RowState s;
+    s.mode = kSearching;
+    s.prefix = 0;
+    s.thr = 0;
+    s.n_eq = 0;
+    s.need = (uint32_t)a.k;
+    s.maxkey = 0;
+    s.arrive = 0;
+    s.n_cand = (uint32_t)n;
+    s.rem = 0;
+    s.total = 0;
+    const bool all = (n == 0) || (a.is_topk ? (a.k >= n) : (a.p >= 1.0f));
+    if (all) {
+      s.mode = kTakeGE;  // every key >= 0
+      s.thr = 0;
+    }
+    w.state[row] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One radix level.  LEVEL 1: digit = key[31:20]; 2: key[19:8] under a 12-bit
+// prefix; 3: key[7:0] under a 24-bit prefix.  Global histograms keep, beside
+// the NB digit bins, NB/64 coarse sums of 64 consecutive bins, so the
+// resolving block finds the crossing in two dependent reads of one wave.
+// ---------------------------------------------------------------------------
+template <int LEVEL, bool TOPP>
+__global__ void __launch_bounds__(kThreads) k_sel_level(SelectArgs a, WsLayout w, int nch) {
+  constexpr int NB = LEVEL == 3 ? 256 : kBins;
+  constexpr int NC = NB / 64;
+  const int c = blockIdx.x, row = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  RowState* sp = &w.state[row];
+  const uint32_t mode = __hip_atomic_load(&sp->mode, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (mode != kSearching) return;
+  const RowState st = *sp;
+  const int32_t n = (int32_t)st.n_cand;
+
+  __shared__ uint32_t hcnt[NB];
+  __shared__ uint64_t hmass[TOPP ? NB : 1];
+  __shared__ uint32_t s_max;
+  __shared__ int s_last;
+  for (int i = threadIdx.x; i < NB; i += kThreads) {
+    hcnt[i] = 0;
+    if (TOPP) hmass[i] = 0;
+  }
+  if (TOPP && threadIdx.x == 0) {
+    uint32_t m = st.maxkey;
+    if (LEVEL == 1) {
+      m = 0;
+      for (int i = 0; i < nch; ++i) {
+        uint32_t v = w.chunkmax[(int64_t)row * nch + i];
+        m = v > m ? v : m;
+      }
+    }
+    s_max = m;
+  }
+  __syncthreads();
+  const float mx = TOPP ? key_score(s_max) : 0.f;
+  const float* xr = a.x + (int64_t)row * a.ldx;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t j = c * kChunk + i * kThreads + threadIdx.x;
+    if (j >= n) continue;
+    const float xv = xr[j];
+    const uint32_t key = score_key(xv);
+    uint32_t digit;
+    if (LEVEL == 1) {
+      digit = key >> 20;
+    } else if (LEVEL == 2) {
+      if ((key >> 20) != st.prefix) continue;
+      digit = (key >> 8) & 0xfffu;
+    } else {
+      if ((key >> 8) != st.prefix) continue;
+      digit = key & 0xffu;
+    }
+    atomicAdd(&hcnt[digit], 1u);
+    if (TOPP) atomicAdd((unsigned long long*)&hmass[digit], (unsigned long long)mass_fixed(xv, mx));
+  }
+  __syncthreads();
+  const int buf = (LEVEL == 2) ? 1 : 0;
+  uint32_t* gc = w.hcnt + ((int64_t)buf * a.rows + row) * kBins;
+  uint64_t* gm = w.hmass + ((int64_t)buf * a.rows + row) * kBins;
+  uint32_t* gcc = w.ccnt + ((int64_t)buf * a.rows + row) * kCoarse;
+  uint64_t* gcm = w.cmass + ((int64_t)buf * a.rows + row) * kCoarse;
+  // flush: one wave per coarse group of 64 bins
+  for (int cg = threadIdx.x >> 6; cg < NC; cg += kWaves) {
+    const int bin = cg * 64 + lane;
+    const uint32_t cn = hcnt[bin];
+    const uint64_t ms = TOPP ? hmass[bin] : 0;
+    if (cn) {
+      atomicAdd(&gc[bin], cn);
+      if (TOPP) atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
+    }
+    uint32_t csum = cn;
+    uint64_t msum = ms;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      csum += __shfl_xor(csum, o, 64);
+      if (TOPP) msum += __shfl_xor(msum, o, 64);
+    }
+    if (lane == 0 && csum) {
+      atomicAdd(&gcc[cg], csum);
+      if (TOPP) atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
+    }
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = atomicAdd(&sp->arrive, 1u);
+    s_last = (old == (uint32_t)gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // ---- resolve (last block of the row, wave 0) ----
+  __shared__ uint32_t r_bin, r_cnt, r_cbefore;
+  __shared__ uint64_t r_mass, r_mbefore, r_target, r_total;
+  if (threadIdx.x < 64) {
+    // step 1: coarse groups in descending order, lane i <-> group NC-1-i
+    const int cgi = NC - 1 - lane;
+    const uint32_t cc = lane < NC ? __hip_atomic_load(&gcc[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    const uint64_t cm = (TOPP && lane < NC) ? __hip_atomic_load(&gcm[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    uint32_t cinc = cc;
+    uint64_t minc = cm;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(cinc, o, 64);
+      const uint64_t z = __shfl_up(minc, o, 64);
+      if (lane >= o) {
+        cinc += y;
+        minc += z;
+      }
+    }
+    const uint64_t mtot = __shfl(minc, 63, 64);
+    uint64_t target = st.rem;
+    if (TOPP && LEVEL == 1) {
+      const double t = (double)a.p * (double)mtot;
+      uint64_t tc = (uint64_t)ceil(t);
+      if (tc < 1) tc = 1;
+      if (tc > mtot) tc = mtot;
+      target = tc;
+    }
+    const uint32_t need = st.need;
+    const uint32_t cbef = cinc - cc;
+    const uint64_t mbef = minc - cm;
+    const bool hit = lane < NC && (TOPP ? (mbef < target && minc >= target)
+                                        : (cbef < need && cinc >= need));
+    const unsigned long long hb = __ballot(hit);
+    int found = -1;
+    uint32_t g_cbef = 0;
+    uint64_t g_mbef = 0;
+    if (hb) {
+      const int src = __ffsll(hb) - 1;
+      found = __shfl(cgi, src, 64);
+      g_cbef = __shfl(cbef, src, 64);
+      g_mbef = __shfl(mbef, src, 64);
+    }
+    // step 2: the 64 bins of the crossing group, descending
+    uint32_t bc = 0;
+    uint64_t bm = 0;
+    int bin = -1;
+    if (found >= 0) {
+      bin = found * 64 + 63 - lane;
+      bc = __hip_atomic_load(&gc[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      bm = TOPP ? __hip_atomic_load(&gm[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+    }
+    uint32_t binc = bc;
+    uint64_t bminc = bm;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(binc, o, 64);
+      const uint64_t z = __shfl_up(bminc, o, 64);
+      if (lane >= o) {
+        binc += y;
+        bminc += z;
+      }
+    }
+    const uint32_t bcb = g_cbef + binc - bc;
+    const uint64_t bmb = g_mbef + bminc - bm;
+    const bool hit2 = found >= 0 && (TOPP ? (bmb < target && bmb + bm >= target)
+                                          : (bcb < need && bcb + bc >= need));
+    const unsigned long long hb2 = __ballot(hit2);
+    if (lane == 0) {
+      r_bin = 0xffffffffu;
+      r_target = target;
+      r_total = mtot;
+    }
+    if (hb2 && lane == __ffsll(hb2) - 1) {
+      r_bin = (uint32_t)bin;
+      r_cnt = bc;
+      r_cbefore = bcb;
+      r_mass = bm;
+      r_mbefore = bmb;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    RowState s = st;
+    s.arrive = 0;
+    const uint64_t target = r_target;
+    if (TOPP && LEVEL == 1) {
+      s.maxkey = s_max;
+      s.total = r_total;
+    }
+    const uint32_t bin = r_bin;
+    if (bin == 0xffffffffu) {
+      // cannot happen for consistent inputs; fall back to taking everything
+      s.mode = kTakeGE;
+      s.thr = 0;
+    } else {
+      const uint32_t cnt_b = r_cnt;
+      const uint32_t new_prefix =
+          LEVEL == 1 ? bin : (LEVEL == 2 ? ((st.prefix << 12) | bin) : ((st.prefix << 8) | bin));
+      const int shift = LEVEL == 1 ? 20 : (LEVEL == 2 ? 8 : 0);
+      const uint32_t bin_lo = new_prefix << shift;
+      if (TOPP) {
+        const uint64_t rem = target - r_mbefore;  // 0 < rem <= mass of bin
+        if (LEVEL < 3) {
+          if (cnt_b == 1 || rem == r_mass) {
+            s.mode = kTakeGE;
+            s.thr = bin_lo;
+          } else {
+            s.prefix = new_prefix;
+            s.rem = rem;
+          }
+        } else {
+          const uint64_t m1 = r_mass / cnt_b;  // every tie has the same mass
+          const uint64_t take = (rem + m1 - 1) / m1;
+          if (take >= cnt_b) {
+            s.mode = kTakeGE;
+            s.thr = bin_lo;
+          } else {
+            s.mode = kTakeTies;
+            s.thr = bin_lo;
+            s.n_eq = (uint32_t)take;
+          }
+        }
+      } else {
+        const uint32_t nd = st.need - r_cbefore;  // 0 < nd <= cnt_b
+        if (nd == cnt_b) {
+          s.mode = kTakeGE;
+          s.thr = bin_lo;
+        } else if (LEVEL < 3) {
+          s.prefix = new_prefix;
+          s.need = nd;
+        } else {
+          s.mode = kTakeTies;
+          s.thr = bin_lo;
+          s.n_eq = nd;
+        }
+      }
+    }
+    *sp = s;
+  }
+  // zero the other histogram buffer for the next level
+  if (LEVEL < 3) {
+    const int nb = 1 - buf;
+    uint32_t* zc = w.hcnt + ((int64_t)nb * a.rows + row) * kBins;
+    uint64_t* zm = w.hmass + ((int64_t)nb * a.rows + row) * kBins;
+    const int nz = LEVEL == 1 ? kBins : 256;
+    for (int i = threadIdx.x; i < nz; i += kThreads) {
+      zc[i] = 0;
+      zm[i] = 0;
+    }
+    if (threadIdx.x < kCoarse) {
+      w.ccnt[((int64_t)nb * a.rows + row) * kCoarse + threadIdx.x] = 0;
+      w.cmass[((int64_t)nb * a.rows + row) * kCoarse + threadIdx.x] = 0;
+    }
+  }
+  __threadfence();
+}
+
+// ---------------------------------------------------------------------------
+// Compaction.  Per chunk: ties count (only when some ties are left out), then
+// emitted-token count, then the writes.  Candidates are visited in index order
+// in rounds of kThreads, so tie ranks and output positions follow the index.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kThreads) k_sel_ties(SelectArgs a, WsLayout w, int nch) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const RowState st = w.state[row];
+  if (st.mode != kTakeTies) return;
+  const int32_t n = (int32_t)st.n_cand;
+  const float* xr = a.x + (int64_t)row * a.ldx;
+  uint32_t cnt = 0;
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t j = c * kChunk + i * kThreads + threadIdx.x;
+    if (j < n && score_key(xr[j]) == st.thr) ++cnt;
+  }
+  __shared__ uint32_t l4[kWaves];
+  uint32_t tot;
+  block_excl_scan<uint32_t>(cnt, l4, tot);
+  if (threadIdx.x == 0) w.cnt_eq[(int64_t)row * nch + c] = tot;
+}
+
+template <bool EMIT>
+__global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, int nch) {
+  const int c = blockIdx.x, row = blockIdx.y;
+  const RowState st = w.state[row];
+  const int32_t n = (int32_t)st.n_cand;
+  const int b = row / a.Hkv;
+  const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
+  const float* xr = a.x + (int64_t)row * a.ldx;
+  __shared__ uint32_t l4[kWaves];
+  uint32_t eq_base = 0;
+  if (st.mode == kTakeTies)
+    for (int i = 0; i < c; ++i) eq_base += w.cnt_eq[(int64_t)row * nch + i];
+  uint32_t out_base = 0, total_out = 0;
+  if (EMIT) {
+    for (int i = 0; i < nch; ++i) {
+      const uint32_t v = w.cnt_out[(int64_t)row * nch + i];
+      if (i < c) out_base += v;
+      total_out += v;
+    }
+  }
+  int32_t* out = a.idx + (int64_t)row * a.cap;
+  uint32_t produced = 0;
+  for (int i = 0; i < kPer; ++i) {
+    const int32_t j = c * kChunk + i * kThreads + threadIdx.x;
+    const bool valid = j < n;
+    uint32_t key = valid ? score_key(xr[j]) : 0u;
+    bool top = false;
+    if (valid) {
+      if (st.mode == kTakeGE) top = key >= st.thr;
+      else top = key > st.thr;
+    }
+    if (st.mode == kTakeTies) {  // uniform branch
+      const bool eq = valid && key == st.thr;
+      uint32_t tot;
+      const uint32_t rank = eq_base + block_excl_scan<uint32_t>(eq ? 1u : 0u, l4, tot);
+      if (eq && rank < st.n_eq) top = true;
+      eq_base += tot;
+    }
+    bool forced = false;
+    if (valid && a.unit == 1) forced = (j < a.n_sink) || (j >= n - a.n_window);
+    const bool sel = valid && (top || forced);
+    uint32_t wgt = 0;
+    if (sel) wgt = a.unit == 1 ? 1u : (uint32_t)min(a.unit, L - j * a.unit);
+    uint32_t tot;
+    const uint32_t pos = block_excl_scan<uint32_t>(wgt, l4, tot);
+    if (EMIT && sel) {
+      const uint32_t o = out_base + produced + pos;
+      if (a.unit == 1) {
+        if (o < (uint32_t)a.cap) out[o] = j;
+      } else {
+        for (uint32_t e = 0; e < wgt; ++e)
+          if (o + e < (uint32_t)a.cap) out[o + e] = j * a.unit + (int32_t)e;
+      }
+    }
+    produced += tot;
+  }
+  if (!EMIT) {
+    if (threadIdx.x == 0) w.cnt_out[(int64_t)row * nch + c] = produced;
+    return;
+  }
+  // pad the tail with -1 and publish the count
+  const uint32_t T = total_out < (uint32_t)a.cap ? total_out : (uint32_t)a.cap;
+  for (int64_t o = (int64_t)T + (int64_t)c * kThreads + threadIdx.x; o < a.cap;
+       o += (int64_t)nch * kThreads)
+    out[o] = -1;
+  if (c == 0 && threadIdx.x == 0) a.count[row] = (int32_t)T;
+}
+
+// ---------------------------------------------------------------------------
+// Row-resident selection: one block per row for rows of up to kRowMax
+// candidates.  Keys of the first kRowRegs * kThreads candidates stay in
+// registers (the rest are re-read from the score row), the three radix levels
+// use one LDS histogram with block barriers only, and the ordered compaction
+// counts selected candidates per (64-candidate wave slice) with ballots, then
+// one block scan over the slices gives every output position.
+// ---------------------------------------------------------------------------
+constexpr int kRowRegs = 64;
+constexpr int kRowMax = 131072;
+constexpr int kRowRounds = kRowMax / kThreads;        // 128 slices per wave
+constexpr int kRowSlices = kRowRounds * kWaves;       // 2048 (round, wave) slices
+
+struct RowRes {
+  uint32_t mode, prefix, thr, n_eq, need;
+  uint64_t rem;
+};
+
+template <bool TOPP>
+__global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t n = n_cand_of(a, row);
+  const int b = row / a.Hkv;
+  const int32_t Lt = clamp_len(a.seq_lens[b], a.max_len);
+  const float* xr = a.x + (int64_t)row * a.ldx;
+  const int rounds = (n + kThreads - 1) / kThreads;
+
+  __shared__ uint32_t hcnt[kBins];
+  __shared__ uint64_t hmass[TOPP ? kBins : 1];
+  __shared__ uint32_t slice[kRowSlices];
+  __shared__ uint32_t red32[kWaves];
+  __shared__ uint64_t red64[kWaves];
+  __shared__ RowRes res;
+  __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef;
+  __shared__ uint64_t s_hit_mass, s_hit_mbef;
+
+  uint32_t keys[kRowRegs];
+  uint32_t mk = 0;
+#pragma unroll
+  for (int i = 0; i < kRowRegs; ++i) {
+    const int32_t e = i * kThreads + t;
+    keys[i] = e < n ? score_key(xr[e]) : 0u;
+    mk = keys[i] > mk ? keys[i] : mk;
+  }
+  for (int i = kRowRegs; i < rounds; ++i) {
+    const int32_t e = i * kThreads + t;
+    if (e < n) {
+      const uint32_t k = score_key(xr[e]);
+      mk = k > mk ? k : mk;
+    }
+  }
+  mk = wave_max_u32(mk);
+  if (lane == 0) red32[wave] = mk;
+  if (t == 0) {
+    res.mode = kSearching;
+    res.prefix = 0;
+    res.thr = 0;
+    res.n_eq = 0;
+    res.need = (uint32_t)a.k;
+    res.rem = 0;
+    if (n == 0 || (a.is_topk ? (a.k >= n) : (a.p >= 1.0f))) res.mode = kTakeGE;
+  }
+  __syncthreads();
+  uint32_t M = 0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) M = red32[i] > M ? red32[i] : M;
+  const float mx = key_score(M);
+
+  // ---- radix levels ----
+  for (int level = 1; level <= 3; ++level) {
+    if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
+    const int NB = level == 3 ? 256 : kBins;
+    const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+    const uint32_t pre = res.prefix;
+    for (int i = t; i < NB; i += kThreads) {
+      hcnt[i] = 0;
+      if (TOPP) hmass[i] = 0;
+    }
+    __syncthreads();
+    auto add = [&](uint32_t key) {
+      bool match;
+      uint32_t digit;
+      if (level == 1) {
+        match = true;
+        digit = key >> 20;
+      } else if (level == 2) {
+        match = (key >> 20) == pre;
+        digit = (key >> 8) & 0xfffu;
+      } else {
+        match = (key >> 8) == pre;
+        digit = key & 0xffu;
+      }
+      if (match) {
+        atomicAdd(&hcnt[digit], 1u);
+        if (TOPP)
+          atomicAdd((unsigned long long*)&hmass[digit],
+                    (unsigned long long)mass_fixed(key_score(key), mx));
+      }
+    };
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i)
+      if (i * kThreads + t < n) add(keys[i]);
+    for (int i = kRowRegs; i < rounds; ++i) {
+      const int32_t e = i * kThreads + t;
+      if (e < n) add(score_key(xr[e]));
+    }
+    __syncthreads();
+    // block scan over bins in descending order: thread t owns positions
+    // [t*per, (t+1)*per), position q <-> bin NB-1-q
+    const int per = NB / kThreads > 0 ? NB / kThreads : 1;
+    const bool owns = t * per < NB;
+    uint32_t cl = 0;
+    uint64_t ml = 0;
+    if (owns)
+      for (int e = 0; e < per; ++e) {
+        const int bin = NB - 1 - (t * per + e);
+        cl += hcnt[bin];
+        if (TOPP) ml += hmass[bin];
+      }
+    uint32_t ctot;
+    uint64_t mtot = 0;
+    const uint32_t cb0 = block_excl_scan<uint32_t>(cl, red32, ctot);
+    const uint64_t mb0 = TOPP ? block_excl_scan<uint64_t>(ml, red64, mtot) : 0ull;
+    uint64_t target = res.rem;
+    if (TOPP && level == 1) {
+      uint64_t tc = (uint64_t)ceil((double)a.p * (double)mtot);
+      if (tc < 1) tc = 1;
+      if (tc > mtot) tc = mtot;
+      target = tc;
+    }
+    const uint32_t need = res.need;
+    if (t == 0) s_hit_bin = 0xffffffffu;
+    __syncthreads();
+    if (owns) {
+      uint32_t cb = cb0;
+      uint64_t mb = mb0;
+      for (int e = 0; e < per; ++e) {
+        const int bin = NB - 1 - (t * per + e);
+        const uint32_t c = hcnt[bin];
+        const uint64_t m = TOPP ? hmass[bin] : 0ull;
+        const bool hit = TOPP ? (mb < target && mb + m >= target) : (cb < need && cb + c >= need);
+        if (hit) {
+          s_hit_bin = bin;
+          s_hit_cnt = c;
+          s_hit_cbef = cb;
+          s_hit_mass = m;
+          s_hit_mbef = mb;
+        }
+        cb += c;
+        mb += m;
+      }
+    }
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t bin = s_hit_bin;
+      if (bin == 0xffffffffu) {
+        res.mode = kTakeGE;  // inconsistent input: take everything
+        res.thr = 0;
+      } else {
+        const uint32_t cnt_b = s_hit_cnt;
+        const uint32_t np = level == 1 ? bin : (level == 2 ? ((pre << 12) | bin) : ((pre << 8) | bin));
+        const uint32_t bin_lo = np << shift;
+        if (TOPP) {
+          const uint64_t rem = target - s_hit_mbef;
+          if (level < 3) {
+            if (cnt_b == 1 || rem == s_hit_mass) {
+              res.mode = kTakeGE;
+              res.thr = bin_lo;
+            } else {
+              res.prefix = np;
+              res.rem = rem;
+            }
+          } else {
+            const uint64_t m1 = s_hit_mass / cnt_b;
+            const uint64_t take = (rem + m1 - 1) / m1;
+            res.thr = bin_lo;
+            if (take >= cnt_b) {
+              res.mode = kTakeGE;
+            } else {
+              res.mode = kTakeTies;
+              res.n_eq = (uint32_t)take;
+            }
+          }
+        } else {
+          const uint32_t nd = need - s_hit_cbef;
+          if (nd == cnt_b) {
+            res.mode = kTakeGE;
+            res.thr = bin_lo;
+          } else if (level < 3) {
+            res.prefix = np;
+            res.need = nd;
+          } else {
+            res.mode = kTakeTies;
+            res.thr = bin_lo;
+            res.n_eq = nd;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- ordered compaction ----
+  const uint32_t mode = res.mode, thr = res.thr, n_eq = res.n_eq;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const int n_slices = rounds * kWaves;
+  // tie ranks reuse the count histogram's LDS (no longer needed)
+  uint32_t* eqoff = hcnt;
+  auto key_at = [&](int i) -> uint32_t {  // rounds beyond the register-resident ones
+    const int32_t e = i * kThreads + t;
+    return e < n ? score_key(xr[e]) : 0u;
+  };
+  auto scan_slices = [&](uint32_t* arr) -> uint32_t {  // in place, exclusive
+    const uint32_t v0 = (2 * t < n_slices) ? arr[2 * t] : 0u;
+    const uint32_t v1 = (2 * t + 1 < n_slices) ? arr[2 * t + 1] : 0u;
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<uint32_t>(v0 + v1, red32, tot);
+    if (2 * t < n_slices) arr[2 * t] = ex;
+    if (2 * t + 1 < n_slices) arr[2 * t + 1] = ex + v0;
+    __syncthreads();
+    return tot;
+  };
+  if (mode == kTakeTies) {  // only when some keys equal to the threshold are left out
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i) {
+      if (i < rounds) {
+        const uint64_t m = __ballot((i * kThreads + t < n) && keys[i] == thr);
+        if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
+      }
+    }
+    for (int i = kRowRegs; i < rounds; ++i) {
+      const uint64_t m = __ballot((i * kThreads + t < n) && key_at(i) == thr);
+      if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    scan_slices(eqoff);
+  }
+  // output weight of candidate (round i, this thread): 0 if not selected,
+  // else 1 token or the page's token count.  Every lane calls it (ballot).
+  auto weight = [&](int i, uint32_t key) -> uint32_t {
+    const int32_t e = i * kThreads + t;
+    const bool valid = e < n;
+    bool top;
+    if (mode == kTakeTies) {
+      const bool eq = valid && key == thr;
+      const uint64_t m = __ballot(eq);
+      top = valid && key > thr;
+      if (eq) top = (eqoff[i * kWaves + wave] + (uint32_t)__popcll(m & lt_mask)) < n_eq;
+    } else {
+      top = valid && key >= thr;
+    }
+    const bool forced = valid && a.unit == 1 && (e < a.n_sink || e >= n - a.n_window);
+    if (!(top || forced)) return 0u;
+    if (a.unit == 1) return 1u;
+    const int32_t r = Lt - e * a.unit;
+    return (uint32_t)(r < a.unit ? r : a.unit);
+  };
+  // pass 1: output count of every (round, wave) slice
+#pragma unroll
+  for (int i = 0; i < kRowRegs; ++i) {
+    if (i < rounds) {
+      const uint32_t sum = wave_sum_u32(weight(i, keys[i]));
+      if (lane == 0) slice[i * kWaves + wave] = sum;
+    }
+  }
+  for (int i = kRowRegs; i < rounds; ++i) {
+    const uint32_t sum = wave_sum_u32(weight(i, key_at(i)));
+    if (lane == 0) slice[i * kWaves + wave] = sum;
+  }
+  __syncthreads();
+  const uint32_t total = scan_slices(slice);
+  // pass 2: write every selected candidate at its slice offset
+  int32_t* out = a.idx + (int64_t)row * a.cap;
+  auto emit = [&](int i, uint32_t wgt) {
+    const uint32_t pos = slice[i * kWaves + wave] + wave_excl_scan_u32(wgt);
+    if (wgt) {
+      const int32_t e = i * kThreads + t;
+      if (a.unit == 1) {
+        if (pos < (uint32_t)a.cap) out[pos] = e;
+      } else {
+        for (uint32_t q = 0; q < wgt; ++q)
+          if (pos + q < (uint32_t)a.cap) out[pos + q] = e * a.unit + (int32_t)q;
+      }
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < kRowRegs; ++i)
+    if (i < rounds) emit(i, weight(i, keys[i]));
+  for (int i = kRowRegs; i < rounds; ++i) emit(i, weight(i, key_at(i)));
+  const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
+  for (int64_t o = (int64_t)T + t; o < a.cap; o += kThreads) out[o] = -1;
+  if (t == 0) a.count[row] = (int32_t)T;
+}
+
+}  // namespace
+
+size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
+  const size_t nch = (size_t)nchunk_of(max_cand < 1 ? 1 : max_cand);
+  size_t b = 0;
+  b += align_up(sizeof(RowState) * rows, 256);
+  b += 3 * align_up(sizeof(uint32_t) * rows * nch, 256);
+  b += align_up(sizeof(uint32_t) * 2 * rows * kBins, 256);
+  b += align_up(sizeof(uint64_t) * 2 * rows * kBins, 256);
+  b += align_up(sizeof(uint32_t) * 2 * rows * kCoarse, 256);
+  b += align_up(sizeof(uint64_t) * 2 * rows * kCoarse, 256);
+  return b;
+}
+
+hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
+  if (a.rows == 0) return hipSuccess;
+  // One block per row when there are enough rows to fill the chip; few long
+  // rows are split over many blocks instead.
+  if (a.max_cand <= kRowMax && a.rows >= 32) {
+    if (a.is_topk) k_select_row<false><<<a.rows, kThreads, 0, st>>>(a);
+    else k_select_row<true><<<a.rows, kThreads, 0, st>>>(a);
+    return hipGetLastError();
+  }
+  const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
+  WsLayout w = carve(ws, a.rows, a.max_cand < 1 ? 1 : a.max_cand);
+  dim3 grid(nch, a.rows);
+  k_sel_init<<<grid, kThreads, 0, st>>>(a, w, nch);
+  if (a.is_topk) {
+    k_sel_level<1, false><<<grid, kThreads, 0, st>>>(a, w, nch);
+    k_sel_level<2, false><<<grid, kThreads, 0, st>>>(a, w, nch);
+    k_sel_level<3, false><<<grid, kThreads, 0, st>>>(a, w, nch);
+  } else {
+    k_sel_level<1, true><<<grid, kThreads, 0, st>>>(a, w, nch);
+    k_sel_level<2, true><<<grid, kThreads, 0, st>>>(a, w, nch);
+    k_sel_level<3, true><<<grid, kThreads, 0, st>>>(a, w, nch);
+  }
+  k_sel_ties<<<grid, kThreads, 0, st>>>(a, w, nch);
+  k_sel_out<false><<<grid, kThreads, 0, st>>>(a, w, nch);
+  k_sel_out<true><<<grid, kThreads, 0, st>>>(a, w, nch);
+  return hipGetLastError();
+}
+
+}  // namespace sa

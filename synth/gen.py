@@ -141,7 +141,7 @@ class DecodeInputs:
         npg = (L + PAGE - 1) // PAGE
         pages = self.page_table[b, :npg].long()
         rows = pool[pages, g]  # [npg, page, width]
-        return rows.reshape(npg * PAGE, -1)[:L]
+        return rows.reshape(npg * PAGE, pool.shape[-1])[:L]
 
     def seq_keys(self, b, g) -> torch.Tensor:
         """Keys of sequence b, group g in token order: [L_b, d]."""
@@ -156,6 +156,13 @@ class DecodeInputs:
 
     def heads(self, g) -> list:
         return list(range(g * self.G, (g + 1) * self.G))
+
+    def to(self, device) -> "DecodeInputs":
+        """Copy with every tensor moved to device (bits unchanged)."""
+        kw = {f: getattr(self, f) for f in self.__dataclass_fields__}
+        for f in ("page_table", "q", "w_q", "w_k", "k_pool", "v_pool"):
+            kw[f] = kw[f].to(device)
+        return DecodeInputs(**kw)
 
 
 @dataclass
@@ -205,7 +212,7 @@ class PrefillInputs:
         return self.v_pool[:, g].reshape(-1, self.d)[: self.N]
 
     def rows(self, pool, g) -> torch.Tensor:
-        return pool[:, g].reshape(self.k_pool.shape[0] * PAGE, -1)[: self.N]
+        return pool[:, g].reshape(self.k_pool.shape[0] * PAGE, pool.shape[-1])[: self.N]
 
     def heads(self, g) -> list:
         return list(range(g * self.G, (g + 1) * self.G))

@@ -1,0 +1,135 @@
+"""The C-ABI library loads and exports every entry point include/sa.h declares,
+and rejects bad arguments on the host (before any launch, so no GPU is
+touched).  CPU only."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+LIB = os.path.join(ROOT, "dynamic_sparse_attention_02_amd", "libsa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB),
+                                reason="libsa.so not built (python -m dynamic_sparse_attention_02_amd.build)")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+def lib():
+    from dynamic_sparse_attention_02_amd import _lib as L
+    return L, L.load()
+
+
+def test_every_declared_symbol_is_exported_and_bound():
+    L, so = lib()
+    names = declared_functions()
+    assert len(names) >= 14, names
+    for n in names:
+        assert hasattr(so, n), f"{n} declared in sa.h but not exported"
+        assert n in L.SIGNATURES, f"{n} has no ctypes signature in the binding"
+    assert set(L.SIGNATURES) == set(names)
+    from dynamic_sparse_attention_02_amd import ops
+    for n in names:
+        if n.startswith("sa_") and n not in ("sa_workspace_size", "sa_status_string",
+                                              "sa_last_error", "sa_version"):
+            assert hasattr(ops, n), f"binding lacks {n}"
+
+
+def test_status_strings_and_version():
+    L, so = lib()
+    assert so.sa_status_string(0) == b"SA_OK"
+    assert so.sa_status_string(3) == b"SA_ERR_CAPACITY"
+    assert so.sa_status_string(99) == b"SA_ERR_UNKNOWN"
+    assert b"gfx950" in so.sa_version()
+
+
+def _shape(L, **kw):
+    base = dict(batch=1, n_q_heads=32, n_kv_heads=4, head_dim=128, idx_rank=16, page_size=64,
+                max_pages=1024, max_len=65536, n_pool_pages=1024)
+    base.update(kw)
+    return L.SaShape(*[base[f] for f, _ in L.SaShape._fields_])
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case fails validation first
+
+
+def test_workspace_sizes():
+    L, so = lib()
+    s = _shape(L)
+    ws = lambda op, prm: so.sa_workspace_size(op, ctypes.byref(s), prm)
+    assert ws(L.SA_OP_INDEX_SCORES, 0) >= 4 * 16 * 4
+    assert ws(L.SA_OP_SELECT, 1 << 22) > ws(L.SA_OP_SELECT, 1024) > 0
+    assert ws(L.SA_OP_SPARSE_DECODE, 65536) > ws(L.SA_OP_SPARSE_DECODE, 64) > 0
+    assert ws(L.SA_OP_DECODE_STEP, 65536) >= ws(L.SA_OP_SELECT, 65536) + ws(L.SA_OP_SPARSE_DECODE, 65536)
+    bad = _shape(L, head_dim=96)
+    assert so.sa_workspace_size(L.SA_OP_SELECT, ctypes.byref(bad), 10) == 0
+
+
+def _pages(L):
+    return L.SaPages(FAKE, FAKE)
+
+
+def test_validation_codes():
+    L, so = lib()
+    s = _shape(L)
+    pg = _pages(L)
+    B = ctypes.byref
+    # select: bad p, capacity, workspace, NULL buffer
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 65536, 0.0, 0, 0, FAKE, FAKE, 65536, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert b"p=" in so.sa_last_error()
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 65536, 1.5, 0, 0, FAKE, FAKE, 65536, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 65536, 0.9, 0, 0, FAKE, FAKE, 1000, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 65536, 0.9, 0, 0, FAKE, FAKE, 65536, FAKE, 16, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 65536, 0.9, 0, 0, FAKE, FAKE, 65536, None, 1 << 30, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_select_topp(B(s), B(pg), None, 65536, 0.9, 0, 0, FAKE, FAKE, 65536, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_select_topp(B(s), B(pg), FAKE, 100, 0.9, 0, 0, FAKE, FAKE, 65536, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_select_topp(None, B(pg), FAKE, 65536, 0.9, 0, 0, FAKE, FAKE, 65536, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    # top-k: k < 1, capacity, pages with sink, unit
+    assert so.sa_select_topk(B(s), B(pg), FAKE, 65536, 0, 1, 0, 0, FAKE, FAKE, 100, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_select_topk(B(s), B(pg), FAKE, 65536, 64, 1, 4, 512, FAKE, FAKE, 579, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    assert so.sa_select_topk(B(s), B(pg), FAKE, 65536, 32, 64, 4, 0, FAKE, FAKE, 2048, FAKE, 1 << 30, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_select_topk(B(s), B(pg), FAKE, 65536, 32, 7, 0, 0, FAKE, FAKE, 2048, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_select_topk(B(s), B(pg), FAKE, 65536, 32, 64, 0, 0, FAKE, FAKE, 2047, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    # shapes
+    for kw, code in ((dict(head_dim=96), L.SA_ERR_UNSUPPORTED), (dict(idx_rank=8), L.SA_ERR_UNSUPPORTED),
+                     (dict(page_size=32), L.SA_ERR_UNSUPPORTED), (dict(n_kv_heads=5), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(n_q_heads=96, n_kv_heads=4), L.SA_ERR_UNSUPPORTED),
+                     (dict(max_len=65537), L.SA_ERR_INVALID_ARGUMENT), (dict(batch=0), L.SA_ERR_INVALID_ARGUMENT),
+                     (dict(n_pool_pages=0), L.SA_ERR_INVALID_ARGUMENT)):
+        bad = _shape(L, **kw)
+        assert so.sa_index_scores(B(bad), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, 1.0, FAKE, 65536, FAKE, 1 << 20, None) == code, kw
+    # decode: workspace too small, bad dtype, NULL count
+    assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 100, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, 7, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, None, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    # decode step: capacity and p
+    assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.9, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 60000, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.0, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 65536, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    # prefill: batch, b_sel, dtype, n_tokens
+    s1 = _shape(L, n_q_heads=32, n_kv_heads=8, max_pages=2048, max_len=131072, n_pool_pages=2048)
+    assert so.sa_sparse_prefill(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2048, 32, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_sparse_prefill(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_F32, FAKE, FAKE, 2048, 64, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_sparse_prefill(B(s1), B(pg), 131073, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2048, 64, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_INVALID_ARGUMENT
+    s2 = _shape(L, batch=2)
+    assert so.sa_select_prefill_topk(B(s2), B(pg), 100, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 64, 2048, FAKE, FAKE, 2048, FAKE, 1 << 30, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_select_prefill_topk(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 64, 2048, FAKE, FAKE, 2000, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    # maintenance calls
+    assert so.sa_index_append(B(s), None, FAKE, L.SA_BF16, FAKE, 5, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_index_append(B(s), FAKE, FAKE, L.SA_BF16, FAKE, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_page_stats(B(s), FAKE, 9, FAKE, FAKE, 3, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_page_scores(B(s), B(pg), FAKE, FAKE, L.SA_BF16, 0.1, FAKE, 10, None) == L.SA_ERR_INVALID_ARGUMENT
+
+
+def test_zero_work_calls_return_ok_without_launch():
+    L, so = lib()
+    s = _shape(L)
+    assert so.sa_index_append(ctypes.byref(s), None, None, L.SA_BF16, None, 0, None, None) == L.SA_OK
+    assert so.sa_page_stats(ctypes.byref(s), None, L.SA_BF16, None, None, 0, None, None) == L.SA_OK
+    assert so.sa_last_error() == b""
