@@ -10,6 +10,8 @@
 
 namespace {
 
+constexpr int kMaxDecodeRows = 4096;  // (sequence, group) rows of one decode call
+
 thread_local std::string g_err;
 
 sa_status fail(sa_status st, const char* fmt, ...) {
@@ -284,6 +286,8 @@ sa_status sa_sparse_decode(const sa_shape* s, const sa_pages* pg, const void* q,
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
   if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
   if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
   SA_TRY(check_ws(ws, ws_bytes, decode_ws(s, cap), fn));
   return hip_status(sa::launch_sparse_decode(to_shape(s), *pg, q, k_pool, v_pool, dt, idx, count,
                                              cap, s_att, out, out_dt, lse, ws, st), fn);
@@ -306,6 +310,8 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   if (top_k == 0 && !(p > 0.f && p <= 1.f))
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: p=%g outside (0, 1]", fn, (double)p);
   if (n_sink < 0 || n_window < 0) return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_sink/n_window < 0", fn);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
   const int64_t cap_needed = top_k > 0 ? topk_cap_needed(s, top_k, 1, n_sink, n_window) : s->max_len;
   if (cap < 1 || cap < cap_needed)
     return fail(SA_ERR_CAPACITY, "%s: cap=%d below the worst-case support %lld", fn, cap, (long long)cap_needed);

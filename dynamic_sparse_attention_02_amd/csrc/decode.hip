@@ -3,15 +3,16 @@
 // section 2.1: attention recomputed with the original q, k, v restricted to
 // the support; one support per group shared by its query heads).
 //
-// The support list of a row (b, g) is cut into chunks of a multiple of 64
-// listed tokens, sized at run time from the list length so that every row has
-// at most about 512 / rows chunks; one block per chunk gathers the K and V
-// rows of 64 tokens at a time
+// The support lists are cut into chunks of a multiple of 64 listed tokens,
+// one size for all rows, chosen at run time from the total list length; a
+// persistent grid of blocks takes the (row, chunk) items in turn.  A block
+// gathers the K and V rows of 64 tokens at a time
 // (16-byte loads, 16 lanes per 256-byte row, staged in LDS), computes the
 // logits of the group's heads with one lane per token (bf16 pairs through
 // v_dot2_f32_bf16, fp32 accumulate), keeps an online softmax per head, and
 // accumulates P.V with one lane per head dimension.  The next tile's rows are
-// loaded into registers while the current tile is processed.  A second kernel
+// loaded into registers, and the pool addresses of the tile after it resolved
+// (list entry -> page table -> row), while the current tile is processed.  A second kernel
 // merges the per-chunk (max, sum, output) partials in chunk order.
 //
 // Bound: HBM bandwidth of the gathered rows (512 B per listed token for
@@ -32,12 +33,22 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
                                           __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Listed tokens per chunk of a row with n listed tokens: a multiple of the
-// 64-token tile, large enough that the row has at most `chunks` chunks.
-__device__ __forceinline__ int32_t chunk_size(int32_t n, int32_t chunks) {
-  const int32_t per = (n + chunks - 1) / chunks;
-  const int32_t c = ((per + kTile - 1) / kTile) * kTile;
-  return c < kTile ? kTile : c;
+// Work decomposition.  Every row's list is cut into chunks of C = 64 * tpc
+// listed tokens; tpc is the same for all rows and follows from the total
+// number of listed tiles and the (persistent) grid size, so that the chunks
+// spread evenly over the blocks.  Items (row, chunk) are numbered row by row
+// and block b takes items b, b + grid, ...
+constexpr int kMaxRowsLds = 4096;  // rows whose chunk prefix fits in LDS
+
+__device__ __forceinline__ int32_t row_count(const int32_t* count, int row, int32_t cap) {
+  int32_t n = count[row];
+  return n < 0 ? 0 : (n > cap ? cap : n);
+}
+
+// Tiles per chunk from the total listed tiles (same result in every block).
+__device__ __forceinline__ int32_t plan_tpc(int64_t total_tiles, int32_t grid) {
+  int64_t t = (total_tiles + 2 * (int64_t)grid - 1) / (2 * (int64_t)grid);
+  return t < 1 ? 1 : (t > 16 ? 16 : (int32_t)t);
 }
 
 template <typename T, int D, int G>
@@ -57,34 +68,67 @@ __global__ void __launch_bounds__((G < 4 ? G : 4) * 64)
 k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
                const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
                const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int32_t cap,
-               Shape s, float s_att, int32_t chunks, int32_t nchunk_max,
+               Shape s, float s_att, int32_t nchunk_max,
                float* __restrict__ part_ml, float* __restrict__ part_o) {
   using C = DecodeCfg<T, D, G>;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int row = b * s.Hkv + g;
-  int32_t n = count[row];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int32_t csize = chunk_size(n, chunks);
-  const int32_t nch = (n + csize - 1) / csize;
-  if ((int32_t)blockIdx.x >= nch) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rows = s.B * s.Hkv;
 
   __shared__ __align__(16) char Ks[kTile * C::PITCH];
   __shared__ __align__(16) char Vs[kTile * C::PITCH];
   __shared__ __align__(16) T Qs[G][D];
   __shared__ __align__(16) float Ps[G][kTile];
+  __shared__ int32_t prefix[kMaxRowsLds + 1];
+  __shared__ int64_t s_tiles;
+  __shared__ int32_t s_red[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < G * D; i += C::NT)
-    Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
-  const int32_t L = clamp_len(seq_lens[b], s.max_len);
-  const int32_t* pt = page_table + (int64_t)b * s.max_pages;
-  const int32_t* list = idx + (int64_t)row * cap;
-  const int64_t head_stride = (int64_t)kPage * D;           // elements per (page, group)
-  const int64_t page_stride = (int64_t)s.Hkv * head_stride;  // elements per page
+  // ---- plan: tiles per chunk and the item prefix over rows ----
+  if (tid == 0) s_tiles = 0;
+  __syncthreads();
+  int64_t my_tiles = 0;
+  for (int r = tid; r < rows; r += C::NT) my_tiles += (row_count(count, r, cap) + kTile - 1) / kTile;
+  atomicAdd((unsigned long long*)&s_tiles, (unsigned long long)my_tiles);
+  __syncthreads();
+  const int32_t tpc = plan_tpc(s_tiles, gridDim.x);
+  const int32_t csize = kTile * tpc;
+  // prefix[r] = items before row r (sequential scan by wave 0, rows <= kMaxRowsLds)
+  if (wave == 0) {
+    int32_t carry = 0;
+    for (int r0 = 0; r0 < rows; r0 += 64) {
+      const int r = r0 + lane;
+      const int32_t c = r < rows ? (row_count(count, r, cap) + csize - 1) / csize : 0;
+      const int32_t inc = (int32_t)wave_incl_scan((uint32_t)c);
+      if (r < rows) prefix[r] = carry + inc - c;
+      carry += __shfl(inc, 63, 64);
+    }
+    if (lane == 0) prefix[rows] = carry;
+  }
+  __syncthreads();
+  const int32_t n_items = prefix[rows];
+  const int64_t head_stride = (int64_t)kPage * D;
+  const int64_t page_stride = (int64_t)s.Hkv * head_stride;
 
-  for (int32_t c = blockIdx.x; c < nch; c += gridDim.x) {
+  for (int32_t item = blockIdx.x; item < n_items; item += gridDim.x) {
+    // row of the item: last r with prefix[r] <= item
+    int lo = 0, hi = rows - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (prefix[mid] <= item) lo = mid; else hi = mid - 1;
+    }
+    const int row = lo;
+    const int32_t c = item - prefix[row];
+    const int b = row / s.Hkv, g = row % s.Hkv;
+    const int32_t n = row_count(count, row, cap);
     const int32_t t0 = c * csize;
     const int32_t t1 = min(n, t0 + csize);
+    const int32_t L = clamp_len(seq_lens[b], s.max_len);
+    const int32_t* pt = page_table + (int64_t)b * s.max_pages;
+    const int32_t* list = idx + (int64_t)row * cap;
+
+    __syncthreads();  // previous item done with Qs
+    for (int i = tid; i < G * D; i += C::NT)
+      Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
+
     float m_run[C::HPW], l_run[C::HPW], acc[C::HPW][C::DPL];
 #pragma unroll
     for (int hh = 0; hh < C::HPW; ++hh) {
@@ -93,30 +137,41 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
 #pragma unroll
       for (int e = 0; e < C::DPL; ++e) acc[hh][e] = 0.f;
     }
-    uint4 kr[C::LPT], vr[C::LPT];
-    auto gather = [&](int32_t ts) {
-      const int32_t nt = min(kTile, t1 - ts);
+    // pool element offsets of the rows this thread moves in a tile
+    int64_t ridn[C::LPT];
+    auto load_rows = [&](int32_t ts, int64_t (&rid)[C::LPT]) {
 #pragma unroll
       for (int i = 0; i < C::LPT; ++i) {
-        const int pc = i * C::NT + tid;
-        const int r = pc / C::CPR, col = pc % C::CPR;
-        if (r < nt) {
+        const int r = (i * C::NT + tid) / C::CPR;
+        rid[i] = -1;
+        if (ts + r < t1) {
           int32_t j = list[ts + r];
           j = j < 0 ? 0 : (j >= L ? (L > 0 ? L - 1 : 0) : j);
           const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
-          const int64_t off = page * page_stride + g * head_stride + (int64_t)(j & 63) * D;
-          kr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + off) + col * 16);
-          vr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + off) + col * 16);
+          rid[i] = page * page_stride + g * head_stride + (int64_t)(j & 63) * D;
+        }
+      }
+    };
+    uint4 kr[C::LPT], vr[C::LPT];
+    auto load_kv = [&](const int64_t (&rid)[C::LPT]) {
+#pragma unroll
+      for (int i = 0; i < C::LPT; ++i) {
+        const int col = (i * C::NT + tid) % C::CPR;
+        if (rid[i] >= 0) {
+          kr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + rid[i]) + col * 16);
+          vr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + rid[i]) + col * 16);
         } else {
           kr[i] = make_uint4(0, 0, 0, 0);
           vr[i] = make_uint4(0, 0, 0, 0);
         }
       }
     };
-    gather(t0);
+    load_rows(t0, ridn);
+    load_kv(ridn);
+    if (t0 + kTile < t1) load_rows(t0 + kTile, ridn);
     for (int32_t ts = t0; ts < t1; ts += kTile) {
       const int32_t nt = min(kTile, t1 - ts);
-      __syncthreads();  // previous tile fully consumed
+      __syncthreads();  // previous tile fully consumed (and Qs written)
 #pragma unroll
       for (int i = 0; i < C::LPT; ++i) {
         const int pc = i * C::NT + tid;
@@ -125,7 +180,10 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
         *reinterpret_cast<uint4*>(Vs + r * C::PITCH + col * 16) = vr[i];
       }
       __syncthreads();
-      if (ts + kTile < t1) gather(ts + kTile);  // overlap next gather with compute
+      if (ts + kTile < t1) {  // next tile's rows in flight, and the addresses after it
+        load_kv(ridn);
+        if (ts + 2 * kTile < t1) load_rows(ts + 2 * kTile, ridn);
+      }
 
       // logits: lane = token of the tile
       float sc[C::HPW];
@@ -232,15 +290,23 @@ constexpr int kMaxChunkW = 4096;  // chunk weights kept in LDS
 template <typename TO>
 __global__ void __launch_bounds__(kCombThreads)
 k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ part_o,
-                 const int32_t* __restrict__ count, int32_t cap, Shape s, int32_t chunks,
+                 const int32_t* __restrict__ count, int32_t cap, Shape s, int32_t split_grid,
                  int32_t nchunk_max, TO* __restrict__ out, float* __restrict__ lse) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = s.Hq / s.Hkv;
   const int row = b * s.Hkv + h / G;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int32_t n = count[row];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int32_t nch = n == 0 ? 0 : (n + chunk_size(n, chunks) - 1) / chunk_size(n, chunks);
+  const int rows = s.B * s.Hkv;
+  __shared__ int64_t s_tiles;
+  if (tid == 0) s_tiles = 0;
+  __syncthreads();
+  int64_t my_tiles = 0;
+  for (int r = tid; r < rows; r += kCombThreads) my_tiles += (row_count(count, r, cap) + kTile - 1) / kTile;
+  atomicAdd((unsigned long long*)&s_tiles, (unsigned long long)my_tiles);
+  __syncthreads();
+  const int32_t csize = kTile * plan_tpc(s_tiles, split_grid);
+  const int32_t n = row_count(count, row, cap);
+  const int32_t nch = (n + csize - 1) / csize;
   const int64_t base = ((int64_t)b * s.Hq + h) * nchunk_max;
   __shared__ float wred[4];
   __shared__ float wts[kMaxChunkW];
@@ -283,11 +349,16 @@ k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ pa
   if (lse && tid == 0) lse[(int64_t)b * s.Hq + h] = nch ? M + logf(lsum) : -INFINITY;
 }
 
-// Chunks per row: enough blocks to cover the chip about twice.
-int chunks_per_row(const Shape& s) {
-  const int rows = s.B * s.Hkv;
-  int c = (512 + rows - 1) / rows;
-  return c < 1 ? 1 : c;
+// Persistent grid of the split kernel: blocks resident on the chip.
+int split_grid(int nchunk_max, int rows) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  const long long most = (long long)nchunk_max * rows;
+  const long long g = 3LL * cus;
+  return (int)(most < g ? (most < 1 ? 1 : most) : g);
 }
 
 template <typename T, int D>
@@ -295,17 +366,16 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
                     const void* v_pool, const int32_t* idx, const int32_t* count, int32_t cap,
                     float s_att, void* out, sa_dtype out_dt, float* lse, void* ws,
                     hipStream_t st) {
-  const int chunks = chunks_per_row(s);
   const int32_t nchunk_max = (cap + kTile - 1) / kTile;
   float* part_ml = (float*)ws;
   float* part_o = part_ml + align_up((size_t)s.B * s.Hq * nchunk_max * 2, 64);
-  int gx = chunks < nchunk_max ? chunks : nchunk_max;
-  dim3 grid(gx, s.Hkv, s.B);
+  const int gx = split_grid(nchunk_max, s.B * s.Hkv);
+  dim3 grid(gx);
   const int G = s.Hq / s.Hkv;
 #define SA_DS(GG)                                                                        \
   k_decode_split<T, D, GG><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(                     \
       (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,   \
-      count, cap, s, s_att, chunks, nchunk_max, part_ml, part_o)
+      count, cap, s, s_att, nchunk_max, part_ml, part_o)
   switch (G) {
     case 1: SA_DS(1); break;
     case 2: SA_DS(2); break;
@@ -317,9 +387,9 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
   dim3 g2(s.Hq, s.B);
   if (out_dt == SA_BF16)
     k_decode_combine<bf16_raw><<<g2, kCombThreads, 0, st>>>(part_ml, part_o, count, cap, s,
-                                                            chunks, nchunk_max, (bf16_raw*)out, lse);
+                                                            gx, nchunk_max, (bf16_raw*)out, lse);
   else
-    k_decode_combine<float><<<g2, kCombThreads, 0, st>>>(part_ml, part_o, count, cap, s, chunks,
+    k_decode_combine<float><<<g2, kCombThreads, 0, st>>>(part_ml, part_o, count, cap, s, gx,
                                                          nchunk_max, (float*)out, lse);
   return hipGetLastError();
 }

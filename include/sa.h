@@ -201,7 +201,8 @@ sa_status sa_select_topk(const sa_shape* shape, const sa_pages* pages, const flo
  * S = idx[b * n_kv_heads + g][0 .. count)
  *   out[b][h] = sum_{j in S} softmax_S(s_att * q[b][h] . k_j) v_j
  *   lse[b][h] = log sum_{j in S} exp(s_att * q[b][h] . k_j)   (lse may be NULL)
- * An empty support gives out = 0 and lse = -inf.  q, k_pool, v_pool of dtype;
+ * An empty support gives out = 0 and lse = -inf.  batch * n_kv_heads <= 4096.
+ * q, k_pool, v_pool of dtype;
  * out [batch][n_q_heads][head_dim] of out_dtype; lse fp32.  List entries must
  * be in [0, seq_lens[b]).  fp32 accumulation. */
 sa_status sa_sparse_decode(const sa_shape* shape, const sa_pages* pages, const void* q,
