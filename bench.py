@@ -316,7 +316,124 @@ def cpu_baseline_decode(inp, kidx, step_bytes, seconds, page_mode, stats):
 
 
 def bench_prefill(args):
-    raise SystemExit("prefill128k: not built yet")
+    """Block selection (top-k 2048 per 64-query block) + block-sparse causal
+    attention over the 128K prefill.  FLOPs = 4 * d * (query, key) pairs
+    attended per head, counted from the actual supports (diagonal pairs
+    causal only)."""
+    import numpy as np
+    import torch
+
+    import synth
+    from dynamic_sparse_attention_02_amd import _lib as L
+    from dynamic_sparse_attention_02_amd import ops
+
+    inp = synth.make_prefill128k(device="cuda")
+    N, Hq, Hkv, d = inp.N, inp.H_q, inp.H_kv, inp.d
+    G = Hq // Hkv
+    shape = ops.make_shape(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                           max_pages=inp.page_table.shape[1], max_len=N,
+                           n_pool_pages=inp.k_pool.shape[0])
+    pages = ops.make_pages(inp.page_table, None)
+    kidx = torch.zeros((inp.k_pool.shape[0], Hkv, 64, 16), dtype=inp.dtype, device="cuda")
+    fill_kidx(ops, shape, inp, kidx)
+    nblk = inp.n_blocks
+    k = inp.top_k
+    cap = min(k, N)
+    idx = torch.empty((nblk * Hkv, cap), dtype=torch.int32, device="cuda")
+    count = torch.empty((nblk * Hkv,), dtype=torch.int32, device="cuda")
+    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_SELECT, shape, N))
+
+    def select():
+        ops.sa_select_prefill_topk(shape, pages, N, inp.q, inp.w_q, kidx, inp.s_idx, 64, k, idx,
+                                   count, ws)
+
+    def attend():
+        ops.sa_sparse_prefill(shape, pages, N, inp.q, inp.k_pool, inp.v_pool, idx, count, 64,
+                              inp.s_att, out, lse)
+
+    select()
+    attend()
+    torch.cuda.synchronize()
+    cnt = count.cpu().numpy().astype(np.int64).reshape(nblk, Hkv)
+    nq = np.minimum(64, N - 64 * np.arange(nblk))
+    pairs = (cnt * nq[:, None]).sum() + Hkv * (nq * (nq + 1) // 2).sum()
+    flops = 4.0 * d * G * float(pairs)
+    steps = max(1, args.steps // 10)
+    t_sel = time_events(select, steps)
+    t_att = time_events(attend, steps)
+    ms = t_sel + t_att
+    tflops = flops / (ms * 1e-3) / 1e12
+    att_tflops = flops / (t_att * 1e-3) / 1e12
+    res = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": steps, "warmup": 1, "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill128k", "tokens": N, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "b_sel": 64, "top_k": k},
+        "algorithmic_flops": flops,
+        "breakdown_ms": {"select": round(t_sel, 4), "attention": round(t_att, 4)},
+        "attention_tflops": round(att_tflops, 2),
+        "roofline": {"kernel": "sparse_prefill", "bound": "mfma", "achieved": round(att_tflops, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "avg_launch_ms": round(t_att, 4)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(inp, kidx, args.cpu_seconds)
+    return res
+
+
+def time_events(fn, n):
+    """Average milliseconds of fn() over n calls (HIP events, current stream)."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    a, b = _events()
+    a.record()
+    for _ in range(n):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def cpu_baseline_prefill(inp, kidx, seconds):
+    """The float64 oracle on a bounded sample of the prefill: whole (query
+    block, group) items (selection + attention), late blocks first."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+
+    g = 0
+    hs = inp.heads(g)
+    K = inp.keys(g).double().cpu().numpy()
+    V = inp.values(g).double().cpu().numpy()
+    kt = inp.rows(kidx, g).double().cpu().numpy()
+    wq = inp.w_q[hs].double().cpu().numpy()
+    nblk = inp.n_blocks
+    flops = 0.0
+    n_items = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for blk in range(nblk - 1, -1, -1):
+            rows = O.prefill_block_rows(blk, 64, inp.N)
+            Qb = inp.q[rows.start:rows.stop][:, hs].double().cpu().numpy()
+            qc = O.prefill_block_query(Qb, wq, inp.s_idx)
+            S_ = O.prefill_block_support(qc, kt, blk, 64, inp.top_k)
+            O.prefill_block_attend(Qb, K, V, S_, blk, 64, inp.s_att)
+            nq = rows.stop - rows.start
+            flops += 4.0 * inp.d * len(hs) * (nq * len(S_) + nq * (nq + 1) / 2)
+            n_items += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_items} (query block, group) items of the last blocks (selection + "
+                      f"attention), float64 numpy, {el:.1f} s",
+            "host_threads_available": cpu_threads_info()}
 
 
 # ---------------------------------------------------------------------------

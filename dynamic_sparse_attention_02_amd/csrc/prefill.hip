@@ -1,20 +1,456 @@
-// Causal block-sparse prefill (placeholder until the kernels land).
+// Causal prefill with supports shared by blocks of b_sel = 64 queries
+// ("Oracle-Guided Sparse Prefill", section 2.1: top-k support per selection
+// block, attention recomputed with the original q, k, v over the support;
+// section 2.2: one head-collapsed indexer channel).
+//
+// Selection: per (query block, group) the block-collapsed indexer query is
+// formed (sum of the block's queries per head, then projected), scores over
+// the keys of all earlier blocks are written for a slab of query blocks, and
+// the row-resident radix select keeps the top k of each row.
+//
+// Attention: one workgroup per (query block, group); each wave owns one query
+// head and the 64 queries of the block, so the 4 heads of a group share every
+// gathered K/V tile.  Per 64-key tile the wave computes S^T = K Q^T and
+// O^T += V^T P^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
+// accumulate).  In this transposed form a lane holds one query's scores, so
+// the online softmax needs one cross-lane exchange per row, and the fp32 S^T
+// accumulator already has the lane layout of the P^T operand once the keys of
+// each 16-key step are taken in the order the accumulator holds them; V is
+// written to LDS transposed so V^T operands are two 8-byte reads.  K/V tiles
+// are double-buffered in LDS with the next tile's rows in flight during the
+// current tile's products.
 #include "sa_internal.h"
 
 namespace sa {
 
-size_t prefill_select_workspace_bytes(const Shape&, int32_t) { return 0; }
+namespace {
 
-hipError_t launch_prefill_select(const Shape&, const sa_pages&, int32_t, const void*, const void*,
-                                 const void*, sa_dtype, float, int32_t, int32_t, int32_t*,
-                                 int32_t*, int32_t, void*, hipStream_t) {
-  return hipErrorNotSupported;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int kQB = 64;     // queries per selection block
+constexpr int kSlab = 256;  // query blocks per score slab
+
+// ---------------------------------------------------------------------------
+// Block-collapsed indexer query: qcb[blk][g][c] = s_idx / (rows * G) *
+// sum_{h in g} sum_d W_q[h][d][c] * (sum_{i in blk} q[i][h][d]).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int32_t Hq,
+             int32_t Hkv, int32_t D, float s_idx, float* __restrict__ qcb) {
+  const int blk = blockIdx.x, g = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int r0 = blk * kQB;
+  const int nr = min(kQB, N - r0);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float acc[kRank];
+#pragma unroll
+  for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
+  for (int pi = threadIdx.x; pi < G * D; pi += 256) {
+    const int h = g * G + pi / D, d = pi % D;
+    float qs = 0.f;
+    for (int i = 0; i < nr; ++i) qs += to_f32<T>(q[((int64_t)(r0 + i) * Hq + h) * D + d]);
+    const T* w = w_q + ((int64_t)h * D + d) * kRank;
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) acc[c] = fmaf(to_f32<T>(w[c]), qs, acc[c]);
+  }
+  __shared__ float red[4][kRank];
+#pragma unroll
+  for (int c = 0; c < kRank; ++c) {
+    float v = wave_sum(acc[c]);
+    if (lane == 0) red[wave][c] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < kRank) {
+    const int c = threadIdx.x;
+    const float v = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
+    qcb[((int64_t)blk * Hkv + g) * kRank + c] = v * (s_idx / (float)(nr * G));
+  }
 }
 
-hipError_t launch_sparse_prefill(const Shape&, const sa_pages&, int32_t, const void*, const void*,
-                                 const void*, const int32_t*, const int32_t*, int32_t, int32_t,
-                                 float, void*, sa_dtype, float*, hipStream_t) {
-  return hipErrorNotSupported;
+// ---------------------------------------------------------------------------
+// Scores of a slab of query blocks: x[(blk - blk0) * Hkv + g][j] =
+// qcb[blk][g] . Kidx[g][j] for j < 64 * blk.  A workgroup covers 256
+// candidates and kRowsT query blocks of one group: each key row is loaded once
+// and scored against every block's query.
+// ---------------------------------------------------------------------------
+constexpr int kRowsT = 32;
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
+                 const float* __restrict__ qcb, int32_t blk0, int32_t blk1, Shape s,
+                 float* __restrict__ x, int64_t ldx) {
+  const int g = blockIdx.z;
+  const int b_lo = blk0 + blockIdx.y * kRowsT;
+  const int b_hi = min(blk1, b_lo + kRowsT);
+  const int32_t j = blockIdx.x * 256 + threadIdx.x;
+  if ((int64_t)blockIdx.x * 256 >= (int64_t)kQB * (b_hi - 1)) return;  // above every row
+  __shared__ float qs[kRowsT][kRank];
+  for (int i = threadIdx.x; i < kRowsT * kRank; i += 256) {
+    const int bb = b_lo + i / kRank;
+    qs[i / kRank][i % kRank] = bb < b_hi ? qcb[((int64_t)bb * s.Hkv + g) * kRank + i % kRank] : 0.f;
+  }
+  __syncthreads();
+  if (j >= kQB * (b_hi - 1)) return;
+  const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+  const T* row = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
+  float k[kRank];
+  if constexpr (sizeof(T) == 2) {
+    const uint4* v = reinterpret_cast<const uint4*>(row);
+    const uint4 a = v[0], b = v[1];
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      k[2 * i] = __uint_as_float(u[i] << 16);
+      k[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kRank; ++i) k[i] = to_f32<T>(row[i]);
+  }
+  for (int bb = b_lo; bb < b_hi; ++bb) {
+    if (j >= kQB * bb) continue;
+    const float* qv = qs[bb - b_lo];
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) a = fmaf(qv[c], k[c], a);
+    x[((int64_t)(bb - blk0) * s.Hkv + g) * ldx + j] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block-sparse causal attention.
+// ---------------------------------------------------------------------------
+constexpr int kKT = 64;                 // keys per tile
+constexpr int kKPitch = 128 * 2 + 16;   // K tile row pitch in bytes (d = 128 bf16)
+constexpr int kVPitch = kKT * 2 + 16;   // V^T tile row pitch in bytes (64 keys bf16)
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+template <int G>
+__global__ void __launch_bounds__(G * 64)
+k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_pool,
+               const bf16_raw* __restrict__ v_pool, const int32_t* __restrict__ pt,
+               const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int32_t cap,
+               int32_t N, Shape s, float s_att, void* __restrict__ out, int32_t out_bf16,
+               float* __restrict__ lse) {
+  constexpr int D = 128;
+  constexpr int NT = G * 64;
+  constexpr int PIECES = kKT * (D * 2 / 16);  // 16-byte pieces per tile per tensor
+  constexpr int LPT = (PIECES + NT - 1) / NT;
+  const int nblk = (N + kQB - 1) / kQB;
+  // heaviest items (late blocks, full supports) first
+  const int item = blockIdx.x;
+  const int blk = nblk - 1 - item / s.Hkv;
+  const int g = item % s.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = g * G + wave;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int row = blk * s.Hkv + g;
+  int32_t nl = count[row];
+  nl = nl < 0 ? 0 : (nl > cap ? cap : nl);
+  const int32_t q0 = blk * kQB;
+  const int32_t nq = min(kQB, N - q0);
+  const int n_list_tiles = (nl + kKT - 1) / kKT;
+  const int n_tiles = n_list_tiles + 1;  // + the diagonal tile
+  const int32_t* list = idx + (int64_t)row * cap;
+
+  __shared__ __align__(16) char Ks[2][kKT * kKPitch];
+  __shared__ __align__(16) char Vt[2][D * kVPitch];
+
+  // Q as the B operand of S^T = K Q^T: Qb[nb][ks] holds query nb*32 + l32,
+  // dims ks*16 + 8*half .. +7
+  bf16x8_t Qb[2][8];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int32_t qi = q0 + nb * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (qi < N)
+        v = *reinterpret_cast<const uint4*>(q + ((int64_t)qi * s.Hq + h) * D + ks * 16 + 8 * half);
+      Qb[nb][ks] = __builtin_bit_cast(bf16x8_t, v);
+    }
+  }
+
+  const int64_t head_stride = (int64_t)kPage * D;
+  const int64_t page_stride = (int64_t)s.Hkv * head_stride;
+  auto key_of = [&](int tile, int r) -> int32_t {  // token index of tile row r, -1 if none
+    if (tile < n_list_tiles) {
+      const int32_t t = tile * kKT + r;
+      return t < nl ? list[t] : -1;
+    }
+    const int32_t kj = q0 + r;
+    return r < nq ? kj : -1;
+  };
+  uint4 kr[LPT], vr[LPT];
+  auto gather = [&](int tile) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int pc = i * NT + tid;
+      const int r = pc >> 4, col = pc & 15;
+      kr[i] = make_uint4(0, 0, 0, 0);
+      vr[i] = make_uint4(0, 0, 0, 0);
+      if (pc < PIECES) {
+        int32_t j = key_of(tile, r);
+        if (j >= 0) {
+          j = j >= N ? N - 1 : j;
+          const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+          const int64_t off = page * page_stride + g * head_stride + (int64_t)(j & 63) * D + col * 8;
+          kr[i] = *reinterpret_cast<const uint4*>(k_pool + off);
+          vr[i] = *reinterpret_cast<const uint4*>(v_pool + off);
+        }
+      }
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int pc = i * NT + tid;
+      if (pc < PIECES) {
+        const int r = pc >> 4, col = pc & 15;
+        *reinterpret_cast<uint4*>(Ks[buf] + r * kKPitch + col * 16) = kr[i];
+        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          *reinterpret_cast<uint16_t*>(Vt[buf] + (col * 8 + 2 * e) * kVPitch + r * 2) = (uint16_t)(w[e] & 0xffffu);
+          *reinterpret_cast<uint16_t*>(Vt[buf] + (col * 8 + 2 * e + 1) * kVPitch + r * 2) = (uint16_t)(w[e] >> 16);
+        }
+      }
+    }
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  const float sl2 = s_att * 1.4426950408889634f;  // scores in log2 units
+
+  gather(0);
+  stage(0);
+  __syncthreads();
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int buf = tile & 1;
+    if (tile + 1 < n_tiles) gather(tile + 1);
+    const bool diag = tile == n_list_tiles;
+    const int nt = diag ? nq : min(kKT, nl - tile * kKT);
+
+    // S^T[key][query] for the 64 keys x 64 queries of this wave's head
+    f32x16_t S[2][2];
+#pragma unroll
+    for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) S[mk][nb][v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) {
+        const uint4 a = *reinterpret_cast<const uint4*>(Ks[buf] + (mk * 32 + l32) * kKPitch + ks * 32 + half * 16);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          S[mk][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Qb[nb][ks], S[mk][nb], 0, 0, 0);
+      }
+    }
+    // online softmax per query (lane's query nb*32 + l32; keys spread over
+    // this lane's 32 accumulator values and the partner lane's)
+    float alpha[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int qloc = nb * 32 + l32;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int kloc = mk * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+          const bool ok = kloc < nt && (!diag || kloc <= qloc);
+          const float t = ok ? S[mk][nb][v] * sl2 : -INFINITY;
+          S[mk][nb][v] = t;
+          mt = fmaxf(mt, t);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run[nb], mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      float lt = 0.f;
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const float p = exp2f(S[mk][nb][v] - m_use);
+          S[mk][nb][v] = p;
+          lt += p;
+        }
+      lt += __shfl_xor(lt, 32, 64);
+      alpha[nb] = exp2f(m_run[nb] - m_use);
+      l_run[nb] = l_run[nb] * alpha[nb] + lt;
+      m_run[nb] = m_new;
+    }
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
+    // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per step in the
+    // accumulator's key order
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int mk = st >> 1, hv = (st & 1) * 8;
+      bf16x8_t Pb[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        uint4 pw;
+        pw.x = pack_bf16x2(S[mk][nb][hv + 0], S[mk][nb][hv + 1]);
+        pw.y = pack_bf16x2(S[mk][nb][hv + 2], S[mk][nb][hv + 3]);
+        pw.z = pack_bf16x2(S[mk][nb][hv + 4], S[mk][nb][hv + 5]);
+        pw.w = pack_bf16x2(S[mk][nb][hv + 6], S[mk][nb][hv + 7]);
+        Pb[nb] = __builtin_bit_cast(bf16x8_t, pw);
+      }
+      const int kbase = mk * 32 + (st & 1) * 16 + 4 * half;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const char* vrow = Vt[buf] + (mb * 32 + l32) * kVPitch;
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kbase * 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (kbase + 8) * 2);
+        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Pb[nb], acc[mb][nb], 0, 0, 0);
+      }
+    }
+    // the other buffer was released by the barrier that ended the previous tile
+    if (tile + 1 < n_tiles) stage(buf ^ 1);
+    __syncthreads();
+  }
+  // normalise and store: lane holds d = mb*32 + 8*(v/4) + 4*half + v%4 of
+  // query nb*32 + l32
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int32_t qi = q0 + nb * 32 + l32;
+    if (qi >= N) continue;
+    const float inv = l_run[nb] > 0.f ? 1.f / l_run[nb] : 0.f;
+    const int64_t obase = ((int64_t)qi * s.Hq + h) * D;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int grp = 0; grp < 4; ++grp) {
+        const int d0 = mb * 32 + 8 * grp + 4 * half;
+        const float o0 = acc[mb][nb][grp * 4 + 0] * inv, o1 = acc[mb][nb][grp * 4 + 1] * inv;
+        const float o2 = acc[mb][nb][grp * 4 + 2] * inv, o3 = acc[mb][nb][grp * 4 + 3] * inv;
+        if (out_bf16) {
+          uint2 w;
+          w.x = pack_bf16x2(o0, o1);
+          w.y = pack_bf16x2(o2, o3);
+          *reinterpret_cast<uint2*>((bf16_raw*)out + obase + d0) = w;
+        } else {
+          *reinterpret_cast<float4*>((float*)out + obase + d0) = make_float4(o0, o1, o2, o3);
+        }
+      }
+    if (lse && half == 0)
+      lse[(int64_t)qi * s.Hq + h] = l_run[nb] > 0.f ? (m_run[nb] + log2f(l_run[nb])) * 0.6931471805599453f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+// Workspace of the prefill selection: block queries + one slab of scores.
+size_t prefill_select_workspace_bytes(const Shape& s, int32_t n_tokens) {
+  const int64_t nblk = (n_tokens + kQB - 1) / kQB;
+  const size_t qcb = align_up((size_t)nblk * s.Hkv * kRank * sizeof(float), 256);
+  const int64_t slab = nblk < kSlab ? nblk : kSlab;
+  const size_t xs = align_up((size_t)slab * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
+  const size_t sel = align_up(select_workspace_bytes((int32_t)(slab * s.Hkv), n_tokens), 256);
+  return qcb + xs + sel;
+}
+
+hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                 const void* q, const void* w_q, const void* kidx_pool,
+                                 sa_dtype dt, float s_idx, int32_t b_sel, int32_t k,
+                                 int32_t* idx, int32_t* count, int32_t cap, void* ws,
+                                 hipStream_t st) {
+  const int nblk = (n_tokens + kQB - 1) / kQB;
+  const int64_t slab = nblk < kSlab ? nblk : kSlab;
+  char* p = (char*)ws;
+  float* qcb = (float*)p;
+  p += align_up((size_t)nblk * s.Hkv * kRank * sizeof(float), 256);
+  float* xs = (float*)p;
+  p += align_up((size_t)slab * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
+  void* sel_ws = p;
+  dim3 g1(nblk, s.Hkv);
+  if (dt == SA_BF16)
+    k_prefill_qc<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q, n_tokens,
+                                               s.Hq, s.Hkv, s.D, s_idx, qcb);
+  else
+    k_prefill_qc<float><<<g1, 256, 0, st>>>((const float*)q, (const float*)w_q, n_tokens, s.Hq,
+                                            s.Hkv, s.D, s_idx, qcb);
+  for (int b0 = 0; b0 < nblk; b0 += (int)slab) {
+    const int b1 = b0 + (int)slab < nblk ? b0 + (int)slab : nblk;
+    const int64_t ldx = (int64_t)kQB * (b1 - 1) > 0 ? (int64_t)kQB * (b1 - 1) : 1;
+    dim3 g2((unsigned)((ldx + 255) / 256), (b1 - b0 + kRowsT - 1) / kRowsT, s.Hkv);
+    if (dt == SA_BF16)
+      k_prefill_scores<bf16_raw><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qcb,
+                                                     b0, b1, s, xs, ldx);
+    else
+      k_prefill_scores<float><<<g2, 256, 0, st>>>((const float*)kidx_pool, pg.page_table, qcb, b0,
+                                                  b1, s, xs, ldx);
+    SelectArgs a{};
+    a.x = xs;
+    a.ldx = ldx;
+    a.seq_lens = nullptr;
+    a.rows = (b1 - b0) * s.Hkv;
+    a.Hkv = s.Hkv;
+    a.max_len = n_tokens;
+    a.unit = 1;
+    a.max_cand = (int32_t)ldx;
+    a.is_topk = 1;
+    a.p = 0.f;
+    a.k = k;
+    a.n_sink = 0;
+    a.n_window = 0;
+    a.idx = idx + (int64_t)b0 * s.Hkv * cap;
+    a.count = count + (int64_t)b0 * s.Hkv;
+    a.cap = cap;
+    a.prefill_bsel = kQB;
+    a.prefill_blk0 = b0;
+    hipError_t e = launch_select(a, sel_ws, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                 const void* q, const void* k_pool, const void* v_pool,
+                                 const int32_t* idx, const int32_t* count, int32_t cap,
+                                 int32_t b_sel, float s_att, void* out, sa_dtype out_dt,
+                                 float* lse, hipStream_t st) {
+  const int nblk = (n_tokens + kQB - 1) / kQB;
+  const int G = s.Hq / s.Hkv;
+  dim3 grid(nblk * s.Hkv);
+#define SA_PA(GG)                                                                           \
+  k_prefill_attn<GG><<<grid, GG * 64, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)k_pool,  \
+                                               (const bf16_raw*)v_pool, pg.page_table, idx,  \
+                                               count, cap, n_tokens, s, s_att, out,          \
+                                               out_dt == SA_BF16, lse)
+  switch (G) {
+    case 1: SA_PA(1); break;
+    case 2: SA_PA(2); break;
+    case 4: SA_PA(4); break;
+    case 8: SA_PA(8); break;
+    default: SA_PA(16); break;
+  }
+#undef SA_PA
+  return hipGetLastError();
 }
 
 }  // namespace sa

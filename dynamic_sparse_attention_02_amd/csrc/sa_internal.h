@@ -135,6 +135,10 @@ struct SelectArgs {
   int32_t* idx;
   int32_t* count;
   int32_t cap;
+  // prefill rows: row r (= (blk - prefill_blk0) * Hkv + g) has
+  // prefill_bsel * blk candidates; 0 for decode rows
+  int32_t prefill_bsel;
+  int32_t prefill_blk0;
 };
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st);

@@ -75,6 +75,7 @@ WsLayout carve(void* ws, int32_t rows, int32_t max_cand) {
 }
 
 __device__ __forceinline__ int32_t n_cand_of(const SelectArgs& a, int row) {
+  if (a.prefill_bsel > 0) return a.prefill_bsel * (a.prefill_blk0 + row / a.Hkv);
   const int b = row / a.Hkv;
   const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
   return a.unit == 1 ? L : (L + a.unit - 1) / a.unit;
@@ -447,7 +448,7 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
   const RowState st = w.state[row];
   const int32_t n = (int32_t)st.n_cand;
   const int b = row / a.Hkv;
-  const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
+  const int32_t L = a.seq_lens ? clamp_len(a.seq_lens[b], a.max_len) : n;
   const float* xr = a.x + (int64_t)row * a.ldx;
   __shared__ uint32_t l4[kWaves];
   uint32_t eq_base = 0;
@@ -517,7 +518,7 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
 // counts selected candidates per (64-candidate wave slice) with ballots, then
 // one block scan over the slices gives every output position.
 // ---------------------------------------------------------------------------
-constexpr int kRowRegs = 64;
+constexpr int kRowRegs = 32;
 constexpr int kRowMax = 131072;
 constexpr int kRowRounds = kRowMax / kThreads;        // 128 slices per wave
 constexpr int kRowSlices = kRowRounds * kWaves;       // 2048 (round, wave) slices
@@ -533,7 +534,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t n = n_cand_of(a, row);
   const int b = row / a.Hkv;
-  const int32_t Lt = clamp_len(a.seq_lens[b], a.max_len);
+  const int32_t Lt = a.seq_lens ? clamp_len(a.seq_lens[b], a.max_len) : n;
   const float* xr = a.x + (int64_t)row * a.ldx;
   const int rounds = (n + kThreads - 1) / kThreads;
 
