@@ -384,6 +384,7 @@ sa_status sa_sparse_prefill(const sa_shape* s, const sa_pages* pg, int32_t n_tok
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
   if (b_sel != 64) return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 64", fn, b_sel);
   if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
+  if (cap > 2048) return fail(SA_ERR_UNSUPPORTED, "%s: cap=%d above 2048 listed keys", fn, cap);
   if (s->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "%s: head_dim must be 128", fn);
   return hip_status(sa::launch_sparse_prefill(to_shape(s), *pg, n_tokens, q, k_pool, v_pool, idx,
                                               count, cap, b_sel, s_att, out, out_dt, lse, st), fn);

@@ -125,10 +125,15 @@ k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
 // ---------------------------------------------------------------------------
 constexpr int kKT = 64;                 // keys per tile
 constexpr int kKPitch = 128 * 2 + 16;   // K tile row pitch in bytes (d = 128 bf16)
-constexpr int kVPitch = kKT * 2 + 16;   // V^T tile row pitch in bytes (64 keys bf16)
+constexpr int kVPitch = kKT * 2 + 8;    // V^T row pitch in bytes (64 keys bf16; 34 dwords)
+constexpr int kMaxListed = 2048;        // listed keys per block the attention kernel takes
 
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+// Two fp32 -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+  const bf16x2_t v = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int G>
@@ -161,6 +166,9 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 
   __shared__ __align__(16) char Ks[2][kKT * kKPitch];
   __shared__ __align__(16) char Vt[2][D * kVPitch];
+  // pool row (page * Hkv + g) * 64 + slot of every key the item visits, in
+  // tile order (listed keys, then the diagonal block); -1 marks padding
+  __shared__ int32_t rows_lds[kMaxListed + kKT];
 
   // Q as the B operand of S^T = K Q^T: Qb[nb][ks] holds query nb*32 + l32,
   // dims ks*16 + 8*half .. +7
@@ -177,30 +185,39 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     }
   }
 
-  const int64_t head_stride = (int64_t)kPage * D;
-  const int64_t page_stride = (int64_t)s.Hkv * head_stride;
-  auto key_of = [&](int tile, int r) -> int32_t {  // token index of tile row r, -1 if none
-    if (tile < n_list_tiles) {
-      const int32_t t = tile * kKT + r;
-      return t < nl ? list[t] : -1;
+  // resolve every key's pool row once (list entry -> page table -> row)
+  const int n_rows_total = n_list_tiles * kKT + kKT;
+  for (int t = tid; t < n_rows_total; t += NT) {
+    int32_t j = -1;
+    if (t < n_list_tiles * kKT) {
+      if (t < nl) j = list[t];
+    } else if (t - n_list_tiles * kKT < nq) {
+      j = q0 + (t - n_list_tiles * kKT);
     }
-    const int32_t kj = q0 + r;
-    return r < nq ? kj : -1;
-  };
+    int32_t rw = -1;
+    if (j >= 0) {
+      j = j >= N ? N - 1 : j;
+      const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+      rw = (int32_t)((page * s.Hkv + g) * kPage + (j & 63));
+    }
+    rows_lds[t] = rw;
+  }
+  __syncthreads();
+  // Gather: piece pc moves 16 bytes (8 head dims, chunk col = pc / 64) of
+  // key row r = pc % 64, so the 64 lanes of a wave hold one chunk of all 64
+  // keys: the transposed V^T stores of a wave then fill one LDS row.
   uint4 kr[LPT], vr[LPT];
   auto gather = [&](int tile) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int pc = i * NT + tid;
-      const int r = pc >> 4, col = pc & 15;
+      const int r = pc & 63, col = pc >> 6;
       kr[i] = make_uint4(0, 0, 0, 0);
       vr[i] = make_uint4(0, 0, 0, 0);
       if (pc < PIECES) {
-        int32_t j = key_of(tile, r);
-        if (j >= 0) {
-          j = j >= N ? N - 1 : j;
-          const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
-          const int64_t off = page * page_stride + g * head_stride + (int64_t)(j & 63) * D + col * 8;
+        const int32_t rw = rows_lds[tile * kKT + r];
+        if (rw >= 0) {
+          const int64_t off = (int64_t)rw * D + col * 8;
           kr[i] = *reinterpret_cast<const uint4*>(k_pool + off);
           vr[i] = *reinterpret_cast<const uint4*>(v_pool + off);
         }
@@ -212,7 +229,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     for (int i = 0; i < LPT; ++i) {
       const int pc = i * NT + tid;
       if (pc < PIECES) {
-        const int r = pc >> 4, col = pc & 15;
+        const int r = pc & 63, col = pc >> 6;
         *reinterpret_cast<uint4*>(Ks[buf] + r * kKPitch + col * 16) = kr[i];
         const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
 #pragma unroll
@@ -263,23 +280,28 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
       }
     }
     // online softmax per query (lane's query nb*32 + l32; keys spread over
-    // this lane's 32 accumulator values and the partner lane's)
+    // this lane's 32 accumulator values and the partner lane's).  Scores are
+    // scaled into log2 units inside the exponent's fused multiply-add.
+    const bool masked = diag || nt < kKT;
     float alpha[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int qloc = nb * 32 + l32;
+      if (masked) {
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kloc = mk * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+            if (!(kloc < nt && (!diag || kloc <= qloc))) S[mk][nb][v] = -INFINITY;
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int kloc = mk * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-          const bool ok = kloc < nt && (!diag || kloc <= qloc);
-          const float t = ok ? S[mk][nb][v] * sl2 : -INFINITY;
-          S[mk][nb][v] = t;
-          mt = fmaxf(mt, t);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, S[mk][nb][v]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
       const float m_new = fmaxf(m_run[nb], mt);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       float lt = 0.f;
@@ -287,21 +309,23 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
       for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-          const float p = exp2f(S[mk][nb][v] - m_use);
+          const float p = __builtin_amdgcn_exp2f(fmaf(S[mk][nb][v], sl2, -m_use));
           S[mk][nb][v] = p;
           lt += p;
         }
       lt += __shfl_xor(lt, 32, 64);
-      alpha[nb] = exp2f(m_run[nb] - m_use);
+      alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
       l_run[nb] = l_run[nb] * alpha[nb] + lt;
       m_run[nb] = m_new;
     }
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
+    }
     // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per step in the
     // accumulator's key order
 #pragma unroll

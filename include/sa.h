@@ -251,7 +251,8 @@ sa_status sa_select_prefill_topk(const sa_shape* shape, const sa_pages* pages,
  *   out[i][h] = sum_j softmax(s_att * q[i][h] . k_j) v_j,  lse[i][h] likewise.
  * Listed keys must precede the block.  q [n_tokens][n_q_heads][head_dim],
  * k_pool, v_pool of dtype (SA_BF16 only); out [n_tokens][n_q_heads][head_dim]
- * of out_dtype; lse [n_tokens][n_q_heads] fp32 or NULL.  b_sel must be 64.
+ * of out_dtype; lse [n_tokens][n_q_heads] fp32 or NULL.  b_sel must be 64,
+ * head_dim 128, cap <= 2048.
  * bf16 matrix-core products with fp32 accumulation and fp32 softmax. */
 sa_status sa_sparse_prefill(const sa_shape* shape, const sa_pages* pages, int32_t n_tokens,
                             const void* q, const void* k_pool, const void* v_pool,
