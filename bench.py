@@ -175,7 +175,17 @@ def bench_decode(args, name):
             ops.sa_index_scores(shape, pages, inp.q, inp.w_q, a, inp.s_idx, x, ws_idx)
             ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
 
+    use_step = not page_mode  # token-level selection: the library's whole-step call
+    if use_step:
+        ws_step = ops.alloc_workspace(ops.workspace_size(L.SA_OP_DECODE_STEP, shape, cap))
+    fused = use_step and rows <= 16 and inp.G >= 4
+
     def run_step(rep):
+        if use_step:
+            ops.sa_decode_step(shape, pages, inp.q, inp.w_q, rep[0], rep[1], rep[2], inp.s_idx,
+                               inp.s_att, sel.get("p", 0.0), 0, n_sink, n_window, x, idx, count,
+                               out, lse, ws_step)
+            return
         run_select(rep)
         ops.sa_sparse_decode(shape, pages, inp.q, rep[1], rep[2], idx, count, inp.s_att, out, lse,
                              ws_dec)
@@ -220,8 +230,12 @@ def bench_decode(args, name):
                                                         out, lse, ws_dec), args.steps, reps=R)
     comp = {"index_scores" if not page_mode else "page_scores": (t_index, index_bytes),
             "select": (t_select, 0), "sparse_decode": (t_decode, kv_bytes)}
-    dom = max((k for k in comp if comp[k][1] > 0), key=lambda k: comp[k][0])
-    dom_ms, dom_bytes = comp[dom]
+    if fused:
+        # the whole step is one kernel: its bytes are the step's
+        dom, dom_ms, dom_bytes = "decode_step (single fused launch)", ms, step_bytes
+    else:
+        dom = max((k for k in comp if comp[k][1] > 0), key=lambda k: comp[k][0])
+        dom_ms, dom_bytes = comp[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     gbs = step_bytes / (ms * 1e-3) / 1e9
     res = {
@@ -249,7 +263,9 @@ def bench_decode(args, name):
         "index_bytes": index_bytes,
         "kv_bytes": kv_bytes,
         "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
-        "breakdown_ms": {k: round(v[0], 5) for k, v in comp.items()},
+        "step_call": "sa_decode_step" + (" (fused)" if fused else "") if use_step else
+                     "sa_page_scores + sa_select_topk + sa_sparse_decode",
+        "separate_calls_ms": {k: round(v[0], 5) for k, v in comp.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,

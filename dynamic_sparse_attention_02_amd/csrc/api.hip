@@ -115,6 +115,16 @@ size_t decode_ws(const sa_shape* s, int64_t cap) {
     if (_st != SA_OK) return _st; \
   } while (0)
 
+// Decode-step workspace: room for the separate calls and for the fused
+// single-launch step (used when the problem has few rows).
+size_t step_ws(const sa_shape* s, int64_t cap) {
+  const size_t unfused = index_ws(s) + select_ws(s, s->max_len) + decode_ws(s, cap);
+  const int rows = s->batch * s->n_kv_heads;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const size_t fused = sa::align_up(sa::fused_workspace_bytes(rows, 256, G, s->head_dim), 256);
+  return unfused > fused ? unfused : fused;
+}
+
 int64_t topk_cap_needed(const sa_shape* s, int32_t k, int32_t unit, int32_t n_sink,
                         int32_t n_window) {
   int64_t need;
@@ -154,7 +164,7 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return sa::align_up(sa::prefill_select_workspace_bytes(sh, (int32_t)param), 256);
     }
     case SA_OP_DECODE_STEP:
-      return index_ws(s) + select_ws(s, s->max_len) + decode_ws(s, param);
+      return step_ws(s, param);
   }
   return 0;
 }
@@ -316,9 +326,14 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   if (cap < 1 || cap < cap_needed)
     return fail(SA_ERR_CAPACITY, "%s: cap=%d below the worst-case support %lld", fn, cap, (long long)cap_needed);
   const size_t w_i = index_ws(s), w_s = select_ws(s, s->max_len), w_d = decode_ws(s, cap);
-  SA_TRY(check_ws(ws, ws_bytes, w_i + w_s + w_d, fn));
+  SA_TRY(check_ws(ws, ws_bytes, step_ws(s, cap), fn));
   char* base = (char*)ws;
   const sa::Shape sh = to_shape(s);
+  int32_t nb = 0, tpb = 0;
+  if (sa::fused_plan(sh, n_sink, n_window, &nb, &tpb))
+    return hip_status(sa::launch_decode_fused(sh, *pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
+                                              s_att, p, top_k, n_sink, n_window, x, ldx, idx, count,
+                                              cap, out, out_dt, lse, ws, nb, tpb, st), fn);
   hipError_t e = sa::launch_index_scores(sh, *pg, q, w_q, kidx_pool, dt, s_idx, x, ldx, (float*)base, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};

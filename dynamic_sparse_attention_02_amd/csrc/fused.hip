@@ -1,0 +1,921 @@
+// Whole decode step in one persistent launch, for problems with few
+// (sequence, group) rows where a chain of separate launches would be latency
+// bound.  Same arithmetic as the separate calls: head-collapsed low-rank
+// indexer scores ("Full Attention Strikes Back", method section 2), top-p by
+// attention mass or top-k found by a radix histogram threshold (method
+// sections 3 and 5) with the sink/window tokens added (method section 1), and
+// exact softmax attention over the support ("Oracle-Guided Sparse Prefill",
+// section 2.1).
+//
+// Each row is served by NB co-resident workgroups, each owning a contiguous
+// range of the row's tokens.  They meet at per-row barriers (a counter in the
+// workspace, bounded spins that raise an error flag instead of waiting
+// forever):
+//   1. collapse the query, score the own tokens (kept in registers), publish
+//      the row maximum;                                          -- barrier
+//   2. per radix level: LDS histogram of the own tokens, flush non-empty bins
+//      to the row's global histogram;                           -- barrier
+//      every workgroup resolves the level from the same global histogram;
+//   3. own selected tokens (minus sink/window) plus an even share of the
+//      sink/window tokens are attended (split-KV partial per workgroup), the
+//      own selected count is published;                          -- barrier
+//   4. ordered write of the index list at the prefix of lower workgroups'
+//      counts, and each workgroup merges a slice of the row's outputs.
+// Histograms, the row maximum and the barrier counters are returned to zero
+// before the launch ends.
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kNT = 256;                  // threads per workgroup
+constexpr int kBinsF = 4096;              // 12-bit digits
+constexpr int kCoarseF = kBinsF / 64;
+constexpr int kTileF = 64;                // attention tile (tokens)
+constexpr uint32_t kSpinLimit = 1u << 20; // about a second of polling, then give up
+constexpr int kMaxNB = 256;
+
+enum : uint32_t { kSearch = 0, kGE = 1, kTies = 2 };
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2f_t;
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2f_t, a),
+                                          __builtin_bit_cast(bf16x2f_t, b), c, false);
+}
+
+struct RowWs {            // per-row control block (zero between launches)
+  uint32_t bar;           // barrier arrivals
+  uint32_t exit;          // workgroups done
+  uint32_t maxkey;        // row maximum score key
+  uint32_t pad[13];
+};
+
+struct FusedArgs {
+  const void* q;          // [B][Hq][D]
+  const void* w_q;        // [Hq][D][16]
+  const void* kidx;       // pool [P][Hkv][64][16]
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  Shape s;
+  float s_idx, s_att, p;
+  int32_t top_k, n_sink, n_window;
+  float* x;
+  int64_t ldx;
+  int32_t* idx;
+  int32_t* count;
+  int32_t cap;
+  void* out;
+  int32_t out_bf16;
+  float* lse;
+  int32_t nb;             // workgroups per row
+  int32_t tpb;            // tokens per workgroup (multiple of kNT)
+  // workspace
+  RowWs* ctl;             // [rows]
+  uint32_t* hcnt;         // [3][rows][kBinsF]
+  uint64_t* hmass;        // [3][rows][kBinsF]
+  uint32_t* ccnt;         // [3][rows][kCoarseF]
+  uint64_t* cmass;        // [3][rows][kCoarseF]
+  uint32_t* blk_sel;      // [rows][nb] selected tokens of each workgroup
+  uint32_t* blk_eq;       // [rows][nb] threshold ties of each workgroup
+  float* part_ml;         // [rows][nb][G][2]
+  float* part_o;          // [rows][nb][G][D]
+  uint32_t* err;          // set to 1 if a barrier gave up waiting
+  uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
+};
+
+constexpr int kTraceSlots = 16;
+
+// Phase timestamp of this workgroup (100 MHz constant clock), thread 0 only.
+__device__ __forceinline__ void stamp(const FusedArgs& a, int slot) {
+  if (threadIdx.x == 0) a.trace[(int64_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
+}
+
+// Per-row barrier: device-scope release before the arrival is counted and
+// acquire after it is observed, so every write of the other workgroups of the
+// row (histogram bins, counts, the row maximum, attention partials) is
+// visible afterwards.  The spin is bounded: a barrier that waits too long
+// raises the error flag and lets the launch finish instead of hanging.
+__device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __threadfence();
+    atomicAdd(ctr, 1u);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        atomicOr(err, 1u);
+        break;
+      }
+    }
+    __threadfence();
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename U>
+__device__ __forceinline__ U blk_scan(U v, U* lds, U& total) {  // exclusive, kNT threads
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  U inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    U y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) lds[w] = inc;
+  __syncthreads();
+  U off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kNT / 64; ++i) {
+    U s = lds[i];
+    if (i < w) off += s;
+    tot += s;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - v;
+}
+
+template <typename T, int D, int G, int TPT>
+__global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
+  constexpr int HPW = G / 4 > 0 ? G / 4 : 1;   // heads per wave (G >= 4)
+  constexpr int DPL = D / 64;
+  constexpr int ROWB = D * (int)sizeof(T);
+  constexpr int CPR = ROWB / 16;
+  constexpr int PITCH = ROWB + 16;
+  constexpr int LPT = kTileF * CPR / kNT;
+  const Shape& s = a.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int NB = a.nb;
+  const int row = blockIdx.x / NB, bi = blockIdx.x % NB;
+  const int rows = s.B * s.Hkv;
+  const int b = row / s.Hkv, g = row % s.Hkv;
+  const int32_t L = clamp_len(a.seq_lens[b], s.max_len);
+  const int32_t n = L;
+  const int32_t j0 = bi * a.tpb;
+  RowWs* ctl = a.ctl + row;
+  uint32_t bar_target = 0;
+
+  // ---- LDS ----
+  __shared__ float s_qc[kRank];
+  __shared__ float red_f[4][kRank];
+  __shared__ uint32_t red_u[4];
+  __shared__ uint64_t red_u64[4];
+  __shared__ uint32_t hcnt_l[kBinsF];
+  __shared__ uint64_t hmass_l[kBinsF];
+  __shared__ __align__(16) char Ks[kTileF * PITCH];
+  __shared__ __align__(16) char Vs[kTileF * PITCH];
+  __shared__ __align__(16) T Qs[G][D];
+  __shared__ __align__(16) float Ps[G][kTileF];
+  __shared__ int32_t my_list[TPT * kNT + 64];
+  __shared__ uint32_t s_mode, s_prefix, s_thr, s_neq, s_need, s_cnt;
+  __shared__ uint64_t s_rem;
+  __shared__ uint32_t s_slice[TPT * 4];
+
+  stamp(a, 0);
+  // ---- 1. scores of the own tokens ----
+  const T* kidx = (const T*)a.kidx;
+  const int32_t* pt = a.page_table + (int64_t)b * s.max_pages;
+  float xk[TPT];
+  uint32_t key[TPT];
+  {
+    // issue the indexer-key loads first, collapse the query while they fly
+    float kv[TPT][kRank];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      if (j < n) {
+        const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+        const T* rowp = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
+        if constexpr (sizeof(T) == 2) {
+          const uint4* v = reinterpret_cast<const uint4*>(rowp);
+          const uint4 x0 = v[0], x1 = v[1];
+          const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            kv[u][2 * i] = __uint_as_float(w8[i] << 16);
+            kv[u][2 * i + 1] = __uint_as_float(w8[i] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < kRank; ++i) kv[u][i] = to_f32<T>(rowp[i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRank; ++i) kv[u][i] = 0.f;
+      }
+    }
+    // head-collapsed query (same order of operations as k_collapse)
+    const T* q = (const T*)a.q;
+    const T* w_q = (const T*)a.w_q;
+    float acc[kRank];
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
+    for (int pi = tid; pi < G * D; pi += kNT) {
+      const int h = g * G + pi / D, i = pi % D;
+      const T* wr = w_q + ((int64_t)h * D + i) * kRank;
+      float w[kRank];
+      if constexpr (sizeof(T) == 2) {
+        const uint4* v = reinterpret_cast<const uint4*>(wr);
+        const uint4 x0 = v[0], x1 = v[1];
+        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          w[2 * k] = __uint_as_float(w8[k] << 16);
+          w[2 * k + 1] = __uint_as_float(w8[k] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < kRank; ++k) w[k] = to_f32<T>(wr[k]);
+      }
+      const float qv = to_f32<T>(q[((int64_t)b * s.Hq + h) * D + i]);
+#pragma unroll
+      for (int c = 0; c < kRank; ++c) acc[c] = fmaf(w[c], qv, acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) {
+      float v = acc[c];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+      if (lane == 0) red_f[wave][c] = v;
+    }
+    __syncthreads();
+    if (tid < kRank)
+      s_qc[tid] = ((red_f[0][tid] + red_f[1][tid]) + (red_f[2][tid] + red_f[3][tid])) * (a.s_idx / (float)G);
+    __syncthreads();
+    float qc[kRank];
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) qc[c] = s_qc[c];
+    uint32_t mk = 0;
+    float* xr = a.x + (int64_t)row * a.ldx;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      float acc1 = 0.f;
+#pragma unroll
+      for (int c = 0; c < kRank; ++c) acc1 = fmaf(qc[c], kv[u][c], acc1);
+      xk[u] = acc1;
+      key[u] = j < n ? score_key(acc1) : 0u;
+      if (j < n) {
+        xr[j] = acc1;
+        mk = key[u] > mk ? key[u] : mk;
+      }
+    }
+    mk = wave_max_u32(mk);
+    if (lane == 0) red_u[wave] = mk;
+    __syncthreads();
+    if (tid == 0) {
+      uint32_t m = 0;
+      for (int i = 0; i < 4; ++i) m = red_u[i] > m ? red_u[i] : m;
+      if (m) atomicMax(&ctl->maxkey, m);
+    }
+  }
+  stamp(a, 1);
+  bar_target += NB;
+  row_barrier(&ctl->bar, bar_target, a.err);
+  stamp(a, 2);
+
+  // ---- 2. threshold by radix levels ----
+  const bool topk = a.top_k > 0;
+  const uint32_t M = __hip_atomic_load(&ctl->maxkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const float mx = key_score(M);
+  if (tid == 0) {
+    s_mode = kSearch;
+    s_prefix = 0;
+    s_thr = 0;
+    s_neq = 0;
+    s_need = (uint32_t)a.top_k;
+    s_rem = 0;
+    if (n == 0 || (topk ? (a.top_k >= n) : (a.p >= 1.0f))) s_mode = kGE;
+  }
+  __syncthreads();
+  for (int level = 1; level <= 3; ++level) {
+    if (s_mode != kSearch) break;  // same decision in every workgroup of the row
+    const int NBIN = level == 3 ? 256 : kBinsF;
+    const int NC = NBIN / 64;
+    const uint32_t pre = s_prefix;
+    const int li = level - 1;
+    uint32_t* gc = a.hcnt + ((int64_t)li * rows + row) * kBinsF;
+    uint64_t* gm = a.hmass + ((int64_t)li * rows + row) * kBinsF;
+    uint32_t* gcc = a.ccnt + ((int64_t)li * rows + row) * kCoarseF;
+    uint64_t* gcm = a.cmass + ((int64_t)li * rows + row) * kCoarseF;
+    if (level == 1) {
+      // every token lands in this level: aggregate in LDS, flush non-empty bins
+      for (int i = tid; i < NBIN; i += kNT) {
+        hcnt_l[i] = 0;
+        hmass_l[i] = 0;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int32_t j = j0 + u * kNT + tid;
+        if (j >= n) continue;
+        const uint32_t digit = key[u] >> 20;
+        atomicAdd(&hcnt_l[digit], 1u);
+        if (!topk) {
+          const float e = __expf(xk[u] - mx);
+          atomicAdd((unsigned long long*)&hmass_l[digit], (unsigned long long)(e * 1099511627776.0f));
+        }
+      }
+      __syncthreads();
+      for (int cg = wave; cg < NC; cg += 4) {
+        const int bin = cg * 64 + lane;
+        const uint32_t cn = hcnt_l[bin];
+        const uint64_t ms = hmass_l[bin];
+        if (cn) {
+          atomicAdd(&gc[bin], cn);
+          if (!topk) atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
+        }
+        uint32_t csum = cn;
+        uint64_t msum = ms;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+          csum += __shfl_xor(csum, o, 64);
+          msum += __shfl_xor(msum, o, 64);
+        }
+        if (lane == 0 && csum) {
+          atomicAdd(&gcc[cg], csum);
+          if (!topk) atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
+        }
+      }
+    } else {
+      // only the tokens of the previous level's crossing bin: few, spread
+      // over the digits, so they go straight to the row's histogram
+#pragma unroll
+      for (int u = 0; u < TPT; ++u) {
+        const int32_t j = j0 + u * kNT + tid;
+        if (j >= n) continue;
+        const uint32_t k = key[u];
+        const bool match = level == 2 ? (k >> 20) == pre : (k >> 8) == pre;
+        if (!match) continue;
+        const uint32_t digit = level == 2 ? ((k >> 8) & 0xfffu) : (k & 0xffu);
+        atomicAdd(&gc[digit], 1u);
+        atomicAdd(&gcc[digit >> 6], 1u);
+        if (!topk) {
+          const uint64_t e = (uint64_t)(__expf(xk[u] - mx) * 1099511627776.0f);
+          atomicAdd((unsigned long long*)&gm[digit], (unsigned long long)e);
+          atomicAdd((unsigned long long*)&gcm[digit >> 6], (unsigned long long)e);
+        }
+      }
+    }
+    stamp(a, 3 * level);
+    bar_target += NB;
+    row_barrier(&ctl->bar, bar_target, a.err);
+    stamp(a, 3 * level + 1);
+    // resolve (wave 0): coarse groups, then the 64 bins of the crossing group
+    if (wave == 0) {
+      const int cgi = NC - 1 - lane;
+      const uint32_t cc = lane < NC ? __hip_atomic_load(&gcc[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+      const uint64_t cm = (!topk && lane < NC) ? __hip_atomic_load(&gcm[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      uint32_t cinc = cc;
+      uint64_t minc = cm;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(cinc, o, 64);
+        const uint64_t z = __shfl_up(minc, o, 64);
+        if (lane >= o) {
+          cinc += y;
+          minc += z;
+        }
+      }
+      const uint64_t mtot = __shfl(minc, 63, 64);
+      uint64_t target = s_rem;
+      if (!topk && level == 1) {
+        uint64_t tc = (uint64_t)ceil((double)a.p * (double)mtot);
+        if (tc < 1) tc = 1;
+        if (tc > mtot) tc = mtot;
+        target = tc;
+      }
+      const uint32_t need = s_need;
+      const uint32_t cbef = cinc - cc;
+      const uint64_t mbef = minc - cm;
+      const bool hit = lane < NC && (!topk ? (mbef < target && minc >= target) : (cbef < need && cinc >= need));
+      const unsigned long long hb = __ballot(hit);
+      int found = -1;
+      uint32_t g_cb = 0;
+      uint64_t g_mb = 0;
+      if (hb) {
+        const int src = __ffsll(hb) - 1;
+        found = __shfl(cgi, src, 64);
+        g_cb = __shfl(cbef, src, 64);
+        g_mb = __shfl(mbef, src, 64);
+      }
+      uint32_t bc = 0;
+      uint64_t bm = 0;
+      int bin = -1;
+      if (found >= 0) {
+        bin = found * 64 + 63 - lane;
+        bc = __hip_atomic_load(&gc[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        bm = !topk ? __hip_atomic_load(&gm[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+      }
+      uint32_t binc = bc;
+      uint64_t bminc = bm;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(binc, o, 64);
+        const uint64_t z = __shfl_up(bminc, o, 64);
+        if (lane >= o) {
+          binc += y;
+          bminc += z;
+        }
+      }
+      const uint32_t bcb = g_cb + binc - bc;
+      const uint64_t bmb = g_mb + bminc - bm;
+      const bool hit2 = found >= 0 && (!topk ? (bmb < target && bmb + bm >= target)
+                                             : (bcb < need && bcb + bc >= need));
+      const unsigned long long hb2 = __ballot(hit2);
+      if (!hb2) {
+        if (lane == 0) {
+          s_mode = kGE;  // inconsistent histogram (cannot happen): take everything
+          s_thr = 0;
+        }
+      } else if (lane == __ffsll(hb2) - 1) {
+        const uint32_t np = level == 1 ? (uint32_t)bin
+                                       : (level == 2 ? ((pre << 12) | (uint32_t)bin) : ((pre << 8) | (uint32_t)bin));
+        const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+        const uint32_t bin_lo = np << shift;
+        if (!topk) {
+          const uint64_t rem = target - bmb;
+          if (level < 3) {
+            if (bc == 1 || rem == bm) {
+              s_mode = kGE;
+              s_thr = bin_lo;
+            } else {
+              s_prefix = np;
+              s_rem = rem;
+            }
+          } else {
+            const uint64_t m1 = bm / bc;
+            const uint64_t take = (rem + m1 - 1) / m1;
+            s_thr = bin_lo;
+            if (take >= bc) {
+              s_mode = kGE;
+            } else {
+              s_mode = kTies;
+              s_neq = (uint32_t)take;
+            }
+          }
+        } else {
+          const uint32_t nd = need - bcb;
+          if (nd == bc) {
+            s_mode = kGE;
+            s_thr = bin_lo;
+          } else if (level < 3) {
+            s_prefix = np;
+            s_need = nd;
+          } else {
+            s_mode = kTies;
+            s_thr = bin_lo;
+            s_neq = nd;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  stamp(a, 11);
+  // ---- 3. own selection, attention over it (plus a share of sink/window) ----
+  const uint32_t mode = s_mode, thr = s_thr, neq = s_neq;
+  uint32_t eq_before = 0;
+  if (mode == kTies) {  // ties left out: rank the threshold ties across workgroups
+    uint32_t e = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) e += (j0 + u * kNT + tid < n && key[u] == thr) ? 1u : 0u;
+    uint32_t tot;
+    blk_scan<uint32_t>(e, red_u, tot);
+    if (tid == 0) __hip_atomic_store(&a.blk_eq[(int64_t)row * NB + bi], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bar_target += NB;
+    row_barrier(&ctl->bar, bar_target, a.err);
+    {
+      uint32_t vb = 0;
+      for (int k = tid; k < bi; k += kNT)
+        vb += __hip_atomic_load(&a.blk_eq[(int64_t)row * NB + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      uint32_t tb;
+      blk_scan<uint32_t>(vb, red_u, tb);
+      if (tid == 0) s_cnt = tb;
+      __syncthreads();
+    }
+    eq_before = s_cnt;
+  }
+  // selection flags in index order (round u, wave, lane) and the own list
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  uint32_t selmask[TPT];  // bit 0: selected, bit 1: forced
+  {
+    uint32_t eq_run = eq_before;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      const bool valid = j < n;
+      bool top = valid && (mode == kTies ? key[u] > thr : key[u] >= thr);
+      if (mode == kTies) {
+        const bool eq = valid && key[u] == thr;
+        const uint64_t m = __ballot(eq);
+        if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
+        __syncthreads();
+        uint32_t before = eq_run;
+        for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
+        uint32_t round_tot = 0;
+        for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
+        if (eq) top = (before + (uint32_t)__popcll(m & lt_mask)) < neq;
+        eq_run += round_tot;
+        __syncthreads();
+      }
+      const bool forced = valid && (j < a.n_sink || j >= n - a.n_window);
+      selmask[u] = (top || forced ? 1u : 0u) | (forced ? 2u : 0u);
+    }
+  }
+  // own non-forced selected tokens -> LDS list (order irrelevant for attention)
+  uint32_t my_sel = 0;
+  {
+    uint32_t cnt_nf = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      my_sel += selmask[u] & 1u;
+      cnt_nf += (selmask[u] == 1u) ? 1u : 0u;
+    }
+    uint32_t tot_nf;
+    const uint32_t off = blk_scan<uint32_t>(cnt_nf, red_u, tot_nf);
+    uint32_t o = off;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+      if (selmask[u] == 1u) my_list[o++] = j0 + u * kNT + tid;
+    uint32_t tot_sel;
+    blk_scan<uint32_t>(my_sel, red_u, tot_sel);
+    // share of the forced tokens: the union of [0, n_sink) and
+    // [n - n_window, n), enumerated in index order and split evenly
+    const int32_t s_end = min(a.n_sink, n);
+    const int32_t w_beg = max(s_end, n - a.n_window);
+    const int32_t nf = s_end + (n - w_beg);
+    const int32_t f0 = (int32_t)(((int64_t)nf * bi) / NB), f1 = (int32_t)(((int64_t)nf * (bi + 1)) / NB);
+    for (int32_t f = f0 + tid; f < f1; f += kNT) {
+      const int32_t j = f < s_end ? f : w_beg + (f - s_end);
+      my_list[tot_nf + (f - f0)] = j;
+    }
+    if (tid == 0) {
+      s_cnt = tot_nf + (uint32_t)(f1 - f0);
+      __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], tot_sel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+  }
+  const int32_t n_att = (int32_t)s_cnt;
+  {
+    const T* k_pool = (const T*)a.k_pool;
+    const T* v_pool = (const T*)a.v_pool;
+    const T* q = (const T*)a.q;
+    for (int i = tid; i < G * D; i += kNT) Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
+    const int64_t head_stride = (int64_t)kPage * D;
+    const int64_t page_stride = (int64_t)s.Hkv * head_stride;
+    float m_run[HPW], l_run[HPW], acc[HPW][DPL];
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      m_run[hh] = -INFINITY;
+      l_run[hh] = 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.f;
+    }
+    uint4 kr[LPT], vr[LPT];
+    auto gather = [&](int32_t ts) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = i * kNT + tid;
+        const int r = pc / CPR, col = pc % CPR;
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+        if (ts + r < n_att) {
+          const int32_t j = my_list[ts + r];
+          const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+          const int64_t off = page * page_stride + g * head_stride + (int64_t)(j & 63) * D;
+          kr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + off) + col * 16);
+          vr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + off) + col * 16);
+        }
+      }
+    };
+    if (n_att > 0) gather(0);
+    for (int32_t ts = 0; ts < n_att; ts += kTileF) {
+      const int32_t nt = min(kTileF, n_att - ts);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = i * kNT + tid;
+        const int r = pc / CPR, col = pc % CPR;
+        *reinterpret_cast<uint4*>(Ks + r * PITCH + col * 16) = kr[i];
+        *reinterpret_cast<uint4*>(Vs + r * PITCH + col * 16) = vr[i];
+      }
+      __syncthreads();
+      if (ts + kTileF < n_att) gather(ts + kTileF);
+      float sc[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) sc[hh] = 0.f;
+      const char* krow = Ks + lane * PITCH;
+#pragma unroll 4
+      for (int pc = 0; pc < CPR; ++pc) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + pc * 16);
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) {
+          const int h = wave * HPW + hh;
+          if constexpr (sizeof(T) == 2) {
+            const uint4 qv = *reinterpret_cast<const uint4*>(&Qs[h][pc * 8]);
+            float t = sc[hh];
+            t = dot2(kv.x, qv.x, t);
+            t = dot2(kv.y, qv.y, t);
+            t = dot2(kv.z, qv.z, t);
+            t = dot2(kv.w, qv.w, t);
+            sc[hh] = t;
+          } else {
+            const float4 qv = *reinterpret_cast<const float4*>(&Qs[h][pc * 4]);
+            float t = sc[hh];
+            t = fmaf(__uint_as_float(kv.x), qv.x, t);
+            t = fmaf(__uint_as_float(kv.y), qv.y, t);
+            t = fmaf(__uint_as_float(kv.z), qv.z, t);
+            t = fmaf(__uint_as_float(kv.w), qv.w, t);
+            sc[hh] = t;
+          }
+        }
+      }
+      float alpha[HPW];
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float sv = lane < nt ? sc[hh] * a.s_att : -INFINITY;
+        const float mt = wave_max(sv);
+        const float m_new = fmaxf(m_run[hh], mt);
+        const float pv = lane < nt ? __expf(sv - m_new) : 0.f;
+        const float lt = wave_sum(pv);
+        alpha[hh] = __expf(m_run[hh] - m_new);
+        l_run[hh] = l_run[hh] * alpha[hh] + lt;
+        m_run[hh] = m_new;
+        Ps[wave * HPW + hh][lane] = pv;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) acc[hh][e] *= alpha[hh];
+      for (int t = 0; t < kTileF; t += 4) {
+        float4 pv4[HPW];
+#pragma unroll
+        for (int hh = 0; hh < HPW; ++hh) pv4[hh] = *reinterpret_cast<const float4*>(&Ps[wave * HPW + hh][t]);
+#pragma unroll
+        for (int uu = 0; uu < 4; ++uu) {
+          float vv[DPL];
+          const char* vrow = Vs + (t + uu) * PITCH;
+          if constexpr (sizeof(T) == 2) {
+            if constexpr (DPL == 2) {
+              const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + lane * 4);
+              vv[0] = __uint_as_float(w << 16);
+              vv[1] = __uint_as_float(w & 0xffff0000u);
+            } else {
+              const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + lane * 2);
+              vv[0] = __uint_as_float((uint32_t)w << 16);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) vv[e] = *reinterpret_cast<const float*>(vrow + (lane * DPL + e) * 4);
+          }
+#pragma unroll
+          for (int hh = 0; hh < HPW; ++hh) {
+            const float pp = uu == 0 ? pv4[hh].x : (uu == 1 ? pv4[hh].y : (uu == 2 ? pv4[hh].z : pv4[hh].w));
+#pragma unroll
+            for (int e = 0; e < DPL; ++e) acc[hh][e] = fmaf(pp, vv[e], acc[hh][e]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPW; ++hh) {
+      const int hl = wave * HPW + hh;
+      const int64_t pi = ((int64_t)row * NB + bi) * G + hl;
+      if (lane == 0) {
+        st_dev(&a.part_ml[pi * 2], m_run[hh]);
+        st_dev(&a.part_ml[pi * 2 + 1], l_run[hh]);
+      }
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) st_dev(&a.part_o[pi * D + lane * DPL + e], acc[hh][e]);
+    }
+  }
+  stamp(a, 12);
+  bar_target += NB;
+  row_barrier(&ctl->bar, bar_target, a.err);
+  stamp(a, 13);
+
+  // ---- 4. ordered index list and the merge of this workgroup's output slice ----
+  {
+    __shared__ uint32_t s_base, s_total;
+    {
+      uint32_t vb = 0, vt = 0;
+      for (int k = tid; k < NB; k += kNT) {
+        const uint32_t v = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        vt += v;
+        if (k < bi) vb += v;
+      }
+      uint32_t tb, tt;
+      blk_scan<uint32_t>(vb, red_u, tb);
+      blk_scan<uint32_t>(vt, red_u, tt);
+      if (tid == 0) {
+        s_base = tb;
+        s_total = tt;
+      }
+      __syncthreads();
+    }
+    int32_t* outl = a.idx + (int64_t)row * a.cap;
+    uint32_t run = s_base;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const bool sel = selmask[u] & 1u;
+      const uint64_t m = __ballot(sel);
+      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
+      __syncthreads();
+      uint32_t before = run;
+      for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
+      uint32_t round_tot = 0;
+      for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
+      if (sel) {
+        const uint32_t pos = before + (uint32_t)__popcll(m & lt_mask);
+        if (pos < (uint32_t)a.cap) outl[pos] = j0 + u * kNT + tid;
+      }
+      run += round_tot;
+      __syncthreads();
+    }
+    const uint32_t total = s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap;
+    const int64_t pad = (int64_t)a.cap - total;
+    const int64_t p0 = total + (pad * bi) / NB, p1 = total + (pad * (bi + 1)) / NB;
+    for (int64_t o = p0 + tid; o < p1; o += kNT) outl[o] = -1;
+    if (bi == 0 && tid == 0) a.count[row] = (int32_t)total;
+    // outputs [bi * opb, (bi + 1) * opb) of the row's G * D values
+    const int n_out = G * D;
+    const int opb = (n_out + NB - 1) / NB;
+    const int o0 = bi * opb;
+    const int lim = min(n_out, o0 + opb);
+    for (int ob = o0; ob < lim; ob += kNT / 16) {
+      // 16 threads per output, each taking every 16th partial
+      const int oo = ob + tid / 16;
+      const int sub = tid % 16;
+      if (oo >= lim) continue;  // whole 16-lane groups skip together
+      const int hl = oo / D, d = oo % D;
+      float M2 = -INFINITY;
+      for (int k = sub; k < NB; k += 16) M2 = fmaxf(M2, ld_dev(&a.part_ml[(((int64_t)row * NB + k) * G + hl) * 2]));
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) M2 = fmaxf(M2, __shfl_xor(M2, o, 16));
+      float lsum = 0.f, osum = 0.f;
+      for (int k = sub; k < NB; k += 16) {
+        const int64_t pi = ((int64_t)row * NB + k) * G + hl;
+        const float mk2 = ld_dev(&a.part_ml[pi * 2]);
+        const float wgt = mk2 == -INFINITY ? 0.f : __expf(mk2 - M2);
+        lsum += ld_dev(&a.part_ml[pi * 2 + 1]) * wgt;
+        osum += ld_dev(&a.part_o[pi * D + d]) * wgt;
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        lsum += __shfl_xor(lsum, o, 16);
+        osum += __shfl_xor(osum, o, 16);
+      }
+      if (sub == 0) {
+        const int h = g * G + hl;
+        const float v = lsum > 0.f ? osum / lsum : 0.f;
+        if (a.out_bf16) ((bf16_raw*)a.out)[((int64_t)b * s.Hq + h) * D + d] = f32_to_bf16(v);
+        else ((float*)a.out)[((int64_t)b * s.Hq + h) * D + d] = v;
+        if (d == 0 && a.lse) a.lse[(int64_t)b * s.Hq + h] = lsum > 0.f ? M2 + logf(lsum) : -INFINITY;
+      }
+    }
+  }
+
+  stamp(a, 14);
+  // ---- clean-up for the next launch: histograms, maximum, counters ----
+  {
+    const int per = (kBinsF + NB - 1) / NB;
+    for (int li = 0; li < 3; ++li) {
+      uint32_t* gc = a.hcnt + ((int64_t)li * rows + row) * kBinsF;
+      uint64_t* gm = a.hmass + ((int64_t)li * rows + row) * kBinsF;
+      for (int i = bi * per + tid; i < min(kBinsF, (bi + 1) * per); i += kNT) {
+        gc[i] = 0;
+        gm[i] = 0;
+      }
+      if (bi == 0 && tid < kCoarseF) {
+        a.ccnt[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
+        a.cmass[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      __threadfence();
+      const uint32_t old = atomicAdd(&ctl->exit, 1u);
+      if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
+        ctl->maxkey = 0;
+        ctl->bar = 0;
+        ctl->exit = 0;
+        __threadfence();
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// Workspace of the fused step; rows * nb workgroups, G heads, D dims.
+size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
+  size_t b = 0;
+  b += align_up(sizeof(RowWs) * rows, 256);
+  b += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
+  b += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
+  b += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
+  b += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
+  b += 2 * align_up(sizeof(uint32_t) * rows * nb, 256);
+  b += align_up(sizeof(float) * rows * nb * G * 2, 256);
+  b += align_up(sizeof(float) * rows * nb * G * D, 256);
+  b += 256;  // error flag
+  b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
+  return b;
+}
+
+// Plan: workgroups per row and tokens per workgroup, or false if the fused
+// step does not apply (too many rows, rows too long, group size < 4).
+bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, int32_t* tpb) {
+  const int rows = s.B * s.Hkv;
+  const int G = s.Hq / s.Hkv;
+  if (G < 4 || rows > 16 || s.max_len < 1) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return false;
+  int n_b = cus / rows;  // one workgroup per compute unit
+  if (n_b > kMaxNB) n_b = kMaxNB;
+  if (n_b < 1) return false;
+  // tokens per workgroup: a power-of-two number of kNT rounds, at most 16
+  const int32_t per = (s.max_len + n_b - 1) / n_b;
+  int32_t rounds = 1;
+  while (rounds * kNT < per) rounds *= 2;
+  if (rounds > 16) return false;
+  // each workgroup's share of the sink/window tokens must fit its list
+  const int64_t forced = (int64_t)n_sink + n_window;
+  if ((forced + n_b - 1) / n_b > 64) return false;
+  *nb = n_b;
+  *tpb = rounds * kNT;
+  return true;
+}
+
+hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q, const void* w_q,
+                               const void* kidx_pool, const void* k_pool, const void* v_pool,
+                               sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
+                               int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
+                               int32_t* idx, int32_t* count, int32_t cap, void* out,
+                               sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
+                               hipStream_t st) {
+  const int rows = s.B * s.Hkv;
+  const int G = s.Hq / s.Hkv;
+  FusedArgs a{};
+  a.q = q; a.w_q = w_q; a.kidx = kidx_pool; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.page_table = pg.page_table; a.seq_lens = pg.seq_lens; a.s = s;
+  a.s_idx = s_idx; a.s_att = s_att; a.p = p; a.top_k = top_k; a.n_sink = n_sink;
+  a.n_window = n_window; a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
+  a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
+  char* w = (char*)ws;
+  a.ctl = (RowWs*)w;            w += align_up(sizeof(RowWs) * rows, 256);
+  a.hcnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
+  a.hmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
+  a.ccnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
+  a.cmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
+  a.blk_sel = (uint32_t*)w;     w += align_up(sizeof(uint32_t) * rows * nb, 256);
+  a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
+  a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
+  a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * s.D, 256);
+  a.err = (uint32_t*)w;           w += 256;
+  a.trace = (uint64_t*)w;
+  const int tpt = tpb / kNT;  // 1, 2, 4, 8 or 16 (fused_plan)
+  dim3 grid(rows * nb);
+#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP><<<grid, kNT, 0, st>>>(a)
+#define SA_FZ_T(TT, DD, GG)              \
+  switch (tpt) {                         \
+    case 1: SA_FZ(TT, DD, GG, 1); break;  \
+    case 2: SA_FZ(TT, DD, GG, 2); break;  \
+    case 4: SA_FZ(TT, DD, GG, 4); break;  \
+    case 8: SA_FZ(TT, DD, GG, 8); break;  \
+    default: SA_FZ(TT, DD, GG, 16); break; \
+  }
+#define SA_FZ_G(TT, DD)                       \
+  switch (G) {                                \
+    case 4: SA_FZ_T(TT, DD, 4); break;        \
+    case 8: SA_FZ_T(TT, DD, 8); break;        \
+    default: SA_FZ_T(TT, DD, 16); break;      \
+  }
+  if (dt == SA_BF16) {
+    if (s.D == 128) { SA_FZ_G(bf16_raw, 128); } else { SA_FZ_G(bf16_raw, 64); }
+  } else {
+    if (s.D == 128) { SA_FZ_G(float, 128); } else { SA_FZ_G(float, 64); }
+  }
+#undef SA_FZ_G
+#undef SA_FZ_T
+#undef SA_FZ
+  return hipGetLastError();
+}
+
+}  // namespace sa
