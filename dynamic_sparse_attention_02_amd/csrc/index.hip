@@ -215,60 +215,98 @@ hipError_t launch_page_stats(const Shape& s, const void* k_pool, sa_dtype dt,
 }
 
 // ---------------------------------------------------------------------------
-// Taylor page scores.  One wave per page: lane l holds D/64 dimensions of the
-// page's mean and variance rows; for each head of the group the two dot
-// products q'.mean and q'^2.var are reduced across the wave.
+// Taylor page scores.  A page's statistics row (mean then variance, 2*D
+// values) is spread over D/8 lanes holding 8 dimensions each (16-byte loads
+// for bf16), so a wave covers 512/D pages per load instruction; four rounds
+// are issued before any is used.  For each head of the group the two dot
+// products q'.mean and q'^2.var are reduced over the page's lanes.
 //   x = mean_h [ q'_h.mean + log1p(0.5 * q'_h^2.var) ] + log(n / page)
 // ---------------------------------------------------------------------------
-constexpr int kPagesPerBlock = 16;  // 4 waves x 4 pages each
+constexpr int kPSRounds = 4;
+
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_raw>(const bf16_raw* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
               const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
               Shape s, float s_att, float* __restrict__ x, int64_t ldx) {
-  constexpr int DPL = D / kWave;  // dims per lane
+  constexpr int LPP = D / 8;            // lanes per page
+  constexpr int PPW = kWave / LPP;      // pages per wave and round
+  constexpr int PPB = 4 * PPW * kPSRounds;
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LPP, slot = lane / LPP;
   const int32_t L = clamp_len(seq_lens[b], s.max_len);
   const int32_t n_pages = (L + kPage - 1) / kPage;
-  const int32_t p0 = blockIdx.x * kPagesPerBlock;
+  const int32_t p0 = blockIdx.x * PPB;
   if (p0 >= n_pages) return;
-  // scaled query of the group's heads, this lane's dimensions
-  float qp[G][DPL];
+  // scaled query of the group's heads, this lane's 8 dimensions
+  float qp[G][8];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+  for (int h = 0; h < G; ++h) {
+    float v[8];
+    load8<T>(q + ((int64_t)b * s.Hq + g * G + h) * D + sub * 8, v);
 #pragma unroll
-    for (int e = 0; e < DPL; ++e)
-      qp[h][e] = s_att * to_f32<T>(q[((int64_t)b * s.Hq + g * G + h) * D + lane * DPL + e]);
+    for (int e = 0; e < 8; ++e) qp[h][e] = s_att * v[e];
+  }
   const int32_t* pt = page_table + (int64_t)b * s.max_pages;
-  for (int pp = wave; pp < kPagesPerBlock; pp += 4) {
-    const int32_t p = p0 + pp;
-    if (p >= n_pages) break;
-    const int64_t page = clamp_page(pt[p], s.n_pool_pages);
-    const T* row = stats + (page * s.Hkv + g) * 2 * (int64_t)D;
-    float mu[DPL], va[DPL];
+  float mu[kPSRounds][8], va[kPSRounds][8];
+  int32_t pg[kPSRounds];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) {
-      mu[e] = to_f32<T>(row[lane * DPL + e]);
-      va[e] = to_f32<T>(row[D + lane * DPL + e]);
+  for (int r = 0; r < kPSRounds; ++r) {
+    pg[r] = p0 + (r * 4 + wave) * PPW + slot;
+    if (pg[r] < n_pages) {
+      const int64_t page = clamp_page(pt[pg[r]], s.n_pool_pages);
+      const T* row = stats + (page * s.Hkv + g) * 2 * (int64_t)D;
+      load8<T>(row + sub * 8, mu[r]);
+      load8<T>(row + D + sub * 8, va[r]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        mu[r][e] = 0.f;
+        va[r][e] = 0.f;
+      }
     }
+  }
+#pragma unroll
+  for (int r = 0; r < kPSRounds; ++r) {
     float acc = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float a = 0.f, c = 0.f;
+      float a1 = 0.f, c1 = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        a = fmaf(qp[h][e], mu[e], a);
-        c = fmaf(qp[h][e] * qp[h][e], va[e], c);
+      for (int e = 0; e < 8; ++e) {
+        a1 = fmaf(qp[h][e], mu[r][e], a1);
+        c1 = fmaf(qp[h][e] * qp[h][e], va[r][e], c1);
       }
-      a = wave_sum(a);
-      c = wave_sum(c);
-      acc += a + log1pf(0.5f * c);
+#pragma unroll
+      for (int o = LPP / 2; o > 0; o >>= 1) {
+        a1 += __shfl_xor(a1, o, LPP);
+        c1 += __shfl_xor(c1, o, LPP);
+      }
+      acc += a1 + log1pf(0.5f * c1);
     }
-    if (lane == 0) {
-      const int nv = (L - p * kPage) < kPage ? (L - p * kPage) : kPage;
-      x[((int64_t)b * s.Hkv + g) * ldx + p] = acc / (float)G + logf((float)nv / (float)kPage);
+    if (sub == 0 && pg[r] < n_pages) {
+      const int nv = (L - pg[r] * kPage) < kPage ? (L - pg[r] * kPage) : kPage;
+      x[((int64_t)b * s.Hkv + g) * ldx + pg[r]] = acc / (float)G + logf((float)nv / (float)kPage);
     }
   }
 }
@@ -277,7 +315,8 @@ template <typename T, int D>
 static void page_scores_g(const Shape& s, const sa_pages& pg, const void* q, const void* st_pool,
                           float s_att, float* x, int64_t ldx, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
-  dim3 grid((s.max_pages + kPagesPerBlock - 1) / kPagesPerBlock, s.Hkv, s.B);
+  constexpr int PPB = 4 * (kWave / (D / 8)) * kPSRounds;
+  dim3 grid((s.max_pages + PPB - 1) / PPB, s.Hkv, s.B);
 #define SA_PS(GG)                                                                          \
   k_page_scores<T, D, GG><<<grid, 256, 0, st>>>((const T*)q, (const T*)st_pool,           \
                                                 pg.page_table, pg.seq_lens, s, s_att, x, ldx)

@@ -821,9 +821,10 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
 
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
-  // One block per row when there are enough rows to fill the chip; few long
-  // rows are split over many blocks instead.
-  if (a.max_cand <= kRowMax && a.rows >= 32) {
+  // One block per row when a row's keys fit in one block's registers, or
+  // when there are enough rows to fill the chip; few long rows are split
+  // over many blocks instead.
+  if (a.max_cand <= kRowRegs * kThreads || (a.max_cand <= kRowMax && a.rows >= 32)) {
     if (a.is_topk) k_select_row<false><<<a.rows, kThreads, 0, st>>>(a);
     else k_select_row<true><<<a.rows, kThreads, 0, st>>>(a);
     return hipGetLastError();

@@ -203,10 +203,12 @@ def test_select_golden(case):
     assert got.tolist() == expect
 
 
-def test_select_exact_ties_across_chunks():
-    n = 9000
+@pytest.mark.parametrize("n", [9000, 40000])
+def test_select_exact_ties_across_chunks(n):
+    """n = 9000: one block per row; n = 40000: a row split over several
+    blocks (more candidates than one block keeps in registers)."""
     x = np.zeros(n, dtype=np.float32)
-    big = [5, 4000, 8999]
+    big = [5, 4000, n - 1]
     x[big] = 3.0
     # top-k threshold falls inside the tie group of zeros that spans chunks
     got = _select_rows([x], [n], k=2503)[0]
@@ -219,10 +221,12 @@ def test_select_exact_ties_across_chunks():
     assert got.tolist() == list(range(100))
 
 
-@pytest.mark.parametrize("seed", [0, 1, 2])
-def test_select_random_ragged(seed):
+@pytest.mark.parametrize("seed,long", [(0, False), (1, False), (2, False), (3, True)])
+def test_select_random_ragged(seed, long):
+    """Ragged rows; with long=True a 40000-candidate row sends every row of
+    the call through the multi-block selection."""
     rng = np.random.default_rng(seed)
-    lens = [1, 63, 700, 2049, 5000]
+    lens = [1, 63, 700, 2049, 5000] + ([40000] if long else [])
     rows = [(rng.standard_normal(L) * 3).astype(np.float32) for L in lens]
     for rule in ({"p": S.f32(0.9)}, {"p": S.f32(0.5)}, {"k": 50}, {"k": 1}):
         for sink, win in ((0, 0), (4, 16)):
