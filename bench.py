@@ -61,12 +61,13 @@ def _events():
 def time_loop(fn, n, warmup=3, reps=1):
     """Average device milliseconds per call of fn(i).
 
-    The calls fn(0) .. fn(reps-1) (one per input replica) are captured once
-    into a HIP graph on a side stream (every library call launches on the
-    current stream), and the graph is replayed until n calls have run, timed
-    with HIP events on that stream: the figure excludes Python and launch
-    overhead between calls, not the gaps between kernels inside a call."""
+    At least 16 calls fn(i % reps) (rotating over the input replicas) are
+    captured once into a HIP graph on a side stream (every library call
+    launches on the current stream), and the graph is replayed until n calls
+    have run, timed with HIP events on that stream: the figure excludes Python
+    and graph-launch overhead between calls, not the gaps between kernels."""
     import torch
+    per_graph = max(reps, 16)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -75,12 +76,12 @@ def time_loop(fn, n, warmup=3, reps=1):
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        for i in range(reps):
-            fn(i)
+        for i in range(per_graph):
+            fn(i % reps)
     torch.cuda.synchronize()
-    n_rep = max(1, math.ceil(n / reps))
+    n_rep = max(1, math.ceil(n / per_graph))
     with torch.cuda.stream(s):
-        for _ in range(max(1, warmup // reps)):
+        for _ in range(max(1, warmup // per_graph)):
             g.replay()
         a, b = _events()
         a.record(s)
@@ -88,7 +89,7 @@ def time_loop(fn, n, warmup=3, reps=1):
             g.replay()
         b.record(s)
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / (n_rep * reps)
+    return a.elapsed_time(b) / (n_rep * per_graph)
 
 
 def fill_kidx(ops, shape, inp, kidx_pool):

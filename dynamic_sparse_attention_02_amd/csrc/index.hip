@@ -218,9 +218,12 @@ hipError_t launch_page_stats(const Shape& s, const void* k_pool, sa_dtype dt,
 // Taylor page scores.  A page's statistics row (mean then variance, 2*D
 // values) is spread over D/8 lanes holding 8 dimensions each (16-byte loads
 // for bf16), so a wave covers 512/D pages per load instruction; four rounds
-// are issued before any is used.  For each head of the group the two dot
-// products q'.mean and q'^2.var are reduced over the page's lanes.
+// are issued before any is used.
 //   x = mean_h [ q'_h.mean + log1p(0.5 * q'_h^2.var) ] + log(n / page)
+// The first term is (sum_h q'_h).mean / G, one dot product per page.  The
+// per-head variance sums are reduced over the page's lanes with DPP row
+// operations, each lane keeps the heads h = sub (mod lanes per page), takes
+// log1p of those, and one more reduction sums them.
 // ---------------------------------------------------------------------------
 constexpr int kPSRounds = 4;
 
@@ -243,6 +246,18 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
   v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
 }
 
+// Sum over aligned groups of N lanes (N = 8 or 16) with DPP row operations;
+// every lane of the group receives the total.
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+  if (N == 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
 k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
@@ -251,6 +266,8 @@ k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
   constexpr int LPP = D / 8;            // lanes per page
   constexpr int PPW = kWave / LPP;      // pages per wave and round
   constexpr int PPB = 4 * PPW * kPSRounds;
+  constexpr int HPL = (G + LPP - 1) / LPP;  // heads kept per lane
+  static_assert(LPP == 8 || LPP == 16, "head_dim 64 or 128");
   const int g = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int sub = lane % LPP, slot = lane / LPP;
@@ -258,15 +275,6 @@ k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
   const int32_t n_pages = (L + kPage - 1) / kPage;
   const int32_t p0 = blockIdx.x * PPB;
   if (p0 >= n_pages) return;
-  // scaled query of the group's heads, this lane's 8 dimensions
-  float qp[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v[8];
-    load8<T>(q + ((int64_t)b * s.Hq + g * G + h) * D + sub * 8, v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qp[h][e] = s_att * v[e];
-  }
   const int32_t* pt = page_table + (int64_t)b * s.max_pages;
   float mu[kPSRounds][8], va[kPSRounds][8];
   int32_t pg[kPSRounds];
@@ -286,24 +294,43 @@ k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
       }
     }
   }
+  // scaled query of the group's heads on this lane's 8 dimensions: the sum
+  // over heads, and the squares per head
+  float qs[8], qq[G][8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qs[e] = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float v[8];
+    load8<T>(q + ((int64_t)b * s.Hq + g * G + h) * D + sub * 8, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float qp = s_att * v[e];
+      qs[e] += qp;
+      qq[h][e] = qp * qp;
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kPSRounds; ++r) {
-    float acc = 0.f;
+    float first = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) first = fmaf(qs[e], mu[r][e], first);
+    float mine[HPL];
+#pragma unroll
+    for (int j = 0; j < HPL; ++j) mine[j] = 0.f;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float a1 = 0.f, c1 = 0.f;
+      float c = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        a1 = fmaf(qp[h][e], mu[r][e], a1);
-        c1 = fmaf(qp[h][e] * qp[h][e], va[r][e], c1);
-      }
-#pragma unroll
-      for (int o = LPP / 2; o > 0; o >>= 1) {
-        a1 += __shfl_xor(a1, o, LPP);
-        c1 += __shfl_xor(c1, o, LPP);
-      }
-      acc += a1 + log1pf(0.5f * c1);
+      for (int e = 0; e < 8; ++e) c = fmaf(qq[h][e], va[r][e], c);
+      c = row_sum<LPP>(c);
+      if (sub == h % LPP) mine[h / LPP] = c;
     }
+    float acc = first;
+#pragma unroll
+    for (int j = 0; j < HPL; ++j)
+      if (j * LPP + sub < G) acc += log1pf(0.5f * mine[j]);
+    acc = row_sum<LPP>(acc);
     if (sub == 0 && pg[r] < n_pages) {
       const int nv = (L - pg[r] * kPage) < kPage ? (L - pg[r] * kPage) : kPage;
       x[((int64_t)b * s.Hkv + g) * ldx + pg[r]] = acc / (float)G + logf((float)nv / (float)kPage);

@@ -49,37 +49,63 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// Cross-lane helpers on DPP row operations (16-lane rows) and readlane; no
+// LDS round trips.  Reductions return the same value in every lane (taken
+// from lanes 0, 16, 32, 48 in a fixed order, so the result is uniform).
+#define SA_DPP(v, ctrl) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), 0xF, 0xF, true))
+#define SA_DPP_ROWS(v, ctrl, rows) \
+  ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)(v), (ctrl), (rows), 0xF, true))
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+template <typename Op>
+__device__ __forceinline__ uint32_t row_allreduce_bits(uint32_t v, Op op) {
+  v = op(v, SA_DPP(v, kDppXor1));
+  v = op(v, SA_DPP(v, kDppXor2));
+  v = op(v, SA_DPP(v, kDppHalfMirror));
+  v = op(v, SA_DPP(v, kDppMirror));
   return v;
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_allreduce_bits(uint32_t v, Op op) {
+  v = row_allreduce_bits(v, op);
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  return __uint_as_float(wave_allreduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return __uint_as_float(wave_allreduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    uint32_t w = __shfl_xor(v, o, kWave);
-    v = w > v ? w : v;
-  }
-  return v;
+  return wave_allreduce_bits(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  return wave_allreduce_bits(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
-// Inclusive prefix sum across the wave.
+// Inclusive prefix sum across the wave: Kogge-Stone inside each row, then
+// the row totals carried into the rows above (row broadcasts).
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    uint32_t w = __shfl_up(v, o, kWave);
-    if (lane >= o) v += w;
-  }
+  v += SA_DPP(v, kDppShr1);
+  v += SA_DPP(v, kDppShr2);
+  v += SA_DPP(v, kDppShr4);
+  v += SA_DPP(v, kDppShr8);
+  v += SA_DPP_ROWS(v, kDppBcast15, 0xA);
+  v += SA_DPP_ROWS(v, kDppBcast31, 0xC);
   return v;
 }
 

@@ -86,10 +86,14 @@ template <typename U>
 __device__ __forceinline__ U block_excl_scan(U v, U* lds4, U& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   U inc = v;
+  if constexpr (sizeof(U) == 4) {
+    inc = wave_incl_scan(v);
+  } else {
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    U y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
+    for (int o = 1; o < 64; o <<= 1) {
+      U y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
   }
   if (lane == 63) lds4[w] = inc;
   __syncthreads();
@@ -514,14 +518,17 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
 // Row-resident selection: one block per row for rows of up to kRowMax
 // candidates.  Keys of the first kRowRegs * kThreads candidates stay in
 // registers (the rest are re-read from the score row), the three radix levels
-// use one LDS histogram with block barriers only, and the ordered compaction
-// counts selected candidates per (64-candidate wave slice) with ballots, then
-// one block scan over the slices gives every output position.
+// use one LDS histogram with block barriers only.  The ordered compaction
+// takes each (64-candidate wave slice)'s selected count from a ballot, one
+// block scan over the slices gives every slice's output offset, and a lane's
+// position inside its slice is the popcount of the ballot below it.  Selected
+// pages are staged in LDS and expanded to tokens by the whole block.
 // ---------------------------------------------------------------------------
 constexpr int kRowRegs = 32;
 constexpr int kRowMax = 131072;
 constexpr int kRowRounds = kRowMax / kThreads;        // 128 slices per wave
 constexpr int kRowSlices = kRowRounds * kWaves;       // 2048 (round, wave) slices
+constexpr int kPList = 4096;                          // pages staged for expansion
 
 struct RowRes {
   uint32_t mode, prefix, thr, n_eq, need;
@@ -541,6 +548,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   __shared__ uint32_t hcnt[kBins];
   __shared__ uint64_t hmass[TOPP ? kBins : 1];
   __shared__ uint32_t slice[kRowSlices];
+  __shared__ int32_t plist[TOPP ? 1 : kPList];
   __shared__ uint32_t red32[kWaves];
   __shared__ uint64_t red64[kWaves];
   __shared__ RowRes res;
@@ -579,11 +587,13 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   for (int i = 0; i < kWaves; ++i) M = red32[i] > M ? red32[i] : M;
   const float mx = key_score(M);
 
-  // ---- radix levels ----
+  // ---- radix levels: digits key[31:20], key[19:8], key[7:0] ----
   for (int level = 1; level <= 3; ++level) {
     if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
     const int NB = level == 3 ? 256 : kBins;
     const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+    const int hshift = level == 2 ? 20 : 8;  // resolved bits above the digit
+    const uint32_t dmask = level == 3 ? 0xffu : 0xfffu;
     const uint32_t pre = res.prefix;
     for (int i = t; i < NB; i += kThreads) {
       hcnt[i] = 0;
@@ -591,19 +601,8 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     }
     __syncthreads();
     auto add = [&](uint32_t key) {
-      bool match;
-      uint32_t digit;
-      if (level == 1) {
-        match = true;
-        digit = key >> 20;
-      } else if (level == 2) {
-        match = (key >> 20) == pre;
-        digit = (key >> 8) & 0xfffu;
-      } else {
-        match = (key >> 8) == pre;
-        digit = key & 0xffu;
-      }
-      if (match) {
+      if (level == 1 || (key >> hshift) == pre) {
+        const uint32_t digit = (key >> shift) & dmask;
         atomicAdd(&hcnt[digit], 1u);
         if (TOPP)
           atomicAdd((unsigned long long*)&hmass[digit],
@@ -717,6 +716,9 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const uint32_t mode = res.mode, thr = res.thr, n_eq = res.n_eq;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const int n_slices = rounds * kWaves;
+  const int32_t unit = a.unit;
+  const int ushift = __ffs(unit) - 1;          // unit is 1 or the page size (powers of two)
+  const int32_t last_w = Lt - (n - 1) * unit;  // tokens of the last candidate (unit > 1)
   // tie ranks reuse the count histogram's LDS (no longer needed)
   uint32_t* eqoff = hcnt;
   auto key_at = [&](int i) -> uint32_t {  // rounds beyond the register-resident ones
@@ -748,9 +750,9 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     __syncthreads();
     scan_slices(eqoff);
   }
-  // output weight of candidate (round i, this thread): 0 if not selected,
-  // else 1 token or the page's token count.  Every lane calls it (ballot).
-  auto weight = [&](int i, uint32_t key) -> uint32_t {
+  // is candidate (round i, this thread) in the support?  Every lane calls it
+  // (ballot inside).
+  auto selected = [&](int i, uint32_t key) -> bool {
     const int32_t e = i * kThreads + t;
     const bool valid = e < n;
     bool top;
@@ -762,45 +764,56 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     } else {
       top = valid && key >= thr;
     }
-    const bool forced = valid && a.unit == 1 && (e < a.n_sink || e >= n - a.n_window);
-    if (!(top || forced)) return 0u;
-    if (a.unit == 1) return 1u;
-    const int32_t r = Lt - e * a.unit;
-    return (uint32_t)(r < a.unit ? r : a.unit);
+    const bool forced = valid && unit == 1 && (e < a.n_sink || e >= n - a.n_window);
+    return top || forced;
   };
-  // pass 1: output count of every (round, wave) slice
+  // pass 1: output tokens of every (round, wave) slice.  Every page but the
+  // row's last holds `unit` tokens.
+  auto count_slice = [&](int i, uint32_t key) {
+    const bool sel = selected(i, key);
+    const uint64_t m = __ballot(sel);
+    uint32_t c = (uint32_t)__popcll(m) << ushift;
+    if (unit > 1 && __ballot(sel && i * kThreads + t == n - 1)) c -= (uint32_t)(unit - last_w);
+    if (lane == 0) slice[i * kWaves + wave] = c;
+  };
 #pragma unroll
-  for (int i = 0; i < kRowRegs; ++i) {
-    if (i < rounds) {
-      const uint32_t sum = wave_sum_u32(weight(i, keys[i]));
-      if (lane == 0) slice[i * kWaves + wave] = sum;
-    }
-  }
-  for (int i = kRowRegs; i < rounds; ++i) {
-    const uint32_t sum = wave_sum_u32(weight(i, key_at(i)));
-    if (lane == 0) slice[i * kWaves + wave] = sum;
-  }
+  for (int i = 0; i < kRowRegs; ++i)
+    if (i < rounds) count_slice(i, keys[i]);
+  for (int i = kRowRegs; i < rounds; ++i) count_slice(i, key_at(i));
   __syncthreads();
   const uint32_t total = scan_slices(slice);
-  // pass 2: write every selected candidate at its slice offset
+  const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
+  // pass 2: every selected candidate at its slice offset plus its rank in the
+  // slice
   int32_t* out = a.idx + (int64_t)row * a.cap;
-  auto emit = [&](int i, uint32_t wgt) {
-    const uint32_t pos = slice[i * kWaves + wave] + wave_excl_scan_u32(wgt);
-    if (wgt) {
-      const int32_t e = i * kThreads + t;
-      if (a.unit == 1) {
-        if (pos < (uint32_t)a.cap) out[pos] = e;
-      } else {
-        for (uint32_t q = 0; q < wgt; ++q)
-          if (pos + q < (uint32_t)a.cap) out[pos + q] = e * a.unit + (int32_t)q;
-      }
+  const bool staged = unit > 1 && (total >> ushift) < (uint32_t)kPList;
+  auto emit = [&](int i, uint32_t key) {
+    const bool sel = selected(i, key);
+    const uint64_t m = __ballot(sel);
+    const uint32_t rank = (uint32_t)__popcll(m & lt_mask);
+    if (!sel) return;
+    const int32_t e = i * kThreads + t;
+    if (unit == 1) {
+      const uint32_t pos = slice[i * kWaves + wave] + rank;
+      if (pos < (uint32_t)a.cap) out[pos] = e;
+    } else if (staged) {
+      plist[(slice[i * kWaves + wave] >> ushift) + rank] = e;
+    } else {
+      const uint32_t pos = slice[i * kWaves + wave] + (rank << ushift);
+      const int32_t w = e == n - 1 ? last_w : unit;
+      for (int32_t q = 0; q < w; ++q)
+        if (pos + q < (uint32_t)a.cap) out[pos + q] = e * unit + q;
     }
   };
 #pragma unroll
   for (int i = 0; i < kRowRegs; ++i)
-    if (i < rounds) emit(i, weight(i, keys[i]));
-  for (int i = kRowRegs; i < rounds; ++i) emit(i, weight(i, key_at(i)));
-  const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
+    if (i < rounds) emit(i, keys[i]);
+  for (int i = kRowRegs; i < rounds; ++i) emit(i, key_at(i));
+  if (staged) {  // block-uniform
+    __syncthreads();
+    for (uint32_t o = t; o < T; o += kThreads)
+      out[o] = (plist[o >> ushift] << ushift) + (int32_t)(o & (uint32_t)(unit - 1));
+  }
   for (int64_t o = (int64_t)T + t; o < a.cap; o += kThreads) out[o] = -1;
   if (t == 0) a.count[row] = (int32_t)T;
 }

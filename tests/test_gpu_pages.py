@@ -94,13 +94,14 @@ def test_page_stats_matches_oracle(dtype):
                 assert np.all(got[-1, 1] == 0.0)  # one token: zero variance
 
 
-@pytest.mark.parametrize("G,dtype", [(1, torch.float32), (4, torch.bfloat16),
-                                     (8, torch.bfloat16), (16, torch.bfloat16)])
-def test_page_scores_matches_oracle(G, dtype):
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, torch.float32), (4, 128, torch.bfloat16),
+                                       (8, 128, torch.bfloat16), (16, 128, torch.bfloat16),
+                                       (2, 64, torch.bfloat16), (16, 64, torch.float32)])
+def test_page_scores_matches_oracle(G, d, dtype):
     """Taylor page scores of every page of ragged rows (an empty row is left
     untouched) from oracle statistics stored in the cache dtype."""
     o = ops()
-    inp = synth.make_decode_custom(B=4, H_q=2 * G, H_kv=2, d=128, seq_lens=[5000, 0, 100, 64],
+    inp = synth.make_decode_custom(B=4, H_q=2 * G, H_kv=2, d=d, seq_lens=[5000, 0, 100, 64],
                                    dtype=dtype, device="cuda", seed=30 + G, hh_frac=0.01,
                                    alpha=10.0, shuffle=True)
     shape = S.shape_of(inp)
