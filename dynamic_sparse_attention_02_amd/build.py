@@ -40,6 +40,12 @@ CFLAGS = [
 ]
 
 
+# Per-source extra flags.  prefill.hip: keep MFMA results and accumulators in
+# arch VGPRs (the softmax reads every score and rescales the output
+# accumulator; in AGPRs each such access costs a copy).
+EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -49,7 +55,7 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *CFLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

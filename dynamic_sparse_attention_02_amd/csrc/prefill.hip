@@ -127,6 +127,7 @@ constexpr int kKT = 64;                 // keys per tile
 constexpr int kKPitch = 128 * 2 + 16;   // K tile row pitch in bytes (d = 128 bf16)
 constexpr int kVPitch = kKT * 2 + 8;    // V^T row pitch in bytes (64 keys bf16; 34 dwords)
 constexpr int kMaxListed = 2048;        // listed keys per block the attention kernel takes
+constexpr float kLazy = 8.f;            // log2 headroom of the lazily raised softmax maximum
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
@@ -136,24 +137,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int G>
-__global__ void __launch_bounds__(G * 64)
+// HB query heads of one group per workgroup (one wave each); a group of G >
+// HB heads takes G / HB workgroups.
+template <int HB>
+__global__ void __launch_bounds__(HB * 64)
 k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_pool,
                const bf16_raw* __restrict__ v_pool, const int32_t* __restrict__ pt,
                const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int32_t cap,
                int32_t N, Shape s, float s_att, void* __restrict__ out, int32_t out_bf16,
                float* __restrict__ lse) {
   constexpr int D = 128;
-  constexpr int NT = G * 64;
+  constexpr int NT = HB * 64;
   constexpr int PIECES = kKT * (D * 2 / 16);  // 16-byte pieces per tile per tensor
   constexpr int LPT = (PIECES + NT - 1) / NT;
   const int nblk = (N + kQB - 1) / kQB;
-  // heaviest items (late blocks, full supports) first
-  const int item = blockIdx.x;
+  const int G = s.Hq / s.Hkv, n_sub = G / HB;
+  // heaviest items (late blocks, full supports) first; workgroups of one
+  // block and group run side by side
+  const int item = blockIdx.x / n_sub, sub = blockIdx.x % n_sub;
   const int blk = nblk - 1 - item / s.Hkv;
   const int g = item % s.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = g * G + wave;
+  const int h = g * G + sub * HB + wave;
   const int half = lane >> 5, l32 = lane & 31;
   const int row = blk * s.Hkv + g;
   int32_t nl = count[row];
@@ -280,10 +285,12 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
       }
     }
     // online softmax per query (lane's query nb*32 + l32; keys spread over
-    // this lane's 32 accumulator values and the partner lane's).  Scores are
-    // scaled into log2 units inside the exponent's fused multiply-add.
+    // this lane's 32 accumulator values and the partner lane's), in log2
+    // units.  The running maximum is raised only when a tile's maximum
+    // exceeds it by more than kLazy (so P stays below 2^kLazy): the output
+    // accumulator is rescaled on those tiles only.
     const bool masked = diag || nt < kKT;
-    float alpha[2];
+    float mt[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int qloc = nb * 32 + l32;
@@ -296,14 +303,34 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
             if (!(kloc < nt && (!diag || kloc <= qloc))) S[mk][nb][v] = -INFINITY;
           }
       }
-      float mt = -INFINITY;
+      float m = -INFINITY;
 #pragma unroll
       for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mt = fmaxf(mt, S[mk][nb][v]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * sl2;
-      const float m_new = fmaxf(m_run[nb], mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        for (int v = 0; v < 16; ++v) m = fmaxf(m, S[mk][nb][v]);
+      mt[nb] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
+    }
+    const bool raise0 = mt[0] > m_run[0] + kLazy, raise1 = mt[1] > m_run[1] + kLazy;
+    if (__ballot(raise0 || raise1)) {
+      float alpha[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const bool r = nb == 0 ? raise0 : raise1;
+        const float m_new = r ? mt[nb] : m_run[nb];
+        alpha[nb] = r ? __builtin_amdgcn_exp2f(m_run[nb] - m_new) : 1.f;  // 0 on the first raise
+        l_run[nb] *= alpha[nb];
+        m_run[nb] = m_new;
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
       float lt = 0.f;
 #pragma unroll
       for (int mk = 0; mk < 2; ++mk)
@@ -313,18 +340,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
           S[mk][nb][v] = p;
           lt += p;
         }
-      lt += __shfl_xor(lt, 32, 64);
-      alpha[nb] = __builtin_amdgcn_exp2f(m_run[nb] - m_use);
-      l_run[nb] = l_run[nb] * alpha[nb] + lt;
-      m_run[nb] = m_new;
-    }
-    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f)) {
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
+      l_run[nb] += lt + __shfl_xor(lt, 32, 64);
     }
     // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per step in the
     // accumulator's key order
@@ -460,18 +476,17 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
                                  float* lse, hipStream_t st) {
   const int nblk = (n_tokens + kQB - 1) / kQB;
   const int G = s.Hq / s.Hkv;
-  dim3 grid(nblk * s.Hkv);
-#define SA_PA(GG)                                                                           \
-  k_prefill_attn<GG><<<grid, GG * 64, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)k_pool,  \
+  const int HB = G < 4 ? G : 4;
+  dim3 grid(nblk * s.Hkv * (G / HB));
+#define SA_PA(HH)                                                                           \
+  k_prefill_attn<HH><<<grid, HH * 64, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)k_pool,  \
                                                (const bf16_raw*)v_pool, pg.page_table, idx,  \
                                                count, cap, n_tokens, s, s_att, out,          \
                                                out_dt == SA_BF16, lse)
-  switch (G) {
+  switch (HB) {
     case 1: SA_PA(1); break;
     case 2: SA_PA(2); break;
-    case 4: SA_PA(4); break;
-    case 8: SA_PA(8); break;
-    default: SA_PA(16); break;
+    default: SA_PA(4); break;
   }
 #undef SA_PA
   return hipGetLastError();

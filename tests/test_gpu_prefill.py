@@ -103,6 +103,17 @@ def test_prefill_small(N, k):
     check_blocks(inp, kt_rows, idx, count, out, lse, k, range(inp.n_blocks), range(inp.H_kv))
 
 
+@pytest.mark.parametrize("H_q,H_kv", [(4, 4), (4, 2), (8, 1), (16, 1)])
+def test_prefill_group_sizes(H_q, H_kv):
+    """G = 1, 2, 8, 16 (a group of more than 4 heads is split over several
+    workgroups that gather the same keys)."""
+    inp = synth.make_prefill_custom(N=450, H_q=H_q, H_kv=H_kv, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=H_q * 10 + H_kv, n_hh=6)
+    kidx, kt_rows = oracle_kidx(inp)
+    idx, count, out, lse = run_prefill(inp, kidx, 96)
+    check_blocks(inp, kt_rows, idx, count, out, lse, 96, range(inp.n_blocks), range(inp.H_kv))
+
+
 def test_prefill_dense_when_k_covers_everything():
     """k >= N: every block attends to all earlier keys, i.e. dense causal
     attention (torch SDPA, float64 CPU)."""
