@@ -93,15 +93,17 @@ __device__ __forceinline__ void stamp(const FusedArgs& a, int slot) {
   if (threadIdx.x == 0) a.trace[(int64_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
-// Per-row barrier: device-scope release before the arrival is counted and
-// acquire after it is observed, so every write of the other workgroups of the
-// row (histogram bins, counts, the row maximum, attention partials) is
-// visible afterwards.  The spin is bounded: a barrier that waits too long
-// raises the error flag and lets the launch finish instead of hanging.
+// Per-row barrier: a device-scope release before the arrival is counted, so
+// every write of the workgroup (histogram bins, counts, the row maximum,
+// attention partials) is performed before any other workgroup of the row can
+// pass.  No acquire fence (an L2 invalidate) follows: every read of data
+// another workgroup produced is itself a device-scope atomic load, which the
+// L2 does not serve stale.  The spin is bounded: a barrier that waits too
+// long raises the error flag and lets the launch finish instead of hanging.
 __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     atomicAdd(ctr, 1u);
     uint32_t spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
@@ -111,7 +113,6 @@ __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint
         break;
       }
     }
-    __threadfence();
   }
   __syncthreads();
 }
@@ -177,7 +178,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   __shared__ __align__(16) char Vs[kTileF * PITCH];
   __shared__ __align__(16) T Qs[G][D];
   __shared__ __align__(16) float Ps[G][kTileF];
-  __shared__ int32_t my_list[TPT * kNT + 64];
+  // pool token rows ((page * Hkv + g) * 64 + slot) of the tokens to attend
+  __shared__ uint32_t my_list[TPT * kNT + 64];
+  // pool pages of the own token range
+  __shared__ int32_t s_pt[TPT * kNT / kPage];
   __shared__ uint32_t s_mode, s_prefix, s_thr, s_neq, s_need, s_cnt;
   __shared__ uint64_t s_rem;
   __shared__ uint32_t s_slice[TPT * 4];
@@ -186,6 +190,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   // ---- 1. scores of the own tokens ----
   const T* kidx = (const T*)a.kidx;
   const int32_t* pt = a.page_table + (int64_t)b * s.max_pages;
+  for (int i = tid; i < TPT * kNT / kPage; i += kNT)
+    s_pt[i] = j0 + i * kPage < n ? (int32_t)clamp_page(pt[(j0 >> 6) + i], s.n_pool_pages) : 0;
+  __syncthreads();
   float xk[TPT];
   uint32_t key[TPT];
   {
@@ -195,7 +202,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     for (int u = 0; u < TPT; ++u) {
       const int32_t j = j0 + u * kNT + tid;
       if (j < n) {
-        const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+        const int64_t page = s_pt[(j - j0) >> 6];
         const T* rowp = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
         if constexpr (sizeof(T) == 2) {
           const uint4* v = reinterpret_cast<const uint4*>(rowp);
@@ -549,7 +556,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint32_t o = off;
 #pragma unroll
     for (int u = 0; u < TPT; ++u)
-      if (selmask[u] == 1u) my_list[o++] = j0 + u * kNT + tid;
+      if (selmask[u] == 1u) {
+        const int32_t jl = u * kNT + tid;  // j - j0
+        my_list[o++] = (uint32_t)(((int64_t)s_pt[jl >> 6] * s.Hkv + g) * kPage + (jl & 63));
+      }
     uint32_t tot_sel;
     blk_scan<uint32_t>(my_sel, red_u, tot_sel);
     // share of the forced tokens: the union of [0, n_sink) and
@@ -560,7 +570,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     const int32_t f0 = (int32_t)(((int64_t)nf * bi) / NB), f1 = (int32_t)(((int64_t)nf * (bi + 1)) / NB);
     for (int32_t f = f0 + tid; f < f1; f += kNT) {
       const int32_t j = f < s_end ? f : w_beg + (f - s_end);
-      my_list[tot_nf + (f - f0)] = j;
+      const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+      my_list[tot_nf + (f - f0)] = (uint32_t)((page * s.Hkv + g) * kPage + (j & 63));
     }
     if (tid == 0) {
       s_cnt = tot_nf + (uint32_t)(f1 - f0);
@@ -574,8 +585,6 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     const T* v_pool = (const T*)a.v_pool;
     const T* q = (const T*)a.q;
     for (int i = tid; i < G * D; i += kNT) Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
-    const int64_t head_stride = (int64_t)kPage * D;
-    const int64_t page_stride = (int64_t)s.Hkv * head_stride;
     float m_run[HPW], l_run[HPW], acc[HPW][DPL];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -584,8 +593,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) acc[hh][e] = 0.f;
     }
-    uint4 kr[LPT], vr[LPT];
-    auto gather = [&](int32_t ts) {
+    // K/V rows of two tiles in flight: the tile being staged and the next
+    uint4 kA[LPT], vA[LPT], kB[LPT], vB[LPT];
+    auto gather = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
@@ -593,16 +603,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
         if (ts + r < n_att) {
-          const int32_t j = my_list[ts + r];
-          const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
-          const int64_t off = page * page_stride + g * head_stride + (int64_t)(j & 63) * D;
+          const int64_t off = (int64_t)my_list[ts + r] * D;
           kr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + off) + col * 16);
           vr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + off) + col * 16);
         }
       }
     };
-    if (n_att > 0) gather(0);
-    for (int32_t ts = 0; ts < n_att; ts += kTileF) {
+    auto tile = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
       const int32_t nt = min(kTileF, n_att - ts);
       __syncthreads();
 #pragma unroll
@@ -613,7 +620,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         *reinterpret_cast<uint4*>(Vs + r * PITCH + col * 16) = vr[i];
       }
       __syncthreads();
-      if (ts + kTileF < n_att) gather(ts + kTileF);
+      if (ts + 2 * kTileF < n_att) gather(ts + 2 * kTileF, kr, vr);
       float sc[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) sc[hh] = 0.f;
@@ -690,6 +697,12 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
           }
         }
       }
+    };
+    if (n_att > 0) gather(0, kA, vA);
+    if (n_att > kTileF) gather(kTileF, kB, vB);
+    for (int32_t ts = 0; ts < n_att; ts += 2 * kTileF) {
+      tile(ts, kA, vA);
+      if (ts + kTileF < n_att) tile(ts + kTileF, kB, vB);
     }
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -806,14 +819,14 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     __syncthreads();
+    // (the zeroing above and the resets below reach the next launch through
+    // the end-of-kernel cache write-back)
     if (tid == 0) {
-      __threadfence();
       const uint32_t old = atomicAdd(&ctl->exit, 1u);
       if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
         ctl->maxkey = 0;
         ctl->bar = 0;
         ctl->exit = 0;
-        __threadfence();
       }
     }
   }
@@ -843,6 +856,8 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, i
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
   if (G < 4 || rows > 16 || s.max_len < 1) return false;
+  // attention lists hold pool token rows as 32-bit values
+  if ((double)s.n_pool_pages * s.Hkv * kPage >= 4294967296.0) return false;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
