@@ -99,7 +99,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
       const int32_t c = r < rows ? (row_count(count, r, cap) + csize - 1) / csize : 0;
       const int32_t inc = (int32_t)wave_incl_scan((uint32_t)c);
       if (r < rows) prefix[r] = carry + inc - c;
-      carry += __shfl(inc, 63, 64);
+      carry += (int32_t)lane_u32((uint32_t)inc, 63);
     }
     if (lane == 0) prefix[rows] = carry;
   }

@@ -127,12 +127,8 @@ __device__ __forceinline__ float ld_dev(const float* p) {
 template <typename U>
 __device__ __forceinline__ U blk_scan(U v, U* lds, U& total) {  // exclusive, kNT threads
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  U inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    U y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
+  static_assert(sizeof(U) == 4, "32-bit scan");
+  const U inc = wave_incl_scan(v);
   if (lane == 63) lds[w] = inc;
   __syncthreads();
   U off = 0, tot = 0;
@@ -251,9 +247,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < kRank; ++c) {
-      float v = acc[c];
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+      const float v = wave_sum(acc[c]);
       if (lane == 0) red_f[wave][c] = v;
     }
     __syncthreads();
@@ -343,13 +337,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
           atomicAdd(&gc[bin], cn);
           if (!topk) atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
         }
-        uint32_t csum = cn;
-        uint64_t msum = ms;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-          csum += __shfl_xor(csum, o, 64);
-          msum += __shfl_xor(msum, o, 64);
-        }
+        const uint32_t csum = wave_sum_u32(cn);
+        const uint64_t msum = topk ? 0ull : wave_sum_u64(ms);
         if (lane == 0 && csum) {
           atomicAdd(&gcc[cg], csum);
           if (!topk) atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
@@ -384,18 +373,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       const int cgi = NC - 1 - lane;
       const uint32_t cc = lane < NC ? __hip_atomic_load(&gcc[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
       const uint64_t cm = (!topk && lane < NC) ? __hip_atomic_load(&gcm[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-      uint32_t cinc = cc;
-      uint64_t minc = cm;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(cinc, o, 64);
-        const uint64_t z = __shfl_up(minc, o, 64);
-        if (lane >= o) {
-          cinc += y;
-          minc += z;
-        }
-      }
-      const uint64_t mtot = __shfl(minc, 63, 64);
+      const uint32_t cinc = wave_incl_scan(cc);
+      const uint64_t minc = wave_incl_scan_u64(cm);
+      const uint64_t mtot = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(minc >> 32), 63) << 32) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)minc, 63);
       uint64_t target = s_rem;
       if (!topk && level == 1) {
         uint64_t tc = (uint64_t)ceil((double)a.p * (double)mtot);
@@ -413,9 +394,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       uint64_t g_mb = 0;
       if (hb) {
         const int src = __ffsll(hb) - 1;
-        found = __shfl(cgi, src, 64);
-        g_cb = __shfl(cbef, src, 64);
-        g_mb = __shfl(mbef, src, 64);
+        found = (int)lane_u32((uint32_t)cgi, src);
+        g_cb = lane_u32(cbef, src);
+        g_mb = lane_u64(mbef, src);
       }
       uint32_t bc = 0;
       uint64_t bm = 0;
@@ -425,17 +406,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         bc = __hip_atomic_load(&gc[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         bm = !topk ? __hip_atomic_load(&gm[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
       }
-      uint32_t binc = bc;
-      uint64_t bminc = bm;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(binc, o, 64);
-        const uint64_t z = __shfl_up(bminc, o, 64);
-        if (lane >= o) {
-          binc += y;
-          bminc += z;
-        }
-      }
+      const uint32_t binc = wave_incl_scan(bc);
+      const uint64_t bminc = wave_incl_scan_u64(bm);
       const uint32_t bcb = g_cb + binc - bc;
       const uint64_t bmb = g_mb + bminc - bm;
       const bool hit2 = found >= 0 && (!topk ? (bmb < target && bmb + bm >= target)
@@ -777,8 +749,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       const int hl = oo / D, d = oo % D;
       float M2 = -INFINITY;
       for (int k = sub; k < NB; k += 16) M2 = fmaxf(M2, ld_dev(&a.part_ml[(((int64_t)row * NB + k) * G + hl) * 2]));
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) M2 = fmaxf(M2, __shfl_xor(M2, o, 16));
+      M2 = row16_max(M2);
       float lsum = 0.f, osum = 0.f;
       for (int k = sub; k < NB; k += 16) {
         const int64_t pi = ((int64_t)row * NB + k) * G + hl;
@@ -787,11 +758,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         lsum += ld_dev(&a.part_ml[pi * 2 + 1]) * wgt;
         osum += ld_dev(&a.part_o[pi * D + d]) * wgt;
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        lsum += __shfl_xor(lsum, o, 16);
-        osum += __shfl_xor(osum, o, 16);
-      }
+      lsum = row16_sum(lsum);
+      osum = row16_sum(osum);
       if (sub == 0) {
         const int h = g * G + hl;
         const float v = lsum > 0.f ? osum / lsum : 0.f;

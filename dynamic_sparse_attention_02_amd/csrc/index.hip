@@ -100,9 +100,7 @@ k_collapse(const T* __restrict__ q, const T* __restrict__ w_q, int32_t Hq, int32
   __shared__ float red[4][kRank];
 #pragma unroll
   for (int c = 0; c < kRank; ++c) {
-    float v = acc[c];
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    const float v = wave_sum(acc[c]);
     if (lane == 0) red[wave][c] = v;
   }
   __syncthreads();

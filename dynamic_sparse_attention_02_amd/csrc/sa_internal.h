@@ -113,6 +113,56 @@ __device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
   return wave_incl_scan(v) - v;
 }
 
+// Sum / maximum over each aligned group of 16 lanes (a DPP row); every lane
+// of the row receives its row's value.
+__device__ __forceinline__ float row16_sum(float v) {
+  return __uint_as_float(row_allreduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+  }));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  return __uint_as_float(row_allreduce_bits(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+// Value of a lane chosen by a wave-uniform index.
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int src) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
+}
+__device__ __forceinline__ uint64_t lane_u64(uint64_t v, int src) {
+  return ((uint64_t)lane_u32((uint32_t)(v >> 32), src) << 32) | lane_u32((uint32_t)v, src);
+}
+
+// 64-bit sums on the same DPP patterns, as (lo, hi) halves with a carry.
+__device__ __forceinline__ void add_u64_parts(uint32_t& lo, uint32_t& hi, uint32_t lo2, uint32_t hi2) {
+  const uint32_t nl = lo + lo2;
+  hi = hi + hi2 + (nl < lo ? 1u : 0u);
+  lo = nl;
+}
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppXor1), SA_DPP(hi, kDppXor1));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppXor2), SA_DPP(hi, kDppXor2));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppHalfMirror), SA_DPP(hi, kDppHalfMirror));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppMirror), SA_DPP(hi, kDppMirror));
+  uint64_t r[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * i) << 32) |
+           (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * i);
+  return (r[0] + r[1]) + (r[2] + r[3]);
+}
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppShr1), SA_DPP(hi, kDppShr1));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppShr2), SA_DPP(hi, kDppShr2));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppShr4), SA_DPP(hi, kDppShr4));
+  add_u64_parts(lo, hi, SA_DPP(lo, kDppShr8), SA_DPP(hi, kDppShr8));
+  add_u64_parts(lo, hi, SA_DPP_ROWS(lo, kDppBcast15, 0xA), SA_DPP_ROWS(hi, kDppBcast15, 0xA));
+  add_u64_parts(lo, hi, SA_DPP_ROWS(lo, kDppBcast31, 0xC), SA_DPP_ROWS(hi, kDppBcast31, 0xC));
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // Clamp helpers for caller-provided paging data (never fault on bad input).
 __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t max_len) {
   return L < 0 ? 0 : (L > max_len ? max_len : L);

@@ -86,15 +86,8 @@ template <typename U>
 __device__ __forceinline__ U block_excl_scan(U v, U* lds4, U& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   U inc = v;
-  if constexpr (sizeof(U) == 4) {
-    inc = wave_incl_scan(v);
-  } else {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      U y = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += y;
-    }
-  }
+  if constexpr (sizeof(U) == 4) inc = wave_incl_scan(v);
+  else inc = wave_incl_scan_u64(v);
   if (lane == 63) lds4[w] = inc;
   __syncthreads();
   U off = 0, tot = 0;
@@ -244,13 +237,8 @@ __global__ void __launch_bounds__(kThreads) k_sel_level(SelectArgs a, WsLayout w
       atomicAdd(&gc[bin], cn);
       if (TOPP) atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
     }
-    uint32_t csum = cn;
-    uint64_t msum = ms;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      csum += __shfl_xor(csum, o, 64);
-      if (TOPP) msum += __shfl_xor(msum, o, 64);
-    }
+    const uint32_t csum = wave_sum_u32(cn);
+    const uint64_t msum = TOPP ? wave_sum_u64(ms) : 0ull;
     if (lane == 0 && csum) {
       atomicAdd(&gcc[cg], csum);
       if (TOPP) atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
@@ -274,18 +262,9 @@ __global__ void __launch_bounds__(kThreads) k_sel_level(SelectArgs a, WsLayout w
     const int cgi = NC - 1 - lane;
     const uint32_t cc = lane < NC ? __hip_atomic_load(&gcc[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     const uint64_t cm = (TOPP && lane < NC) ? __hip_atomic_load(&gcm[cgi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-    uint32_t cinc = cc;
-    uint64_t minc = cm;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(cinc, o, 64);
-      const uint64_t z = __shfl_up(minc, o, 64);
-      if (lane >= o) {
-        cinc += y;
-        minc += z;
-      }
-    }
-    const uint64_t mtot = __shfl(minc, 63, 64);
+    const uint32_t cinc = wave_incl_scan(cc);
+    const uint64_t minc = wave_incl_scan_u64(cm);
+    const uint64_t mtot = lane_u64(minc, 63);
     uint64_t target = st.rem;
     if (TOPP && LEVEL == 1) {
       const double t = (double)a.p * (double)mtot;
@@ -305,9 +284,9 @@ __global__ void __launch_bounds__(kThreads) k_sel_level(SelectArgs a, WsLayout w
     uint64_t g_mbef = 0;
     if (hb) {
       const int src = __ffsll(hb) - 1;
-      found = __shfl(cgi, src, 64);
-      g_cbef = __shfl(cbef, src, 64);
-      g_mbef = __shfl(mbef, src, 64);
+      found = (int)lane_u32((uint32_t)cgi, src);
+      g_cbef = lane_u32(cbef, src);
+      g_mbef = lane_u64(mbef, src);
     }
     // step 2: the 64 bins of the crossing group, descending
     uint32_t bc = 0;
@@ -318,17 +297,8 @@ __global__ void __launch_bounds__(kThreads) k_sel_level(SelectArgs a, WsLayout w
       bc = __hip_atomic_load(&gc[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       bm = TOPP ? __hip_atomic_load(&gm[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
     }
-    uint32_t binc = bc;
-    uint64_t bminc = bm;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(binc, o, 64);
-      const uint64_t z = __shfl_up(bminc, o, 64);
-      if (lane >= o) {
-        binc += y;
-        bminc += z;
-      }
-    }
+    const uint32_t binc = wave_incl_scan(bc);
+    const uint64_t bminc = wave_incl_scan_u64(bm);
     const uint32_t bcb = g_cbef + binc - bc;
     const uint64_t bmb = g_mbef + bminc - bm;
     const bool hit2 = found >= 0 && (TOPP ? (bmb < target && bmb + bm >= target)
