@@ -34,6 +34,10 @@ constexpr int kSlab = 256;  // query blocks per score slab
 // ---------------------------------------------------------------------------
 // Block-collapsed indexer query: qcb[blk][g][c] = s_idx / (rows * G) *
 // sum_{h in g} sum_d W_q[h][d][c] * (sum_{i in blk} q[i][h][d]).
+// Thread t sums 8 consecutive dims (one 16-byte load for bf16) of one head
+// over a share of the block's rows; the shares are added in LDS, then each
+// thread projects its (head, dims) chunk and the block reduces the rank-16
+// result.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256)
@@ -44,21 +48,52 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
   const int r0 = blk * kQB;
   const int nr = min(kQB, N - r0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int chunks = G * D / 8;              // (head, 8 dims) chunks: <= 256
+  const int parts = 256 / chunks;            // row shares per chunk
+  const int ch = threadIdx.x % chunks, part = threadIdx.x / chunks;
+  const int h = g * G + (ch * 8) / D, d0 = (ch * 8) % D;
+  __shared__ float qs[256][8];               // each thread's partial sums
+  float acc8[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+  if (part < parts) {
+    for (int i = part; i < nr; i += parts) {
+      const T* src = q + ((int64_t)(r0 + i) * Hq + h) * D + d0;
+      if constexpr (sizeof(T) == 2) {
+        const uint4 v = *reinterpret_cast<const uint4*>(src);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc8[2 * e] += __uint_as_float(w[e] << 16);
+          acc8[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc8[e] += to_f32<T>(src[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qs[threadIdx.x][e] = acc8[e];
+  __syncthreads();
+  // projection of this thread's chunk (first `chunks` threads)
   float acc[kRank];
 #pragma unroll
   for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
-  for (int pi = threadIdx.x; pi < G * D; pi += 256) {
-    const int h = g * G + pi / D, d = pi % D;
-    float qs = 0.f;
-    for (int i = 0; i < nr; ++i) qs += to_f32<T>(q[((int64_t)(r0 + i) * Hq + h) * D + d]);
-    const T* w = w_q + ((int64_t)h * D + d) * kRank;
+  if (threadIdx.x < chunks) {
 #pragma unroll
-    for (int c = 0; c < kRank; ++c) acc[c] = fmaf(to_f32<T>(w[c]), qs, acc[c]);
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.f;
+      for (int pp = 0; pp < parts; ++pp) v += qs[pp * chunks + ch][e];
+      const T* wr = w_q + ((int64_t)h * D + d0 + e) * kRank;
+#pragma unroll
+      for (int c = 0; c < kRank; ++c) acc[c] = fmaf(to_f32<T>(wr[c]), v, acc[c]);
+    }
   }
   __shared__ float red[4][kRank];
 #pragma unroll
   for (int c = 0; c < kRank; ++c) {
-    float v = wave_sum(acc[c]);
+    const float v = wave_sum(acc[c]);
     if (lane == 0) red[wave][c] = v;
   }
   __syncthreads();

@@ -495,6 +495,10 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
 // pages are staged in LDS and expanded to tokens by the whole block.
 // ---------------------------------------------------------------------------
 constexpr int kRowRegs = 32;
+// rounds after the register-resident ones kept in LDS (top-k has no mass
+// histogram, so more LDS is free for keys)
+constexpr int kCacheRoundsTopk = 24;
+constexpr int kCacheRoundsTopp = 16;
 constexpr int kRowMax = 131072;
 constexpr int kRowRounds = kRowMax / kThreads;        // 128 slices per wave
 constexpr int kRowSlices = kRowRounds * kWaves;       // 2048 (round, wave) slices
@@ -525,6 +529,10 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef;
   __shared__ uint64_t s_hit_mass, s_hit_mbef;
 
+  constexpr int kCacheRounds = TOPP ? kCacheRoundsTopp : kCacheRoundsTopk;
+  __shared__ uint32_t kcache[kCacheRounds * kThreads];
+  const int cached_end = kRowRegs + kCacheRounds;  // rounds [kRowRegs, cached_end) live in LDS
+
   uint32_t keys[kRowRegs];
   uint32_t mk = 0;
 #pragma unroll
@@ -533,11 +541,19 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     keys[i] = e < n ? score_key(xr[e]) : 0u;
     mk = keys[i] > mk ? keys[i] : mk;
   }
-  for (int i = kRowRegs; i < rounds; ++i) {
+  for (int i = kRowRegs; i < rounds && i < cached_end; ++i) {
     const int32_t e = i * kThreads + t;
-    if (e < n) {
-      const uint32_t k = score_key(xr[e]);
-      mk = k > mk ? k : mk;
+    const uint32_t k = e < n ? score_key(xr[e]) : 0u;
+    kcache[(i - kRowRegs) * kThreads + t] = k;
+    mk = k > mk ? k : mk;
+  }
+  if (TOPP) {  // the row maximum (mass reference) needs every key
+    for (int i = cached_end; i < rounds; ++i) {
+      const int32_t e = i * kThreads + t;
+      if (e < n) {
+        const uint32_t k = score_key(xr[e]);
+        mk = k > mk ? k : mk;
+      }
     }
   }
   mk = wave_max_u32(mk);
@@ -584,7 +600,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       if (i * kThreads + t < n) add(keys[i]);
     for (int i = kRowRegs; i < rounds; ++i) {
       const int32_t e = i * kThreads + t;
-      if (e < n) add(score_key(xr[e]));
+      if (e < n) add(i < cached_end ? kcache[(i - kRowRegs) * kThreads + t] : score_key(xr[e]));
     }
     __syncthreads();
     // block scan over bins in descending order: thread t owns positions
@@ -693,6 +709,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   uint32_t* eqoff = hcnt;
   auto key_at = [&](int i) -> uint32_t {  // rounds beyond the register-resident ones
     const int32_t e = i * kThreads + t;
+    if (i < cached_end) return kcache[(i - kRowRegs) * kThreads + t];
     return e < n ? score_key(xr[e]) : 0u;
   };
   auto scan_slices = [&](uint32_t* arr) -> uint32_t {  // in place, exclusive
