@@ -9,8 +9,10 @@
 // the row-resident radix select keeps the top k of each row.
 //
 // Attention: one workgroup per (query block, group); each wave owns one query
-// head and the 64 queries of the block, so the 4 heads of a group share every
-// gathered K/V tile.  Per 64-key tile the wave computes S^T = K Q^T and
+// head and 32 of the block's 64 queries (two waves per head, so a wave needs
+// few enough registers for two waves to share each SIMD and overlap one's
+// matrix-core products with the other's softmax); the heads of a group share
+// every gathered K/V tile.  Per 64-key tile the wave computes S^T = K Q^T and
 // O^T += V^T P^T on the matrix cores (v_mfma_f32_32x32x16_bf16, fp32
 // accumulate).  In this transposed form a lane holds one query's scores, so
 // the online softmax needs one cross-lane exchange per row, and the fp32 S^T
@@ -172,17 +174,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// HB query heads of one group per workgroup (one wave each); a group of G >
-// HB heads takes G / HB workgroups.
+// HB query heads of one group per workgroup (two waves each, 32 queries per
+// wave); a group of G > HB heads takes G / HB workgroups.
 template <int HB>
-__global__ void __launch_bounds__(HB * 64)
+__global__ void __launch_bounds__(HB * 2 * 64)
 k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_pool,
                const bf16_raw* __restrict__ v_pool, const int32_t* __restrict__ pt,
                const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int32_t cap,
                int32_t N, Shape s, float s_att, void* __restrict__ out, int32_t out_bf16,
                float* __restrict__ lse) {
   constexpr int D = 128;
-  constexpr int NT = HB * 64;
+  constexpr int NBQ = 1;        // 32-query blocks per wave
+  constexpr int WPH = 2 / NBQ;  // waves per head
+  constexpr int NT = HB * WPH * 64;
   constexpr int PIECES = kKT * (D * 2 / 16);  // 16-byte pieces per tile per tensor
   constexpr int LPT = (PIECES + NT - 1) / NT;
   const int nblk = (N + kQB - 1) / kQB;
@@ -193,7 +197,8 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   const int blk = nblk - 1 - item / s.Hkv;
   const int g = item % s.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int h = g * G + sub * HB + wave;
+  const int h = g * G + sub * HB + wave / WPH;
+  const int qpart = wave % WPH;
   const int half = lane >> 5, l32 = lane & 31;
   const int row = blk * s.Hkv + g;
   int32_t nl = count[row];
@@ -212,10 +217,10 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 
   // Q as the B operand of S^T = K Q^T: Qb[nb][ks] holds query nb*32 + l32,
   // dims ks*16 + 8*half .. +7
-  bf16x8_t Qb[2][8];
+  bf16x8_t Qb[NBQ][8];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int32_t qi = q0 + nb * 32 + l32;
+  for (int nb = 0; nb < NBQ; ++nb) {
+    const int32_t qi = q0 + (qpart * NBQ + nb) * 32 + l32;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -281,14 +286,19 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][NBQ];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  float m_run[NBQ], l_run[NBQ];
+#pragma unroll
+  for (int nb = 0; nb < NBQ; ++nb) {
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.f;
+  }
   const float sl2 = s_att * 1.4426950408889634f;  // scores in log2 units
 
   gather(0);
@@ -301,11 +311,11 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     const int nt = diag ? nq : min(kKT, nl - tile * kKT);
 
     // S^T[key][query] for the 64 keys x 64 queries of this wave's head
-    f32x16_t S[2][2];
+    f32x16_t S[2][NBQ];
 #pragma unroll
     for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) S[mk][nb][v] = 0.f;
 #pragma unroll
@@ -315,7 +325,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
         const uint4 a = *reinterpret_cast<const uint4*>(Ks[buf] + (mk * 32 + l32) * kKPitch + ks * 32 + half * 16);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NBQ; ++nb)
           S[mk][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Qb[nb][ks], S[mk][nb], 0, 0, 0);
       }
     }
@@ -325,10 +335,10 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     // exceeds it by more than kLazy (so P stays below 2^kLazy): the output
     // accumulator is rescaled on those tiles only.
     const bool masked = diag || nt < kKT;
-    float mt[2];
+    float mt[NBQ];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int qloc = nb * 32 + l32;
+    for (int nb = 0; nb < NBQ; ++nb) {
+      const int qloc = (qpart * NBQ + nb) * 32 + l32;
       if (masked) {
 #pragma unroll
         for (int mk = 0; mk < 2; ++mk)
@@ -345,12 +355,17 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
         for (int v = 0; v < 16; ++v) m = fmaxf(m, S[mk][nb][v]);
       mt[nb] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
     }
-    const bool raise0 = mt[0] > m_run[0] + kLazy, raise1 = mt[1] > m_run[1] + kLazy;
-    if (__ballot(raise0 || raise1)) {
-      float alpha[2];
+    bool raise[NBQ], any_raise = false;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bool r = nb == 0 ? raise0 : raise1;
+    for (int nb = 0; nb < NBQ; ++nb) {
+      raise[nb] = mt[nb] > m_run[nb] + kLazy;
+      any_raise = any_raise || raise[nb];
+    }
+    if (__ballot(any_raise)) {
+      float alpha[NBQ];
+#pragma unroll
+      for (int nb = 0; nb < NBQ; ++nb) {
+        const bool r = raise[nb];
         const float m_new = r ? mt[nb] : m_run[nb];
         alpha[nb] = r ? __builtin_amdgcn_exp2f(m_run[nb] - m_new) : 1.f;  // 0 on the first raise
         l_run[nb] *= alpha[nb];
@@ -359,12 +374,12 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBQ; ++nb) {
       const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
       float lt = 0.f;
 #pragma unroll
@@ -382,9 +397,9 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int mk = st >> 1, hv = (st & 1) * 8;
-      bf16x8_t Pb[2];
+      bf16x8_t Pb[NBQ];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+      for (int nb = 0; nb < NBQ; ++nb) {
         uint4 pw;
         pw.x = pack_bf16x2(S[mk][nb][hv + 0], S[mk][nb][hv + 1]);
         pw.y = pack_bf16x2(S[mk][nb][hv + 2], S[mk][nb][hv + 3]);
@@ -400,7 +415,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
         const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (kbase + 8) * 2);
         const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NBQ; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Pb[nb], acc[mb][nb], 0, 0, 0);
       }
     }
@@ -411,8 +426,8 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   // normalise and store: lane holds d = mb*32 + 8*(v/4) + 4*half + v%4 of
   // query nb*32 + l32
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int32_t qi = q0 + nb * 32 + l32;
+  for (int nb = 0; nb < NBQ; ++nb) {
+    const int32_t qi = q0 + (qpart * NBQ + nb) * 32 + l32;
     if (qi >= N) continue;
     const float inv = l_run[nb] > 0.f ? 1.f / l_run[nb] : 0.f;
     const int64_t obase = ((int64_t)qi * s.Hq + h) * D;
@@ -514,10 +529,10 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
   const int HB = G < 4 ? G : 4;
   dim3 grid(nblk * s.Hkv * (G / HB));
 #define SA_PA(HH)                                                                           \
-  k_prefill_attn<HH><<<grid, HH * 64, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)k_pool,  \
-                                               (const bf16_raw*)v_pool, pg.page_table, idx,  \
-                                               count, cap, n_tokens, s, s_att, out,          \
-                                               out_dt == SA_BF16, lse)
+  k_prefill_attn<HH><<<grid, HH * 2 * 64, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)k_pool, \
+                                                   (const bf16_raw*)v_pool, pg.page_table, idx, \
+                                                   count, cap, n_tokens, s, s_att, out,         \
+                                                   out_dt == SA_BF16, lse)
   switch (HB) {
     case 1: SA_PA(1); break;
     case 2: SA_PA(2); break;
