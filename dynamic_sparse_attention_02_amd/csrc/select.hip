@@ -533,6 +533,29 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   __shared__ uint32_t kcache[kCacheRounds * kThreads];
   const int cached_end = kRowRegs + kCacheRounds;  // rounds [kRowRegs, cached_end) live in LDS
 
+  // Visit rounds [kRowRegs, rounds): LDS-cached rounds one at a time, then
+  // the score-row rounds 8 at a time with their loads issued together
+  // (branch-free: an out-of-range lane reads the row's last score and gets
+  // key 0).
+  auto for_rounds = [&](auto&& fn) {
+    const int c_end = rounds < cached_end ? rounds : cached_end;
+    for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * kThreads + t]);
+    const int32_t last = n > 0 ? n - 1 : 0;
+    for (int i0 = c_end; i0 < rounds; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        v[u] = xr[e < n ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        if (i0 + u < rounds) fn(i0 + u, e < n ? score_key(v[u]) : 0u);
+      }
+    }
+  };
+
   uint32_t keys[kRowRegs];
   uint32_t mk = 0;
 #pragma unroll
@@ -541,17 +564,40 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     keys[i] = e < n ? score_key(xr[e]) : 0u;
     mk = keys[i] > mk ? keys[i] : mk;
   }
-  for (int i = kRowRegs; i < rounds && i < cached_end; ++i) {
-    const int32_t e = i * kThreads + t;
-    const uint32_t k = e < n ? score_key(xr[e]) : 0u;
-    kcache[(i - kRowRegs) * kThreads + t] = k;
-    mk = k > mk ? k : mk;
+  {
+    const int32_t last = n > 0 ? n - 1 : 0;
+    const int c_end = rounds < cached_end ? rounds : cached_end;
+    for (int i0 = kRowRegs; i0 < c_end; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        v[u] = xr[e < n ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        if (i0 + u < c_end) {
+          const uint32_t k = e < n ? score_key(v[u]) : 0u;
+          kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
+          mk = k > mk ? k : mk;
+        }
+      }
+    }
   }
   if (TOPP) {  // the row maximum (mass reference) needs every key
-    for (int i = cached_end; i < rounds; ++i) {
-      const int32_t e = i * kThreads + t;
-      if (e < n) {
-        const uint32_t k = score_key(xr[e]);
+    const int32_t last = n > 0 ? n - 1 : 0;
+    for (int i0 = cached_end; i0 < rounds; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        v[u] = xr[e < n ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        const uint32_t k = e < n ? score_key(v[u]) : 0u;
         mk = k > mk ? k : mk;
       }
     }
@@ -598,10 +644,9 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
 #pragma unroll
     for (int i = 0; i < kRowRegs; ++i)
       if (i * kThreads + t < n) add(keys[i]);
-    for (int i = kRowRegs; i < rounds; ++i) {
-      const int32_t e = i * kThreads + t;
-      if (e < n) add(i < cached_end ? kcache[(i - kRowRegs) * kThreads + t] : score_key(xr[e]));
-    }
+    for_rounds([&](int i, uint32_t k) {
+      if (i * kThreads + t < n) add(k);
+    });
     __syncthreads();
     // block scan over bins in descending order: thread t owns positions
     // [t*per, (t+1)*per), position q <-> bin NB-1-q
@@ -707,11 +752,6 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const int32_t last_w = Lt - (n - 1) * unit;  // tokens of the last candidate (unit > 1)
   // tie ranks reuse the count histogram's LDS (no longer needed)
   uint32_t* eqoff = hcnt;
-  auto key_at = [&](int i) -> uint32_t {  // rounds beyond the register-resident ones
-    const int32_t e = i * kThreads + t;
-    if (i < cached_end) return kcache[(i - kRowRegs) * kThreads + t];
-    return e < n ? score_key(xr[e]) : 0u;
-  };
   auto scan_slices = [&](uint32_t* arr) -> uint32_t {  // in place, exclusive
     const uint32_t v0 = (2 * t < n_slices) ? arr[2 * t] : 0u;
     const uint32_t v1 = (2 * t + 1 < n_slices) ? arr[2 * t + 1] : 0u;
@@ -730,10 +770,10 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
         if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
       }
     }
-    for (int i = kRowRegs; i < rounds; ++i) {
-      const uint64_t m = __ballot((i * kThreads + t < n) && key_at(i) == thr);
+    for_rounds([&](int i, uint32_t k) {
+      const uint64_t m = __ballot((i * kThreads + t < n) && k == thr);
       if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
-    }
+    });
     __syncthreads();
     scan_slices(eqoff);
   }
@@ -766,7 +806,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
 #pragma unroll
   for (int i = 0; i < kRowRegs; ++i)
     if (i < rounds) count_slice(i, keys[i]);
-  for (int i = kRowRegs; i < rounds; ++i) count_slice(i, key_at(i));
+  for_rounds([&](int i, uint32_t k) { count_slice(i, k); });
   __syncthreads();
   const uint32_t total = scan_slices(slice);
   const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
@@ -795,7 +835,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
 #pragma unroll
   for (int i = 0; i < kRowRegs; ++i)
     if (i < rounds) emit(i, keys[i]);
-  for (int i = kRowRegs; i < rounds; ++i) emit(i, key_at(i));
+  for_rounds([&](int i, uint32_t k) { emit(i, k); });
   if (staged) {  // block-uniform
     __syncthreads();
     for (uint32_t o = t; o < T; o += kThreads)
