@@ -558,11 +558,30 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
 
   uint32_t keys[kRowRegs];
   uint32_t mk = 0;
+  {
+    // 8 rounds per batch, loads issued together (rounds past the row skip
+    // whole batches; lanes past it read the last score and get key 0)
+    const int32_t last = n > 0 ? n - 1 : 0;
 #pragma unroll
-  for (int i = 0; i < kRowRegs; ++i) {
-    const int32_t e = i * kThreads + t;
-    keys[i] = e < n ? score_key(xr[e]) : 0u;
-    mk = keys[i] > mk ? keys[i] : mk;
+    for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
+      if (i0 < rounds) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t e = (i0 + u) * kThreads + t;
+          v[u] = xr[e < n ? e : last];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t e = (i0 + u) * kThreads + t;
+          keys[i0 + u] = e < n ? score_key(v[u]) : 0u;
+          mk = keys[i0 + u] > mk ? keys[i0 + u] : mk;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) keys[i0 + u] = 0u;
+      }
+    }
   }
   {
     const int32_t last = n > 0 ? n - 1 : 0;
