@@ -34,12 +34,20 @@ Parity status of each function (what pins it, from the tests in
 * ``prefill_*``          pinned: early blocks equal dense causal attention
                          (torch SDPA, is_causal), segment permutation
                          invariance, query covariance.
+* ``rla_*``              pinned: single-token state is the outer product;
+                         zero keys give the plain mean of the unselected
+                         values; one unselected token returns its value; a
+                         full support leaves nothing; the subtraction form
+                         equals the direct sum; linear in V, invariant under
+                         a joint key/value permutation.
 
 Parity unpinned (our readings, fixed only by our own written definitions, no
 worked example on the pages): the indexer scale ``s_idx``, the mean over a
 group's heads (and over a query block) of the projected query, the union of
 the always-kept sink/window tokens after selection, the log-domain mean over a
-group's heads of the page score, and the partial-page term log(n/page).
+group's heads of the page score, the partial-page term log(n/page), and the
+residual linear attention's feature map on the raw (unscaled) query/key rows
+with the unselected set taken as the complement of the final support.
 """
 
 from .sparse_attention import *  # noqa: F401,F403

@@ -17,7 +17,11 @@ against the pages:
   budget k is a runtime knob).
 * "SPLA: Block Sparse Plus Linear Attention" -- section 2.1 (block score from a
   second-order Taylor expansion around the block mean, exp(q.kbar) times
-  (1 + q^T Cov(k) q / 2), with the covariance replaced by its diagonal).
+  (1 + q^T Cov(k) q / 2), with the covariance replaced by its diagonal);
+  section 2.2 (residual linear attention over the blocks left out of the
+  support, with the parameter-free exponential feature map, computed by
+  subtracting the selected blocks' linear-attention terms from a global
+  state).
 * "Sparser Block-Sparse Attention via Token Permutation" (PBS-Attn) -- section 1
   (attention output is invariant to a joint permutation of key/value pairs and
   covariant with a permutation of the queries).
@@ -57,6 +61,10 @@ __all__ = [
     "prefill_block_attend",
     "group_of_head",
     "heads_of_group",
+    "rla_feature",
+    "rla_state",
+    "rla_unselected",
+    "rla_by_subtraction",
 ]
 
 
@@ -379,3 +387,59 @@ def prefill_block_attend(Q_blk, K, V, S, blk: int, b_sel: int, s_att: float):
         o[i] = oi
         lse[i] = li
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Residual linear attention over the unselected tokens (SPLA section 2.2)
+# ---------------------------------------------------------------------------
+
+
+def rla_feature(x) -> np.ndarray:
+    """The parameter-free exponential feature map, applied elementwise:
+    phi(x)_i = exp(x_i) (reading: on the raw query/key rows, no scale)."""
+    return np.exp(f64(x))
+
+
+def rla_state(K, V):
+    """Global linear-attention state of one key/value group over all n
+    cached tokens: S = sum_j phi(k_j) v_j^T  [d, d_v]  and  z = sum_j phi(k_j)
+    [d].  (The recurrent state the page keeps; built here from scratch.)"""
+    phk = rla_feature(K)
+    return phk.T @ f64(V), phk.sum(axis=0)
+
+
+def rla_unselected(q_heads, K, V, support):
+    """Residual linear attention of each head over the tokens NOT in the
+    support, as direct sums (the definition):
+        num_h = sum_{j not in S} (phi(q_h) . phi(k_j)) v_j      [d_v]
+        den_h = sum_{j not in S}  phi(q_h) . phi(k_j)
+    and o_rla_h = num_h / den_h (the caller normalises; the page applies a
+    learned RMS norm and gate on top, outside this path).
+    q_heads [G, d], K/V [n, d], support: token indices -> (num [G, d_v], den [G])."""
+    q_heads, K, V = f64(q_heads), f64(K), f64(V)
+    n = K.shape[0]
+    keep = np.ones(n, dtype=bool)
+    keep[np.asarray(support, dtype=np.int64)] = False
+    G = q_heads.shape[0]
+    num = np.zeros((G, V.shape[1]))
+    den = np.zeros(G)
+    phq = rla_feature(q_heads)
+    for h in range(G):
+        for j in np.nonzero(keep)[0]:
+            w = float(phq[h] @ rla_feature(K[j]))
+            num[h] += w * V[j]
+            den[h] += w
+    return num, den
+
+
+def rla_by_subtraction(q_heads, S_all, z_all, K_sel, V_sel):
+    """The IO-efficient form of the same quantity: the global state's terms
+    minus the selected tokens' terms, so unselected keys and values are never
+    read again:  num_h = phi(q_h)^T S_all - sum_{j in S} (phi(q_h).phi(k_j)) v_j,
+    den_h = phi(q_h) . z_all - sum_{j in S} phi(q_h) . phi(k_j)."""
+    phq = rla_feature(q_heads)
+    phk = rla_feature(K_sel)
+    w = phq @ phk.T                       # [G, |S|]
+    num = phq @ f64(S_all) - w @ f64(V_sel)
+    den = phq @ f64(z_all) - w.sum(axis=1)
+    return num, den

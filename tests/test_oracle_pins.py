@@ -506,3 +506,87 @@ def test_prefill_support_excludes_own_block_and_is_topk():
     assert len(S) == k and S.max() < blk * b_sel
     x = kt[: blk * b_sel] @ qc
     assert x[S].min() > np.delete(x, S).max()
+
+
+# ---------------------------------------------------------------------------
+# Residual linear attention over the unselected tokens (SPLA section 2.2)
+# ---------------------------------------------------------------------------
+
+
+def _rla_case(seed, n=40, d=8, G=3, scale=0.5):
+    rng = _rng(seed)
+    q = rng.standard_normal((G, d)) * scale
+    K = rng.standard_normal((n, d)) * scale
+    V = rng.standard_normal((n, d))
+    return q, K, V
+
+
+def test_rla_state_single_token_is_outer_product():
+    k = np.array([[0.5, -1.0, 0.0]])
+    v = np.array([[2.0, 3.0, -1.0]])
+    S, z = O.rla_state(k, v)
+    e = np.exp(k[0])
+    for i in range(3):
+        for j in range(3):
+            assert S[i, j] == e[i] * v[0, j]
+    assert np.array_equal(z, e)
+
+
+def test_rla_zero_keys_give_mean_of_unselected_values():
+    """k = 0: every key's feature is all ones, so all weights are equal and
+    num / den is the plain mean of the unselected values."""
+    q, _, V = _rla_case(31)
+    K = np.zeros((V.shape[0], q.shape[1]))
+    support = [0, 3, 7, 8, 20]
+    num, den = O.rla_unselected(q, K, V, support)
+    rest = np.delete(V, support, axis=0)
+    for h in range(q.shape[0]):
+        np.testing.assert_allclose(num[h] / den[h], rest.mean(axis=0), rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(den[h], len(rest) * np.exp(q[h]).sum(), rtol=1e-13)
+
+
+def test_rla_single_unselected_token_returns_its_value():
+    q, K, V = _rla_case(32, n=6)
+    support = [0, 1, 2, 4, 5]
+    num, den = O.rla_unselected(q, K, V, support)
+    for h in range(q.shape[0]):
+        w = np.exp(q[h] + K[3]).sum()   # phi(q).phi(k) = sum_i exp(q_i + k_i)
+        np.testing.assert_allclose(den[h], w, rtol=1e-13)
+        np.testing.assert_allclose(num[h] / den[h], V[3], rtol=1e-12, atol=1e-13)
+
+
+def test_rla_full_support_leaves_nothing():
+    q, K, V = _rla_case(33)
+    num, den = O.rla_unselected(q, K, V, np.arange(K.shape[0]))
+    assert np.all(num == 0) and np.all(den == 0)
+    S_all, z_all = O.rla_state(K, V)
+    num2, den2 = O.rla_by_subtraction(q, S_all, z_all, K, V)
+    np.testing.assert_allclose(num2, 0, atol=1e-12 * np.abs(q).max() * np.abs(S_all).max())
+    np.testing.assert_allclose(den2, 0, atol=1e-12 * np.abs(z_all).max() * 10)
+
+
+def test_rla_subtraction_equals_direct_sum():
+    """The page's IO-efficient subtraction form and the definition agree (the
+    identity the fused kernel relies on)."""
+    q, K, V = _rla_case(34, n=60)
+    rng = _rng(35)
+    support = np.sort(rng.choice(60, 17, replace=False))
+    num, den = O.rla_unselected(q, K, V, support)
+    S_all, z_all = O.rla_state(K, V)
+    num2, den2 = O.rla_by_subtraction(q, S_all, z_all, K[support], V[support])
+    np.testing.assert_allclose(num2, num, rtol=1e-10, atol=1e-10 * np.abs(num).max())
+    np.testing.assert_allclose(den2, den, rtol=1e-12)
+
+
+def test_rla_linear_in_values_and_permutation_invariant():
+    q, K, V = _rla_case(36, n=30)
+    support = [2, 5, 11]
+    num, den = O.rla_unselected(q, K, V, support)
+    num2, den2 = O.rla_unselected(q, K, 2.0 * V, support)
+    np.testing.assert_allclose(num2, 2.0 * num, rtol=1e-13)
+    np.testing.assert_array_equal(den2, den)
+    perm = _rng(37).permutation(30)
+    inv = np.argsort(perm)
+    num3, den3 = O.rla_unselected(q, K[perm], V[perm], inv[support])
+    np.testing.assert_allclose(num3, num, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(den3, den, rtol=1e-12)
