@@ -103,10 +103,10 @@ size_t select_ws(const sa_shape* s, int64_t max_cand) {
   return sa::align_up(sa::select_workspace_bytes(s->batch * s->n_kv_heads, (int32_t)max_cand), 256);
 }
 
-size_t decode_ws(const sa_shape* s, int64_t cap) {
+size_t decode_ws(const sa_shape* s, int64_t cap, bool rla = false) {
   if (cap < 1) cap = 1;
   sa::Shape sh = to_shape(s);
-  return sa::align_up(sa::decode_workspace_bytes(sh, (int32_t)cap), 256);
+  return sa::align_up(sa::decode_workspace_bytes(sh, (int32_t)cap, rla), 256);
 }
 
 #define SA_TRY(expr)            \
@@ -165,6 +165,8 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
     }
     case SA_OP_DECODE_STEP:
       return step_ws(s, param);
+    case SA_OP_SPARSE_DECODE_RLA:
+      return decode_ws(s, param, true);
   }
   return 0;
 }
@@ -301,6 +303,40 @@ sa_status sa_sparse_decode(const sa_shape* s, const sa_pages* pg, const void* q,
   SA_TRY(check_ws(ws, ws_bytes, decode_ws(s, cap), fn));
   return hip_status(sa::launch_sparse_decode(to_shape(s), *pg, q, k_pool, v_pool, dt, idx, count,
                                              cap, s_att, out, out_dt, lse, ws, st), fn);
+}
+
+sa_status sa_sparse_decode_rla(const sa_shape* s, const sa_pages* pg, const void* q,
+                               const void* k_pool, const void* v_pool, sa_dtype dt,
+                               const int32_t* idx, const int32_t* count, int32_t cap, float s_att,
+                               void* out, sa_dtype out_dt, float* lse, const float* rla_state,
+                               float* rla_num, float* rla_den, void* ws, size_t ws_bytes,
+                               hipStream_t st) {
+  const char* fn = "sa_sparse_decode_rla";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, true, fn));
+  if (!valid_dtype(dt) || !valid_dtype(out_dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !k_pool || !v_pool || !idx || !count || !out || !rla_state || !rla_num || !rla_den)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
+  SA_TRY(check_ws(ws, ws_bytes, decode_ws(s, cap, true), fn));
+  return hip_status(sa::launch_sparse_decode_rla(to_shape(s), *pg, q, k_pool, v_pool, dt, idx,
+                                                 count, cap, s_att, out, out_dt, lse, rla_state,
+                                                 rla_num, rla_den, ws, st), fn);
+}
+
+sa_status sa_rla_state(const sa_shape* s, const sa_pages* pg, const void* k_pool,
+                       const void* v_pool, sa_dtype dt, int32_t first_token, float* state,
+                       hipStream_t st) {
+  const char* fn = "sa_rla_state";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, true, fn));
+  if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!k_pool || !v_pool || !state) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (first_token < 0) return fail(SA_ERR_INVALID_ARGUMENT, "%s: first_token=%d < 0", fn, first_token);
+  return hip_status(sa::launch_rla_state(to_shape(s), *pg, k_pool, v_pool, dt, first_token, state, st), fn);
 }
 
 sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, const void* w_q,

@@ -63,13 +63,20 @@ struct DecodeCfg {
   static constexpr int DPL = D / kWave;           // head dims per lane in P.V
 };
 
-template <typename T, int D, int G>
+// RLA: also the residual linear attention terms of the listed tokens
+// ("SPLA", section 2.2): with phi = exp elementwise, per head
+//   w_j = phi(q) . phi(k_j),  num += w_j v_j,  den += w_j
+// from the K/V rows already staged for the exact attention.
+constexpr int kPhiPitch = 4;  // extra floats per phi(K) row in LDS (bank spread)
+
+template <typename T, int D, int G, bool RLA>
 __global__ void __launch_bounds__((G < 4 ? G : 4) * 64)
 k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
                const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
                const int32_t* __restrict__ idx, const int32_t* __restrict__ count, int32_t cap,
                Shape s, float s_att, int32_t nchunk_max,
-               float* __restrict__ part_ml, float* __restrict__ part_o) {
+               float* __restrict__ part_ml, float* __restrict__ part_o,
+               float* __restrict__ part_rnum, float* __restrict__ part_rden) {
   using C = DecodeCfg<T, D, G>;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int rows = s.B * s.Hkv;
@@ -78,6 +85,9 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   __shared__ __align__(16) char Vs[kTile * C::PITCH];
   __shared__ __align__(16) T Qs[G][D];
   __shared__ __align__(16) float Ps[G][kTile];
+  __shared__ __align__(16) float PhiK[RLA ? kTile : 1][RLA ? D + kPhiPitch : 1];
+  __shared__ __align__(16) float PhiQ[RLA ? G : 1][RLA ? D : 1];
+  __shared__ __align__(16) float Ws[RLA ? G : 1][RLA ? kTile : 1];
   __shared__ int32_t prefix[kMaxRowsLds + 1];
   __shared__ int64_t s_tiles;
   __shared__ int32_t s_red[4];
@@ -126,8 +136,20 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
     const int32_t* list = idx + (int64_t)row * cap;
 
     __syncthreads();  // previous item done with Qs
-    for (int i = tid; i < G * D; i += C::NT)
-      Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
+    for (int i = tid; i < G * D; i += C::NT) {
+      const T qv = q[((int64_t)b * s.Hq + g * G) * D + i];
+      Qs[i / D][i % D] = qv;
+      if (RLA) PhiQ[i / D][i % D] = __expf(to_f32<T>(qv));
+    }
+    float racc[RLA ? C::HPW : 1][RLA ? C::DPL : 1], rden[RLA ? C::HPW : 1];
+    if (RLA) {
+#pragma unroll
+      for (int hh = 0; hh < C::HPW; ++hh) {
+        rden[hh] = 0.f;
+#pragma unroll
+        for (int e = 0; e < C::DPL; ++e) racc[hh][e] = 0.f;
+      }
+    }
 
     float m_run[C::HPW], l_run[C::HPW], acc[C::HPW][C::DPL];
 #pragma unroll
@@ -178,6 +200,21 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
         const int r = pc / C::CPR, col = pc % C::CPR;
         *reinterpret_cast<uint4*>(Ks + r * C::PITCH + col * 16) = kr[i];
         *reinterpret_cast<uint4*>(Vs + r * C::PITCH + col * 16) = vr[i];
+        if (RLA) {
+          constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
+          const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+          float* dst = &PhiK[r][col * EPP];
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              dst[2 * e] = __expf(__uint_as_float(w[e] << 16));
+              dst[2 * e + 1] = __expf(__uint_as_float(w[e] & 0xffff0000u));
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[e] = __expf(__uint_as_float(w[e]));
+          }
+        }
       }
       __syncthreads();
       if (ts + kTile < t1) {  // next tile's rows in flight, and the addresses after it
@@ -228,6 +265,32 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
         m_run[hh] = m_new;
         Ps[wave * C::HPW + hh][lane] = p;
       }
+      if (RLA) {  // w = phi(q_h) . phi(k_lane)
+        float wv[C::HPW];
+#pragma unroll
+        for (int hh = 0; hh < C::HPW; ++hh) wv[hh] = 0.f;
+        const float* prow = &PhiK[lane][0];
+#pragma unroll 4
+        for (int i = 0; i < D; i += 4) {
+          const float4 pk = *reinterpret_cast<const float4*>(prow + i);
+#pragma unroll
+          for (int hh = 0; hh < C::HPW; ++hh) {
+            const float4 pq = *reinterpret_cast<const float4*>(&PhiQ[wave * C::HPW + hh][i]);
+            float a = wv[hh];
+            a = fmaf(pq.x, pk.x, a);
+            a = fmaf(pq.y, pk.y, a);
+            a = fmaf(pq.z, pk.z, a);
+            a = fmaf(pq.w, pk.w, a);
+            wv[hh] = a;
+          }
+        }
+#pragma unroll
+        for (int hh = 0; hh < C::HPW; ++hh) {
+          const float w = lane < nt ? wv[hh] : 0.f;
+          rden[hh] += wave_sum(w);
+          Ws[wave * C::HPW + hh][lane] = w;
+        }
+      }
       __syncthreads();
       // P.V: lane owns DPL consecutive dims of the wave's heads
 #pragma unroll
@@ -235,10 +298,12 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
 #pragma unroll
         for (int e = 0; e < C::DPL; ++e) acc[hh][e] *= alpha[hh];
       for (int t = 0; t < kTile; t += 4) {
-        float4 pv[C::HPW];
+        float4 pv[C::HPW], wv4[RLA ? C::HPW : 1];
 #pragma unroll
-        for (int hh = 0; hh < C::HPW; ++hh)
+        for (int hh = 0; hh < C::HPW; ++hh) {
           pv[hh] = *reinterpret_cast<const float4*>(&Ps[wave * C::HPW + hh][t]);
+          if (RLA) wv4[hh] = *reinterpret_cast<const float4*>(&Ws[wave * C::HPW + hh][t]);
+        }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           float vv[C::DPL];
@@ -262,6 +327,11 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
             const float p = u == 0 ? pv[hh].x : (u == 1 ? pv[hh].y : (u == 2 ? pv[hh].z : pv[hh].w));
 #pragma unroll
             for (int e = 0; e < C::DPL; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+            if (RLA) {
+              const float w = u == 0 ? wv4[hh].x : (u == 1 ? wv4[hh].y : (u == 2 ? wv4[hh].z : wv4[hh].w));
+#pragma unroll
+              for (int e = 0; e < C::DPL; ++e) racc[hh][e] = fmaf(w, vv[e], racc[hh][e]);
+            }
           }
         }
       }
@@ -277,6 +347,11 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
       }
 #pragma unroll
       for (int e = 0; e < C::DPL; ++e) part_o[pi * D + lane * C::DPL + e] = acc[hh][e];
+      if (RLA) {
+        if (lane == 0) part_rden[pi] = rden[hh];
+#pragma unroll
+        for (int e = 0; e < C::DPL; ++e) part_rnum[pi * D + lane * C::DPL + e] = racc[hh][e];
+      }
     }
   }
 }
@@ -287,11 +362,17 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
 constexpr int kCombThreads = 256;
 constexpr int kMaxChunkW = 4096;  // chunk weights kept in LDS
 
-template <typename TO>
+// With RLA, also the residual linear attention over the unselected tokens by
+// subtraction: num = phi(q)^T S_all - sum_chunks num_sel, den = phi(q) . z_all
+// - sum_chunks den_sel (state [B][Hkv][D][D + 1], column D = z).
+template <typename TO, typename TQ, bool RLA>
 __global__ void __launch_bounds__(kCombThreads)
 k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ part_o,
                  const int32_t* __restrict__ count, int32_t cap, Shape s, int32_t split_grid,
-                 int32_t nchunk_max, TO* __restrict__ out, float* __restrict__ lse) {
+                 int32_t nchunk_max, TO* __restrict__ out, float* __restrict__ lse,
+                 const TQ* __restrict__ q, const float* __restrict__ rla_state,
+                 const float* __restrict__ part_rnum, const float* __restrict__ part_rden,
+                 float* __restrict__ rla_num, float* __restrict__ rla_den) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int G = s.Hq / s.Hkv;
   const int row = b * s.Hkv + h / G;
@@ -347,6 +428,99 @@ k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ pa
     out[((int64_t)b * s.Hq + h) * D + d] = from_f32<TO>(nch ? t / lsum : 0.f);
   }
   if (lse && tid == 0) lse[(int64_t)b * s.Hq + h] = nch ? M + logf(lsum) : -INFINITY;
+  if (RLA) {
+    __shared__ float phq[128];
+    __shared__ float rred[kCombThreads], dred[kCombThreads];
+    const TQ* qh = q + ((int64_t)b * s.Hq + h) * D;
+    for (int i = tid; i < D; i += kCombThreads) phq[i] = __expf(to_f32<TQ>(qh[i]));
+    __syncthreads();
+    const float* st = rla_state + ((int64_t)b * s.Hkv + h / G) * D * (D + 1);
+    // phi(q)^T S_all for dim d over rows i = gi, gi + NG, ...; z with it
+    float a = 0.f, zz = 0.f;
+    for (int i = gi; i < D; i += NG) {
+      a = fmaf(phq[i], st[(int64_t)i * (D + 1) + d], a);
+      if (d == 0) zz = fmaf(phq[i], st[(int64_t)i * (D + 1) + D], zz);
+    }
+    // selected terms of the chunks, in chunk order
+    float sn = 0.f, sd = 0.f;
+    for (int c = gi; c < nch; c += NG) {
+      sn += part_rnum[(base + c) * D + d];
+      if (d == 0) sd += part_rden[base + c];
+    }
+    rred[tid] = a - sn;
+    dred[tid] = zz - sd;
+    __syncthreads();
+    if (gi == 0) {
+      float t = 0.f, td = 0.f;
+      for (int k = 0; k < NG; ++k) {
+        t += rred[k * D + d];
+        td += dred[k * D + d];
+      }
+      rla_num[((int64_t)b * s.Hq + h) * D + d] = t;
+      if (d == 0) rla_den[(int64_t)b * s.Hq + h] = td;
+    }
+  }
+}
+
+// Residual linear attention state ("SPLA", section 2.2): for each (sequence,
+// group), S[i][c] += sum_j exp(k_j[i]) v_j[c] and z[i] += sum_j exp(k_j[i])
+// over tokens j in [first, seq_lens[b]).  Workgroup = 16 rows of S (a
+// stripe); thread (r, cg) owns row r's columns cg, cg + 16, ... and, for
+// cg = 0, z[r].  Tokens go through LDS 32 at a time; fixed summation order.
+constexpr int kRlaTok = 32;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256)
+k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
+            const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+            Shape s, int32_t first, float* __restrict__ state) {
+  constexpr int NC = D / 16;  // columns per thread
+  const int stripe = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int t = threadIdx.x, r = t / 16, cg = t % 16;
+  const int i = stripe * 16 + r;
+  const int32_t L = clamp_len(seq_lens[b], s.max_len);
+  const int32_t* pt = page_table + (int64_t)b * s.max_pages;
+  __shared__ float phk[kRlaTok][16];
+  __shared__ float vs[kRlaTok][D];
+  float acc[NC], zacc = 0.f;
+#pragma unroll
+  for (int m = 0; m < NC; ++m) acc[m] = 0.f;
+  for (int32_t j0 = first < 0 ? 0 : first; j0 < L; j0 += kRlaTok) {
+    __syncthreads();
+    // K: 32 tokens x this stripe's 16 dims; V: 32 tokens x D dims
+    for (int e = t; e < kRlaTok * 16; e += 256) {
+      const int tk = e / 16, dd = e % 16;
+      const int32_t j = j0 + tk;
+      float v = 0.f;
+      if (j < L) {
+        const int64_t row = (clamp_page(pt[j >> 6], s.n_pool_pages) * s.Hkv + g) * kPage + (j & 63);
+        v = __expf(to_f32<T>(k_pool[row * D + stripe * 16 + dd]));
+      }
+      phk[tk][dd] = v;
+    }
+    for (int e = t; e < kRlaTok * D; e += 256) {
+      const int tk = e / D, dd = e % D;
+      const int32_t j = j0 + tk;
+      float v = 0.f;
+      if (j < L) {
+        const int64_t row = (clamp_page(pt[j >> 6], s.n_pool_pages) * s.Hkv + g) * kPage + (j & 63);
+        v = to_f32<T>(v_pool[row * D + dd]);
+      }
+      vs[tk][dd] = v;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int tk = 0; tk < kRlaTok; ++tk) {
+      const float p = phk[tk][r];
+#pragma unroll
+      for (int m = 0; m < NC; ++m) acc[m] = fmaf(p, vs[tk][cg + 16 * m], acc[m]);
+      zacc += p;
+    }
+  }
+  float* st = state + ((int64_t)b * s.Hkv + g) * D * (D + 1) + (int64_t)i * (D + 1);
+#pragma unroll
+  for (int m = 0; m < NC; ++m) st[cg + 16 * m] += acc[m];
+  if (cg == 0) st[D] += zacc;
 }
 
 // Persistent grid of the split kernel: blocks resident on the chip.
@@ -361,21 +535,30 @@ int split_grid(int nchunk_max, int rows) {
   return (int)(most < g ? (most < 1 ? 1 : most) : g);
 }
 
-template <typename T, int D>
+struct RlaArgs {
+  const float* state;  // [B][Hkv][D][D + 1]
+  float* num;          // [B][Hq][D]
+  float* den;          // [B][Hq]
+};
+
+template <typename T, int D, bool RLA>
 hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const void* k_pool,
                     const void* v_pool, const int32_t* idx, const int32_t* count, int32_t cap,
                     float s_att, void* out, sa_dtype out_dt, float* lse, void* ws,
-                    hipStream_t st) {
+                    const RlaArgs& rla, hipStream_t st) {
   const int32_t nchunk_max = (cap + kTile - 1) / kTile;
+  const size_t n_part = (size_t)s.B * s.Hq * nchunk_max;
   float* part_ml = (float*)ws;
-  float* part_o = part_ml + align_up((size_t)s.B * s.Hq * nchunk_max * 2, 64);
+  float* part_o = part_ml + align_up(n_part * 2, 64);
+  float* part_rnum = part_o + align_up(n_part * D, 64);
+  float* part_rden = part_rnum + align_up(n_part * D, 64);
   const int gx = split_grid(nchunk_max, s.B * s.Hkv);
   dim3 grid(gx);
   const int G = s.Hq / s.Hkv;
-#define SA_DS(GG)                                                                        \
-  k_decode_split<T, D, GG><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(                     \
-      (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,   \
-      count, cap, s, s_att, nchunk_max, part_ml, part_o)
+#define SA_DS(GG)                                                                          \
+  k_decode_split<T, D, GG, RLA><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(                  \
+      (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,     \
+      count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden)
   switch (G) {
     case 1: SA_DS(1); break;
     case 2: SA_DS(2); break;
@@ -386,20 +569,39 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
 #undef SA_DS
   dim3 g2(s.Hq, s.B);
   if (out_dt == SA_BF16)
-    k_decode_combine<bf16_raw><<<g2, kCombThreads, 0, st>>>(part_ml, part_o, count, cap, s,
-                                                            gx, nchunk_max, (bf16_raw*)out, lse);
+    k_decode_combine<bf16_raw, T, RLA><<<g2, kCombThreads, 0, st>>>(
+        part_ml, part_o, count, cap, s, gx, nchunk_max, (bf16_raw*)out, lse, (const T*)q,
+        rla.state, part_rnum, part_rden, rla.num, rla.den);
   else
-    k_decode_combine<float><<<g2, kCombThreads, 0, st>>>(part_ml, part_o, count, cap, s, gx,
-                                                         nchunk_max, (float*)out, lse);
+    k_decode_combine<float, T, RLA><<<g2, kCombThreads, 0, st>>>(
+        part_ml, part_o, count, cap, s, gx, nchunk_max, (float*)out, lse, (const T*)q,
+        rla.state, part_rnum, part_rden, rla.num, rla.den);
   return hipGetLastError();
+}
+
+template <bool RLA>
+hipError_t launch_decode(const Shape& s, const sa_pages& pg, const void* q, const void* k_pool,
+                         const void* v_pool, sa_dtype dt, const int32_t* idx, const int32_t* count,
+                         int32_t cap, float s_att, void* out, sa_dtype out_dt, float* lse, void* ws,
+                         const RlaArgs& rla, hipStream_t st) {
+  if (s.B == 0) return hipSuccess;
+  if (dt == SA_BF16) {
+    if (s.D == 128)
+      return launch_t<bf16_raw, 128, RLA>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, rla, st);
+    return launch_t<bf16_raw, 64, RLA>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, rla, st);
+  }
+  if (s.D == 128)
+    return launch_t<float, 128, RLA>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, rla, st);
+  return launch_t<float, 64, RLA>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, rla, st);
 }
 
 }  // namespace
 
-size_t decode_workspace_bytes(const Shape& s, int32_t cap) {
-  const size_t nchunk_max = (size_t)(cap + kTile - 1) / kTile;
-  const size_t n_ml = align_up((size_t)s.B * s.Hq * nchunk_max * 2, 64);
-  return (n_ml + (size_t)s.B * s.Hq * nchunk_max * s.D) * sizeof(float);
+size_t decode_workspace_bytes(const Shape& s, int32_t cap, bool rla) {
+  const size_t n_part = (size_t)s.B * s.Hq * (size_t)((cap + kTile - 1) / kTile);
+  size_t n = align_up(n_part * 2, 64) + align_up(n_part * s.D, 64);
+  if (rla) n += align_up(n_part * s.D, 64) + align_up(n_part, 64);
+  return n * sizeof(float);
 }
 
 hipError_t launch_sparse_decode(const Shape& s, const sa_pages& pg, const void* q,
@@ -407,15 +609,41 @@ hipError_t launch_sparse_decode(const Shape& s, const sa_pages& pg, const void* 
                                 const int32_t* idx, const int32_t* count, int32_t cap,
                                 float s_att, void* out, sa_dtype out_dt, float* lse,
                                 void* ws, hipStream_t st) {
-  if (s.B == 0) return hipSuccess;
+  return launch_decode<false>(s, pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
+                              lse, ws, RlaArgs{nullptr, nullptr, nullptr}, st);
+}
+
+hipError_t launch_sparse_decode_rla(const Shape& s, const sa_pages& pg, const void* q,
+                                    const void* k_pool, const void* v_pool, sa_dtype dt,
+                                    const int32_t* idx, const int32_t* count, int32_t cap,
+                                    float s_att, void* out, sa_dtype out_dt, float* lse,
+                                    const float* rla_state, float* rla_num, float* rla_den,
+                                    void* ws, hipStream_t st) {
+  return launch_decode<true>(s, pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
+                             lse, ws, RlaArgs{rla_state, rla_num, rla_den}, st);
+}
+
+hipError_t launch_rla_state(const Shape& s, const sa_pages& pg, const void* k_pool,
+                            const void* v_pool, sa_dtype dt, int32_t first, float* state,
+                            hipStream_t st) {
+  if (s.B == 0 || s.Hkv == 0) return hipSuccess;
+  dim3 grid(s.D / 16, s.Hkv, s.B);
   if (dt == SA_BF16) {
     if (s.D == 128)
-      return launch_t<bf16_raw, 128>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, st);
-    return launch_t<bf16_raw, 64>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, st);
+      k_rla_state<bf16_raw, 128><<<grid, 256, 0, st>>>((const bf16_raw*)k_pool, (const bf16_raw*)v_pool,
+                                                       pg.page_table, pg.seq_lens, s, first, state);
+    else
+      k_rla_state<bf16_raw, 64><<<grid, 256, 0, st>>>((const bf16_raw*)k_pool, (const bf16_raw*)v_pool,
+                                                      pg.page_table, pg.seq_lens, s, first, state);
+  } else {
+    if (s.D == 128)
+      k_rla_state<float, 128><<<grid, 256, 0, st>>>((const float*)k_pool, (const float*)v_pool,
+                                                    pg.page_table, pg.seq_lens, s, first, state);
+    else
+      k_rla_state<float, 64><<<grid, 256, 0, st>>>((const float*)k_pool, (const float*)v_pool,
+                                                   pg.page_table, pg.seq_lens, s, first, state);
   }
-  if (s.D == 128)
-    return launch_t<float, 128>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, st);
-  return launch_t<float, 64>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, st);
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -219,7 +219,16 @@ struct SelectArgs {
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 
-size_t decode_workspace_bytes(const Shape& s, int32_t cap);
+size_t decode_workspace_bytes(const Shape& s, int32_t cap, bool rla = false);
+hipError_t launch_sparse_decode_rla(const Shape& s, const sa_pages& pg, const void* q,
+                                    const void* k_pool, const void* v_pool, sa_dtype dt,
+                                    const int32_t* idx, const int32_t* count, int32_t cap,
+                                    float s_att, void* out, sa_dtype out_dt, float* lse,
+                                    const float* rla_state, float* rla_num, float* rla_den,
+                                    void* ws, hipStream_t st);
+hipError_t launch_rla_state(const Shape& s, const sa_pages& pg, const void* k_pool,
+                            const void* v_pool, sa_dtype dt, int32_t first, float* state,
+                            hipStream_t st);
 hipError_t launch_sparse_decode(const Shape& s, const sa_pages& pg, const void* q,
                                 const void* k_pool, const void* v_pool, sa_dtype dt,
                                 const int32_t* idx, const int32_t* count, int32_t cap,

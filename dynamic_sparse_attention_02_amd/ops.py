@@ -27,6 +27,8 @@ __all__ = [
     "sa_select_topp",
     "sa_select_topk",
     "sa_sparse_decode",
+    "sa_sparse_decode_rla",
+    "sa_rla_state",
     "sa_decode_step",
     "sa_select_prefill_topk",
     "sa_sparse_prefill",
@@ -143,6 +145,24 @@ def sa_sparse_decode(shape, pages, q, k_pool, v_pool, idx, count, s_att, out, ls
                                    int(idx.shape[-1]), float(s_att), _dev(out), _dt(out), _dev(lse),
                                    wp, wn, _stream(stream))
     L.check(st, "sa_sparse_decode")
+
+
+def sa_sparse_decode_rla(shape, pages, q, k_pool, v_pool, idx, count, s_att, out, lse, rla_state,
+                         rla_num, rla_den, ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_sparse_decode_rla(ctypes.byref(shape), ctypes.byref(pages), _dev(q),
+                                       _dev(k_pool), _dev(v_pool), _dt(q), _dev(idx), _dev(count),
+                                       int(idx.shape[-1]), float(s_att), _dev(out), _dt(out),
+                                       _dev(lse), _dev(rla_state), _dev(rla_num), _dev(rla_den),
+                                       wp, wn, _stream(stream))
+    L.check(st, "sa_sparse_decode_rla")
+
+
+def sa_rla_state(shape, pages, k_pool, v_pool, first_token, state, stream=None):
+    st = L.load().sa_rla_state(ctypes.byref(shape), ctypes.byref(pages), _dev(k_pool),
+                               _dev(v_pool), _dt(k_pool), int(first_token), _dev(state),
+                               _stream(stream))
+    L.check(st, "sa_rla_state")
 
 
 def sa_decode_step(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att, p, top_k,

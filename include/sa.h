@@ -95,7 +95,8 @@ typedef enum {
   SA_OP_SELECT = 1,          /* param = max candidates per row (tokens or pages) */
   SA_OP_SPARSE_DECODE = 2,   /* param = cap of the support lists                 */
   SA_OP_PREFILL_SELECT = 3,  /* param = n_tokens of the prefill                  */
-  SA_OP_DECODE_STEP = 4      /* param = cap                                      */
+  SA_OP_DECODE_STEP = 4,     /* param = cap                                      */
+  SA_OP_SPARSE_DECODE_RLA = 5 /* param = cap                                     */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -210,6 +211,40 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_pages* pages, const v
                            const int32_t* idx, const int32_t* count, int32_t cap,
                            float s_att, void* out, sa_dtype out_dtype, float* lse,
                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Residual linear attention state ("SPLA", section 2.2: the tokens left out
+ * of the support are condensed into a linear-attention state; feature map
+ * phi(x) = exp(x) elementwise, applied to the raw key rows): for each sequence
+ * b and group g, over tokens j in [first_token, seq_lens[b]),
+ *   state[b][g][i][c] += sum_j exp(k_j[i]) v_j[c]   (c < head_dim)
+ *   state[b][g][i][head_dim] += sum_j exp(k_j[i])
+ * state [batch][n_kv_heads][head_dim][head_dim + 1] fp32, accumulated in
+ * place (the caller zero-fills it for a fresh build and passes the first new
+ * token to extend it); k_pool, v_pool of dtype.  Cache maintenance, off the
+ * per-step path.  Deterministic (one owner per state element, fixed order). */
+sa_status sa_rla_state(const sa_shape* shape, const sa_pages* pages, const void* k_pool,
+                       const void* v_pool, sa_dtype dtype, int32_t first_token, float* state,
+                       hipStream_t stream);
+
+/* sa_sparse_decode plus the residual linear attention over the tokens NOT in
+ * the support ("SPLA", section 2.2, subtraction form: the global state's term
+ * minus the listed tokens' terms, computed from the K/V rows the exact
+ * attention already loads, so unlisted rows are never read):
+ *   rla_num[b][h][:] = phi(q)^T S[b][g] - sum_{j in S} (phi(q) . phi(k_j)) v_j
+ *   rla_den[b][h]    = phi(q) . z[b][g] - sum_{j in S}  phi(q) . phi(k_j)
+ * with phi = exp elementwise on the raw q and k rows and (S, z) from
+ * sa_rla_state over the whole sequence.  rla_num / rla_den is the linear
+ * attention over the unlisted tokens (the learned gate and RMS norm the page
+ * applies on top stay with the caller).  rla_state as written by
+ * sa_rla_state; rla_num [batch][n_q_heads][head_dim] fp32, rla_den
+ * [batch][n_q_heads] fp32.  Other arguments, outputs and limits as
+ * sa_sparse_decode; workspace from SA_OP_SPARSE_DECODE_RLA. */
+sa_status sa_sparse_decode_rla(const sa_shape* shape, const sa_pages* pages, const void* q,
+                               const void* k_pool, const void* v_pool, sa_dtype dtype,
+                               const int32_t* idx, const int32_t* count, int32_t cap,
+                               float s_att, void* out, sa_dtype out_dtype, float* lse,
+                               const float* rla_state, float* rla_num, float* rla_den,
+                               void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* One whole decode step: sa_index_scores, then sa_select_topp (p in (0, 1])
  * or, if top_k > 0, sa_select_topk with unit 1, then sa_sparse_decode.  The

@@ -109,6 +109,14 @@ def test_validation_codes():
     assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 100, None) == L.SA_ERR_WORKSPACE
     assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, 7, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_sparse_decode(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, None, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    # decode with the residual linear attention tail: workspace covers the
+    # extra partials, NULL state; state build: negative first token
+    ws_plain = so.sa_workspace_size(L.SA_OP_SPARSE_DECODE, B(s), 65536)
+    assert so.sa_workspace_size(L.SA_OP_SPARSE_DECODE_RLA, B(s), 65536) > ws_plain
+    assert so.sa_sparse_decode_rla(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, FAKE, FAKE, FAKE, FAKE, ws_plain, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_sparse_decode_rla(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_rla_state(B(s), B(pg), FAKE, FAKE, L.SA_BF16, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_rla_state(B(s), B(pg), FAKE, FAKE, L.SA_BF16, 0, None, None) == L.SA_ERR_INVALID_ARGUMENT
     # decode step: capacity and p
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.9, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 60000, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.0, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 65536, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
