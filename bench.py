@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--warm", action="store_true",
                     help="reuse one input replica every step (cache-warm)")
+    ap.add_argument("--rla", action="store_true",
+                    help="decode workloads: the step also forms the residual linear attention "
+                         "over the unselected tokens (sa_sparse_decode_rla; state built first)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (5 dispatches): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -102,6 +105,7 @@ KERNEL_SOURCES = {
     "page_scores": ["index.hip"],
     "index_scores": ["index.hip"],
     "sparse_decode": ["decode.hip"],
+    "sparse_decode_rla": ["decode.hip"],
     "sparse_prefill": ["prefill.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
@@ -239,7 +243,14 @@ def bench_decode(args, name):
             ops.sa_index_scores(shape, pages, inp.q, inp.w_q, a, inp.s_idx, x, ws_idx)
             ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
 
-    use_step = not page_mode  # token-level selection: the library's whole-step call
+    use_step = not page_mode and not args.rla  # token-level selection: the whole-step call
+    if args.rla:  # state of every sequence's cache (maintenance, outside the timed steps)
+        rla_state = torch.zeros((B, Hkv, d, d + 1), dtype=torch.float32, device=dev)
+        ops.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, 0, rla_state)
+        rla_num = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        rla_den = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+        ws_dec = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SPARSE_DECODE_RLA, shape, cap))
+        state_bytes = rla_state.numel() * 4
     if use_step:
         ws_step = ops.alloc_workspace(ops.workspace_size(L.SA_OP_DECODE_STEP, shape, cap))
     fused = use_step and rows <= 16 and inp.G >= 4
@@ -251,14 +262,23 @@ def bench_decode(args, name):
                                out, lse, ws_step)
             return
         run_select(rep)
-        ops.sa_sparse_decode(shape, pages, inp.q, rep[1], rep[2], idx, count, inp.s_att, out, lse,
-                             ws_dec)
+        decode_call(rep)
+
+    def decode_call(rep):
+        if args.rla:
+            ops.sa_sparse_decode_rla(shape, pages, inp.q, rep[1], rep[2], idx, count, inp.s_att, out,
+                                     lse, rla_state, rla_num, rla_den, ws_dec)
+        else:
+            ops.sa_sparse_decode(shape, pages, inp.q, rep[1], rep[2], idx, count, inp.s_att, out,
+                                 lse, ws_dec)
 
     base = (cache_a, inp.k_pool, inp.v_pool)
     run_step(base)
     torch.cuda.synchronize()
     counts = count.cpu().numpy().astype(np.int64)
     kv_bytes = int(counts.sum()) * 2 * d * 2
+    if args.rla:
+        kv_bytes += state_bytes  # the decode call also reads each group's state
     index_bytes = int(sum(per_row_index_bytes[b] for b in range(B) for _ in range(Hkv)))
     step_bytes = index_bytes + kv_bytes
 
@@ -289,11 +309,10 @@ def bench_decode(args, name):
                                                        count, ws_sel) if page_mode else
                                     ops.sa_select_topp(shape, pages, x, sel["p"], n_sink,
                                                        n_window, idx, count, ws_sel)), args.steps)
-    t_decode = time_loop(lambda i: ops.sa_sparse_decode(shape, pages, inp.q, reps[i][1],
-                                                        reps[i][2], idx, count, inp.s_att,
-                                                        out, lse, ws_dec), args.steps, reps=R)
+    t_decode = time_loop(lambda i: decode_call(reps[i]), args.steps, reps=R)
     comp = {"index_scores" if not page_mode else "page_scores": (t_index, index_bytes),
-            "select": (t_select, 0), "sparse_decode": (t_decode, kv_bytes)}
+            "select": (t_select, 0),
+            ("sparse_decode_rla" if args.rla else "sparse_decode"): (t_decode, kv_bytes)}
     if fused:
         # the whole step is one kernel: its bytes are the step's
         dom, dom_ms, dom_bytes = "decode_step (single fused launch)", ms, step_bytes
@@ -316,7 +335,8 @@ def bench_decode(args, name):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name, "batch": B, "context": (Lmax if B == 1 else
+        "config": {"workload": name + ("+rla" if args.rla else ""), "batch": B,
+                   "context": (Lmax if B == 1 else
                                                               [min(inp.seq_lens), Lmax]),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "selection": ("top-%d pages (Taylor page score)" % sel["k_pages"]
@@ -327,8 +347,10 @@ def bench_decode(args, name):
         "index_bytes": index_bytes,
         "kv_bytes": kv_bytes,
         "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
-        "step_call": "sa_decode_step" + (" (fused)" if fused else "") if use_step else
-                     "sa_page_scores + sa_select_topk + sa_sparse_decode",
+        "step_call": ("sa_decode_step" + (" (fused)" if fused else "")) if use_step else
+                     ((("sa_page_scores + sa_select_topk") if page_mode else
+                       "sa_index_scores + sa_select_topp") +
+                      (" + sa_sparse_decode_rla" if args.rla else " + sa_sparse_decode")),
         "separate_calls_ms": {k: round(v[0], 5) for k, v in comp.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
