@@ -245,7 +245,7 @@ def bench_decode(args, name):
 
     use_step = not page_mode and not args.rla  # token-level selection: the whole-step call
     if args.rla:  # state of every sequence's cache (maintenance, outside the timed steps)
-        rla_state = torch.zeros((B, Hkv, d, d + 1), dtype=torch.float32, device=dev)
+        rla_state = torch.zeros((B, Hkv, d + 1, d), dtype=torch.float32, device=dev)
         ops.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, 0, rla_state)
         rla_num = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         rla_den = torch.empty((B, Hq), dtype=torch.float32, device=dev)

@@ -364,7 +364,7 @@ constexpr int kMaxChunkW = 4096;  // chunk weights kept in LDS
 
 // With RLA, also the residual linear attention over the unselected tokens by
 // subtraction: num = phi(q)^T S_all - sum_chunks num_sel, den = phi(q) . z_all
-// - sum_chunks den_sel (state [B][Hkv][D][D + 1], column D = z).
+// - sum_chunks den_sel (state [B][Hkv][D + 1][D]: rows 0 .. D-1 = S, row D = z).
 template <typename TO, typename TQ, bool RLA>
 __global__ void __launch_bounds__(kCombThreads)
 k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ part_o,
@@ -409,62 +409,91 @@ k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ pa
   if (lane == 0) wred[wave] = l;
   __syncthreads();
   const float lsum = (wred[0] + wred[1]) + (wred[2] + wred[3]);
+  // output dims in float4 columns: thread (dq, gi) takes chunks gi, gi + NG, ...
   const int D = s.D;
-  const int NG = kCombThreads / D;
-  const int d = tid % D, gi = tid / D;
-  float o = 0.f;
-  if (nch <= kMaxChunkW) {
-#pragma unroll 8
-    for (int c = gi; c < nch; c += NG) o = fmaf(wts[c], part_o[(base + c) * D + d], o);
-  } else {
-    for (int c = gi; c < nch; c += NG)
-      o = fmaf(__expf(part_ml[(base + c) * 2] - M), part_o[(base + c) * D + d], o);
+  const int DQ = D / 4;
+  const int NG = kCombThreads / DQ;
+  const int dq = tid % DQ, gi = tid / DQ;
+  __shared__ float4 ored4[kCombThreads];
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
+  for (int c = gi; c < nch; c += NG) {
+    const float wc = nch <= kMaxChunkW ? wts[c] : __expf(part_ml[(base + c) * 2] - M);
+    const float4 p = *reinterpret_cast<const float4*>(&part_o[(base + c) * D + 4 * dq]);
+    o.x = fmaf(wc, p.x, o.x);
+    o.y = fmaf(wc, p.y, o.y);
+    o.z = fmaf(wc, p.z, o.z);
+    o.w = fmaf(wc, p.w, o.w);
   }
-  ored[tid] = o;
+  ored4[tid] = o;
   __syncthreads();
   if (gi == 0) {
-    float t = 0.f;
-    for (int k = 0; k < NG; ++k) t += ored[k * D + d];
-    out[((int64_t)b * s.Hq + h) * D + d] = from_f32<TO>(nch ? t / lsum : 0.f);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < NG; ++k) {
+      const float4 v = ored4[k * DQ + dq];
+      t.x += v.x;
+      t.y += v.y;
+      t.z += v.z;
+      t.w += v.w;
+    }
+    const float inv = nch ? 1.f / lsum : 0.f;
+    TO* op = out + ((int64_t)b * s.Hq + h) * D + 4 * dq;
+    op[0] = from_f32<TO>(nch ? t.x * inv : 0.f);
+    op[1] = from_f32<TO>(nch ? t.y * inv : 0.f);
+    op[2] = from_f32<TO>(nch ? t.z * inv : 0.f);
+    op[3] = from_f32<TO>(nch ? t.w * inv : 0.f);
   }
   if (lse && tid == 0) lse[(int64_t)b * s.Hq + h] = nch ? M + logf(lsum) : -INFINITY;
   if (RLA) {
     __shared__ float phq[128];
-    __shared__ float rred[kCombThreads], dred[kCombThreads];
     const TQ* qh = q + ((int64_t)b * s.Hq + h) * D;
     for (int i = tid; i < D; i += kCombThreads) phq[i] = __expf(to_f32<TQ>(qh[i]));
-    __syncthreads();
-    const float* st = rla_state + ((int64_t)b * s.Hkv + h / G) * D * (D + 1);
-    // phi(q)^T S_all for dim d over rows i = gi, gi + NG, ...; z with it
-    float a = 0.f, zz = 0.f;
+    __syncthreads();  // (also: every thread is past its ored4 read)
+    const float* st = rla_state + ((int64_t)b * s.Hkv + h / G) * (D + 1) * D;
+    // phi(q)^T S over rows i = gi, gi + NG, ..., minus the chunks' selected terms
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
     for (int i = gi; i < D; i += NG) {
-      a = fmaf(phq[i], st[(int64_t)i * (D + 1) + d], a);
-      if (d == 0) zz = fmaf(phq[i], st[(int64_t)i * (D + 1) + D], zz);
+      const float4 r = *reinterpret_cast<const float4*>(&st[(int64_t)i * D + 4 * dq]);
+      a.x = fmaf(phq[i], r.x, a.x);
+      a.y = fmaf(phq[i], r.y, a.y);
+      a.z = fmaf(phq[i], r.z, a.z);
+      a.w = fmaf(phq[i], r.w, a.w);
     }
-    // selected terms of the chunks, in chunk order
-    float sn = 0.f, sd = 0.f;
+#pragma unroll 4
     for (int c = gi; c < nch; c += NG) {
-      sn += part_rnum[(base + c) * D + d];
-      if (d == 0) sd += part_rden[base + c];
+      const float4 r = *reinterpret_cast<const float4*>(&part_rnum[(base + c) * D + 4 * dq]);
+      a.x -= r.x;
+      a.y -= r.y;
+      a.z -= r.z;
+      a.w -= r.w;
     }
-    rred[tid] = a - sn;
-    dred[tid] = zz - sd;
+    ored4[tid] = a;
+    // denominator: phi(q) . z (row D of the state) minus the chunks' sums
+    float dz = 0.f;
+    for (int i = tid; i < D; i += kCombThreads) dz = fmaf(phq[i], st[(int64_t)D * D + i], dz);
+    for (int c = tid; c < nch; c += kCombThreads) dz -= part_rden[base + c];
+    dz = wave_sum(dz);
+    if (lane == 0) wred[wave] = dz;
     __syncthreads();
     if (gi == 0) {
-      float t = 0.f, td = 0.f;
+      float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int k = 0; k < NG; ++k) {
-        t += rred[k * D + d];
-        td += dred[k * D + d];
+        const float4 v = ored4[k * DQ + dq];
+        t.x += v.x;
+        t.y += v.y;
+        t.z += v.z;
+        t.w += v.w;
       }
-      rla_num[((int64_t)b * s.Hq + h) * D + d] = t;
-      if (d == 0) rla_den[(int64_t)b * s.Hq + h] = td;
+      *reinterpret_cast<float4*>(&rla_num[((int64_t)b * s.Hq + h) * D + 4 * dq]) = t;
     }
+    if (tid == 0) rla_den[(int64_t)b * s.Hq + h] = (wred[0] + wred[1]) + (wred[2] + wred[3]);
   }
 }
 
 // Residual linear attention state ("SPLA", section 2.2): for each (sequence,
-// group), S[i][c] += sum_j exp(k_j[i]) v_j[c] and z[i] += sum_j exp(k_j[i])
-// over tokens j in [first, seq_lens[b]).  Workgroup = 16 rows of S (a
+// group), S[i][c] += sum_j exp(k_j[i]) v_j[c] (rows 0 .. D-1) and
+// z[i] += sum_j exp(k_j[i]) (row D) over tokens j in [first, seq_lens[b]).  Workgroup = 16 rows of S (a
 // stripe); thread (r, cg) owns row r's columns cg, cg + 16, ... and, for
 // cg = 0, z[r].  Tokens go through LDS 32 at a time; fixed summation order.
 constexpr int kRlaTok = 32;
@@ -517,10 +546,10 @@ k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
       zacc += p;
     }
   }
-  float* st = state + ((int64_t)b * s.Hkv + g) * D * (D + 1) + (int64_t)i * (D + 1);
+  float* st = state + ((int64_t)b * s.Hkv + g) * (D + 1) * D;
 #pragma unroll
-  for (int m = 0; m < NC; ++m) st[cg + 16 * m] += acc[m];
-  if (cg == 0) st[D] += zacc;
+  for (int m = 0; m < NC; ++m) st[(int64_t)i * D + cg + 16 * m] += acc[m];
+  if (cg == 0) st[(int64_t)D * D + i] += zacc;
 }
 
 // Persistent grid of the split kernel: blocks resident on the chip.
@@ -536,7 +565,7 @@ int split_grid(int nchunk_max, int rows) {
 }
 
 struct RlaArgs {
-  const float* state;  // [B][Hkv][D][D + 1]
+  const float* state;  // [B][Hkv][D + 1][D]
   float* num;          // [B][Hq][D]
   float* den;          // [B][Hq]
 };

@@ -216,9 +216,9 @@ sa_status sa_sparse_decode(const sa_shape* shape, const sa_pages* pages, const v
  * of the support are condensed into a linear-attention state; feature map
  * phi(x) = exp(x) elementwise, applied to the raw key rows): for each sequence
  * b and group g, over tokens j in [first_token, seq_lens[b]),
- *   state[b][g][i][c] += sum_j exp(k_j[i]) v_j[c]   (c < head_dim)
- *   state[b][g][i][head_dim] += sum_j exp(k_j[i])
- * state [batch][n_kv_heads][head_dim][head_dim + 1] fp32, accumulated in
+ *   state[b][g][i][c] += sum_j exp(k_j[i]) v_j[c]   (i, c < head_dim)
+ *   state[b][g][head_dim][i] += sum_j exp(k_j[i])
+ * state [batch][n_kv_heads][head_dim + 1][head_dim] fp32, accumulated in
  * place (the caller zero-fills it for a fresh build and passes the first new
  * token to extend it); k_pool, v_pool of dtype.  Cache maintenance, off the
  * per-step path.  Deterministic (one owner per state element, fixed order). */

@@ -33,7 +33,7 @@ def gpu_state(inp, first=0, lens=None, state=None):
                                                                       device="cuda")
     pages = o.make_pages(inp.page_table, lens_t)
     if state is None:
-        state = torch.zeros((inp.B, inp.H_kv, inp.d, inp.d + 1), dtype=torch.float32,
+        state = torch.zeros((inp.B, inp.H_kv, inp.d + 1, inp.d), dtype=torch.float32,
                             device="cuda")
     o.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, first, state)
     torch.cuda.synchronize()
@@ -41,14 +41,14 @@ def gpu_state(inp, first=0, lens=None, state=None):
 
 
 def oracle_state(inp):
-    st = np.zeros((inp.B, inp.H_kv, inp.d, inp.d + 1))
+    st = np.zeros((inp.B, inp.H_kv, inp.d + 1, inp.d))
     for b in range(inp.B):
         for g in range(inp.H_kv):
             if inp.seq_lens[b] == 0:
                 continue
             Sm, z = O.rla_state(S.to_np(inp.seq_keys(b, g)), S.to_np(inp.seq_values(b, g)))
-            st[b, g, :, :inp.d] = Sm
-            st[b, g, :, inp.d] = z
+            st[b, g, :inp.d] = Sm
+            st[b, g, inp.d] = z
     return st
 
 
