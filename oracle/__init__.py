@@ -40,6 +40,16 @@ Parity status of each function (what pins it, from the tests in
                          full support leaves nothing; the subtraction form
                          equals the direct sum; linear in V, invariant under
                          a joint key/value permutation.
+* ``head_mean_attention``, ``oracle_support``, ``support_coverage``,
+  ``support_overlap``
+                         pinned: the head-averaged distribution equals the
+                         head mean of torch scaled_dot_product_attention
+                         weights (float64, one-hot values); two-key logistic
+                         closed form; equal keys give the uniform
+                         distribution; the top-k oracle support has the
+                         largest coverage of all k-subsets and the top-p one
+                         the smallest size reaching p (brute force); hand-made
+                         overlaps.
 
 Parity unpinned (our readings, fixed only by our own written definitions, no
 worked example on the pages): the indexer scale ``s_idx``, the mean over a

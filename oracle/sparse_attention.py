@@ -65,6 +65,11 @@ __all__ = [
     "rla_state",
     "rla_unselected",
     "rla_by_subtraction",
+    "head_mean_attention",
+    "mass_scores",
+    "oracle_support",
+    "support_coverage",
+    "support_overlap",
 ]
 
 
@@ -301,6 +306,61 @@ def attend(q_heads, K, V, s_att: float):
         o[h] = (w @ V) / l
         lse[h] = m + math.log(l)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# Attention-mass oracle support (Oracle-Guided Sparse Prefill 2.1)
+# ---------------------------------------------------------------------------
+
+
+def head_mean_attention(q_heads, K, s_att: float) -> np.ndarray:
+    """Token importance of one query position for one key/value group: the
+    dense attention distribution of each of the group's query heads over all
+    keys, averaged over those heads.
+
+    q_heads: [G, d], K: [n, d]  ->  P [n] (P >= 0, sum 1 when n > 0).
+    """
+    q_heads, K = f64(q_heads), f64(K)
+    G, n = q_heads.shape[0], K.shape[0]
+    P = np.zeros(n)
+    if n == 0:
+        return P
+    for h in range(G):
+        logits = s_att * (K @ q_heads[h])
+        w = np.exp(logits - logits.max())
+        P += w / w.sum()
+    return P / G
+
+
+def mass_scores(P) -> np.ndarray:
+    """log P: as candidate scores, the selection rules above rank by P and
+    their softmax mass is P itself, so they return the oracle support."""
+    with np.errstate(divide="ignore"):
+        return np.log(f64(P))
+
+
+def oracle_support(P, *, k=None, p=None) -> np.ndarray:
+    """Attention-mass oracle support: the k tokens of largest P (the page's
+    top-k rule), or the shortest prefix in that order whose P sum reaches p.
+    Equal P values are taken lower index first; ascending indices."""
+    if (p is None) == (k is None):
+        raise ValueError("give exactly one of p, k")
+    x = mass_scores(P)
+    return select_topk(x, k) if k is not None else select_topp(x, p)
+
+
+def support_coverage(P, S) -> float:
+    """Dense attention mass a support covers: sum of P over the support."""
+    P = f64(P)
+    total = 0.0
+    for j in S:
+        total += P[int(j)]
+    return total
+
+
+def support_overlap(S, S_ref) -> int:
+    """Number of tokens two supports have in common."""
+    return len(set(int(j) for j in S) & set(int(j) for j in S_ref))
 
 
 def decode_row(q_heads, w_q_heads, ktil, K, V, *, s_idx, s_att, p=None, k=None,

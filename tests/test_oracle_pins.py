@@ -590,3 +590,77 @@ def test_rla_linear_in_values_and_permutation_invariant():
     num3, den3 = O.rla_unselected(q, K[perm], V[perm], inv[support])
     np.testing.assert_allclose(num3, num, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(den3, den, rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Attention-mass oracle support (Oracle-Guided Sparse Prefill section 2.1)
+# ---------------------------------------------------------------------------
+
+
+def test_head_mean_attention_is_mean_of_sdpa_weights():
+    """With one-hot values (V = I) torch's attention output is the weight
+    row itself; averaging it over the group's heads gives P."""
+    rng = _rng(40)
+    G, d, n = 4, 16, 37
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((n, d))
+    s = 0.7 / math.sqrt(d)
+    W = _sdpa(q[None, :, None, :], K[None, None], np.eye(n)[None, None], s)[0, :, 0]  # [G, n]
+    P = O.head_mean_attention(q, K, s)
+    np.testing.assert_allclose(P, W.mean(axis=0), rtol=1e-12, atol=1e-16)
+    assert abs(P.sum() - 1.0) < 1e-13 and np.all(P >= 0)
+
+
+def test_head_mean_attention_two_keys_logistic():
+    q = np.array([[1.0, 2.0]])
+    K = np.array([[0.5, 0.0], [0.0, 1.0]])
+    s = 0.3
+    a = s * (0.5 - 2.0)                 # logit difference of key 0 over key 1
+    P = O.head_mean_attention(q, K, s)
+    np.testing.assert_allclose(P, [1 / (1 + math.exp(-a)), 1 / (1 + math.exp(a))], rtol=1e-14)
+
+
+def test_head_mean_attention_equal_keys_uniform_and_heads_symmetric():
+    rng = _rng(41)
+    q = rng.standard_normal((3, 8))
+    K = np.tile(rng.standard_normal(8), (9, 1))
+    np.testing.assert_allclose(O.head_mean_attention(q, K, 0.5), np.full(9, 1 / 9), rtol=1e-14)
+    K = rng.standard_normal((20, 8))
+    P = O.head_mean_attention(q, K, 0.5)
+    np.testing.assert_allclose(O.head_mean_attention(q[::-1], K, 0.5), P, rtol=1e-13)
+    perm = rng.permutation(20)
+    np.testing.assert_allclose(O.head_mean_attention(q, K[perm], 0.5), P[perm], rtol=1e-13)
+    # one head locked on key 5 gives it at least 1/G of the averaged mass
+    u = K[5] / np.linalg.norm(K[5])
+    K2, q2 = K.copy(), q.copy()
+    K2[5] = 20.0 * u
+    q2[1] = 5.0 * u                      # logit 100 on key 5, at most ~5|k| elsewhere
+    assert O.head_mean_attention(q2, K2, 1.0)[5] >= 1 / 3 - 1e-9
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_oracle_support_brute_force(seed):
+    rng = _rng(50 + seed)
+    n = int(rng.integers(3, 10))
+    P = rng.dirichlet(np.full(n, 0.5))
+    for k in range(1, n + 1):
+        S = O.oracle_support(P, k=k)
+        best = max(sum(P[list(c)]) for c in itertools.combinations(range(n), k))
+        assert len(S) == k and abs(O.support_coverage(P, S) - best) < 1e-15
+    for p in (0.3, 0.5, 0.8, 0.95):
+        S = O.oracle_support(P, p=p)
+        assert O.support_coverage(P, S) >= p
+        smaller = [sum(P[list(c)]) for c in itertools.combinations(range(n), len(S) - 1)]
+        assert len(S) == 1 or max(smaller) < p
+
+
+def test_oracle_support_ties_and_coverage_edges():
+    P = np.array([0.25, 0.125, 0.25, 0.125, 0.25])
+    assert O.oracle_support(P, k=2).tolist() == [0, 2]
+    assert O.oracle_support(P, k=4).tolist() == [0, 1, 2, 4]
+    assert O.oracle_support(P, p=0.5).tolist() == [0, 2]
+    assert O.oracle_support(P, p=0.75).tolist() == [0, 2, 4]
+    assert O.support_coverage(P, []) == 0.0
+    assert O.support_coverage(P, range(5)) == 1.0
+    assert O.support_overlap([1, 4, 7, 9], [0, 4, 9, 11]) == 2
+    assert O.support_overlap([], [3]) == 0
