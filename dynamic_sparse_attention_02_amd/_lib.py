@@ -29,6 +29,7 @@ SA_OP_SPARSE_DECODE = 2
 SA_OP_PREFILL_SELECT = 3
 SA_OP_DECODE_STEP = 4
 SA_OP_SPARSE_DECODE_RLA = 5
+SA_OP_ATTENTION_MASS = 6
 
 
 class SaShape(ctypes.Structure):
@@ -71,6 +72,9 @@ SIGNATURES = {
     "sa_sparse_decode_rla": (ctypes.c_int, [_SH, _PG, _P, _P, _P, ctypes.c_int, _P, _P, _I32, _F,
                                             _P, ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
     "sa_rla_state": (ctypes.c_int, [_SH, _PG, _P, _P, ctypes.c_int, _I32, _P, _P]),
+    "sa_attention_mass": (ctypes.c_int, [_SH, _PG, _P, _P, ctypes.c_int, _F, _P, _I64, _P, _SZ, _P]),
+    "sa_support_coverage": (ctypes.c_int, [_SH, _PG, _P, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P,
+                                           _P]),
     "sa_decode_step": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F, _F, _I32,
                                       _I32, _I32, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P,
                                       _SZ, _P]),

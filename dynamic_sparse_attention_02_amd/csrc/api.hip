@@ -109,6 +109,10 @@ size_t decode_ws(const sa_shape* s, int64_t cap, bool rla = false) {
   return sa::align_up(sa::decode_workspace_bytes(sh, (int32_t)cap, rla), 256);
 }
 
+size_t mass_ws(const sa_shape* s) {
+  return sa::align_up(sa::mass_workspace_bytes(to_shape(s)), 256);
+}
+
 #define SA_TRY(expr)            \
   do {                          \
     sa_status _st = (expr);     \
@@ -167,6 +171,8 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return step_ws(s, param);
     case SA_OP_SPARSE_DECODE_RLA:
       return decode_ws(s, param, true);
+    case SA_OP_ATTENTION_MASS:
+      return mass_ws(s);
   }
   return 0;
 }
@@ -337,6 +343,42 @@ sa_status sa_rla_state(const sa_shape* s, const sa_pages* pg, const void* k_pool
   if (!k_pool || !v_pool || !state) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
   if (first_token < 0) return fail(SA_ERR_INVALID_ARGUMENT, "%s: first_token=%d < 0", fn, first_token);
   return hip_status(sa::launch_rla_state(to_shape(s), *pg, k_pool, v_pool, dt, first_token, state, st), fn);
+}
+
+sa_status sa_attention_mass(const sa_shape* s, const sa_pages* pg, const void* q,
+                            const void* k_pool, sa_dtype dt, float s_att, float* x, int64_t ldx,
+                            void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_attention_mass";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, true, fn));
+  if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !k_pool || !x) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (ldx < s->max_len) return fail(SA_ERR_INVALID_ARGUMENT, "%s: ldx=%lld < max_len=%d", fn, (long long)ldx, s->max_len);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
+  SA_TRY(check_ws(ws, ws_bytes, mass_ws(s), fn));
+  return hip_status(sa::launch_attention_mass(to_shape(s), *pg, q, k_pool, dt, s_att, x, ldx, ws, st), fn);
+}
+
+sa_status sa_support_coverage(const sa_shape* s, const sa_pages* pg, const float* x, int64_t ldx,
+                              const int32_t* idx, const int32_t* count, int32_t cap,
+                              const int32_t* ref_idx, const int32_t* ref_count, int32_t ref_cap,
+                              float* mass, int32_t* overlap, hipStream_t st) {
+  const char* fn = "sa_support_coverage";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, true, fn));
+  if (!x || !idx || !count || !mass) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (ref_idx && (!ref_count || !overlap))
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: ref_idx given without ref_count/overlap", fn);
+  if (ldx < s->max_len) return fail(SA_ERR_INVALID_ARGUMENT, "%s: ldx=%lld < max_len=%d", fn, (long long)ldx, s->max_len);
+  if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
+  if (ref_idx && ref_cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: ref_cap=%d < 1", fn, ref_cap);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
+  return hip_status(sa::launch_coverage(to_shape(s), *pg, x, ldx, idx, count, cap, ref_idx,
+                                        ref_idx ? ref_count : nullptr, ref_cap, mass,
+                                        ref_idx ? overlap : nullptr, st), fn);
 }
 
 sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, const void* w_q,

@@ -257,6 +257,15 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
                                sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
                                hipStream_t st);
 
+size_t mass_workspace_bytes(const Shape& s);
+hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q,
+                                 const void* k_pool, sa_dtype dt, float s_att, float* x,
+                                 int64_t ldx, void* ws, hipStream_t st);
+hipError_t launch_coverage(const Shape& s, const sa_pages& pg, const float* x, int64_t ldx,
+                           const int32_t* idx, const int32_t* count, int32_t cap,
+                           const int32_t* ridx, const int32_t* rcount, int32_t rcap, float* mass,
+                           int32_t* overlap, hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace sa

@@ -29,6 +29,8 @@ __all__ = [
     "sa_sparse_decode",
     "sa_sparse_decode_rla",
     "sa_rla_state",
+    "sa_attention_mass",
+    "sa_support_coverage",
     "sa_decode_step",
     "sa_select_prefill_topk",
     "sa_sparse_prefill",
@@ -163,6 +165,24 @@ def sa_rla_state(shape, pages, k_pool, v_pool, first_token, state, stream=None):
                                _dev(v_pool), _dt(k_pool), int(first_token), _dev(state),
                                _stream(stream))
     L.check(st, "sa_rla_state")
+
+
+def sa_attention_mass(shape, pages, q, k_pool, s_att, x, ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_attention_mass(ctypes.byref(shape), ctypes.byref(pages), _dev(q),
+                                    _dev(k_pool), _dt(q), float(s_att), _dev(x), int(x.stride(0)),
+                                    wp, wn, _stream(stream))
+    L.check(st, "sa_attention_mass")
+
+
+def sa_support_coverage(shape, pages, x, idx, count, mass, ref_idx=None, ref_count=None,
+                        overlap=None, stream=None):
+    st = L.load().sa_support_coverage(ctypes.byref(shape), ctypes.byref(pages), _dev(x),
+                                      int(x.stride(0)), _dev(idx), _dev(count), int(idx.shape[-1]),
+                                      _dev(ref_idx), _dev(ref_count),
+                                      int(ref_idx.shape[-1]) if ref_idx is not None else 0,
+                                      _dev(mass), _dev(overlap), _stream(stream))
+    L.check(st, "sa_support_coverage")
 
 
 def sa_decode_step(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att, p, top_k,

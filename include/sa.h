@@ -96,7 +96,8 @@ typedef enum {
   SA_OP_SPARSE_DECODE = 2,   /* param = cap of the support lists                 */
   SA_OP_PREFILL_SELECT = 3,  /* param = n_tokens of the prefill                  */
   SA_OP_DECODE_STEP = 4,     /* param = cap                                      */
-  SA_OP_SPARSE_DECODE_RLA = 5 /* param = cap                                     */
+  SA_OP_SPARSE_DECODE_RLA = 5, /* param = cap                                    */
+  SA_OP_ATTENTION_MASS = 6     /* param unused                                   */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -256,6 +257,43 @@ sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const voi
                          float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
                          void* out, sa_dtype out_dtype, float* lse, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Attention-mass oracle support and coverage
+ * ------------------------------------------------------------------------- */
+
+/* Dense head-averaged attention mass ("Oracle-Guided Sparse Prefill",
+ * section 2.1: the oracle takes the full attention distribution of each query
+ * head and averages it over the heads into one token-importance distribution
+ * P): for each sequence b and group g, row = b * n_kv_heads + g, and every
+ * token j < seq_lens[b],
+ *   x[row][j] = ln( (1/G) sum_{h in g} softmax_j(s_att * q[b][h] . k_j) )
+ * (natural log, fp32; entries j >= seq_lens[b] are not written).  Since the
+ * softmax of x is P itself and x orders tokens as P does, sa_select_topk on x
+ * returns the attention-mass top-k oracle support and sa_select_topp on x the
+ * shortest prefix by mass that reaches p.  q [batch][n_q_heads][head_dim],
+ * k_pool of dtype; x [batch * n_kv_heads][ldx], ldx >= max_len;
+ * batch * n_kv_heads <= 4096; workspace from SA_OP_ATTENTION_MASS (left
+ * zeroed).  Reads every cached key: an instrument and reference policy, not a
+ * sparse step.  fp32 logits and accumulation; deterministic. */
+sa_status sa_attention_mass(const sa_shape* shape, const sa_pages* pages, const void* q,
+                            const void* k_pool, sa_dtype dtype, float s_att, float* x,
+                            int64_t ldx, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Coverage of a support under the attention mass ("Oracle-Guided Sparse
+ * Prefill", section 2.1, and "Full Attention Strikes Back", results: the
+ * attention mass a sparse support keeps): for each row,
+ *   mass[row]    = sum_{j in S} exp(x[row][j])     S = idx[row][0 .. count)
+ *   overlap[row] = | S  intersect  R |             R = ref_idx[row][0 .. ref_count)
+ * with x as written by sa_attention_mass.  List entries outside
+ * [0, seq_lens[b]) are skipped; lists as the selection calls write them
+ * (strictly ascending).  ref_idx may be NULL (then ref_count, overlap are
+ * ignored and may be NULL).  mass [batch * n_kv_heads] fp32, overlap int32.
+ * fp32 sums in a fixed order (deterministic). */
+sa_status sa_support_coverage(const sa_shape* shape, const sa_pages* pages, const float* x,
+                              int64_t ldx, const int32_t* idx, const int32_t* count, int32_t cap,
+                              const int32_t* ref_idx, const int32_t* ref_count, int32_t ref_cap,
+                              float* mass, int32_t* overlap, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Causal prefill with supports shared by blocks of b_sel queries

@@ -117,6 +117,17 @@ def test_validation_codes():
     assert so.sa_sparse_decode_rla(B(s), B(pg), FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 65536, 0.1, FAKE, L.SA_F32, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_rla_state(B(s), B(pg), FAKE, FAKE, L.SA_BF16, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_rla_state(B(s), B(pg), FAKE, FAKE, L.SA_BF16, 0, None, None) == L.SA_ERR_INVALID_ARGUMENT
+    # attention mass and coverage
+    ws_mass = so.sa_workspace_size(L.SA_OP_ATTENTION_MASS, B(s), 0)
+    assert ws_mass >= 32 * 65536 * 4  # [rows][G][max_len] fp32 logits
+    assert so.sa_attention_mass(B(s), B(pg), FAKE, FAKE, L.SA_BF16, 0.1, FAKE, 65535, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_attention_mass(B(s), B(pg), FAKE, FAKE, L.SA_BF16, 0.1, FAKE, 65536, FAKE, ws_mass - 1, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_attention_mass(B(s), B(pg), None, FAKE, L.SA_BF16, 0.1, FAKE, 65536, FAKE, ws_mass, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_attention_mass(B(s), B(pg), FAKE, FAKE, 7, 0.1, FAKE, 65536, FAKE, ws_mass, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_support_coverage(B(s), B(pg), FAKE, 65536, FAKE, FAKE, 0, None, None, 0, FAKE, None, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_support_coverage(B(s), B(pg), FAKE, 65536, FAKE, FAKE, 64, FAKE, None, 64, FAKE, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_support_coverage(B(s), B(pg), FAKE, 65536, FAKE, FAKE, 64, FAKE, FAKE, 0, FAKE, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_support_coverage(B(s), B(pg), FAKE, 65536, FAKE, FAKE, 64, None, None, 0, None, None, None) == L.SA_ERR_INVALID_ARGUMENT
     # decode step: capacity and p
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.9, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 60000, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.0, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 65536, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
