@@ -48,6 +48,10 @@ def parse():
     ap.add_argument("--rla", action="store_true",
                     help="decode workloads: the step also forms the residual linear attention "
                          "over the unselected tokens (sa_sparse_decode_rla; state built first)")
+    ap.add_argument("--policy", default="indexer", choices=["indexer", "oracle"],
+                    help="token-level decode workloads: take the support from the low-rank "
+                         "indexer (default) or from the dense head-averaged attention mass "
+                         "(the attention-mass oracle: sa_attention_mass + sa_select_topp)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (5 dispatches): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -107,6 +111,7 @@ KERNEL_SOURCES = {
     "sparse_decode": ["decode.hip"],
     "sparse_decode_rla": ["decode.hip"],
     "sparse_prefill": ["prefill.hip"],
+    "attention_mass": ["mass.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -204,6 +209,9 @@ def bench_decode(args, name):
     lens = inp.seq_lens_tensor()
     pages = ops.make_pages(inp.page_table, lens)
     page_mode = name == "decode1m"
+    oracle_policy = args.policy == "oracle"
+    if oracle_policy and page_mode:
+        raise SystemExit("--policy oracle takes a token-level workload (decode64k or batched)")
     sel = inp.select
     n_sink, n_window = sel.get("n_sink", 0), sel.get("n_window", 0)
 
@@ -224,7 +232,8 @@ def bench_decode(args, name):
         cache_a = kidx
         cap = Lmax
         x = torch.empty((rows, Lmax), dtype=torch.float32, device=dev)
-        per_row_index_bytes = [L * 16 * 2 for L in inp.seq_lens]
+        # indexer: the 32 B K~ row of every token; oracle: the full K row
+        per_row_index_bytes = [L * (d * 2 if oracle_policy else 16 * 2) for L in inp.seq_lens]
     idx = torch.empty((rows, cap), dtype=torch.int32, device=dev)
     count = torch.empty((rows,), dtype=torch.int32, device=dev)
     out = torch.empty((B, Hq, d), dtype=inp.dtype, device=dev)
@@ -232,6 +241,8 @@ def bench_decode(args, name):
     ws_sel = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SELECT, shape, x.shape[1]))
     ws_dec = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SPARSE_DECODE, shape, cap))
     ws_idx = ops.alloc_workspace(ops.workspace_size(L.SA_OP_INDEX_SCORES, shape, 0))
+    ws_mass = (ops.alloc_workspace(ops.workspace_size(L.SA_OP_ATTENTION_MASS, shape, 0))
+               if not page_mode else None)
 
     # bytes a step must touch (index part: all of it; K/V: the selected rows)
     def run_select(rep):
@@ -239,11 +250,15 @@ def bench_decode(args, name):
         if page_mode:
             ops.sa_page_scores(shape, pages, inp.q, a, inp.s_att, x)
             ops.sa_select_topk(shape, pages, x, k_pages, 64, 0, 0, idx, count, ws_sel)
+        elif oracle_policy:
+            ops.sa_attention_mass(shape, pages, inp.q, kp, inp.s_att, x, ws_mass)
+            ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
         else:
             ops.sa_index_scores(shape, pages, inp.q, inp.w_q, a, inp.s_idx, x, ws_idx)
             ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
 
-    use_step = not page_mode and not args.rla  # token-level selection: the whole-step call
+    # token-level indexer selection: the whole-step call
+    use_step = not page_mode and not args.rla and not oracle_policy
     if args.rla:  # state of every sequence's cache (maintenance, outside the timed steps)
         rla_state = torch.zeros((B, Hkv, d + 1, d), dtype=torch.float32, device=dev)
         ops.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, 0, rla_state)
@@ -300,6 +315,10 @@ def bench_decode(args, name):
     if page_mode:
         t_index = time_loop(lambda i: ops.sa_page_scores(shape, pages, inp.q, reps[i][0],
                                                          inp.s_att, x), args.steps, reps=R)
+    elif oracle_policy:
+        t_index = time_loop(lambda i: ops.sa_attention_mass(shape, pages, inp.q, reps[i][1],
+                                                            inp.s_att, x, ws_mass),
+                            args.steps, reps=R)
     else:
         t_index = time_loop(lambda i: ops.sa_index_scores(shape, pages, inp.q, inp.w_q,
                                                           reps[i][0], inp.s_idx, x, ws_idx),
@@ -310,7 +329,8 @@ def bench_decode(args, name):
                                     ops.sa_select_topp(shape, pages, x, sel["p"], n_sink,
                                                        n_window, idx, count, ws_sel)), args.steps)
     t_decode = time_loop(lambda i: decode_call(reps[i]), args.steps, reps=R)
-    comp = {"index_scores" if not page_mode else "page_scores": (t_index, index_bytes),
+    first = "page_scores" if page_mode else ("attention_mass" if oracle_policy else "index_scores")
+    comp = {first: (t_index, index_bytes),
             "select": (t_select, 0),
             ("sparse_decode_rla" if args.rla else "sparse_decode"): (t_decode, kv_bytes)}
     if fused:
@@ -321,6 +341,7 @@ def bench_decode(args, name):
         dom_ms, dom_bytes = comp[dom]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     gbs = step_bytes / (ms * 1e-3) / 1e9
+    res_workload = name + ("+rla" if args.rla else "") + ("+oracle" if oracle_policy else "")
     res = {
         "metric": METRIC,
         "value": round(gbs, 2),
@@ -335,12 +356,13 @@ def bench_decode(args, name):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": name + ("+rla" if args.rla else ""), "batch": B,
+        "config": {"workload": res_workload, "batch": B,
                    "context": (Lmax if B == 1 else
                                                               [min(inp.seq_lens), Lmax]),
                    "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "selection": ("top-%d pages (Taylor page score)" % sel["k_pages"]
                                  if page_mode else
+                                 ("dense attention mass " if oracle_policy else "") +
                                  f"top-p {sel['p']} + sink {n_sink} + window {n_window}"),
                    "input_replicas": R},
         "step_bytes": step_bytes,
@@ -349,20 +371,50 @@ def bench_decode(args, name):
         "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
         "step_call": ("sa_decode_step" + (" (fused)" if fused else "")) if use_step else
                      ((("sa_page_scores + sa_select_topk") if page_mode else
-                       "sa_index_scores + sa_select_topp") +
+                       ("sa_attention_mass" if oracle_policy else "sa_index_scores") +
+                       " + sa_select_topp") +
                       (" + sa_sparse_decode_rla" if args.rla else " + sa_sparse_decode")),
         "separate_calls_ms": {k: round(v[0], 5) for k, v in comp.items()},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": recorded_traffic(name, dom),
+                     "traffic": recorded_traffic(res_workload, dom),
                      "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
     }
-    if not args.no_cpu_baseline:
+    if not page_mode:
+        res["coverage"] = support_coverage(ops, shape, pages, inp, base, x.shape[1], idx, count,
+                                           sel["p"], ws_mass, ws_sel, run_step)
+    if not args.no_cpu_baseline and not oracle_policy:
         res["cpu_baseline"] = cpu_baseline_decode(inp, cache_a if not page_mode else None,
                                                   step_bytes, args.cpu_seconds, page_mode,
                                                   stats if page_mode else None)
     return res
+
+
+def support_coverage(ops, shape, pages, inp, base, ldx, idx, count, p, ws_mass, ws_sel, run_step):
+    """Dense attention mass the step's supports keep (outside the timed
+    region): the head-averaged dense distribution of every row, the mass of
+    the step's support under it, and the attention-mass oracle's own top-p
+    support (without sink/window) for comparison."""
+    import torch
+    rows = count.numel()
+    xm = torch.empty((rows, ldx), dtype=torch.float32, device="cuda")
+    run_step(base)
+    ops.sa_attention_mass(shape, pages, inp.q, base[1], inp.s_att, xm, ws_mass)
+    idx_o, count_o = torch.empty_like(idx), torch.empty_like(count)
+    ops.sa_select_topp(shape, pages, xm, p, 0, 0, idx_o, count_o, ws_sel)
+    mass = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    ov = torch.empty((rows,), dtype=torch.int32, device="cuda")
+    ops.sa_support_coverage(shape, pages, xm, idx, count, mass, idx_o, count_o, ov)
+    torch.cuda.synchronize()
+    lens = inp.seq_lens_tensor().repeat_interleave(inp.H_kv).double()
+    m = mass.double()
+    return {"dense_mass_kept_mean": round(float(m.mean()), 4),
+            "dense_mass_kept_min": round(float(m.min()), 4),
+            "budget_fraction": round(float(count.double().sum() / lens.sum()), 5),
+            "oracle_topp_budget_fraction": round(float(count_o.double().sum() / lens.sum()), 5),
+            "support_in_oracle_topp": round(float(ov.double().sum() / count.double().sum()), 4),
+            "p": p}
 
 
 def cpu_baseline_decode(inp, kidx, step_bytes, seconds, page_mode, stats):

@@ -5,13 +5,15 @@
 // reaches p), and the yardstick for how much of that mass another support
 // covers.
 //
-// k_mass_logits: one workgroup per (512-token chunk, row).  The chunk's 64-token
-// pages of K are staged in LDS with coalesced 16-byte loads (the next page's
-// loads in flight while the current one is scored); one lane per token forms
+// k_mass_logits: one workgroup per (256-token chunk, row).  The chunk's 64-token
+// pages of K are staged in LDS with coalesced 16-byte loads (the next two
+// pages' loads in flight while the current one is scored); one lane per token forms
 // the logits of the group's heads (bf16 pairs through v_dot2_f32_bf16, fp32
 // accumulate) in base 2 and writes them to the workspace, and each wave keeps
-// a running (max, sum) per head.  The last workgroup of a row to finish merges
-// the chunks' pairs into the per-head log2 normaliser.
+// a running (max, sum) per head for the chunk.
+// k_mass_norm: per row, the chunks' pairs merged into each head's log2
+// normaliser (a launch of its own: no cross-workgroup fences in the hot
+// kernel).
 // k_mass_finish: per token, the natural log of the head mean of
 // 2^(logit - normaliser).
 // k_coverage: per row, the summed mass of a support and its overlap with a
@@ -26,7 +28,7 @@ namespace sa {
 
 namespace {
 
-constexpr int kMassChunk = 512;          // tokens per workgroup
+constexpr int kMassChunk = 256;          // tokens per workgroup
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -54,7 +56,6 @@ struct MassWs {
   float* lg;        // [rows][G][ldl] base-2 logits
   float2* part;     // [rows][nchunk][G] (max, sum) per chunk and head
   float* norm;      // [rows][G] log2 of each head's softmax normaliser
-  uint32_t* ctr;    // [rows] finished chunks (zero between calls)
   int64_t ldl;
   int32_t nchunk;
 };
@@ -65,6 +66,8 @@ k_mass_logits(const T* __restrict__ q, const T* __restrict__ k_pool,
               const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
               Shape s, float c2, MassWs w) {
   using C = MassCfg<T, D, G>;
+  constexpr int QP = G * D * (int)sizeof(T) / 16;        // 16-byte pieces of the group's queries
+  constexpr int QPT = (QP + C::NT - 1) / C::NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row = blockIdx.y, ch = blockIdx.x;
   const int b = row / s.Hkv, g = row % s.Hkv;
@@ -72,23 +75,40 @@ k_mass_logits(const T* __restrict__ q, const T* __restrict__ k_pool,
   const int32_t t0 = ch * kMassChunk;
   if (t0 >= L) return;  // this chunk is past the sequence: takes no part
   const int32_t t1 = min(L, t0 + kMassChunk);
-  const int32_t nch = (L + kMassChunk - 1) / kMassChunk;
 
   __shared__ __align__(16) char Ks[kPage * C::PITCH];
   __shared__ __align__(16) T Qs[G][D];
-  __shared__ int s_last;
 
-  for (int i = tid; i < G * D; i += C::NT) Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
-
+  // queries first, then the first two pages: waiting for the queries then
+  // leaves the page loads in flight
+  const char* qsrc = reinterpret_cast<const char*>(q + ((int64_t)b * s.Hq + g * G) * D);
+  u32x4m_t qr[QPT];
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int pc = i * C::NT + tid;
+    if (pc < QP) qr[i] = *reinterpret_cast<const u32x4m_t*>(qsrc + pc * 16);
+  }
   const int64_t head_stride = (int64_t)kPage * D;
   const int64_t page_stride = (int64_t)s.Hkv * head_stride;
   const int32_t* pt = page_table + (int64_t)b * s.max_pages;
-  u32x4m_t kr[C::LPT];
-  // ts is a multiple of 64 below L, so pt[ts / 64] is a listed page; rows of
-  // the last page past L are read (the page exists) and masked below.
   const char* kbase = reinterpret_cast<const char*>(k_pool + g * head_stride) + tid * 16;
   const int64_t npool = s.n_pool_pages;
-#define SA_MASS_PAGE(ts) (kbase + clamp_page(pt[(ts) >> 6], npool) * page_stride * (int64_t)sizeof(T))
+  // ts is a multiple of 64 below L, so pt[ts / 64] is a listed page; rows of
+  // the last page past L are read (the page exists) and masked below.
+#define SA_MASS_LOAD(buf, ts)                                                               \
+  do {                                                                                      \
+    const char* src_ = kbase + clamp_page(pt[(ts) >> 6], npool) * page_stride * (int64_t)sizeof(T); \
+    _Pragma("unroll") for (int i_ = 0; i_ < C::LPT; ++i_)                                   \
+      buf[i_] = *reinterpret_cast<const u32x4m_t*>(src_ + i_ * C::NT * 16);                 \
+  } while (0)
+  u32x4m_t kA[C::LPT], kB[C::LPT];
+  SA_MASS_LOAD(kA, t0);
+  if (t0 + kPage < t1) SA_MASS_LOAD(kB, t0 + kPage);
+#pragma unroll
+  for (int i = 0; i < QPT; ++i) {
+    const int pc = i * C::NT + tid;
+    if (pc < QP) *reinterpret_cast<u32x4m_t*>(reinterpret_cast<char*>(&Qs[0][0]) + pc * 16) = qr[i];
+  }
 
   float m_run[C::HPW], l_run[C::HPW];
 #pragma unroll
@@ -98,26 +118,22 @@ k_mass_logits(const T* __restrict__ q, const T* __restrict__ k_pool,
   }
   float* lg_row = w.lg + (int64_t)row * G * w.ldl;
 
-  {
-    const char* src = SA_MASS_PAGE(t0);
-#pragma unroll
-    for (int i = 0; i < C::LPT; ++i) kr[i] = *reinterpret_cast<const u32x4m_t*>(src + i * C::NT * 16);
-  }
-  for (int32_t ts = t0; ts < t1; ts += kPage) {
-    const int32_t nt = min(kPage, t1 - ts);
-    __syncthreads();  // previous page consumed (and Qs written)
-#pragma unroll
-    for (int i = 0; i < C::LPT; ++i) {
-      const int pc = i * C::NT + tid;
-      *reinterpret_cast<u32x4m_t*>(Ks + (pc / C::CPR) * C::PITCH + (pc % C::CPR) * 16) = kr[i];
-    }
-    __syncthreads();
-    if (ts + kPage < t1) {
-      const char* src = SA_MASS_PAGE(ts + kPage);
-#pragma unroll
-      for (int i = 0; i < C::LPT; ++i) kr[i] = *reinterpret_cast<const u32x4m_t*>(src + i * C::NT * 16);
-    }
+  // one page: stage it in LDS, refill its registers with the page two ahead,
+  // score the staged page
+#define SA_MASS_PAGE(buf, ts)                                                               \
+  do {                                                                                      \
+    const int32_t nt_ = min(kPage, t1 - (ts));                                              \
+    __syncthreads();                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < C::LPT; ++i_) {                                 \
+      const int pc_ = i_ * C::NT + tid;                                                     \
+      *reinterpret_cast<u32x4m_t*>(Ks + (pc_ / C::CPR) * C::PITCH + (pc_ % C::CPR) * 16) = buf[i_]; \
+    }                                                                                       \
+    __syncthreads();                                                                        \
+    if ((ts) + 2 * kPage < t1) SA_MASS_LOAD(buf, (ts) + 2 * kPage);                         \
+    score_page(ts, nt_);                                                                    \
+  } while (0)
 
+  auto score_page = [&](int32_t ts, int32_t nt) {
     float sc[C::HPW];
 #pragma unroll
     for (int hh = 0; hh < C::HPW; ++hh) sc[hh] = 0.f;
@@ -156,39 +172,49 @@ k_mass_logits(const T* __restrict__ q, const T* __restrict__ k_pool,
       l_run[hh] = l_run[hh] * exp2f(m_run[hh] - m_new) + wave_sum(e);
       m_run[hh] = m_new;
     }
+  };
+
+  for (int32_t ts = t0; ts < t1; ts += 2 * kPage) {
+    SA_MASS_PAGE(kA, ts);
+    if (ts + kPage < t1) SA_MASS_PAGE(kB, ts + kPage);
   }
-
 #undef SA_MASS_PAGE
+#undef SA_MASS_LOAD
 
-  // ---- publish the chunk's pairs; the row's last workgroup merges them ----
+  // ---- the chunk's (max, sum) per head ----
   float2* part = w.part + ((int64_t)row * w.nchunk + ch) * G;
   if (lane == 0) {
 #pragma unroll
     for (int hh = 0; hh < C::HPW; ++hh) part[wave * C::HPW + hh] = make_float2(m_run[hh], l_run[hh]);
   }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&w.ctr[row], 1u);
-    s_last = (old == (uint32_t)nch - 1);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (tid == 0) __hip_atomic_store(&w.ctr[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t* prow = reinterpret_cast<uint64_t*>(w.part + (int64_t)row * w.nchunk * G);
-#pragma unroll
-  for (int hh = 0; hh < C::HPW; ++hh) {
-    const int h = wave * C::HPW + hh;
+}
+
+// Per row and head: merge the chunks' (max, sum) pairs in chunk order into
+// log2 of the softmax normaliser.  One wave per head.
+template <int G>
+__global__ void __launch_bounds__(256)
+k_mass_norm(const int32_t* __restrict__ seq_lens, Shape s, MassWs w) {
+  const int row = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int32_t L = clamp_len(seq_lens[row / s.Hkv], s.max_len);
+  if (L == 0) return;
+  const int32_t nch = (L + kMassChunk - 1) / kMassChunk;
+  const float2* prow = w.part + (int64_t)row * w.nchunk * G;
+  constexpr int kBatch = 8;  // pairs per lane loaded before merging
+  for (int h = wave; h < G; h += 4) {
     float m = -INFINITY, l = 0.f;
-    for (int c = lane; c < nch; c += kWave) {  // chunk partials in chunk order per lane
-      const uint64_t bits = __hip_atomic_load(prow + (int64_t)c * G + h, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-      const float mc = __uint_as_float((uint32_t)bits);
-      const float lc = __uint_as_float((uint32_t)(bits >> 32));
-      const float mn = fmaxf(m, mc);
-      l = l * exp2f(m - mn) + lc * exp2f(mc - mn);
-      m = mn;
+    for (int c0 = 0; c0 < nch; c0 += kBatch * kWave) {  // lane's chunks in chunk order
+      float2 v[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int c = c0 + k * kWave + lane;
+        v[k] = c < nch ? prow[(int64_t)c * G + h] : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const float mn = fmaxf(m, v[k].x);
+        l = (mn == -INFINITY) ? 0.f : l * exp2f(m - mn) + v[k].y * exp2f(v[k].x - mn);
+        m = mn;
+      }
     }
     const float M = wave_max(m);
     const float Ls = wave_sum(m == -INFINITY ? 0.f : l * exp2f(m - M));
@@ -278,7 +304,7 @@ k_coverage(const float* __restrict__ x, int64_t ldx, const int32_t* __restrict__
 struct MassLayout {
   int64_t ldl;
   int32_t nchunk;
-  size_t off_part, off_norm, off_ctr, total;
+  size_t off_part, off_norm, total;
 };
 
 MassLayout mass_layout(const Shape& s) {
@@ -293,8 +319,6 @@ MassLayout mass_layout(const Shape& s) {
   off += align_up((size_t)rows * m.nchunk * G * sizeof(float2), 256);
   m.off_norm = off;
   off += align_up((size_t)rows * G * sizeof(float), 256);
-  m.off_ctr = off;
-  off += align_up((size_t)rows * sizeof(uint32_t), 256);
   m.total = off;
   return m;
 }
@@ -309,6 +333,7 @@ hipError_t launch_mass_t(const Shape& s, const sa_pages& pg, const void* q, cons
   case GG:                                                                                     \
     k_mass_logits<T, D, GG><<<grid, MassCfg<T, D, GG>::NT, 0, st>>>(                           \
         (const T*)q, (const T*)k_pool, pg.page_table, pg.seq_lens, s, c2, w);                  \
+    k_mass_norm<GG><<<s.B * s.Hkv, 256, 0, st>>>(pg.seq_lens, s, w);                           \
     k_mass_finish<GG><<<grid, 256, 0, st>>>(pg.seq_lens, s, w, x, ldx);                        \
     break;
   switch (G) {
@@ -336,7 +361,6 @@ hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void*
   w.lg = (float*)base;
   w.part = (float2*)(base + m.off_part);
   w.norm = (float*)(base + m.off_norm);
-  w.ctr = (uint32_t*)(base + m.off_ctr);
   w.ldl = m.ldl;
   w.nchunk = m.nchunk;
   if (dt == SA_BF16)

@@ -273,8 +273,10 @@ sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const voi
  * returns the attention-mass top-k oracle support and sa_select_topp on x the
  * shortest prefix by mass that reaches p.  q [batch][n_q_heads][head_dim],
  * k_pool of dtype; x [batch * n_kv_heads][ldx], ldx >= max_len;
- * batch * n_kv_heads <= 4096; workspace from SA_OP_ATTENTION_MASS (left
- * zeroed).  Reads every cached key: an instrument and reference policy, not a
+ * batch * n_kv_heads <= 4096; workspace from SA_OP_ATTENTION_MASS, which
+ * needs no zero-fill but is left holding the logits (an exception to the
+ * zeroing convention: do not share it with the other calls' workspaces).
+ * Reads every cached key: an instrument and reference policy, not a
  * sparse step.  fp32 logits and accumulation; deterministic. */
 sa_status sa_attention_mass(const sa_shape* shape, const sa_pages* pages, const void* q,
                             const void* k_pool, sa_dtype dtype, float s_att, float* x,
