@@ -40,6 +40,13 @@ Parity status of each function (what pins it, from the tests in
                          full support leaves nothing; the subtraction form
                          equals the direct sum; linear in V, invariant under
                          a joint key/value permutation.
+* ``prefill_query_*``    pinned: a support of every causal key gives dense
+                         causal attention (torch SDPA, is_causal); with one
+                         head per group, or identical per-head channels, the
+                         mean-of-probabilities ranking equals the logits
+                         ranking; the probability mean is a distribution and
+                         its top-k holds the largest mass (brute force); the
+                         own token is always kept.
 * ``head_mean_attention``, ``oracle_support``, ``support_coverage``,
   ``support_overlap``
                          pinned: the head-averaged distribution equals the

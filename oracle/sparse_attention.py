@@ -59,6 +59,9 @@ __all__ = [
     "prefill_block_query",
     "prefill_block_support",
     "prefill_block_attend",
+    "prefill_query_scores",
+    "prefill_query_support",
+    "prefill_query_attend",
     "group_of_head",
     "heads_of_group",
     "rla_feature",
@@ -447,6 +450,49 @@ def prefill_block_attend(Q_blk, K, V, S, blk: int, b_sel: int, s_att: float):
         o[i] = oi
         lse[i] = li
     return o, lse
+
+
+def prefill_query_scores(q_i, w_q_heads, ktil, i: int, s_idx: float, aggregate: str = "logits"):
+    """Per-query (b_sel = 1) scores of query position i for one group over
+    its causal candidates j <= i (Oracle-Guided Sparse Prefill 2.1, per-query
+    granularity: each query chooses its own support).
+
+    aggregate = "logits": the head-collapsed channel, q_c = s_idx * mean_h
+    W_q[h]^T q_{i,h}, scores q_c . Ktil_j (as in decode).
+    aggregate = "probs": each head's own low-rank logits
+    s_idx * (W_q[h]^T q_{i,h}) . Ktil_j turned into a softmax over the
+    candidates, averaged over the heads; the score is the log of that mean
+    (so the selection rules rank by the mean probability).
+
+    q_i: [G, d], w_q_heads: [G, d, r], ktil: [>= i+1, r] -> [i + 1]
+    """
+    q_i, w_q_heads, kt = f64(q_i), f64(w_q_heads), f64(ktil)[: i + 1]
+    if aggregate == "logits":
+        return token_scores(collapse_query(q_i, w_q_heads, s_idx), kt)
+    if aggregate != "probs":
+        raise ValueError("aggregate must be 'logits' or 'probs'")
+    G = q_i.shape[0]
+    P = np.zeros(i + 1)
+    for h in range(G):
+        x = kt @ (s_idx * (w_q_heads[h].T @ q_i[h]))
+        w = np.exp(x - x.max())
+        P += w / w.sum()
+    with np.errstate(divide="ignore"):
+        return np.log(P / G)
+
+
+def prefill_query_support(x, i: int, k: int) -> np.ndarray:
+    """Support of query i: top-k of its scores over j <= i (all of them when
+    there are at most k), plus the query's own token, which is always kept
+    (the per-query counterpart of the always-attended diagonal block)."""
+    return with_sink_window(select_topk(x, k), i + 1, 0, 1)
+
+
+def prefill_query_attend(q_i, K, V, S, s_att: float):
+    """Exact attention of query i (all heads of the group) over its support
+    (which holds the query's own token)."""
+    S = [int(j) for j in S]
+    return attend(q_i, f64(K)[S], f64(V)[S], s_att)
 
 
 # ---------------------------------------------------------------------------

@@ -664,3 +664,73 @@ def test_oracle_support_ties_and_coverage_edges():
     assert O.support_coverage(P, range(5)) == 1.0
     assert O.support_overlap([1, 4, 7, 9], [0, 4, 9, 11]) == 2
     assert O.support_overlap([], [3]) == 0
+
+
+# ---------------------------------------------------------------------------
+# Per-query prefill supports (Oracle-Guided Sparse Prefill section 2.1, b_sel = 1)
+# ---------------------------------------------------------------------------
+
+
+def _pq_case(seed, N=40, G=3, d=8, r=4):
+    rng = _rng(seed)
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    W = rng.standard_normal((G, d, r)) / math.sqrt(d)
+    Kt = rng.standard_normal((N, r))
+    return Q, K, V, W, Kt
+
+
+def test_prefill_query_full_support_is_dense_causal():
+    Q, K, V, W, Kt = _pq_case(60)
+    N, G, d = Q.shape
+    s = 1 / math.sqrt(d)
+    ref = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], V[None, None], s, causal=True)[0]
+    for i in (0, 1, 17, N - 1):
+        for agg in ("logits", "probs"):
+            x = O.prefill_query_scores(Q[i], W, Kt, i, 1.0, agg)
+            S = O.prefill_query_support(x, i, k=N)
+            assert S.tolist() == list(range(i + 1))
+            o, _ = O.prefill_query_attend(Q[i], K, V, S, s)
+            np.testing.assert_allclose(o, ref[:, i], rtol=1e-12, atol=1e-13)
+
+
+def test_prefill_query_own_token_always_kept():
+    Q, K, V, W, Kt = _pq_case(61)
+    for agg in ("logits", "probs"):
+        for i in range(6, 40):
+            x = O.prefill_query_scores(Q[i], W, Kt, i, 1.0, agg)
+            top = O.select_topk(x, 5)
+            S = O.prefill_query_support(x, i, k=5)
+            assert i in S and S.max() == i
+            assert len(S) == (5 if i in top else 6)
+            assert set(S.tolist()) - {i} <= set(top.tolist())
+
+
+def test_prefill_query_probs_equal_logits_for_one_channel():
+    """Softmax is monotone: with one head per group, or identical per-head
+    projected queries, ranking by the probability mean is ranking by logits."""
+    Q, K, V, W, Kt = _pq_case(62, G=1)
+    for i in (5, 30):
+        xl = O.prefill_query_scores(Q[i], W, Kt, i, 0.7, "logits")
+        xp = O.prefill_query_scores(Q[i], W, Kt, i, 0.7, "probs")
+        assert np.array_equal(O.candidate_order(xl), O.candidate_order(xp))
+    Q, K, V, W, Kt = _pq_case(63, G=4)
+    Q[:, :] = Q[:, :1]
+    W[:] = W[:1]
+    xl = O.prefill_query_scores(Q[33], W, Kt, 33, 0.7, "logits")
+    xp = O.prefill_query_scores(Q[33], W, Kt, 33, 0.7, "probs")
+    assert np.array_equal(O.candidate_order(xl), O.candidate_order(xp))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_prefill_query_probs_topk_brute_force(seed):
+    Q, K, V, W, Kt = _pq_case(70 + seed, N=9, G=3)
+    i = 8
+    x = O.prefill_query_scores(Q[i], W, Kt, i, 1.3, "probs")
+    P = np.exp(x)
+    assert abs(P.sum() - 1.0) < 1e-12
+    for k in (1, 3, 6):
+        S = O.select_topk(x, k)
+        best = max(P[list(c)].sum() for c in itertools.combinations(range(i + 1), k))
+        assert abs(P[S].sum() - best) < 1e-14
