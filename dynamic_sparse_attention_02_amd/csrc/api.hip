@@ -173,6 +173,10 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return decode_ws(s, param, true);
     case SA_OP_ATTENTION_MASS:
       return mass_ws(s);
+    case SA_OP_PREFILL_QUERY: {
+      sa::Shape sh = to_shape(s);
+      return sa::align_up(sa::prefill_query_workspace_bytes(sh, s->max_len, param < 1 ? 1 : (int32_t)param), 256);
+    }
   }
   return 0;
 }
@@ -438,12 +442,12 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   return hip_status(e, fn);
 }
 
-sa_status sa_select_prefill_topk(const sa_shape* s, const sa_pages* pg, int32_t n_tokens,
-                                 const void* q, const void* w_q, const void* kidx_pool,
-                                 sa_dtype dt, float s_idx, int32_t b_sel, int32_t k, int32_t* idx,
-                                 int32_t* count, int32_t cap, void* ws, size_t ws_bytes,
-                                 hipStream_t st) {
-  const char* fn = "sa_select_prefill_topk";
+static sa_status prefill_select_common(const char* fn, const sa_shape* s, const sa_pages* pg,
+                                       int32_t n_tokens, const void* q, const void* w_q,
+                                       const void* kidx_pool, sa_dtype dt, float s_idx,
+                                       int32_t b_sel, int32_t k, int32_t* idx, int32_t* count,
+                                       int32_t cap, void* ws, size_t ws_bytes, hipStream_t st,
+                                       bool probs) {
   SA_TRY(check_shape(s, fn));
   SA_TRY(check_pages(pg, false, fn));
   if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
@@ -451,14 +455,58 @@ sa_status sa_select_prefill_topk(const sa_shape* s, const sa_pages* pg, int32_t 
   if (!q || !w_q || !kidx_pool || !idx || !count) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
   if (n_tokens < 1 || n_tokens > s->max_len)
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
-  if (b_sel != 64) return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 64", fn, b_sel);
+  if (probs ? b_sel != 1 : (b_sel != 64 && b_sel != 1))
+    return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be %s", fn, b_sel, probs ? "1" : "1 or 64");
   if (k < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: k=%d < 1", fn, k);
-  const int64_t need = k < n_tokens ? k : n_tokens;
+  const int64_t kk = b_sel == 1 ? (int64_t)k + 1 : (int64_t)k;  // per query: plus the own token
+  const int64_t need = kk < n_tokens ? kk : n_tokens;
   if (cap < 1 || cap < need) return fail(SA_ERR_CAPACITY, "%s: cap=%d below %lld", fn, cap, (long long)need);
   const sa::Shape sh = to_shape(s);
   SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::prefill_select_workspace_bytes(sh, n_tokens), 256), fn));
   return hip_status(sa::launch_prefill_select(sh, *pg, n_tokens, q, w_q, kidx_pool, dt, s_idx, b_sel,
-                                              k, idx, count, cap, ws, st), fn);
+                                              k, idx, count, cap, ws, st, probs), fn);
+}
+
+sa_status sa_select_prefill_topk(const sa_shape* s, const sa_pages* pg, int32_t n_tokens,
+                                 const void* q, const void* w_q, const void* kidx_pool,
+                                 sa_dtype dt, float s_idx, int32_t b_sel, int32_t k, int32_t* idx,
+                                 int32_t* count, int32_t cap, void* ws, size_t ws_bytes,
+                                 hipStream_t st) {
+  return prefill_select_common("sa_select_prefill_topk", s, pg, n_tokens, q, w_q, kidx_pool, dt,
+                               s_idx, b_sel, k, idx, count, cap, ws, ws_bytes, st, false);
+}
+
+sa_status sa_select_prefill_topk_probs(const sa_shape* s, const sa_pages* pg, int32_t n_tokens,
+                                       const void* q, const void* w_q, const void* kidx_pool,
+                                       sa_dtype dt, float s_idx, int32_t b_sel, int32_t k,
+                                       int32_t* idx, int32_t* count, int32_t cap, void* ws,
+                                       size_t ws_bytes, hipStream_t st) {
+  return prefill_select_common("sa_select_prefill_topk_probs", s, pg, n_tokens, q, w_q, kidx_pool,
+                               dt, s_idx, b_sel, k, idx, count, cap, ws, ws_bytes, st, true);
+}
+
+sa_status sa_sparse_prefill_query(const sa_shape* s, const sa_pages* pg, int32_t n_tokens,
+                                  const void* q, const void* k_pool, const void* v_pool,
+                                  sa_dtype dt, const int32_t* idx, const int32_t* count,
+                                  int32_t cap, float s_att, void* out, sa_dtype out_dt, float* lse,
+                                  void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_sparse_prefill_query";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, false, fn));
+  if (!valid_dtype(dt) || !valid_dtype(out_dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (s->batch != 1) return fail(SA_ERR_UNSUPPORTED, "%s: prefill takes batch=1", fn);
+  if (!q || !k_pool || !v_pool || !idx || !count || !out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (n_tokens < 1 || n_tokens > s->max_len)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
+  if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  if (s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: n_kv_heads above %d", fn, kMaxDecodeRows);
+  const sa::Shape sh = to_shape(s);
+  SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::prefill_query_workspace_bytes(sh, n_tokens, cap), 256), fn));
+  return hip_status(sa::launch_sparse_prefill_query(sh, *pg, n_tokens, q, k_pool, v_pool, dt, idx,
+                                                    count, cap, s_att, out, out_dt, lse, ws, st), fn);
 }
 
 sa_status sa_sparse_prefill(const sa_shape* s, const sa_pages* pg, int32_t n_tokens, const void* q,
@@ -475,7 +523,8 @@ sa_status sa_sparse_prefill(const sa_shape* s, const sa_pages* pg, int32_t n_tok
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
   if (n_tokens < 1 || n_tokens > s->max_len)
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
-  if (b_sel != 64) return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 64", fn, b_sel);
+  if (b_sel != 64)
+    return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 64 (per query: sa_sparse_prefill_query)", fn, b_sel);
   if (cap < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: cap=%d < 1", fn, cap);
   if (cap > 2048) return fail(SA_ERR_UNSUPPORTED, "%s: cap=%d above 2048 listed keys", fn, cap);
   if (s->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "%s: head_dim must be 128", fn);

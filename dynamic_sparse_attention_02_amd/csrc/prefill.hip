@@ -33,6 +33,11 @@ typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 constexpr int kQB = 64;     // queries per selection block
 constexpr int kSlab = 256;  // query blocks per score slab
 
+__global__ void k_iota1(int32_t* __restrict__ v, int32_t n) {
+  const int32_t i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) v[i] = i + 1;
+}
+
 // ---------------------------------------------------------------------------
 // Block-collapsed indexer query: qcb[blk][g][c] = s_idx / (rows * G) *
 // sum_{h in g} sum_d W_q[h][d][c] * (sum_{i in blk} q[i][h][d]).
@@ -44,11 +49,11 @@ constexpr int kSlab = 256;  // query blocks per score slab
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int32_t Hq,
-             int32_t Hkv, int32_t D, float s_idx, float* __restrict__ qcb) {
+             int32_t Hkv, int32_t D, int32_t bsel, float s_idx, float* __restrict__ qcb) {
   const int blk = blockIdx.x, g = blockIdx.y;
   const int G = Hq / Hkv;
-  const int r0 = blk * kQB;
-  const int nr = min(kQB, N - r0);
+  const int r0 = blk * bsel;
+  const int nr = min(bsel, N - r0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunks = G * D / 8;              // (head, 8 dims) chunks: <= 256
   const int parts = 256 / chunks;            // row shares per chunk
@@ -108,29 +113,32 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
 
 // ---------------------------------------------------------------------------
 // Scores of a slab of query blocks: x[(blk - blk0) * Hkv + g][j] =
-// qcb[blk][g] . Kidx[g][j] for j < 64 * blk.  A workgroup covers 256
-// candidates and kRowsT query blocks of one group: each key row is loaded once
-// and scored against every block's query.
+// qcb[blk][g] . Kidx[g][j] for j < bsel * blk + self (the keys of earlier
+// blocks; per query, bsel = 1 and self = 1: the keys up to and including the
+// query's own).  A workgroup covers 256 candidates and kRowsT query blocks of
+// one group: each key row is loaded once and scored against every block's
+// query.
 // ---------------------------------------------------------------------------
 constexpr int kRowsT = 32;
 
 template <typename T>
 __global__ void __launch_bounds__(256)
 k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
-                 const float* __restrict__ qcb, int32_t blk0, int32_t blk1, Shape s,
-                 float* __restrict__ x, int64_t ldx) {
+                 const float* __restrict__ qcb, int32_t blk0, int32_t blk1, int32_t bsel,
+                 int32_t self, Shape s, float* __restrict__ x, int64_t ldx) {
   const int g = blockIdx.z;
   const int b_lo = blk0 + blockIdx.y * kRowsT;
   const int b_hi = min(blk1, b_lo + kRowsT);
   const int32_t j = blockIdx.x * 256 + threadIdx.x;
-  if ((int64_t)blockIdx.x * 256 >= (int64_t)kQB * (b_hi - 1)) return;  // above every row
+  const int32_t lim_hi = bsel * (b_hi - 1) + self;  // candidates of the slab's last row
+  if ((int64_t)blockIdx.x * 256 >= (int64_t)lim_hi) return;  // above every row
   __shared__ float qs[kRowsT][kRank];
   for (int i = threadIdx.x; i < kRowsT * kRank; i += 256) {
     const int bb = b_lo + i / kRank;
     qs[i / kRank][i % kRank] = bb < b_hi ? qcb[((int64_t)bb * s.Hkv + g) * kRank + i % kRank] : 0.f;
   }
   __syncthreads();
-  if (j >= kQB * (b_hi - 1)) return;
+  if (j >= lim_hi) return;
   const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
   const T* row = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
   float k[kRank];
@@ -148,12 +156,145 @@ k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
     for (int i = 0; i < kRank; ++i) k[i] = to_f32<T>(row[i]);
   }
   for (int bb = b_lo; bb < b_hi; ++bb) {
-    if (j >= kQB * bb) continue;
+    if (j >= bsel * bb + self) continue;
     const float* qv = qs[bb - b_lo];
     float a = 0.f;
 #pragma unroll
     for (int c = 0; c < kRank; ++c) a = fmaf(qv[c], k[c], a);
     x[((int64_t)(bb - blk0) * s.Hkv + g) * ldx + j] = a;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Per-query selection by the mean of the heads' probabilities (the
+// aggregation the attention-mass oracle uses, applied to the low-rank
+// channels): each head keeps its own projected query, its logits over the
+// candidates j <= i become a softmax, and the score of j is the log of the
+// mean over the group's heads of those probabilities.
+// ---------------------------------------------------------------------------
+
+// qh[i][h][c] = s_idx * sum_d W_q[h][d][c] q[i][h][d].  One workgroup per
+// (query, group); thread = (head, D/16 dims), so a head's 16 threads are one
+// DPP row.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_prefill_qh(const T* __restrict__ q, const T* __restrict__ w_q, int32_t Hq, int32_t Hkv,
+             int32_t D, float s_idx, float* __restrict__ qh) {
+  const int i = blockIdx.x, g = blockIdx.y;
+  const int G = Hq / Hkv;
+  const int t = threadIdx.x;
+  if (t >= G * 16) return;  // whole 16-lane rows leave together
+  const int h = g * G + (t >> 4), part = t & 15;
+  const int dpt = D / 16;
+  float acc[kRank];
+#pragma unroll
+  for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
+  for (int e = 0; e < dpt; ++e) {
+    const int d = part * dpt + e;
+    const float v = to_f32<T>(q[((int64_t)i * Hq + h) * D + d]);
+    const T* wr = w_q + ((int64_t)h * D + d) * kRank;
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) acc[c] = fmaf(to_f32<T>(wr[c]), v, acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < kRank; ++c) {
+    const float v = row16_sum(acc[c]);
+    if (part == 0) qh[((int64_t)i * Hq + h) * kRank + c] = v * s_idx;
+  }
+}
+
+constexpr int kRowsQ = 8;     // query rows per workgroup in the per-head passes
+constexpr float kLog2eP = 1.4426950408889634f;
+
+// MODE 0: per (256-candidate tile, query, head) and wave, the max and the sum
+// of 2^(x - max) of the head's base-2 logits over the wave's candidates
+// j <= i.  MODE 1: the scores x[row][j] = ln((1/G) sum_h 2^(x_h - lse2_h)).
+template <typename T, int G, int MODE>
+__global__ void __launch_bounds__(256)
+k_prefill_hprob(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
+                const float* __restrict__ qh, const float* __restrict__ lse2, int32_t q0,
+                int32_t q1, Shape s, float2* __restrict__ part, int32_t nparts,
+                float* __restrict__ x, int64_t ldx) {
+  const int g = blockIdx.z;
+  const int b_lo = q0 + blockIdx.y * kRowsQ;
+  const int b_hi = min(q1, b_lo + kRowsQ);
+  const int tile = blockIdx.x;
+  const int32_t j = tile * 256 + threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if ((int64_t)tile * 256 >= (int64_t)b_hi) return;  // past the last row's candidates (j <= b_hi - 1)
+  __shared__ float qs[kRowsQ][G][kRank];
+  for (int e = threadIdx.x; e < kRowsQ * G * kRank; e += 256) {
+    const int r = e / (G * kRank), hc = e % (G * kRank);
+    const int bb = b_lo + r;
+    qs[r][hc / kRank][hc % kRank] =
+        bb < b_hi ? qh[((int64_t)bb * s.Hq + g * G) * kRank + hc] * kLog2eP : 0.f;
+  }
+  __syncthreads();
+  float k[kRank];
+  if (j < b_hi) {
+    const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
+    const T* row = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) k[c] = to_f32<T>(row[c]);
+  } else {
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) k[c] = 0.f;
+  }
+  for (int bb = b_lo; bb < b_hi; ++bb) {
+    if ((int64_t)tile * 256 > bb) continue;  // whole tile past row bb (uniform)
+    const bool ok = j <= bb;
+    const int64_t r = (int64_t)(bb - q0) * s.Hkv + g;
+    if (MODE == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < kRank; ++c) a = fmaf(qs[bb - b_lo][h][c], k[c], a);
+        const float m = wave_max(ok ? a : -INFINITY);
+        const float l = wave_sum(ok ? exp2f(a - m) : 0.f);
+        if (lane == 0) part[(r * nparts + tile * 4 + wave) * G + h] = make_float2(m, l);
+      }
+    } else {
+      if (!ok) continue;
+      float u[G];
+      float M = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int c = 0; c < kRank; ++c) a = fmaf(qs[bb - b_lo][h][c], k[c], a);
+        u[h] = a - lse2[((int64_t)bb * s.Hq + g * G) + h];
+        M = fmaxf(M, u[h]);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int h = 0; h < G; ++h) sum += exp2f(u[h] - M);
+      x[r * ldx + j] = 0.6931471805599453f * (M + log2f(sum)) - logf((float)G);
+    }
+  }
+}
+
+// lse2[i][h] = log2 sum_{j <= i} 2^(x_h): the wave partials of query i merged
+// in order; one wave per head.
+template <int G>
+__global__ void __launch_bounds__(256)
+k_prefill_hnorm(const float2* __restrict__ part, int32_t nparts, int32_t q0, int32_t Hq,
+                int32_t Hkv, float* __restrict__ lse2) {
+  const int r = blockIdx.x;  // (query - q0) * Hkv + g
+  const int i = q0 + r / Hkv, g = r % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int np = min(nparts, ((i + 1) + 63) / 64);  // waves that saw candidates of row i
+  for (int h = wave; h < G; h += 4) {
+    float m = -INFINITY, l = 0.f;
+    for (int c = lane; c < np; c += 64) {
+      const float2 v = part[((int64_t)r * nparts + c) * G + h];
+      const float mn = fmaxf(m, v.x);
+      l = (mn == -INFINITY) ? 0.f : l * exp2f(m - mn) + v.y * exp2f(v.x - mn);
+      m = mn;
+    }
+    const float M = wave_max(m);
+    const float Ls = wave_sum(m == -INFINITY ? 0.f : l * exp2f(m - M));
+    if (lane == 0) lse2[(int64_t)i * Hq + g * G + h] = M + log2f(Ls);
   }
 }
 
@@ -452,48 +593,125 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   }
 }
 
+// Selection plan: rows of query blocks (bsel = 64) or of queries (bsel = 1)
+// are scored and selected a slab at a time.
+struct PrefillSelPlan {
+  int32_t nblk;      // query blocks (or queries)
+  int64_t slab;      // blocks per slab
+  int32_t self;      // the own token is a candidate (per query)
+  int64_t ldx;       // score row stride (candidates of the last row)
+  int32_t nparts;    // per-head passes: wave partials per row
+  size_t off_x, off_part, off_lse, off_sel, total;
+};
+
+PrefillSelPlan prefill_sel_plan(const Shape& s, int32_t n_tokens, int32_t bsel, bool probs) {
+  PrefillSelPlan p;
+  p.nblk = (n_tokens + bsel - 1) / bsel;
+  p.self = bsel == 1 ? 1 : 0;
+  if (bsel == 1) {  // query slabs of about 512 MB of scores, 256 .. 4096 queries
+    int64_t q = ((int64_t)512 << 20) / ((int64_t)s.Hkv * n_tokens * 4);
+    q = q < 256 ? 256 : (q > 4096 ? 4096 : q);
+    p.slab = p.nblk < q ? p.nblk : q;
+  } else {
+    p.slab = p.nblk < kSlab ? p.nblk : kSlab;
+  }
+  p.ldx = n_tokens > 1 ? n_tokens : 1;
+  p.nparts = probs ? (int32_t)(((n_tokens + 255) / 256) * 4) : 0;
+  const int G = s.Hq / s.Hkv;
+  size_t off = probs ? align_up((size_t)n_tokens * s.Hq * kRank * sizeof(float), 256)
+                     : align_up((size_t)p.nblk * s.Hkv * kRank * sizeof(float), 256);
+  p.off_x = off;
+  off += align_up((size_t)p.slab * s.Hkv * (size_t)p.ldx * sizeof(float), 256);
+  p.off_part = off;
+  if (probs) off += align_up((size_t)p.slab * s.Hkv * p.nparts * G * sizeof(float2), 256);
+  p.off_lse = off;
+  if (probs) off += align_up((size_t)n_tokens * s.Hq * sizeof(float), 256);
+  p.off_sel = off;
+  off += align_up(select_workspace_bytes((int32_t)(p.slab * s.Hkv), n_tokens), 256);
+  p.total = off;
+  return p;
+}
+
 }  // namespace
 
-// Workspace of the prefill selection: block queries + one slab of scores.
+// Workspace of the prefill selection: the larger of the three plans (block
+// supports; per-query with logits; per-query with probabilities).
 size_t prefill_select_workspace_bytes(const Shape& s, int32_t n_tokens) {
-  const int64_t nblk = (n_tokens + kQB - 1) / kQB;
-  const size_t qcb = align_up((size_t)nblk * s.Hkv * kRank * sizeof(float), 256);
-  const int64_t slab = nblk < kSlab ? nblk : kSlab;
-  const size_t xs = align_up((size_t)slab * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
-  const size_t sel = align_up(select_workspace_bytes((int32_t)(slab * s.Hkv), n_tokens), 256);
-  return qcb + xs + sel;
+  size_t a = prefill_sel_plan(s, n_tokens, kQB, false).total;
+  const size_t b = prefill_sel_plan(s, n_tokens, 1, false).total;
+  const size_t c = prefill_sel_plan(s, n_tokens, 1, true).total;
+  a = a > b ? a : b;
+  return a > c ? a : c;
 }
 
 hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_tokens,
                                  const void* q, const void* w_q, const void* kidx_pool,
                                  sa_dtype dt, float s_idx, int32_t b_sel, int32_t k,
                                  int32_t* idx, int32_t* count, int32_t cap, void* ws,
-                                 hipStream_t st) {
-  const int nblk = (n_tokens + kQB - 1) / kQB;
-  const int64_t slab = nblk < kSlab ? nblk : kSlab;
-  char* p = (char*)ws;
-  float* qcb = (float*)p;
-  p += align_up((size_t)nblk * s.Hkv * kRank * sizeof(float), 256);
-  float* xs = (float*)p;
-  p += align_up((size_t)slab * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
-  void* sel_ws = p;
-  dim3 g1(nblk, s.Hkv);
-  if (dt == SA_BF16)
-    k_prefill_qc<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q, n_tokens,
-                                               s.Hq, s.Hkv, s.D, s_idx, qcb);
-  else
-    k_prefill_qc<float><<<g1, 256, 0, st>>>((const float*)q, (const float*)w_q, n_tokens, s.Hq,
-                                            s.Hkv, s.D, s_idx, qcb);
-  for (int b0 = 0; b0 < nblk; b0 += (int)slab) {
-    const int b1 = b0 + (int)slab < nblk ? b0 + (int)slab : nblk;
-    const int64_t ldx = (int64_t)kQB * (b1 - 1) > 0 ? (int64_t)kQB * (b1 - 1) : 1;
-    dim3 g2((unsigned)((ldx + 255) / 256), (b1 - b0 + kRowsT - 1) / kRowsT, s.Hkv);
-    if (dt == SA_BF16)
-      k_prefill_scores<bf16_raw><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qcb,
-                                                     b0, b1, s, xs, ldx);
-    else
-      k_prefill_scores<float><<<g2, 256, 0, st>>>((const float*)kidx_pool, pg.page_table, qcb, b0,
-                                                  b1, s, xs, ldx);
+                                 hipStream_t st, bool probs) {
+  const PrefillSelPlan P = prefill_sel_plan(s, n_tokens, b_sel, probs);
+  const int G = s.Hq / s.Hkv;
+  char* base = (char*)ws;
+  float* qv = (float*)base;  // qcb [nblk][Hkv][16] or, per head, qh [n][Hq][16]
+  float* xs = (float*)(base + P.off_x);
+  float2* part = (float2*)(base + P.off_part);
+  float* lse2 = (float*)(base + P.off_lse);
+  void* sel_ws = base + P.off_sel;
+  const bool bf = dt == SA_BF16;
+  if (probs) {
+    dim3 g1(n_tokens, s.Hkv);
+    if (bf) k_prefill_qh<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q,
+                                                      s.Hq, s.Hkv, s.D, s_idx, qv);
+    else k_prefill_qh<float><<<g1, 256, 0, st>>>((const float*)q, (const float*)w_q, s.Hq, s.Hkv,
+                                                 s.D, s_idx, qv);
+  } else {
+    dim3 g1(P.nblk, s.Hkv);
+    if (bf) k_prefill_qc<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q,
+                                                      n_tokens, s.Hq, s.Hkv, s.D, b_sel, s_idx, qv);
+    else k_prefill_qc<float><<<g1, 256, 0, st>>>((const float*)q, (const float*)w_q, n_tokens, s.Hq,
+                                                 s.Hkv, s.D, b_sel, s_idx, qv);
+  }
+  for (int b0 = 0; b0 < P.nblk; b0 += (int)P.slab) {
+    const int b1 = b0 + (int)P.slab < P.nblk ? b0 + (int)P.slab : P.nblk;
+    const int64_t cand_hi = (int64_t)b_sel * (b1 - 1) + P.self;  // candidates of the last row
+    const int64_t ldx = cand_hi > 0 ? cand_hi : 1;
+    if (probs) {
+      const int ntile = (int)((cand_hi + 255) / 256);
+      dim3 g2(ntile > 0 ? ntile : 1, (b1 - b0 + kRowsQ - 1) / kRowsQ, s.Hkv);
+#define SA_HP(GG)                                                                               \
+  case GG:                                                                                      \
+    if (bf) {                                                                                   \
+      k_prefill_hprob<bf16_raw, GG, 0><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool,          \
+          pg.page_table, qv, lse2, b0, b1, s, part, P.nparts, xs, ldx);                         \
+      k_prefill_hnorm<GG><<<(b1 - b0) * s.Hkv, 256, 0, st>>>(part, P.nparts, b0, s.Hq, s.Hkv, lse2); \
+      k_prefill_hprob<bf16_raw, GG, 1><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool,          \
+          pg.page_table, qv, lse2, b0, b1, s, part, P.nparts, xs, ldx);                         \
+    } else {                                                                                    \
+      k_prefill_hprob<float, GG, 0><<<g2, 256, 0, st>>>((const float*)kidx_pool,                \
+          pg.page_table, qv, lse2, b0, b1, s, part, P.nparts, xs, ldx);                         \
+      k_prefill_hnorm<GG><<<(b1 - b0) * s.Hkv, 256, 0, st>>>(part, P.nparts, b0, s.Hq, s.Hkv, lse2); \
+      k_prefill_hprob<float, GG, 1><<<g2, 256, 0, st>>>((const float*)kidx_pool,                \
+          pg.page_table, qv, lse2, b0, b1, s, part, P.nparts, xs, ldx);                         \
+    }                                                                                           \
+    break;
+      switch (G) {
+        SA_HP(1)
+        SA_HP(2)
+        SA_HP(4)
+        SA_HP(8)
+        SA_HP(16)
+        default: return hipErrorNotSupported;
+      }
+#undef SA_HP
+    } else {
+      dim3 g2((unsigned)((ldx + 255) / 256), (b1 - b0 + kRowsT - 1) / kRowsT, s.Hkv);
+      if (bf)
+        k_prefill_scores<bf16_raw><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table,
+                                                       qv, b0, b1, b_sel, P.self, s, xs, ldx);
+      else
+        k_prefill_scores<float><<<g2, 256, 0, st>>>((const float*)kidx_pool, pg.page_table, qv,
+                                                    b0, b1, b_sel, P.self, s, xs, ldx);
+    }
     SelectArgs a{};
     a.x = xs;
     a.ldx = ldx;
@@ -507,13 +725,51 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     a.p = 0.f;
     a.k = k;
     a.n_sink = 0;
-    a.n_window = 0;
+    a.n_window = P.self;  // per query: the own token is always kept
     a.idx = idx + (int64_t)b0 * s.Hkv * cap;
     a.count = count + (int64_t)b0 * s.Hkv;
     a.cap = cap;
-    a.prefill_bsel = kQB;
+    a.prefill_bsel = b_sel;
     a.prefill_blk0 = b0;
+    a.prefill_self = P.self;
     hipError_t e = launch_select(a, sel_ws, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
+
+// Per-query attention: the split-KV decode kernels with every query row as a
+// "sequence" of length i + 1 that shares the one page table row.
+size_t prefill_query_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t cap) {
+  Shape s2 = s;
+  s2.B = kPrefillQuerySlab;
+  return align_up((size_t)n_tokens * sizeof(int32_t), 256) + decode_workspace_bytes(s2, cap);
+}
+
+hipError_t launch_sparse_prefill_query(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       sa_dtype dt, const int32_t* idx, const int32_t* count,
+                                       int32_t cap, float s_att, void* out, sa_dtype out_dt,
+                                       float* lse, void* ws, hipStream_t st) {
+  int32_t* lens = (int32_t*)ws;
+  void* dws = (char*)ws + align_up((size_t)n_tokens * sizeof(int32_t), 256);
+  k_iota1<<<(n_tokens + 255) / 256, 256, 0, st>>>(lens, n_tokens);
+  const size_t qe = dt == SA_BF16 ? 2 : 4, oe = out_dt == SA_BF16 ? 2 : 4;
+  // the decode kernels plan at most 4096 (row, group) pairs per launch
+  const int32_t qslab = kPrefillQuerySlab < 4096 / s.Hkv ? kPrefillQuerySlab : 4096 / s.Hkv;
+  for (int32_t q0 = 0; q0 < n_tokens; q0 += qslab) {
+    const int32_t nq = n_tokens - q0 < qslab ? n_tokens - q0 : qslab;
+    Shape s2 = s;
+    s2.B = nq;
+    s2.max_pages = 0;  // every query row reads page-table row 0
+    sa_pages p2;
+    p2.page_table = pg.page_table;
+    p2.seq_lens = lens + q0;
+    hipError_t e = launch_sparse_decode(
+        s2, p2, (const char*)q + (size_t)q0 * s.Hq * s.D * qe, k_pool, v_pool, dt,
+        idx + (int64_t)q0 * s.Hkv * cap, count + (int64_t)q0 * s.Hkv, cap, s_att,
+        (char*)out + (size_t)q0 * s.Hq * s.D * oe, out_dt, lse ? lse + (int64_t)q0 * s.Hq : nullptr,
+        dws, st);
     if (e != hipSuccess) return e;
   }
   return hipGetLastError();

@@ -215,6 +215,7 @@ struct SelectArgs {
   // prefill_bsel * blk candidates; 0 for decode rows
   int32_t prefill_bsel;
   int32_t prefill_blk0;
+  int32_t prefill_self;     // per-query rows: the own token is a candidate too
 };
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st);
@@ -240,7 +241,14 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
                                  const void* q, const void* w_q, const void* kidx_pool,
                                  sa_dtype dt, float s_idx, int32_t b_sel, int32_t k,
                                  int32_t* idx, int32_t* count, int32_t cap, void* ws,
-                                 hipStream_t st);
+                                 hipStream_t st, bool probs = false);
+constexpr int32_t kPrefillQuerySlab = 512;  // query rows per per-query attention launch
+size_t prefill_query_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t cap);
+hipError_t launch_sparse_prefill_query(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                       const void* q, const void* k_pool, const void* v_pool,
+                                       sa_dtype dt, const int32_t* idx, const int32_t* count,
+                                       int32_t cap, float s_att, void* out, sa_dtype out_dt,
+                                       float* lse, void* ws, hipStream_t st);
 hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_tokens,
                                  const void* q, const void* k_pool, const void* v_pool,
                                  const int32_t* idx, const int32_t* count, int32_t cap,

@@ -75,7 +75,7 @@ WsLayout carve(void* ws, int32_t rows, int32_t max_cand) {
 }
 
 __device__ __forceinline__ int32_t n_cand_of(const SelectArgs& a, int row) {
-  if (a.prefill_bsel > 0) return a.prefill_bsel * (a.prefill_blk0 + row / a.Hkv);
+  if (a.prefill_bsel > 0) return a.prefill_bsel * (a.prefill_blk0 + row / a.Hkv) + a.prefill_self;
   const int b = row / a.Hkv;
   const int32_t L = clamp_len(a.seq_lens[b], a.max_len);
   return a.unit == 1 ? L : (L + a.unit - 1) / a.unit;

@@ -34,6 +34,8 @@ __all__ = [
     "sa_decode_step",
     "sa_select_prefill_topk",
     "sa_sparse_prefill",
+    "sa_select_prefill_topk_probs",
+    "sa_sparse_prefill_query",
     "version",
 ]
 
@@ -214,3 +216,24 @@ def sa_sparse_prefill(shape, pages, n_tokens, q, k_pool, v_pool, idx, count, b_s
                                     _dev(count), int(idx.shape[-1]), int(b_sel), float(s_att),
                                     _dev(out), _dt(out), _dev(lse), _stream(stream))
     L.check(st, "sa_sparse_prefill")
+
+
+def sa_select_prefill_topk_probs(shape, pages, n_tokens, q, w_q, kidx_pool, s_idx, b_sel, k, idx,
+                                 count, ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_select_prefill_topk_probs(ctypes.byref(shape), ctypes.byref(pages),
+                                               int(n_tokens), _dev(q), _dev(w_q), _dev(kidx_pool),
+                                               _dt(q), float(s_idx), int(b_sel), int(k), _dev(idx),
+                                               _dev(count), int(idx.shape[-1]), wp, wn,
+                                               _stream(stream))
+    L.check(st, "sa_select_prefill_topk_probs")
+
+
+def sa_sparse_prefill_query(shape, pages, n_tokens, q, k_pool, v_pool, idx, count, s_att, out, lse,
+                            ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_sparse_prefill_query(ctypes.byref(shape), ctypes.byref(pages), int(n_tokens),
+                                          _dev(q), _dev(k_pool), _dev(v_pool), _dt(q), _dev(idx),
+                                          _dev(count), int(idx.shape[-1]), float(s_att), _dev(out),
+                                          _dt(out), _dev(lse), wp, wn, _stream(stream))
+    L.check(st, "sa_sparse_prefill_query")

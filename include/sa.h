@@ -97,7 +97,8 @@ typedef enum {
   SA_OP_PREFILL_SELECT = 3,  /* param = n_tokens of the prefill                  */
   SA_OP_DECODE_STEP = 4,     /* param = cap                                      */
   SA_OP_SPARSE_DECODE_RLA = 5, /* param = cap                                    */
-  SA_OP_ATTENTION_MASS = 6     /* param unused                                   */
+  SA_OP_ATTENTION_MASS = 6,    /* param unused                                   */
+  SA_OP_PREFILL_QUERY = 7      /* param = cap                                    */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -301,23 +302,63 @@ sa_status sa_support_coverage(const sa_shape* shape, const sa_pages* pages, cons
  * Causal prefill with supports shared by blocks of b_sel queries
  * ------------------------------------------------------------------------- */
 
-/* Block supports ("Oracle-Guided Sparse Prefill", sections 2.1 and 2.2): for
- * query block blk = rows [blk * b_sel, min(n_tokens, (blk + 1) * b_sel)) and
- * group g,
+/* Prefill supports ("Oracle-Guided Sparse Prefill", sections 2.1 and 2.2:
+ * one support per selection block of b_sel queries, b_sel = 64, or per query,
+ * b_sel = 1).  b_sel = 64: for query block blk = rows
+ * [blk * b_sel, min(n_tokens, (blk + 1) * b_sel)) and group g,
  *   q_c = s_idx * mean_{i in blk, h in g} W_q[h]^T q[i][h]
  * scores x_j = q_c . Kidx[g][j] over the keys of earlier blocks,
  * j < blk * b_sel, and keeps the top k of them (all when there are at most k)
  * ranked as in sa_select_topk.  Output idx[blk * n_kv_heads + g][cap]
  * ascending, -1 padded, count likewise; cap >= min(k, n_tokens).  The block's
  * own keys are not listed: sa_sparse_prefill always attends to them causally.
+ * b_sel = 1 (per query, the rule of a decode step on the prefix): row
+ * i * n_kv_heads + g keeps the top k of x_j = q_c(i) . Kidx[g][j] over
+ * j <= i, q_c(i) = s_idx * mean_{h in g} W_q[h]^T q[i][h], plus the query's
+ * own token i, which is always listed; cap >= min(k + 1, n_tokens); the lists
+ * feed sa_sparse_prefill_query.
  * q [n_tokens][n_q_heads][head_dim], w_q, kidx_pool of dtype; page_table row 0
- * of pages maps the single sequence. */
+ * of pages maps the single sequence; workspace from SA_OP_PREFILL_SELECT
+ * (param = n_tokens). */
 sa_status sa_select_prefill_topk(const sa_shape* shape, const sa_pages* pages,
                                  int32_t n_tokens, const void* q, const void* w_q,
                                  const void* kidx_pool, sa_dtype dtype, float s_idx,
                                  int32_t b_sel, int32_t k, int32_t* idx, int32_t* count,
                                  int32_t cap, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* Per-query supports ranked by the mean of the heads' probabilities (the
+ * aggregation the oracle of "Oracle-Guided Sparse Prefill", section 2.1,
+ * uses, applied to the low-rank channels instead of the head-collapsed one):
+ * b_sel must be 1; for query i and group g, each head h in g scores
+ * x_hj = s_idx * (W_q[h]^T q[i][h]) . Kidx[g][j] over j <= i, and the
+ * candidates are ranked by P_j = mean_h softmax_j(x_hj) (ties lower index
+ * first); the top k plus the own token are listed as for
+ * sa_select_prefill_topk with b_sel = 1.  Same arguments, outputs and
+ * workspace. */
+sa_status sa_select_prefill_topk_probs(const sa_shape* shape, const sa_pages* pages,
+                                       int32_t n_tokens, const void* q, const void* w_q,
+                                       const void* kidx_pool, sa_dtype dtype, float s_idx,
+                                       int32_t b_sel, int32_t k, int32_t* idx, int32_t* count,
+                                       int32_t cap, void* ws, size_t ws_bytes,
+                                       hipStream_t stream);
+
+/* Per-query sparse prefill attention ("Oracle-Guided Sparse Prefill",
+ * section 2.1, per-query granularity): query i, head h of group g attends to
+ * the listed keys S = idx[i * n_kv_heads + g][0 .. count) only (lists from
+ * sa_select_prefill_topk with b_sel = 1 hold the query's own token):
+ *   out[i][h] = sum_{j in S} softmax_S(s_att * q[i][h] . k_j) v_j,  lse likewise.
+ * List entries must be in [0, i].  The group's heads share every gathered
+ * K/V row (split-KV kernels of sa_sparse_decode, each query a sequence of
+ * length i + 1 on page-table row 0).  q [n_tokens][n_q_heads][head_dim],
+ * k_pool, v_pool of dtype; out of out_dtype; lse fp32 or NULL; workspace from
+ * SA_OP_PREFILL_QUERY (param = cap, sized for n_tokens = max_len). */
+sa_status sa_sparse_prefill_query(const sa_shape* shape, const sa_pages* pages,
+                                  int32_t n_tokens, const void* q, const void* k_pool,
+                                  const void* v_pool, sa_dtype dtype, const int32_t* idx,
+                                  const int32_t* count, int32_t cap, float s_att, void* out,
+                                  sa_dtype out_dtype, float* lse, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
 
 /* Block-sparse causal prefill attention ("Oracle-Guided Sparse Prefill",
  * section 2.1): row i of block blk, head h of group g attends to the listed

@@ -139,6 +139,16 @@ def test_validation_codes():
     s2 = _shape(L, batch=2)
     assert so.sa_select_prefill_topk(B(s2), B(pg), 100, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 64, 2048, FAKE, FAKE, 2048, FAKE, 1 << 30, None) == L.SA_ERR_UNSUPPORTED
     assert so.sa_select_prefill_topk(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 64, 2048, FAKE, FAKE, 2000, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
+    # per-query prefill: b_sel, capacity (k + 1 with the own token), workspace
+    assert so.sa_select_prefill_topk(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 1, 2048, FAKE, FAKE, 2048, FAKE, 1 << 40, None) == L.SA_ERR_CAPACITY
+    assert so.sa_select_prefill_topk(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 2, 2048, FAKE, FAKE, 2049, FAKE, 1 << 40, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_select_prefill_topk_probs(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 64, 2048, FAKE, FAKE, 2049, FAKE, 1 << 40, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_select_prefill_topk_probs(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 1, 0, FAKE, FAKE, 2049, FAKE, 1 << 40, None) == L.SA_ERR_INVALID_ARGUMENT
+    ws_q = so.sa_workspace_size(L.SA_OP_PREFILL_QUERY, B(s1), 2049)
+    assert ws_q > 131072 * 4
+    assert so.sa_sparse_prefill_query(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2049, 0.1, FAKE, L.SA_BF16, None, FAKE, ws_q - 1, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_sparse_prefill_query(B(s1), B(pg), 0, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2049, 0.1, FAKE, L.SA_BF16, None, FAKE, ws_q, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_sparse_prefill(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2048, 1, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_UNSUPPORTED
     # maintenance calls
     assert so.sa_index_append(B(s), None, FAKE, L.SA_BF16, FAKE, 5, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_index_append(B(s), FAKE, FAKE, L.SA_BF16, FAKE, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
