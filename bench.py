@@ -40,7 +40,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode64k",
-                    choices=["decode64k", "decode1m", "batched", "prefill128k"])
+                    choices=["decode64k", "decode1m", "batched", "prefill128k",
+                             "prefill32k_query"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--warm", action="store_true",
@@ -52,6 +53,9 @@ def parse():
                     help="token-level decode workloads: take the support from the low-rank "
                          "indexer (default) or from the dense head-averaged attention mass "
                          "(the attention-mass oracle: sa_attention_mass + sa_select_topp)")
+    ap.add_argument("--aggregate", default="logits", choices=["logits", "probs"],
+                    help="prefill32k_query: rank by the head-collapsed logits or by the mean of "
+                         "the heads' probabilities (sa_select_prefill_topk_probs)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run only a plain 1 GiB device copy (5 dispatches): the reference "
                          "for scaling FETCH_SIZE / WRITE_SIZE counter readings to bytes")
@@ -112,6 +116,7 @@ KERNEL_SOURCES = {
     "sparse_decode_rla": ["decode.hip"],
     "sparse_prefill": ["prefill.hip"],
     "attention_mass": ["mass.hip"],
+    "sparse_prefill_query": ["decode.hip", "prefill.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -545,6 +550,117 @@ def bench_prefill(args):
     return res
 
 
+def bench_prefill_query(args):
+    """Per-query (b_sel = 1) prefill at 32K: a top-2048 support per (query,
+    group) plus the own token, and each query's attention over its list
+    (split-KV kernels).  Bytes = 512 B of K/V per listed key per group (what
+    the per-query gather needs); FLOPs = 4 * d per listed key per head."""
+    import numpy as np
+    import torch
+
+    import synth
+    from dynamic_sparse_attention_02_amd import _lib as L
+    from dynamic_sparse_attention_02_amd import ops
+
+    inp = synth.make_prefill_query32k(device="cuda")
+    N, Hq, Hkv, d = inp.N, inp.H_q, inp.H_kv, inp.d
+    G = Hq // Hkv
+    probs = args.aggregate == "probs"
+    shape = ops.make_shape(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
+                           max_pages=inp.page_table.shape[1], max_len=N,
+                           n_pool_pages=inp.k_pool.shape[0])
+    pages = ops.make_pages(inp.page_table, None)
+    kidx = torch.zeros((inp.k_pool.shape[0], Hkv, 64, 16), dtype=inp.dtype, device="cuda")
+    fill_kidx(ops, shape, inp, kidx)
+    k = inp.top_k
+    cap = min(k + 1, N)
+    idx = torch.empty((N * Hkv, cap), dtype=torch.int32, device="cuda")
+    count = torch.empty((N * Hkv,), dtype=torch.int32, device="cuda")
+    out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
+    ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_SELECT, shape, N))
+    ws_a = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_QUERY, shape, cap))
+    sel_fn = ops.sa_select_prefill_topk_probs if probs else ops.sa_select_prefill_topk
+
+    def select():
+        sel_fn(shape, pages, N, inp.q, inp.w_q, kidx, inp.s_idx, 1, k, idx, count, ws)
+
+    def attend():
+        ops.sa_sparse_prefill_query(shape, pages, N, inp.q, inp.k_pool, inp.v_pool, idx, count,
+                                    inp.s_att, out, lse, ws_a)
+
+    select()
+    attend()
+    torch.cuda.synchronize()
+    listed = int(count.cpu().numpy().astype(np.int64).sum())
+    flops = 4.0 * d * G * float(listed)
+    kv_bytes = listed * 2 * d * 2
+    for _ in range(args.warmup):
+        select()
+        attend()
+    t_sel = time_events(select, args.steps)
+    t_att = time_events(attend, args.steps)
+    ms = t_sel + t_att
+    gbs = kv_bytes / (t_att * 1e-3) / 1e9
+    name = "prefill32k_query" + ("+probs" if probs else "")
+    res = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
+                   "b_sel": 1, "top_k": k,
+                   "aggregate": "mean of head probabilities" if probs else "head-collapsed logits"},
+        "algorithmic_flops": flops, "kv_bytes": kv_bytes,
+        "budget_fraction": round(listed / (Hkv * N * (N + 1) / 2), 5),
+        "breakdown_ms": {"select": round(t_sel, 4), "attention": round(t_att, 4)},
+        "attention_tflops": round(flops / (t_att * 1e-3) / 1e12, 3),
+        "roofline": {"kernel": "sparse_prefill_query", "bound": "hbm", "achieved": round(gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic(name, "sparse_prefill_query"),
+                     "bytes_per_launch": kv_bytes, "avg_launch_ms": round(t_att, 4),
+                     "note": "gathered K/V rows per listed key; the 134 MB cache of this "
+                             "workload fits the last-level cache, so rows repeat from it"},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill_query(inp, kidx, args.cpu_seconds, probs)
+    return res
+
+
+def cpu_baseline_prefill_query(inp, kidx, seconds, probs):
+    """The float64 oracle on a bounded sample of the per-query prefill: whole
+    (query, group) rows (scores, support, attention), last queries first."""
+    import oracle as O
+    from threadpoolctl import threadpool_limits
+
+    g = 0
+    hs = inp.heads(g)
+    K = inp.keys(g).double().cpu().numpy()
+    V = inp.values(g).double().cpu().numpy()
+    kt = inp.rows(kidx, g).double().cpu().numpy()
+    wq = inp.w_q[hs].double().cpu().numpy()
+    flops = 0.0
+    n_rows = 0
+    t0 = time.perf_counter()
+    with threadpool_limits():
+        threads = blas_threads()
+        for i in range(inp.N - 1, -1, -1):
+            qi = inp.q[i, hs].double().cpu().numpy()
+            x = O.prefill_query_scores(qi, wq, kt, i, inp.s_idx, "probs" if probs else "logits")
+            S_ = O.prefill_query_support(x, i, inp.top_k)
+            O.prefill_query_attend(qi, K, V, S_, inp.s_att)
+            flops += 4.0 * inp.d * len(hs) * len(S_)
+            n_rows += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_rows} (query, group) rows of the last queries (scores + support + "
+                      f"attention), float64 numpy, {el:.1f} s",
+            "host_threads_available": cpu_threads_info()}
+
+
 def time_events(fn, n):
     """Average milliseconds of fn() over n calls (HIP events, current stream)."""
     import torch
@@ -617,6 +733,8 @@ def main():
     pkg.load_library()
     if args.workload == "prefill128k":
         res = bench_prefill(args)
+    elif args.workload == "prefill32k_query":
+        res = bench_prefill_query(args)
     else:
         res = bench_decode(args, args.workload)
     print(json.dumps(res))

@@ -31,6 +31,7 @@ __all__ = [
     "make_decode1m",
     "make_batched_decode",
     "make_prefill128k",
+    "make_prefill_query32k",
     "make_decode_custom",
     "make_prefill_custom",
     "seed_of",
@@ -463,6 +464,16 @@ def make_prefill_custom(*, name="prefill_custom", N=512, H_q=8, H_kv=2, d=64,
         w_q=w_q, w_k=w_k, k_pool=k_pool, v_pool=v_pool, page_table=table.to(device),
         s_idx=math.sqrt(d) / r, s_att=1.0 / math.sqrt(d), b_sel=b_sel, top_k=top_k,
         planted=planted)
+
+
+def make_prefill_query32k(device="cpu", seed=0, N=32768) -> PrefillInputs:
+    """Per-query (b_sel = 1) causal sparse prefill at 32K: the 128K recipe
+    (32 query / 8 key-value heads, d=128, bf16, 0.5% column heavy hitters per
+    group) with one top-2048 support per query."""
+    return make_prefill_custom(
+        name="prefill32k_query", N=N, H_q=32, H_kv=8, d=128, dtype=torch.bfloat16, device=device,
+        seed=seed, cfg=6, n_hh=int(round(0.005 * N)), q_shift=2.0, k_shift=8.0,
+        b_sel=1, top_k=2048, tied=True)
 
 
 def make_prefill128k(device="cpu", seed=0, N=131072) -> PrefillInputs:

@@ -132,3 +132,18 @@ def test_query_prefill_deterministic():
     b = run_query_prefill(inp, kidx, 100, probs=True)
     for u, v in zip(a, b):
         assert torch.equal(u, v)
+
+
+@pytest.mark.parametrize("probs", [False, True])
+def test_query_prefill_32k_workload_sampled(probs):
+    """The per-query 32K workload as the bench runs it (32/8 heads, d=128,
+    bf16, top-2048 per query): sampled (query, group) rows against the
+    oracle, early, boundary and late queries."""
+    inp = synth.make_prefill_query32k(device="cuda")
+    groups = [0, 5]
+    kidx, kt_rows = oracle_kidx(inp, groups=groups)
+    idx, count, out, lse = run_query_prefill(inp, kidx, inp.top_k, probs=probs)
+    queries = [0, 2047, 2048, 2049, 9000, 20000, 32767]
+    n_diff = check_queries(inp, kt_rows, idx, count, out, lse, inp.top_k, queries, groups,
+                           probs=probs)
+    print(f"prefill32k_query probs={probs}: tolerated support differences {n_diff}")
