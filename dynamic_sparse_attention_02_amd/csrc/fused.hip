@@ -93,17 +93,22 @@ __device__ __forceinline__ void stamp(const FusedArgs& a, int slot) {
   if (threadIdx.x == 0) a.trace[(int64_t)blockIdx.x * kTraceSlots + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
-// Per-row barrier: a device-scope release before the arrival is counted, so
-// every write of the workgroup (histogram bins, counts, the row maximum,
-// attention partials) is performed before any other workgroup of the row can
-// pass.  No acquire fence (an L2 invalidate) follows: every read of data
-// another workgroup produced is itself a device-scope atomic load, which the
-// L2 does not serve stale.  The spin is bounded: a barrier that waits too
+// Per-row barrier.  Everything one workgroup hands to another (histogram
+// bins, counts, the row maximum, attention partials) is written with
+// device-scope atomics or device-scope stores, which complete at the
+// device's coherence point, and read with device-scope loads, which the L2
+// does not serve stale.  So the barrier needs no L2 write-back or
+// invalidate: each wave waits until its own memory operations have
+// completed, then one thread counts the arrival.  (A release fence here
+// would write back every dirty L2 line on each arrival, which costs several
+// microseconds per barrier.)  The spin is bounded: a barrier that waits too
 // long raises the error flag and lets the launch finish instead of hanging.
 __device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's loads, stores and atomics completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
   if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     atomicAdd(ctr, 1u);
     uint32_t spins = 0;
     while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
