@@ -47,6 +47,15 @@ Parity status of each function (what pins it, from the tests in
                          ranking; the probability mean is a distribution and
                          its top-k holds the largest mass (brute force); the
                          own token is always kept.
+* ``pbs_*``              pinned: importance is a distribution and equals the
+                         head/query mean of causal torch SDPA weights; the
+                         permutation maps every segment onto itself, sorts by
+                         importance and moves a planted key to its segment's
+                         front; block scores are linear in the pooled means;
+                         with every block selected the attention is dense
+                         causal SDPA; on scattered heavy hitters the permuted
+                         top block covers more attention mass than any
+                         natural block (the method's purpose).
 * ``head_mean_attention``, ``oracle_support``, ``support_coverage``,
   ``support_overlap``
                          pinned: the head-averaged distribution equals the
@@ -64,7 +73,10 @@ group's heads (and over a query block) of the projected query, the union of
 the always-kept sink/window tokens after selection, the log-domain mean over a
 group's heads of the page score, the partial-page term log(n/page), and the
 residual linear attention's feature map on the raw (unscaled) query/key rows
-with the unselected set taken as the complement of the final support.
+with the unselected set taken as the complement of the final support; for the
+segment permutation, the importance as the mean attention probability of the
+last query block, the query's own segment kept in natural order, and top-k
+block selection.
 """
 
 from .sparse_attention import *  # noqa: F401,F403

@@ -24,7 +24,9 @@ against the pages:
   state).
 * "Sparser Block-Sparse Attention via Token Permutation" (PBS-Attn) -- section 1
   (attention output is invariant to a joint permutation of key/value pairs and
-  covariant with a permutation of the queries).
+  covariant with a permutation of the queries); sections 2 to 4 (keys
+  reordered inside fixed-size segments by a global importance taken from the
+  last query block, block selection by mean pooling on the reordered keys).
 
 Group convention (grouped-query attention): with G = H_q / H_kv, query head h
 belongs to key/value group g = h // G.
@@ -62,6 +64,11 @@ __all__ = [
     "prefill_query_scores",
     "prefill_query_support",
     "prefill_query_attend",
+    "pbs_importance",
+    "pbs_permutation",
+    "pbs_block_keys",
+    "pbs_block_scores",
+    "pbs_block_support",
     "group_of_head",
     "heads_of_group",
     "rla_feature",
@@ -493,6 +500,85 @@ def prefill_query_attend(q_i, K, V, S, s_att: float):
     (which holds the query's own token)."""
     S = [int(j) for j in S]
     return attend(q_i, f64(K)[S], f64(V)[S], s_att)
+
+
+# ---------------------------------------------------------------------------
+# Segment-permuted block selection (PBS-Attn, sections 2 to 4)
+# ---------------------------------------------------------------------------
+
+
+def pbs_importance(Q_last, K, first: int, s_att: float) -> np.ndarray:
+    """Global key importance from the last query block (PBS-Attn section 3):
+    each query i of the block (position first + i) and each head of the
+    group attends causally to keys j <= first + i; the importance of key j is
+    the mean over those (query, head) pairs of the attention probability
+    (zero where the key is in a query's future).
+
+    Q_last: [n_rows, G, d], K: [N, d] -> [N]
+    """
+    Q_last, K = f64(Q_last), f64(K)
+    n_rows, G, _ = Q_last.shape
+    imp = np.zeros(K.shape[0])
+    for i in range(n_rows):
+        L = first + i + 1
+        for h in range(G):
+            z = s_att * (K[:L] @ Q_last[i, h])
+            w = np.exp(z - z.max())
+            imp[:L] += w / w.sum()
+    return imp / (n_rows * G)
+
+
+def pbs_permutation(importance, seg: int) -> np.ndarray:
+    """Segment permutation (PBS-Attn sections 2 and 3): the positions of each
+    segment [s * seg, (s + 1) * seg) are reordered by importance, largest
+    first (equal importance: lower position first); no key leaves its
+    segment.  perm[p] = the position of the key placed at p."""
+    imp = f64(importance)
+    N = imp.shape[0]
+    perm = np.arange(N)
+    for s0 in range(0, N, seg):
+        idx = np.arange(s0, min(N, s0 + seg))
+        order = np.lexsort((idx, -imp[idx]))
+        perm[s0:s0 + len(idx)] = idx[order]
+    return perm
+
+
+def pbs_block_keys(perm, blk: int, b_sel: int, seg: int, c: int) -> np.ndarray:
+    """Keys of candidate block c of query block blk: a block of the permuted
+    order in a segment that ends before the query block's segment, or, inside
+    its own segment, a block in natural order (a permutation there would put
+    later keys before earlier ones)."""
+    own_seg_first_block = (blk * b_sel // seg) * seg // b_sel
+    if c < own_seg_first_block:
+        return np.asarray(perm[c * b_sel:(c + 1) * b_sel], dtype=np.int64)
+    return np.arange(c * b_sel, (c + 1) * b_sel)
+
+
+def pbs_block_scores(Q_blk, K, perm, blk: int, b_sel: int, seg: int) -> np.ndarray:
+    """Mean-pooled block scores (PBS-Attn section 4): the mean of the block's
+    queries over its rows and the group's heads, dotted with the mean of each
+    candidate block's keys, for the blk earlier blocks.
+
+    Q_blk: [n_rows, G, d], K: [N, d] -> [blk]
+    """
+    Q_blk, K = f64(Q_blk), f64(K)
+    qbar = Q_blk.reshape(-1, Q_blk.shape[-1]).mean(axis=0)
+    x = np.zeros(blk)
+    for c in range(blk):
+        kbar = K[pbs_block_keys(perm, blk, b_sel, seg, c)].mean(axis=0)
+        x[c] = qbar @ kbar
+    return x
+
+
+def pbs_block_support(x, perm, blk: int, b_sel: int, seg: int, k_blocks: int) -> np.ndarray:
+    """Keys of the top-k candidate blocks (ties lower block first), ascending;
+    the query block's own keys are attended causally on top (as in
+    prefill_block_attend)."""
+    if blk == 0:
+        return np.zeros(0, dtype=np.int64)
+    blocks = select_topk(x, k_blocks)
+    keys = np.concatenate([pbs_block_keys(perm, blk, b_sel, seg, int(c)) for c in blocks])
+    return np.sort(keys)
 
 
 # ---------------------------------------------------------------------------

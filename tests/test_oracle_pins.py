@@ -734,3 +734,105 @@ def test_prefill_query_probs_topk_brute_force(seed):
         S = O.select_topk(x, k)
         best = max(P[list(c)].sum() for c in itertools.combinations(range(i + 1), k))
         assert abs(P[S].sum() - best) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Segment-permuted block selection (PBS-Attn sections 2 to 4)
+# ---------------------------------------------------------------------------
+
+
+def test_pbs_importance_is_mean_of_causal_sdpa_weights():
+    rng = _rng(80)
+    N, G, d, b = 50, 2, 8, 6
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    s = 0.4
+    first = N - b
+    imp = O.pbs_importance(Q[first:], K, first, s)
+    W = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], np.eye(N)[None, None], s,
+              causal=True)[0]                      # [G, N, N] weights
+    np.testing.assert_allclose(imp, W[:, first:, :].mean(axis=(0, 1)), rtol=1e-12, atol=1e-16)
+    assert abs(imp.sum() - 1.0) < 1e-12
+
+
+def test_pbs_permutation_is_segmentwise_sort():
+    rng = _rng(81)
+    imp = rng.random(70)
+    imp[[3, 4]] = 0.5                                  # a tie: lower position first
+    perm = O.pbs_permutation(imp, 16)
+    assert sorted(perm.tolist()) == list(range(70))
+    for s0 in range(0, 70, 16):
+        seg = perm[s0:s0 + 16]
+        assert seg.min() >= s0 and seg.max() < s0 + 16
+        assert np.all(np.diff(imp[seg]) <= 0)
+    p0 = perm[:16].tolist()
+    if imp[3] == imp[4]:
+        assert p0.index(3) < p0.index(4)
+    imp2 = np.zeros(40)
+    imp2[29] = 1.0                                     # planted key goes to its segment's front
+    assert O.pbs_permutation(imp2, 10)[20] == 29
+
+
+def test_pbs_block_keys_and_scores_linear():
+    rng = _rng(82)
+    N, G, d, b_sel, seg = 256, 2, 8, 16, 64
+    K = rng.standard_normal((N, d))
+    Q = rng.standard_normal((N, G, d))
+    perm = O.pbs_permutation(rng.random(N), seg)
+    blk = 9                                            # own segment = blocks 8..11
+    keys = [O.pbs_block_keys(perm, blk, b_sel, seg, c) for c in range(blk)]
+    assert np.array_equal(np.sort(np.concatenate(keys)), np.arange(blk * b_sel))
+    assert np.array_equal(keys[8], np.arange(128, 144))          # own segment: natural order
+    assert np.array_equal(keys[3], perm[48:64])                  # earlier segment: permuted
+    x = O.pbs_block_scores(Q[blk * b_sel:(blk + 1) * b_sel], K, perm, blk, b_sel, seg)
+    qbar = Q[blk * b_sel:(blk + 1) * b_sel].reshape(-1, d).mean(axis=0)
+    for c in (0, 5, 8):
+        np.testing.assert_allclose(x[c], np.mean(K[keys[c]] @ qbar), rtol=1e-12)
+
+
+def test_pbs_all_blocks_is_dense_causal():
+    rng = _rng(83)
+    N, G, d, b_sel, seg = 192, 2, 16, 32, 64
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    s = 1 / math.sqrt(d)
+    perm = O.pbs_permutation(O.pbs_importance(Q[-b_sel:], K, N - b_sel, s), seg)
+    ref = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], V[None, None], s, causal=True)[0]
+    for blk in range(N // b_sel):
+        rows = O.prefill_block_rows(blk, b_sel, N)
+        x = O.pbs_block_scores(Q[rows.start:rows.stop], K, perm, blk, b_sel, seg)
+        S_ = O.pbs_block_support(x, perm, blk, b_sel, seg, k_blocks=100)
+        assert np.array_equal(S_, np.arange(blk * b_sel))
+        o, _ = O.prefill_block_attend(Q[rows.start:rows.stop], K, V, S_, blk, b_sel, s)
+        np.testing.assert_allclose(o, np.transpose(ref[:, rows.start:rows.stop], (1, 0, 2)),
+                                   rtol=1e-11, atol=1e-12)
+
+
+def test_pbs_permutation_concentrates_scattered_heavy_hitters():
+    """Four heavy-hitter keys scattered over each segment: after the
+    segment permutation one block of each earlier segment holds all of them,
+    and the top block per segment covers more attention mass than the best
+    natural block (the gain the page reports, on a constructed input)."""
+    rng = _rng(84)
+    N, G, d, b_sel, seg = 512, 1, 16, 16, 128
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    K = rng.standard_normal((N, d)) * 0.3
+    Q = rng.standard_normal((N, G, d)) * 0.3 + 2.0 * u
+    hh = [s0 + o for s0 in range(0, N, seg) for o in (5, 37, 70, 101)]
+    K[hh] += 4.0 * u
+    s = 1 / math.sqrt(d)
+    imp = O.pbs_importance(Q[-b_sel:], K, N - b_sel, s)
+    perm = O.pbs_permutation(imp, seg)
+    for s0 in range(0, N - seg, seg):
+        assert set(perm[s0:s0 + 4].tolist()) == {s0 + 5, s0 + 37, s0 + 70, s0 + 101}
+    blk = N // b_sel - 1
+    P = O.head_mean_attention(Q[blk * b_sel], K[:blk * b_sel], s)
+    x = O.pbs_block_scores(Q[blk * b_sel:], K, perm, blk, b_sel, seg)
+    n_perm_blocks = (blk * b_sel // seg) * seg // b_sel
+    best_perm = max(P[O.pbs_block_keys(perm, blk, b_sel, seg, c)].sum() for c in range(n_perm_blocks))
+    best_nat = max(P[c * b_sel:(c + 1) * b_sel].sum() for c in range(n_perm_blocks))
+    assert best_perm > 2 * best_nat
+    top = O.select_topk(x[:n_perm_blocks], 3)
+    assert all(perm[c * b_sel] in hh for c in top)      # the chosen blocks lead with heavy hitters
