@@ -31,6 +31,8 @@ SA_OP_DECODE_STEP = 4
 SA_OP_SPARSE_DECODE_RLA = 5
 SA_OP_ATTENTION_MASS = 6
 SA_OP_PREFILL_QUERY = 7
+SA_OP_PBS_IMPORTANCE = 8
+SA_OP_PBS_SELECT = 9
 
 
 class SaShape(ctypes.Structure):
@@ -85,6 +87,11 @@ SIGNATURES = {
                                                     _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
     "sa_sparse_prefill_query": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _P, _P,
                                                _I32, _F, _P, ctypes.c_int, _P, _P, _SZ, _P]),
+    "sa_pbs_importance": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, ctypes.c_int, _F, _I32, _P, _P,
+                                         _SZ, _P]),
+    "sa_pbs_permutation": (ctypes.c_int, [_SH, _P, _I32, _I32, _P, _P]),
+    "sa_pbs_select": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _P,
+                                     _P, _I32, _P, _SZ, _P]),
     "sa_sparse_prefill": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _P, _P, _I32,
                                          _I32, _F, _P, ctypes.c_int, _P, _P]),
     "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),

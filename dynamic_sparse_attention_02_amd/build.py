@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsa.so")
 ARCH = os.environ.get("SA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.hip", "index.hip", "select.hip", "decode.hip", "prefill.hip", "fused.hip", "mass.hip"]
+SOURCES = ["api.hip", "index.hip", "select.hip", "decode.hip", "prefill.hip", "fused.hip", "mass.hip", "pbs.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}",

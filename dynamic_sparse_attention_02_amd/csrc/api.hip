@@ -173,6 +173,14 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return decode_ws(s, param, true);
     case SA_OP_ATTENTION_MASS:
       return mass_ws(s);
+    case SA_OP_PBS_IMPORTANCE: {
+      sa::Shape sh = to_shape(s);
+      return sa::align_up(sa::pbs_importance_workspace_bytes(sh, s->max_len, param < 1 ? 1 : (int32_t)param), 256);
+    }
+    case SA_OP_PBS_SELECT: {
+      sa::Shape sh = to_shape(s);
+      return sa::align_up(sa::pbs_select_workspace_bytes(sh, s->max_len, param < 1 ? 1 : (int32_t)param), 256);
+    }
     case SA_OP_PREFILL_QUERY: {
       sa::Shape sh = to_shape(s);
       return sa::align_up(sa::prefill_query_workspace_bytes(sh, s->max_len, param < 1 ? 1 : (int32_t)param), 256);
@@ -507,6 +515,66 @@ sa_status sa_sparse_prefill_query(const sa_shape* s, const sa_pages* pg, int32_t
   SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::prefill_query_workspace_bytes(sh, n_tokens, cap), 256), fn));
   return hip_status(sa::launch_sparse_prefill_query(sh, *pg, n_tokens, q, k_pool, v_pool, dt, idx,
                                                     count, cap, s_att, out, out_dt, lse, ws, st), fn);
+}
+
+static sa_status pbs_common(const char* fn, const sa_shape* s, const sa_pages* pg, int32_t n_tokens) {
+  SA_TRY(check_shape(s, fn));
+  if (pg) SA_TRY(check_pages(pg, false, fn));
+  if (s->batch != 1) return fail(SA_ERR_UNSUPPORTED, "%s: prefill takes batch=1", fn);
+  if (n_tokens < 1 || n_tokens > s->max_len)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
+  return SA_OK;
+}
+
+sa_status sa_pbs_importance(const sa_shape* s, const sa_pages* pg, int32_t n_tokens, const void* q,
+                            const void* k_pool, sa_dtype dt, float s_att, int32_t n_rows,
+                            float* importance, void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_pbs_importance";
+  if (!pg) return fail(SA_ERR_INVALID_ARGUMENT, "%s: pages is NULL", fn);
+  SA_TRY(pbs_common(fn, s, pg, n_tokens));
+  if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !k_pool || !importance) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (n_rows < 1 || n_rows > n_tokens)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_rows=%d outside [1, n_tokens=%d]", fn, n_rows, n_tokens);
+  if ((int64_t)n_rows * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: n_rows * n_kv_heads above %d", fn, kMaxDecodeRows);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  const sa::Shape sh = to_shape(s);
+  SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::pbs_importance_workspace_bytes(sh, n_tokens, n_rows), 256), fn));
+  return hip_status(sa::launch_pbs_importance(sh, *pg, n_tokens, q, k_pool, dt, s_att, n_rows,
+                                              importance, ws, st), fn);
+}
+
+sa_status sa_pbs_permutation(const sa_shape* s, const float* importance, int32_t n_tokens,
+                             int32_t seg, int32_t* perm, hipStream_t st) {
+  const char* fn = "sa_pbs_permutation";
+  SA_TRY(pbs_common(fn, s, nullptr, n_tokens));
+  if (!importance || !perm) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (seg < 64 || seg > 4096 || seg % 64 != 0)
+    return fail(SA_ERR_UNSUPPORTED, "%s: seg=%d must be a multiple of 64 in [64, 4096]", fn, seg);
+  return hip_status(sa::launch_pbs_permutation(to_shape(s), importance, n_tokens, seg, perm, st), fn);
+}
+
+sa_status sa_pbs_select(const sa_shape* s, const sa_pages* pg, int32_t n_tokens, const void* q,
+                        const void* k_pool, sa_dtype dt, const int32_t* perm, int32_t seg,
+                        int32_t b_sel, int32_t k_blocks, int32_t* idx, int32_t* count, int32_t cap,
+                        void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_pbs_select";
+  if (!pg) return fail(SA_ERR_INVALID_ARGUMENT, "%s: pages is NULL", fn);
+  SA_TRY(pbs_common(fn, s, pg, n_tokens));
+  if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !k_pool || !perm || !idx || !count) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (b_sel != 64) return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 64", fn, b_sel);
+  if (seg < 64 || seg > 4096 || seg % 64 != 0)
+    return fail(SA_ERR_UNSUPPORTED, "%s: seg=%d must be a multiple of 64 in [64, 4096]", fn, seg);
+  if (k_blocks < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: k_blocks=%d < 1", fn, k_blocks);
+  const int64_t nblk = (n_tokens + 63) / 64;
+  const int64_t kb = k_blocks < nblk - 1 ? k_blocks : (nblk - 1 > 0 ? nblk - 1 : 0);
+  if (cap < 1 || cap < kb * 64) return fail(SA_ERR_CAPACITY, "%s: cap=%d below %lld", fn, cap, (long long)(kb * 64));
+  const sa::Shape sh = to_shape(s);
+  SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::pbs_select_workspace_bytes(sh, n_tokens, k_blocks), 256), fn));
+  return hip_status(sa::launch_pbs_select(sh, *pg, n_tokens, q, k_pool, dt, perm, seg, k_blocks, idx,
+                                          count, cap, ws, st), fn);
 }
 
 sa_status sa_sparse_prefill(const sa_shape* s, const sa_pages* pg, int32_t n_tokens, const void* q,

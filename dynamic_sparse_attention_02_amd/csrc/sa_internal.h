@@ -274,6 +274,18 @@ hipError_t launch_coverage(const Shape& s, const sa_pages& pg, const float* x, i
                            const int32_t* ridx, const int32_t* rcount, int32_t rcap, float* mass,
                            int32_t* overlap, hipStream_t st);
 
+size_t pbs_importance_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t n_rows);
+size_t pbs_select_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t k_blocks);
+hipError_t launch_pbs_importance(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                 const void* q, const void* k_pool, sa_dtype dt, float s_att,
+                                 int32_t n_rows, float* imp, void* ws, hipStream_t st);
+hipError_t launch_pbs_permutation(const Shape& s, const float* imp, int32_t n_tokens, int32_t seg,
+                                  int32_t* perm, hipStream_t st);
+hipError_t launch_pbs_select(const Shape& s, const sa_pages& pg, int32_t n_tokens, const void* q,
+                             const void* k_pool, sa_dtype dt, const int32_t* perm, int32_t seg,
+                             int32_t k_blocks, int32_t* idx, int32_t* count, int32_t cap,
+                             void* ws, hipStream_t st);
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 }  // namespace sa

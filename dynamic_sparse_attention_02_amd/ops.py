@@ -36,6 +36,9 @@ __all__ = [
     "sa_sparse_prefill",
     "sa_select_prefill_topk_probs",
     "sa_sparse_prefill_query",
+    "sa_pbs_importance",
+    "sa_pbs_permutation",
+    "sa_pbs_select",
     "version",
 ]
 
@@ -237,3 +240,27 @@ def sa_sparse_prefill_query(shape, pages, n_tokens, q, k_pool, v_pool, idx, coun
                                           _dev(count), int(idx.shape[-1]), float(s_att), _dev(out),
                                           _dt(out), _dev(lse), wp, wn, _stream(stream))
     L.check(st, "sa_sparse_prefill_query")
+
+
+def sa_pbs_importance(shape, pages, n_tokens, q, k_pool, s_att, n_rows, importance, ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_pbs_importance(ctypes.byref(shape), ctypes.byref(pages), int(n_tokens), _dev(q),
+                                    _dev(k_pool), _dt(q), float(s_att), int(n_rows),
+                                    _dev(importance), wp, wn, _stream(stream))
+    L.check(st, "sa_pbs_importance")
+
+
+def sa_pbs_permutation(shape, importance, n_tokens, seg, perm, stream=None):
+    st = L.load().sa_pbs_permutation(ctypes.byref(shape), _dev(importance), int(n_tokens), int(seg),
+                                     _dev(perm), _stream(stream))
+    L.check(st, "sa_pbs_permutation")
+
+
+def sa_pbs_select(shape, pages, n_tokens, q, k_pool, perm, seg, b_sel, k_blocks, idx, count, ws,
+                  stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_pbs_select(ctypes.byref(shape), ctypes.byref(pages), int(n_tokens), _dev(q),
+                                _dev(k_pool), _dt(q), _dev(perm), int(seg), int(b_sel),
+                                int(k_blocks), _dev(idx), _dev(count), int(idx.shape[-1]), wp, wn,
+                                _stream(stream))
+    L.check(st, "sa_pbs_select")

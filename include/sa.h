@@ -98,7 +98,9 @@ typedef enum {
   SA_OP_DECODE_STEP = 4,     /* param = cap                                      */
   SA_OP_SPARSE_DECODE_RLA = 5, /* param = cap                                    */
   SA_OP_ATTENTION_MASS = 6,    /* param unused                                   */
-  SA_OP_PREFILL_QUERY = 7      /* param = cap                                    */
+  SA_OP_PREFILL_QUERY = 7,     /* param = cap                                    */
+  SA_OP_PBS_IMPORTANCE = 8,    /* param = n_rows                                 */
+  SA_OP_PBS_SELECT = 9         /* param = k_blocks                               */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -359,6 +361,52 @@ sa_status sa_sparse_prefill_query(const sa_shape* shape, const sa_pages* pages,
                                   const int32_t* count, int32_t cap, float s_att, void* out,
                                   sa_dtype out_dtype, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* Segment-permuted block selection ("Sparser Block-Sparse Attention via Token
+ * Permutation", sections 2 to 4), three calls whose lists feed
+ * sa_sparse_prefill.
+ *
+ * Key importance (section 3: estimated from the last query block): with
+ * first = n_tokens - n_rows, for every group g and key j,
+ *   importance[g][j] = mean over rows i < n_rows and heads h in g of
+ *                      softmax_{j' <= first + i}(s_att * q[first + i][h] . k_j')[j]
+ * (zero where j > first + i).  importance [n_kv_heads][n_tokens] fp32;
+ * n_rows * n_kv_heads <= 4096; workspace from SA_OP_PBS_IMPORTANCE
+ * (param = n_rows, sized for n_tokens = max_len; it needs no zero-fill and is
+ * left holding intermediate values, so it is not shared with the zeroed
+ * workspaces of the other calls).  q, k_pool of dtype. */
+sa_status sa_pbs_importance(const sa_shape* shape, const sa_pages* pages, int32_t n_tokens,
+                            const void* q, const void* k_pool, sa_dtype dtype, float s_att,
+                            int32_t n_rows, float* importance, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Segment permutation (sections 2 and 3): inside every segment
+ * [s * seg, (s + 1) * seg) of every group the positions are ordered by
+ * importance, largest first (equal values: lower position first):
+ * perm[g][p] = position of the key placed at p; no key leaves its segment.
+ * seg a multiple of 64 in [64, 4096]; perm [n_kv_heads][n_tokens] int32.
+ * No workspace. */
+sa_status sa_pbs_permutation(const sa_shape* shape, const float* importance, int32_t n_tokens,
+                             int32_t seg, int32_t* perm, hipStream_t stream);
+
+/* Block selection on the permuted keys (section 4: mean pooling): query
+ * block blk (rows [64 blk, 64 blk + 64)) and group g score each earlier key
+ * block c < blk by qbar . kbar_c, qbar = mean of q over the block's rows and
+ * the group's heads, kbar_c = mean of the 64 keys of block c, where block c
+ * of a segment before the query block's own segment is taken in the
+ * permuted order (keys perm[g][64 c .. 64 c + 63]) and a block of the own
+ * segment in natural order; the top k_blocks blocks (ties lower block first)
+ * are expanded to key lists idx[blk * n_kv_heads + g][cap] (block order,
+ * the permuted order inside a block; not sorted), count = 64 * blocks,
+ * cap >= 64 * min(k_blocks, blk); the own block is attended causally by
+ * sa_sparse_prefill on top.  b_sel must be 64; perm as written by
+ * sa_pbs_permutation (or any per-segment permutation); workspace from
+ * SA_OP_PBS_SELECT (param = k_blocks, sized for n_tokens = max_len). */
+sa_status sa_pbs_select(const sa_shape* shape, const sa_pages* pages, int32_t n_tokens,
+                        const void* q, const void* k_pool, sa_dtype dtype, const int32_t* perm,
+                        int32_t seg, int32_t b_sel, int32_t k_blocks, int32_t* idx,
+                        int32_t* count, int32_t cap, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
 
 /* Block-sparse causal prefill attention ("Oracle-Guided Sparse Prefill",
  * section 2.1): row i of block blk, head h of group g attends to the listed

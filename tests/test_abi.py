@@ -149,6 +149,18 @@ def test_validation_codes():
     assert so.sa_sparse_prefill_query(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2049, 0.1, FAKE, L.SA_BF16, None, FAKE, ws_q - 1, None) == L.SA_ERR_WORKSPACE
     assert so.sa_sparse_prefill_query(B(s1), B(pg), 0, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2049, 0.1, FAKE, L.SA_BF16, None, FAKE, ws_q, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_sparse_prefill(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2048, 1, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_UNSUPPORTED
+    # segment permutation: segment length, sizes, capacity
+    assert so.sa_pbs_permutation(B(s1), FAKE, 131072, 100, FAKE, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_pbs_permutation(B(s1), FAKE, 131072, 8192, FAKE, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_pbs_permutation(B(s1), None, 131072, 2048, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
+    ws_pi = so.sa_workspace_size(L.SA_OP_PBS_IMPORTANCE, B(s1), 64)
+    assert so.sa_pbs_importance(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 0, FAKE, FAKE, ws_pi, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert so.sa_pbs_importance(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 64, FAKE, FAKE, ws_pi - 1, None) == L.SA_ERR_WORKSPACE
+    assert so.sa_pbs_importance(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 1000, FAKE, FAKE, 1 << 40, None) == L.SA_ERR_UNSUPPORTED
+    ws_ps = so.sa_workspace_size(L.SA_OP_PBS_SELECT, B(s1), 32)
+    assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 64, 32, FAKE, FAKE, 2047, FAKE, ws_ps, None) == L.SA_ERR_CAPACITY
+    assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 32, 32, FAKE, FAKE, 2048, FAKE, ws_ps, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 64, 32, FAKE, FAKE, 2048, FAKE, ws_ps - 1, None) == L.SA_ERR_WORKSPACE
     # maintenance calls
     assert so.sa_index_append(B(s), None, FAKE, L.SA_BF16, FAKE, 5, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_index_append(B(s), FAKE, FAKE, L.SA_BF16, FAKE, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT

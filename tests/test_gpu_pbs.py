@@ -1,0 +1,166 @@
+"""GPU parity of the segment-permuted block selection ("Sparser Block-Sparse
+Attention via Token Permutation", sections 2 to 4) against the float64
+oracle: last-block key importance, the per-segment permutation (bit-exact on
+the oracle's importance), block selection on the oracle's permutation, and
+the prefill attention over the resulting lists."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests import _support as S
+from tests.test_gpu_prefill import prefill_shape
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+B_SEL = 64
+
+
+def ops():
+    from dynamic_sparse_attention_02_amd import ops as _ops
+    return _ops
+
+
+def _lib():
+    from dynamic_sparse_attention_02_amd import _lib as L
+    return L
+
+
+def _inputs(N, H_q=8, H_kv=2, d=128, dtype=torch.bfloat16, seed=0, n_hh=16):
+    return synth.make_prefill_custom(N=N, H_q=H_q, H_kv=H_kv, d=d, dtype=dtype, device="cuda",
+                                     seed=seed, n_hh=n_hh)
+
+
+def gpu_importance(inp, n_rows=B_SEL):
+    o = ops()
+    shape = prefill_shape(inp)
+    pages = o.make_pages(inp.page_table, None)
+    imp = torch.full((inp.H_kv, inp.N), float("nan"), dtype=torch.float32, device="cuda")
+    ws = o.alloc_workspace(o.workspace_size(_lib().SA_OP_PBS_IMPORTANCE, shape, n_rows))
+    o.sa_pbs_importance(shape, pages, inp.N, inp.q, inp.k_pool, inp.s_att, n_rows, imp, ws)
+    torch.cuda.synchronize()
+    return imp
+
+
+def oracle_importance(inp, g, n_rows=B_SEL):
+    hs = inp.heads(g)
+    first = inp.N - n_rows
+    return O.pbs_importance(S.to_np(inp.q[first:][:, hs]), S.to_np(inp.keys(g)), first, inp.s_att)
+
+
+def gpu_permutation(inp, imp, seg):
+    o = ops()
+    perm = torch.full((inp.H_kv, inp.N), -7, dtype=torch.int32, device="cuda")
+    o.sa_pbs_permutation(prefill_shape(inp), imp, inp.N, seg, perm)
+    torch.cuda.synchronize()
+    return perm
+
+
+def gpu_select_attend(inp, perm, seg, k_blocks, out_dtype=torch.bfloat16, attend=True):
+    o = ops()
+    shape = prefill_shape(inp)
+    pages = o.make_pages(inp.page_table, None)
+    nblk = inp.n_blocks
+    cap = max(64, 64 * min(k_blocks, max(nblk - 1, 1)))
+    idx = torch.full((nblk * inp.H_kv, cap), -7, dtype=torch.int32, device="cuda")
+    count = torch.full((nblk * inp.H_kv,), -7, dtype=torch.int32, device="cuda")
+    ws = o.alloc_workspace(o.workspace_size(_lib().SA_OP_PBS_SELECT, shape, k_blocks))
+    o.sa_pbs_select(shape, pages, inp.N, inp.q, inp.k_pool, perm, seg, B_SEL, k_blocks, idx, count, ws)
+    if not attend:  # the block-sparse attention takes bf16 inputs only
+        torch.cuda.synchronize()
+        return idx, count, None, None
+    out = torch.full((inp.N, inp.H_q, inp.d), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((inp.N, inp.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    o.sa_sparse_prefill(shape, pages, inp.N, inp.q, inp.k_pool, inp.v_pool, idx, count, B_SEL,
+                        inp.s_att, out, lse)
+    torch.cuda.synchronize()
+    return idx, count, out, lse
+
+
+@pytest.mark.parametrize("N,dtype,H_q,H_kv", [(1000, torch.bfloat16, 8, 2), (700, torch.float32, 4, 1),
+                                             (1500, torch.bfloat16, 16, 2)])
+def test_pbs_importance_matches_oracle(N, dtype, H_q, H_kv):
+    inp = _inputs(N, H_q=H_q, H_kv=H_kv, dtype=dtype, seed=N)
+    imp = gpu_importance(inp).cpu().numpy().astype(np.float64)
+    for g in range(inp.H_kv):
+        ref = oracle_importance(inp, g)
+        err = np.abs(imp[g] - ref)
+        assert np.all(err <= 1e-4 * ref + 1e-9 * ref.max()), (g, float((err / (ref + 1e-30)).max()))
+        assert abs(imp[g].sum() - 1.0) < 1e-4
+
+
+def test_pbs_permutation_bit_exact_on_oracle_importance():
+    """The oracle's importance (rounded to fp32, with planted exact ties) is
+    permuted identically by both sides, including the partial last segment."""
+    inp = _inputs(1000, seed=3)
+    rng = np.random.default_rng(5)
+    imp = np.stack([oracle_importance(inp, g) for g in range(inp.H_kv)]).astype(np.float32)
+    imp[0, 130:140] = imp[0, 130]          # ties broken by position
+    imp[1, 900:1000] = 0.0
+    imp[1, rng.choice(1000, 50, replace=False)] = np.float32(1e-3)
+    for seg in (64, 256, 4096):
+        perm = gpu_permutation(inp, torch.from_numpy(imp).cuda(), seg).cpu().numpy()
+        for g in range(inp.H_kv):
+            ref = O.pbs_permutation(imp[g].astype(np.float64), seg)
+            assert np.array_equal(perm[g], ref), (seg, g)
+
+
+@pytest.mark.parametrize("N,seg,k_blocks,dtype", [(1000, 256, 4, torch.bfloat16),
+                                                  (1600, 512, 6, torch.bfloat16),
+                                                  (700, 128, 3, torch.float32)])
+def test_pbs_select_and_attention_match_oracle(N, seg, k_blocks, dtype):
+    """Block selection on the oracle's permutation (support equal up to
+    block-score ties) and the attention over the GPU's lists."""
+    inp = _inputs(N, dtype=dtype, seed=N + seg)
+    perm_o = np.stack([O.pbs_permutation(oracle_importance(inp, g), seg) for g in range(inp.H_kv)])
+    perm = torch.from_numpy(perm_o.astype(np.int32)).cuda()
+    attend = dtype == torch.bfloat16
+    idx, count, out, lse = gpu_select_attend(inp, perm, seg, k_blocks, attend=attend)
+    tol = S.TOL[dtype]
+    for g in range(inp.H_kv):
+        hs = inp.heads(g)
+        K = S.to_np(inp.keys(g))
+        V = S.to_np(inp.values(g))
+        for blk in range(inp.n_blocks):
+            rows = O.prefill_block_rows(blk, B_SEL, N)
+            Qb = S.to_np(inp.q[rows.start:rows.stop][:, hs])
+            x = O.pbs_block_scores(Qb, K, perm_o[g], blk, B_SEL, seg)
+            gl = np.sort(S.gpu_support(idx, count, blk * inp.H_kv + g))
+            if blk == 0:
+                assert len(gl) == 0
+            else:
+                assert len(gl) % 64 == 0
+                gblocks = sorted({c for c in range(blk)
+                                  if set(O.pbs_block_keys(perm_o[g], blk, B_SEL, seg, c)) <= set(gl.tolist())})
+                assert len(gblocks) * 64 == len(gl), "list is not a union of candidate blocks"
+                core = O.select_topk(x, k_blocks)
+                S.check_support(np.array(gblocks), x, core, L=blk, k=k_blocks)
+            if attend:
+                o_ref, l_ref = O.prefill_block_attend(Qb, K, V, gl, blk, B_SEL, inp.s_att)
+                go = S.to_np(out[rows.start:rows.stop][:, hs])
+                assert S.max_abs(go, o_ref) <= tol, (g, blk, S.max_abs(go, o_ref))
+
+
+def test_pbs_pipeline_all_blocks_is_dense_causal():
+    """GPU importance -> GPU permutation -> selection with every block kept:
+    dense causal attention (torch SDPA in float64 on the CPU); the GPU
+    permutation sorts each segment by the GPU importance."""
+    inp = _inputs(640, H_q=4, H_kv=1, dtype=torch.bfloat16, seed=11, n_hh=8)
+    imp = gpu_importance(inp)
+    perm = gpu_permutation(inp, imp, 128)
+    p, im = perm.cpu().numpy()[0], imp.cpu().numpy()[0]
+    for s0 in range(0, 640, 128):
+        seg = p[s0:s0 + 128]
+        assert sorted(seg.tolist()) == list(range(s0, min(640, s0 + 128)))
+        assert np.all(np.diff(im[seg]) <= 0)
+    idx, count, out, lse = gpu_select_attend(inp, perm, 128, 100, out_dtype=torch.float32)
+    assert np.array_equal(count.cpu().numpy(), 64 * np.arange(10))
+    q = inp.q.double().cpu().permute(1, 0, 2)[None]
+    K = inp.keys(0).double().cpu()[None, None]
+    V = inp.values(0).double().cpu()[None, None]
+    ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=inp.s_att,
+                                                           is_causal=True)[0].permute(1, 0, 2)
+    assert S.max_abs(out.double().cpu().numpy(), ref.numpy()) <= S.TOL[torch.bfloat16]
