@@ -53,6 +53,13 @@ def parse():
                     help="token-level decode workloads: take the support from the low-rank "
                          "indexer (default) or from the dense head-averaged attention mass "
                          "(the attention-mass oracle: sa_attention_mass + sa_select_topp)")
+    ap.add_argument("--selection", default="indexer", choices=["indexer", "pbs"],
+                    help="prefill128k: block supports from the low-rank indexer (default) or from "
+                         "the segment-permuted mean-pooled blocks (sa_pbs_*; segments of 2048, "
+                         "importance from the last 64 queries, top-32 blocks)")
+    ap.add_argument("--coverage", action="store_true",
+                    help="prefill128k: also report the dense attention mass the supports keep on "
+                         "8 sampled (query block, group) items (float64 on the host, untimed)")
     ap.add_argument("--aggregate", default="logits", choices=["logits", "probs"],
                     help="prefill32k_query: rank by the head-collapsed logits or by the mean of "
                          "the heads' probabilities (sa_select_prefill_topk_probs)")
@@ -117,6 +124,7 @@ KERNEL_SOURCES = {
     "sparse_prefill": ["prefill.hip"],
     "attention_mass": ["mass.hip"],
     "sparse_prefill_query": ["decode.hip", "prefill.hip"],
+    "pbs_select": ["pbs.hip", "mass.hip", "select.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -491,6 +499,8 @@ def bench_prefill(args):
     inp = synth.make_prefill128k(device="cuda")
     N, Hq, Hkv, d = inp.N, inp.H_q, inp.H_kv, inp.d
     G = Hq // Hkv
+    pbs = args.selection == "pbs"
+    seg, k_blocks = 2048, inp.top_k // 64
     shape = ops.make_shape(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
                            max_pages=inp.page_table.shape[1], max_len=N,
                            n_pool_pages=inp.k_pool.shape[0])
@@ -504,9 +514,21 @@ def bench_prefill(args):
     count = torch.empty((nblk * Hkv,), dtype=torch.int32, device="cuda")
     out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
-    ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_SELECT, shape, N))
+    if pbs:
+        imp = torch.empty((Hkv, N), dtype=torch.float32, device="cuda")
+        perm = torch.empty((Hkv, N), dtype=torch.int32, device="cuda")
+        ws_imp = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PBS_IMPORTANCE, shape, 64))
+        ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PBS_SELECT, shape, k_blocks))
+    else:
+        ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_SELECT, shape, N))
 
     def select():
+        if pbs:
+            ops.sa_pbs_importance(shape, pages, N, inp.q, inp.k_pool, inp.s_att, 64, imp, ws_imp)
+            ops.sa_pbs_permutation(shape, imp, N, seg, perm)
+            ops.sa_pbs_select(shape, pages, N, inp.q, inp.k_pool, perm, seg, 64, k_blocks, idx,
+                              count, ws)
+            return
         ops.sa_select_prefill_topk(shape, pages, N, inp.q, inp.w_q, kidx, inp.s_idx, 64, k, idx,
                                    count, ws)
 
@@ -534,8 +556,10 @@ def bench_prefill(args):
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": steps, "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "prefill128k", "tokens": N, "q_heads": Hq, "kv_heads": Hkv,
-                   "head_dim": d, "b_sel": 64, "top_k": k},
+        "config": {"workload": "prefill128k" + ("+pbs" if pbs else ""), "tokens": N,
+                   "q_heads": Hq, "kv_heads": Hkv, "head_dim": d, "b_sel": 64, "top_k": k,
+                   "selection": ("segment-permuted mean-pooled blocks (segment %d, top-%d blocks)"
+                                 % (seg, k_blocks)) if pbs else "low-rank indexer, top-k keys"},
         "algorithmic_flops": flops,
         "breakdown_ms": {"select": round(t_sel, 4), "attention": round(t_att, 4)},
         "attention_tflops": round(att_tflops, 2),
@@ -545,7 +569,11 @@ def bench_prefill(args):
                      "traffic": recorded_traffic("prefill128k", "sparse_prefill"),
                      "flops_per_launch": flops, "avg_launch_ms": round(t_att, 4)},
     }
-    if not args.no_cpu_baseline:
+    if pbs:
+        res["breakdown_ms"]["pbs_select_parts"] = "importance + permutation + block selection"
+    if args.coverage:
+        res["coverage"] = prefill_coverage(inp, idx, count)
+    if not args.no_cpu_baseline and not pbs:
         res["cpu_baseline"] = cpu_baseline_prefill(inp, kidx, args.cpu_seconds)
     return res
 
@@ -659,6 +687,32 @@ def cpu_baseline_prefill_query(inp, kidx, seconds, probs):
             "sample": f"{n_rows} (query, group) rows of the last queries (scores + support + "
                       f"attention), float64 numpy, {el:.1f} s",
             "host_threads_available": cpu_threads_info()}
+
+
+def prefill_coverage(inp, idx, count):
+    """Dense attention mass (head mean of each query row's causal softmax)
+    that the block supports plus the causal diagonal keep, on sampled
+    (query block, group) items; float64 on the host, outside the timed
+    region."""
+    import numpy as np
+
+    import oracle as O
+
+    nblk = inp.n_blocks
+    kept = []
+    for g in (0, inp.H_kv - 1):
+        hs = inp.heads(g)
+        K = inp.keys(g).double().cpu().numpy()
+        for blk in (nblk // 4, nblk // 2, 3 * nblk // 4, nblk - 1):
+            n = int(count[blk * inp.H_kv + g])
+            sup = idx[blk * inp.H_kv + g, :n].cpu().numpy().astype(np.int64)
+            for i in range(blk * 64, min(inp.N, blk * 64 + 64), 8):
+                P = O.head_mean_attention(inp.q[i, hs].double().cpu().numpy(), K[:i + 1], inp.s_att)
+                kept.append(P[sup].sum() + P[blk * 64:i + 1].sum())
+    kept = np.array(kept)
+    return {"dense_mass_kept_mean": round(float(kept.mean()), 4),
+            "dense_mass_kept_min": round(float(kept.min()), 4),
+            "sample": "8 query rows of each of 4 query blocks x 2 groups"}
 
 
 def time_events(fn, n):
