@@ -58,6 +58,7 @@ struct MassWs {
   float* norm;      // [rows][G] log2 of each head's softmax normaliser
   int64_t ldl;
   int32_t nchunk;
+  int32_t rows_fast;  // grid x = rows (rows sharing a key cache read a chunk together)
 };
 
 template <typename T, int D, int G>
@@ -69,7 +70,7 @@ k_mass_logits(const T* __restrict__ q, const T* __restrict__ k_pool,
   constexpr int QP = G * D * (int)sizeof(T) / 16;        // 16-byte pieces of the group's queries
   constexpr int QPT = (QP + C::NT - 1) / C::NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int row = blockIdx.y, ch = blockIdx.x;
+  const int row = w.rows_fast ? blockIdx.x : blockIdx.y, ch = w.rows_fast ? blockIdx.y : blockIdx.x;
   const int b = row / s.Hkv, g = row % s.Hkv;
   const int32_t L = clamp_len(seq_lens[b], s.max_len);
   const int32_t t0 = ch * kMassChunk;
@@ -226,7 +227,7 @@ template <int G>
 __global__ void __launch_bounds__(256)
 k_mass_finish(const int32_t* __restrict__ seq_lens, Shape s, MassWs w, float* __restrict__ x,
               int64_t ldx) {
-  const int row = blockIdx.y, ch = blockIdx.x;
+  const int row = w.rows_fast ? blockIdx.x : blockIdx.y, ch = w.rows_fast ? blockIdx.y : blockIdx.x;
   const int b = row / s.Hkv;
   const int32_t L = clamp_len(seq_lens[b], s.max_len);
   const int32_t t0 = ch * kMassChunk;
@@ -327,7 +328,7 @@ template <typename T, int D>
 hipError_t launch_mass_t(const Shape& s, const sa_pages& pg, const void* q, const void* k_pool,
                          float s_att, float* x, int64_t ldx, const MassWs& w, hipStream_t st) {
   const int G = s.Hq / s.Hkv;
-  const dim3 grid(w.nchunk, s.B * s.Hkv);
+  const dim3 grid = w.rows_fast ? dim3(s.B * s.Hkv, w.nchunk) : dim3(w.nchunk, s.B * s.Hkv);
   const float c2 = s_att * kLog2e;
 #define SA_MASS_G(GG)                                                                          \
   case GG:                                                                                     \
@@ -354,7 +355,7 @@ size_t mass_workspace_bytes(const Shape& s) { return mass_layout(s).total; }
 
 hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q, const void* k_pool,
                                  sa_dtype dt, float s_att, float* x, int64_t ldx, void* ws,
-                                 hipStream_t st) {
+                                 hipStream_t st, bool rows_fast) {
   const MassLayout m = mass_layout(s);
   char* base = (char*)ws;
   MassWs w;
@@ -363,6 +364,7 @@ hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void*
   w.norm = (float*)(base + m.off_norm);
   w.ldl = m.ldl;
   w.nchunk = m.nchunk;
+  w.rows_fast = rows_fast && m.nchunk <= 65535 ? 1 : 0;
   if (dt == SA_BF16)
     return s.D == 128 ? launch_mass_t<bf16_raw, 128>(s, pg, q, k_pool, s_att, x, ldx, w, st)
                       : launch_mass_t<bf16_raw, 64>(s, pg, q, k_pool, s_att, x, ldx, w, st);

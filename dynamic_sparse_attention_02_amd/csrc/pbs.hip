@@ -87,20 +87,61 @@ k_pbs_sort(const float* __restrict__ imp, int32_t N, int32_t seg, int32_t* __res
 }
 
 // qbar[blk][g][d] = mean over the block's rows i and the group's heads h of
-// q[i][h][d] (rows outer, heads inner, fp32).  One workgroup per (block, group),
-// thread = dim.
+// q[i][h][d] (fp32).  One workgroup per (block, group): thread t sums 8 dims
+// (chunk t % (D / 8)) over the (row, head) pairs t / (D / 8), + 256 / (D / 8),
+// ... with 16-byte loads issued together; the shares meet in LDS.
 template <typename T>
-__global__ void __launch_bounds__(128)
+__global__ void __launch_bounds__(256)
 k_pbs_qbar(const T* __restrict__ q, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
            float* __restrict__ qbar) {
-  const int blk = blockIdx.x, g = blockIdx.y, d = threadIdx.x;
-  if (d >= D) return;
+  const int blk = blockIdx.x, g = blockIdx.y, t = threadIdx.x;
   const int G = Hq / Hkv;
   const int32_t r0 = blk * kBlk, nr = min(kBlk, N - r0);
-  float acc = 0.f;
-  for (int i = 0; i < nr; ++i)
-    for (int hh = 0; hh < G; ++hh) acc += to_f32<T>(q[((int64_t)(r0 + i) * Hq + g * G + hh) * D + d]);
-  qbar[((int64_t)blk * Hkv + g) * D + d] = acc / (float)(nr * G);
+  const int nch = D / 8;             // 8-dim chunks: 8 or 16
+  const int sh = 256 / nch;          // shares
+  const int c = t % nch, share = t / nch;
+  const int pairs = nr * G;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int p0 = share; p0 < pairs; p0 += 4 * sh) {
+    float v[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + u * sh;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[u][e] = 0.f;
+      if (p < pairs) {
+        const T* src = q + ((int64_t)(r0 + p / G) * Hq + g * G + p % G) * D + c * 8;
+        if constexpr (sizeof(T) == 2) {
+          const uint4 w = *reinterpret_cast<const uint4*>(src);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[u][2 * e] = __uint_as_float(ww[e] << 16);
+            v[u][2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[u][e] = src[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += v[u][e];
+  }
+  __shared__ float part[256][9];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[t][e] = acc[e];
+  __syncthreads();
+  if (t < D) {
+    const int cc = t / 8, e = t % 8;
+    float s = 0.f;
+    for (int j = 0; j < sh; ++j) s += part[j * nch + cc][e];
+    qbar[((int64_t)blk * Hkv + g) * D + t] = s / (float)pairs;
+  }
 }
 
 // kbar[0][g][c][d]: mean of the keys of natural block c; kbar[1][g][c][d]:
@@ -125,32 +166,65 @@ k_pbs_kbar(const T* __restrict__ k_pool, const int32_t* __restrict__ pt, Shape s
 }
 
 // x[(blk, g)][c] = qbar[blk][g] . kbar[c < own segment's first block ? 1 : 0][g][c]
-// for c < blk.  A workgroup covers 256 candidate blocks and kRowsB query
-// blocks of one group.
-constexpr int kRowsB = 16;
+// for c < blk: a 64 x 64 tile of (query block, candidate block) per
+// workgroup, both key variants accumulated side by side (fp32, dims in
+// order), 4 x 4 outputs per thread, 16-dim steps staged in LDS.
 __global__ void __launch_bounds__(256)
 k_pbs_scores(const float* __restrict__ qbar, const float* __restrict__ kbar, int32_t nblk,
              int32_t nkb, int32_t Hkv, int32_t D, int32_t seg_blocks, float* __restrict__ x,
              int64_t ldx) {
   const int g = blockIdx.z;
-  const int b_lo = blockIdx.y * kRowsB;
-  const int b_hi = min(nblk, b_lo + kRowsB);
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (blockIdx.x * 256 >= b_hi - 1) return;  // past every row's candidates
-  __shared__ float qs[kRowsB][128];
-  for (int e = threadIdx.x; e < kRowsB * D; e += 256) {
-    const int r = e / D, d = e % D;
-    qs[r][d] = b_lo + r < b_hi ? qbar[((int64_t)(b_lo + r) * Hkv + g) * D + d] : 0.f;
+  const int b0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+  if (c0 >= min(nblk, b0 + 64) - 1 || c0 >= nkb) return;  // no candidate of any row in the tile
+  const int t = threadIdx.x, tr = t / 16, tc = t % 16;
+  __shared__ float qs[16][65];
+  __shared__ float kp[16][65];
+  __shared__ float kn[16][65];
+  float ap[4][4], an[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ap[i][j] = an[i][j] = 0.f;
+  const float* kb_nat = kbar + (int64_t)g * nkb * D;
+  const float* kb_perm = kbar + ((int64_t)Hkv + g) * nkb * D;
+  for (int d0 = 0; d0 < D; d0 += 16) {
+    __syncthreads();
+    for (int e = t; e < 64 * 16; e += 256) {
+      const int r = e / 16, dd = e % 16;
+      const int blk = b0 + r, c = c0 + r;
+      qs[dd][r] = blk < nblk ? qbar[((int64_t)blk * Hkv + g) * D + d0 + dd] : 0.f;
+      kn[dd][r] = c < nkb ? kb_nat[(int64_t)c * D + d0 + dd] : 0.f;
+      kp[dd][r] = c < nkb ? kb_perm[(int64_t)c * D + d0 + dd] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dd = 0; dd < 16; ++dd) {
+      float a[4], bp[4], bn[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        a[i] = qs[dd][tr * 4 + i];
+        bp[i] = kp[dd][tc * 4 + i];
+        bn[i] = kn[dd][tc * 4 + i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          ap[i][j] = fmaf(a[i], bp[j], ap[i][j]);
+          an[i][j] = fmaf(a[i], bn[j], an[i][j]);
+        }
+    }
   }
-  __syncthreads();
-  if (c >= b_hi - 1 || c >= nkb) return;
-  for (int blk = b_lo; blk < b_hi; ++blk) {
-    if (c >= blk) continue;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int blk = b0 + tr * 4 + i;
+    if (blk >= nblk) continue;
     const int own_first = (blk / seg_blocks) * seg_blocks;
-    const float* kv = kbar + (((int64_t)(c < own_first ? 1 : 0) * Hkv + g) * nkb + c) * D;
-    float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(qs[blk - b_lo][d], kv[d], acc);
-    x[((int64_t)blk * Hkv + g) * ldx + c] = acc;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c = c0 + tc * 4 + j;
+      if (c < blk && c < nkb) x[((int64_t)blk * Hkv + g) * ldx + c] = c < own_first ? ap[i][j] : an[i][j];
+    }
   }
 }
 
@@ -259,7 +333,8 @@ hipError_t launch_pbs_importance(const Shape& s, const sa_pages& pg, int32_t n_t
   p2.seq_lens = lens;
   const size_t qe = dt == SA_BF16 ? 2 : 4;
   hipError_t e = launch_attention_mass(s2, p2, (const char*)q + (size_t)first * s.Hq * s.D * qe,
-                                       k_pool, dt, s_att, x, L.ldx, base + L.off_mass, st);
+                                       k_pool, dt, s_att, x, L.ldx, base + L.off_mass, st,
+                                       /*rows_fast=*/true);
   if (e != hipSuccess) return e;
   dim3 grid((n_tokens + 255) / 256, s.Hkv);
   k_pbs_importance<<<grid, 256, 0, st>>>(x, L.ldx, n_rows, first, s.Hkv, n_tokens, imp);
@@ -287,15 +362,15 @@ hipError_t launch_pbs_select(const Shape& s, const sa_pages& pg, int32_t n_token
   const int64_t ldx = L.nblk > 1 ? L.nblk : 1;
   const int seg_blocks = seg / kBlk;
   dim3 gq(L.nblk, s.Hkv);
-  if (dt == SA_BF16) k_pbs_qbar<bf16_raw><<<gq, 128, 0, st>>>((const bf16_raw*)q, n_tokens, s.Hq, s.Hkv, s.D, qbar);
-  else k_pbs_qbar<float><<<gq, 128, 0, st>>>((const float*)q, n_tokens, s.Hq, s.Hkv, s.D, qbar);
+  if (dt == SA_BF16) k_pbs_qbar<bf16_raw><<<gq, 256, 0, st>>>((const bf16_raw*)q, n_tokens, s.Hq, s.Hkv, s.D, qbar);
+  else k_pbs_qbar<float><<<gq, 256, 0, st>>>((const float*)q, n_tokens, s.Hq, s.Hkv, s.D, qbar);
   if (L.nkb > 0) {
     dim3 gk(L.nkb, s.Hkv, 2);
     if (dt == SA_BF16)
       k_pbs_kbar<bf16_raw><<<gk, 128, 0, st>>>((const bf16_raw*)k_pool, pg.page_table, s, n_tokens, perm, kbar);
     else
       k_pbs_kbar<float><<<gk, 128, 0, st>>>((const float*)k_pool, pg.page_table, s, n_tokens, perm, kbar);
-    dim3 gs((unsigned)((ldx + 255) / 256), (L.nblk + kRowsB - 1) / kRowsB, s.Hkv);
+    dim3 gs((unsigned)((L.nkb + 63) / 64), (L.nblk + 63) / 64, s.Hkv);
     k_pbs_scores<<<gs, 256, 0, st>>>(qbar, kbar, L.nblk, L.nkb, s.Hkv, s.D, seg_blocks, x, ldx);
   }
   SelectArgs a{};

@@ -268,7 +268,7 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
 size_t mass_workspace_bytes(const Shape& s);
 hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q,
                                  const void* k_pool, sa_dtype dt, float s_att, float* x,
-                                 int64_t ldx, void* ws, hipStream_t st);
+                                 int64_t ldx, void* ws, hipStream_t st, bool rows_fast = false);
 hipError_t launch_coverage(const Shape& s, const sa_pages& pg, const float* x, int64_t ldx,
                            const int32_t* idx, const int32_t* count, int32_t cap,
                            const int32_t* ridx, const int32_t* rcount, int32_t rcap, float* mass,
