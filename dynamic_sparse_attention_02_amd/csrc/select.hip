@@ -494,7 +494,8 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
 // position inside its slice is the popcount of the ballot below it.  Selected
 // pages are staged in LDS and expanded to tokens by the whole block.
 // ---------------------------------------------------------------------------
-constexpr int kRowRegs = 32;
+constexpr int kRowRegsTopp = 32;
+constexpr int kRowRegsTopk = 48;
 // rounds after the register-resident ones kept in LDS (top-k has no mass
 // histogram, so more LDS is free for keys)
 constexpr int kCacheRoundsTopk = 24;
@@ -509,8 +510,11 @@ struct RowRes {
   uint64_t rem;
 };
 
-template <bool TOPP>
+// RR: register-resident rounds (more only pays for rows that would otherwise
+// re-read scores: top-k with more than (32 + LDS rounds) * kThreads candidates).
+template <bool TOPP, int RR>
 __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
+  constexpr int kRowRegs = RR;
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t n = n_cand_of(a, row);
@@ -883,9 +887,11 @@ hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   // One block per row when a row's keys fit in one block's registers, or
   // when there are enough rows to fill the chip; few long rows are split
   // over many blocks instead.
-  if (a.max_cand <= kRowRegs * kThreads || (a.max_cand <= kRowMax && a.rows >= 32)) {
-    if (a.is_topk) k_select_row<false><<<a.rows, kThreads, 0, st>>>(a);
-    else k_select_row<true><<<a.rows, kThreads, 0, st>>>(a);
+  if (a.max_cand <= kRowRegsTopp * kThreads || (a.max_cand <= kRowMax && a.rows >= 32)) {
+    if (!a.is_topk) k_select_row<true, kRowRegsTopp><<<a.rows, kThreads, 0, st>>>(a);
+    else if (a.max_cand > (kRowRegsTopp + kCacheRoundsTopk) * kThreads)
+      k_select_row<false, kRowRegsTopk><<<a.rows, kThreads, 0, st>>>(a);
+    else k_select_row<false, kRowRegsTopp><<<a.rows, kThreads, 0, st>>>(a);
     return hipGetLastError();
   }
   const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
