@@ -38,7 +38,8 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 // number of listed tiles and the (persistent) grid size, so that the chunks
 // spread evenly over the blocks.  Items (row, chunk) are numbered row by row
 // and block b takes items b, b + grid, ...
-constexpr int kMaxRowsLds = 4096;  // rows whose chunk prefix fits in LDS
+constexpr int kMaxRowsLds = 4096;    // rows whose chunk prefix fits in LDS
+constexpr int kSmallRowsLds = 256;   // a smaller prefix leaves LDS for a fourth workgroup per CU
 
 __device__ __forceinline__ int32_t row_count(const int32_t* count, int row, int32_t cap) {
   int32_t n = count[row];
@@ -69,7 +70,7 @@ struct DecodeCfg {
 // from the K/V rows already staged for the exact attention.
 constexpr int kPhiPitch = 4;  // extra floats per phi(K) row in LDS (bank spread)
 
-template <typename T, int D, int G, bool RLA>
+template <typename T, int D, int G, bool RLA, int RMAX>
 __global__ void __launch_bounds__((G < 4 ? G : 4) * 64)
 k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* __restrict__ v_pool,
                const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
@@ -88,7 +89,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   __shared__ __align__(16) float PhiK[RLA ? kTile : 1][RLA ? D + kPhiPitch : 1];
   __shared__ __align__(16) float PhiQ[RLA ? G : 1][RLA ? D : 1];
   __shared__ __align__(16) float Ws[RLA ? G : 1][RLA ? kTile : 1];
-  __shared__ int32_t prefix[kMaxRowsLds + 1];
+  __shared__ int32_t prefix[RMAX + 1];
   __shared__ int64_t s_tiles;
   __shared__ int32_t s_red[4];
 
@@ -101,7 +102,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   __syncthreads();
   const int32_t tpc = plan_tpc(s_tiles, gridDim.x);
   const int32_t csize = kTile * tpc;
-  // prefix[r] = items before row r (sequential scan by wave 0, rows <= kMaxRowsLds)
+  // prefix[r] = items before row r (sequential scan by wave 0, rows <= RMAX)
   if (wave == 0) {
     int32_t carry = 0;
     for (int r0 = 0; r0 < rows; r0 += 64) {
@@ -553,14 +554,14 @@ k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
 }
 
 // Persistent grid of the split kernel: blocks resident on the chip.
-int split_grid(int nchunk_max, int rows) {
+int split_grid(int nchunk_max, int rows, int per_cu) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus <= 0)
     cus = 256;
   const long long most = (long long)nchunk_max * rows;
-  const long long g = 3LL * cus;
+  const long long g = (long long)per_cu * cus;
   return (int)(most < g ? (most < 1 ? 1 : most) : g);
 }
 
@@ -581,13 +582,21 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
   float* part_o = part_ml + align_up(n_part * 2, 64);
   float* part_rnum = part_o + align_up(n_part * D, 64);
   float* part_rden = part_rnum + align_up(n_part * D, 64);
-  const int gx = split_grid(nchunk_max, s.B * s.Hkv);
-  dim3 grid(gx);
   const int G = s.Hq / s.Hkv;
-#define SA_DS(GG)                                                                          \
-  k_decode_split<T, D, GG, RLA><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(                  \
-      (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,     \
-      count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden)
+  // few rows: the small row prefix frees LDS for four workgroups per CU
+  // (where registers allow: up to four heads per group without the tail)
+  const bool small = s.B * s.Hkv <= kSmallRowsLds;
+  const int gx = split_grid(nchunk_max, s.B * s.Hkv, small && G <= 4 && !RLA ? 4 : 3);
+  dim3 grid(gx);
+#define SA_DS(GG)                                                                              \
+  if (small)                                                                                   \
+    k_decode_split<T, D, GG, RLA, kSmallRowsLds><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(     \
+        (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,      \
+        count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden);              \
+  else                                                                                         \
+    k_decode_split<T, D, GG, RLA, kMaxRowsLds><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(       \
+        (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,      \
+        count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden)
   switch (G) {
     case 1: SA_DS(1); break;
     case 2: SA_DS(2); break;
