@@ -566,7 +566,8 @@ def bench_prefill(args):
         "roofline": {"kernel": "sparse_prefill", "bound": "mfma", "achieved": round(att_tflops, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(att_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": recorded_traffic("prefill128k", "sparse_prefill"),
+                     "traffic": recorded_traffic("prefill128k" + ("+pbs" if pbs else ""),
+                                                 "sparse_prefill"),
                      "flops_per_launch": flops, "avg_launch_ms": round(t_att, 4)},
     }
     if pbs:
