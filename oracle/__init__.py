@@ -47,6 +47,12 @@ Parity status of each function (what pins it, from the tests in
                          ranking; the probability mean is a distribution and
                          its top-k holds the largest mass (brute force); the
                          own token is always kept.
+* ``prefill_oracle_*``   pinned: the block support is the top-k of the mean
+                         of the block rows' causal torch SDPA weights over
+                         earlier keys; the per-query support holds the
+                         largest mass of all k-subsets (brute force) and the
+                         own token; k covering every candidate gives dense
+                         causal attention.
 * ``pbs_*``              pinned: importance is a distribution and equals the
                          head/query mean of causal torch SDPA weights; the
                          permutation maps every segment onto itself, sorts by

@@ -64,6 +64,8 @@ __all__ = [
     "prefill_query_scores",
     "prefill_query_support",
     "prefill_query_attend",
+    "prefill_oracle_query_support",
+    "prefill_oracle_block_support",
     "pbs_importance",
     "pbs_permutation",
     "pbs_block_keys",
@@ -500,6 +502,29 @@ def prefill_query_attend(q_i, K, V, S, s_att: float):
     (which holds the query's own token)."""
     S = [int(j) for j in S]
     return attend(q_i, f64(K)[S], f64(V)[S], s_att)
+
+
+def prefill_oracle_query_support(q_i, K, i: int, s_att: float, k: int) -> np.ndarray:
+    """Attention-mass oracle support of query i (Oracle-Guided Sparse Prefill
+    2.1, per-query granularity): the top k of the head-averaged causal dense
+    distribution over j <= i, plus the query's own token (kept as in
+    prefill_query_support)."""
+    P = head_mean_attention(q_i, f64(K)[: i + 1], s_att)
+    return with_sink_window(select_topk(mass_scores(P), k), i + 1, 0, 1)
+
+
+def prefill_oracle_block_support(Q_blk, K, blk: int, b_sel: int, s_att: float, k: int) -> np.ndarray:
+    """Attention-mass oracle support shared by query block blk (section 2.1,
+    selection-block granularity): the causal dense distributions of the
+    block's queries, averaged over its rows and the group's heads, ranked
+    over the keys of earlier blocks j < b_sel * blk (the block's own keys are
+    attended causally on top, as for every block support)."""
+    n_cand = blk * b_sel
+    if n_cand == 0:
+        return np.zeros(0, dtype=np.int64)
+    n_rows = f64(Q_blk).shape[0]
+    imp = pbs_importance(Q_blk, f64(K)[: n_cand + n_rows], n_cand, s_att)
+    return select_topk(mass_scores(imp[:n_cand]), k)
 
 
 # ---------------------------------------------------------------------------

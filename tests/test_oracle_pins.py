@@ -836,3 +836,60 @@ def test_pbs_permutation_concentrates_scattered_heavy_hitters():
     assert best_perm > 2 * best_nat
     top = O.select_topk(x[:n_perm_blocks], 3)
     assert all(perm[c * b_sel] in hh for c in top)      # the chosen blocks lead with heavy hitters
+
+
+# ---------------------------------------------------------------------------
+# Prefill attention-mass oracle supports (Oracle-Guided Sparse Prefill 2.1)
+# ---------------------------------------------------------------------------
+
+
+def test_prefill_oracle_block_support_from_sdpa_weights():
+    rng = _rng(90)
+    N, G, d, b_sel = 96, 2, 8, 16
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    s = 0.6
+    W = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], np.eye(N)[None, None], s,
+              causal=True)[0]                                  # [G, N, N]
+    for blk in (1, 3, 5):
+        rows = O.prefill_block_rows(blk, b_sel, N)
+        S_ = O.prefill_oracle_block_support(Q[rows.start:rows.stop], K, blk, b_sel, s, k=7)
+        P = W[:, rows.start:rows.stop, : blk * b_sel].mean(axis=(0, 1))
+        ref = np.sort(np.argsort(-P, kind="stable")[:7])
+        assert np.array_equal(S_, ref)
+    assert len(O.prefill_oracle_block_support(Q[:16], K, 0, b_sel, s, k=7)) == 0
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_prefill_oracle_query_support_brute_force(seed):
+    rng = _rng(91 + seed)
+    G, d, i = 3, 6, 8
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((12, d))
+    P = O.head_mean_attention(q, K[: i + 1], 0.8)
+    for k in (1, 3, 5):
+        S_ = O.prefill_oracle_query_support(q, K, i, 0.8, k)
+        assert i in S_
+        top = set(S_.tolist()) - ({i} if len(S_) > k else set())
+        best = max(P[list(c)].sum() for c in itertools.combinations(range(i + 1), k))
+        assert abs(P[sorted(top)].sum() - best) < 1e-14
+
+
+def test_prefill_oracle_full_budget_is_dense_causal():
+    rng = _rng(94)
+    N, G, d, b_sel = 64, 2, 8, 16
+    Q = rng.standard_normal((N, G, d))
+    K = rng.standard_normal((N, d))
+    V = rng.standard_normal((N, d))
+    s = 1 / math.sqrt(d)
+    ref = _sdpa(np.transpose(Q, (1, 0, 2))[None], K[None, None], V[None, None], s, causal=True)[0]
+    for blk in range(N // b_sel):
+        rows = O.prefill_block_rows(blk, b_sel, N)
+        S_ = O.prefill_oracle_block_support(Q[rows.start:rows.stop], K, blk, b_sel, s, k=N)
+        o, _ = O.prefill_block_attend(Q[rows.start:rows.stop], K, V, S_, blk, b_sel, s)
+        np.testing.assert_allclose(o, np.transpose(ref[:, rows.start:rows.stop], (1, 0, 2)),
+                                   rtol=1e-11, atol=1e-12)
+    for i in (0, 17, 63):
+        S_ = O.prefill_oracle_query_support(Q[i], K, i, s, k=N)
+        o, _ = O.prefill_query_attend(Q[i], K, V, S_, s)
+        np.testing.assert_allclose(o, ref[:, i], rtol=1e-11, atol=1e-12)
