@@ -33,6 +33,7 @@ SA_OP_ATTENTION_MASS = 6
 SA_OP_PREFILL_QUERY = 7
 SA_OP_PBS_IMPORTANCE = 8
 SA_OP_PBS_SELECT = 9
+SA_OP_PREFILL_ORACLE = 10
 
 
 class SaShape(ctypes.Structure):
@@ -87,6 +88,8 @@ SIGNATURES = {
                                                     _I32, _I32, _P, _P, _I32, _P, _SZ, _P]),
     "sa_sparse_prefill_query": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _P, _P,
                                                _I32, _F, _P, ctypes.c_int, _P, _P, _SZ, _P]),
+    "sa_select_prefill_oracle": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, ctypes.c_int, _F, _I32,
+                                                _I32, _P, _P, _I32, _P, _SZ, _P]),
     "sa_pbs_importance": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, ctypes.c_int, _F, _I32, _P, _P,
                                          _SZ, _P]),
     "sa_pbs_permutation": (ctypes.c_int, [_SH, _P, _I32, _I32, _P, _P]),

@@ -173,6 +173,10 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return decode_ws(s, param, true);
     case SA_OP_ATTENTION_MASS:
       return mass_ws(s);
+    case SA_OP_PREFILL_ORACLE: {
+      sa::Shape sh = to_shape(s);
+      return sa::align_up(sa::prefill_oracle_workspace_bytes(sh, s->max_len), 256);
+    }
     case SA_OP_PBS_IMPORTANCE: {
       sa::Shape sh = to_shape(s);
       return sa::align_up(sa::pbs_importance_workspace_bytes(sh, s->max_len, param < 1 ? 1 : (int32_t)param), 256);
@@ -524,6 +528,28 @@ static sa_status pbs_common(const char* fn, const sa_shape* s, const sa_pages* p
   if (n_tokens < 1 || n_tokens > s->max_len)
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: n_tokens=%d outside [1, max_len=%d]", fn, n_tokens, s->max_len);
   return SA_OK;
+}
+
+sa_status sa_select_prefill_oracle(const sa_shape* s, const sa_pages* pg, int32_t n_tokens,
+                                  const void* q, const void* k_pool, sa_dtype dt, float s_att,
+                                  int32_t b_sel, int32_t k, int32_t* idx, int32_t* count,
+                                  int32_t cap, void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_select_prefill_oracle";
+  if (!pg) return fail(SA_ERR_INVALID_ARGUMENT, "%s: pages is NULL", fn);
+  SA_TRY(pbs_common(fn, s, pg, n_tokens));
+  if (!valid_dtype(dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !k_pool || !idx || !count) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (b_sel != 1 && b_sel != 64) return fail(SA_ERR_UNSUPPORTED, "%s: b_sel=%d must be 1 or 64", fn, b_sel);
+  if (k < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: k=%d < 1", fn, k);
+  if (s->n_kv_heads > 64) return fail(SA_ERR_UNSUPPORTED, "%s: n_kv_heads above 64", fn);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  const int64_t kk = b_sel == 1 ? (int64_t)k + 1 : (int64_t)k;
+  const int64_t need = kk < n_tokens ? kk : n_tokens;
+  if (cap < 1 || cap < need) return fail(SA_ERR_CAPACITY, "%s: cap=%d below %lld", fn, cap, (long long)need);
+  const sa::Shape sh = to_shape(s);
+  SA_TRY(check_ws(ws, ws_bytes, sa::align_up(sa::prefill_oracle_workspace_bytes(sh, n_tokens), 256), fn));
+  return hip_status(sa::launch_prefill_oracle_select(sh, *pg, n_tokens, q, k_pool, dt, s_att, b_sel,
+                                                     k, idx, count, cap, ws, st), fn);
 }
 
 sa_status sa_pbs_importance(const sa_shape* s, const sa_pages* pg, int32_t n_tokens, const void* q,

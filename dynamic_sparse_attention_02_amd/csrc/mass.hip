@@ -302,6 +302,27 @@ k_coverage(const float* __restrict__ x, int64_t ldx, const int32_t* __restrict__
   }
 }
 
+// Block form of the prefill oracle: xb[(b, g)][j] = ln of the mean over the
+// block's rows r of exp(x[(r, g)][j]) (each row's head-averaged causal
+// distribution) for the candidates j < 64 * (blk0 + b) of earlier blocks.
+__global__ void __launch_bounds__(256)
+k_block_mass(const float* __restrict__ x, int64_t ldx, int32_t nq, int32_t Hkv, int32_t blk0,
+             float* __restrict__ xb) {
+  const int b = blockIdx.y, g = blockIdx.z;
+  const int32_t j = blockIdx.x * 256 + threadIdx.x;
+  const int32_t n_cand = kPage * (blk0 + b);
+  if (j >= n_cand) return;
+  const int r0 = b * kPage, nr = min(kPage, nq - r0);
+  float acc = 0.f;
+  for (int r = 0; r < nr; ++r) acc += expf(x[((int64_t)(r0 + r) * Hkv + g) * ldx + j]);
+  xb[((int64_t)b * Hkv + g) * ldx + j] = logf(acc / (float)nr);
+}
+
+__global__ void k_slab_lens(int32_t* __restrict__ lens, int32_t n, int32_t first) {
+  const int32_t i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) lens[i] = first + i + 1;
+}
+
 struct MassLayout {
   int64_t ldl;
   int32_t nchunk;
@@ -349,9 +370,110 @@ hipError_t launch_mass_t(const Shape& s, const sa_pages& pg, const void* q, cons
   return hipGetLastError();
 }
 
+// Prefill oracle plan: query slabs of up to 256 queries (a multiple of 64,
+// at most 4096 (query, group) rows per launch).
+struct OracleLayout {
+  int32_t qs;
+  size_t off_lens, off_x, off_xb, off_mass, off_sel, total;
+};
+
+OracleLayout oracle_layout(const Shape& s, int32_t n_tokens) {
+  OracleLayout L;
+  int32_t q = (4096 / s.Hkv) / kPage * kPage;
+  L.qs = q < kPage ? kPage : (q > 256 ? 256 : q);
+  Shape s2 = s;
+  s2.B = L.qs;
+  s2.max_len = n_tokens;
+  size_t off = 0;
+  L.off_lens = off;
+  off += align_up((size_t)L.qs * sizeof(int32_t), 256);
+  L.off_x = off;
+  off += align_up((size_t)L.qs * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
+  L.off_xb = off;
+  off += align_up((size_t)(L.qs / kPage) * s.Hkv * (size_t)n_tokens * sizeof(float), 256);
+  L.off_mass = off;
+  off += align_up(mass_layout(s2).total, 256);
+  L.off_sel = off;
+  off += align_up(select_workspace_bytes(L.qs * s.Hkv, n_tokens), 256);
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 size_t mass_workspace_bytes(const Shape& s) { return mass_layout(s).total; }
+
+size_t prefill_oracle_workspace_bytes(const Shape& s, int32_t n_tokens) {
+  return oracle_layout(s, n_tokens).total;
+}
+
+hipError_t launch_prefill_oracle_select(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                        const void* q, const void* k_pool, sa_dtype dt,
+                                        float s_att, int32_t b_sel, int32_t k, int32_t* idx,
+                                        int32_t* count, int32_t cap, void* ws, hipStream_t st) {
+  const OracleLayout L = oracle_layout(s, n_tokens);
+  char* base = (char*)ws;
+  int32_t* lens = (int32_t*)(base + L.off_lens);
+  float* xq = (float*)(base + L.off_x);
+  float* xb = (float*)(base + L.off_xb);
+  const size_t qe = dt == SA_BF16 ? 2 : 4;
+  for (int32_t q0 = 0; q0 < n_tokens; q0 += L.qs) {
+    const int32_t nq = n_tokens - q0 < L.qs ? n_tokens - q0 : L.qs;
+    k_slab_lens<<<(nq + 255) / 256, 256, 0, st>>>(lens, nq, q0);
+    Shape s2 = s;
+    s2.B = nq;
+    s2.max_len = n_tokens;
+    s2.max_pages = 0;  // every query row reads page-table row 0
+    sa_pages p2;
+    p2.page_table = pg.page_table;
+    p2.seq_lens = lens;
+    hipError_t e = launch_attention_mass(s2, p2, (const char*)q + (size_t)q0 * s.Hq * s.D * qe,
+                                         k_pool, dt, s_att, xq, n_tokens, base + L.off_mass, st,
+                                         /*rows_fast=*/true);
+    if (e != hipSuccess) return e;
+    SelectArgs a{};
+    a.ldx = n_tokens;
+    a.seq_lens = nullptr;
+    a.Hkv = s.Hkv;
+    a.max_len = n_tokens;
+    a.unit = 1;
+    a.is_topk = 1;
+    a.p = 0.f;
+    a.k = k;
+    a.n_sink = 0;
+    a.cap = cap;
+    if (b_sel == 1) {  // per query: candidates j <= i, the own token always kept
+      a.x = xq;
+      a.rows = nq * s.Hkv;
+      a.max_cand = q0 + nq;
+      a.n_window = 1;
+      a.idx = idx + (int64_t)q0 * s.Hkv * cap;
+      a.count = count + (int64_t)q0 * s.Hkv;
+      a.prefill_bsel = 1;
+      a.prefill_blk0 = q0;
+      a.prefill_self = 1;
+    } else {  // per 64-query block: candidates of earlier blocks
+      const int32_t blk0 = q0 / kPage, nb = (nq + kPage - 1) / kPage;
+      const int32_t cand_hi = kPage * (blk0 + nb - 1);
+      if (cand_hi > 0) {
+        dim3 grid((cand_hi + 255) / 256, nb, s.Hkv);
+        k_block_mass<<<grid, 256, 0, st>>>(xq, n_tokens, nq, s.Hkv, blk0, xb);
+      }
+      a.x = xb;
+      a.rows = nb * s.Hkv;
+      a.max_cand = cand_hi > 0 ? cand_hi : 1;
+      a.n_window = 0;
+      a.idx = idx + (int64_t)blk0 * s.Hkv * cap;
+      a.count = count + (int64_t)blk0 * s.Hkv;
+      a.prefill_bsel = kPage;
+      a.prefill_blk0 = blk0;
+      a.prefill_self = 0;
+    }
+    e = launch_select(a, base + L.off_sel, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q, const void* k_pool,
                                  sa_dtype dt, float s_att, float* x, int64_t ldx, void* ws,

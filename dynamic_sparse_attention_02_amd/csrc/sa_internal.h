@@ -274,6 +274,11 @@ hipError_t launch_coverage(const Shape& s, const sa_pages& pg, const float* x, i
                            const int32_t* ridx, const int32_t* rcount, int32_t rcap, float* mass,
                            int32_t* overlap, hipStream_t st);
 
+size_t prefill_oracle_workspace_bytes(const Shape& s, int32_t n_tokens);
+hipError_t launch_prefill_oracle_select(const Shape& s, const sa_pages& pg, int32_t n_tokens,
+                                        const void* q, const void* k_pool, sa_dtype dt,
+                                        float s_att, int32_t b_sel, int32_t k, int32_t* idx,
+                                        int32_t* count, int32_t cap, void* ws, hipStream_t st);
 size_t pbs_importance_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t n_rows);
 size_t pbs_select_workspace_bytes(const Shape& s, int32_t n_tokens, int32_t k_blocks);
 hipError_t launch_pbs_importance(const Shape& s, const sa_pages& pg, int32_t n_tokens,

@@ -36,6 +36,7 @@ __all__ = [
     "sa_sparse_prefill",
     "sa_select_prefill_topk_probs",
     "sa_sparse_prefill_query",
+    "sa_select_prefill_oracle",
     "sa_pbs_importance",
     "sa_pbs_permutation",
     "sa_pbs_select",
@@ -264,3 +265,13 @@ def sa_pbs_select(shape, pages, n_tokens, q, k_pool, perm, seg, b_sel, k_blocks,
                                 int(k_blocks), _dev(idx), _dev(count), int(idx.shape[-1]), wp, wn,
                                 _stream(stream))
     L.check(st, "sa_pbs_select")
+
+
+def sa_select_prefill_oracle(shape, pages, n_tokens, q, k_pool, s_att, b_sel, k, idx, count, ws,
+                             stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_select_prefill_oracle(ctypes.byref(shape), ctypes.byref(pages), int(n_tokens),
+                                           _dev(q), _dev(k_pool), _dt(q), float(s_att), int(b_sel),
+                                           int(k), _dev(idx), _dev(count), int(idx.shape[-1]), wp,
+                                           wn, _stream(stream))
+    L.check(st, "sa_select_prefill_oracle")

@@ -100,7 +100,8 @@ typedef enum {
   SA_OP_ATTENTION_MASS = 6,    /* param unused                                   */
   SA_OP_PREFILL_QUERY = 7,     /* param = cap                                    */
   SA_OP_PBS_IMPORTANCE = 8,    /* param = n_rows                                 */
-  SA_OP_PBS_SELECT = 9         /* param = k_blocks                               */
+  SA_OP_PBS_SELECT = 9,        /* param = k_blocks                               */
+  SA_OP_PREFILL_ORACLE = 10    /* param unused                                   */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -361,6 +362,27 @@ sa_status sa_sparse_prefill_query(const sa_shape* shape, const sa_pages* pages,
                                   const int32_t* count, int32_t cap, float s_att, void* out,
                                   sa_dtype out_dtype, float* lse, void* ws, size_t ws_bytes,
                                   hipStream_t stream);
+
+/* Attention-mass oracle supports for prefill ("Oracle-Guided Sparse Prefill",
+ * section 2.1: the full causal attention distribution of each query,
+ * averaged over the group's heads, and its top k, per query or shared by a
+ * selection block).  b_sel = 1: row i * n_kv_heads + g lists the top k of
+ * P_i(j) = mean_{h in g} softmax_{j' <= i}(s_att * q[i][h] . k_j')[j] over
+ * j <= i plus the query's own token (cap >= min(k + 1, n_tokens); lists for
+ * sa_sparse_prefill_query).  b_sel = 64: row blk * n_kv_heads + g lists the
+ * top k over the keys of earlier blocks j < 64 blk of the mean of P_i over
+ * the block's queries i (cap >= min(k, n_tokens); lists for
+ * sa_sparse_prefill, which adds the block's own keys causally).  Ties lower
+ * index first; lists ascending, -1 padded.  Reads every causal key for every
+ * query: an instrument and reference, not a sparse step.  q, k_pool of
+ * dtype; n_kv_heads <= 64; workspace from SA_OP_PREFILL_ORACLE (sized for
+ * n_tokens = max_len; needs no zero-fill, left holding intermediate values,
+ * so not shared with the zeroed workspaces of other calls). */
+sa_status sa_select_prefill_oracle(const sa_shape* shape, const sa_pages* pages,
+                                  int32_t n_tokens, const void* q, const void* k_pool,
+                                  sa_dtype dtype, float s_att, int32_t b_sel, int32_t k,
+                                  int32_t* idx, int32_t* count, int32_t cap, void* ws,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* Segment-permuted block selection ("Sparser Block-Sparse Attention via Token
  * Permutation", sections 2 to 4), three calls whose lists feed

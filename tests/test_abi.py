@@ -161,6 +161,11 @@ def test_validation_codes():
     assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 64, 32, FAKE, FAKE, 2047, FAKE, ws_ps, None) == L.SA_ERR_CAPACITY
     assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 32, 32, FAKE, FAKE, 2048, FAKE, ws_ps, None) == L.SA_ERR_UNSUPPORTED
     assert so.sa_pbs_select(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, FAKE, 2048, 64, 32, FAKE, FAKE, 2048, FAKE, ws_ps - 1, None) == L.SA_ERR_WORKSPACE
+    # prefill attention-mass oracle: b_sel, capacity
+    ws_po = so.sa_workspace_size(L.SA_OP_PREFILL_ORACLE, B(s1), 0)
+    assert so.sa_select_prefill_oracle(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 32, 2048, FAKE, FAKE, 2048, FAKE, ws_po, None) == L.SA_ERR_UNSUPPORTED
+    assert so.sa_select_prefill_oracle(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 1, 2048, FAKE, FAKE, 2048, FAKE, ws_po, None) == L.SA_ERR_CAPACITY
+    assert so.sa_select_prefill_oracle(B(s1), B(pg), 131072, FAKE, FAKE, L.SA_BF16, 0.1, 64, 2048, FAKE, FAKE, 2048, FAKE, ws_po - 1, None) == L.SA_ERR_WORKSPACE
     # maintenance calls
     assert so.sa_index_append(B(s), None, FAKE, L.SA_BF16, FAKE, 5, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT
     assert so.sa_index_append(B(s), FAKE, FAKE, L.SA_BF16, FAKE, -1, FAKE, None) == L.SA_ERR_INVALID_ARGUMENT

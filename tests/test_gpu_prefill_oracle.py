@@ -1,0 +1,104 @@
+"""GPU parity of the attention-mass oracle supports for prefill ("Oracle-Guided
+Sparse Prefill", section 2.1) against the float64 oracle: per-query and
+64-query-block supports from the causal dense distributions, and the
+attention over them through the per-query and block-sparse kernels."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from tests import _support as S
+from tests.test_gpu_prefill import prefill_shape
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def ops():
+    from dynamic_sparse_attention_02_amd import ops as _ops
+    return _ops
+
+
+def _lib():
+    from dynamic_sparse_attention_02_amd import _lib as L
+    return L
+
+
+def gpu_oracle(inp, b_sel, k):
+    o = ops()
+    shape = prefill_shape(inp)
+    pages = o.make_pages(inp.page_table, None)
+    rows = (inp.N if b_sel == 1 else inp.n_blocks) * inp.H_kv
+    cap = min(k + 1 if b_sel == 1 else k, inp.N)
+    idx = torch.full((rows, cap), -7, dtype=torch.int32, device="cuda")
+    count = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    ws = o.alloc_workspace(o.workspace_size(_lib().SA_OP_PREFILL_ORACLE, shape, 0))
+    o.sa_select_prefill_oracle(shape, pages, inp.N, inp.q, inp.k_pool, inp.s_att, b_sel, k, idx,
+                               count, ws)
+    torch.cuda.synchronize()
+    return idx, count, shape, pages
+
+
+def _log_mass(P):
+    with np.errstate(divide="ignore"):
+        return np.log(P)
+
+
+@pytest.mark.parametrize("N,k,H_q,H_kv", [(700, 50, 8, 2), (333, 400, 4, 1), (1100, 96, 16, 2)])
+def test_prefill_oracle_per_query(N, k, H_q, H_kv):
+    inp = synth.make_prefill_custom(N=N, H_q=H_q, H_kv=H_kv, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=N, n_hh=8)
+    idx, count, shape, pages = gpu_oracle(inp, 1, k)
+    o = ops()
+    out = torch.full((N, H_q, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, H_q), dtype=torch.float32, device="cuda")
+    ws_a = o.alloc_workspace(o.workspace_size(_lib().SA_OP_PREFILL_QUERY, shape, idx.shape[1]))
+    o.sa_sparse_prefill_query(shape, pages, N, inp.q, inp.k_pool, inp.v_pool, idx, count,
+                              inp.s_att, out, lse, ws_a)
+    torch.cuda.synchronize()
+    for g in range(H_kv):
+        hs = inp.heads(g)
+        K = S.to_np(inp.keys(g))
+        V = S.to_np(inp.values(g))
+        for i in sorted({0, 1, k - 1, k, k + 1, N // 2, N - 1} & set(range(N))):
+            qi = S.to_np(inp.q[i, hs])
+            x = _log_mass(O.head_mean_attention(qi, K[: i + 1], inp.s_att))
+            core = O.select_topk(x, k)
+            gsup = S.gpu_support(idx, count, i * H_kv + g)
+            S.check_support(gsup, x, core, L=i + 1, k=k, n_window=1)
+            assert np.array_equal(O.with_sink_window(core, i + 1, 0, 1),
+                                  O.prefill_oracle_query_support(qi, K, i, inp.s_att, k))
+            o_ref, _ = O.prefill_query_attend(qi, K, V, gsup, inp.s_att)
+            assert S.max_abs(S.to_np(out[i, hs]), o_ref) <= 2e-2
+
+
+@pytest.mark.parametrize("N,k,H_q,H_kv", [(1000, 200, 8, 2), (640, 2048, 4, 1), (1300, 64, 16, 2)])
+def test_prefill_oracle_per_block(N, k, H_q, H_kv):
+    inp = synth.make_prefill_custom(N=N, H_q=H_q, H_kv=H_kv, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=N + 1, n_hh=8)
+    idx, count, shape, pages = gpu_oracle(inp, 64, k)
+    o = ops()
+    out = torch.full((N, H_q, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, H_q), dtype=torch.float32, device="cuda")
+    o.sa_sparse_prefill(shape, pages, N, inp.q, inp.k_pool, inp.v_pool, idx, count, 64,
+                        inp.s_att, out, lse)
+    torch.cuda.synchronize()
+    for g in range(H_kv):
+        hs = inp.heads(g)
+        K = S.to_np(inp.keys(g))
+        V = S.to_np(inp.values(g))
+        for blk in range(inp.n_blocks):
+            rows = O.prefill_block_rows(blk, 64, N)
+            Qb = S.to_np(inp.q[rows.start:rows.stop][:, hs])
+            gsup = S.gpu_support(idx, count, blk * H_kv + g)
+            n_cand = 64 * blk
+            if n_cand == 0:
+                assert len(gsup) == 0
+            else:
+                imp = O.pbs_importance(Qb, K[: rows.stop], n_cand, inp.s_att)
+                x = _log_mass(imp[:n_cand])
+                S.check_support(gsup, x, O.select_topk(x, k), L=n_cand, k=k)
+            o_ref, _ = O.prefill_block_attend(Qb, K, V, gsup, blk, 64, inp.s_att)
+            assert S.max_abs(S.to_np(out[rows.start:rows.stop][:, hs]), o_ref) <= 2e-2
