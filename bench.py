@@ -53,10 +53,12 @@ def parse():
                     help="token-level decode workloads: take the support from the low-rank "
                          "indexer (default) or from the dense head-averaged attention mass "
                          "(the attention-mass oracle: sa_attention_mass + sa_select_topp)")
-    ap.add_argument("--selection", default="indexer", choices=["indexer", "pbs"],
+    ap.add_argument("--selection", default="indexer", choices=["indexer", "pbs", "oracle"],
                     help="prefill128k: block supports from the low-rank indexer (default) or from "
                          "the segment-permuted mean-pooled blocks (sa_pbs_*; segments of 2048, "
-                         "importance from the last 64 queries, top-32 blocks)")
+                         "importance from the last 64 queries, top-32 blocks); prefill32k_query: "
+                         "oracle = per-query supports from the dense attention mass "
+                         "(sa_select_prefill_oracle)")
     ap.add_argument("--coverage", action="store_true",
                     help="prefill128k: also report the dense attention mass the supports keep on "
                          "8 sampled (query block, group) items (float64 on the host, untimed)")
@@ -595,6 +597,7 @@ def bench_prefill_query(args):
     N, Hq, Hkv, d = inp.N, inp.H_q, inp.H_kv, inp.d
     G = Hq // Hkv
     probs = args.aggregate == "probs"
+    oracle_sel = args.selection == "oracle"
     shape = ops.make_shape(batch=1, n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d,
                            max_pages=inp.page_table.shape[1], max_len=N,
                            n_pool_pages=inp.k_pool.shape[0])
@@ -607,11 +610,16 @@ def bench_prefill_query(args):
     count = torch.empty((N * Hkv,), dtype=torch.int32, device="cuda")
     out = torch.empty((N, Hq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((N, Hq), dtype=torch.float32, device="cuda")
-    ws = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_SELECT, shape, N))
+    ws = ops.alloc_workspace(ops.workspace_size(
+        L.SA_OP_PREFILL_ORACLE if oracle_sel else L.SA_OP_PREFILL_SELECT, shape, N))
     ws_a = ops.alloc_workspace(ops.workspace_size(L.SA_OP_PREFILL_QUERY, shape, cap))
     sel_fn = ops.sa_select_prefill_topk_probs if probs else ops.sa_select_prefill_topk
 
     def select():
+        if oracle_sel:
+            ops.sa_select_prefill_oracle(shape, pages, N, inp.q, inp.k_pool, inp.s_att, 1, k, idx,
+                                         count, ws)
+            return
         sel_fn(shape, pages, N, inp.q, inp.w_q, kidx, inp.s_idx, 1, k, idx, count, ws)
 
     def attend():
@@ -631,7 +639,7 @@ def bench_prefill_query(args):
     t_att = time_events(attend, args.steps)
     ms = t_sel + t_att
     gbs = kv_bytes / (t_att * 1e-3) / 1e9
-    name = "prefill32k_query" + ("+probs" if probs else "")
+    name = "prefill32k_query" + ("+probs" if probs else "") + ("+oracle" if oracle_sel else "")
     res = {
         "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -639,7 +647,8 @@ def bench_prefill_query(args):
         "data": "synthetic",
         "config": {"workload": name, "tokens": N, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "b_sel": 1, "top_k": k,
-                   "aggregate": "mean of head probabilities" if probs else "head-collapsed logits"},
+                   "aggregate": ("dense attention mass (oracle)" if oracle_sel else
+                                 "mean of head probabilities" if probs else "head-collapsed logits")},
         "algorithmic_flops": flops, "kv_bytes": kv_bytes,
         "budget_fraction": round(listed / (Hkv * N * (N + 1) / 2), 5),
         "breakdown_ms": {"select": round(t_sel, 4), "attention": round(t_att, 4)},
@@ -651,7 +660,7 @@ def bench_prefill_query(args):
                      "note": "gathered K/V rows per listed key; the 134 MB cache of this "
                              "workload fits the last-level cache, so rows repeat from it"},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not oracle_sel:
         res["cpu_baseline"] = cpu_baseline_prefill_query(inp, kidx, args.cpu_seconds, probs)
     return res
 
