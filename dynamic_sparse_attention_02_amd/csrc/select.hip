@@ -487,26 +487,32 @@ __global__ void __launch_bounds__(kThreads) k_sel_out(SelectArgs a, WsLayout w, 
 // ---------------------------------------------------------------------------
 // Row-resident selection: one block per row for rows of up to kRowMax
 // candidates.  Keys of the first kRowRegs * kThreads candidates stay in
-// registers (the rest are re-read from the score row), the three radix levels
-// use one LDS histogram with block barriers only.  The ordered compaction
-// takes each (64-candidate wave slice)'s selected count from a ballot, one
-// block scan over the slices gives every slice's output offset, and a lane's
-// position inside its slice is the popcount of the ballot below it.  Selected
-// pages are staged in LDS and expanded to tokens by the whole block.
+// registers, the next kCacheRounds * kThreads in LDS, the rest are re-read
+// from the score row.  Only two passes touch every candidate: the one that
+// loads the keys (and, for top-k, builds the level-1 histogram on the way),
+// and a filter pass that marks every candidate above the level-1 threshold
+// bin in an LDS bitmap (one ballot word per wave and round) and gathers the
+// candidates inside that bin into an LDS buffer.  Levels 2 and 3 and the
+// final marking run over that buffer alone (over every candidate again only
+// when the bin overflows it).  Keys equal to the final threshold are ranked in
+// index order by a block scan over a second bitmap; the ascending index list
+// is a block scan over the bitmap's word popcounts.  Selected pages are
+// staged in LDS and expanded to tokens by the whole block.
 // ---------------------------------------------------------------------------
 constexpr int kRowRegsTopp = 32;
 constexpr int kRowRegsTopk = 48;
 // rounds after the register-resident ones kept in LDS (top-k has no mass
 // histogram, so more LDS is free for keys)
-constexpr int kCacheRoundsTopk = 24;
-constexpr int kCacheRoundsTopp = 16;
+constexpr int kCacheRoundsTopk = 22;
+constexpr int kCacheRoundsTopp = 14;
 constexpr int kRowMax = 131072;
-constexpr int kRowRounds = kRowMax / kThreads;        // 128 slices per wave
-constexpr int kRowSlices = kRowRounds * kWaves;       // 2048 (round, wave) slices
-constexpr int kPList = 4096;                          // pages staged for expansion
+constexpr int kMapWords = kRowMax / 64;   // 64-bit bitmap words: one per (round, wave)
+constexpr int kBufCap = 4096;             // candidates of the level-1 bin held in LDS
+constexpr int kBufPerWave = kBufCap / kWaves;  // each wave fills its own segment
+static_assert(kMapWords * 2 == kBins, "the tie bitmap reuses the count histogram");
 
 struct RowRes {
-  uint32_t mode, prefix, thr, n_eq, need;
+  uint32_t mode, prefix, thr, n_eq, need, all;
   uint64_t rem;
 };
 
@@ -515,6 +521,7 @@ struct RowRes {
 template <bool TOPP, int RR>
 __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   constexpr int kRowRegs = RR;
+  constexpr int kCacheRounds = TOPP ? kCacheRoundsTopp : kCacheRoundsTopk;
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t n = n_cand_of(a, row);
@@ -522,19 +529,23 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const int32_t Lt = a.seq_lens ? clamp_len(a.seq_lens[b], a.max_len) : n;
   const float* xr = a.x + (int64_t)row * a.ldx;
   const int rounds = (n + kThreads - 1) / kThreads;
+  const int32_t last = n > 0 ? n - 1 : 0;
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
 
-  __shared__ uint32_t hcnt[kBins];
+  __shared__ __align__(16) uint32_t hcnt[kBins];  // digit counts; after the last level, the tie bitmap
   __shared__ uint64_t hmass[TOPP ? kBins : 1];
-  __shared__ uint32_t slice[kRowSlices];
-  __shared__ int32_t plist[TOPP ? 1 : kPList];
+  __shared__ uint64_t selmap[kMapWords];  // bit e: candidate e is selected
+  __shared__ uint32_t kcache[kCacheRounds * kThreads];
+  __shared__ uint32_t bkey[kBufCap];
+  __shared__ int32_t bidx[kBufCap];  // after the marking, the staged page list
   __shared__ uint32_t red32[kWaves];
   __shared__ uint64_t red64[kWaves];
   __shared__ RowRes res;
-  __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef;
+  __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef, s_last;
+  __shared__ uint32_t s_wcnt[kWaves];
   __shared__ uint64_t s_hit_mass, s_hit_mbef;
-
-  constexpr int kCacheRounds = TOPP ? kCacheRoundsTopp : kCacheRoundsTopk;
-  __shared__ uint32_t kcache[kCacheRounds * kThreads];
+  uint32_t* const sel32 = reinterpret_cast<uint32_t*>(selmap);
+  uint32_t* const tie32 = hcnt;
   const int cached_end = kRowRegs + kCacheRounds;  // rounds [kRowRegs, cached_end) live in LDS
 
   // Visit rounds [kRowRegs, rounds): LDS-cached rounds one at a time, then
@@ -544,7 +555,6 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   auto for_rounds = [&](auto&& fn) {
     const int c_end = rounds < cached_end ? rounds : cached_end;
     for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * kThreads + t]);
-    const int32_t last = n > 0 ? n - 1 : 0;
     for (int i0 = c_end; i0 < rounds; i0 += 8) {
       float v[8];
 #pragma unroll
@@ -559,118 +569,122 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       }
     }
   };
-
   uint32_t keys[kRowRegs];
-  uint32_t mk = 0;
-  {
-    // 8 rounds per batch, loads issued together (rounds past the row skip
-    // whole batches; lanes past it read the last score and get key 0)
-    const int32_t last = n > 0 ? n - 1 : 0;
+  // every round (wave-uniform calls; fn checks the candidate's validity)
+  auto for_all = [&](auto&& fn) {
 #pragma unroll
-    for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
-      if (i0 < rounds) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t e = (i0 + u) * kThreads + t;
-          v[u] = xr[e < n ? e : last];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t e = (i0 + u) * kThreads + t;
-          keys[i0 + u] = e < n ? score_key(v[u]) : 0u;
-          mk = keys[i0 + u] > mk ? keys[i0 + u] : mk;
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) keys[i0 + u] = 0u;
-      }
+    for (int i = 0; i < kRowRegs; ++i)
+      if (i < rounds) fn(i, keys[i]);
+    for_rounds(fn);
+  };
+  // digit of `key` at `level` into the histogram when its resolved high bits
+  // equal `pre`
+  auto hist_add = [&](uint32_t key, int level, uint32_t pre, float mx) {
+    const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+    const int hshift = level == 2 ? 20 : 8;
+    const uint32_t dmask = level == 3 ? 0xffu : 0xfffu;
+    if (level == 1 || (key >> hshift) == pre) {
+      const uint32_t digit = (key >> shift) & dmask;
+      atomicAdd(&hcnt[digit], 1u);
+      if (TOPP)
+        atomicAdd((unsigned long long*)&hmass[digit],
+                  (unsigned long long)mass_fixed(key_score(key), mx));
     }
-  }
-  {
-    const int32_t last = n > 0 ? n - 1 : 0;
-    const int c_end = rounds < cached_end ? rounds : cached_end;
-    for (int i0 = kRowRegs; i0 < c_end; i0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        v[u] = xr[e < n ? e : last];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        if (i0 + u < c_end) {
-          const uint32_t k = e < n ? score_key(v[u]) : 0u;
-          kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
-          mk = k > mk ? k : mk;
-        }
-      }
-    }
-  }
-  if (TOPP) {  // the row maximum (mass reference) needs every key
-    const int32_t last = n > 0 ? n - 1 : 0;
-    for (int i0 = cached_end; i0 < rounds; i0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        v[u] = xr[e < n ? e : last];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        const uint32_t k = e < n ? score_key(v[u]) : 0u;
-        mk = k > mk ? k : mk;
-      }
-    }
-  }
-  mk = wave_max_u32(mk);
-  if (lane == 0) red32[wave] = mk;
+  };
+
   if (t == 0) {
     res.mode = kSearching;
     res.prefix = 0;
     res.thr = 0;
     res.n_eq = 0;
     res.need = (uint32_t)a.k;
+    res.all = 0;
     res.rem = 0;
     if (n == 0 || (a.is_topk ? (a.k >= n) : (a.p >= 1.0f))) res.mode = kTakeGE;
+    s_last = 0;
+  }
+  for (int i = t; i < kBins; i += kThreads) {
+    hcnt[i] = 0;
+    if (TOPP) hmass[i] = 0;
   }
   __syncthreads();
-  uint32_t M = 0;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) M = red32[i] > M ? red32[i] : M;
-  const float mx = key_score(M);
 
-  // ---- radix levels: digits key[31:20], key[19:8], key[7:0] ----
-  for (int level = 1; level <= 3; ++level) {
-    if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
-    const int NB = level == 3 ? 256 : kBins;
-    const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
-    const int hshift = level == 2 ? 20 : 8;  // resolved bits above the digit
-    const uint32_t dmask = level == 3 ? 0xffu : 0xfffu;
-    const uint32_t pre = res.prefix;
-    for (int i = t; i < NB; i += kThreads) {
-      hcnt[i] = 0;
-      if (TOPP) hmass[i] = 0;
-    }
-    __syncthreads();
-    auto add = [&](uint32_t key) {
-      if (level == 1 || (key >> hshift) == pre) {
-        const uint32_t digit = (key >> shift) & dmask;
-        atomicAdd(&hcnt[digit], 1u);
-        if (TOPP)
-          atomicAdd((unsigned long long*)&hmass[digit],
-                    (unsigned long long)mass_fixed(key_score(key), mx));
-      }
-    };
+  // ---- load: keys to registers and LDS; top-k builds the level-1 histogram,
+  // top-p takes the row maximum (the mass reference) first ----
+  uint32_t mk = 0;
+  // top-k: padding lanes (key 0) are counted into bin 0 and taken out below
+  auto take = [&](int32_t e, uint32_t key) {
+    if (TOPP) mk = key > mk ? key : mk;
+    else hist_add(key, 1, 0, 0.f);
+  };
+  // every register round's load is issued before the first is used (raw
+  // score bits; lanes past the row read its last score)
 #pragma unroll
-    for (int i = 0; i < kRowRegs; ++i)
-      if (i * kThreads + t < n) add(keys[i]);
-    for_rounds([&](int i, uint32_t k) {
-      if (i * kThreads + t < n) add(k);
+  for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
+    if (i0 < rounds) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        keys[i0 + u] = __float_as_uint(xr[e < n ? e : last]);
+      }
+    }
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
+    if (i0 < rounds) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        keys[i0 + u] = e < n ? score_key(__uint_as_float(keys[i0 + u])) : 0u;
+        if (i0 + u < rounds) take(e, keys[i0 + u]);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) keys[i0 + u] = 0u;
+    }
+  }
+  for (int i0 = kRowRegs; i0 < rounds; i0 += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int32_t e = (i0 + u) * kThreads + t;
+      v[u] = xr[e < n ? e : last];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int32_t e = (i0 + u) * kThreads + t;
+      if (i0 + u < rounds) {
+        const uint32_t k = e < n ? score_key(v[u]) : 0u;
+        if (i0 + u < cached_end) kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
+        take(e, k);
+      }
+    }
+  }
+  if (!TOPP && t == 0) atomicSub(&hcnt[0], (uint32_t)(rounds * kThreads - n));
+  float mx = 0.f;
+  if (TOPP) {
+    mk = wave_max_u32(mk);
+    if (lane == 0) red32[wave] = mk;
+  }
+  __syncthreads();
+  if (TOPP) {
+    uint32_t M = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) M = red32[i] > M ? red32[i] : M;
+    mx = key_score(M);
+    for_all([&](int i, uint32_t k) {
+      if (i * kThreads + t < n) hist_add(k, 1, 0, mx);
     });
     __syncthreads();
+  }
+
+  // Resolve a level from its histogram: the bin (in descending order) where
+  // the running count reaches the candidates still needed (top-k), or the
+  // running mass the target (top-p).  Ends with a barrier.
+  auto resolve = [&](int level) {
+    const int NB = level == 3 ? 256 : kBins;
+    const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+    const uint32_t pre = res.prefix;
     // block scan over bins in descending order: thread t owns positions
     // [t*per, (t+1)*per), position q <-> bin NB-1-q
     const int per = NB / kThreads > 0 ? NB / kThreads : 1;
@@ -722,6 +736,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       if (bin == 0xffffffffu) {
         res.mode = kTakeGE;  // inconsistent input: take everything
         res.thr = 0;
+        res.all = 1;
       } else {
         const uint32_t cnt_b = s_hit_cnt;
         const uint32_t np = level == 1 ? bin : (level == 2 ? ((pre << 12) | bin) : ((pre << 8) | bin));
@@ -738,13 +753,13 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
             }
           } else {
             const uint64_t m1 = s_hit_mass / cnt_b;
-            const uint64_t take = (rem + m1 - 1) / m1;
+            const uint64_t take_n = (rem + m1 - 1) / m1;
             res.thr = bin_lo;
-            if (take >= cnt_b) {
+            if (take_n >= cnt_b) {
               res.mode = kTakeGE;
             } else {
               res.mode = kTakeTies;
-              res.n_eq = (uint32_t)take;
+              res.n_eq = (uint32_t)take_n;
             }
           }
         } else {
@@ -764,110 +779,195 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       }
     }
     __syncthreads();
+  };
+
+  // ---- level 1, then the filter pass ----
+  if (res.mode == kSearching) resolve(1);
+  const uint32_t mode1 = res.mode, thr1 = res.thr, B1 = res.prefix;
+  if (mode1 == kSearching) {
+    // bins above B1 are in; bin B1 goes to this wave's buffer segment
+    uint32_t wcnt = 0;  // wave-uniform fill of the segment
+    for_all([&](int i, uint32_t k) {
+      const int32_t e = i * kThreads + t;
+      const bool valid = e < n;
+      const uint32_t d = k >> 20;
+      const uint64_t m = __ballot(valid && d > B1);
+      if (lane == 0) selmap[i * kWaves + wave] = m;
+      const bool in = valid && d == B1;
+      const uint64_t mb = __ballot(in);
+      if (mb) {
+        const uint32_t p = wcnt + (uint32_t)__popcll(mb & lt_mask);
+        if (in && p < (uint32_t)kBufPerWave) {
+          bkey[wave * kBufPerWave + p] = k;
+          bidx[wave * kBufPerWave + p] = e;
+        }
+        wcnt += (uint32_t)__popcll(mb);
+      }
+    });
+    if (lane == 0) s_wcnt[wave] = wcnt;
+  } else {
+    // key >= thr1 decides every candidate
+    for_all([&](int i, uint32_t k) {
+      const uint64_t m = __ballot(i * kThreads + t < n && k >= thr1);
+      if (lane == 0) selmap[i * kWaves + wave] = m;
+    });
+  }
+  __syncthreads();
+  bool use_buf = true;
+  if (mode1 == kSearching) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) use_buf = use_buf && s_wcnt[w] <= (uint32_t)kBufPerWave;
+  }
+  // buffer slot j holds a candidate when it lies inside its wave's fill
+  auto in_buf = [&](int j) { return (uint32_t)(j % kBufPerWave) < s_wcnt[j / kBufPerWave]; };
+
+  // ---- levels 2 and 3 over the bin's candidates ----
+  for (int level = 2; level <= 3; ++level) {
+    if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
+    const int NB = level == 3 ? 256 : kBins;
+    const uint32_t pre = res.prefix;
+    for (int i = t; i < NB; i += kThreads) {
+      hcnt[i] = 0;
+      if (TOPP) hmass[i] = 0;
+    }
+    __syncthreads();
+    if (use_buf) {
+      for (int j = t; j < kBufCap; j += kThreads)
+        if (in_buf(j)) hist_add(bkey[j], level, pre, mx);
+    } else {
+      for_all([&](int i, uint32_t k) {
+        if (i * kThreads + t < n) hist_add(k, level, pre, mx);
+      });
+    }
+    __syncthreads();
+    resolve(level);
   }
 
-  // ---- ordered compaction ----
+  // ---- final marking of the bin's candidates ----
   const uint32_t mode = res.mode, thr = res.thr, n_eq = res.n_eq;
-  const uint64_t lt_mask = (1ull << lane) - 1ull;
-  const int n_slices = rounds * kWaves;
+  const bool take_all = res.all != 0;
+  const bool ties = mode1 == kSearching && mode == kTakeTies;
+  const int nw = (n + 31) >> 5;  // 32-bit bitmap words of the row
+  if (ties) {
+    for (int i = t; i < nw; i += kThreads) tie32[i] = 0;
+    __syncthreads();
+  }
+  if (mode1 == kSearching) {
+    if (use_buf) {
+      for (int j = t; j < kBufCap; j += kThreads) {
+        if (!in_buf(j)) continue;
+        const uint32_t k = bkey[j];
+        const int32_t e = bidx[j];
+        if (k > thr || (mode == kTakeGE && k == thr)) atomicOr(&sel32[e >> 5], 1u << (e & 31));
+        else if (ties && k == thr) atomicOr(&tie32[e >> 5], 1u << (e & 31));
+      }
+    } else {
+      for_all([&](int i, uint32_t k) {
+        const int32_t e = i * kThreads + t;
+        const bool in = e < n && (k >> 20) == B1;
+        const uint64_t ms = __ballot(in && (k > thr || (mode == kTakeGE && k == thr)));
+        const uint64_t me = __ballot(in && ties && k == thr);
+        if (lane == 0) {
+          selmap[i * kWaves + wave] |= ms;
+          if (ties) reinterpret_cast<uint64_t*>(tie32)[i * kWaves + wave] = me;
+        }
+      });
+    }
+    __syncthreads();
+  }
+
+  // ---- ordered compaction: thread t owns bitmap words [4t, 4t + 4) ----
+  uint32_t sw[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) sw[w] = 4 * t + w < nw ? sel32[4 * t + w] : 0u;
+  if (ties) {  // the n_eq lowest-index keys equal to the threshold
+    uint32_t tw[4], c = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      tw[w] = 4 * t + w < nw ? tie32[4 * t + w] : 0u;
+      c += (uint32_t)__popc(tw[w]);
+    }
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<uint32_t>(c, red32, tot);
+    uint32_t left = before < n_eq ? n_eq - before : 0u;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t bits = tw[w], keep = 0;
+      while (bits && left) {
+        keep |= bits & (0u - bits);
+        bits &= bits - 1u;
+        --left;
+      }
+      sw[w] |= keep;
+    }
+  }
   const int32_t unit = a.unit;
   const int ushift = __ffs(unit) - 1;          // unit is 1 or the page size (powers of two)
   const int32_t last_w = Lt - (n - 1) * unit;  // tokens of the last candidate (unit > 1)
-  // tie ranks reuse the count histogram's LDS (no longer needed)
-  uint32_t* eqoff = hcnt;
-  auto scan_slices = [&](uint32_t* arr) -> uint32_t {  // in place, exclusive
-    const uint32_t v0 = (2 * t < n_slices) ? arr[2 * t] : 0u;
-    const uint32_t v1 = (2 * t + 1 < n_slices) ? arr[2 * t + 1] : 0u;
-    uint32_t tot;
-    const uint32_t ex = block_excl_scan<uint32_t>(v0 + v1, red32, tot);
-    if (2 * t < n_slices) arr[2 * t] = ex;
-    if (2 * t + 1 < n_slices) arr[2 * t + 1] = ex + v0;
-    __syncthreads();
-    return tot;
-  };
-  if (mode == kTakeTies) {  // only when some keys equal to the threshold are left out
+  uint32_t c = 0;
 #pragma unroll
-    for (int i = 0; i < kRowRegs; ++i) {
-      if (i < rounds) {
-        const uint64_t m = __ballot((i * kThreads + t < n) && keys[i] == thr);
-        if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
+  for (int w = 0; w < 4; ++w) {
+    const int widx = 4 * t + w;
+    if (widx < nw) {
+      const int32_t lo = widx * 32;
+      const uint32_t vm = n - lo >= 32 ? ~0u : ((1u << (n - lo)) - 1u);
+      uint32_t fm = 0;
+      if (unit == 1) {  // always-kept sink and window candidates
+        if (a.n_sink > lo) fm |= a.n_sink - lo >= 32 ? ~0u : ((1u << (a.n_sink - lo)) - 1u);
+        const int32_t ws = n - a.n_window;
+        if (ws < lo + 32) fm |= ws <= lo ? ~0u : (~0u << (ws - lo));
+      }
+      sw[w] = ((take_all ? ~0u : sw[w]) | fm) & vm;
+      if (unit > 1 && widx == ((n - 1) >> 5)) s_last = (sw[w] >> ((n - 1) & 31)) & 1u;
+    }
+    c += (uint32_t)__popc(sw[w]);
+  }
+  uint32_t total;
+  uint32_t rank = block_excl_scan<uint32_t>(c, red32, total);  // barriers publish s_last
+  int32_t* out = a.idx + (int64_t)row * a.cap;
+  uint32_t T;
+  if (unit == 1) {
+    T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t bits = sw[w];
+      while (bits) {
+        const int j = __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (rank < (uint32_t)a.cap) out[rank] = (4 * t + w) * 32 + j;
+        ++rank;
       }
     }
-    for_rounds([&](int i, uint32_t k) {
-      const uint64_t m = __ballot((i * kThreads + t < n) && k == thr);
-      if (lane == 0) eqoff[i * kWaves + wave] = (uint32_t)__popcll(m);
-    });
-    __syncthreads();
-    scan_slices(eqoff);
-  }
-  // is candidate (round i, this thread) in the support?  Every lane calls it
-  // (ballot inside).
-  auto selected = [&](int i, uint32_t key) -> bool {
-    const int32_t e = i * kThreads + t;
-    const bool valid = e < n;
-    bool top;
-    if (mode == kTakeTies) {
-      const bool eq = valid && key == thr;
-      const uint64_t m = __ballot(eq);
-      top = valid && key > thr;
-      if (eq) top = (eqoff[i * kWaves + wave] + (uint32_t)__popcll(m & lt_mask)) < n_eq;
-    } else {
-      top = valid && key >= thr;
-    }
-    const bool forced = valid && unit == 1 && (e < a.n_sink || e >= n - a.n_window);
-    return top || forced;
-  };
-  // pass 1: output tokens of every (round, wave) slice.  Every page but the
-  // row's last holds `unit` tokens.
-  auto count_slice = [&](int i, uint32_t key) {
-    const bool sel = selected(i, key);
-    const uint64_t m = __ballot(sel);
-    uint32_t c = (uint32_t)__popcll(m) << ushift;
-    if (unit > 1 && __ballot(sel && i * kThreads + t == n - 1)) c -= (uint32_t)(unit - last_w);
-    if (lane == 0) slice[i * kWaves + wave] = c;
-  };
+  } else {
+    const uint32_t tokens = (total << ushift) - (s_last ? (uint32_t)(unit - last_w) : 0u);
+    T = tokens < (uint32_t)a.cap ? tokens : (uint32_t)a.cap;
+    const bool staged = total < (uint32_t)kBufCap;
 #pragma unroll
-  for (int i = 0; i < kRowRegs; ++i)
-    if (i < rounds) count_slice(i, keys[i]);
-  for_rounds([&](int i, uint32_t k) { count_slice(i, k); });
-  __syncthreads();
-  const uint32_t total = scan_slices(slice);
-  const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
-  // pass 2: every selected candidate at its slice offset plus its rank in the
-  // slice
-  int32_t* out = a.idx + (int64_t)row * a.cap;
-  const bool staged = unit > 1 && (total >> ushift) < (uint32_t)kPList;
-  auto emit = [&](int i, uint32_t key) {
-    const bool sel = selected(i, key);
-    const uint64_t m = __ballot(sel);
-    const uint32_t rank = (uint32_t)__popcll(m & lt_mask);
-    if (!sel) return;
-    const int32_t e = i * kThreads + t;
-    if (unit == 1) {
-      const uint32_t pos = slice[i * kWaves + wave] + rank;
-      if (pos < (uint32_t)a.cap) out[pos] = e;
-    } else if (staged) {
-      plist[(slice[i * kWaves + wave] >> ushift) + rank] = e;
-    } else {
-      const uint32_t pos = slice[i * kWaves + wave] + (rank << ushift);
-      const int32_t w = e == n - 1 ? last_w : unit;
-      for (int32_t q = 0; q < w; ++q)
-        if (pos + q < (uint32_t)a.cap) out[pos + q] = e * unit + q;
+    for (int w = 0; w < 4; ++w) {
+      uint32_t bits = sw[w];
+      while (bits) {
+        const int32_t e = (4 * t + w) * 32 + __ffs(bits) - 1;
+        bits &= bits - 1u;
+        if (staged) {
+          bidx[rank] = e;
+        } else {
+          const uint32_t pos = rank << ushift;
+          const int32_t wd = e == n - 1 ? last_w : unit;
+          for (int32_t q = 0; q < wd; ++q)
+            if (pos + q < (uint32_t)a.cap) out[pos + q] = e * unit + q;
+        }
+        ++rank;
+      }
     }
-  };
-#pragma unroll
-  for (int i = 0; i < kRowRegs; ++i)
-    if (i < rounds) emit(i, keys[i]);
-  for_rounds([&](int i, uint32_t k) { emit(i, k); });
-  if (staged) {  // block-uniform
-    __syncthreads();
-    for (uint32_t o = t; o < T; o += kThreads)
-      out[o] = (plist[o >> ushift] << ushift) + (int32_t)(o & (uint32_t)(unit - 1));
+    if (staged) {  // block-uniform
+      __syncthreads();
+      for (uint32_t o = t; o < T; o += kThreads)
+        out[o] = (bidx[o >> ushift] << ushift) + (int32_t)(o & (uint32_t)(unit - 1));
+    }
   }
   for (int64_t o = (int64_t)T + t; o < a.cap; o += kThreads) out[o] = -1;
   if (t == 0) a.count[row] = (int32_t)T;
 }
-
 }  // namespace
 
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {

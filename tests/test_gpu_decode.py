@@ -238,6 +238,32 @@ def test_select_random_ragged(seed, long):
                                 n_sink=sink, n_window=win)
 
 
+@pytest.mark.parametrize("seed", [0, 1])
+def test_select_long_rows_one_block_per_row(seed):
+    """32 long rows (40K..131072 candidates, one block per row): keys held in
+    registers, in LDS and re-read from the score row.  Quantised rows put
+    thousands of exact ties into the threshold's level-1 bin (more than the
+    bin's LDS buffer holds), continuous rows only a few hundred."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(40000, 131073, size=32).tolist()
+    lens[0] = 131072
+    rows = []
+    for b, L in enumerate(lens):
+        if b % 2:
+            rows.append((rng.integers(0, 8, L) * 0.5).astype(np.float32))
+        else:
+            rows.append((rng.standard_normal(L) * 2).astype(np.float32))
+    for rule in ({"k": 2048}, {"p": S.f32(0.9)}):
+        got = _select_rows(rows, lens, n_sink=4, n_window=64, **rule)
+        for b, L in enumerate(lens):
+            xo = rows[b].astype(np.float64)
+            core = O.select_topp(xo, rule["p"]) if "p" in rule else O.select_topk(xo, rule["k"])
+            S.check_support(got[b], xo, core, L=L, p=rule.get("p"), k=rule.get("k"),
+                            n_sink=4, n_window=64)
+            if "k" in rule:  # exact scores: ties go lowest index first on both sides
+                assert got[b].tolist() == O.with_sink_window(core, L, 4, 64).tolist()
+
+
 def test_select_pages_expand():
     rng = np.random.default_rng(5)
     lens = [64 * 40 + 17, 64 * 3]
