@@ -38,11 +38,11 @@ template <> __device__ __forceinline__ float from_f32<float>(float v) { return v
 template <> __device__ __forceinline__ bf16_raw from_f32<bf16_raw>(float v) { return f32_to_bf16(v); }
 
 // Order-preserving map of an fp32 score to uint32: a < b  <=>  key(a) < key(b);
-// -0 and +0 map to the same key.
+// -0 and +0 map to the same key (adding +0 turns -0 into +0).  Negative
+// scores have every bit flipped, the others only the sign bit.
 __device__ __forceinline__ uint32_t score_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u << 1) == 0u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;

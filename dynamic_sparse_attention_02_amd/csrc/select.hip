@@ -511,6 +511,12 @@ constexpr int kBufCap = 4096;             // candidates of the level-1 bin held 
 constexpr int kBufPerWave = kBufCap / kWaves;  // each wave fills its own segment
 static_assert(kMapWords * 2 == kBins, "the tie bitmap reuses the count histogram");
 
+// Raw buffer view of a score row: full rounds load with the round's byte
+// offset in a scalar register and the lane's in a vector one.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const float* p, int32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, n * 4, 0x00020000);
+}
+
 struct RowRes {
   uint32_t mode, prefix, thr, n_eq, need, all;
   uint64_t rem;
@@ -529,15 +535,24 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const int32_t Lt = a.seq_lens ? clamp_len(a.seq_lens[b], a.max_len) : n;
   const float* xr = a.x + (int64_t)row * a.ldx;
   const int rounds = (n + kThreads - 1) / kThreads;
+  const int full = n / kThreads;  // rounds with every lane inside the row
   const int32_t last = n > 0 ? n - 1 : 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(xr, n);
+  // score of round i (every lane inside the row) as raw bits
+  auto load_full = [&](int i) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, i * kThreads * 4, 0);
+  };
 
   __shared__ __align__(16) uint32_t hcnt[kBins];  // digit counts; after the last level, the tie bitmap
   __shared__ uint64_t hmass[TOPP ? kBins : 1];
   __shared__ uint64_t selmap[kMapWords];  // bit e: candidate e is selected
   __shared__ uint32_t kcache[kCacheRounds * kThreads];
-  __shared__ uint32_t bkey[kBufCap];
-  __shared__ int32_t bidx[kBufCap];  // after the marking, the staged page list
+  // level-1 bin candidates: keys in [0, kBufCap), indices in [kBufCap, 2 kBufCap);
+  // after the marking, the index half stages the page list
+  __shared__ uint32_t bufm[2 * kBufCap];
+  uint32_t* const bkey = bufm;
+  int32_t* const bidx = reinterpret_cast<int32_t*>(bufm + kBufCap);
   __shared__ uint32_t red32[kWaves];
   __shared__ uint64_t red64[kWaves];
   __shared__ RowRes res;
@@ -557,15 +572,22 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * kThreads + t]);
     for (int i0 = c_end; i0 < rounds; i0 += 8) {
       float v[8];
+      if (i0 + 8 <= full) {
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        v[u] = xr[e < n ? e : last];
-      }
+        for (int u = 0; u < 8; ++u) v[u] = __uint_as_float(load_full(i0 + u));
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        if (i0 + u < rounds) fn(i0 + u, e < n ? score_key(v[u]) : 0u);
+        for (int u = 0; u < 8; ++u) fn(i0 + u, score_key(v[u]));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t e = (i0 + u) * kThreads + t;
+          v[u] = xr[e < n ? e : last];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t e = (i0 + u) * kThreads + t;
+          if (i0 + u < rounds) fn(i0 + u, e < n ? score_key(v[u]) : 0u);
+        }
       }
     }
   };
@@ -607,21 +629,25 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     hcnt[i] = 0;
     if (TOPP) hmass[i] = 0;
   }
+  for (int i = t; i < rounds * kWaves; i += kThreads) selmap[i] = 0;
   __syncthreads();
 
   // ---- load: keys to registers and LDS; top-k builds the level-1 histogram,
   // top-p takes the row maximum (the mass reference) first ----
   uint32_t mk = 0;
   // top-k: padding lanes (key 0) are counted into bin 0 and taken out below
-  auto take = [&](int32_t e, uint32_t key) {
+  auto take = [&](uint32_t key) {
     if (TOPP) mk = key > mk ? key : mk;
     else hist_add(key, 1, 0, 0.f);
   };
   // every register round's load is issued before the first is used (raw
-  // score bits; lanes past the row read its last score)
+  // score bits; in the row's last round, lanes past it read its last score)
 #pragma unroll
   for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
-    if (i0 < rounds) {
+    if (i0 + 8 <= full) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) keys[i0 + u] = load_full(i0 + u);
+    } else if (i0 < rounds) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int32_t e = (i0 + u) * kThreads + t;
@@ -631,12 +657,18 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   }
 #pragma unroll
   for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
-    if (i0 < rounds) {
+    if (i0 + 8 <= full) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        keys[i0 + u] = score_key(__uint_as_float(keys[i0 + u]));
+        take(keys[i0 + u]);
+      }
+    } else if (i0 < rounds) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int32_t e = (i0 + u) * kThreads + t;
         keys[i0 + u] = e < n ? score_key(__uint_as_float(keys[i0 + u])) : 0u;
-        if (i0 + u < rounds) take(e, keys[i0 + u]);
+        if (i0 + u < rounds) take(keys[i0 + u]);
       }
     } else {
 #pragma unroll
@@ -645,18 +677,29 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   }
   for (int i0 = kRowRegs; i0 < rounds; i0 += 16) {
     float v[16];
+    if (i0 + 16 <= full) {
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int32_t e = (i0 + u) * kThreads + t;
-      v[u] = xr[e < n ? e : last];
-    }
+      for (int u = 0; u < 16; ++u) v[u] = __uint_as_float(load_full(i0 + u));
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int32_t e = (i0 + u) * kThreads + t;
-      if (i0 + u < rounds) {
-        const uint32_t k = e < n ? score_key(v[u]) : 0u;
+      for (int u = 0; u < 16; ++u) {
+        const uint32_t k = score_key(v[u]);
         if (i0 + u < cached_end) kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
-        take(e, k);
+        take(k);
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        v[u] = xr[e < n ? e : last];
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int32_t e = (i0 + u) * kThreads + t;
+        if (i0 + u < rounds) {
+          const uint32_t k = e < n ? score_key(v[u]) : 0u;
+          if (i0 + u < cached_end) kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
+          take(k);
+        }
       }
     }
   }
@@ -785,31 +828,38 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   if (res.mode == kSearching) resolve(1);
   const uint32_t mode1 = res.mode, thr1 = res.thr, B1 = res.prefix;
   if (mode1 == kSearching) {
-    // bins above B1 are in; bin B1 goes to this wave's buffer segment
+    // bins above B1 are in; bin B1 goes to this wave's buffer segment.  The
+    // bitmap starts cleared, so a round with no key in or above bin B1 costs
+    // one compare.
     uint32_t wcnt = 0;  // wave-uniform fill of the segment
-    for_all([&](int i, uint32_t k) {
-      const int32_t e = i * kThreads + t;
-      const bool valid = e < n;
-      const uint32_t d = k >> 20;
-      const uint64_t m = __ballot(valid && d > B1);
-      if (lane == 0) selmap[i * kWaves + wave] = m;
-      const bool in = valid && d == B1;
-      const uint64_t mb = __ballot(in);
+    const uint32_t lo1 = B1 << 20, top1 = lo1 | 0xfffffu;  // bin B1 = [lo1, top1]
+    uint64_t* const smap = selmap + wave;
+    auto filter = [&](int i, uint32_t k, bool hi) {  // hi: valid and key >= lo1
+      const uint64_t mh = __builtin_amdgcn_ballot_w64(hi);
+      if (mh == 0) return;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(k > top1) & mh;
+      if (m && lane == 0) smap[i * kWaves] = m;
+      const uint64_t mb = mh & ~m;
       if (mb) {
-        const uint32_t p = wcnt + (uint32_t)__popcll(mb & lt_mask);
-        if (in && p < (uint32_t)kBufPerWave) {
+        const uint32_t p = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, wcnt));
+        if (hi && k <= top1 && p < (uint32_t)kBufPerWave) {
           bkey[wave * kBufPerWave + p] = k;
-          bidx[wave * kBufPerWave + p] = e;
+          bidx[wave * kBufPerWave + p] = i * kThreads + t;
         }
         wcnt += (uint32_t)__popcll(mb);
       }
-    });
+    };
+    if (lo1 > 0)  // padding lanes (key 0) lie below the bin
+      for_all([&](int i, uint32_t k) { filter(i, k, k >= lo1); });
+    else
+      for_all([&](int i, uint32_t k) { filter(i, k, i * kThreads + t < n); });
     if (lane == 0) s_wcnt[wave] = wcnt;
   } else {
     // key >= thr1 decides every candidate
     for_all([&](int i, uint32_t k) {
       const uint64_t m = __ballot(i * kThreads + t < n && k >= thr1);
-      if (lane == 0) selmap[i * kWaves + wave] = m;
+      if (lane == 0 && m) selmap[i * kWaves + wave] = m;
     });
   }
   __syncthreads();
