@@ -81,8 +81,8 @@ __device__ __forceinline__ int32_t n_cand_of(const SelectArgs& a, int row) {
   return a.unit == 1 ? L : (L + a.unit - 1) / a.unit;
 }
 
-// Exclusive block scan (kThreads threads) of an unsigned value.
-template <typename U>
+// Exclusive block scan (NW waves) of an unsigned value.
+template <typename U, int NW = kWaves>
 __device__ __forceinline__ U block_excl_scan(U v, U* lds4, U& total) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   U inc = v;
@@ -92,7 +92,7 @@ __device__ __forceinline__ U block_excl_scan(U v, U* lds4, U& total) {
   __syncthreads();
   U off = 0, tot = 0;
 #pragma unroll
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < NW; ++i) {
     U s = lds4[i];
     if (i < w) off += s;
     tot += s;
@@ -505,10 +505,10 @@ constexpr int kRowRegsTopk = 48;
 // histogram, so more LDS is free for keys)
 constexpr int kCacheRoundsTopk = 22;
 constexpr int kCacheRoundsTopp = 14;
+constexpr int kCacheRoundsHalf = 7;  // 512-thread top-k blocks: two per CU share its LDS
 constexpr int kRowMax = 131072;
 constexpr int kMapWords = kRowMax / 64;   // 64-bit bitmap words: one per (round, wave)
 constexpr int kBufCap = 4096;             // candidates of the level-1 bin held in LDS
-constexpr int kBufPerWave = kBufCap / kWaves;  // each wave fills its own segment
 static_assert(kMapWords * 2 == kBins, "the tie bitmap reuses the count histogram");
 
 // Raw buffer view of a score row: full rounds load with the round's byte
@@ -522,74 +522,86 @@ struct RowRes {
   uint64_t rem;
 };
 
-// RR: register-resident rounds (more only pays for rows that would otherwise
-// re-read scores: top-k with more than (32 + LDS rounds) * kThreads candidates).
-template <bool TOPP, int RR>
-__global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
+// RR: register-resident rounds; NT: threads per block (1024: one block per
+// CU; 512: two, for top-k, whose blocks fit twice into the LDS).
+template <bool TOPP, int RR, int NT>
+__global__ void __launch_bounds__(NT) k_select_row(SelectArgs a) {
+  constexpr int NW = NT / 64;
+  constexpr int WPT = (kRowMax / 32) / NT;    // 32-bit bitmap words per thread
+  constexpr int kBufPerW = kBufCap / NW;      // each wave fills its own buffer segment
   constexpr int kRowRegs = RR;
-  constexpr int kCacheRounds = TOPP ? kCacheRoundsTopp : kCacheRoundsTopk;
+  constexpr int kCacheRounds =
+      NT == 512 ? kCacheRoundsHalf : (TOPP ? kCacheRoundsTopp : kCacheRoundsTopk);
   const int row = blockIdx.x;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int32_t n = n_cand_of(a, row);
   const int b = row / a.Hkv;
   const int32_t Lt = a.seq_lens ? clamp_len(a.seq_lens[b], a.max_len) : n;
   const float* xr = a.x + (int64_t)row * a.ldx;
-  const int rounds = (n + kThreads - 1) / kThreads;
-  const int full = n / kThreads;  // rounds with every lane inside the row
+  const int rounds = (n + NT - 1) / NT;
+  const int full = n / NT;  // rounds with every lane inside the row
   const int32_t last = n > 0 ? n - 1 : 0;
   const uint64_t lt_mask = (1ull << lane) - 1ull;
   const __amdgpu_buffer_rsrc_t rs = row_rsrc(xr, n);
   // score of round i (every lane inside the row) as raw bits
   auto load_full = [&](int i) -> uint32_t {
-    return __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, i * kThreads * 4, 0);
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, i * NT * 4, 0);
   };
 
   __shared__ __align__(16) uint32_t hcnt[kBins];  // digit counts; after the last level, the tie bitmap
   __shared__ uint64_t hmass[TOPP ? kBins : 1];
   __shared__ uint64_t selmap[kMapWords];  // bit e: candidate e is selected
-  __shared__ uint32_t kcache[kCacheRounds * kThreads];
+  __shared__ uint32_t kcache[kCacheRounds * NT];
   // level-1 bin candidates: keys in [0, kBufCap), indices in [kBufCap, 2 kBufCap);
   // after the marking, the index half stages the page list
   __shared__ uint32_t bufm[2 * kBufCap];
   uint32_t* const bkey = bufm;
   int32_t* const bidx = reinterpret_cast<int32_t*>(bufm + kBufCap);
-  __shared__ uint32_t red32[kWaves];
-  __shared__ uint64_t red64[kWaves];
+  __shared__ uint32_t red32[NW];
+  __shared__ uint64_t red64[NW];
   __shared__ RowRes res;
   __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef, s_last;
-  __shared__ uint32_t s_wcnt[kWaves];
+  __shared__ uint32_t s_wcnt[NW];
   __shared__ uint64_t s_hit_mass, s_hit_mbef;
   uint32_t* const sel32 = reinterpret_cast<uint32_t*>(selmap);
   uint32_t* const tie32 = hcnt;
   const int cached_end = kRowRegs + kCacheRounds;  // rounds [kRowRegs, cached_end) live in LDS
 
-  // Visit rounds [kRowRegs, rounds): LDS-cached rounds one at a time, then
-  // the score-row rounds 8 at a time with their loads issued together
-  // (branch-free: an out-of-range lane reads the row's last score and gets
-  // key 0).
+  // Full rounds [ib, ie) from the score row, two batches of 8 in turn: one
+  // batch's loads are in flight while the other is consumed (round indices
+  // past ie are clamped to ie - 1, so every load is issued unconditionally).
+  // fn(i, raw score bits).
+  auto stream_full = [&](int ib, int ie, auto&& fn) {
+    if (ib >= ie) return;
+    uint32_t va[8], vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) va[u] = load_full(min(ib + u, ie - 1));
+    for (int i0 = ib; i0 < ie; i0 += 16) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vb[u] = load_full(min(i0 + 8 + u, ie - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < ie) fn(i0 + u, va[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) va[u] = load_full(min(i0 + 16 + u, ie - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 8 + u < ie) fn(i0 + 8 + u, vb[u]);
+    }
+  };
+  // The row's partial last round (round `full`), lanes past the row read its
+  // last score and get key 0.
+  auto partial_key = [&]() -> uint32_t {
+    const int32_t e = full * NT + t;
+    const float v = xr[e < n ? e : last];
+    return e < n ? score_key(v) : 0u;
+  };
+  // Visit rounds [kRowRegs, rounds): LDS-cached rounds, then the score row.
   auto for_rounds = [&](auto&& fn) {
     const int c_end = rounds < cached_end ? rounds : cached_end;
-    for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * kThreads + t]);
-    for (int i0 = c_end; i0 < rounds; i0 += 8) {
-      float v[8];
-      if (i0 + 8 <= full) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = __uint_as_float(load_full(i0 + u));
-#pragma unroll
-        for (int u = 0; u < 8; ++u) fn(i0 + u, score_key(v[u]));
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t e = (i0 + u) * kThreads + t;
-          v[u] = xr[e < n ? e : last];
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int32_t e = (i0 + u) * kThreads + t;
-          if (i0 + u < rounds) fn(i0 + u, e < n ? score_key(v[u]) : 0u);
-        }
-      }
-    }
+    for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * NT + t]);
+    stream_full(c_end, full, [&](int i, uint32_t raw) { fn(i, score_key(__uint_as_float(raw))); });
+    if (rounds > full && full >= c_end) fn(full, partial_key());
   };
   uint32_t keys[kRowRegs];
   // every round (wave-uniform calls; fn checks the candidate's validity)
@@ -625,11 +637,11 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     if (n == 0 || (a.is_topk ? (a.k >= n) : (a.p >= 1.0f))) res.mode = kTakeGE;
     s_last = 0;
   }
-  for (int i = t; i < kBins; i += kThreads) {
+  for (int i = t; i < kBins; i += NT) {
     hcnt[i] = 0;
     if (TOPP) hmass[i] = 0;
   }
-  for (int i = t; i < rounds * kWaves; i += kThreads) selmap[i] = 0;
+  for (int i = t; i < rounds * NW; i += NT) selmap[i] = 0;
   __syncthreads();
 
   // ---- load: keys to registers and LDS; top-k builds the level-1 histogram,
@@ -650,7 +662,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     } else if (i0 < rounds) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
+        const int32_t e = (i0 + u) * NT + t;
         keys[i0 + u] = __float_as_uint(xr[e < n ? e : last]);
       }
     }
@@ -666,7 +678,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     } else if (i0 < rounds) {
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
+        const int32_t e = (i0 + u) * NT + t;
         keys[i0 + u] = e < n ? score_key(__uint_as_float(keys[i0 + u])) : 0u;
         if (i0 + u < rounds) take(keys[i0 + u]);
       }
@@ -675,35 +687,14 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       for (int u = 0; u < 8; ++u) keys[i0 + u] = 0u;
     }
   }
-  for (int i0 = kRowRegs; i0 < rounds; i0 += 16) {
-    float v[16];
-    if (i0 + 16 <= full) {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) v[u] = __uint_as_float(load_full(i0 + u));
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const uint32_t k = score_key(v[u]);
-        if (i0 + u < cached_end) kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
-        take(k);
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        v[u] = xr[e < n ? e : last];
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int32_t e = (i0 + u) * kThreads + t;
-        if (i0 + u < rounds) {
-          const uint32_t k = e < n ? score_key(v[u]) : 0u;
-          if (i0 + u < cached_end) kcache[(i0 + u - kRowRegs) * kThreads + t] = k;
-          take(k);
-        }
-      }
-    }
-  }
-  if (!TOPP && t == 0) atomicSub(&hcnt[0], (uint32_t)(rounds * kThreads - n));
+  // later rounds: LDS cache, then keys only for the histogram / maximum
+  auto keep = [&](int i, uint32_t k) {
+    if (i < cached_end) kcache[(i - kRowRegs) * NT + t] = k;
+    take(k);
+  };
+  stream_full(kRowRegs, full, [&](int i, uint32_t raw) { keep(i, score_key(__uint_as_float(raw))); });
+  if (rounds > full && full >= kRowRegs) keep(full, partial_key());
+  if (!TOPP && t == 0) atomicSub(&hcnt[0], (uint32_t)(rounds * NT - n));
   float mx = 0.f;
   if (TOPP) {
     mk = wave_max_u32(mk);
@@ -713,10 +704,10 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   if (TOPP) {
     uint32_t M = 0;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) M = red32[i] > M ? red32[i] : M;
+    for (int i = 0; i < NW; ++i) M = red32[i] > M ? red32[i] : M;
     mx = key_score(M);
     for_all([&](int i, uint32_t k) {
-      if (i * kThreads + t < n) hist_add(k, 1, 0, mx);
+      if (i * NT + t < n) hist_add(k, 1, 0, mx);
     });
     __syncthreads();
   }
@@ -730,7 +721,7 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     const uint32_t pre = res.prefix;
     // block scan over bins in descending order: thread t owns positions
     // [t*per, (t+1)*per), position q <-> bin NB-1-q
-    const int per = NB / kThreads > 0 ? NB / kThreads : 1;
+    const int per = NB / NT > 0 ? NB / NT : 1;
     const bool owns = t * per < NB;
     uint32_t cl = 0;
     uint64_t ml = 0;
@@ -742,8 +733,8 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       }
     uint32_t ctot;
     uint64_t mtot = 0;
-    const uint32_t cb0 = block_excl_scan<uint32_t>(cl, red32, ctot);
-    const uint64_t mb0 = TOPP ? block_excl_scan<uint64_t>(ml, red64, mtot) : 0ull;
+    const uint32_t cb0 = block_excl_scan<uint32_t, NW>(cl, red32, ctot);
+    const uint64_t mb0 = TOPP ? block_excl_scan<uint64_t, NW>(ml, red64, mtot) : 0ull;
     uint64_t target = res.rem;
     if (TOPP && level == 1) {
       uint64_t tc = (uint64_t)ceil((double)a.p * (double)mtot);
@@ -838,14 +829,14 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       const uint64_t mh = __builtin_amdgcn_ballot_w64(hi);
       if (mh == 0) return;
       const uint64_t m = __builtin_amdgcn_ballot_w64(k > top1) & mh;
-      if (m && lane == 0) smap[i * kWaves] = m;
+      if (m && lane == 0) smap[i * NW] = m;
       const uint64_t mb = mh & ~m;
       if (mb) {
         const uint32_t p = __builtin_amdgcn_mbcnt_hi(
             (uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, wcnt));
-        if (hi && k <= top1 && p < (uint32_t)kBufPerWave) {
-          bkey[wave * kBufPerWave + p] = k;
-          bidx[wave * kBufPerWave + p] = i * kThreads + t;
+        if (hi && k <= top1 && p < (uint32_t)kBufPerW) {
+          bkey[wave * kBufPerW + p] = k;
+          bidx[wave * kBufPerW + p] = i * NT + t;
         }
         wcnt += (uint32_t)__popcll(mb);
       }
@@ -853,40 +844,40 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     if (lo1 > 0)  // padding lanes (key 0) lie below the bin
       for_all([&](int i, uint32_t k) { filter(i, k, k >= lo1); });
     else
-      for_all([&](int i, uint32_t k) { filter(i, k, i * kThreads + t < n); });
+      for_all([&](int i, uint32_t k) { filter(i, k, i * NT + t < n); });
     if (lane == 0) s_wcnt[wave] = wcnt;
   } else {
     // key >= thr1 decides every candidate
     for_all([&](int i, uint32_t k) {
-      const uint64_t m = __ballot(i * kThreads + t < n && k >= thr1);
-      if (lane == 0 && m) selmap[i * kWaves + wave] = m;
+      const uint64_t m = __ballot(i * NT + t < n && k >= thr1);
+      if (lane == 0 && m) selmap[i * NW + wave] = m;
     });
   }
   __syncthreads();
   bool use_buf = true;
   if (mode1 == kSearching) {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) use_buf = use_buf && s_wcnt[w] <= (uint32_t)kBufPerWave;
+    for (int w = 0; w < NW; ++w) use_buf = use_buf && s_wcnt[w] <= (uint32_t)kBufPerW;
   }
   // buffer slot j holds a candidate when it lies inside its wave's fill
-  auto in_buf = [&](int j) { return (uint32_t)(j % kBufPerWave) < s_wcnt[j / kBufPerWave]; };
+  auto in_buf = [&](int j) { return (uint32_t)(j % kBufPerW) < s_wcnt[j / kBufPerW]; };
 
   // ---- levels 2 and 3 over the bin's candidates ----
   for (int level = 2; level <= 3; ++level) {
     if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
     const int NB = level == 3 ? 256 : kBins;
     const uint32_t pre = res.prefix;
-    for (int i = t; i < NB; i += kThreads) {
+    for (int i = t; i < NB; i += NT) {
       hcnt[i] = 0;
       if (TOPP) hmass[i] = 0;
     }
     __syncthreads();
     if (use_buf) {
-      for (int j = t; j < kBufCap; j += kThreads)
+      for (int j = t; j < kBufCap; j += NT)
         if (in_buf(j)) hist_add(bkey[j], level, pre, mx);
     } else {
       for_all([&](int i, uint32_t k) {
-        if (i * kThreads + t < n) hist_add(k, level, pre, mx);
+        if (i * NT + t < n) hist_add(k, level, pre, mx);
       });
     }
     __syncthreads();
@@ -899,12 +890,12 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const bool ties = mode1 == kSearching && mode == kTakeTies;
   const int nw = (n + 31) >> 5;  // 32-bit bitmap words of the row
   if (ties) {
-    for (int i = t; i < nw; i += kThreads) tie32[i] = 0;
+    for (int i = t; i < nw; i += NT) tie32[i] = 0;
     __syncthreads();
   }
   if (mode1 == kSearching) {
     if (use_buf) {
-      for (int j = t; j < kBufCap; j += kThreads) {
+      for (int j = t; j < kBufCap; j += NT) {
         if (!in_buf(j)) continue;
         const uint32_t k = bkey[j];
         const int32_t e = bidx[j];
@@ -913,35 +904,35 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
       }
     } else {
       for_all([&](int i, uint32_t k) {
-        const int32_t e = i * kThreads + t;
+        const int32_t e = i * NT + t;
         const bool in = e < n && (k >> 20) == B1;
         const uint64_t ms = __ballot(in && (k > thr || (mode == kTakeGE && k == thr)));
         const uint64_t me = __ballot(in && ties && k == thr);
         if (lane == 0) {
-          selmap[i * kWaves + wave] |= ms;
-          if (ties) reinterpret_cast<uint64_t*>(tie32)[i * kWaves + wave] = me;
+          selmap[i * NW + wave] |= ms;
+          if (ties) reinterpret_cast<uint64_t*>(tie32)[i * NW + wave] = me;
         }
       });
     }
     __syncthreads();
   }
 
-  // ---- ordered compaction: thread t owns bitmap words [4t, 4t + 4) ----
-  uint32_t sw[4];
+  // ---- ordered compaction: thread t owns bitmap words [WPT t, WPT (t + 1)) ----
+  uint32_t sw[WPT];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) sw[w] = 4 * t + w < nw ? sel32[4 * t + w] : 0u;
+  for (int w = 0; w < WPT; ++w) sw[w] = WPT * t + w < nw ? sel32[WPT * t + w] : 0u;
   if (ties) {  // the n_eq lowest-index keys equal to the threshold
-    uint32_t tw[4], c = 0;
+    uint32_t tw[WPT], c = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      tw[w] = 4 * t + w < nw ? tie32[4 * t + w] : 0u;
+    for (int w = 0; w < WPT; ++w) {
+      tw[w] = WPT * t + w < nw ? tie32[WPT * t + w] : 0u;
       c += (uint32_t)__popc(tw[w]);
     }
     uint32_t tot;
-    const uint32_t before = block_excl_scan<uint32_t>(c, red32, tot);
+    const uint32_t before = block_excl_scan<uint32_t, NW>(c, red32, tot);
     uint32_t left = before < n_eq ? n_eq - before : 0u;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < WPT; ++w) {
       uint32_t bits = tw[w], keep = 0;
       while (bits && left) {
         keep |= bits & (0u - bits);
@@ -956,8 +947,8 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
   const int32_t last_w = Lt - (n - 1) * unit;  // tokens of the last candidate (unit > 1)
   uint32_t c = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int widx = 4 * t + w;
+  for (int w = 0; w < WPT; ++w) {
+    const int widx = WPT * t + w;
     if (widx < nw) {
       const int32_t lo = widx * 32;
       const uint32_t vm = n - lo >= 32 ? ~0u : ((1u << (n - lo)) - 1u);
@@ -973,18 +964,18 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     c += (uint32_t)__popc(sw[w]);
   }
   uint32_t total;
-  uint32_t rank = block_excl_scan<uint32_t>(c, red32, total);  // barriers publish s_last
+  uint32_t rank = block_excl_scan<uint32_t, NW>(c, red32, total);  // barriers publish s_last
   int32_t* out = a.idx + (int64_t)row * a.cap;
   uint32_t T;
   if (unit == 1) {
     T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < WPT; ++w) {
       uint32_t bits = sw[w];
       while (bits) {
         const int j = __ffs(bits) - 1;
         bits &= bits - 1u;
-        if (rank < (uint32_t)a.cap) out[rank] = (4 * t + w) * 32 + j;
+        if (rank < (uint32_t)a.cap) out[rank] = (WPT * t + w) * 32 + j;
         ++rank;
       }
     }
@@ -993,10 +984,10 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     T = tokens < (uint32_t)a.cap ? tokens : (uint32_t)a.cap;
     const bool staged = total < (uint32_t)kBufCap;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < WPT; ++w) {
       uint32_t bits = sw[w];
       while (bits) {
-        const int32_t e = (4 * t + w) * 32 + __ffs(bits) - 1;
+        const int32_t e = (WPT * t + w) * 32 + __ffs(bits) - 1;
         bits &= bits - 1u;
         if (staged) {
           bidx[rank] = e;
@@ -1011,11 +1002,11 @@ __global__ void __launch_bounds__(kThreads) k_select_row(SelectArgs a) {
     }
     if (staged) {  // block-uniform
       __syncthreads();
-      for (uint32_t o = t; o < T; o += kThreads)
+      for (uint32_t o = t; o < T; o += NT)
         out[o] = (bidx[o >> ushift] << ushift) + (int32_t)(o & (uint32_t)(unit - 1));
     }
   }
-  for (int64_t o = (int64_t)T + t; o < a.cap; o += kThreads) out[o] = -1;
+  for (int64_t o = (int64_t)T + t; o < a.cap; o += NT) out[o] = -1;
   if (t == 0) a.count[row] = (int32_t)T;
 }
 }  // namespace
@@ -1038,10 +1029,8 @@ hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   // when there are enough rows to fill the chip; few long rows are split
   // over many blocks instead.
   if (a.max_cand <= kRowRegsTopp * kThreads || (a.max_cand <= kRowMax && a.rows >= 32)) {
-    if (!a.is_topk) k_select_row<true, kRowRegsTopp><<<a.rows, kThreads, 0, st>>>(a);
-    else if (a.max_cand > (kRowRegsTopp + kCacheRoundsTopk) * kThreads)
-      k_select_row<false, kRowRegsTopk><<<a.rows, kThreads, 0, st>>>(a);
-    else k_select_row<false, kRowRegsTopp><<<a.rows, kThreads, 0, st>>>(a);
+    if (!a.is_topk) k_select_row<true, kRowRegsTopp, kThreads><<<a.rows, kThreads, 0, st>>>(a);
+    else k_select_row<false, kRowRegsTopk, 512><<<a.rows, 512, 0, st>>>(a);
     return hipGetLastError();
   }
   const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
