@@ -121,7 +121,10 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
 // ---------------------------------------------------------------------------
 constexpr int kRowsT = 32;
 
-template <typename T>
+// K16: instead of the fp32 score, the top 16 bits of its order-preserving key,
+// two candidates per 32-bit word (ldx then counts words): candidate j in
+// word (j / 128) * 64 + j % 64, low half for j % 128 < 64, else high.
+template <typename T, bool K16>
 __global__ void __launch_bounds__(256)
 k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
                  const float* __restrict__ qcb, int32_t blk0, int32_t blk1, int32_t bsel,
@@ -161,7 +164,12 @@ k_prefill_scores(const T* __restrict__ kidx, const int32_t* __restrict__ pt,
     float a = 0.f;
 #pragma unroll
     for (int c = 0; c < kRank; ++c) a = fmaf(qv[c], k[c], a);
-    x[((int64_t)(bb - blk0) * s.Hkv + g) * ldx + j] = a;
+    const int64_t r = (int64_t)(bb - blk0) * s.Hkv + g;
+    if (K16)
+      reinterpret_cast<uint16_t*>(x)[r * 2 * ldx + 2 * ((j >> 7) * 64 + (j & 63)) + ((j >> 6) & 1)] =
+          (uint16_t)(score_key(a) >> 16);
+    else
+      x[r * ldx + j] = a;
   }
 }
 
@@ -675,6 +683,9 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     const int b1 = b0 + (int)P.slab < P.nblk ? b0 + (int)P.slab : P.nblk;
     const int64_t cand_hi = (int64_t)b_sel * (b1 - 1) + P.self;  // candidates of the last row
     const int64_t ldx = cand_hi > 0 ? cand_hi : 1;
+    // logit scores go to the selection as 16-bit keys (exact scores of the
+    // threshold bin are recomputed there) when its one-block rows take them
+    const bool key16 = !probs && ldx <= kSelectRowMax;
     if (probs) {
       const int ntile = (int)((cand_hi + 255) / 256);
       dim3 g2(ntile > 0 ? ntile : 1, (b1 - b0 + kRowsQ - 1) / kRowsQ, s.Hkv);
@@ -705,18 +716,36 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
 #undef SA_HP
     } else {
       dim3 g2((unsigned)((ldx + 255) / 256), (b1 - b0 + kRowsT - 1) / kRowsT, s.Hkv);
-      if (bf)
-        k_prefill_scores<bf16_raw><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table,
-                                                       qv, b0, b1, b_sel, P.self, s, xs, ldx);
-      else
-        k_prefill_scores<float><<<g2, 256, 0, st>>>((const float*)kidx_pool, pg.page_table, qv,
-                                                    b0, b1, b_sel, P.self, s, xs, ldx);
+      const int64_t ldw = ((ldx + 127) / 128) * 64;  // 16-bit keys: words per row
+      if (key16) {
+        if (bf)
+          k_prefill_scores<bf16_raw, true><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool,
+              pg.page_table, qv, b0, b1, b_sel, P.self, s, xs, ldw);
+        else
+          k_prefill_scores<float, true><<<g2, 256, 0, st>>>((const float*)kidx_pool,
+              pg.page_table, qv, b0, b1, b_sel, P.self, s, xs, ldw);
+      } else {
+        if (bf)
+          k_prefill_scores<bf16_raw, false><<<g2, 256, 0, st>>>((const bf16_raw*)kidx_pool,
+              pg.page_table, qv, b0, b1, b_sel, P.self, s, xs, ldx);
+        else
+          k_prefill_scores<float, false><<<g2, 256, 0, st>>>((const float*)kidx_pool,
+              pg.page_table, qv, b0, b1, b_sel, P.self, s, xs, ldx);
+      }
     }
     SelectArgs a{};
     a.x = xs;
-    a.ldx = ldx;
+    a.ldx = key16 ? ((ldx + 127) / 128) * 64 : ldx;
     a.seq_lens = nullptr;
     a.rows = (b1 - b0) * s.Hkv;
+    if (key16) {
+      a.key16 = 1;
+      a.qcb = qv;
+      a.kidx = kidx_pool;
+      a.kidx_bf16 = bf ? 1 : 0;
+      a.pt = pg.page_table;
+      a.n_pool_pages = s.n_pool_pages;
+    }
     a.Hkv = s.Hkv;
     a.max_len = n_tokens;
     a.unit = 1;

@@ -216,7 +216,18 @@ struct SelectArgs {
   int32_t prefill_bsel;
   int32_t prefill_blk0;
   int32_t prefill_self;     // per-query rows: the own token is a candidate too
+  // 16-bit key rows (prefill top-k, rows of at most kSelectRowMax candidates):
+  // x then holds ldx 32-bit words per row, candidate c's top 16 key bits in
+  // word (c / 128) * 64 + c % 64 (low half for c % 128 < 64, else high), and
+  // the threshold bin's exact scores are recomputed from qcb and kidx.
+  int32_t key16;
+  const float* qcb;         // [blocks][Hkv][16] block-mean low-rank queries
+  const void* kidx;         // indexer key pool [pages][Hkv][64][16]
+  int32_t kidx_bf16;
+  const int32_t* pt;        // the sequence's page-table row
+  int64_t n_pool_pages;
 };
+constexpr int kSelectRowMax = 131072;  // longest row the one-block-per-row selection takes
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 

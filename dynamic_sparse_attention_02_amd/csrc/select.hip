@@ -506,7 +506,7 @@ constexpr int kRowRegsTopk = 48;
 constexpr int kCacheRoundsTopk = 22;
 constexpr int kCacheRoundsTopp = 14;
 constexpr int kCacheRoundsHalf = 7;  // 512-thread top-k blocks: two per CU share its LDS
-constexpr int kRowMax = 131072;
+constexpr int kRowMax = kSelectRowMax;
 constexpr int kMapWords = kRowMax / 64;   // 64-bit bitmap words: one per (round, wave)
 constexpr int kBufCap = 4096;             // candidates of the level-1 bin held in LDS
 static_assert(kMapWords * 2 == kBins, "the tie bitmap reuses the count histogram");
@@ -1009,6 +1009,406 @@ __global__ void __launch_bounds__(NT) k_select_row(SelectArgs a) {
   for (int64_t o = (int64_t)T + t; o < a.cap; o += NT) out[o] = -1;
   if (t == 0) a.count[row] = (int32_t)T;
 }
+// ---------------------------------------------------------------------------
+// Row selection over 16-bit keys (prefill top-k).  The score rows hold the
+// top 16 bits of each candidate's order-preserving key, two per 32-bit word:
+// in every 128-candidate block, candidate c sits in word (c / 128) * 64 +
+// c % 64, low half for c % 128 < 64, high half otherwise, so the 64 lanes of
+// a wave reading 64 consecutive words hold the block's first 64 candidates in
+// their low halves and the next 64 in their high halves: each half gives one
+// whole bitmap word per ballot.  The 16 bits hold the level-1 digit (12 bits)
+// exactly, so the load and filter passes are those of k_select_row; the
+// candidates of the threshold bin get their exact fp32 score recomputed from
+// the block's mean query and the indexer keys (same products in the same
+// order as the score kernel, so the same float), and levels 2-3, the ties
+// and the marking run on exact keys.
+// ---------------------------------------------------------------------------
+template <int RR, int NT>
+__global__ void __launch_bounds__(NT) k_select_row16(SelectArgs a) {
+  constexpr int NW = NT / 64;
+  constexpr int WPT = (kRowMax / 32) / NT;    // 32-bit bitmap words per thread
+  constexpr int kBufPerW = kBufCap / NW;      // each wave fills its own buffer segment
+  constexpr int kRowRegs = RR;
+  constexpr int kCacheRounds = kCacheRoundsHalf;
+  const int row = blockIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int32_t n = n_cand_of(a, row);
+  const uint32_t* xr = reinterpret_cast<const uint32_t*>(a.x) + (int64_t)row * a.ldx;  // ldx: words
+  const int nwords = ((n + 127) / 128) * 64;
+  const int rounds = (nwords + NT - 1) / NT;
+  const int full = n / (2 * NT);  // rounds whose 2 * NT candidates all lie inside the row
+  const uint64_t lt_mask = (1ull << lane) - 1ull;
+  const __amdgpu_buffer_rsrc_t rs = row_rsrc(reinterpret_cast<const float*>(xr), nwords);
+  auto load_full = [&](int i) -> uint32_t {
+    return __builtin_amdgcn_raw_buffer_load_b32(rs, t * 4, i * NT * 4, 0);
+  };
+  // candidate of the low half of round i in this lane (the high half is +64)
+  auto cand_lo = [&](int i) -> int32_t { return 2 * (i * NT + wave * 64) + lane; };
+
+  __shared__ __align__(16) uint32_t hcnt[kBins];  // digit counts; after the last level, the tie bitmap
+  __shared__ uint64_t selmap[kMapWords];          // bit c: candidate c is selected
+  __shared__ uint32_t kcache[kCacheRounds * NT];
+  __shared__ uint32_t bufm[2 * kBufCap];
+  uint32_t* const bkey = bufm;
+  int32_t* const bidx = reinterpret_cast<int32_t*>(bufm + kBufCap);
+  __shared__ uint32_t red32[NW];
+  __shared__ RowRes res;
+  __shared__ uint32_t s_hit_bin, s_hit_cnt, s_hit_cbef;
+  __shared__ uint32_t s_wcnt[NW];
+  __shared__ float s_q[kRank];
+  uint32_t* const sel32 = reinterpret_cast<uint32_t*>(selmap);
+  uint32_t* const tie32 = hcnt;
+  const int cached_end = kRowRegs + kCacheRounds;
+
+  // the row's partial round (round `full`, if any): halves past the row read 0
+  auto partial_word = [&]() -> uint32_t {
+    const int32_t w = full * NT + t;
+    const uint32_t v = w < nwords ? xr[w] : 0u;
+    const int32_t c = cand_lo(full);
+    return (c < n ? (v & 0xffffu) : 0u) | (c + 64 < n ? (v & 0xffff0000u) : 0u);
+  };
+  auto stream_full = [&](int ib, int ie, auto&& fn) {
+    if (ib >= ie) return;
+    uint32_t va[8], vb[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) va[u] = load_full(min(ib + u, ie - 1));
+    for (int i0 = ib; i0 < ie; i0 += 16) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) vb[u] = load_full(min(i0 + 8 + u, ie - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < ie) fn(i0 + u, va[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) va[u] = load_full(min(i0 + 16 + u, ie - 1));
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + 8 + u < ie) fn(i0 + 8 + u, vb[u]);
+    }
+  };
+  auto for_rounds = [&](auto&& fn) {
+    const int c_end = rounds < cached_end ? rounds : cached_end;
+    for (int i = kRowRegs; i < c_end; ++i) fn(i, kcache[(i - kRowRegs) * NT + t]);
+    stream_full(c_end, full, fn);
+    if (rounds > full && full >= c_end) fn(full, partial_word());
+  };
+  uint32_t words[kRowRegs];
+  auto for_all = [&](auto&& fn) {  // fn(round, packed word); halves past the row are 0
+#pragma unroll
+    for (int i = 0; i < kRowRegs; ++i)
+      if (i < rounds) fn(i, words[i]);
+    for_rounds(fn);
+  };
+  // exact key of candidate c: the score kernel's product of the block's mean
+  // query with the candidate's indexer key
+  const int g = row % a.Hkv;
+  auto exact_key = [&](int32_t c) -> uint32_t {
+    const int64_t page = clamp_page(a.pt[c >> 6], a.n_pool_pages);
+    const int64_t off = ((page * a.Hkv + g) * kPage + (c & 63)) * kRank;
+    float s = 0.f;
+    if (a.kidx_bf16) {
+      typedef uint32_t w4_t __attribute__((ext_vector_type(4)));
+      const w4_t* v = reinterpret_cast<const w4_t*>(reinterpret_cast<const bf16_raw*>(a.kidx) + off);
+      const w4_t x0 = v[0], x1 = v[1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u = i < 4 ? x0[i & 3] : x1[i & 3];
+        s = fmaf(s_q[2 * i], __uint_as_float(u << 16), s);
+        s = fmaf(s_q[2 * i + 1], __uint_as_float(u & 0xffff0000u), s);
+      }
+    } else {
+      const float* kv = reinterpret_cast<const float*>(a.kidx) + off;
+#pragma unroll
+      for (int i = 0; i < kRank; ++i) s = fmaf(s_q[i], kv[i], s);
+    }
+    return score_key(s);
+  };
+  auto hist_add = [&](uint32_t key, int level, uint32_t pre) {
+    const int shift = level == 2 ? 8 : 0;
+    const int hshift = level == 2 ? 20 : 8;
+    const uint32_t dmask = level == 3 ? 0xffu : 0xfffu;
+    if ((key >> hshift) == pre) atomicAdd(&hcnt[(key >> shift) & dmask], 1u);
+  };
+
+  if (t == 0) {
+    res.mode = kSearching;
+    res.prefix = 0;
+    res.thr = 0;
+    res.n_eq = 0;
+    res.need = (uint32_t)a.k;
+    res.all = 0;
+    res.rem = 0;
+    if (n == 0 || a.k >= n) res.mode = kTakeGE;
+  }
+  if (t < kRank) {
+    const int blk = a.prefill_blk0 + row / a.Hkv;
+    s_q[t] = a.qcb[((int64_t)blk * a.Hkv + g) * kRank + t];
+  }
+  for (int i = t; i < kBins; i += NT) hcnt[i] = 0;
+  for (int i = t; i < 2 * rounds * NW; i += NT) selmap[i] = 0;
+  __syncthreads();
+
+  // ---- load: packed keys to registers and LDS, level-1 histogram of both
+  // halves (halves past the row hold 0, counted into bin 0 and taken out) ----
+  auto take = [&](uint32_t w) {
+    atomicAdd(&hcnt[(w & 0xffffu) >> 4], 1u);
+    atomicAdd(&hcnt[w >> 20], 1u);
+  };
+#pragma unroll
+  for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
+    if (i0 + 8 <= full) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) words[i0 + u] = load_full(i0 + u);
+    } else if (i0 < rounds) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) words[i0 + u] = i0 + u < full ? load_full(i0 + u) : (i0 + u == full ? partial_word() : 0u);
+    }
+  }
+#pragma unroll
+  for (int i0 = 0; i0 < kRowRegs; i0 += 8) {
+    if (i0 < rounds) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (i0 + u < rounds) take(words[i0 + u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) words[i0 + u] = 0u;
+    }
+  }
+  auto keep = [&](int i, uint32_t w) {
+    if (i < cached_end) kcache[(i - kRowRegs) * NT + t] = w;
+    take(w);
+  };
+  stream_full(kRowRegs, full, keep);
+  if (rounds > full && full >= kRowRegs) keep(full, partial_word());
+  if (t == 0) atomicSub(&hcnt[0], (uint32_t)(2 * rounds * NT - n));
+  __syncthreads();
+
+  // Resolve a level from its histogram (counts only): the bin, in descending
+  // order, where the running count reaches the candidates still needed.
+  auto resolve = [&](int level) {
+    const int NB = level == 3 ? 256 : kBins;
+    const int shift = level == 1 ? 20 : (level == 2 ? 8 : 0);
+    const uint32_t pre = res.prefix;
+    const int per = NB / NT > 0 ? NB / NT : 1;
+    const bool owns = t * per < NB;
+    uint32_t cl = 0;
+    if (owns)
+      for (int e = 0; e < per; ++e) cl += hcnt[NB - 1 - (t * per + e)];
+    uint32_t ctot;
+    const uint32_t cb0 = block_excl_scan<uint32_t, NW>(cl, red32, ctot);
+    const uint32_t need = res.need;
+    if (t == 0) s_hit_bin = 0xffffffffu;
+    __syncthreads();
+    if (owns) {
+      uint32_t cb = cb0;
+      for (int e = 0; e < per; ++e) {
+        const int bin = NB - 1 - (t * per + e);
+        const uint32_t c = hcnt[bin];
+        if (cb < need && cb + c >= need) {
+          s_hit_bin = bin;
+          s_hit_cnt = c;
+          s_hit_cbef = cb;
+        }
+        cb += c;
+      }
+    }
+    __syncthreads();
+    if (t == 0) {
+      const uint32_t bin = s_hit_bin;
+      if (bin == 0xffffffffu) {
+        res.mode = kTakeGE;  // inconsistent input: take everything
+        res.thr = 0;
+        res.all = 1;
+      } else {
+        const uint32_t cnt_b = s_hit_cnt;
+        const uint32_t np = level == 1 ? bin : (level == 2 ? ((pre << 12) | bin) : ((pre << 8) | bin));
+        const uint32_t bin_lo = np << shift;
+        const uint32_t nd = need - s_hit_cbef;
+        if (nd == cnt_b) {
+          res.mode = kTakeGE;
+          res.thr = bin_lo;
+        } else if (level < 3) {
+          res.prefix = np;
+          res.need = nd;
+        } else {
+          res.mode = kTakeTies;
+          res.thr = bin_lo;
+          res.n_eq = nd;
+        }
+      }
+    }
+    __syncthreads();
+  };
+
+  // ---- level 1, then the filter pass ----
+  if (res.mode == kSearching) resolve(1);
+  const uint32_t mode1 = res.mode, thr1 = res.thr, B1 = res.prefix;
+  if (mode1 == kSearching) {
+    uint32_t wcnt = 0;  // wave-uniform fill of the buffer segment
+    const uint32_t lo1 = B1 << 4, top1 = lo1 | 0xfu;  // bin B1 in 16-bit keys: [lo1, top1]
+    uint64_t* const smap = selmap + 2 * wave;
+    // one half of a round: k16 its keys, hi: valid and k16 >= lo1
+    auto half = [&](int i, int h, uint32_t k16, bool hi) {
+      const uint64_t mh = __builtin_amdgcn_ballot_w64(hi);
+      if (mh == 0) return;
+      const uint64_t m = __builtin_amdgcn_ballot_w64(k16 > top1) & mh;
+      if (m && lane == 0) smap[2 * i * NW + h] = m;
+      const uint64_t mb = mh & ~m;
+      if (mb) {
+        const uint32_t p = __builtin_amdgcn_mbcnt_hi(
+            (uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, wcnt));
+        if (hi && k16 <= top1 && p < (uint32_t)kBufPerW) bidx[wave * kBufPerW + p] = cand_lo(i) + 64 * h;
+        wcnt += (uint32_t)__popcll(mb);
+      }
+    };
+    auto filter = [&](int i, uint32_t w) {
+      const uint32_t kl = w & 0xffffu, kh = w >> 16;
+      if (lo1 > 0) {  // halves past the row (key 0) lie below the bin
+        half(i, 0, kl, kl >= lo1);
+        half(i, 1, kh, kh >= lo1);
+      } else {
+        half(i, 0, kl, cand_lo(i) < n);
+        half(i, 1, kh, cand_lo(i) + 64 < n);
+      }
+    };
+    for_all(filter);
+    if (lane == 0) s_wcnt[wave] = wcnt;
+  } else {
+    const uint32_t t16 = thr1 >> 16;  // level-1 thresholds are bin floors: exact in 16 bits
+    for_all([&](int i, uint32_t w) {
+      const int32_t c = cand_lo(i);
+      const uint64_t ml = __builtin_amdgcn_ballot_w64(c < n && (w & 0xffffu) >= t16);
+      const uint64_t mh = __builtin_amdgcn_ballot_w64(c + 64 < n && (w >> 16) >= t16);
+      if (lane == 0) {
+        if (ml) selmap[2 * (i * NW + wave)] = ml;
+        if (mh) selmap[2 * (i * NW + wave) + 1] = mh;
+      }
+    });
+  }
+  __syncthreads();
+  bool use_buf = true;
+  if (mode1 == kSearching) {
+#pragma unroll
+    for (int w = 0; w < NW; ++w) use_buf = use_buf && s_wcnt[w] <= (uint32_t)kBufPerW;
+  }
+  auto in_buf = [&](int j) { return (uint32_t)(j % kBufPerW) < s_wcnt[j / kBufPerW]; };
+  // exact keys of the buffered candidates
+  if (mode1 == kSearching && use_buf) {
+    for (int j = t; j < kBufCap; j += NT)
+      if (in_buf(j)) bkey[j] = exact_key(bidx[j]);
+    __syncthreads();
+  }
+  // fallback (bin overflowed its buffer): every candidate of bin B1, exact;
+  // rare, so it re-reads the packed keys from the score row one round at a
+  // time instead of walking the register copies
+  auto for_bin = [&](auto&& fn) {  // fn(candidate, exact key)
+#pragma unroll 1
+    for (int i = 0; i < rounds; ++i) {
+      const uint32_t w = i < full ? load_full(i) : partial_word();
+      const int32_t c = cand_lo(i);
+      if (c < n && ((w & 0xffffu) >> 4) == B1) fn(c, exact_key(c));
+      if (c + 64 < n && (w >> 20) == B1) fn(c + 64, exact_key(c + 64));
+    }
+  };
+
+  // ---- levels 2 and 3 over the bin's candidates ----
+  for (int level = 2; level <= 3; ++level) {
+    if (res.mode != kSearching) break;  // block-uniform (read after a barrier)
+    const int NB = level == 3 ? 256 : kBins;
+    const uint32_t pre = res.prefix;
+    for (int i = t; i < NB; i += NT) hcnt[i] = 0;
+    __syncthreads();
+    if (use_buf) {
+      for (int j = t; j < kBufCap; j += NT)
+        if (in_buf(j)) hist_add(bkey[j], level, pre);
+    } else {
+      for_bin([&](int32_t c, uint32_t k) { hist_add(k, level, pre); });
+    }
+    __syncthreads();
+    resolve(level);
+  }
+
+  // ---- final marking of the bin's candidates ----
+  const uint32_t mode = res.mode, thr = res.thr, n_eq = res.n_eq;
+  const bool take_all = res.all != 0;
+  const bool ties = mode1 == kSearching && mode == kTakeTies;
+  const int nw = (n + 31) >> 5;  // 32-bit bitmap words of the row
+  if (ties) {
+    for (int i = t; i < nw; i += NT) tie32[i] = 0;
+    __syncthreads();
+  }
+  if (mode1 == kSearching) {
+    auto mark = [&](int32_t c, uint32_t k) {
+      if (k > thr || (mode == kTakeGE && k == thr)) atomicOr(&sel32[c >> 5], 1u << (c & 31));
+      else if (ties && k == thr) atomicOr(&tie32[c >> 5], 1u << (c & 31));
+    };
+    if (use_buf) {
+      for (int j = t; j < kBufCap; j += NT)
+        if (in_buf(j)) mark(bidx[j], bkey[j]);
+    } else {
+      for_bin(mark);
+    }
+    __syncthreads();
+  }
+
+  // ---- ordered compaction: thread t owns bitmap words [WPT t, WPT (t + 1)) ----
+  uint32_t sw[WPT];
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) sw[w] = WPT * t + w < nw ? sel32[WPT * t + w] : 0u;
+  if (ties) {  // the n_eq lowest-index keys equal to the threshold
+    uint32_t tw[WPT], c = 0;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      tw[w] = WPT * t + w < nw ? tie32[WPT * t + w] : 0u;
+      c += (uint32_t)__popc(tw[w]);
+    }
+    uint32_t tot;
+    const uint32_t before = block_excl_scan<uint32_t, NW>(c, red32, tot);
+    uint32_t left = before < n_eq ? n_eq - before : 0u;
+#pragma unroll
+    for (int w = 0; w < WPT; ++w) {
+      uint32_t bits = tw[w], keepb = 0;
+      while (bits && left) {
+        keepb |= bits & (0u - bits);
+        bits &= bits - 1u;
+        --left;
+      }
+      sw[w] |= keepb;
+    }
+  }
+  uint32_t c = 0;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) {
+    const int widx = WPT * t + w;
+    if (widx < nw) {
+      const int32_t lo = widx * 32;
+      const uint32_t vm = n - lo >= 32 ? ~0u : ((1u << (n - lo)) - 1u);
+      uint32_t fm = 0;  // always-kept sink and window candidates
+      if (a.n_sink > lo) fm |= a.n_sink - lo >= 32 ? ~0u : ((1u << (a.n_sink - lo)) - 1u);
+      const int32_t ws = n - a.n_window;
+      if (ws < lo + 32) fm |= ws <= lo ? ~0u : (~0u << (ws - lo));
+      sw[w] = ((take_all ? ~0u : sw[w]) | fm) & vm;
+    }
+    c += (uint32_t)__popc(sw[w]);
+  }
+  uint32_t total;
+  uint32_t rank = block_excl_scan<uint32_t, NW>(c, red32, total);
+  int32_t* out = a.idx + (int64_t)row * a.cap;
+  const uint32_t T = total < (uint32_t)a.cap ? total : (uint32_t)a.cap;
+#pragma unroll
+  for (int w = 0; w < WPT; ++w) {
+    uint32_t bits = sw[w];
+    while (bits) {
+      const int j = __ffs(bits) - 1;
+      bits &= bits - 1u;
+      if (rank < (uint32_t)a.cap) out[rank] = (WPT * t + w) * 32 + j;
+      ++rank;
+    }
+  }
+  for (int64_t o = (int64_t)T + t; o < a.cap; o += NT) out[o] = -1;
+  if (t == 0) a.count[row] = (int32_t)T;
+}
+
 }  // namespace
 
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
@@ -1025,6 +1425,11 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
 
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   if (a.rows == 0) return hipSuccess;
+  if (a.key16) {  // prefill top-k over 16-bit keys (rows of at most kRowMax candidates)
+    if (!a.is_topk || a.unit != 1 || a.max_cand > kRowMax) return hipErrorInvalidValue;
+    k_select_row16<kRowRegsTopk, 512><<<a.rows, 512, 0, st>>>(a);
+    return hipGetLastError();
+  }
   // One block per row when a row's keys fit in one block's registers, or
   // when there are enough rows to fill the chip; few long rows are split
   // over many blocks instead.

@@ -147,3 +147,37 @@ def test_prefill128k_sampled_blocks():
     blocks = sorted(fixed + others)
     n_diff = check_blocks(inp, kt_rows, idx, count, out, lse, k, blocks, groups)
     print(f"prefill128k: groups {groups}, tolerated support differences {n_diff}")
+
+
+def quantised_kidx(inp, seed, probs=(0.8, 0.15, 0.05)):
+    """Indexer keys drawn from three fixed 16-vectors (rounded to the cache
+    dtype): every block's scores take three values, in long tie groups."""
+    rng = np.random.default_rng(seed)
+    vecs = S.store_round(rng.standard_normal((len(probs), 16)), inp.dtype)
+    kt = vecs[rng.choice(len(probs), size=inp.N, p=list(probs))]
+    pool = torch.zeros((inp.k_pool.shape[0], inp.H_kv, 64, 16), dtype=inp.dtype)
+    full = torch.zeros((pool.shape[0] * 64, 16), dtype=inp.dtype)
+    full[: inp.N] = torch.from_numpy(kt).to(inp.dtype)
+    for g in range(inp.H_kv):
+        pool[:, g] = full.view(pool.shape[0], 64, 16)
+    return pool.to(inp.device), {g: kt for g in range(inp.H_kv)}
+
+
+def test_prefill_select_long_tie_groups():
+    """Top-2048 over rows of up to 20K candidates whose scores take three
+    values: the threshold falls inside a tie group of thousands of candidates
+    (more than the selection keeps per wave for its exact second pass), and
+    the lists must be exactly the oracle's, ties lowest index first."""
+    inp = synth.make_prefill_custom(N=20000, H_q=4, H_kv=1, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=21, n_hh=4)
+    kidx, kt_rows = quantised_kidx(inp, 3)
+    k = 2048
+    idx, count, out, lse = run_prefill(inp, kidx, k)
+    blocks = [1, 33, 40, 150, inp.n_blocks - 1]
+    check_blocks(inp, kt_rows, idx, count, out, lse, k, blocks, [0])
+    wq = S.to_np(inp.w_q[inp.heads(0)])
+    for blk in blocks:
+        rows = O.prefill_block_rows(blk, B_SEL, inp.N)
+        qc = O.prefill_block_query(S.to_np(inp.q[rows.start:rows.stop][:, inp.heads(0)]), wq, inp.s_idx)
+        core = O.prefill_block_support(qc, kt_rows[0], blk, B_SEL, k)
+        assert S.gpu_support(idx, count, blk).tolist() == core.tolist(), blk

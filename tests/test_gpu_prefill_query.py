@@ -147,3 +147,22 @@ def test_query_prefill_32k_workload_sampled(probs):
     n_diff = check_queries(inp, kt_rows, idx, count, out, lse, inp.top_k, queries, groups,
                            probs=probs)
     print(f"prefill32k_query probs={probs}: tolerated support differences {n_diff}")
+
+
+def test_query_prefill_long_tie_groups():
+    """Per-query top-k over indexer keys drawn from three fixed vectors (long
+    exact tie groups across the threshold): lists exactly the oracle's, ties
+    lowest index first, the own token always kept."""
+    from tests.test_gpu_prefill import quantised_kidx
+    inp = synth.make_prefill_custom(N=6000, H_q=4, H_kv=1, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=23, n_hh=4)
+    kidx, kt_rows = quantised_kidx(inp, 5, probs=(0.7, 0.2, 0.1))
+    k = 700
+    idx, count, out, lse = run_query_prefill(inp, kidx, k)
+    queries = [0, 699, 700, 2500, 5999]
+    check_queries(inp, kt_rows, idx, count, out, lse, k, queries, [0])
+    wq = S.to_np(inp.w_q[inp.heads(0)])
+    for i in queries:
+        x = O.prefill_query_scores(S.to_np(inp.q[i, inp.heads(0)]), wq, kt_rows[0], i, inp.s_idx, "logits")
+        expect = O.with_sink_window(O.select_topk(x, k), i + 1, 0, 1)
+        assert S.gpu_support(idx, count, i).tolist() == expect.tolist(), i
