@@ -1435,7 +1435,10 @@ hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   // over many blocks instead.
   if (a.max_cand <= kRowRegsTopp * kThreads || (a.max_cand <= kRowMax && a.rows >= 32)) {
     if (!a.is_topk) k_select_row<true, kRowRegsTopp, kThreads><<<a.rows, kThreads, 0, st>>>(a);
-    else k_select_row<false, kRowRegsTopk, 512><<<a.rows, 512, 0, st>>>(a);
+    // top-k: two 512-thread blocks per CU when the rows fill the chip, else
+    // 1024 threads per row (half the rounds per thread)
+    else if (a.rows >= 256) k_select_row<false, kRowRegsTopk, 512><<<a.rows, 512, 0, st>>>(a);
+    else k_select_row<false, kRowRegsTopk, kThreads><<<a.rows, kThreads, 0, st>>>(a);
     return hipGetLastError();
   }
   const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
