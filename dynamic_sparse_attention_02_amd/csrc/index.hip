@@ -223,7 +223,9 @@ hipError_t launch_page_stats(const Shape& s, const void* k_pool, sa_dtype dt,
 // operations, each lane keeps the heads h = sub (mod lanes per page), takes
 // log1p of those, and one more reduction sums them.
 // ---------------------------------------------------------------------------
-constexpr int kPSRounds = 4;
+// pages per lane: one (small blocks, many of them, outrun a few large ones:
+// the group's scaled query is staged once per block in LDS)
+constexpr int kPSRounds = 1;
 
 template <typename T>
 __device__ __forceinline__ void load8(const T* p, float (&v)[8]);
@@ -292,22 +294,30 @@ k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
       }
     }
   }
-  // scaled query of the group's heads on this lane's 8 dimensions: the sum
-  // over heads, and the squares per head
+  // scaled query of the group's heads: the sum over heads and the squares
+  // per head, formed once per block in LDS (every page of the block reuses
+  // them), then this lane's 8 dimensions in registers
+  __shared__ __align__(16) float s_qs[D];
+  __shared__ __align__(16) float s_qq[G][D];
+  const T* qg = q + ((int64_t)b * s.Hq + g * G) * D;
+  for (int e = threadIdx.x; e < D; e += 256) {
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qp = s_att * to_f32<T>(qg[h * D + e]);
+      sum += qp;
+      s_qq[h][e] = qp * qp;
+    }
+    s_qs[e] = sum;
+  }
+  __syncthreads();
   float qs[8], qq[G][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) qs[e] = 0.f;
+  for (int e = 0; e < 8; ++e) qs[e] = s_qs[sub * 8 + e];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v[8];
-    load8<T>(q + ((int64_t)b * s.Hq + g * G + h) * D + sub * 8, v);
+  for (int h = 0; h < G; ++h)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float qp = s_att * v[e];
-      qs[e] += qp;
-      qq[h][e] = qp * qp;
-    }
-  }
+    for (int e = 0; e < 8; ++e) qq[h][e] = s_qq[h][sub * 8 + e];
 #pragma unroll
   for (int r = 0; r < kPSRounds; ++r) {
     float first = 0.f;
