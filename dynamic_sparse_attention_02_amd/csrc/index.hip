@@ -215,8 +215,7 @@ hipError_t launch_page_stats(const Shape& s, const void* k_pool, sa_dtype dt,
 // ---------------------------------------------------------------------------
 // Taylor page scores.  A page's statistics row (mean then variance, 2*D
 // values) is spread over D/8 lanes holding 8 dimensions each (16-byte loads
-// for bf16), so a wave covers 512/D pages per load instruction; four rounds
-// are issued before any is used.
+// for bf16), so a wave covers 512/D pages per load instruction.
 //   x = mean_h [ q'_h.mean + log1p(0.5 * q'_h^2.var) ] + log(n / page)
 // The first term is (sum_h q'_h).mean / G, one dot product per page.  The
 // per-head variance sums are reduced over the page's lanes with DPP row
@@ -226,37 +225,6 @@ hipError_t launch_page_stats(const Shape& s, const void* k_pool, sa_dtype dt,
 // pages per lane: one (small blocks, many of them, outrun a few large ones:
 // the group's scaled query is staged once per block in LDS)
 constexpr int kPSRounds = 1;
-
-template <typename T>
-__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
-template <>
-__device__ __forceinline__ void load8<bf16_raw>(const bf16_raw* p, float (&v)[8]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = __uint_as_float(w[i] << 16);
-    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
-  }
-}
-template <>
-__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-}
-
-// Sum over aligned groups of N lanes (N = 8 or 16) with DPP row operations;
-// every lane of the group receives the total.
-template <int N>
-__device__ __forceinline__ float row_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
-  if (N == 16)
-    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
-  return v;
-}
 
 template <typename T, int D, int G>
 __global__ void __launch_bounds__(256)
@@ -294,55 +262,19 @@ k_page_scores(const T* __restrict__ q, const T* __restrict__ stats,
       }
     }
   }
-  // scaled query of the group's heads: the sum over heads and the squares
-  // per head, formed once per block in LDS (every page of the block reuses
-  // them), then this lane's 8 dimensions in registers
+  // scaled query of the group's heads, formed once per block in LDS (every
+  // page of the block reuses it), then this lane's 8 dimensions in registers
   __shared__ __align__(16) float s_qs[D];
   __shared__ __align__(16) float s_qq[G][D];
-  const T* qg = q + ((int64_t)b * s.Hq + g * G) * D;
-  for (int e = threadIdx.x; e < D; e += 256) {
-    float sum = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float qp = s_att * to_f32<T>(qg[h * D + e]);
-      sum += qp;
-      s_qq[h][e] = qp * qp;
-    }
-    s_qs[e] = sum;
-  }
+  stage_page_query<T, D, G>(q + ((int64_t)b * s.Hq + g * G) * D, s_att, s_qs, s_qq, 256);
   __syncthreads();
   float qs[8], qq[G][8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) qs[e] = s_qs[sub * 8 + e];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qq[h][e] = s_qq[h][sub * 8 + e];
+  page_query_lane<D, G>(s_qs, s_qq, sub, qs, qq);
 #pragma unroll
   for (int r = 0; r < kPSRounds; ++r) {
-    float first = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) first = fmaf(qs[e], mu[r][e], first);
-    float mine[HPL];
-#pragma unroll
-    for (int j = 0; j < HPL; ++j) mine[j] = 0.f;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float c = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) c = fmaf(qq[h][e], va[r][e], c);
-      c = row_sum<LPP>(c);
-      if (sub == h % LPP) mine[h / LPP] = c;
-    }
-    float acc = first;
-#pragma unroll
-    for (int j = 0; j < HPL; ++j)
-      if (j * LPP + sub < G) acc += log1pf(0.5f * mine[j]);
-    acc = row_sum<LPP>(acc);
-    if (sub == 0 && pg[r] < n_pages) {
-      const int nv = (L - pg[r] * kPage) < kPage ? (L - pg[r] * kPage) : kPage;
-      x[((int64_t)b * s.Hkv + g) * ldx + pg[r]] = acc / (float)G + logf((float)nv / (float)kPage);
-    }
+    const float acc = page_score_sum<LPP, G>(mu[r], va[r], qs, qq, sub);
+    if (sub == 0 && pg[r] < n_pages)
+      x[((int64_t)b * s.Hkv + g) * ldx + pg[r]] = page_score_final<G>(acc, L, pg[r]);
   }
 }
 

@@ -125,6 +125,105 @@ __device__ __forceinline__ float row16_max(float v) {
     return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
   }));
 }
+// ---------------------------------------------------------------------------
+// Taylor page scores ("SPLA", section 2.1, diagonal covariance), shared by
+// the page-score kernel and the fused page step so
+// both form every score with the same operations in the same order: a page
+// is spread over D / 8 lanes, 8 dimensions each.
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<bf16_raw>(const bf16_raw* p, float (&v)[8]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __uint_as_float(w[i] << 16);
+    v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+
+// Sum over aligned groups of N lanes (N = 8 or 16) with DPP row operations;
+// every lane of the group receives the total.
+template <int N>
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, true));
+  if (N == 16)
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+// The group's scaled query q'_h = s_att q_h in LDS: the sum over heads
+// s_qs[e] = sum_h q'_h[e] and the squares s_qq[h][e] = q'_h[e]^2 (nt threads
+// of the block take part; the caller synchronises).
+template <typename T, int D, int G>
+__device__ __forceinline__ void stage_page_query(const T* qg, float s_att, float* s_qs,
+                                                 float (*s_qq)[D], int nt) {
+  for (int e = threadIdx.x; e < D; e += nt) {
+    float sum = 0.f;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float qp = s_att * to_f32<T>(qg[h * D + e]);
+      sum += qp;
+      s_qq[h][e] = qp * qp;
+    }
+    s_qs[e] = sum;
+  }
+}
+// This lane's 8 dimensions (sub = lane within the page's lanes) of them.
+template <int D, int G>
+__device__ __forceinline__ void page_query_lane(const float* s_qs, const float (*s_qq)[D], int sub,
+                                                float (&qs)[8], float (&qq)[G][8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) qs[e] = s_qs[sub * 8 + e];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qq[h][e] = s_qq[h][sub * 8 + e];
+}
+// sum_h [q'_h . mean + log1p(0.5 q'_h^2 . var)] of the page whose 8 mean and
+// variance dimensions of this lane are mu, va; every lane of the page gets it.
+template <int LPP, int G>
+__device__ __forceinline__ float page_score_sum(const float (&mu)[8], const float (&va)[8],
+                                                const float (&qs)[8], const float (&qq)[G][8],
+                                                int sub) {
+  constexpr int HPL = (G + LPP - 1) / LPP;  // heads kept per lane
+  float first = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) first = fmaf(qs[e], mu[e], first);
+  float mine[HPL];
+#pragma unroll
+  for (int j = 0; j < HPL; ++j) mine[j] = 0.f;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float c = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c = fmaf(qq[h][e], va[e], c);
+    c = row_sum<LPP>(c);
+    if (sub == h % LPP) mine[h / LPP] = c;
+  }
+  float acc = first;
+#pragma unroll
+  for (int j = 0; j < HPL; ++j)
+    if (j * LPP + sub < G) acc += log1pf(0.5f * mine[j]);
+  return row_sum<LPP>(acc);
+}
+// The page score: the head mean plus log(valid tokens / page size).
+template <int G>
+__device__ __forceinline__ float page_score_final(float sum, int32_t L, int32_t page) {
+  const int nv = (L - page * kPage) < kPage ? (L - page * kPage) : kPage;
+  return sum / (float)G + logf((float)nv / (float)kPage);
+}
+
 // Value of a lane chosen by a wave-uniform index.
 __device__ __forceinline__ uint32_t lane_u32(uint32_t v, int src) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, src);
