@@ -119,6 +119,7 @@ def time_loop(fn, n, warmup=3, reps=1):
 # while these are unchanged).
 KERNEL_SOURCES = {
     "decode_step (single fused launch)": ["fused.hip"],
+    "decode_step_pages (single fused launch)": ["fused.hip"],
     "page_scores": ["index.hip"],
     "index_scores": ["index.hip"],
     "sparse_decode": ["decode.hip"],
@@ -272,8 +273,8 @@ def bench_decode(args, name):
             ops.sa_index_scores(shape, pages, inp.q, inp.w_q, a, inp.s_idx, x, ws_idx)
             ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
 
-    # token-level indexer selection: the whole-step call
-    use_step = not page_mode and not args.rla and not oracle_policy
+    # the whole-step call (token-level indexer or page-level Taylor scores)
+    use_step = not args.rla and not oracle_policy
     if args.rla:  # state of every sequence's cache (maintenance, outside the timed steps)
         rla_state = torch.zeros((B, Hkv, d + 1, d), dtype=torch.float32, device=dev)
         ops.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, 0, rla_state)
@@ -282,10 +283,17 @@ def bench_decode(args, name):
         ws_dec = ops.alloc_workspace(ops.workspace_size(L.SA_OP_SPARSE_DECODE_RLA, shape, cap))
         state_bytes = rla_state.numel() * 4
     if use_step:
-        ws_step = ops.alloc_workspace(ops.workspace_size(L.SA_OP_DECODE_STEP, shape, cap))
+        ws_step = ops.alloc_workspace(ops.workspace_size(
+            L.SA_OP_DECODE_STEP_PAGES if page_mode else L.SA_OP_DECODE_STEP, shape, cap))
     fused = use_step and rows <= 16 and inp.G >= 4
+    if page_mode:
+        fused = fused and k_pages <= 32 and inp.dtype == torch.bfloat16
 
     def run_step(rep):
+        if use_step and page_mode:
+            ops.sa_decode_step_pages(shape, pages, inp.q, rep[0], rep[1], rep[2], inp.s_att,
+                                     k_pages, x, idx, count, out, lse, ws_step)
+            return
         if use_step:
             ops.sa_decode_step(shape, pages, inp.q, inp.w_q, rep[0], rep[1], rep[2], inp.s_idx,
                                inp.s_att, sel.get("p", 0.0), 0, n_sink, n_window, x, idx, count,
@@ -350,7 +358,8 @@ def bench_decode(args, name):
             ("sparse_decode_rla" if args.rla else "sparse_decode"): (t_decode, kv_bytes)}
     if fused:
         # the whole step is one kernel: its bytes are the step's
-        dom, dom_ms, dom_bytes = "decode_step (single fused launch)", ms, step_bytes
+        dom = "decode_step%s (single fused launch)" % ("_pages" if page_mode else "")
+        dom_ms, dom_bytes = ms, step_bytes
     else:
         dom = max((k for k in comp if comp[k][1] > 0), key=lambda k: comp[k][0])
         dom_ms, dom_bytes = comp[dom]
@@ -384,7 +393,8 @@ def bench_decode(args, name):
         "index_bytes": index_bytes,
         "kv_bytes": kv_bytes,
         "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
-        "step_call": ("sa_decode_step" + (" (fused)" if fused else "")) if use_step else
+        "step_call": (("sa_decode_step_pages" if page_mode else "sa_decode_step") +
+                      (" (fused)" if fused else "")) if use_step else
                      ((("sa_page_scores + sa_select_topk") if page_mode else
                        ("sa_attention_mass" if oracle_policy else "sa_index_scores") +
                        " + sa_select_topp") +

@@ -34,6 +34,7 @@ SA_OP_PREFILL_QUERY = 7
 SA_OP_PBS_IMPORTANCE = 8
 SA_OP_PBS_SELECT = 9
 SA_OP_PREFILL_ORACLE = 10
+SA_OP_DECODE_STEP_PAGES = 11
 
 
 class SaShape(ctypes.Structure):
@@ -82,6 +83,8 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F, _F, _I32,
                                       _I32, _I32, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P,
                                       _SZ, _P]),
+    "sa_decode_step_pages": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, ctypes.c_int, _F, _I32, _P,
+                                            _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P, _SZ, _P]),
     "sa_select_prefill_topk": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _F, _I32,
                                               _I32, _P, _P, _I32, _P, _SZ, _P]),
     "sa_select_prefill_topk_probs": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _F,

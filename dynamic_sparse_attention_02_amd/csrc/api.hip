@@ -129,6 +129,16 @@ size_t step_ws(const sa_shape* s, int64_t cap) {
   return unfused > fused ? unfused : fused;
 }
 
+// Page-level step workspace: the separate calls or the fused step.
+size_t step_pages_ws(const sa_shape* s, int64_t cap) {
+  const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
+  const size_t unfused = select_ws(s, n_cand) + decode_ws(s, cap);
+  const int rows = s->batch * s->n_kv_heads;
+  const int G = s->n_q_heads / s->n_kv_heads;
+  const size_t fused = sa::align_up(sa::fused_workspace_bytes(rows, 256, G, s->head_dim), 256);
+  return unfused > fused ? unfused : fused;
+}
+
 int64_t topk_cap_needed(const sa_shape* s, int32_t k, int32_t unit, int32_t n_sink,
                         int32_t n_window) {
   int64_t need;
@@ -169,6 +179,8 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
     }
     case SA_OP_DECODE_STEP:
       return step_ws(s, param);
+    case SA_OP_DECODE_STEP_PAGES:
+      return step_pages_ws(s, param);
     case SA_OP_SPARSE_DECODE_RLA:
       return decode_ws(s, param, true);
     case SA_OP_ATTENTION_MASS:
@@ -451,6 +463,62 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   if (e != hipSuccess) return hip_status(e, fn);
   e = sa::launch_sparse_decode(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
                                lse, base + w_i + w_s, st);
+  return hip_status(e, fn);
+}
+
+sa_status sa_decode_step_pages(const sa_shape* s, const sa_pages* pg, const void* q,
+                               const void* stats_pool, const void* k_pool, const void* v_pool,
+                               sa_dtype dt, float s_att, int32_t top_k, float* x, int64_t ldx,
+                               int32_t* idx, int32_t* count, int32_t cap, void* out,
+                               sa_dtype out_dt, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t st) {
+  const char* fn = "sa_decode_step_pages";
+  SA_TRY(check_shape(s, fn));
+  SA_TRY(check_pages(pg, true, fn));
+  if (!valid_dtype(dt) || !valid_dtype(out_dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
+  if (!q || !stats_pool || !k_pool || !v_pool || !x || !idx || !count || !out)
+    return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  if (ldx < s->max_pages) return fail(SA_ERR_INVALID_ARGUMENT, "%s: ldx=%lld < max_pages=%d", fn, (long long)ldx, s->max_pages);
+  if (top_k < 1) return fail(SA_ERR_INVALID_ARGUMENT, "%s: top_k=%d < 1", fn, top_k);
+  if (!(s_att == s_att)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: s_att is NaN", fn);
+  if ((int64_t)s->batch * s->n_kv_heads > kMaxDecodeRows)
+    return fail(SA_ERR_UNSUPPORTED, "%s: batch * n_kv_heads above %d", fn, kMaxDecodeRows);
+  const int64_t cap_needed = topk_cap_needed(s, top_k, s->page_size, 0, 0);
+  if (cap < 1 || cap < cap_needed)
+    return fail(SA_ERR_CAPACITY, "%s: cap=%d below the worst-case support %lld", fn, cap, (long long)cap_needed);
+  SA_TRY(check_ws(ws, ws_bytes, step_pages_ws(s, cap), fn));
+  const sa::Shape sh = to_shape(s);
+  int32_t nb = 0, tpb = 0;
+  if (dt == SA_BF16 && sa::fused_plan_pages(sh, top_k, &nb, &tpb))
+    return hip_status(sa::launch_decode_fused_pages(sh, *pg, q, stats_pool, k_pool, v_pool, s_att,
+                                                    top_k, x, ldx, idx, count, cap, out, out_dt,
+                                                    lse, ws, nb, tpb, st), fn);
+  const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
+  const size_t w_s = select_ws(s, n_cand);
+  char* base = (char*)ws;
+  hipError_t e = sa::launch_page_scores(sh, *pg, q, stats_pool, dt, s_att, x, ldx, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  sa::SelectArgs a{};
+  a.x = x;
+  a.ldx = ldx;
+  a.seq_lens = pg->seq_lens;
+  a.rows = s->batch * s->n_kv_heads;
+  a.Hkv = s->n_kv_heads;
+  a.max_len = s->max_len;
+  a.unit = s->page_size;
+  a.max_cand = (int32_t)n_cand;
+  a.is_topk = 1;
+  a.p = 0.f;
+  a.k = top_k;
+  a.n_sink = 0;
+  a.n_window = 0;
+  a.idx = idx;
+  a.count = count;
+  a.cap = cap;
+  e = sa::launch_select(a, base, st);
+  if (e != hipSuccess) return hip_status(e, fn);
+  e = sa::launch_sparse_decode(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
+                               lse, base + w_s, st);
   return hip_status(e, fn);
 }
 

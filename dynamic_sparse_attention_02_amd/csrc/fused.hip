@@ -23,6 +23,13 @@
 //      counts, and each workgroup merges a slice of the row's outputs.
 // Histograms, the row maximum and the barrier counters are returned to zero
 // before the launch ends.
+//
+// Page mode runs the same phases over a sequence's 64-token pages: Taylor
+// page scores from the mean and diagonal variance of each page's keys
+// ("SPLA", section 2.1) in phase 1, a top-k of pages in phase 2, and in
+// phase 3 every workgroup publishes its selected pages, meets the others and
+// reads the row's page list, then attends an even slice of the row's tokens
+// (the selected pages are few and may sit in one workgroup's range).
 #include "sa_internal.h"
 
 namespace sa {
@@ -35,6 +42,7 @@ constexpr int kCoarseF = kBinsF / 64;
 constexpr int kTileF = 64;                // attention tile (tokens)
 constexpr uint32_t kSpinLimit = 1u << 20; // about a second of polling, then give up
 constexpr int kMaxNB = 256;
+constexpr int kFusedMaxPages = 32;        // page mode: largest top-k (pages)
 
 enum : uint32_t { kSearch = 0, kGE = 1, kTies = 2 };
 
@@ -45,14 +53,14 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 struct RowWs {            // per-row control block (zero between launches)
-  uint32_t bar;           // barrier arrivals
   uint32_t exit;          // workgroups done
   uint32_t maxkey;        // row maximum score key
-  uint32_t pad[13];
+  uint32_t pad[14];
 };
 
 struct FusedArgs {
   const void* q;          // [B][Hq][D]
+  const void* stats;      // page mode: page statistics pool [P][Hkv][2][D]
   const void* w_q;        // [Hq][D][16]
   const void* kidx;       // pool [P][Hkv][64][16]
   const void* k_pool;
@@ -84,6 +92,8 @@ struct FusedArgs {
   float* part_o;          // [rows][nb][G][D]
   uint32_t* err;          // set to 1 if a barrier gave up waiting
   uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
+  int32_t* plist;         // page mode: [rows][nb][kFusedMaxPages][2] own pages (sequence, pool)
+  uint32_t* flags;        // [rows][kMaxNB] barrier arrival flags (barriers passed)
 };
 
 constexpr int kTraceSlots = 16;
@@ -99,22 +109,28 @@ __device__ __forceinline__ void stamp(const FusedArgs& a, int slot) {
 // device's coherence point, and read with device-scope loads, which the L2
 // does not serve stale.  So the barrier needs no L2 write-back or
 // invalidate: each wave waits until its own memory operations have
-// completed, then one thread counts the arrival.  (A release fence here
-// would write back every dirty L2 line on each arrival, which costs several
-// microseconds per barrier.)  The spin is bounded: a barrier that waits too
-// long raises the error flag and lets the launch finish instead of hanging.
-__device__ __forceinline__ void row_barrier(uint32_t* ctr, uint32_t target, uint32_t* err) {
+// completed, then the workgroup raises its own arrival flag to the barrier's
+// number.  One wave per workgroup polls the row's flags (one per workgroup,
+// adjacent, so a poll is one vector load) until all reached that number.
+// Separate flags keep the arrivals from queueing on one counter.  The spin
+// is bounded: a barrier that waits too long raises the error flag and lets
+// the launch finish instead of hanging.
+__device__ __forceinline__ void row_barrier(uint32_t* flags, int nb, int bi, uint32_t epoch, uint32_t* err) {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // this wave's loads, stores and atomics completed
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    atomicAdd(ctr, 1u);
+  if (threadIdx.x < kWave) {
+    if (threadIdx.x == 0) __hip_atomic_store(&flags[bi], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0;
-    while (__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    for (;;) {
+      bool ok = true;
+      for (int k = (int)threadIdx.x; k < nb; k += kWave)
+        ok = ok && __hip_atomic_load(&flags[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
+      if (__all(ok)) break;
       __builtin_amdgcn_s_sleep(1);
       if (++spins > kSpinLimit) {
-        atomicOr(err, 1u);
+        if (threadIdx.x == 0) atomicOr(err, 1u);
         break;
       }
     }
@@ -148,7 +164,9 @@ __device__ __forceinline__ U blk_scan(U v, U* lds, U& total) {  // exclusive, kN
   return off + inc - v;
 }
 
-template <typename T, int D, int G, int TPT>
+// PAGES: the candidates are the sequence's pages, scored by the Taylor page
+// score; the top-k pages' tokens are attended and listed.
+template <typename T, int D, int G, int TPT, bool PAGES>
 __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   constexpr int HPW = G / 4 > 0 ? G / 4 : 1;   // heads per wave (G >= 4)
   constexpr int DPL = D / 64;
@@ -163,10 +181,11 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   const int rows = s.B * s.Hkv;
   const int b = row / s.Hkv, g = row % s.Hkv;
   const int32_t L = clamp_len(a.seq_lens[b], s.max_len);
-  const int32_t n = L;
+  const int32_t n = PAGES ? (L + kPage - 1) / kPage : L;  // candidates of the row
   const int32_t j0 = bi * a.tpb;
   RowWs* ctl = a.ctl + row;
-  uint32_t bar_target = 0;
+  uint32_t epoch = 0;                       // barriers passed
+  uint32_t* flags = a.flags + (int64_t)row * kMaxNB;
 
   // ---- LDS ----
   __shared__ float s_qc[kRank];
@@ -180,22 +199,92 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   __shared__ __align__(16) T Qs[G][D];
   __shared__ __align__(16) float Ps[G][kTileF];
   // pool token rows ((page * Hkv + g) * 64 + slot) of the tokens to attend
-  __shared__ uint32_t my_list[TPT * kNT + 64];
+  __shared__ uint32_t my_list[PAGES ? kFusedMaxPages * kPage : TPT * kNT + 64];
   // pool pages of the own token range
   __shared__ int32_t s_pt[TPT * kNT / kPage];
   __shared__ uint32_t s_mode, s_prefix, s_thr, s_neq, s_need, s_cnt;
   __shared__ uint64_t s_rem;
   __shared__ uint32_t s_slice[TPT * 4];
+  // page mode: the own selected pages in index order (sequence page, pool page)
+  __shared__ int32_t s_spj[kFusedMaxPages], s_spp[kFusedMaxPages];
+  __shared__ uint32_t s_np;
 
   stamp(a, 0);
-  // ---- 1. scores of the own tokens ----
-  const T* kidx = (const T*)a.kidx;
   const int32_t* pt = a.page_table + (int64_t)b * s.max_pages;
+  float xk[TPT];
+  uint32_t key[TPT];
+  if constexpr (PAGES) {
+    // ---- 1. Taylor scores of the own pages: D / 8 lanes per page as in the
+    // page-score kernel (same operations, same scores).  The page table
+    // entries and the query are fetched together, then up to 16 rounds of
+    // page statistics are in flight at once; the scores are gathered in LDS
+    // in candidate order (the slot of a page first holds its pool page) ----
+    constexpr int LPP = D / 8, PPW = kWave / LPP, PPI = 4 * PPW;  // pages per workgroup round
+    constexpr int PBM = G >= 16 ? 8 : 16;
+    constexpr int NR = TPT * kNT / PPI, PB = NR < PBM ? NR : PBM;   // rounds, rounds in flight
+    static_assert(sizeof(T) == 2, "page mode: bf16 statistics");
+    __shared__ __align__(16) float s_qs[D];
+    __shared__ __align__(16) float s_qq[G][D];
+    __shared__ float s_ps[TPT * kNT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      s_ps[u * kNT + tid] = __int_as_float(j < n ? (int32_t)clamp_page(pt[j], s.n_pool_pages) : 0);
+    }
+    stage_page_query<T, D, G>((const T*)a.q + ((int64_t)b * s.Hq + g * G) * D, a.s_att, s_qs, s_qq, kNT);
+    // the group's query rows for the attention phase
+    for (int i = tid; i < G * D; i += kNT) Qs[i / D][i % D] = ((const T*)a.q)[((int64_t)b * s.Hq + g * G) * D + i];
+    __syncthreads();
+    const int sub = lane % LPP, slot = lane / LPP;
+    const T* stats = (const T*)a.stats;
+    typedef uint32_t w4_t __attribute__((ext_vector_type(4)));
+    for (int r0 = 0; r0 < NR; r0 += PB) {
+      w4_t mraw[PB], vraw[PB];
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int32_t jl = (r0 + u) * PPI + wave * PPW + slot;
+        mraw[u] = w4_t{0u, 0u, 0u, 0u};
+        vraw[u] = w4_t{0u, 0u, 0u, 0u};
+        if (j0 + jl < n) {
+          const int64_t page = __float_as_int(s_ps[jl]);
+          const T* rowp = stats + (page * s.Hkv + g) * 2 * (int64_t)D + sub * 8;
+          mraw[u] = *reinterpret_cast<const w4_t*>(rowp);
+          vraw[u] = *reinterpret_cast<const w4_t*>(rowp + D);
+        }
+      }
+      float qs[8], qq[G][8];
+      page_query_lane<D, G>(s_qs, s_qq, sub, qs, qq);
+#pragma unroll
+      for (int u = 0; u < PB; ++u) {
+        const int32_t jl = (r0 + u) * PPI + wave * PPW + slot;
+        float mu[8], va[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          mu[2 * i] = __uint_as_float(mraw[u][i] << 16);
+          mu[2 * i + 1] = __uint_as_float(mraw[u][i] & 0xffff0000u);
+          va[2 * i] = __uint_as_float(vraw[u][i] << 16);
+          va[2 * i + 1] = __uint_as_float(vraw[u][i] & 0xffff0000u);
+        }
+        const float sum = page_score_sum<LPP, G>(mu, va, qs, qq, sub);
+        if (sub == 0 && j0 + jl < n) s_ps[jl] = page_score_final<G>(sum, L, j0 + jl);
+      }
+    }
+    __syncthreads();
+    float* xr = a.x + (int64_t)row * a.ldx;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      xk[u] = j < n ? s_ps[u * kNT + tid] : 0.f;
+      key[u] = j < n ? score_key(xk[u]) : 0u;
+      if (j < n) xr[j] = xk[u];
+    }
+    stamp(a, 1);
+  } else {
+    // ---- 1. scores of the own tokens ----
+  const T* kidx = (const T*)a.kidx;
   for (int i = tid; i < TPT * kNT / kPage; i += kNT)
     s_pt[i] = j0 + i * kPage < n ? (int32_t)clamp_page(pt[(j0 >> 6) + i], s.n_pool_pages) : 0;
   __syncthreads();
-  float xk[TPT];
-  uint32_t key[TPT];
   {
     // issue the indexer-key loads first, collapse the query while they fly
     float kv[TPT][kRank];
@@ -255,6 +344,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       const float v = wave_sum(acc[c]);
       if (lane == 0) red_f[wave][c] = v;
     }
+    // the group's query rows for the attention phase (just read by the collapse)
+    for (int i = tid; i < G * D; i += kNT) Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
     __syncthreads();
     if (tid < kRank)
       s_qc[tid] = ((red_f[0][tid] + red_f[1][tid]) + (red_f[2][tid] + red_f[3][tid])) * (a.s_idx / (float)G);
@@ -286,9 +377,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       if (m) atomicMax(&ctl->maxkey, m);
     }
   }
-  stamp(a, 1);
-  bar_target += NB;
-  row_barrier(&ctl->bar, bar_target, a.err);
+    stamp(a, 1);
+    // the row maximum is the top-p mass reference
+    row_barrier(flags, NB, bi, ++epoch, a.err);
+  }
   stamp(a, 2);
 
   // ---- 2. threshold by radix levels ----
@@ -316,8 +408,32 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint32_t* gcc = a.ccnt + ((int64_t)li * rows + row) * kCoarseF;
     uint64_t* gcm = a.cmass + ((int64_t)li * rows + row) * kCoarseF;
     if (level == 1) {
-      // every token lands in this level: aggregate in LDS, flush non-empty bins
-      for (int i = tid; i < NBIN; i += kNT) {
+      // every candidate lands in this level: aggregate in LDS, flush the
+      // non-empty bins of the coarse groups the own candidates span
+      uint32_t dhi = 0, dlo_c = 0;  // highest digit + 1, complement of the lowest
+#pragma unroll
+      for (int u = 0; u < TPT; ++u)
+        if (j0 + u * kNT + tid < n) {
+          const uint32_t dg = key[u] >> 20;
+          dhi = dg + 1 > dhi ? dg + 1 : dhi;
+          dlo_c = ~dg > dlo_c ? ~dg : dlo_c;
+        }
+      dhi = wave_max_u32(dhi);
+      dlo_c = wave_max_u32(dlo_c);
+      if (lane == 0) {
+        red_u[wave] = dhi;
+        s_slice[wave] = dlo_c;  // (s_slice is free until the selection)
+      }
+      __syncthreads();
+      uint32_t hi = 0, lo_c = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        hi = red_u[w] > hi ? red_u[w] : hi;
+        lo_c = s_slice[w] > lo_c ? s_slice[w] : lo_c;
+      }
+      // coarse groups [cg_lo, cg_hi) hold every own candidate (none if hi == 0)
+      const int cg_lo = hi ? (int)(~lo_c >> 6) : 0, cg_hi = hi ? (int)((hi - 1) >> 6) + 1 : 0;
+      for (int i = cg_lo * 64 + tid; i < cg_hi * 64; i += kNT) {
         hcnt_l[i] = 0;
         hmass_l[i] = 0;
       }
@@ -334,7 +450,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         }
       }
       __syncthreads();
-      for (int cg = wave; cg < NC; cg += 4) {
+      for (int cg = cg_lo + wave; cg < cg_hi; cg += 4) {
         const int bin = cg * 64 + lane;
         const uint32_t cn = hcnt_l[bin];
         const uint64_t ms = hmass_l[bin];
@@ -370,8 +486,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     stamp(a, 3 * level);
-    bar_target += NB;
-    row_barrier(&ctl->bar, bar_target, a.err);
+    row_barrier(flags, NB, bi, ++epoch, a.err);
     stamp(a, 3 * level + 1);
     // resolve (wave 0): coarse groups, then the 64 bins of the crossing group
     if (wave == 0) {
@@ -479,8 +594,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint32_t tot;
     blk_scan<uint32_t>(e, red_u, tot);
     if (tid == 0) __hip_atomic_store(&a.blk_eq[(int64_t)row * NB + bi], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bar_target += NB;
-    row_barrier(&ctl->bar, bar_target, a.err);
+    row_barrier(flags, NB, bi, ++epoch, a.err);
     {
       uint32_t vb = 0;
       for (int k = tid; k < bi; k += kNT)
@@ -519,6 +633,77 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       selmask[u] = (top || forced ? 1u : 0u) | (forced ? 2u : 0u);
     }
   }
+  if constexpr (PAGES) {
+    // own selected pages in index order; each expands to its tokens (all 64
+    // but the sequence's last page, which is also the last in this order)
+    uint32_t run = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      const bool sel = selmask[u] & 1u;
+      const uint64_t m = __ballot(sel);
+      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
+      __syncthreads();
+      uint32_t before = run;
+      for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
+      uint32_t round_tot = 0;
+      for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
+      if (sel) {
+        const uint32_t k = before + (uint32_t)__popcll(m & lt_mask);
+        if (k < (uint32_t)kFusedMaxPages) {  // at most top_k <= kFusedMaxPages pages per row
+          s_spj[k] = j;
+          s_spp[k] = (int32_t)clamp_page(pt[j], s.n_pool_pages);
+        }
+      }
+      run += round_tot;
+      __syncthreads();
+    }
+    // publish the own pages, meet, and gather the row's page list in index
+    // order (workgroups own ascending page ranges); the row's tokens are
+    // then split evenly over its workgroups for the attention
+    const uint32_t np = run < (uint32_t)kFusedMaxPages ? run : (uint32_t)kFusedMaxPages;
+    int32_t* pl = a.plist + ((int64_t)row * NB + bi) * 2 * kFusedMaxPages;
+    if (tid < np) {
+      __hip_atomic_store(&pl[2 * tid], s_spj[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&pl[2 * tid + 1], s_spp[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (tid == 0) __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    row_barrier(flags, NB, bi, ++epoch, a.err);
+    {
+      // each workgroup's count and first page in one round trip (most
+      // workgroups hold at most one selected page)
+      const int32_t* src = a.plist + ((int64_t)row * NB + tid) * 2 * kFusedMaxPages;
+      uint32_t c = 0;
+      int32_t pj = 0, pp = 0;
+      if (tid < NB) {
+        c = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pj = __hip_atomic_load(&src[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        pp = __hip_atomic_load(&src[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      uint32_t tot;
+      const uint32_t off = blk_scan<uint32_t>(c, red_u, tot);
+      if (c > 0 && off < (uint32_t)kFusedMaxPages) {
+        s_spj[off] = pj;
+        s_spp[off] = pp;
+      }
+      for (uint32_t i2 = 1; i2 < c && off + i2 < (uint32_t)kFusedMaxPages; ++i2) {
+        s_spj[off + i2] = __hip_atomic_load(&src[2 * i2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_spp[off + i2] = __hip_atomic_load(&src[2 * i2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (tid == 0) s_np = tot < (uint32_t)kFusedMaxPages ? tot : (uint32_t)kFusedMaxPages;
+      __syncthreads();
+    }
+    const uint32_t npr = s_np;
+    // every listed page holds 64 tokens but the sequence's last page
+    const uint32_t tot_tok = npr == 0 ? 0u
+        : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
+    const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
+    const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
+    for (uint32_t e = t0 + tid; e < t1; e += kNT)
+      my_list[e - t0] = (uint32_t)(((int64_t)s_spp[e / kPage] * s.Hkv + g) * kPage + (e % kPage));
+    if (tid == 0) s_cnt = t1 - t0;
+    __syncthreads();
+  } else {
   // own non-forced selected tokens -> LDS list (order irrelevant for attention)
   uint32_t my_sel = 0;
   {
@@ -556,12 +741,11 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     }
     __syncthreads();
   }
+  }
   const int32_t n_att = (int32_t)s_cnt;
   {
     const T* k_pool = (const T*)a.k_pool;
     const T* v_pool = (const T*)a.v_pool;
-    const T* q = (const T*)a.q;
-    for (int i = tid; i < G * D; i += kNT) Qs[i / D][i % D] = q[((int64_t)b * s.Hq + g * G) * D + i];
     float m_run[HPW], l_run[HPW], acc[HPW][DPL];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -694,14 +878,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     }
   }
   stamp(a, 12);
-  bar_target += NB;
-  row_barrier(&ctl->bar, bar_target, a.err);
+  row_barrier(flags, NB, bi, ++epoch, a.err);
   stamp(a, 13);
 
   // ---- 4. ordered index list and the merge of this workgroup's output slice ----
   {
     __shared__ uint32_t s_base, s_total;
-    {
+    if constexpr (!PAGES) {
       uint32_t vb = 0, vt = 0;
       for (int k = tid; k < NB; k += kNT) {
         const uint32_t v = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -718,6 +901,18 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       __syncthreads();
     }
     int32_t* outl = a.idx + (int64_t)row * a.cap;
+    if constexpr (PAGES) {
+      // the own token slice of the row's list (the attention's slice)
+      const uint32_t npr = s_np;
+      const uint32_t tot_tok = npr == 0 ? 0u
+          : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
+      const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
+      const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
+      for (uint32_t e = t0 + tid; e < t1 && e < (uint32_t)a.cap; e += kNT)
+        outl[e] = s_spj[e / kPage] * kPage + (int32_t)(e % kPage);
+      if (tid == 0) s_total = tot_tok;
+      __syncthreads();
+    } else {
     uint32_t run = s_base;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
@@ -736,6 +931,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       run += round_tot;
       __syncthreads();
     }
+    }
     const uint32_t total = s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap;
     const int64_t pad = (int64_t)a.cap - total;
     const int64_t p0 = total + (pad * bi) / NB, p1 = total + (pad * (bi + 1)) / NB;
@@ -752,16 +948,33 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       const int sub = tid % 16;
       if (oo >= lim) continue;  // whole 16-lane groups skip together
       const int hl = oo / D, d = oo % D;
+      // every partial this lane merges, loaded in one round trip
+      constexpr int KP = kMaxNB / 16;
+      float pm[KP], pl[KP], po[KP];
+#pragma unroll
+      for (int t = 0; t < KP; ++t) {
+        const int k = sub + 16 * t;
+        pm[t] = -INFINITY;
+        pl[t] = 0.f;
+        po[t] = 0.f;
+        if (k < NB) {
+          const int64_t pi = ((int64_t)row * NB + k) * G + hl;
+          pm[t] = ld_dev(&a.part_ml[pi * 2]);
+          pl[t] = ld_dev(&a.part_ml[pi * 2 + 1]);
+          po[t] = ld_dev(&a.part_o[pi * D + d]);
+        }
+      }
       float M2 = -INFINITY;
-      for (int k = sub; k < NB; k += 16) M2 = fmaxf(M2, ld_dev(&a.part_ml[(((int64_t)row * NB + k) * G + hl) * 2]));
+#pragma unroll
+      for (int t = 0; t < KP; ++t) M2 = fmaxf(M2, pm[t]);
       M2 = row16_max(M2);
       float lsum = 0.f, osum = 0.f;
-      for (int k = sub; k < NB; k += 16) {
-        const int64_t pi = ((int64_t)row * NB + k) * G + hl;
-        const float mk2 = ld_dev(&a.part_ml[pi * 2]);
-        const float wgt = mk2 == -INFINITY ? 0.f : __expf(mk2 - M2);
-        lsum += ld_dev(&a.part_ml[pi * 2 + 1]) * wgt;
-        osum += ld_dev(&a.part_o[pi * D + d]) * wgt;
+#pragma unroll
+      for (int t = 0; t < KP; ++t) {
+        if (sub + 16 * t >= NB) break;
+        const float wgt = pm[t] == -INFINITY ? 0.f : __expf(pm[t] - M2);
+        lsum += pl[t] * wgt;
+        osum += po[t] * wgt;
       }
       lsum = row16_sum(lsum);
       osum = row16_sum(osum);
@@ -798,7 +1011,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       const uint32_t old = atomicAdd(&ctl->exit, 1u);
       if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
         ctl->maxkey = 0;
-        ctl->bar = 0;
+        for (int k = 0; k < NB; ++k) flags[k] = 0;
         ctl->exit = 0;
       }
     }
@@ -820,6 +1033,8 @@ size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   b += align_up(sizeof(float) * rows * nb * G * D, 256);
   b += 256;  // error flag
   b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
+  b += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
+  b += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
   return b;
 }
 
@@ -851,6 +1066,76 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, i
   return true;
 }
 
+// Plan of the page-level step: the candidates are the ceil(max_len / 64)
+// pages, at most kFusedMaxPages of them selected.
+bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb) {
+  if (top_k < 1 || top_k > kFusedMaxPages) return false;
+  Shape sp = s;
+  sp.max_len = (s.max_len + kPage - 1) / kPage;
+  return fused_plan(sp, 0, 0, nb, tpb);
+}
+
+namespace {
+
+// Carves the workspace laid out by fused_workspace_bytes.
+void fused_ws(FusedArgs& a, void* ws, int rows, int nb, int G, int D) {
+  char* w = (char*)ws;
+  a.ctl = (RowWs*)w;            w += align_up(sizeof(RowWs) * rows, 256);
+  a.hcnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
+  a.hmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
+  a.ccnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
+  a.cmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
+  a.blk_sel = (uint32_t*)w;     w += align_up(sizeof(uint32_t) * rows * nb, 256);
+  a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
+  a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
+  a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * D, 256);
+  a.err = (uint32_t*)w;         w += 256;
+  a.trace = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
+  a.plist = (int32_t*)w;         w += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
+  a.flags = (uint32_t*)w;
+}
+
+}  // namespace
+
+hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const void* q,
+                                     const void* stats_pool, const void* k_pool, const void* v_pool,
+                                     float s_att, int32_t top_k, float* x, int64_t ldx,
+                                     int32_t* idx, int32_t* count, int32_t cap, void* out,
+                                     sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
+                                     hipStream_t st) {
+  const int rows = s.B * s.Hkv;
+  const int G = s.Hq / s.Hkv;
+  FusedArgs a{};
+  a.q = q; a.stats = stats_pool; a.k_pool = k_pool; a.v_pool = v_pool;
+  a.page_table = pg.page_table; a.seq_lens = pg.seq_lens; a.s = s;
+  a.s_att = s_att; a.p = 0.f; a.top_k = top_k; a.n_sink = 0; a.n_window = 0;
+  a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
+  a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
+  fused_ws(a, ws, rows, nb, G, s.D);
+  const int tpt = tpb / kNT;
+  dim3 grid(rows * nb);
+#define SA_FP(DD, GG, PP) k_decode_fused<bf16_raw, DD, GG, PP, true><<<grid, kNT, 0, st>>>(a)
+#define SA_FP_T(DD, GG)                  \
+  switch (tpt) {                         \
+    case 1: SA_FP(DD, GG, 1); break;     \
+    case 2: SA_FP(DD, GG, 2); break;     \
+    case 4: SA_FP(DD, GG, 4); break;     \
+    case 8: SA_FP(DD, GG, 8); break;     \
+    default: SA_FP(DD, GG, 16); break;   \
+  }
+#define SA_FP_G(DD)                      \
+  switch (G) {                           \
+    case 4: SA_FP_T(DD, 4); break;       \
+    case 8: SA_FP_T(DD, 8); break;       \
+    default: SA_FP_T(DD, 16); break;     \
+  }
+  if (s.D == 128) { SA_FP_G(128); } else { SA_FP_G(64); }
+#undef SA_FP_G
+#undef SA_FP_T
+#undef SA_FP
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q, const void* w_q,
                                const void* kidx_pool, const void* k_pool, const void* v_pool,
                                sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
@@ -866,21 +1151,10 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
   a.s_idx = s_idx; a.s_att = s_att; a.p = p; a.top_k = top_k; a.n_sink = n_sink;
   a.n_window = n_window; a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
   a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
-  char* w = (char*)ws;
-  a.ctl = (RowWs*)w;            w += align_up(sizeof(RowWs) * rows, 256);
-  a.hcnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
-  a.hmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
-  a.ccnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
-  a.cmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
-  a.blk_sel = (uint32_t*)w;     w += align_up(sizeof(uint32_t) * rows * nb, 256);
-  a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
-  a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
-  a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * s.D, 256);
-  a.err = (uint32_t*)w;           w += 256;
-  a.trace = (uint64_t*)w;
+  fused_ws(a, ws, rows, nb, G, s.D);
   const int tpt = tpb / kNT;  // 1, 2, 4, 8 or 16 (fused_plan)
   dim3 grid(rows * nb);
-#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP><<<grid, kNT, 0, st>>>(a)
+#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP, false><<<grid, kNT, 0, st>>>(a)
 #define SA_FZ_T(TT, DD, GG)              \
   switch (tpt) {                         \
     case 1: SA_FZ(TT, DD, GG, 1); break;  \

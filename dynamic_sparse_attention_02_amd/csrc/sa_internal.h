@@ -367,6 +367,13 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
 
 size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D);
 bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, int32_t* tpb);
+bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb);
+hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const void* q,
+                                     const void* stats_pool, const void* k_pool, const void* v_pool,
+                                     float s_att, int32_t top_k, float* x, int64_t ldx,
+                                     int32_t* idx, int32_t* count, int32_t cap, void* out,
+                                     sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
+                                     hipStream_t st);
 hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q, const void* w_q,
                                const void* kidx_pool, const void* k_pool, const void* v_pool,
                                sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,

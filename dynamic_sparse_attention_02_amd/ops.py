@@ -32,6 +32,7 @@ __all__ = [
     "sa_attention_mass",
     "sa_support_coverage",
     "sa_decode_step",
+    "sa_decode_step_pages",
     "sa_select_prefill_topk",
     "sa_sparse_prefill",
     "sa_select_prefill_topk_probs",
@@ -201,6 +202,17 @@ def sa_decode_step(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att
                                  int(idx.shape[-1]), _dev(out), _dt(out), _dev(lse), wp, wn,
                                  _stream(stream))
     L.check(st, "sa_decode_step")
+
+
+def sa_decode_step_pages(shape, pages, q, stats_pool, k_pool, v_pool, s_att, top_k, x, idx, count,
+                         out, lse, ws, stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_decode_step_pages(ctypes.byref(shape), ctypes.byref(pages), _dev(q),
+                                       _dev(stats_pool), _dev(k_pool), _dev(v_pool), _dt(q),
+                                       float(s_att), int(top_k), _dev(x), int(x.stride(0)),
+                                       _dev(idx), _dev(count), int(idx.shape[-1]), _dev(out),
+                                       _dt(out), _dev(lse), wp, wn, _stream(stream))
+    L.check(st, "sa_decode_step_pages")
 
 
 def sa_select_prefill_topk(shape, pages, n_tokens, q, w_q, kidx_pool, s_idx, b_sel, k, idx,

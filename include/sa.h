@@ -101,7 +101,8 @@ typedef enum {
   SA_OP_PREFILL_QUERY = 7,     /* param = cap                                    */
   SA_OP_PBS_IMPORTANCE = 8,    /* param = n_rows                                 */
   SA_OP_PBS_SELECT = 9,        /* param = k_blocks                               */
-  SA_OP_PREFILL_ORACLE = 10    /* param unused                                   */
+  SA_OP_PREFILL_ORACLE = 10,   /* param unused                                   */
+  SA_OP_DECODE_STEP_PAGES = 11 /* param = cap                                    */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -261,6 +262,24 @@ sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const voi
                          float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
                          void* out, sa_dtype out_dtype, float* lse, void* ws,
                          size_t ws_bytes, hipStream_t stream);
+
+/* One whole page-level decode step ("SPLA", section 2.1: pages ranked by the
+ * Taylor score, the top_k pages attended exactly): sa_page_scores, then
+ * sa_select_topk with unit = page_size (n_sink = n_window = 0), then
+ * sa_sparse_decode, with the same results as those three calls.  The page
+ * scores x ([batch * n_kv_heads][ldx] fp32, ldx >= max_pages), idx and count
+ * are outputs too; cap >= min(top_k * page_size, max_len).  stats_pool as
+ * written by sa_page_stats; q, stats_pool, k_pool, v_pool of dtype.  With few
+ * rows (batch * n_kv_heads <= 16, group size >= 4, top_k <= 32, bf16) the step
+ * runs as one persistent launch whose workgroups meet at bounded in-memory
+ * barriers; otherwise as the three launches.  Workspace from
+ * SA_OP_DECODE_STEP_PAGES (param = cap). */
+sa_status sa_decode_step_pages(const sa_shape* shape, const sa_pages* pages, const void* q,
+                               const void* stats_pool, const void* k_pool, const void* v_pool,
+                               sa_dtype dtype, float s_att, int32_t top_k, float* x, int64_t ldx,
+                               int32_t* idx, int32_t* count, int32_t cap, void* out,
+                               sa_dtype out_dtype, float* lse, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Attention-mass oracle support and coverage

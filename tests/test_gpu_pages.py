@@ -231,3 +231,129 @@ def test_decode1m_workload():
         found.append(len(gp & set(inp.planted[(0, g)].tolist())))
     print(f"decode1m: planted pages selected per group {found} of 16, "
           f"tolerated support differences {n_diff}")
+
+
+def run_step_pages(inp, pool, k_pages, out_dtype=torch.float32, ws=None):
+    """sa_decode_step_pages: the whole page-level step in one call."""
+    o = ops()
+    from dynamic_sparse_attention_02_amd import _lib as L
+    shape = S.shape_of(inp)
+    pages = o.make_pages(inp.page_table, inp.seq_lens_tensor())
+    rows = inp.B * inp.H_kv
+    cap = min(k_pages * PAGE, max(max(inp.seq_lens), 1))
+    x = torch.full((rows, inp.max_pages), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.full((rows, cap), -7, dtype=torch.int32, device="cuda")
+    count = torch.full((rows,), -7, dtype=torch.int32, device="cuda")
+    out = torch.full((inp.B, inp.H_q, inp.d), float("nan"), dtype=out_dtype, device="cuda")
+    lse = torch.full((inp.B, inp.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    if ws is None:
+        ws = o.alloc_workspace(o.workspace_size(L.SA_OP_DECODE_STEP_PAGES, shape, cap))
+    o.sa_decode_step_pages(shape, pages, inp.q, pool, inp.k_pool, inp.v_pool, inp.s_att, k_pages,
+                           x, idx, count, out, lse, ws)
+    torch.cuda.synchronize()
+    return x, idx, count, out, lse
+
+
+def assert_same_step(inp, a, b, tol):
+    """Same page scores, index lists and counts; outputs within tol (the two
+    paths sum the softmax in different orders)."""
+    xa, ia, ca, oa, la = a
+    xb, ib, cb, ob, lb = b
+    for r in range(inp.B * inp.H_kv):
+        L = inp.seq_lens[r // inp.H_kv]
+        npg = (L + PAGE - 1) // PAGE
+        assert torch.equal(xa[r, :npg], xb[r, :npg]), r
+    assert torch.equal(ca, cb)
+    assert torch.equal(ia, ib)
+    assert S.max_abs(S.to_np(oa), S.to_np(ob)) <= tol
+    fin = torch.isfinite(lb)
+    assert torch.equal(fin, torch.isfinite(la))
+    assert S.max_abs(la[fin].cpu().numpy(), lb[fin].cpu().numpy()) <= max(tol, 1e-5) * max(
+        1.0, float(lb[fin].abs().max()) if fin.any() else 1.0)
+
+
+@pytest.mark.parametrize("G,d,k_pages,seq_lens", [
+    (4, 128, 6, [64 * 40 + 17, 0, 64 * 3, 2500]),
+    (8, 128, 32, [64 * 700 + 1, 64 * 31, 64 * 500]),
+    (16, 128, 1, [100000, 65]),
+    (8, 64, 17, [64 * 900, 64 * 2000 + 63]),
+])
+def test_decode_step_pages_fused_matches_calls(G, d, k_pages, seq_lens):
+    """The one-launch page-level step (bf16, few rows, top-k <= 32 pages)
+    against the three separate calls and against the oracle: ragged rows with
+    partial last pages, an empty row, rows with fewer pages than k."""
+    inp = synth.make_decode_custom(B=len(seq_lens), H_q=2 * G, H_kv=2, d=d, seq_lens=seq_lens,
+                                   dtype=torch.bfloat16, device="cuda", seed=40 + G + k_pages,
+                                   hh_frac=0.01, alpha=10.0, shuffle=True)
+    pool, rows = oracle_stats_pool(inp)
+    tol = S.TOL[torch.bfloat16]
+    ref = run_page_decode(inp, pool, k_pages)
+    got = run_step_pages(inp, pool, k_pages)
+    assert_same_step(inp, got, ref, tol)
+    check_page_rows(inp, rows, *got, k_pages, range(inp.H_kv), tol)
+
+
+@pytest.mark.parametrize("dtype,G,k_pages", [(torch.float32, 8, 6), (torch.bfloat16, 2, 6),
+                                             (torch.bfloat16, 8, 40)])
+def test_decode_step_pages_separate_path(dtype, G, k_pages):
+    """Problems outside the one-launch plan (fp32, group size 2, more than 32
+    pages) run as the three calls, with the same results."""
+    inp = synth.make_decode_custom(B=3, H_q=2 * G, H_kv=2, d=128,
+                                   seq_lens=[64 * 60 + 5, 64 * 3, 3000], dtype=dtype,
+                                   device="cuda", seed=60 + G, hh_frac=0.01, alpha=10.0,
+                                   shuffle=True)
+    pool, rows = oracle_stats_pool(inp)
+    ref = run_page_decode(inp, pool, k_pages)
+    got = run_step_pages(inp, pool, k_pages)
+    assert_same_step(inp, got, ref, S.TOL[dtype])
+    check_page_rows(inp, rows, *got, k_pages, range(inp.H_kv), S.TOL[dtype])
+
+
+def test_decode_step_pages_ties():
+    """Exact ties spread over workgroups: every 100th page of a row has zero
+    mean and unit variance, every other page zero statistics, so the scores
+    take two values (and the length term of a partial last page).  Row 0 has
+    30 tied high pages for 20 places: the 20 lowest indices win; row 1 has 8
+    high pages and 12 places among the tied low pages.  Two calls on one
+    workspace, both equal to the three separate calls."""
+    from dynamic_sparse_attention_02_amd import _lib as L
+    o = ops()
+    inp = synth.make_decode_custom(B=2, H_q=16, H_kv=2, d=128, seq_lens=[64 * 3000 + 9, 64 * 777],
+                                   dtype=torch.bfloat16, device="cuda", seed=71, shuffle=True)
+    pool = torch.zeros((inp.n_pages, inp.H_kv, 2, inp.d), dtype=inp.dtype, device="cuda")
+    for b in range(inp.B):
+        pids, _ = seq_pages(inp, b)
+        pool[pids[::100].cuda(), :, 1] = 1.0
+    k_pages = 20
+    shape = S.shape_of(inp)
+    ws = o.alloc_workspace(o.workspace_size(L.SA_OP_DECODE_STEP_PAGES, shape, k_pages * PAGE))
+    ref = run_page_decode(inp, pool, k_pages)
+    want = {0: list(range(0, 2000, 100)),
+            1: sorted(list(range(0, 777, 100)) + list(range(1, 13)))}
+    for _ in range(2):
+        got = run_step_pages(inp, pool, k_pages, ws=ws)
+        assert_same_step(inp, got, ref, S.TOL[torch.bfloat16])
+        idx, count = got[1], got[2]
+        for r in range(inp.B * inp.H_kv):
+            b = r // inp.H_kv
+            toks = S.gpu_support(idx, count, r)
+            assert toks.tolist() == O.expand_pages(np.array(want[b]), inp.seq_lens[b],
+                                                   PAGE).tolist(), r
+
+
+def test_decode_step_pages_decode1m():
+    """The 1M-token page workload through the one-launch step: the same
+    scores, lists and counts as the three calls and outputs within the bf16
+    bound, twice on one workspace; then against the oracle."""
+    from dynamic_sparse_attention_02_amd import _lib as L
+    o = ops()
+    inp = synth.make_decode1m(device="cuda")
+    k_pages = inp.select["k_pages"]
+    pool, rows = oracle_stats_pool(inp)
+    shape = S.shape_of(inp)
+    ws = o.alloc_workspace(o.workspace_size(L.SA_OP_DECODE_STEP_PAGES, shape, k_pages * PAGE))
+    ref = run_page_decode(inp, pool, k_pages, out_dtype=torch.bfloat16)
+    for _ in range(2):
+        got = run_step_pages(inp, pool, k_pages, out_dtype=torch.bfloat16, ws=ws)
+        assert_same_step(inp, got, ref, S.TOL[torch.bfloat16])
+    check_page_rows(inp, rows, *got, k_pages, range(inp.H_kv), S.TOL[torch.bfloat16])
