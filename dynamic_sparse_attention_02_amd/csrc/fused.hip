@@ -54,8 +54,7 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 struct RowWs {            // per-row control block (zero between launches)
   uint32_t exit;          // workgroups done
-  uint32_t maxkey;        // row maximum score key
-  uint32_t pad[14];
+  uint32_t pad[15];
 };
 
 struct FusedArgs {
@@ -92,6 +91,7 @@ struct FusedArgs {
   float* part_o;          // [rows][nb][G][D]
   uint32_t* err;          // set to 1 if a barrier gave up waiting
   uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
+  uint64_t* mflag;        // [rows][kMaxNB] marker bit 32 | own maximum score key
   int32_t* plist;         // page mode: [rows][nb][kFusedMaxPages][2] own pages (sequence, pool)
   uint32_t* flags;        // [rows][kMaxNB] barrier arrival flags (barriers passed)
 };
@@ -136,6 +136,46 @@ __device__ __forceinline__ void row_barrier(uint32_t* flags, int nb, int bi, uin
     }
   }
   __syncthreads();
+}
+
+// The first barrier of a top-p row also yields the row's maximum score key:
+// each workgroup stores its own maximum under a marker bit in one 64-bit
+// word (written once per launch, so a word never changes while another
+// workgroup polls it), and the polling wave reduces the words once every
+// one is marked.  Bounded like row_barrier.
+__device__ __forceinline__ uint32_t row_barrier_max(uint64_t* mflag, int nb, int bi, uint32_t mine,
+                                                    uint32_t* err) {
+  __shared__ uint32_t s_rowmax;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    if (threadIdx.x == 0)
+      __hip_atomic_store(&mflag[bi], (1ull << 32) | mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t spins = 0;
+    for (;;) {
+      bool ok = true;
+      uint32_t m = 0;
+      for (int k = (int)threadIdx.x; k < nb; k += kWave) {
+        const uint64_t f = __hip_atomic_load(&mflag[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = ok && (f >> 32) != 0;
+        m = (uint32_t)f > m ? (uint32_t)f : m;
+      }
+      const bool done = __all(ok);
+      if (done || ++spins > kSpinLimit) {
+        m = wave_max_u32(m);
+        if (threadIdx.x == 0) {
+          s_rowmax = m;
+          if (!done) atomicOr(err, 1u);
+        }
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+  __syncthreads();
+  return s_rowmax;
 }
 
 __device__ __forceinline__ void st_dev(float* p, float v) {
@@ -213,6 +253,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   const int32_t* pt = a.page_table + (int64_t)b * s.max_pages;
   float xk[TPT];
   uint32_t key[TPT];
+  uint32_t M = 0;         // row maximum score key (top-p)
+  uint32_t own_max = 0;   // this workgroup's maximum (thread 0)
   if constexpr (PAGES) {
     // ---- 1. Taylor scores of the own pages: D / 8 lanes per page as in the
     // page-score kernel (same operations, same scores).  The page table
@@ -372,20 +414,18 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     if (lane == 0) red_u[wave] = mk;
     __syncthreads();
     if (tid == 0) {
-      uint32_t m = 0;
-      for (int i = 0; i < 4; ++i) m = red_u[i] > m ? red_u[i] : m;
-      if (m) atomicMax(&ctl->maxkey, m);
+      for (int i = 0; i < 4; ++i) mk = red_u[i] > mk ? red_u[i] : mk;
+      own_max = mk;
     }
   }
     stamp(a, 1);
     // the row maximum is the top-p mass reference
-    row_barrier(flags, NB, bi, ++epoch, a.err);
+    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, a.err);
   }
   stamp(a, 2);
 
   // ---- 2. threshold by radix levels ----
   const bool topk = a.top_k > 0;
-  const uint32_t M = __hip_atomic_load(&ctl->maxkey, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float mx = key_score(M);
   if (tid == 0) {
     s_mode = kSearch;
@@ -450,19 +490,22 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         }
       }
       __syncthreads();
+      stamp(a, 15);
       for (int cg = cg_lo + wave; cg < cg_hi; cg += 4) {
         const int bin = cg * 64 + lane;
         const uint32_t cn = hcnt_l[bin];
         const uint64_t ms = hmass_l[bin];
+        // top-p resolves level 1 by mass alone: its counts would only
+        // serve the single-candidate shortcut, so they are not sent
         if (cn) {
-          atomicAdd(&gc[bin], cn);
-          if (!topk) atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
+          if (topk) atomicAdd(&gc[bin], cn);
+          else atomicAdd((unsigned long long*)&gm[bin], (unsigned long long)ms);
         }
         const uint32_t csum = wave_sum_u32(cn);
         const uint64_t msum = topk ? 0ull : wave_sum_u64(ms);
         if (lane == 0 && csum) {
-          atomicAdd(&gcc[cg], csum);
-          if (!topk) atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
+          if (topk) atomicAdd(&gcc[cg], csum);
+          else atomicAdd((unsigned long long*)&gcm[cg], (unsigned long long)msum);
         }
       }
     } else {
@@ -743,9 +786,169 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   }
   }
   const int32_t n_att = (int32_t)s_cnt;
+  stamp(a, 5);
   {
     const T* k_pool = (const T*)a.k_pool;
     const T* v_pool = (const T*)a.v_pool;
+    if constexpr (sizeof(T) == 2) {
+    // Matrix-core attention: in each 64-token tile wave w takes tokens
+    // [16w, 16w + 16).  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves a lane
+    // with 4 tokens of one head (head = lane % 16, the group's heads padded
+    // to 16 with zero queries), which is the lane layout of the P^T operand
+    // of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, so each wave runs its own
+    // online softmax without exchanging scores.  P enters the product as a
+    // bf16 high part plus the bf16 rounding of the remainder (16 significant
+    // bits); V is staged transposed.  The four waves' softmax states are
+    // merged once at the end.
+    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+    typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+    typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+    constexpr int VP = kTileF + 4;  // V^T row pitch in bf16 (8-byte aligned rows)
+    constexpr int KS = D / 32, MB = D / 16;
+    static_assert(D * VP * 2 <= kTileF * PITCH, "V^T tile fits the V buffer");
+    static_assert(2 * D * 16 * 4 <= kTileF * PITCH, "two waves' outputs fit one tile buffer");
+    __shared__ float s_wm[4][16], s_wl[4][16];
+    bf16_raw* Vt = reinterpret_cast<bf16_raw*>(Vs);
+    const int hq = lane & 15, lg = lane >> 4;
+    bf16x8_t qB[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (hq < G) w = *reinterpret_cast<const uint4*>(&Qs[hq < G ? hq : 0][32 * ks + 8 * lg]);
+      qB[ks] = __builtin_bit_cast(bf16x8_t, w);
+    }
+    f32x4_t oacc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+    // K rows: 16 lanes per row (contiguous loads); V rows: one row per lane,
+    // so a wave's transposed LDS writes cover 64 consecutive tokens.  NBUF
+    // tiles of rows are in flight
+    constexpr int NBUF = 2;
+    uint4 kq[NBUF][LPT], vq[NBUF][LPT];
+    auto gather = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = i * kNT + tid;
+        const int rk = pc / CPR, ck = pc % CPR;
+        const int rv = pc % kTileF, cv = pc / kTileF;
+        kr[i] = make_uint4(0, 0, 0, 0);
+        vr[i] = make_uint4(0, 0, 0, 0);
+        if (ts + rk < n_att)
+          kr[i] = *reinterpret_cast<const uint4*>(k_pool + (int64_t)my_list[ts + rk] * D + ck * 8);
+        if (ts + rv < n_att)
+          vr[i] = *reinterpret_cast<const uint4*>(v_pool + (int64_t)my_list[ts + rv] * D + cv * 8);
+      }
+    };
+    auto tile = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
+      const int32_t nt = min(kTileF, n_att - ts);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int pc = i * kNT + tid;
+        const int rk = pc / CPR, ck = pc % CPR;
+        const int rv = pc % kTileF, cv = pc / kTileF;
+        *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) = kr[i];
+        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Vt[(cv * 8 + 2 * e) * VP + rv] = (bf16_raw)(w[e] & 0xffffu);
+          Vt[(cv * 8 + 2 * e + 1) * VP + rv] = (bf16_raw)(w[e] >> 16);
+        }
+      }
+      __syncthreads();
+      if (ts + NBUF * kTileF < n_att) gather(ts + NBUF * kTileF, kr, vr);
+      f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qB[ks], S, 0, 0, 0);
+      }
+      float sv[4], mt = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = 16 * wave + 4 * lg + v < nt ? S[v] * a.s_att : -INFINITY;
+        mt = fmaxf(mt, sv[v]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float mu = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __expf(m_run - mu);  // 0 before the first valid token
+      float pv[4], ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[v] = __expf(sv[v] - mu);
+        ls += pv[v];
+      }
+      l_run = l_run * alpha + ls;
+      m_run = m_new;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        const bf16_raw h0 = f32_to_bf16(pv[2 * v]), h1 = f32_to_bf16(pv[2 * v + 1]);
+        const bf16_raw l0 = f32_to_bf16(pv[2 * v] - bf16_to_f32(h0));
+        const bf16_raw l1 = f32_to_bf16(pv[2 * v + 1] - bf16_to_f32(h1));
+        hi[v] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        lo[v] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+      }
+      const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(hi[0], hi[1]));
+      const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(lo[0], lo[1]));
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        oacc[mb] *= alpha;
+        const uint2 vv = *reinterpret_cast<const uint2*>(Vt + (16 * mb + hq) * VP + 16 * wave + 4 * lg);
+        const s16x4_t av = __builtin_bit_cast(s16x4_t, vv);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u)
+      if (u * kTileF < n_att) gather(u * kTileF, kq[u], vq[u]);
+    for (int32_t ts = 0; ts < n_att; ts += NBUF * kTileF) {
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u)
+        if (ts + u * kTileF < n_att) tile(ts + u * kTileF, kq[u], vq[u]);
+    }
+    stamp(a, 8);
+    // merge the waves: lane (lg, hq) holds O^T[16 mb + 4 lg + v][hq]
+    float lw = l_run;
+    lw += __shfl_xor(lw, 16, 64);
+    lw += __shfl_xor(lw, 32, 64);
+    __syncthreads();  // the tile buffers are free
+    float* ob = reinterpret_cast<float*>(wave < 2 ? Ks : Vs) + (wave & 1) * D * 16;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ob[(16 * mb + 4 * lg + v) * 16 + hq] = oacc[mb][v];
+    if (lane < 16) {
+      s_wm[wave][lane] = m_run;
+      s_wl[wave][lane] = lw;
+    }
+    __syncthreads();
+    for (int e = tid; e < G * D; e += kNT) {
+      const int hl = e / D, d = e % D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, s_wm[w][hl]);
+      float lsum = 0.f, osum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float wt = s_wm[w][hl] == -INFINITY ? 0.f : __expf(s_wm[w][hl] - M);
+        const float* obw = reinterpret_cast<const float*>(w < 2 ? Ks : Vs) + (w & 1) * D * 16;
+        lsum += s_wl[w][hl] * wt;
+        osum += obw[d * 16 + hl] * wt;
+      }
+      const int64_t pi = ((int64_t)row * NB + bi) * G + hl;
+      st_dev(&a.part_o[pi * D + d], osum);
+      if (d == 0) {
+        st_dev(&a.part_ml[pi * 2], M);
+        st_dev(&a.part_ml[pi * 2 + 1], lsum);
+      }
+    }
+    } else {
     float m_run[HPW], l_run[HPW], acc[HPW][DPL];
 #pragma unroll
     for (int hh = 0; hh < HPW; ++hh) {
@@ -876,67 +1079,19 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) st_dev(&a.part_o[pi * D + lane * DPL + e], acc[hh][e]);
     }
+    }
   }
   stamp(a, 12);
   row_barrier(flags, NB, bi, ++epoch, a.err);
   stamp(a, 13);
 
-  // ---- 4. ordered index list and the merge of this workgroup's output slice ----
+  // ---- 4. merge of this workgroup's output slice and the ordered index list ----
   {
-    __shared__ uint32_t s_base, s_total;
-    if constexpr (!PAGES) {
-      uint32_t vb = 0, vt = 0;
-      for (int k = tid; k < NB; k += kNT) {
-        const uint32_t v = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        vt += v;
-        if (k < bi) vb += v;
-      }
-      uint32_t tb, tt;
-      blk_scan<uint32_t>(vb, red_u, tb);
-      blk_scan<uint32_t>(vt, red_u, tt);
-      if (tid == 0) {
-        s_base = tb;
-        s_total = tt;
-      }
-      __syncthreads();
-    }
-    int32_t* outl = a.idx + (int64_t)row * a.cap;
-    if constexpr (PAGES) {
-      // the own token slice of the row's list (the attention's slice)
-      const uint32_t npr = s_np;
-      const uint32_t tot_tok = npr == 0 ? 0u
-          : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
-      const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
-      const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
-      for (uint32_t e = t0 + tid; e < t1 && e < (uint32_t)a.cap; e += kNT)
-        outl[e] = s_spj[e / kPage] * kPage + (int32_t)(e % kPage);
-      if (tid == 0) s_total = tot_tok;
-      __syncthreads();
-    } else {
-    uint32_t run = s_base;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-      const bool sel = selmask[u] & 1u;
-      const uint64_t m = __ballot(sel);
-      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
-      __syncthreads();
-      uint32_t before = run;
-      for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
-      uint32_t round_tot = 0;
-      for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
-      if (sel) {
-        const uint32_t pos = before + (uint32_t)__popcll(m & lt_mask);
-        if (pos < (uint32_t)a.cap) outl[pos] = j0 + u * kNT + tid;
-      }
-      run += round_tot;
-      __syncthreads();
-    }
-    }
-    const uint32_t total = s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap;
-    const int64_t pad = (int64_t)a.cap - total;
-    const int64_t p0 = total + (pad * bi) / NB, p1 = total + (pad * (bi + 1)) / NB;
-    for (int64_t o = p0 + tid; o < p1; o += kNT) outl[o] = -1;
-    if (bi == 0 && tid == 0) a.count[row] = (int32_t)total;
+    // the workgroups' selected counts, loaded now and used after the merge
+    // (so their round trip overlaps the partials')
+    uint32_t bsel = 0;
+    if constexpr (!PAGES)
+      if (tid < NB) bsel = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     // outputs [bi * opb, (bi + 1) * opb) of the row's G * D values
     const int n_out = G * D;
     const int opb = (n_out + NB - 1) / NB;
@@ -986,6 +1141,55 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         if (d == 0 && a.lse) a.lse[(int64_t)b * s.Hq + h] = lsum > 0.f ? M2 + logf(lsum) : -INFINITY;
       }
     }
+    __shared__ uint32_t s_base, s_total;
+    if constexpr (!PAGES) {
+      const uint32_t vt = bsel, vb = tid < bi ? bsel : 0u;
+      uint32_t tb, tt;
+      blk_scan<uint32_t>(vb, red_u, tb);
+      blk_scan<uint32_t>(vt, red_u, tt);
+      if (tid == 0) {
+        s_base = tb;
+        s_total = tt;
+      }
+      __syncthreads();
+    }
+    int32_t* outl = a.idx + (int64_t)row * a.cap;
+    if constexpr (PAGES) {
+      // the own token slice of the row's list (the attention's slice)
+      const uint32_t npr = s_np;
+      const uint32_t tot_tok = npr == 0 ? 0u
+          : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
+      const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
+      const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
+      for (uint32_t e = t0 + tid; e < t1 && e < (uint32_t)a.cap; e += kNT)
+        outl[e] = s_spj[e / kPage] * kPage + (int32_t)(e % kPage);
+      if (tid == 0) s_total = tot_tok;
+      __syncthreads();
+    } else {
+    uint32_t run = s_base;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const bool sel = selmask[u] & 1u;
+      const uint64_t m = __ballot(sel);
+      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
+      __syncthreads();
+      uint32_t before = run;
+      for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
+      uint32_t round_tot = 0;
+      for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
+      if (sel) {
+        const uint32_t pos = before + (uint32_t)__popcll(m & lt_mask);
+        if (pos < (uint32_t)a.cap) outl[pos] = j0 + u * kNT + tid;
+      }
+      run += round_tot;
+      __syncthreads();
+    }
+    }
+    const uint32_t total = s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap;
+    const int64_t pad = (int64_t)a.cap - total;
+    const int64_t p0 = total + (pad * bi) / NB, p1 = total + (pad * (bi + 1)) / NB;
+    for (int64_t o = p0 + tid; o < p1; o += kNT) outl[o] = -1;
+    if (bi == 0 && tid == 0) a.count[row] = (int32_t)total;
   }
 
   stamp(a, 14);
@@ -1010,8 +1214,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     if (tid == 0) {
       const uint32_t old = atomicAdd(&ctl->exit, 1u);
       if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
-        ctl->maxkey = 0;
-        for (int k = 0; k < NB; ++k) flags[k] = 0;
+        for (int k = 0; k < NB; ++k) {
+          flags[k] = 0;
+          a.mflag[(int64_t)row * kMaxNB + k] = 0;
+        }
         ctl->exit = 0;
       }
     }
@@ -1035,6 +1241,7 @@ size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
   b += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
   b += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
+  b += align_up(sizeof(uint64_t) * rows * kMaxNB, 256);
   return b;
 }
 
@@ -1092,7 +1299,8 @@ void fused_ws(FusedArgs& a, void* ws, int rows, int nb, int G, int D) {
   a.err = (uint32_t*)w;         w += 256;
   a.trace = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
   a.plist = (int32_t*)w;         w += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
-  a.flags = (uint32_t*)w;
+  a.flags = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
+  a.mflag = (uint64_t*)w;
 }
 
 }  // namespace
