@@ -510,7 +510,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     } else {
       // only the tokens of the previous level's crossing bin: few, spread
-      // over the digits, so they go straight to the row's histogram
+      // over the digits, so they go straight to the row's fine bins; the
+      // coarse groups (which all of them share) are summed in LDS first
+      if (tid < NC) {
+        hcnt_l[tid] = 0;
+        hmass_l[tid] = 0;
+      }
+      __syncthreads();
 #pragma unroll
       for (int u = 0; u < TPT; ++u) {
         const int32_t j = j0 + u * kNT + tid;
@@ -520,12 +526,17 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         if (!match) continue;
         const uint32_t digit = level == 2 ? ((k >> 8) & 0xfffu) : (k & 0xffu);
         atomicAdd(&gc[digit], 1u);
-        atomicAdd(&gcc[digit >> 6], 1u);
+        atomicAdd(&hcnt_l[digit >> 6], 1u);
         if (!topk) {
           const uint64_t e = (uint64_t)(__expf(xk[u] - mx) * 1099511627776.0f);
           atomicAdd((unsigned long long*)&gm[digit], (unsigned long long)e);
-          atomicAdd((unsigned long long*)&gcm[digit >> 6], (unsigned long long)e);
+          atomicAdd((unsigned long long*)&hmass_l[digit >> 6], (unsigned long long)e);
         }
+      }
+      __syncthreads();
+      if (tid < NC && hcnt_l[tid]) {
+        atomicAdd(&gcc[tid], hcnt_l[tid]);
+        if (!topk) atomicAdd((unsigned long long*)&gcm[tid], (unsigned long long)hmass_l[tid]);
       }
     }
     stamp(a, 3 * level);
