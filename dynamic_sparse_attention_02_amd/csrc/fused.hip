@@ -205,8 +205,9 @@ __device__ __forceinline__ U blk_scan(U v, U* lds, U& total) {  // exclusive, kN
 }
 
 // PAGES: the candidates are the sequence's pages, scored by the Taylor page
-// score; the top-k pages' tokens are attended and listed.
-template <typename T, int D, int G, int TPT, bool PAGES>
+// score; the top-k pages' tokens are attended and listed.  SEL: selection
+// only, over scores given in x (no attention, no outputs).
+template <typename T, int D, int G, int TPT, bool PAGES, bool SEL>
 __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   constexpr int HPW = G / 4 > 0 ? G / 4 : 1;   // heads per wave (G >= 4)
   constexpr int DPL = D / 64;
@@ -321,6 +322,26 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       if (j < n) xr[j] = xk[u];
     }
     stamp(a, 1);
+  } else if constexpr (SEL) {
+    // ---- 1. the own candidates' given scores ----
+    const float* xr = a.x + (int64_t)row * a.ldx;
+    uint32_t mk = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      xk[u] = j < n ? xr[j] : 0.f;
+      key[u] = j < n ? score_key(xk[u]) : 0u;
+      mk = key[u] > mk ? key[u] : mk;
+    }
+    mk = wave_max_u32(mk);
+    if (lane == 0) red_u[wave] = mk;
+    __syncthreads();
+    if (tid == 0) {
+      for (int i = 0; i < 4; ++i) mk = red_u[i] > mk ? red_u[i] : mk;
+      own_max = mk;
+    }
+    stamp(a, 1);
+    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, a.err);
   } else {
     // ---- 1. scores of the own tokens ----
   const T* kidx = (const T*)a.kidx;
@@ -757,6 +778,14 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       my_list[e - t0] = (uint32_t)(((int64_t)s_spp[e / kPage] * s.Hkv + g) * kPage + (e % kPage));
     if (tid == 0) s_cnt = t1 - t0;
     __syncthreads();
+  } else if constexpr (SEL) {
+    // the own selected count, for the ordered list
+    uint32_t my_sel = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) my_sel += selmask[u] & 1u;
+    uint32_t tot_sel;
+    blk_scan<uint32_t>(my_sel, red_u, tot_sel);
+    if (tid == 0) __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], tot_sel, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
   // own non-forced selected tokens -> LDS list (order irrelevant for attention)
   uint32_t my_sel = 0;
@@ -796,9 +825,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     __syncthreads();
   }
   }
-  const int32_t n_att = (int32_t)s_cnt;
   stamp(a, 5);
-  {
+  if constexpr (!SEL) {
+  const int32_t n_att = (int32_t)s_cnt;
     const T* k_pool = (const T*)a.k_pool;
     const T* v_pool = (const T*)a.v_pool;
     if constexpr (sizeof(T) == 2) {
@@ -1103,6 +1132,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint32_t bsel = 0;
     if constexpr (!PAGES)
       if (tid < NB) bsel = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (!SEL) {
     // outputs [bi * opb, (bi + 1) * opb) of the row's G * D values
     const int n_out = G * D;
     const int opb = (n_out + NB - 1) / NB;
@@ -1151,6 +1181,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         else ((float*)a.out)[((int64_t)b * s.Hq + h) * D + d] = v;
         if (d == 0 && a.lse) a.lse[(int64_t)b * s.Hq + h] = lsum > 0.f ? M2 + logf(lsum) : -INFINITY;
       }
+    }
     }
     __shared__ uint32_t s_base, s_total;
     if constexpr (!PAGES) {
@@ -1333,7 +1364,7 @@ hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const v
   fused_ws(a, ws, rows, nb, G, s.D);
   const int tpt = tpb / kNT;
   dim3 grid(rows * nb);
-#define SA_FP(DD, GG, PP) k_decode_fused<bf16_raw, DD, GG, PP, true><<<grid, kNT, 0, st>>>(a)
+#define SA_FP(DD, GG, PP) k_decode_fused<bf16_raw, DD, GG, PP, true, false><<<grid, kNT, 0, st>>>(a)
 #define SA_FP_T(DD, GG)                  \
   switch (tpt) {                         \
     case 1: SA_FP(DD, GG, 1); break;     \
@@ -1355,6 +1386,52 @@ hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const v
   return hipGetLastError();
 }
 
+// Selection only over given scores (unit 1, few long rows) in one persistent
+// launch: the same levels, ties and ordered list as the fused step.
+bool select_fused_plan(const SelectArgs& sa, int32_t* nb, int32_t* tpb) {
+  if (sa.unit != 1 || sa.key16 || sa.prefill_bsel != 0 || sa.Hkv < 1 || sa.rows % sa.Hkv != 0) return false;
+  Shape s{};
+  s.B = sa.rows / sa.Hkv;
+  s.Hkv = sa.Hkv;
+  s.Hq = 4 * sa.Hkv;  // (the group size plays no part in selection)
+  s.max_len = sa.max_len;
+  s.n_pool_pages = 1;
+  return fused_plan(s, sa.n_sink, sa.n_window, nb, tpb);
+}
+
+hipError_t launch_select_fused(const SelectArgs& sa, void* ws, int32_t nb, int32_t tpb,
+                               hipStream_t st) {
+  FusedArgs a{};
+  a.s.B = sa.rows / sa.Hkv;
+  a.s.Hkv = sa.Hkv;
+  a.s.Hq = 4 * sa.Hkv;
+  a.s.max_len = sa.max_len;
+  a.seq_lens = sa.seq_lens;
+  a.p = sa.p;
+  a.top_k = sa.is_topk ? sa.k : 0;
+  a.n_sink = sa.n_sink;
+  a.n_window = sa.n_window;
+  a.x = const_cast<float*>(sa.x);
+  a.ldx = sa.ldx;
+  a.idx = sa.idx;
+  a.count = sa.count;
+  a.cap = sa.cap;
+  a.nb = nb;
+  a.tpb = tpb;
+  fused_ws(a, ws, sa.rows, nb, 1, 0);
+  dim3 grid(sa.rows * nb);
+#define SA_FS(PP) k_decode_fused<float, 64, 4, PP, false, true><<<grid, kNT, 0, st>>>(a)
+  switch (tpb / kNT) {
+    case 1: SA_FS(1); break;
+    case 2: SA_FS(2); break;
+    case 4: SA_FS(4); break;
+    case 8: SA_FS(8); break;
+    default: SA_FS(16); break;
+  }
+#undef SA_FS
+  return hipGetLastError();
+}
+
 hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q, const void* w_q,
                                const void* kidx_pool, const void* k_pool, const void* v_pool,
                                sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
@@ -1373,7 +1450,7 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
   fused_ws(a, ws, rows, nb, G, s.D);
   const int tpt = tpb / kNT;  // 1, 2, 4, 8 or 16 (fused_plan)
   dim3 grid(rows * nb);
-#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP, false><<<grid, kNT, 0, st>>>(a)
+#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP, false, false><<<grid, kNT, 0, st>>>(a)
 #define SA_FZ_T(TT, DD, GG)              \
   switch (tpt) {                         \
     case 1: SA_FZ(TT, DD, GG, 1); break;  \

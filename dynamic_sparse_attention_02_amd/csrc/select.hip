@@ -1420,6 +1420,11 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
   b += align_up(sizeof(uint64_t) * 2 * rows * kBins, 256);
   b += align_up(sizeof(uint32_t) * 2 * rows * kCoarse, 256);
   b += align_up(sizeof(uint64_t) * 2 * rows * kCoarse, 256);
+  // few long rows may run as one persistent launch instead
+  if (rows <= 16) {
+    const size_t f = fused_workspace_bytes(rows, 256, 1, 0);
+    if (f > b) b = f;
+  }
   return b;
 }
 
@@ -1441,6 +1446,10 @@ hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
     else k_select_row<false, kRowRegsTopk, kThreads><<<a.rows, kThreads, 0, st>>>(a);
     return hipGetLastError();
   }
+  // few long rows: one persistent launch whose workgroups split each row and
+  // meet at in-memory barriers, if the rows fit its plan
+  int32_t fnb = 0, ftpb = 0;
+  if (a.rows <= 16 && select_fused_plan(a, &fnb, &ftpb)) return launch_select_fused(a, ws, fnb, ftpb, st);
   const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
   WsLayout w = carve(ws, a.rows, a.max_cand < 1 ? 1 : a.max_cand);
   dim3 grid(nch, a.rows);

@@ -23,8 +23,10 @@
  *    buffer; the library never allocates or frees memory.  Scratch memory is
  *    passed in as a workspace whose size comes from sa_workspace_size().
  *  - A workspace must be zero-filled once before its first use; every call
- *    leaves the parts it relies on zero again.  Calls that share a workspace
- *    must be ordered (same stream, or synchronised).
+ *    leaves the parts it relies on zero again, so one workspace serves any
+ *    number of calls of the same entry point and shape (its layout depends
+ *    on both; other parts may be left holding intermediate values).  Calls
+ *    that share a workspace must be ordered (same stream, or synchronised).
  *  - Every call is asynchronous on the given HIP stream (NULL = default
  *    stream) and never synchronises the host.
  *  - Arguments are checked on the host before anything is launched; a failed

@@ -203,16 +203,19 @@ def test_select_golden(case):
     assert got.tolist() == expect
 
 
-@pytest.mark.parametrize("n", [9000, 40000])
-def test_select_exact_ties_across_chunks(n):
+@pytest.mark.parametrize("n,R", [(9000, 1), (40000, 1), (40000, 20)])
+def test_select_exact_ties_across_chunks(n, R):
     """n = 9000: one block per row; n = 40000: a row split over several
-    blocks (more candidates than one block keeps in registers)."""
+    blocks (more candidates than one block keeps in registers): with one row
+    by the persistent launch whose workgroups meet at in-memory barriers,
+    with 20 rows by the multi-launch path with per-chunk histograms."""
     x = np.zeros(n, dtype=np.float32)
     big = [5, 4000, n - 1]
     x[big] = 3.0
     # top-k threshold falls inside the tie group of zeros that spans chunks
-    got = _select_rows([x], [n], k=2503)[0]
-    assert got.tolist() == sorted(big + [j for j in range(n) if j not in big][:2500])
+    want = sorted(big + [j for j in range(n) if j not in big][:2500])
+    for got in _select_rows([x] * R, [n] * R, k=2503):
+        assert got.tolist() == want
     # all equal, top-p 0.5 -> exactly half the candidates, lowest indices
     got = _select_rows([np.zeros(5000, np.float32)], [5000], p=0.5)[0]
     assert got.tolist() == list(range(2500))
@@ -221,12 +224,16 @@ def test_select_exact_ties_across_chunks(n):
     assert got.tolist() == list(range(100))
 
 
-@pytest.mark.parametrize("seed,long", [(0, False), (1, False), (2, False), (3, True)])
+@pytest.mark.parametrize("seed,long", [(0, None), (1, None), (2, None), (3, "split"), (4, "multi")])
 def test_select_random_ragged(seed, long):
-    """Ragged rows; with long=True a 40000-candidate row sends every row of
-    the call through the multi-block selection."""
+    """Ragged rows.  A 40000-candidate row sends every row of the call
+    through a selection that splits rows over many workgroups: among 6 rows
+    ("split") the persistent launch whose workgroups meet at in-memory
+    barriers, among 20 rows ("multi") the multi-launch path with per-chunk
+    histograms."""
     rng = np.random.default_rng(seed)
-    lens = [1, 63, 700, 2049, 5000] + ([40000] if long else [])
+    lens = ([1, 63, 700, 2049, 5000] + ([40000] if long else [])
+            + ([300] * 14 if long == "multi" else []))
     rows = [(rng.standard_normal(L) * 3).astype(np.float32) for L in lens]
     for rule in ({"p": S.f32(0.9)}, {"p": S.f32(0.5)}, {"k": 50}, {"k": 1}):
         for sink, win in ((0, 0), (4, 16)):
