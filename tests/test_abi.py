@@ -65,7 +65,12 @@ def test_workspace_sizes():
     s = _shape(L)
     ws = lambda op, prm: so.sa_workspace_size(op, ctypes.byref(s), prm)
     assert ws(L.SA_OP_INDEX_SCORES, 0) >= 4 * 16 * 4
-    assert ws(L.SA_OP_SELECT, 1 << 22) > ws(L.SA_OP_SELECT, 1024) > 0
+    # few rows: room for the persistent selection too (its size does not
+    # depend on the candidates); many rows: grows with the candidates
+    assert ws(L.SA_OP_SELECT, 1 << 22) >= ws(L.SA_OP_SELECT, 1024) > 0
+    s32 = _shape(L, batch=8)
+    assert (so.sa_workspace_size(L.SA_OP_SELECT, ctypes.byref(s32), 1 << 22)
+            > so.sa_workspace_size(L.SA_OP_SELECT, ctypes.byref(s32), 1024) > 0)
     assert ws(L.SA_OP_SPARSE_DECODE, 65536) > ws(L.SA_OP_SPARSE_DECODE, 64) > 0
     assert ws(L.SA_OP_DECODE_STEP, 65536) >= ws(L.SA_OP_SELECT, 65536) + ws(L.SA_OP_SPARSE_DECODE, 65536)
     bad = _shape(L, head_dim=96)
