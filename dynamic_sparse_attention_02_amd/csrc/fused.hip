@@ -8,21 +8,21 @@
 // section 2.1).
 //
 // Each row is served by NB co-resident workgroups, each owning a contiguous
-// range of the row's tokens.  They meet at per-row barriers (a counter in the
-// workspace, bounded spins that raise an error flag instead of waiting
-// forever):
-//   1. collapse the query, score the own tokens (kept in registers), publish
-//      the row maximum;                                          -- barrier
+// range of the row's tokens.  They meet at per-row barriers (one arrival flag
+// per workgroup in the workspace, bounded spins that raise an error flag
+// instead of waiting forever):
+//   1. collapse the query, score the own tokens (kept in registers); top-p
+//      rows exchange their maxima in the first barrier's flag words;
+//                                                               -- barrier
 //   2. per radix level: LDS histogram of the own tokens, flush non-empty bins
 //      to the row's global histogram;                           -- barrier
 //      every workgroup resolves the level from the same global histogram;
 //   3. own selected tokens (minus sink/window) plus an even share of the
-//      sink/window tokens are attended (split-KV partial per workgroup), the
-//      own selected count is published;                          -- barrier
-//   4. ordered write of the index list at the prefix of lower workgroups'
-//      counts, and each workgroup merges a slice of the row's outputs.
-// Histograms, the row maximum and the barrier counters are returned to zero
-// before the launch ends.
+//      sink/window tokens are attended (split-KV partial per workgroup; bf16
+//      on the matrix cores), the own selected count is published; -- barrier
+//   4. each workgroup merges a slice of the row's outputs, and writes its
+//      part of the index list at the prefix of lower workgroups' counts.
+// Histograms and barrier flags are returned to zero before the launch ends.
 //
 // Page mode runs the same phases over a sequence's 64-token pages: Taylor
 // page scores from the mean and diagonal variance of each page's keys
@@ -30,6 +30,8 @@
 // phase 3 every workgroup publishes its selected pages, meets the others and
 // reads the row's page list, then attends an even slice of the row's tokens
 // (the selected pages are few and may sit in one workgroup's range).
+// Selection-only mode takes the scores from memory in phase 1 and stops
+// after the index list.
 #include "sa_internal.h"
 
 namespace sa {
