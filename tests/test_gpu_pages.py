@@ -272,17 +272,19 @@ def assert_same_step(inp, a, b, tol):
         1.0, float(lb[fin].abs().max()) if fin.any() else 1.0)
 
 
-@pytest.mark.parametrize("G,d,k_pages,seq_lens", [
-    (4, 128, 6, [64 * 40 + 17, 0, 64 * 3, 2500]),
-    (8, 128, 32, [64 * 700 + 1, 64 * 31, 64 * 500]),
-    (16, 128, 1, [100000, 65]),
-    (8, 64, 17, [64 * 900, 64 * 2000 + 63]),
+@pytest.mark.parametrize("G,d,k_pages,seq_lens,hkv", [
+    (4, 128, 6, [64 * 40 + 17, 0, 64 * 3, 2500], 2),
+    (8, 128, 32, [64 * 700 + 1, 64 * 31, 64 * 500], 2),
+    (16, 128, 1, [100000, 65], 2),
+    (8, 64, 17, [64 * 900, 64 * 2000 + 63], 2),
+    (8, 128, 20, [64 * 3000 + 5], 1),
 ])
-def test_decode_step_pages_fused_matches_calls(G, d, k_pages, seq_lens):
+def test_decode_step_pages_fused_matches_calls(G, d, k_pages, seq_lens, hkv):
     """The one-launch page-level step (bf16, few rows, top-k <= 32 pages)
     against the three separate calls and against the oracle: ragged rows with
-    partial last pages, an empty row, rows with fewer pages than k."""
-    inp = synth.make_decode_custom(B=len(seq_lens), H_q=2 * G, H_kv=2, d=d, seq_lens=seq_lens,
+    partial last pages, an empty row, rows with fewer pages than k, and one
+    row served by every compute unit."""
+    inp = synth.make_decode_custom(B=len(seq_lens), H_q=hkv * G, H_kv=hkv, d=d, seq_lens=seq_lens,
                                    dtype=torch.bfloat16, device="cuda", seed=40 + G + k_pages,
                                    hh_frac=0.01, alpha=10.0, shuffle=True)
     pool, rows = oracle_stats_pool(inp)
@@ -309,8 +311,10 @@ def test_decode_step_pages_separate_path(dtype, G, k_pages):
     check_page_rows(inp, rows, *got, k_pages, range(inp.H_kv), S.TOL[dtype])
 
 
-def test_decode_step_pages_ties():
-    """Exact ties spread over workgroups: every 100th page of a row has zero
+@pytest.mark.parametrize("hkv,lens", [(2, [64 * 3000 + 9, 64 * 777]), (1, [64 * 3000 + 9])])
+def test_decode_step_pages_ties(hkv, lens):
+    """Exact ties spread over workgroups (four rows, or one row served by
+    every compute unit): every 100th page of a row has zero
     mean and unit variance, every other page zero statistics, so the scores
     take two values (and the length term of a partial last page).  Row 0 has
     30 tied high pages for 20 places: the 20 lowest indices win; row 1 has 8
@@ -318,7 +322,7 @@ def test_decode_step_pages_ties():
     workspace, both equal to the three separate calls."""
     from dynamic_sparse_attention_02_amd import _lib as L
     o = ops()
-    inp = synth.make_decode_custom(B=2, H_q=16, H_kv=2, d=128, seq_lens=[64 * 3000 + 9, 64 * 777],
+    inp = synth.make_decode_custom(B=len(lens), H_q=8 * hkv, H_kv=hkv, d=128, seq_lens=lens,
                                    dtype=torch.bfloat16, device="cuda", seed=71, shuffle=True)
     pool = torch.zeros((inp.n_pages, inp.H_kv, 2, inp.d), dtype=inp.dtype, device="cuda")
     for b in range(inp.B):
