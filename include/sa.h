@@ -29,6 +29,13 @@
  *    that share a workspace must be ordered (same stream, or synchronised).
  *  - Every call is asynchronous on the given HIP stream (NULL = default
  *    stream) and never synchronises the host.
+ *  - Few-row problems may run as one persistent launch (one workgroup per
+ *    compute unit, the workgroups of a row meeting at in-memory barriers):
+ *    sa_decode_step and sa_decode_step_pages with batch * n_kv_heads <= 16,
+ *    and sa_select_topp / sa_select_topk on up to 16 long rows.  Such a
+ *    launch needs the compute units to itself while it runs (no kernel of
+ *    another stream resident beside it); a barrier that waits about a second
+ *    gives up so the launch ends, and that call's outputs are then wrong.
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check returns an error code, launches nothing and writes nothing.
  *    sa_last_error() then gives a message (per calling thread).  A failed
@@ -256,7 +263,10 @@ sa_status sa_sparse_decode_rla(const sa_shape* shape, const sa_pages* pages, con
 
 /* One whole decode step: sa_index_scores, then sa_select_topp (p in (0, 1])
  * or, if top_k > 0, sa_select_topk with unit 1, then sa_sparse_decode.  The
- * scores x ([batch * n_kv_heads][ldx] fp32), idx and count are outputs too. */
+ * scores x ([batch * n_kv_heads][ldx] fp32), idx and count are outputs too.
+ * With few rows (batch * n_kv_heads <= 16, group size >= 4) the step runs as
+ * one persistent launch with the same scores, lists and counts as the three
+ * calls and outputs equal within rounding. */
 sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const void* q,
                          const void* w_q, const void* kidx_pool, const void* k_pool,
                          const void* v_pool, sa_dtype dtype, float s_idx, float s_att,
