@@ -216,6 +216,9 @@ def test_select_exact_ties_across_chunks(n, R):
     want = sorted(big + [j for j in range(n) if j not in big][:2500])
     for got in _select_rows([x] * R, [n] * R, k=2503):
         assert got.tolist() == want
+    # top-p over equal scores: the tie group spans every workgroup of the row
+    for got in _select_rows([np.zeros(n, np.float32)] * R, [n] * R, p=0.5):
+        assert got.tolist() == list(range(n // 2))
     # all equal, top-p 0.5 -> exactly half the candidates, lowest indices
     got = _select_rows([np.zeros(5000, np.float32)], [5000], p=0.5)[0]
     assert got.tolist() == list(range(2500))
