@@ -472,33 +472,27 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint64_t* gcm = a.cmass + ((int64_t)li * rows + row) * kCoarseF;
     if (level == 1) {
       // every candidate lands in this level: aggregate in LDS, flush the
-      // non-empty bins of the coarse groups the own candidates span
-      uint32_t dhi = 0, dlo_c = 0;  // highest digit + 1, complement of the lowest
+      // non-empty bins of the coarse groups the own candidates occupy (a
+      // 64-bit mask of them; scores of both signs leave wide gaps)
+      uint64_t occ = 0;
 #pragma unroll
       for (int u = 0; u < TPT; ++u)
-        if (j0 + u * kNT + tid < n) {
-          const uint32_t dg = key[u] >> 20;
-          dhi = dg + 1 > dhi ? dg + 1 : dhi;
-          dlo_c = ~dg > dlo_c ? ~dg : dlo_c;
-        }
-      dhi = wave_max_u32(dhi);
-      dlo_c = wave_max_u32(dlo_c);
-      if (lane == 0) {
-        red_u[wave] = dhi;
-        s_slice[wave] = dlo_c;  // (s_slice is free until the selection)
-      }
+        if (j0 + u * kNT + tid < n) occ |= 1ull << (key[u] >> 26);
+      const uint32_t occ_lo = wave_allreduce_bits((uint32_t)occ, [](uint32_t x, uint32_t y) { return x | y; });
+      const uint32_t occ_hi = wave_allreduce_bits((uint32_t)(occ >> 32), [](uint32_t x, uint32_t y) { return x | y; });
+      if (lane == 0) red_u64[wave] = ((uint64_t)occ_hi << 32) | occ_lo;
       __syncthreads();
-      uint32_t hi = 0, lo_c = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        hi = red_u[w] > hi ? red_u[w] : hi;
-        lo_c = s_slice[w] > lo_c ? s_slice[w] : lo_c;
-      }
-      // coarse groups [cg_lo, cg_hi) hold every own candidate (none if hi == 0)
-      const int cg_lo = hi ? (int)(~lo_c >> 6) : 0, cg_hi = hi ? (int)((hi - 1) >> 6) + 1 : 0;
-      for (int i = cg_lo * 64 + tid; i < cg_hi * 64; i += kNT) {
-        hcnt_l[i] = 0;
-        hmass_l[i] = 0;
+      const uint64_t occ_all = red_u64[0] | red_u64[1] | red_u64[2] | red_u64[3];
+      {
+        uint64_t m = occ_all;
+        for (int k = 0; m; ++k) {  // the k-th occupied group goes to wave k mod 4
+          const int cgz = __ffsll((long long)m) - 1;
+          m &= m - 1;
+          if ((k & 3) == wave) {
+            hcnt_l[cgz * 64 + lane] = 0;
+            hmass_l[cgz * 64 + lane] = 0;
+          }
+        }
       }
       __syncthreads();
 #pragma unroll
@@ -514,7 +508,11 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
       __syncthreads();
       stamp(a, 15);
-      for (int cg = cg_lo + wave; cg < cg_hi; cg += 4) {
+      uint64_t mrem = occ_all;
+      for (int k = 0; mrem; ++k) {
+        const int cg = __ffsll((long long)mrem) - 1;
+        mrem &= mrem - 1;
+        if ((k & 3) != wave) continue;
         const int bin = cg * 64 + lane;
         const uint32_t cn = hcnt_l[bin];
         const uint64_t ms = hmass_l[bin];
