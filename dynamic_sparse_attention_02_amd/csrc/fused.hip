@@ -1124,6 +1124,23 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   stamp(a, 12);
   row_barrier(flags, NB, bi, ++epoch, a.err);
   stamp(a, 13);
+  // no workgroup reads the row's histograms after the last barrier: return
+  // this workgroup's slice of them to zero for the next launch
+  {
+    const int per = (kBinsF + NB - 1) / NB;
+    for (int li = 0; li < 3; ++li) {
+      uint32_t* gc = a.hcnt + ((int64_t)li * rows + row) * kBinsF;
+      uint64_t* gm = a.hmass + ((int64_t)li * rows + row) * kBinsF;
+      for (int i = bi * per + tid; i < min(kBinsF, (bi + 1) * per); i += kNT) {
+        gc[i] = 0;
+        gm[i] = 0;
+      }
+      if (bi == 0 && tid < kCoarseF) {
+        a.ccnt[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
+        a.cmass[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
+      }
+    }
+  }
 
   // ---- 4. merge of this workgroup's output slice and the ordered index list ----
   {
@@ -1208,23 +1225,26 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       if (tid == 0) s_total = tot_tok;
       __syncthreads();
     } else {
+    // every round's per-wave counts first, so one barrier serves all rounds
+    uint64_t msk[TPT];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      msk[u] = __ballot(selmask[u] & 1u);
+      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(msk[u]);
+    }
+    __syncthreads();
     uint32_t run = s_base;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const bool sel = selmask[u] & 1u;
-      const uint64_t m = __ballot(sel);
-      if (lane == 0) s_slice[u * 4 + wave] = (uint32_t)__popcll(m);
-      __syncthreads();
       uint32_t before = run;
       for (int w = 0; w < wave; ++w) before += s_slice[u * 4 + w];
       uint32_t round_tot = 0;
       for (int w = 0; w < 4; ++w) round_tot += s_slice[u * 4 + w];
-      if (sel) {
-        const uint32_t pos = before + (uint32_t)__popcll(m & lt_mask);
+      if (selmask[u] & 1u) {
+        const uint32_t pos = before + (uint32_t)__popcll(msk[u] & lt_mask);
         if (pos < (uint32_t)a.cap) outl[pos] = j0 + u * kNT + tid;
       }
       run += round_tot;
-      __syncthreads();
     }
     }
     const uint32_t total = s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap;
@@ -1235,24 +1255,12 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   }
 
   stamp(a, 14);
-  // ---- clean-up for the next launch: histograms, maximum, counters ----
+  // ---- clean-up for the next launch: the barrier flags (the histograms
+  // were zeroed after the last barrier) ----
   {
-    const int per = (kBinsF + NB - 1) / NB;
-    for (int li = 0; li < 3; ++li) {
-      uint32_t* gc = a.hcnt + ((int64_t)li * rows + row) * kBinsF;
-      uint64_t* gm = a.hmass + ((int64_t)li * rows + row) * kBinsF;
-      for (int i = bi * per + tid; i < min(kBinsF, (bi + 1) * per); i += kNT) {
-        gc[i] = 0;
-        gm[i] = 0;
-      }
-      if (bi == 0 && tid < kCoarseF) {
-        a.ccnt[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
-        a.cmass[((int64_t)li * rows + row) * kCoarseF + tid] = 0;
-      }
-    }
     __syncthreads();
-    // (the zeroing above and the resets below reach the next launch through
-    // the end-of-kernel cache write-back)
+    // (the zeroing and the resets below reach the next launch through the
+    // end-of-kernel cache write-back)
     if (tid == 0) {
       const uint32_t old = atomicAdd(&ctl->exit, 1u);
       if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
