@@ -793,7 +793,7 @@ def cpu_baseline_prefill(inp, kidx, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU only (one GPU's share of the work); --gpus must be 1",
                           "n_gpus_requested": args.gpus}))
         sys.exit(2)
     import torch
