@@ -838,17 +838,14 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     // of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, so each wave runs its own
     // online softmax without exchanging scores.  P enters the product as a
     // bf16 high part plus the bf16 rounding of the remainder (16 significant
-    // bits); V is staged transposed.  The four waves' softmax states are
-    // merged once at the end.
+    // bits); K and V are staged row-major.  The four waves' softmax states
+    // are merged once at the end.
     typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
     typedef __attribute__((ext_vector_type(4))) short s16x4_t;
     typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-    constexpr int VP = kTileF + 4;  // V^T row pitch in bf16 (8-byte aligned rows)
     constexpr int KS = D / 32, MB = D / 16;
-    static_assert(D * VP * 2 <= kTileF * PITCH, "V^T tile fits the V buffer");
     static_assert(2 * D * 16 * 4 <= kTileF * PITCH, "two waves' outputs fit one tile buffer");
     __shared__ float s_wm[4][16], s_wl[4][16];
-    bf16_raw* Vt = reinterpret_cast<bf16_raw*>(Vs);
     const int hq = lane & 15, lg = lane >> 4;
     bf16x8_t qB[KS];
 #pragma unroll
@@ -861,8 +858,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
-    // K rows: 16 lanes per row (contiguous loads); V rows: one row per lane,
-    // so a wave's transposed LDS writes cover 64 consecutive tokens.  NBUF
+    // K and V rows: 16 lanes per row (contiguous loads), staged row-major;
+    // the V^T operand is gathered from four rows by 2-byte LDS reads.  NBUF
     // tiles of rows are in flight
     constexpr int NBUF = 2;
     uint4 kq[NBUF][LPT], vq[NBUF][LPT];
@@ -871,13 +868,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
         const int rk = pc / CPR, ck = pc % CPR;
-        const int rv = pc % kTileF, cv = pc / kTileF;
         kr[i] = make_uint4(0, 0, 0, 0);
         vr[i] = make_uint4(0, 0, 0, 0);
-        if (ts + rk < n_att)
-          kr[i] = *reinterpret_cast<const uint4*>(k_pool + (int64_t)my_list[ts + rk] * D + ck * 8);
-        if (ts + rv < n_att)
-          vr[i] = *reinterpret_cast<const uint4*>(v_pool + (int64_t)my_list[ts + rv] * D + cv * 8);
+        if (ts + rk < n_att) {
+          const int64_t off = (int64_t)my_list[ts + rk] * D + ck * 8;
+          kr[i] = *reinterpret_cast<const uint4*>(k_pool + off);
+          vr[i] = *reinterpret_cast<const uint4*>(v_pool + off);
+        }
       }
     };
     auto tile = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
@@ -887,14 +884,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
         const int rk = pc / CPR, ck = pc % CPR;
-        const int rv = pc % kTileF, cv = pc / kTileF;
         *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) = kr[i];
-        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Vt[(cv * 8 + 2 * e) * VP + rv] = (bf16_raw)(w[e] & 0xffffu);
-          Vt[(cv * 8 + 2 * e + 1) * VP + rv] = (bf16_raw)(w[e] >> 16);
-        }
+        *reinterpret_cast<uint4*>(Vs + rk * PITCH + ck * 16) = vr[i];
       }
       __syncthreads();
       if (ts + NBUF * kTileF < n_att) gather(ts + NBUF * kTileF, kr, vr);
@@ -938,8 +929,12 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         oacc[mb] *= alpha;
-        const uint2 vv = *reinterpret_cast<const uint2*>(Vt + (16 * mb + hq) * VP + 16 * wave + 4 * lg);
-        const s16x4_t av = __builtin_bit_cast(s16x4_t, vv);
+        const char* vcol = Vs + (16 * wave + 4 * lg) * PITCH + (16 * mb + hq) * 2;
+        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
+        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + PITCH);
+        const uint32_t v2 = *reinterpret_cast<const uint16_t*>(vcol + 2 * PITCH);
+        const uint32_t v3 = *reinterpret_cast<const uint16_t*>(vcol + 3 * PITCH);
+        const s16x4_t av = __builtin_bit_cast(s16x4_t, make_uint2(v0 | (v1 << 16), v2 | (v3 << 16)));
         oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
         oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
       }
