@@ -136,6 +136,16 @@ def test_validation_codes():
     # decode step: capacity and p
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.9, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 60000, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_CAPACITY
     assert so.sa_decode_step(B(s), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, 0.0, 0, 4, 512, FAKE, 65536, FAKE, FAKE, 65536, FAKE, L.SA_F32, None, FAKE, 1 << 30, None) == L.SA_ERR_INVALID_ARGUMENT
+    # page-level decode step: top_k, score row width, capacity, workspace,
+    # NULL statistics (shape: 1024 pages of 64 tokens, so cap >= k * 64)
+    ws_pg = so.sa_workspace_size(L.SA_OP_DECODE_STEP_PAGES, B(s), 2048)
+    assert ws_pg >= so.sa_workspace_size(L.SA_OP_SPARSE_DECODE, B(s), 2048)
+    step_pg = lambda *a: so.sa_decode_step_pages(B(s), B(pg), *a)
+    assert step_pg(FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 0.1, 0, FAKE, 1024, FAKE, FAKE, 2048, FAKE, L.SA_F32, None, FAKE, ws_pg, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert step_pg(FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 0.1, 32, FAKE, 1023, FAKE, FAKE, 2048, FAKE, L.SA_F32, None, FAKE, ws_pg, None) == L.SA_ERR_INVALID_ARGUMENT
+    assert step_pg(FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 0.1, 32, FAKE, 1024, FAKE, FAKE, 2047, FAKE, L.SA_F32, None, FAKE, ws_pg, None) == L.SA_ERR_CAPACITY
+    assert step_pg(FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 0.1, 32, FAKE, 1024, FAKE, FAKE, 2048, FAKE, L.SA_F32, None, FAKE, ws_pg - 1, None) == L.SA_ERR_WORKSPACE
+    assert step_pg(FAKE, None, FAKE, FAKE, L.SA_BF16, 0.1, 32, FAKE, 1024, FAKE, FAKE, 2048, FAKE, L.SA_F32, None, FAKE, ws_pg, None) == L.SA_ERR_INVALID_ARGUMENT
     # prefill: batch, b_sel, dtype, n_tokens
     s1 = _shape(L, n_q_heads=32, n_kv_heads=8, max_pages=2048, max_len=131072, n_pool_pages=2048)
     assert so.sa_sparse_prefill(B(s1), B(pg), 131072, FAKE, FAKE, FAKE, L.SA_BF16, FAKE, FAKE, 2048, 32, 0.1, FAKE, L.SA_BF16, None, None) == L.SA_ERR_UNSUPPORTED
