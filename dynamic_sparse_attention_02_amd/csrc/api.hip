@@ -119,24 +119,26 @@ size_t mass_ws(const sa_shape* s) {
     if (_st != SA_OK) return _st; \
   } while (0)
 
-// Decode-step workspace: room for the separate calls and for the fused
-// single-launch step (used when the problem has few rows).
-size_t step_ws(const sa_shape* s, int64_t cap) {
-  const size_t unfused = index_ws(s) + select_ws(s, s->max_len) + decode_ws(s, cap);
+// Region of the persistent single-launch step, placed after the separate
+// calls' regions so that a workspace shared by calls that take different
+// paths (the plan depends on n_sink / n_window, not on the shape alone) never
+// lets one path's state alias the other's.
+size_t fused_region(const sa_shape* s) {
   const int rows = s->batch * s->n_kv_heads;
   const int G = s->n_q_heads / s->n_kv_heads;
-  const size_t fused = sa::align_up(sa::fused_workspace_bytes(rows, 256, G, s->head_dim), 256);
-  return unfused > fused ? unfused : fused;
+  if (rows > 16 || G < 4) return 0;
+  return sa::align_up(sa::fused_workspace_bytes(rows, 256, G, s->head_dim), 256);
 }
 
-// Page-level step workspace: the separate calls or the fused step.
+// Decode-step workspace: index | select | decode | fused step.
+size_t step_ws(const sa_shape* s, int64_t cap) {
+  return index_ws(s) + select_ws(s, s->max_len) + decode_ws(s, cap) + fused_region(s);
+}
+
+// Page-level step workspace: select | decode | fused step.
 size_t step_pages_ws(const sa_shape* s, int64_t cap) {
   const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
-  const size_t unfused = select_ws(s, n_cand) + decode_ws(s, cap);
-  const int rows = s->batch * s->n_kv_heads;
-  const int G = s->n_q_heads / s->n_kv_heads;
-  const size_t fused = sa::align_up(sa::fused_workspace_bytes(rows, 256, G, s->head_dim), 256);
-  return unfused > fused ? unfused : fused;
+  return select_ws(s, n_cand) + decode_ws(s, cap) + fused_region(s);
 }
 
 int64_t topk_cap_needed(const sa_shape* s, int32_t k, int32_t unit, int32_t n_sink,
@@ -436,10 +438,11 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   char* base = (char*)ws;
   const sa::Shape sh = to_shape(s);
   int32_t nb = 0, tpb = 0;
-  if (sa::fused_plan(sh, n_sink, n_window, &nb, &tpb))
+  if (sa::fused_plan(sh, n_sink, n_window, dt, 0, &nb, &tpb))
     return hip_status(sa::launch_decode_fused(sh, *pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
                                               s_att, p, top_k, n_sink, n_window, x, ldx, idx, count,
-                                              cap, out, out_dt, lse, ws, nb, tpb, st), fn);
+                                              cap, out, out_dt, lse, base + w_i + w_s + w_d, nb, tpb,
+                                              st), fn);
   hipError_t e = sa::launch_index_scores(sh, *pg, q, w_q, kidx_pool, dt, s_idx, x, ldx, (float*)base, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};
@@ -488,14 +491,15 @@ sa_status sa_decode_step_pages(const sa_shape* s, const sa_pages* pg, const void
     return fail(SA_ERR_CAPACITY, "%s: cap=%d below the worst-case support %lld", fn, cap, (long long)cap_needed);
   SA_TRY(check_ws(ws, ws_bytes, step_pages_ws(s, cap), fn));
   const sa::Shape sh = to_shape(s);
+  const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
+  const size_t w_s = select_ws(s, n_cand);
+  char* base = (char*)ws;
   int32_t nb = 0, tpb = 0;
   if (dt == SA_BF16 && sa::fused_plan_pages(sh, top_k, &nb, &tpb))
     return hip_status(sa::launch_decode_fused_pages(sh, *pg, q, stats_pool, k_pool, v_pool, s_att,
                                                     top_k, x, ldx, idx, count, cap, out, out_dt,
-                                                    lse, ws, nb, tpb, st), fn);
-  const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
-  const size_t w_s = select_ws(s, n_cand);
-  char* base = (char*)ws;
+                                                    lse, base + w_s + decode_ws(s, cap), nb, tpb,
+                                                    st), fn);
   hipError_t e = sa::launch_page_scores(sh, *pg, q, stats_pool, dt, s_att, x, ldx, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};

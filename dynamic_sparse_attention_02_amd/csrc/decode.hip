@@ -512,9 +512,14 @@ k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
   const int32_t* pt = page_table + (int64_t)b * s.max_pages;
   __shared__ float phk[kRlaTok][16];
   __shared__ float vs[kRlaTok][D];
-  float acc[NC], zacc = 0.f;
+  // compensated (Kahan) sums: the error of a state element stays a few fp32
+  // rounding units of its magnitude however many tokens the cache holds
+  float acc[NC], cmp[NC], zacc = 0.f, zcmp = 0.f;
 #pragma unroll
-  for (int m = 0; m < NC; ++m) acc[m] = 0.f;
+  for (int m = 0; m < NC; ++m) {
+    acc[m] = 0.f;
+    cmp[m] = 0.f;
+  }
   for (int32_t j0 = first < 0 ? 0 : first; j0 < L; j0 += kRlaTok) {
     __syncthreads();
     // K: 32 tokens x this stripe's 16 dims; V: 32 tokens x D dims
@@ -543,8 +548,16 @@ k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
     for (int tk = 0; tk < kRlaTok; ++tk) {
       const float p = phk[tk][r];
 #pragma unroll
-      for (int m = 0; m < NC; ++m) acc[m] = fmaf(p, vs[tk][cg + 16 * m], acc[m]);
-      zacc += p;
+      for (int m = 0; m < NC; ++m) {
+        const float y = fmaf(p, vs[tk][cg + 16 * m], -cmp[m]);
+        const float t2 = acc[m] + y;
+        cmp[m] = (t2 - acc[m]) - y;
+        acc[m] = t2;
+      }
+      const float yz = p - zcmp;
+      const float tz = zacc + yz;
+      zcmp = (tz - zacc) - yz;
+      zacc = tz;
     }
   }
   float* st = state + ((int64_t)b * s.Hkv + g) * (D + 1) * D;

@@ -32,6 +32,10 @@
 // (the selected pages are few and may sit in one workgroup's range).
 // Selection-only mode takes the scores from memory in phase 1 and stops
 // after the index list.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -56,7 +60,8 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 struct RowWs {            // per-row control block (zero between launches)
   uint32_t exit;          // workgroups done
-  uint32_t pad[15];
+  uint32_t err;           // set if a barrier of the row gave up waiting
+  uint32_t pad[14];
 };
 
 struct FusedArgs {
@@ -91,7 +96,6 @@ struct FusedArgs {
   uint32_t* blk_eq;       // [rows][nb] threshold ties of each workgroup
   float* part_ml;         // [rows][nb][G][2]
   float* part_o;          // [rows][nb][G][D]
-  uint32_t* err;          // set to 1 if a barrier gave up waiting
   uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
   uint64_t* mflag;        // [rows][kMaxNB] marker bit 32 | own maximum score key
   int32_t* plist;         // page mode: [rows][nb][kFusedMaxPages][2] own pages (sequence, pool)
@@ -227,6 +231,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   const int32_t n = PAGES ? (L + kPage - 1) / kPage : L;  // candidates of the row
   const int32_t j0 = bi * a.tpb;
   RowWs* ctl = a.ctl + row;
+  uint32_t* err = &ctl->err;
   uint32_t epoch = 0;                       // barriers passed
   uint32_t* flags = a.flags + (int64_t)row * kMaxNB;
 
@@ -246,6 +251,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   // pool pages of the own token range
   __shared__ int32_t s_pt[TPT * kNT / kPage];
   __shared__ uint32_t s_mode, s_prefix, s_thr, s_neq, s_need, s_cnt;
+  __shared__ uint32_t s_base, s_total;
   __shared__ uint64_t s_rem;
   __shared__ uint32_t s_slice[TPT * 4];
   // page mode: the own selected pages in index order (sequence page, pool page)
@@ -343,7 +349,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       own_max = mk;
     }
     stamp(a, 1);
-    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, a.err);
+    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, err);
   } else {
     // ---- 1. scores of the own tokens ----
   const T* kidx = (const T*)a.kidx;
@@ -443,7 +449,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   }
     stamp(a, 1);
     // the row maximum is the top-p mass reference
-    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, a.err);
+    if (a.top_k <= 0) M = row_barrier_max(a.mflag + (int64_t)row * kMaxNB, NB, bi, own_max, err);
   }
   stamp(a, 2);
 
@@ -561,7 +567,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     stamp(a, 3 * level);
-    row_barrier(flags, NB, bi, ++epoch, a.err);
+    row_barrier(flags, NB, bi, ++epoch, err);
     stamp(a, 3 * level + 1);
     // resolve (wave 0): coarse groups, then the 64 bins of the crossing group
     if (wave == 0) {
@@ -669,7 +675,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     uint32_t tot;
     blk_scan<uint32_t>(e, red_u, tot);
     if (tid == 0) __hip_atomic_store(&a.blk_eq[(int64_t)row * NB + bi], tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    row_barrier(flags, NB, bi, ++epoch, a.err);
+    row_barrier(flags, NB, bi, ++epoch, err);
     {
       uint32_t vb = 0;
       for (int k = tid; k < bi; k += kNT)
@@ -743,7 +749,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       __hip_atomic_store(&pl[2 * tid + 1], s_spp[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     if (tid == 0) __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    row_barrier(flags, NB, bi, ++epoch, a.err);
+    row_barrier(flags, NB, bi, ++epoch, err);
     {
       // each workgroup's count and first page in one round trip (most
       // workgroups hold at most one selected page)
@@ -1117,7 +1123,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     }
   }
   stamp(a, 12);
-  row_barrier(flags, NB, bi, ++epoch, a.err);
+  row_barrier(flags, NB, bi, ++epoch, err);
   stamp(a, 13);
   // no workgroup reads the row's histograms after the last barrier: return
   // this workgroup's slice of them to zero for the next launch
@@ -1195,7 +1201,6 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     }
-    __shared__ uint32_t s_base, s_total;
     if constexpr (!PAGES) {
       const uint32_t vt = bsel, vb = tid < bi ? bsel : 0u;
       uint32_t tb, tt;
@@ -1246,23 +1251,29 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     const int64_t pad = (int64_t)a.cap - total;
     const int64_t p0 = total + (pad * bi) / NB, p1 = total + (pad * (bi + 1)) / NB;
     for (int64_t o = p0 + tid; o < p1; o += kNT) outl[o] = -1;
-    if (bi == 0 && tid == 0) a.count[row] = (int32_t)total;
   }
 
   stamp(a, 14);
-  // ---- clean-up for the next launch: the barrier flags (the histograms
-  // were zeroed after the last barrier) ----
+  // ---- exit: the last workgroup of the row to leave writes the row's count
+  // (-1 if any barrier of the row gave up, so a caller sees the failure) and
+  // returns the barrier flags, the error word and the exit counter to zero
+  // for the next launch (the histograms were zeroed after the last barrier) ----
   {
     __syncthreads();
-    // (the zeroing and the resets below reach the next launch through the
-    // end-of-kernel cache write-back)
     if (tid == 0) {
+      // this workgroup's error report completes before its exit is counted
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       const uint32_t old = atomicAdd(&ctl->exit, 1u);
       if (old == (uint32_t)NB - 1) {  // every workgroup of the row has left its barriers
+        const uint32_t failed = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        a.count[row] = failed ? -1 : (int32_t)(s_total < (uint32_t)a.cap ? s_total : (uint32_t)a.cap);
         for (int k = 0; k < NB; ++k) {
           flags[k] = 0;
           a.mflag[(int64_t)row * kMaxNB + k] = 0;
         }
+        *err = 0;
         ctl->exit = 0;
       }
     }
@@ -1282,7 +1293,6 @@ size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   b += 2 * align_up(sizeof(uint32_t) * rows * nb, 256);
   b += align_up(sizeof(float) * rows * nb * G * 2, 256);
   b += align_up(sizeof(float) * rows * nb * G * D, 256);
-  b += 256;  // error flag
   b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
   b += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
   b += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
@@ -1290,9 +1300,62 @@ size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   return b;
 }
 
+namespace {
+
+// The kernel instance a plan launches (mode 0: token step, 1: page step,
+// 2: selection only).
+template <typename T, int D, int G, bool PAGES, bool SEL>
+const void* fused_instance(int tpt) {
+  switch (tpt) {
+    case 1: return (const void*)k_decode_fused<T, D, G, 1, PAGES, SEL>;
+    case 2: return (const void*)k_decode_fused<T, D, G, 2, PAGES, SEL>;
+    case 4: return (const void*)k_decode_fused<T, D, G, 4, PAGES, SEL>;
+    case 8: return (const void*)k_decode_fused<T, D, G, 8, PAGES, SEL>;
+    default: return (const void*)k_decode_fused<T, D, G, 16, PAGES, SEL>;
+  }
+}
+
+template <typename T, int D, bool PAGES>
+const void* fused_instance_g(int G, int tpt) {
+  switch (G) {
+    case 4: return fused_instance<T, D, 4, PAGES, false>(tpt);
+    case 8: return fused_instance<T, D, 8, PAGES, false>(tpt);
+    default: return fused_instance<T, D, 16, PAGES, false>(tpt);
+  }
+}
+
+const void* fused_kernel_for(sa_dtype dt, int D, int G, int tpt, int mode) {
+  if (mode == 2) return fused_instance<float, 64, 4, false, true>(tpt);
+  if (mode == 1) return D == 128 ? fused_instance_g<bf16_raw, 128, true>(G, tpt)
+                                 : fused_instance_g<bf16_raw, 64, true>(G, tpt);
+  if (dt == SA_BF16) return D == 128 ? fused_instance_g<bf16_raw, 128, false>(G, tpt)
+                                     : fused_instance_g<bf16_raw, 64, false>(G, tpt);
+  return D == 128 ? fused_instance_g<float, 128, false>(G, tpt) : fused_instance_g<float, 64, false>(G, tpt);
+}
+
+// Whether a workgroup of the kernel fits a compute unit (registers and LDS):
+// the persistent launch places one workgroup per compute unit and every one
+// must be resident at once.  Cached per kernel instance and device.
+bool fused_resident(const void* fn, int dev) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, bool> cache;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nblk = 0;
+  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, fn, kNT, 0) == hipSuccess && nblk >= 1;
+  cache[key] = ok;
+  return ok;
+}
+
+}  // namespace
+
 // Plan: workgroups per row and tokens per workgroup, or false if the fused
-// step does not apply (too many rows, rows too long, group size < 4).
-bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, int32_t* tpb) {
+// step does not apply (too many rows, rows too long, group size < 4, or a
+// workgroup of the instance would not fit a compute unit).
+bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, int mode,
+                int32_t* nb, int32_t* tpb) {
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
   if (G < 4 || rows > 16 || s.max_len < 1) return false;
@@ -1313,6 +1376,7 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, i
   // each workgroup's share of the sink/window tokens must fit its list
   const int64_t forced = (int64_t)n_sink + n_window;
   if ((forced + n_b - 1) / n_b > 64) return false;
+  if (!fused_resident(fused_kernel_for(dt, s.D, G, rounds, mode), dev)) return false;
   *nb = n_b;
   *tpb = rounds * kNT;
   return true;
@@ -1324,7 +1388,7 @@ bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb) 
   if (top_k < 1 || top_k > kFusedMaxPages) return false;
   Shape sp = s;
   sp.max_len = (s.max_len + kPage - 1) / kPage;
-  return fused_plan(sp, 0, 0, nb, tpb);
+  return fused_plan(sp, 0, 0, SA_BF16, 1, nb, tpb);
 }
 
 namespace {
@@ -1341,7 +1405,6 @@ void fused_ws(FusedArgs& a, void* ws, int rows, int nb, int G, int D) {
   a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
   a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
   a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * D, 256);
-  a.err = (uint32_t*)w;         w += 256;
   a.trace = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
   a.plist = (int32_t*)w;         w += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
   a.flags = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
@@ -1397,9 +1460,10 @@ bool select_fused_plan(const SelectArgs& sa, int32_t* nb, int32_t* tpb) {
   s.B = sa.rows / sa.Hkv;
   s.Hkv = sa.Hkv;
   s.Hq = 4 * sa.Hkv;  // (the group size plays no part in selection)
+  s.D = 64;
   s.max_len = sa.max_len;
   s.n_pool_pages = 1;
-  return fused_plan(s, sa.n_sink, sa.n_window, nb, tpb);
+  return fused_plan(s, sa.n_sink, sa.n_window, SA_F32, 2, nb, tpb);
 }
 
 hipError_t launch_select_fused(const SelectArgs& sa, void* ws, int32_t nb, int32_t tpb,

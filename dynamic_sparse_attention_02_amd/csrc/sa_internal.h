@@ -366,7 +366,8 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
                                  float* lse, hipStream_t st);
 
 size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D);
-bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, int32_t* nb, int32_t* tpb);
+bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, int mode,
+                int32_t* nb, int32_t* tpb);
 bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb);
 bool select_fused_plan(const SelectArgs& sa, int32_t* nb, int32_t* tpb);
 hipError_t launch_select_fused(const SelectArgs& sa, void* ws, int32_t nb, int32_t tpb,

@@ -1411,7 +1411,10 @@ __global__ void __launch_bounds__(NT) k_select_row16(SelectArgs a) {
 
 }  // namespace
 
-size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
+namespace {
+
+// Multi-launch path: row state, per-chunk counters and the level histograms.
+size_t select_multi_bytes(int32_t rows, int32_t max_cand) {
   const size_t nch = (size_t)nchunk_of(max_cand < 1 ? 1 : max_cand);
   size_t b = 0;
   b += align_up(sizeof(RowState) * rows, 256);
@@ -1420,11 +1423,18 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
   b += align_up(sizeof(uint64_t) * 2 * rows * kBins, 256);
   b += align_up(sizeof(uint32_t) * 2 * rows * kCoarse, 256);
   b += align_up(sizeof(uint64_t) * 2 * rows * kCoarse, 256);
-  // few long rows may run as one persistent launch instead
-  if (rows <= 16) {
-    const size_t f = fused_workspace_bytes(rows, 256, 1, 0);
-    if (f > b) b = f;
-  }
+  return b;
+}
+
+}  // namespace
+
+// Few long rows may run as one persistent launch instead of the multi-launch
+// path (which one depends on n_sink / n_window too): its state sits in a
+// region of its own after the multi-launch region, so calls of either path
+// can share a workspace.
+size_t select_workspace_bytes(int32_t rows, int32_t max_cand) {
+  size_t b = select_multi_bytes(rows, max_cand);
+  if (rows <= 16) b += align_up(fused_workspace_bytes(rows, 256, 1, 0), 256);
   return b;
 }
 
@@ -1449,7 +1459,8 @@ hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st) {
   // few long rows: one persistent launch whose workgroups split each row and
   // meet at in-memory barriers, if the rows fit its plan
   int32_t fnb = 0, ftpb = 0;
-  if (a.rows <= 16 && select_fused_plan(a, &fnb, &ftpb)) return launch_select_fused(a, ws, fnb, ftpb, st);
+  if (a.rows <= 16 && select_fused_plan(a, &fnb, &ftpb))
+    return launch_select_fused(a, (char*)ws + select_multi_bytes(a.rows, a.max_cand), fnb, ftpb, st);
   const int nch = nchunk_of(a.max_cand < 1 ? 1 : a.max_cand);
   WsLayout w = carve(ws, a.rows, a.max_cand < 1 ? 1 : a.max_cand);
   dim3 grid(nch, a.rows);

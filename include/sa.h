@@ -32,10 +32,14 @@
  *  - Few-row problems may run as one persistent launch (one workgroup per
  *    compute unit, the workgroups of a row meeting at in-memory barriers):
  *    sa_decode_step and sa_decode_step_pages with batch * n_kv_heads <= 16,
- *    and sa_select_topp / sa_select_topk on up to 16 long rows.  Such a
- *    launch needs the compute units to itself while it runs (no kernel of
- *    another stream resident beside it); a barrier that waits about a second
- *    gives up so the launch ends, and that call's outputs are then wrong.
+ *    and sa_select_topp / sa_select_topk on up to 16 long rows.  The library
+ *    takes that path only when the runtime reports that a workgroup of the
+ *    kernel fits a compute unit; the launch still needs the compute units to
+ *    itself while it runs (no kernel of another stream resident beside it).
+ *    A barrier that waits about a second gives up so the launch ends: every
+ *    row whose barrier gave up then reports count[row] = -1 (its list and
+ *    outputs are invalid), and the next call on the workspace starts clean.
+ *    Whenever count[row] >= 0 the row's results are complete.
  *  - Arguments are checked on the host before anything is launched; a failed
  *    check returns an error code, launches nothing and writes nothing.
  *    sa_last_error() then gives a message (per calling thread).  A failed
@@ -261,12 +265,20 @@ sa_status sa_sparse_decode_rla(const sa_shape* shape, const sa_pages* pages, con
                                const float* rla_state, float* rla_num, float* rla_den,
                                void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* One whole decode step: sa_index_scores, then sa_select_topp (p in (0, 1])
- * or, if top_k > 0, sa_select_topk with unit 1, then sa_sparse_decode.  The
- * scores x ([batch * n_kv_heads][ldx] fp32), idx and count are outputs too.
- * With few rows (batch * n_kv_heads <= 16, group size >= 4) the step runs as
- * one persistent launch with the same scores, lists and counts as the three
- * calls and outputs equal within rounding. */
+/* One whole decode step ("Full Attention Strikes Back", method sections 2, 3
+ * and 5: low-rank indexer scores of every cached key, a dynamic top-p support
+ * by a sort-free histogram threshold, sparse decode over it; "Oracle-Guided
+ * Sparse Prefill", section 2.1: exact attention recomputed over the support):
+ * sa_index_scores, then sa_select_topp (p in (0, 1]) or, if top_k > 0,
+ * sa_select_topk with unit 1, then sa_sparse_decode.  The scores x
+ * ([batch * n_kv_heads][ldx] fp32), idx and count are outputs too.  With few
+ * rows (batch * n_kv_heads <= 16, group size >= 4) the step runs as one
+ * persistent launch with the same scores, lists and counts as the three
+ * calls and outputs equal within rounding (count[row] = -1 marks a row whose
+ * barrier gave up, see the conventions above).  Workspace from
+ * SA_OP_DECODE_STEP (param = cap); it holds the separate calls' regions and
+ * the persistent launch's region side by side, so one workspace serves calls
+ * that take either path. */
 sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const void* q,
                          const void* w_q, const void* kidx_pool, const void* k_pool,
                          const void* v_pool, sa_dtype dtype, float s_idx, float s_att,
