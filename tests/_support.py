@@ -82,16 +82,20 @@ def oracle_decode_row(inp, b, g, kt=None, *, p=None, k=None, n_sink=0, n_window=
     return out
 
 
-def allowed_diff(x, core, *, p=None, k=None):
+def allowed_diff(x, core, *, p=None, k=None, extra=None):
     """Candidates whose membership may differ from the oracle's (tie band and
-    top-p mass boundary), given the oracle scores x and its core support."""
+    top-p mass boundary), given the oracle scores x and its core support.
+    extra: optional per-candidate widening of the band (a bound on how far
+    the GPU's score of that candidate may sit from the oracle's for a reason
+    other than arithmetic, e.g. indexer keys the GPU built itself)."""
     x = np.asarray(x, dtype=np.float64)
     n = x.shape[0]
     if n == 0 or len(core) == n:
         tau = x.min() if n else 0.0
     else:
         tau = x[core].min()
-    band = set(np.nonzero(np.abs(x - tau) <= TIE_REL * max(1.0, abs(tau)))[0].tolist())
+    width = TIE_REL * max(1.0, abs(tau)) + (0.0 if extra is None else np.asarray(extra))
+    band = set(np.nonzero(np.abs(x - tau) <= width)[0].tolist())
     if p is not None and n:
         order = O.candidate_order(x)
         cum = np.cumsum(O.softmax_mass(x)[order])
@@ -103,9 +107,21 @@ def allowed_diff(x, core, *, p=None, k=None):
     return band
 
 
-def check_support(gpu_list, x, core, *, L, p=None, k=None, n_sink=0, n_window=0):
+def check_support(gpu_list, x, core, *, L, p=None, k=None, n_sink=0, n_window=0, extra=None):
     """gpu_list: ascending GPU support (union included).  Returns the number
-    of tolerated differences; raises AssertionError on a real mismatch."""
+    of tolerated differences; raises AssertionError on a real mismatch.
+
+    A difference is tolerated only for candidates in the tie band or at the
+    top-p mass boundary (allowed_diff), and the GPU set must still satisfy
+    the selection rule under the oracle's own scores:
+      top-k: the same size as the oracle's;
+      top-p: its core (the GPU set without the forced tokens, plus the
+      forced tokens the oracle's core holds) reaches p in oracle mass, and
+      dropping its lowest-ranked member leaves less than p, each up to
+      MASS_EPS plus the spread of the masses inside the band (a swap of two
+      tied candidates changes the sums by that much).  So a threshold one
+      bin off inside the band fails whether it drops band members or adds
+      them."""
     gpu = np.asarray(gpu_list, dtype=np.int64)
     assert np.all(np.diff(gpu) > 0), "GPU support not strictly ascending"
     assert gpu.size == 0 or (gpu[0] >= 0 and gpu[-1] < L), "GPU support out of range"
@@ -115,17 +131,73 @@ def check_support(gpu_list, x, core, *, L, p=None, k=None, n_sink=0, n_window=0)
         return 0
     forced = set(range(min(n_sink, L))) | set(range(max(0, L - n_window), L))
     assert not (diff & forced), f"forced tokens differ: {sorted(diff & forced)[:10]}"
-    ok = allowed_diff(x, core, p=p, k=k)
+    ok = allowed_diff(x, core, p=p, k=k, extra=extra)
     bad = sorted(diff - ok)
     assert not bad, (f"{len(bad)} support differences outside the tie band, e.g. {bad[:10]} "
                      f"(x={[float(x[j]) for j in bad[:5]]})")
     if k is not None:
         assert len(gpu) == len(full), "top-k support size differs"
+    if p is not None and p < 1.0:
+        check_topp_rule(gpu, x, core, p, forced, ok)
     return len(diff)
+
+
+def check_topp_rule(gpu, x, core, p, forced, band):
+    """The GPU's top-p core reaches p and is minimal, in oracle mass."""
+    x = np.asarray(x, dtype=np.float64)
+    P = O.softmax_mass(x)
+    core_set = set(int(j) for j in core)
+    # Whether a forced token inside the band counts toward the GPU's core
+    # cannot be seen from its list: count such tokens for the reach check and
+    # leave them out for the minimality check.
+    cg = (set(gpu.tolist()) - forced) | (forced & core_set)
+    fb = forced & band
+    bandP = P[np.array(sorted(band), dtype=np.int64)] if band else np.zeros(1)
+    slack = MASS_EPS + float(bandP.max() - bandP.min())
+    hi = np.array(sorted(cg | fb), dtype=np.int64)
+    mass_hi = float(P[hi].sum()) if hi.size else 0.0
+    assert mass_hi >= p - slack, f"GPU top-p core holds mass {mass_hi:.9f} < p = {p}"
+    lo = np.array(sorted(cg - fb), dtype=np.int64)
+    if lo.size == 0:
+        return
+    order = O.candidate_order(x)
+    rank = np.empty(x.shape[0], dtype=np.int64)
+    rank[order] = np.arange(x.shape[0])
+    lowest = lo[np.argmax(rank[lo])]
+    rest = float(P[lo].sum()) - float(P[lowest])
+    assert rest < p + slack, (
+        f"GPU top-p core is not minimal: without its lowest-ranked member {int(lowest)} it "
+        f"still holds {rest:.9f} >= p = {p}")
+
+
+def kidx_score_slack(q_c, kt_oracle, kt_gpu) -> np.ndarray:
+    """Per-token bound on |x_gpu - x_oracle| that comes from indexer keys the
+    GPU built itself (sa_index_append) rather than from the oracle:
+    sum_i |q_c[i]| * |K~_gpu[j, i] - K~_oracle[j, i]|."""
+    return np.abs(np.asarray(kt_gpu, np.float64) - np.asarray(kt_oracle, np.float64)) @ np.abs(q_c)
+
+
+def check_gpu_kidx(kt_gpu, kt_oracle, K, w_k, dtype):
+    """Indexer keys built on the GPU against the oracle: the GPU sums the d
+    products in fp32 (error at most d 2^-24 sum_i |k_i w_i|) and rounds once
+    to the cache dtype (at most half a unit in the last place), so each key
+    lies within that bound of the exact float64 value; and it equals the
+    oracle's rounded value except for the few sums within the fp32 error of
+    a rounding midpoint."""
+    got = np.asarray(kt_gpu, np.float64)
+    ref = np.asarray(kt_oracle, np.float64)
+    K, w_k = np.asarray(K, np.float64), np.asarray(w_k, np.float64)
+    exact = K @ w_k
+    e32 = K.shape[1] * 2.0 ** -24 * (np.abs(K) @ np.abs(w_k))
+    half_ulp = (2.0 ** -8 if dtype == torch.bfloat16 else 2.0 ** -24) * (np.abs(exact) + e32)
+    assert np.all(np.abs(got - exact) <= 1.01 * (e32 + half_ulp)), "indexer key off its bound"
+    mism = got != ref
+    assert mism.mean() < 1e-3, f"{mism.mean():.2e} of the indexer keys differ from the oracle's"
 
 
 def gpu_support(idx: torch.Tensor, count: torch.Tensor, row: int) -> np.ndarray:
     n = int(count.view(-1)[row])
+    assert n >= 0, f"row {row} reports count {n} (a persistent launch's barrier gave up)"
     lst = idx.view(count.numel(), -1)[row].cpu().numpy()
     assert np.all(lst[n:] == -1), "padding is not -1"
     return lst[:n].astype(np.int64)

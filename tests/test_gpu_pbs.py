@@ -164,3 +164,61 @@ def test_pbs_pipeline_all_blocks_is_dense_causal():
     ref = torch.nn.functional.scaled_dot_product_attention(q, K, V, scale=inp.s_att,
                                                            is_causal=True)[0].permute(1, 0, 2)
     assert S.max_abs(out.double().cpu().numpy(), ref.numpy()) <= S.TOL[torch.bfloat16]
+
+
+def test_pbs_prefill128k_sampled_blocks():
+    """The 128K prefill workload with the segment-permuted selection exactly
+    as the bench runs it (importance from the last 64 queries, segments of
+    2048 keys, top-32 blocks, block-sparse attention over the lists).  For
+    two seeded groups: the importance against the oracle; the permutation
+    bit-exact when fed the oracle's importance; for every group the GPU's own
+    permutation is a descending per-segment sort of the GPU's importance;
+    then, on a seeded sample of 64 query blocks, the block selection on the
+    GPU's permutation against the oracle's block scores over that same
+    permutation, and the attention over the GPU's lists."""
+    inp = synth.make_prefill128k(device="cuda")
+    seg, k_blocks, N = 2048, inp.top_k // B_SEL, inp.N
+    imp = gpu_importance(inp)
+    perm = gpu_permutation(inp, imp, seg)
+    idx, count, out, lse = gpu_select_attend(inp, perm, seg, k_blocks)
+    im, pm = imp.cpu().numpy(), perm.cpu().numpy()
+    for g in range(inp.H_kv):
+        for s0 in range(0, N, seg):
+            sp = pm[g, s0:s0 + seg]
+            assert np.array_equal(np.sort(sp), np.arange(s0, min(N, s0 + seg))), (g, s0)
+            v = im[g, sp]
+            assert np.all((v[:-1] > v[1:]) | ((v[:-1] == v[1:]) & (sp[:-1] < sp[1:]))), (g, s0)
+    rng = np.random.default_rng(9)
+    groups = sorted(rng.choice(inp.H_kv, 2, replace=False).tolist())
+    for g in groups:
+        ref = oracle_importance(inp, g)
+        err = np.abs(im[g].astype(np.float64) - ref)
+        assert np.all(err <= 1e-4 * ref + 1e-9 * ref.max()), g
+        ref32 = np.stack([ref.astype(np.float32)] * inp.H_kv)
+        p_o = gpu_permutation(inp, torch.from_numpy(ref32).cuda(), seg).cpu().numpy()[g]
+        assert np.array_equal(p_o, O.pbs_permutation(ref.astype(np.float32).astype(np.float64), seg))
+    nblk = inp.n_blocks
+    fixed = [0, 1, 31, 32, 33, 63, nblk - 1]
+    blocks = sorted(fixed + rng.choice(np.setdiff1d(np.arange(nblk), fixed), 57,
+                                       replace=False).tolist())
+    for g in groups:
+        hs = inp.heads(g)
+        K = S.to_np(inp.keys(g))
+        V = S.to_np(inp.values(g))
+        for blk in blocks:
+            rows = O.prefill_block_rows(blk, B_SEL, N)
+            Qb = S.to_np(inp.q[rows.start:rows.stop][:, hs])
+            gl = S.gpu_support(idx, count, blk * inp.H_kv + g)
+            if blk == 0:
+                assert len(gl) == 0
+            else:
+                x = O.pbs_block_scores(Qb, K, pm[g], blk, B_SEL, seg)
+                assert len(gl) == 64 * min(k_blocks, blk)
+                keyset = set(gl.tolist())
+                gblocks = [c for c in range(blk)
+                           if set(O.pbs_block_keys(pm[g], blk, B_SEL, seg, c).tolist()) <= keyset]
+                assert len(gblocks) * 64 == len(gl), "list is not a union of candidate blocks"
+                S.check_support(np.array(gblocks), x, O.select_topk(x, k_blocks), L=blk, k=k_blocks)
+            o_ref, l_ref = O.prefill_block_attend(Qb, K, V, np.sort(gl), blk, B_SEL, inp.s_att)
+            go = S.to_np(out[rows.start:rows.stop][:, hs])
+            assert S.max_abs(go, o_ref) <= S.TOL[torch.bfloat16], (g, blk)

@@ -102,3 +102,39 @@ def test_prefill_oracle_per_block(N, k, H_q, H_kv):
                 S.check_support(gsup, x, O.select_topk(x, k), L=n_cand, k=k)
             o_ref, _ = O.prefill_block_attend(Qb, K, V, gsup, blk, 64, inp.s_att)
             assert S.max_abs(S.to_np(out[rows.start:rows.stop][:, hs]), o_ref) <= 2e-2
+
+
+def test_prefill_oracle_32k_workload_sampled():
+    """The attention-mass oracle supports of the per-query 32K workload as
+    the bench runs them (32/8 heads, d=128, bf16, each query's top 2048 keys
+    of the head-averaged causal distribution plus its own token) and the
+    attention over them: sampled queries (early, at the k boundary, late and
+    seeded others), every group."""
+    inp = synth.make_prefill_query32k(device="cuda")
+    N, k = inp.N, inp.top_k
+    idx, count, shape, pages = gpu_oracle(inp, 1, k)
+    o = ops()
+    out = torch.full((N, inp.H_q, inp.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((N, inp.H_q), dtype=torch.float32, device="cuda")
+    ws_a = o.alloc_workspace(o.workspace_size(_lib().SA_OP_PREFILL_QUERY, shape, idx.shape[1]))
+    o.sa_sparse_prefill_query(shape, pages, N, inp.q, inp.k_pool, inp.v_pool, idx, count,
+                              inp.s_att, out, lse, ws_a)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    fixed = [0, 1, k - 1, k, k + 1, N // 2, N - 1]
+    queries = sorted(set(fixed) | set(rng.choice(N, 9, replace=False).tolist()))
+    n_diff = 0
+    for g in range(inp.H_kv):
+        hs = inp.heads(g)
+        K = S.to_np(inp.keys(g))
+        V = S.to_np(inp.values(g))
+        for i in queries:
+            qi = S.to_np(inp.q[i, hs])
+            x = _log_mass(O.head_mean_attention(qi, K[: i + 1], inp.s_att))
+            core = O.select_topk(x, k)
+            gsup = S.gpu_support(idx, count, i * inp.H_kv + g)
+            n_diff += S.check_support(gsup, x, core, L=i + 1, k=k, n_window=1)
+            o_ref, _ = O.prefill_query_attend(qi, K, V, gsup, inp.s_att)
+            assert S.max_abs(S.to_np(out[i, hs]), o_ref) <= 2e-2, (i, g)
+    print(f"prefill32k oracle supports: {len(queries)} queries x {inp.H_kv} groups, "
+          f"tolerated support differences {n_diff}")

@@ -128,3 +128,57 @@ def test_decode_rla_matches_oracle(rule, dtype, d):
             assert np.all(np.abs(gn - rn) <= 3e-5 * wabs.max(axis=1, keepdims=True)), (b, g)
             if len(sup) == inp.seq_lens[b]:  # nothing left out: only rounding remains
                 assert np.all(np.abs(gd) <= 3e-5 * wsum)
+
+
+def test_rla_decode64k_full_size():
+    """The 64K decode workload with the residual linear attention tail, as
+    the bench runs it: the state of the whole 65536-token cache by
+    sa_rla_state, then indexer scores, top-p 0.9 with sink 4 and window 512,
+    and sa_sparse_decode_rla; every group against the oracle (state element
+    by element, unselected-token terms against the direct sums)."""
+    o = ops()
+    from dynamic_sparse_attention_02_amd import _lib as L
+    inp = synth.make_decode64k(device="cpu").to("cuda")
+    kidx = S.oracle_kidx_pool(inp)
+    shape = S.shape_of(inp)
+    pages = o.make_pages(inp.page_table, inp.seq_lens_tensor())
+    cap = max(inp.seq_lens)
+    state = gpu_state(inp)
+    st = state.cpu().numpy().astype(np.float64)
+    x, idx, count, out, lse = S.empty_like_outputs(inp, cap)
+    out = out.to(torch.bfloat16)
+    ws_i = o.alloc_workspace(o.workspace_size(L.SA_OP_INDEX_SCORES, shape, 0))
+    ws_s = o.alloc_workspace(o.workspace_size(L.SA_OP_SELECT, shape, cap))
+    ws_r = o.alloc_workspace(o.workspace_size(L.SA_OP_SPARSE_DECODE_RLA, shape, cap))
+    p = S.f32(0.9)
+    o.sa_index_scores(shape, pages, inp.q, inp.w_q, kidx, inp.s_idx, x, ws_i)
+    o.sa_select_topp(shape, pages, x, p, 4, 512, idx, count, ws_s)
+    num = torch.full((inp.B, inp.H_q, inp.d), float("nan"), dtype=torch.float32, device="cuda")
+    den = torch.full((inp.B, inp.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    o.sa_sparse_decode_rla(shape, pages, inp.q, inp.k_pool, inp.v_pool, idx, count, inp.s_att,
+                           out, lse, state, num, den, ws_r)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for g in range(inp.H_kv):
+        hs = inp.heads(g)
+        K = S.to_np(inp.seq_keys(0, g))
+        V = S.to_np(inp.seq_values(0, g))
+        # state: each term carries the fp32 exponential's relative error (a
+        # few 1e-7 for these keys) and the compensated sum adds a few fp32
+        # rounding units, so an element stays within 2e-6 of the sum of the
+        # magnitudes of its terms, however long the cache
+        Sm, z = O.rla_state(K, V)
+        mag = O.rla_feature(K).T @ np.abs(V)
+        assert np.all(np.abs(st[0, g, :inp.d] - Sm) <= 2e-6 * mag + 1e-30), g
+        assert np.all(np.abs(st[0, g, inp.d] - z) <= 2e-6 * z), g
+        q = S.to_np(inp.q[0, hs])
+        sup = S.gpu_support(idx, count, g)
+        rn, rd = O.rla_unselected(q, K, V, sup)
+        wsum, wabs = _unselected_scale(q, K, V)
+        gn, gd = S.to_np(num[0, hs]), S.to_np(den[0, hs])
+        assert np.all(np.abs(gd - rd) <= 3e-5 * wsum), (g, gd, rd)
+        assert np.all(np.abs(gn - rn) <= 3e-5 * wabs.max(axis=1, keepdims=True)), g
+        worst = max(worst, float((np.abs(gd - rd) / wsum).max()))
+        o_ref, _ = O.attend(q, K[sup], V[sup], inp.s_att)
+        assert S.max_abs(S.to_np(out[0, hs]), o_ref) <= 2e-2, g
+    print(f"rla decode64k: worst denominator error {worst:.2e} of the summed weights")

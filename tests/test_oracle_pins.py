@@ -87,10 +87,22 @@ def test_golden_through_scores(case):
     if kind == "topk":
         assert O.select_topk(x, int(param)).tolist() == expect
         return
+    got = O.select_topp(x, param).tolist()
     cums = np.cumsum(np.sort(masses)[::-1])
-    if param < 1 and np.any(np.abs(cums - param) < 1e-12):
-        pytest.skip("p on an exact running sum")
-    assert O.select_topp(x, param).tolist() == expect
+    if not (param < 1 and np.any(np.abs(cums - param) < 1e-12)) or len(set(masses)) == 1:
+        # p away from every running sum, or all masses equal (exp(0) = 1 each,
+        # so the masses are exact): the rule decides
+        assert got == expect
+        return
+    # p on an exact running sum of unequal masses: log and exp round, so the
+    # sum at the boundary may land on either side of p; the expected set or
+    # it plus the next candidate is accepted, and p -/+ 1e-9 (beyond any
+    # float64 rounding here) gives exactly those two sets
+    order = O.candidate_order(x)
+    alt = sorted(expect + [int(order[len(expect)])])
+    assert got in (expect, alt)
+    assert O.select_topp(x, param - 1e-9).tolist() == expect
+    assert O.select_topp(x, param + 1e-9).tolist() == alt
 
 
 def test_softmax_mass_closed_form_and_shift():
@@ -495,6 +507,42 @@ def test_prefill_block_query_permutation_invariant():
     c = O.prefill_block_query(Qb[:, ::-1], Wq[::-1], 0.7)
     np.testing.assert_allclose(a, b, rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(a, c, rtol=1e-13, atol=1e-14)
+
+
+def test_prefill_block_query_closed_form():
+    """Value pins for the block query ("Oracle-Guided Sparse Prefill", section
+    2.2 indexer shared by a block; the mean over the block's queries and the
+    group's heads): with coordinate projectors W_q[h] = c_h [e_0 e_1] and
+    queries q_{i,h} = (i, h, 5, ...), the block query is s_idx times the
+    averages of c_h * i and c_h * h, which integer data give exactly."""
+    n_rows, G, d, r = 64, 4, 8, 2
+    c = np.array([1.0, 2.0, 3.0, 4.0])
+    Wq = np.zeros((G, d, r))
+    for h in range(G):
+        Wq[h, 0, 0] = c[h]
+        Wq[h, 1, 1] = c[h]
+    Qb = np.full((n_rows, G, d), 5.0)
+    for i in range(n_rows):
+        for h in range(G):
+            Qb[i, h, 0] = i
+            Qb[i, h, 1] = h
+    got = O.prefill_block_query(Qb, Wq, 0.5)
+    mean_c_i = c.mean() * (n_rows - 1) / 2.0          # mean over (i, h) of c_h * i
+    mean_c_h = float((c * np.arange(G)).mean())       # mean over (i, h) of c_h * h
+    np.testing.assert_allclose(got, 0.5 * np.array([mean_c_i, mean_c_h]), rtol=0, atol=1e-13)
+    # a one-row block is the decode step's head-collapsed query of that row,
+    # and the block query is the mean of its rows' collapsed queries
+    Q, K, V, Wq2, kt = _prefill_case(23)
+    rows = [O.collapse_query(Q[i], Wq2, 0.7) for i in range(128, 192)]
+    np.testing.assert_allclose(O.prefill_block_query(Q[128:129], Wq2, 0.7), rows[0],
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(O.prefill_block_query(Q[128:192], Wq2, 0.7), np.mean(rows, axis=0),
+                               rtol=1e-12, atol=1e-13)
+    # linear in the queries: doubling one row shifts the mean by that row / n
+    Qd = Q[128:192].copy()
+    Qd[7] *= 2.0
+    np.testing.assert_allclose(O.prefill_block_query(Qd, Wq2, 0.7),
+                               np.mean(rows, axis=0) + rows[7] / 64.0, rtol=1e-12, atol=1e-13)
 
 
 def test_prefill_support_excludes_own_block_and_is_topk():
