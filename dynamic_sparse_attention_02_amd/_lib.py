@@ -83,6 +83,9 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F, _F, _I32,
                                       _I32, _I32, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P,
                                       _SZ, _P]),
+    "sa_decode_step_noalloc": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F,
+                                              _F, _I32, _I32, _I32, _P, _I64, _P, _P, _I32, _P,
+                                              ctypes.c_int, _P, _P]),
     "sa_decode_step_pages": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, ctypes.c_int, _F, _I32, _P,
                                             _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P, _SZ, _P]),
     "sa_select_prefill_topk": (ctypes.c_int, [_SH, _PG, _I32, _P, _P, _P, ctypes.c_int, _F, _I32,

@@ -4,6 +4,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "sa_internal.h"
@@ -411,13 +412,61 @@ sa_status sa_support_coverage(const sa_shape* s, const sa_pages* pg, const float
                                         ref_idx ? overlap : nullptr, st), fn);
 }
 
-sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, const void* w_q,
-                         const void* kidx_pool, const void* k_pool, const void* v_pool,
-                         sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
-                         int32_t n_sink, int32_t n_window, float* x, int64_t ldx, int32_t* idx,
-                         int32_t* count, int32_t cap, void* out, sa_dtype out_dt, float* lse,
-                         void* ws, size_t ws_bytes, hipStream_t st) {
-  const char* fn = "sa_decode_step";
+}  // extern "C"
+
+namespace {
+
+// Scratch of sa_decode_step_noalloc: one copy per device, held until the
+// process ends.  Its front holds the persistent launches' zero part laid out
+// for the most rows they serve, so every call finds it zero whatever its
+// shape; the rest is the workspace of one call.  Host code never uses the
+// array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+__global__ void k_zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+// Device address of this device's scratch; set up on the first call on a
+// device (its zero part cleared once, by a fill kernel on the caller's
+// stream).  NULL on failure.
+void* scratch_on_device(hipStream_t st, hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev]) return g_scratch_ptr[dev];
+  void* ptr = nullptr;
+  *err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (*err != hipSuccess || !ptr) return nullptr;
+  const size_t words = sa::fused_zero_bytes(sa::kFusedMaxRows) / 4;
+  k_zero_words<<<256, 256, 0, st>>>((uint32_t*)ptr, words);
+  *err = hipGetLastError();
+  if (*err != hipSuccess) return nullptr;
+  g_scratch_ptr[dev] = ptr;
+  return ptr;
+}
+
+// sa_decode_step on the caller's workspace, or (use_scratch) on this
+// device's scratch, whose front is the persistent launches' zero part; every
+// argument is checked before the scratch is set up or anything launched.
+sa_status decode_step_impl(const char* fn, const sa_shape* s, const sa_pages* pg, const void* q,
+                           const void* w_q, const void* kidx_pool, const void* k_pool,
+                           const void* v_pool, sa_dtype dt, float s_idx, float s_att, float p,
+                           int32_t top_k, int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
+                           int32_t* idx, int32_t* count, int32_t cap, void* out, sa_dtype out_dt,
+                           float* lse, void* ws, size_t ws_bytes, bool use_scratch, hipStream_t st) {
   SA_TRY(check_shape(s, fn));
   SA_TRY(check_pages(pg, true, fn));
   if (!valid_dtype(dt) || !valid_dtype(out_dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
@@ -434,6 +483,21 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   if (cap < 1 || cap < cap_needed)
     return fail(SA_ERR_CAPACITY, "%s: cap=%d below the worst-case support %lld", fn, cap, (long long)cap_needed);
   const size_t w_i = index_ws(s), w_s = select_ws(s, s->max_len), w_d = decode_ws(s, cap);
+  void* zero = nullptr;
+  if (use_scratch) {
+    const size_t zb = sa::fused_zero_bytes(sa::kFusedMaxRows);
+    const size_t need = zb + step_ws(s, cap);
+    if (need > kScratchBytes)
+      return fail(SA_ERR_WORKSPACE, "%s: this shape needs %zu bytes of scratch, above the %zu the "
+                  "library holds per device (use sa_decode_step with a workspace)", fn, need,
+                  kScratchBytes);
+    hipError_t e = hipSuccess;
+    char* sc = (char*)scratch_on_device(st, &e);
+    if (!sc) return hip_status(e == hipSuccess ? hipErrorInvalidValue : e, fn);
+    zero = sc;
+    ws = sc + zb;
+    ws_bytes = kScratchBytes - zb;
+  }
   SA_TRY(check_ws(ws, ws_bytes, step_ws(s, cap), fn));
   char* base = (char*)ws;
   const sa::Shape sh = to_shape(s);
@@ -441,8 +505,8 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   if (sa::fused_plan(sh, n_sink, n_window, dt, 0, &nb, &tpb))
     return hip_status(sa::launch_decode_fused(sh, *pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
                                               s_att, p, top_k, n_sink, n_window, x, ldx, idx, count,
-                                              cap, out, out_dt, lse, base + w_i + w_s + w_d, nb, tpb,
-                                              st), fn);
+                                              cap, out, out_dt, lse, base + w_i + w_s + w_d, zero, nb,
+                                              tpb, st), fn);
   hipError_t e = sa::launch_index_scores(sh, *pg, q, w_q, kidx_pool, dt, s_idx, x, ldx, (float*)base, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};
@@ -462,11 +526,38 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
   a.idx = idx;
   a.count = count;
   a.cap = cap;
+  a.fused_zero = zero;
   e = sa::launch_select(a, base + w_i, st);
   if (e != hipSuccess) return hip_status(e, fn);
   e = sa::launch_sparse_decode(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
                                lse, base + w_i + w_s, st);
   return hip_status(e, fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, const void* w_q,
+                         const void* kidx_pool, const void* k_pool, const void* v_pool,
+                         sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
+                         int32_t n_sink, int32_t n_window, float* x, int64_t ldx, int32_t* idx,
+                         int32_t* count, int32_t cap, void* out, sa_dtype out_dt, float* lse,
+                         void* ws, size_t ws_bytes, hipStream_t st) {
+  return decode_step_impl("sa_decode_step", s, pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
+                          s_att, p, top_k, n_sink, n_window, x, ldx, idx, count, cap, out, out_dt,
+                          lse, ws, ws_bytes, false, st);
+}
+
+sa_status sa_decode_step_noalloc(const sa_shape* s, const sa_pages* pg, const void* q,
+                                 const void* w_q, const void* kidx_pool, const void* k_pool,
+                                 const void* v_pool, sa_dtype dt, float s_idx, float s_att, float p,
+                                 int32_t top_k, int32_t n_sink, int32_t n_window, float* x,
+                                 int64_t ldx, int32_t* idx, int32_t* count, int32_t cap, void* out,
+                                 sa_dtype out_dt, float* lse, hipStream_t st) {
+  return decode_step_impl("sa_decode_step_noalloc", s, pg, q, w_q, kidx_pool, k_pool, v_pool, dt,
+                          s_idx, s_att, p, top_k, n_sink, n_window, x, ldx, idx, count, cap, out,
+                          out_dt, lse, nullptr, 0, true, st);
 }
 
 sa_status sa_decode_step_pages(const sa_shape* s, const sa_pages* pg, const void* q,
@@ -498,8 +589,8 @@ sa_status sa_decode_step_pages(const sa_shape* s, const sa_pages* pg, const void
   if (dt == SA_BF16 && sa::fused_plan_pages(sh, top_k, &nb, &tpb))
     return hip_status(sa::launch_decode_fused_pages(sh, *pg, q, stats_pool, k_pool, v_pool, s_att,
                                                     top_k, x, ldx, idx, count, cap, out, out_dt,
-                                                    lse, base + w_s + decode_ws(s, cap), nb, tpb,
-                                                    st), fn);
+                                                    lse, base + w_s + decode_ws(s, cap), nullptr,
+                                                    nb, tpb, st), fn);
   hipError_t e = sa::launch_page_scores(sh, *pg, q, stats_pool, dt, s_att, x, ldx, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};

@@ -1282,22 +1282,42 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 
 }  // namespace
 
-// Workspace of the fused step; rows * nb workgroups, G heads, D dims.
-size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
+// Workspace of the fused step, in two parts.  The zero part holds what must
+// be zero when a launch starts and is zero again when it ends (row control
+// words, level histograms, barrier flags); it is laid out for rows_cap rows
+// and a launch uses the first rows of it, so its offsets do not depend on
+// the launch's shape.  The data part (counts, partial outputs, page lists,
+// phase stamps) is written before it is read.
+size_t fused_zero_bytes(int32_t rows_cap) {
   size_t b = 0;
-  b += align_up(sizeof(RowWs) * rows, 256);
-  b += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
-  b += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
-  b += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
-  b += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
+  b += align_up(sizeof(RowWs) * rows_cap, 256);
+  b += align_up(sizeof(uint32_t) * 3 * rows_cap * kBinsF, 256);
+  b += align_up(sizeof(uint64_t) * 3 * rows_cap * kBinsF, 256);
+  b += align_up(sizeof(uint32_t) * 3 * rows_cap * kCoarseF, 256);
+  b += align_up(sizeof(uint64_t) * 3 * rows_cap * kCoarseF, 256);
+  b += align_up(sizeof(uint32_t) * rows_cap * kMaxNB, 256);
+  b += align_up(sizeof(uint64_t) * rows_cap * kMaxNB, 256);
+  return b;
+}
+
+namespace {
+
+size_t fused_data_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
+  size_t b = 0;
   b += 2 * align_up(sizeof(uint32_t) * rows * nb, 256);
   b += align_up(sizeof(float) * rows * nb * G * 2, 256);
   b += align_up(sizeof(float) * rows * nb * G * D, 256);
   b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
   b += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
-  b += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
-  b += align_up(sizeof(uint64_t) * rows * kMaxNB, 256);
   return b;
+}
+
+}  // namespace
+
+// Workspace of the fused step; rows * nb workgroups, G heads, D dims: the
+// zero part for these rows, then the data part.
+size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
+  return fused_zero_bytes(rows) + fused_data_bytes(rows, nb, G, D);
 }
 
 namespace {
@@ -1358,7 +1378,7 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, i
                 int32_t* nb, int32_t* tpb) {
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
-  if (G < 4 || rows > 16 || s.max_len < 1) return false;
+  if (G < 4 || rows > kFusedMaxRows || s.max_len < 1) return false;
   // attention lists hold pool token rows as 32-bit values
   if ((double)s.n_pool_pages * s.Hkv * kPage >= 4294967296.0) return false;
   int dev = 0, cus = 0;
@@ -1393,22 +1413,26 @@ bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb) 
 
 namespace {
 
-// Carves the workspace laid out by fused_workspace_bytes.
-void fused_ws(FusedArgs& a, void* ws, int rows, int nb, int G, int D) {
-  char* w = (char*)ws;
-  a.ctl = (RowWs*)w;            w += align_up(sizeof(RowWs) * rows, 256);
-  a.hcnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kBinsF, 256);
-  a.hmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kBinsF, 256);
-  a.ccnt = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * 3 * rows * kCoarseF, 256);
-  a.cmass = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * 3 * rows * kCoarseF, 256);
+// Carves the workspace laid out by fused_workspace_bytes.  zero: the zero
+// part to use instead of the one at the front of ws (laid out for
+// kFusedMaxRows rows), or NULL.
+void fused_ws(FusedArgs& a, void* ws, void* zero, int rows, int nb, int G, int D) {
+  const int rows_cap = zero ? kFusedMaxRows : rows;
+  char* z = zero ? (char*)zero : (char*)ws;
+  a.ctl = (RowWs*)z;            z += align_up(sizeof(RowWs) * rows_cap, 256);
+  a.hcnt = (uint32_t*)z;        z += align_up(sizeof(uint32_t) * 3 * rows_cap * kBinsF, 256);
+  a.hmass = (uint64_t*)z;       z += align_up(sizeof(uint64_t) * 3 * rows_cap * kBinsF, 256);
+  a.ccnt = (uint32_t*)z;        z += align_up(sizeof(uint32_t) * 3 * rows_cap * kCoarseF, 256);
+  a.cmass = (uint64_t*)z;       z += align_up(sizeof(uint64_t) * 3 * rows_cap * kCoarseF, 256);
+  a.flags = (uint32_t*)z;       z += align_up(sizeof(uint32_t) * rows_cap * kMaxNB, 256);
+  a.mflag = (uint64_t*)z;
+  char* w = (char*)ws + fused_zero_bytes(rows);
   a.blk_sel = (uint32_t*)w;     w += align_up(sizeof(uint32_t) * rows * nb, 256);
   a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
   a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
   a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * D, 256);
   a.trace = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
-  a.plist = (int32_t*)w;         w += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
-  a.flags = (uint32_t*)w;        w += align_up(sizeof(uint32_t) * rows * kMaxNB, 256);
-  a.mflag = (uint64_t*)w;
+  a.plist = (int32_t*)w;
 }
 
 }  // namespace
@@ -1417,8 +1441,8 @@ hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const v
                                      const void* stats_pool, const void* k_pool, const void* v_pool,
                                      float s_att, int32_t top_k, float* x, int64_t ldx,
                                      int32_t* idx, int32_t* count, int32_t cap, void* out,
-                                     sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
-                                     hipStream_t st) {
+                                     sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
+                                     int32_t tpb, hipStream_t st) {
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
   FusedArgs a{};
@@ -1427,7 +1451,7 @@ hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const v
   a.s_att = s_att; a.p = 0.f; a.top_k = top_k; a.n_sink = 0; a.n_window = 0;
   a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
   a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
-  fused_ws(a, ws, rows, nb, G, s.D);
+  fused_ws(a, ws, zero, rows, nb, G, s.D);
   const int tpt = tpb / kNT;
   dim3 grid(rows * nb);
 #define SA_FP(DD, GG, PP) k_decode_fused<bf16_raw, DD, GG, PP, true, false><<<grid, kNT, 0, st>>>(a)
@@ -1485,7 +1509,7 @@ hipError_t launch_select_fused(const SelectArgs& sa, void* ws, int32_t nb, int32
   a.cap = sa.cap;
   a.nb = nb;
   a.tpb = tpb;
-  fused_ws(a, ws, sa.rows, nb, 1, 0);
+  fused_ws(a, ws, sa.fused_zero, sa.rows, nb, 1, 0);
   dim3 grid(sa.rows * nb);
 #define SA_FS(PP) k_decode_fused<float, 64, 4, PP, false, true><<<grid, kNT, 0, st>>>(a)
   switch (tpb / kNT) {
@@ -1504,8 +1528,8 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
                                sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
                                int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
                                int32_t* idx, int32_t* count, int32_t cap, void* out,
-                               sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
-                               hipStream_t st) {
+                               sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
+                               int32_t tpb, hipStream_t st) {
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
   FusedArgs a{};
@@ -1514,7 +1538,7 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
   a.s_idx = s_idx; a.s_att = s_att; a.p = p; a.top_k = top_k; a.n_sink = n_sink;
   a.n_window = n_window; a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
   a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
-  fused_ws(a, ws, rows, nb, G, s.D);
+  fused_ws(a, ws, zero, rows, nb, G, s.D);
   const int tpt = tpb / kNT;  // 1, 2, 4, 8 or 16 (fused_plan)
   dim3 grid(rows * nb);
 #define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP, false, false><<<grid, kNT, 0, st>>>(a)

@@ -325,6 +325,9 @@ struct SelectArgs {
   int32_t kidx_bf16;
   const int32_t* pt;        // the sequence's page-table row
   int64_t n_pool_pages;
+  // host side: the zero part the persistent few-row launch uses instead of
+  // the one in its workspace region (NULL: its own)
+  void* fused_zero;
 };
 constexpr int kSelectRowMax = 131072;  // longest row the one-block-per-row selection takes
 size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
@@ -365,7 +368,9 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
                                  int32_t b_sel, float s_att, void* out, sa_dtype out_dt,
                                  float* lse, hipStream_t st);
 
+constexpr int kFusedMaxRows = 16;  // rows a persistent launch serves at most
 size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D);
+size_t fused_zero_bytes(int32_t rows_cap);
 bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, int mode,
                 int32_t* nb, int32_t* tpb);
 bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb);
@@ -376,15 +381,15 @@ hipError_t launch_decode_fused_pages(const Shape& s, const sa_pages& pg, const v
                                      const void* stats_pool, const void* k_pool, const void* v_pool,
                                      float s_att, int32_t top_k, float* x, int64_t ldx,
                                      int32_t* idx, int32_t* count, int32_t cap, void* out,
-                                     sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
-                                     hipStream_t st);
+                                     sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
+                                     int32_t tpb, hipStream_t st);
 hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q, const void* w_q,
                                const void* kidx_pool, const void* k_pool, const void* v_pool,
                                sa_dtype dt, float s_idx, float s_att, float p, int32_t top_k,
                                int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
                                int32_t* idx, int32_t* count, int32_t cap, void* out,
-                               sa_dtype out_dt, float* lse, void* ws, int32_t nb, int32_t tpb,
-                               hipStream_t st);
+                               sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
+                               int32_t tpb, hipStream_t st);
 
 size_t mass_workspace_bytes(const Shape& s);
 hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q,

@@ -204,6 +204,17 @@ def sa_decode_step(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att
     L.check(st, "sa_decode_step")
 
 
+def sa_decode_step_noalloc(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att, p,
+                           top_k, n_sink, n_window, x, idx, count, out, lse, stream=None):
+    st = L.load().sa_decode_step_noalloc(ctypes.byref(shape), ctypes.byref(pages), _dev(q),
+                                         _dev(w_q), _dev(kidx_pool), _dev(k_pool), _dev(v_pool),
+                                         _dt(q), float(s_idx), float(s_att), float(p), int(top_k),
+                                         int(n_sink), int(n_window), _dev(x), int(x.stride(0)),
+                                         _dev(idx), _dev(count), int(idx.shape[-1]), _dev(out),
+                                         _dt(out), _dev(lse), _stream(stream))
+    L.check(st, "sa_decode_step_noalloc")
+
+
 def sa_decode_step_pages(shape, pages, q, stats_pool, k_pool, v_pool, s_att, top_k, x, idx, count,
                          out, lse, ws, stream=None):
     wp, wn = _ws(ws)

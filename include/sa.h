@@ -287,6 +287,25 @@ sa_status sa_decode_step(const sa_shape* shape, const sa_pages* pages, const voi
                          void* out, sa_dtype out_dtype, float* lse, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* sa_decode_step for callers that cannot allocate memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same arguments, results and kernels, minus the workspace.  Its scratch is
+ * a 64 MiB array the library holds on each device it runs on until the
+ * process ends (set up, and its zero-state part cleared by a fill kernel on
+ * the given stream, by the first call on a device).  Shapes whose workspace
+ * (SA_OP_DECODE_STEP) plus that zero-state part exceed it are rejected with
+ * SA_ERR_WORKSPACE before anything is launched.  The call allocates nothing.
+ * Every call on a device shares that device's scratch and leaves it as the
+ * previous call's state: calls that overlap on one device (different
+ * streams without ordering, or different host threads) race, so they must
+ * be ordered like calls sharing a workspace. */
+sa_status sa_decode_step_noalloc(const sa_shape* shape, const sa_pages* pages, const void* q,
+                                 const void* w_q, const void* kidx_pool, const void* k_pool,
+                                 const void* v_pool, sa_dtype dtype, float s_idx, float s_att,
+                                 float p, int32_t top_k, int32_t n_sink, int32_t n_window,
+                                 float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
+                                 void* out, sa_dtype out_dtype, float* lse, hipStream_t stream);
+
 /* One whole page-level decode step ("SPLA", section 2.1: pages ranked by the
  * Taylor score, the top_k pages attended exactly): sa_page_scores, then
  * sa_select_topk with unit = page_size (n_sink = n_window = 0), then

@@ -194,3 +194,22 @@ def test_zero_work_calls_return_ok_without_launch():
     assert so.sa_index_append(ctypes.byref(s), None, None, L.SA_BF16, None, 0, None, None) == L.SA_OK
     assert so.sa_page_stats(ctypes.byref(s), None, L.SA_BF16, None, None, 0, None, None) == L.SA_OK
     assert so.sa_last_error() == b""
+
+
+def test_decode_step_noalloc_rejects_before_touching_the_device():
+    """The allocation-free decode step checks its arguments, and whether the
+    shape fits the library's scratch, before it sets up anything on a device:
+    these calls return on the host."""
+    L, so = lib()
+    s = _shape(L)
+    pg = L.SaPages(FAKE, FAKE)
+    B = ctypes.byref
+    call = lambda sh, p, cap, **kw: so.sa_decode_step_noalloc(
+        B(sh), B(pg), FAKE, FAKE, FAKE, FAKE, FAKE, L.SA_BF16, 1.0, 0.1, p, 0, 4, 512, FAKE,
+        sh.max_len, FAKE, FAKE, cap, FAKE, L.SA_F32, None, None)
+    assert call(s, 0.9, 60000) == L.SA_ERR_CAPACITY
+    assert call(s, 0.0, 65536) == L.SA_ERR_INVALID_ARGUMENT
+    # 32 sequences of up to 128K tokens need far more than the 64 MiB scratch
+    big = _shape(L, batch=32, n_kv_heads=8, max_pages=2048, max_len=131072, n_pool_pages=65536)
+    assert call(big, 0.9, 131072) == L.SA_ERR_WORKSPACE
+    assert b"scratch" in so.sa_last_error()
