@@ -294,14 +294,12 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
       for (int u = 0; u < PB; ++u) {
         const int32_t jl = (r0 + u) * PPI + wave * PPW + slot;
-        mraw[u] = w4_t{0u, 0u, 0u, 0u};
-        vraw[u] = w4_t{0u, 0u, 0u, 0u};
-        if (j0 + jl < n) {
-          const int64_t page = __float_as_int(s_ps[jl]);
-          const T* rowp = stats + (page * s.Hkv + g) * 2 * (int64_t)D + sub * 8;
-          mraw[u] = *reinterpret_cast<const w4_t*>(rowp);
-          vraw[u] = *reinterpret_cast<const w4_t*>(rowp + D);
-        }
+        // (branch-free: a slot past the row holds pool page 0, whose
+        // statistics are read and whose score is not kept)
+        const int64_t page = __float_as_int(s_ps[jl]);
+        const T* rowp = stats + (page * s.Hkv + g) * 2 * (int64_t)D + sub * 8;
+        mraw[u] = *reinterpret_cast<const w4_t*>(rowp);
+        vraw[u] = *reinterpret_cast<const w4_t*>(rowp + D);
       }
       float qs[8], qq[G][8];
       page_query_lane<D, G>(s_qs, s_qq, sub, qs, qq);
@@ -353,63 +351,78 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   } else {
     // ---- 1. scores of the own tokens ----
   const T* kidx = (const T*)a.kidx;
-  for (int i = tid; i < TPT * kNT / kPage; i += kNT)
-    s_pt[i] = j0 + i * kPage < n ? (int32_t)clamp_page(pt[(j0 >> 6) + i], s.n_pool_pages) : 0;
-  __syncthreads();
+  const T* q = (const T*)a.q;
+  const T* w_q = (const T*)a.w_q;
   {
-    // issue the indexer-key loads first, collapse the query while they fly
-    float kv[TPT][kRank];
+    // Issued together: the pool pages of the own tokens (per lane straight
+    // from the page table; a wave's lanes share each page, so a round is one
+    // broadcast load), and the collapse's projector rows and query values.
+    // The indexer keys follow as soon as the pages arrive, and the collapse
+    // is computed while they are in flight.
+    // (branch-free: a token past the row reads the row's last valid entry,
+    // or entry 0 of an empty row, and its key is zeroed after the load, so
+    // the compiler need not wait for each load where it is issued)
+    const int32_t jlast = n > 0 ? n - 1 : 0;
+    int64_t pgu[TPT];
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-      const int32_t j = j0 + u * kNT + tid;
-      if (j < n) {
-        const int64_t page = s_pt[(j - j0) >> 6];
-        const T* rowp = kidx + ((page * s.Hkv + g) * kPage + (j & 63)) * kRank;
-        if constexpr (sizeof(T) == 2) {
-          const uint4* v = reinterpret_cast<const uint4*>(rowp);
-          const uint4 x0 = v[0], x1 = v[1];
-          const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            kv[u][2 * i] = __uint_as_float(w8[i] << 16);
-            kv[u][2 * i + 1] = __uint_as_float(w8[i] & 0xffff0000u);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < kRank; ++i) kv[u][i] = to_f32<T>(rowp[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < kRank; ++i) kv[u][i] = 0.f;
-      }
+      const int32_t j = min(j0 + u * kNT + tid, jlast);
+      pgu[u] = clamp_page(pt[j >> 6], s.n_pool_pages);
     }
-    // head-collapsed query (same order of operations as k_collapse)
-    const T* q = (const T*)a.q;
-    const T* w_q = (const T*)a.w_q;
-    float acc[kRank];
+    for (int i = tid; i < TPT * kNT / kPage; i += kNT)  // (for the lists; the barriers below publish it)
+      s_pt[i] = j0 + i * kPage < n ? (int32_t)clamp_page(pt[(j0 >> 6) + i], s.n_pool_pages) : 0;
+    constexpr int NPI = G * D / kNT;  // collapse products per thread
+    static_assert(G * D % kNT == 0, "whole collapse rounds");
+    float w[NPI][kRank], qv[NPI];
 #pragma unroll
-    for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
-    for (int pi = tid; pi < G * D; pi += kNT) {
+    for (int ip = 0; ip < NPI; ++ip) {
+      const int pi = tid + ip * kNT;
       const int h = g * G + pi / D, i = pi % D;
       const T* wr = w_q + ((int64_t)h * D + i) * kRank;
-      float w[kRank];
       if constexpr (sizeof(T) == 2) {
         const uint4* v = reinterpret_cast<const uint4*>(wr);
         const uint4 x0 = v[0], x1 = v[1];
         const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          w[2 * k] = __uint_as_float(w8[k] << 16);
-          w[2 * k + 1] = __uint_as_float(w8[k] & 0xffff0000u);
+          w[ip][2 * k] = __uint_as_float(w8[k] << 16);
+          w[ip][2 * k + 1] = __uint_as_float(w8[k] & 0xffff0000u);
         }
       } else {
 #pragma unroll
-        for (int k = 0; k < kRank; ++k) w[k] = to_f32<T>(wr[k]);
+        for (int k = 0; k < kRank; ++k) w[ip][k] = to_f32<T>(wr[k]);
       }
-      const float qv = to_f32<T>(q[((int64_t)b * s.Hq + h) * D + i]);
-#pragma unroll
-      for (int c = 0; c < kRank; ++c) acc[c] = fmaf(w[c], qv, acc[c]);
+      qv[ip] = to_f32<T>(q[((int64_t)b * s.Hq + h) * D + i]);
     }
+    float kv[TPT][kRank];
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t jt = j0 + u * kNT + tid;
+      const bool valid = jt < n;
+      const int32_t j = min(jt, jlast);
+      const T* rowp = kidx + ((pgu[u] * s.Hkv + g) * kPage + (j & 63)) * kRank;
+      if constexpr (sizeof(T) == 2) {
+        const uint4* v = reinterpret_cast<const uint4*>(rowp);
+        const uint4 x0 = v[0], x1 = v[1];
+        const uint32_t w8[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          kv[u][2 * i] = valid ? __uint_as_float(w8[i] << 16) : 0.f;
+          kv[u][2 * i + 1] = valid ? __uint_as_float(w8[i] & 0xffff0000u) : 0.f;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRank; ++i) kv[u][i] = valid ? to_f32<T>(rowp[i]) : 0.f;
+      }
+    }
+    // head-collapsed query (same order of operations as k_collapse)
+    float acc[kRank];
+#pragma unroll
+    for (int c = 0; c < kRank; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int ip = 0; ip < NPI; ++ip)
+#pragma unroll
+      for (int c = 0; c < kRank; ++c) acc[c] = fmaf(w[ip][c], qv[ip], acc[c]);
 #pragma unroll
     for (int c = 0; c < kRank; ++c) {
       const float v = wave_sum(acc[c]);
@@ -865,36 +878,43 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
     // K and V rows: 16 lanes per row (contiguous loads), staged row-major;
-    // the V^T operand is gathered from four rows by 2-byte LDS reads.  NBUF
-    // tiles of rows are in flight
-    constexpr int NBUF = 2;
-    uint4 kq[NBUF][LPT], vq[NBUF][LPT];
-    auto gather = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
+    // the V^T operand is gathered from four rows by 2-byte LDS reads.  Tiles
+    // go in pairs through two register buffers: while a tile is computed the
+    // next tile's rows and the following pair's are in flight.  The gathers
+    // are branch-free (rows past the list re-read its last token, whose
+    // scores are masked), so the compiler waits for one buffer's loads at a
+    // staging, not for every load in flight.
+    // (each buffer is one vector value, so it stays in registers)
+    typedef uint32_t kvv_t __attribute__((ext_vector_type(4 * LPT)));
+    kvv_t kA, vA, kB, vB;
+    auto gather = [&](int32_t ts, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
         const int rk = pc / CPR, ck = pc % CPR;
-        kr[i] = make_uint4(0, 0, 0, 0);
-        vr[i] = make_uint4(0, 0, 0, 0);
-        if (ts + rk < n_att) {
-          const int64_t off = (int64_t)my_list[ts + rk] * D + ck * 8;
-          kr[i] = *reinterpret_cast<const uint4*>(k_pool + off);
-          vr[i] = *reinterpret_cast<const uint4*>(v_pool + off);
-        }
+        const int32_t e = min(ts + rk, n_att - 1);
+        const int64_t off = (int64_t)my_list[e] * D + ck * 8;
+        const uint4 k4 = *reinterpret_cast<const uint4*>(k_pool + off);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(v_pool + off);
+        kr[4 * i] = k4.x; kr[4 * i + 1] = k4.y; kr[4 * i + 2] = k4.z; kr[4 * i + 3] = k4.w;
+        vr[4 * i] = v4.x; vr[4 * i + 1] = v4.y; vr[4 * i + 2] = v4.z; vr[4 * i + 3] = v4.w;
       }
     };
-    auto tile = [&](int32_t ts, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
-      const int32_t nt = min(kTileF, n_att - ts);
+    auto stage = [&](const kvv_t& kr, const kvv_t& vr) __attribute__((always_inline)) {
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
         const int rk = pc / CPR, ck = pc % CPR;
-        *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) = kr[i];
-        *reinterpret_cast<uint4*>(Vs + rk * PITCH + ck * 16) = vr[i];
+        *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) =
+            make_uint4(kr[4 * i], kr[4 * i + 1], kr[4 * i + 2], kr[4 * i + 3]);
+        *reinterpret_cast<uint4*>(Vs + rk * PITCH + ck * 16) =
+            make_uint4(vr[4 * i], vr[4 * i + 1], vr[4 * i + 2], vr[4 * i + 3]);
       }
       __syncthreads();
-      if (ts + NBUF * kTileF < n_att) gather(ts + NBUF * kTileF, kr, vr);
+    };
+    auto compute = [&](int32_t ts) __attribute__((always_inline)) {
+      const int32_t nt = min(kTileF, n_att - ts);
       f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
 #pragma unroll
@@ -945,13 +965,22 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
       }
     };
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u)
-      if (u * kTileF < n_att) gather(u * kTileF, kq[u], vq[u]);
-    for (int32_t ts = 0; ts < n_att; ts += NBUF * kTileF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u)
-        if (ts + u * kTileF < n_att) tile(ts + u * kTileF, kq[u], vq[u]);
+    int32_t ts = 0;
+    if (n_att > 0) {
+      gather(0, kA, vA);
+      gather(kTileF, kB, vB);
+      for (; ts + kTileF < n_att; ts += 2 * kTileF) {  // both tiles of the pair hold tokens
+        stage(kA, vA);
+        gather(ts + 2 * kTileF, kA, vA);
+        compute(ts);
+        stage(kB, vB);
+        gather(ts + 3 * kTileF, kB, vB);
+        compute(ts + kTileF);
+      }
+      if (ts < n_att) {  // an odd last tile
+        stage(kA, vA);
+        compute(ts);
+      }
     }
     stamp(a, 8);
     // merge the waves: lane (lg, hq) holds O^T[16 mb + 4 lg + v][hq]

@@ -190,38 +190,68 @@ __device__ __forceinline__ void page_query_lane(const float* s_qs, const float (
 #pragma unroll
     for (int e = 0; e < 8; ++e) qq[h][e] = s_qq[h][sub * 8 + e];
 }
-// sum_h [q'_h . mean + log1p(0.5 q'_h^2 . var)] of the page whose 8 mean and
+// One step of a reduce-scatter over the lanes of a page: the lanes split in
+// two halves by the DPP pairing CTRL (each lane's partner sits in the other
+// half); a lane keeps half of its N partial sums (the lower half the first
+// N / 2, the upper half the rest), adding its partner's partials of those.
+// With one sum left the step adds the partner's whole sum instead.
+template <int N, int CTRL>
+__device__ __forceinline__ void page_reduce_step(float* v, int sub, int bit) {
+  if constexpr (N > 1) {
+    const bool upper = (sub & bit) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float keep = upper ? v[N / 2 + i] : v[i];
+      const float send = upper ? v[i] : v[N / 2 + i];
+      v[i] = keep + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(send), CTRL, 0xF, 0xF, true));
+    }
+  } else {
+    v[0] += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v[0]), CTRL, 0xF, 0xF, true));
+  }
+}
+// sum_h [q'_h . mean + log(1 + 0.5 q'_h^2 . var)] of the page whose 8 mean and
 // variance dimensions of this lane are mu, va; every lane of the page gets it.
+// The G per-head variance sums are reduce-scattered over the page's lanes
+// (widest pairing first), so each lane ends holding whole sums of
+// max(1, G / LPP) heads, each head held by max(1, LPP / G) lanes; every lane
+// takes the logarithm of its own, and one row sum adds them (scaled by the
+// repetition) to the mean term.
 template <int LPP, int G>
 __device__ __forceinline__ float page_score_sum(const float (&mu)[8], const float (&va)[8],
                                                 const float (&qs)[8], const float (&qq)[G][8],
                                                 int sub) {
-  constexpr int HPL = (G + LPP - 1) / LPP;  // heads kept per lane
+  static_assert(LPP == 8 || LPP == 16, "a page spreads over 8 or 16 lanes");
   float first = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) first = fmaf(qs[e], mu[e], first);
-  float mine[HPL];
-#pragma unroll
-  for (int j = 0; j < HPL; ++j) mine[j] = 0.f;
+  float v[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     float c = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) c = fmaf(qq[h][e], va[e], c);
-    c = row_sum<LPP>(c);
-    if (sub == h % LPP) mine[h / LPP] = c;
+    v[h] = c;
   }
-  float acc = first;
+  constexpr int N0 = G;
+  constexpr int N1 = LPP == 16 ? (N0 > 1 ? N0 / 2 : 1) : N0;
+  constexpr int N2 = N1 > 1 ? N1 / 2 : 1;
+  constexpr int N3 = N2 > 1 ? N2 / 2 : 1;
+  constexpr int N4 = N3 > 1 ? N3 / 2 : 1;
+  if constexpr (LPP == 16) page_reduce_step<N0, kDppMirror>(v, sub, 8);
+  page_reduce_step<N1, kDppHalfMirror>(v, sub, 4);
+  page_reduce_step<N2, kDppXor2>(v, sub, 2);
+  page_reduce_step<N3, kDppXor1>(v, sub, 1);
+  constexpr int DUP = LPP / G > 1 ? LPP / G : 1;  // lanes holding each head's sum
+  float lp = 0.f;
 #pragma unroll
-  for (int j = 0; j < HPL; ++j)
-    if (j * LPP + sub < G) acc += log1pf(0.5f * mine[j]);
-  return row_sum<LPP>(acc);
+  for (int i = 0; i < N4; ++i) lp += __logf(1.0f + 0.5f * v[i]);
+  return row_sum<LPP>(first + lp * (1.0f / (float)DUP));
 }
 // The page score: the head mean plus log(valid tokens / page size).
 template <int G>
 __device__ __forceinline__ float page_score_final(float sum, int32_t L, int32_t page) {
   const int nv = (L - page * kPage) < kPage ? (L - page * kPage) : kPage;
-  return sum / (float)G + logf((float)nv / (float)kPage);
+  return sum * (1.0f / (float)G) + (nv < kPage ? __logf((float)nv * (1.0f / (float)kPage)) : 0.f);
 }
 
 // Value of a lane chosen by a wave-uniform index.
