@@ -18,6 +18,10 @@
 // Bound: HBM bandwidth of the gathered rows (512 B per listed token for
 // d = 128 bf16).  No matrix cores: the per-token work is a G x d by d x 1
 // product, too thin to fill an MFMA tile.
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -47,9 +51,10 @@ __device__ __forceinline__ int32_t row_count(const int32_t* count, int row, int3
 }
 
 // Tiles per chunk from the total listed tiles (same result in every block).
+constexpr int kMaxTpc = 16;
 __device__ __forceinline__ int32_t plan_tpc(int64_t total_tiles, int32_t grid) {
   int64_t t = (total_tiles + 2 * (int64_t)grid - 1) / (2 * (int64_t)grid);
-  return t < 1 ? 1 : (t > 16 ? 16 : (int32_t)t);
+  return t < 1 ? 1 : (t > kMaxTpc ? kMaxTpc : (int32_t)t);
 }
 
 template <typename T, int D, int G>
@@ -90,6 +95,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   __shared__ __align__(16) float PhiQ[RLA ? G : 1][RLA ? D : 1];
   __shared__ __align__(16) float Ws[RLA ? G : 1][RLA ? kTile : 1];
   __shared__ int32_t prefix[RMAX + 1];
+  __shared__ uint32_t s_rid[kMaxTpc * kTile];  // pool rows of the item's listed tokens
   __shared__ int64_t s_tiles;
   __shared__ int32_t s_red[4];
 
@@ -136,12 +142,19 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
     const int32_t* pt = page_table + (int64_t)b * s.max_pages;
     const int32_t* list = idx + (int64_t)row * cap;
 
-    __syncthreads();  // previous item done with Qs
+    __syncthreads();  // previous item done with Qs and the row list
+    // pool row of every listed token of the chunk (page << 6 | slot)
+    for (int32_t e = tid; e < t1 - t0; e += C::NT) {
+      int32_t j = list[t0 + e];
+      j = j < 0 ? 0 : (j >= L ? (L > 0 ? L - 1 : 0) : j);
+      s_rid[e] = ((uint32_t)clamp_page(pt[j >> 6], s.n_pool_pages) << 6) | (uint32_t)(j & 63);
+    }
     for (int i = tid; i < G * D; i += C::NT) {
       const T qv = q[((int64_t)b * s.Hq + g * G) * D + i];
       Qs[i / D][i % D] = qv;
       if (RLA) PhiQ[i / D][i % D] = __expf(to_f32<T>(qv));
     }
+    __syncthreads();  // the row list is read by every thread's gathers below
     float racc[RLA ? C::HPW : 1][RLA ? C::DPL : 1], rden[RLA ? C::HPW : 1];
     if (RLA) {
 #pragma unroll
@@ -160,50 +173,40 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
 #pragma unroll
       for (int e = 0; e < C::DPL; ++e) acc[hh][e] = 0.f;
     }
-    // pool element offsets of the rows this thread moves in a tile
-    int64_t ridn[C::LPT];
-    auto load_rows = [&](int32_t ts, int64_t (&rid)[C::LPT]) {
-#pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        const int r = (i * C::NT + tid) / C::CPR;
-        rid[i] = -1;
-        if (ts + r < t1) {
-          int32_t j = list[ts + r];
-          j = j < 0 ? 0 : (j >= L ? (L > 0 ? L - 1 : 0) : j);
-          const int64_t page = clamp_page(pt[j >> 6], s.n_pool_pages);
-          rid[i] = page * page_stride + g * head_stride + (int64_t)(j & 63) * D;
-        }
-      }
-    };
-    uint4 kr[C::LPT], vr[C::LPT];
-    auto load_kv = [&](const int64_t (&rid)[C::LPT]) {
-#pragma unroll
-      for (int i = 0; i < C::LPT; ++i) {
-        const int col = (i * C::NT + tid) % C::CPR;
-        if (rid[i] >= 0) {
-          kr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + rid[i]) + col * 16);
-          vr[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + rid[i]) + col * 16);
-        } else {
-          kr[i] = make_uint4(0, 0, 0, 0);
-          vr[i] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    load_rows(t0, ridn);
-    load_kv(ridn);
-    if (t0 + kTile < t1) load_rows(t0 + kTile, ridn);
-    for (int32_t ts = t0; ts < t1; ts += kTile) {
-      const int32_t nt = min(kTile, t1 - ts);
-      __syncthreads();  // previous tile fully consumed (and Qs written)
+    // Tiles of K/V rows go through registers (one vector value per buffer,
+    // so they stay in registers) into LDS.  The gathers are branch-free:
+    // rows past the chunk re-read its last token, whose logits are masked.
+    // With two buffers (up to 8 pieces per thread) the next tile's rows and
+    // the one after are in flight while a tile is computed; the addresses
+    // come from the LDS row list, so no dependent load sits between a
+    // prefetch and the staging that needs it.
+    typedef uint32_t kvv_t __attribute__((ext_vector_type(4 * C::LPT)));
+    auto gather = [&](int32_t ts, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < C::LPT; ++i) {
         const int pc = i * C::NT + tid;
         const int r = pc / C::CPR, col = pc % C::CPR;
-        *reinterpret_cast<uint4*>(Ks + r * C::PITCH + col * 16) = kr[i];
-        *reinterpret_cast<uint4*>(Vs + r * C::PITCH + col * 16) = vr[i];
+        const uint32_t v = s_rid[min(ts + r, t1 - 1) - t0];
+        const int64_t off = (((int64_t)(v >> 6) * s.Hkv + g) * kPage + (v & 63)) * D;
+        const uint4 k4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(k_pool + off) + col * 16);
+        const uint4 v4 = *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(v_pool + off) + col * 16);
+        kr[4 * i] = k4.x; kr[4 * i + 1] = k4.y; kr[4 * i + 2] = k4.z; kr[4 * i + 3] = k4.w;
+        vr[4 * i] = v4.x; vr[4 * i + 1] = v4.y; vr[4 * i + 2] = v4.z; vr[4 * i + 3] = v4.w;
+      }
+    };
+    auto stage = [&](const kvv_t& kr, const kvv_t& vr) __attribute__((always_inline)) {
+      __syncthreads();  // previous tile fully consumed
+#pragma unroll
+      for (int i = 0; i < C::LPT; ++i) {
+        const int pc = i * C::NT + tid;
+        const int r = pc / C::CPR, col = pc % C::CPR;
+        const uint4 k4 = make_uint4(kr[4 * i], kr[4 * i + 1], kr[4 * i + 2], kr[4 * i + 3]);
+        *reinterpret_cast<uint4*>(Ks + r * C::PITCH + col * 16) = k4;
+        *reinterpret_cast<uint4*>(Vs + r * C::PITCH + col * 16) =
+            make_uint4(vr[4 * i], vr[4 * i + 1], vr[4 * i + 2], vr[4 * i + 3]);
         if (RLA) {
           constexpr int EPP = 16 / (int)sizeof(T);  // elements per 16-byte piece
-          const uint32_t w[4] = {kr[i].x, kr[i].y, kr[i].z, kr[i].w};
+          const uint32_t w[4] = {k4.x, k4.y, k4.z, k4.w};
           float* dst = &PhiK[r][col * EPP];
           if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -218,123 +221,147 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
         }
       }
       __syncthreads();
-      if (ts + kTile < t1) {  // next tile's rows in flight, and the addresses after it
-        load_kv(ridn);
-        if (ts + 2 * kTile < t1) load_rows(ts + 2 * kTile, ridn);
-      }
-
-      // logits: lane = token of the tile
-      float sc[C::HPW];
-#pragma unroll
-      for (int hh = 0; hh < C::HPW; ++hh) sc[hh] = 0.f;
-      const char* krow = Ks + lane * C::PITCH;
-#pragma unroll 4
-      for (int pc = 0; pc < C::CPR; ++pc) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + pc * 16);
-#pragma unroll
-        for (int hh = 0; hh < C::HPW; ++hh) {
-          const int h = wave * C::HPW + hh;
-          if constexpr (sizeof(T) == 2) {
-            const uint4 qv = *reinterpret_cast<const uint4*>(&Qs[h][pc * 8]);
-            float a = sc[hh];
-            a = dot2_bf16(kv.x, qv.x, a);
-            a = dot2_bf16(kv.y, qv.y, a);
-            a = dot2_bf16(kv.z, qv.z, a);
-            a = dot2_bf16(kv.w, qv.w, a);
-            sc[hh] = a;
-          } else {
-            const float4 qv = *reinterpret_cast<const float4*>(&Qs[h][pc * 4]);
-            float a = sc[hh];
-            a = fmaf(__uint_as_float(kv.x), qv.x, a);
-            a = fmaf(__uint_as_float(kv.y), qv.y, a);
-            a = fmaf(__uint_as_float(kv.z), qv.z, a);
-            a = fmaf(__uint_as_float(kv.w), qv.w, a);
-            sc[hh] = a;
-          }
-        }
-      }
-      float alpha[C::HPW];
-#pragma unroll
-      for (int hh = 0; hh < C::HPW; ++hh) {
-        const float sv = lane < nt ? sc[hh] * s_att : -INFINITY;
-        const float mt = wave_max(sv);
-        const float m_new = fmaxf(m_run[hh], mt);
-        const float p = lane < nt ? __expf(sv - m_new) : 0.f;
-        const float lt = wave_sum(p);
-        alpha[hh] = __expf(m_run[hh] - m_new);
-        l_run[hh] = l_run[hh] * alpha[hh] + lt;
-        m_run[hh] = m_new;
-        Ps[wave * C::HPW + hh][lane] = p;
-      }
-      if (RLA) {  // w = phi(q_h) . phi(k_lane)
-        float wv[C::HPW];
-#pragma unroll
-        for (int hh = 0; hh < C::HPW; ++hh) wv[hh] = 0.f;
-        const float* prow = &PhiK[lane][0];
-#pragma unroll 4
-        for (int i = 0; i < D; i += 4) {
-          const float4 pk = *reinterpret_cast<const float4*>(prow + i);
-#pragma unroll
+    };
+    auto compute = [&](int32_t ts) __attribute__((always_inline)) {
+      const int32_t nt = min(kTile, t1 - ts);
+        // logits: lane = token of the tile
+        float sc[C::HPW];
+  #pragma unroll
+        for (int hh = 0; hh < C::HPW; ++hh) sc[hh] = 0.f;
+        const char* krow = Ks + lane * C::PITCH;
+  #pragma unroll 4
+        for (int pc = 0; pc < C::CPR; ++pc) {
+          const uint4 kv = *reinterpret_cast<const uint4*>(krow + pc * 16);
+  #pragma unroll
           for (int hh = 0; hh < C::HPW; ++hh) {
-            const float4 pq = *reinterpret_cast<const float4*>(&PhiQ[wave * C::HPW + hh][i]);
-            float a = wv[hh];
-            a = fmaf(pq.x, pk.x, a);
-            a = fmaf(pq.y, pk.y, a);
-            a = fmaf(pq.z, pk.z, a);
-            a = fmaf(pq.w, pk.w, a);
-            wv[hh] = a;
-          }
-        }
-#pragma unroll
-        for (int hh = 0; hh < C::HPW; ++hh) {
-          const float w = lane < nt ? wv[hh] : 0.f;
-          rden[hh] += wave_sum(w);
-          Ws[wave * C::HPW + hh][lane] = w;
-        }
-      }
-      __syncthreads();
-      // P.V: lane owns DPL consecutive dims of the wave's heads
-#pragma unroll
-      for (int hh = 0; hh < C::HPW; ++hh)
-#pragma unroll
-        for (int e = 0; e < C::DPL; ++e) acc[hh][e] *= alpha[hh];
-      for (int t = 0; t < kTile; t += 4) {
-        float4 pv[C::HPW], wv4[RLA ? C::HPW : 1];
-#pragma unroll
-        for (int hh = 0; hh < C::HPW; ++hh) {
-          pv[hh] = *reinterpret_cast<const float4*>(&Ps[wave * C::HPW + hh][t]);
-          if (RLA) wv4[hh] = *reinterpret_cast<const float4*>(&Ws[wave * C::HPW + hh][t]);
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float vv[C::DPL];
-          const char* vrow = Vs + (t + u) * C::PITCH;
-          if constexpr (sizeof(T) == 2) {
-            if constexpr (C::DPL == 2) {
-              const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + lane * 4);
-              vv[0] = __uint_as_float(w << 16);
-              vv[1] = __uint_as_float(w & 0xffff0000u);
+            const int h = wave * C::HPW + hh;
+            if constexpr (sizeof(T) == 2) {
+              const uint4 qv = *reinterpret_cast<const uint4*>(&Qs[h][pc * 8]);
+              float a = sc[hh];
+              a = dot2_bf16(kv.x, qv.x, a);
+              a = dot2_bf16(kv.y, qv.y, a);
+              a = dot2_bf16(kv.z, qv.z, a);
+              a = dot2_bf16(kv.w, qv.w, a);
+              sc[hh] = a;
             } else {
-              const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + lane * 2);
-              vv[0] = __uint_as_float((uint32_t)w << 16);
-            }
-          } else {
-#pragma unroll
-            for (int e = 0; e < C::DPL; ++e)
-              vv[e] = *reinterpret_cast<const float*>(vrow + (lane * C::DPL + e) * 4);
-          }
-#pragma unroll
-          for (int hh = 0; hh < C::HPW; ++hh) {
-            const float p = u == 0 ? pv[hh].x : (u == 1 ? pv[hh].y : (u == 2 ? pv[hh].z : pv[hh].w));
-#pragma unroll
-            for (int e = 0; e < C::DPL; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
-            if (RLA) {
-              const float w = u == 0 ? wv4[hh].x : (u == 1 ? wv4[hh].y : (u == 2 ? wv4[hh].z : wv4[hh].w));
-#pragma unroll
-              for (int e = 0; e < C::DPL; ++e) racc[hh][e] = fmaf(w, vv[e], racc[hh][e]);
+              const float4 qv = *reinterpret_cast<const float4*>(&Qs[h][pc * 4]);
+              float a = sc[hh];
+              a = fmaf(__uint_as_float(kv.x), qv.x, a);
+              a = fmaf(__uint_as_float(kv.y), qv.y, a);
+              a = fmaf(__uint_as_float(kv.z), qv.z, a);
+              a = fmaf(__uint_as_float(kv.w), qv.w, a);
+              sc[hh] = a;
             }
           }
         }
+        float alpha[C::HPW];
+  #pragma unroll
+        for (int hh = 0; hh < C::HPW; ++hh) {
+          const float sv = lane < nt ? sc[hh] * s_att : -INFINITY;
+          const float mt = wave_max(sv);
+          const float m_new = fmaxf(m_run[hh], mt);
+          const float p = lane < nt ? __expf(sv - m_new) : 0.f;
+          const float lt = wave_sum(p);
+          alpha[hh] = __expf(m_run[hh] - m_new);
+          l_run[hh] = l_run[hh] * alpha[hh] + lt;
+          m_run[hh] = m_new;
+          Ps[wave * C::HPW + hh][lane] = p;
+        }
+        if (RLA) {  // w = phi(q_h) . phi(k_lane)
+          float wv[C::HPW];
+  #pragma unroll
+          for (int hh = 0; hh < C::HPW; ++hh) wv[hh] = 0.f;
+          const float* prow = &PhiK[lane][0];
+  #pragma unroll 4
+          for (int i = 0; i < D; i += 4) {
+            const float4 pk = *reinterpret_cast<const float4*>(prow + i);
+  #pragma unroll
+            for (int hh = 0; hh < C::HPW; ++hh) {
+              const float4 pq = *reinterpret_cast<const float4*>(&PhiQ[wave * C::HPW + hh][i]);
+              float a = wv[hh];
+              a = fmaf(pq.x, pk.x, a);
+              a = fmaf(pq.y, pk.y, a);
+              a = fmaf(pq.z, pk.z, a);
+              a = fmaf(pq.w, pk.w, a);
+              wv[hh] = a;
+            }
+          }
+  #pragma unroll
+          for (int hh = 0; hh < C::HPW; ++hh) {
+            const float w = lane < nt ? wv[hh] : 0.f;
+            rden[hh] += wave_sum(w);
+            Ws[wave * C::HPW + hh][lane] = w;
+          }
+        }
+        __syncthreads();
+        // P.V: lane owns DPL consecutive dims of the wave's heads
+  #pragma unroll
+        for (int hh = 0; hh < C::HPW; ++hh)
+  #pragma unroll
+          for (int e = 0; e < C::DPL; ++e) acc[hh][e] *= alpha[hh];
+        for (int t = 0; t < kTile; t += 4) {
+          float4 pv[C::HPW], wv4[RLA ? C::HPW : 1];
+  #pragma unroll
+          for (int hh = 0; hh < C::HPW; ++hh) {
+            pv[hh] = *reinterpret_cast<const float4*>(&Ps[wave * C::HPW + hh][t]);
+            if (RLA) wv4[hh] = *reinterpret_cast<const float4*>(&Ws[wave * C::HPW + hh][t]);
+          }
+  #pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float vv[C::DPL];
+            const char* vrow = Vs + (t + u) * C::PITCH;
+            if constexpr (sizeof(T) == 2) {
+              if constexpr (C::DPL == 2) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(vrow + lane * 4);
+                vv[0] = __uint_as_float(w << 16);
+                vv[1] = __uint_as_float(w & 0xffff0000u);
+              } else {
+                const uint16_t w = *reinterpret_cast<const uint16_t*>(vrow + lane * 2);
+                vv[0] = __uint_as_float((uint32_t)w << 16);
+              }
+            } else {
+  #pragma unroll
+              for (int e = 0; e < C::DPL; ++e)
+                vv[e] = *reinterpret_cast<const float*>(vrow + (lane * C::DPL + e) * 4);
+            }
+  #pragma unroll
+            for (int hh = 0; hh < C::HPW; ++hh) {
+              const float p = u == 0 ? pv[hh].x : (u == 1 ? pv[hh].y : (u == 2 ? pv[hh].z : pv[hh].w));
+  #pragma unroll
+              for (int e = 0; e < C::DPL; ++e) acc[hh][e] = fmaf(p, vv[e], acc[hh][e]);
+              if (RLA) {
+                const float w = u == 0 ? wv4[hh].x : (u == 1 ? wv4[hh].y : (u == 2 ? wv4[hh].z : wv4[hh].w));
+  #pragma unroll
+                for (int e = 0; e < C::DPL; ++e) racc[hh][e] = fmaf(w, vv[e], racc[hh][e]);
+              }
+            }
+          }
+        }
+    };
+    if constexpr (C::LPT <= 8) {
+      kvv_t kA, vA, kB, vB;
+      int32_t ts = t0;
+      gather(t0, kA, vA);
+      gather(t0 + kTile, kB, vB);
+      for (; ts + kTile < t1; ts += 2 * kTile) {  // both tiles of the pair hold tokens
+        stage(kA, vA);
+        gather(ts + 2 * kTile, kA, vA);
+        compute(ts);
+        stage(kB, vB);
+        gather(ts + 3 * kTile, kB, vB);
+        compute(ts + kTile);
+      }
+      if (ts < t1) {  // an odd last tile
+        stage(kA, vA);
+        compute(ts);
+      }
+    } else {
+      kvv_t kA, vA;
+      gather(t0, kA, vA);
+      for (int32_t ts = t0; ts < t1; ts += kTile) {
+        stage(kA, vA);
+        if (ts + kTile < t1) gather(ts + kTile, kA, vA);
+        compute(ts);
       }
     }
     // partials of this chunk
@@ -566,6 +593,23 @@ k_rla_state(const T* __restrict__ k_pool, const T* __restrict__ v_pool,
   if (cg == 0) st[(int64_t)D * D + i] += zacc;
 }
 
+// Workgroups of a kernel instance resident per compute unit (registers and
+// LDS), from the runtime; cached per instance and device.
+int resident_per_cu(const void* fn, int threads) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  std::lock_guard<std::mutex> lk(mu);
+  const auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 1) n = 1;
+  cache[key] = n;
+  return n;
+}
+
 // Persistent grid of the split kernel: blocks resident on the chip.
 int split_grid(int nchunk_max, int rows, int per_cu) {
   int dev = 0, cus = 0;
@@ -596,20 +640,26 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
   float* part_rnum = part_o + align_up(n_part * D, 64);
   float* part_rden = part_rnum + align_up(n_part * D, 64);
   const int G = s.Hq / s.Hkv;
-  // few rows: the small row prefix frees LDS for four workgroups per CU
-  // (where registers allow: up to four heads per group without the tail)
+  // few rows: the small row prefix leaves more LDS per workgroup free; the
+  // persistent grid is as many workgroups as stay resident together
   const bool small = s.B * s.Hkv <= kSmallRowsLds;
-  const int gx = split_grid(nchunk_max, s.B * s.Hkv, small && G <= 4 && !RLA ? 4 : 3);
-  dim3 grid(gx);
+  int gx = 1;
 #define SA_DS(GG)                                                                              \
-  if (small)                                                                                   \
-    k_decode_split<T, D, GG, RLA, kSmallRowsLds><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(     \
-        (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,      \
-        count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden);              \
-  else                                                                                         \
-    k_decode_split<T, D, GG, RLA, kMaxRowsLds><<<grid, DecodeCfg<T, D, GG>::NT, 0, st>>>(       \
-        (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,      \
-        count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden)
+  {                                                                                            \
+    const void* fn = small ? (const void*)k_decode_split<T, D, GG, RLA, kSmallRowsLds>         \
+                           : (const void*)k_decode_split<T, D, GG, RLA, kMaxRowsLds>;          \
+    constexpr int NT = DecodeCfg<T, D, GG>::NT;                                                \
+    gx = split_grid(nchunk_max, s.B * s.Hkv, resident_per_cu(fn, NT));                         \
+    dim3 grid(gx);                                                                             \
+    if (small)                                                                                 \
+      k_decode_split<T, D, GG, RLA, kSmallRowsLds><<<grid, NT, 0, st>>>(                        \
+          (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,    \
+          count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden);            \
+    else                                                                                       \
+      k_decode_split<T, D, GG, RLA, kMaxRowsLds><<<grid, NT, 0, st>>>(                          \
+          (const T*)q, (const T*)k_pool, (const T*)v_pool, pg.page_table, pg.seq_lens, idx,    \
+          count, cap, s, s_att, nchunk_max, part_ml, part_o, part_rnum, part_rden);            \
+  }
   switch (G) {
     case 1: SA_DS(1); break;
     case 2: SA_DS(2); break;
@@ -636,6 +686,8 @@ hipError_t launch_decode(const Shape& s, const sa_pages& pg, const void* q, cons
                          int32_t cap, float s_att, void* out, sa_dtype out_dt, float* lse, void* ws,
                          const RlaArgs& rla, hipStream_t st) {
   if (s.B == 0) return hipSuccess;
+  // the kernels keep a listed token's pool row as page << 6 | slot in 32 bits
+  if (s.n_pool_pages >= ((int64_t)1 << 26)) return hipErrorNotSupported;
   if (dt == SA_BF16) {
     if (s.D == 128)
       return launch_t<bf16_raw, 128, RLA>(s, pg, q, k_pool, v_pool, idx, count, cap, s_att, out, out_dt, lse, ws, rla, st);
