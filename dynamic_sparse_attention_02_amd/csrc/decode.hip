@@ -51,10 +51,16 @@ __device__ __forceinline__ int32_t row_count(const int32_t* count, int row, int3
 }
 
 // Tiles per chunk from the total listed tiles (same result in every block).
-constexpr int kMaxTpc = 16;
+// At most 16 tiles per chunk (4 with the residual linear attention, whose
+// larger LDS footprint leaves no room for a longer row list); a chunk starts
+// with one dependent round trip for its rows, but longer chunks than this
+// balance the blocks worse.
+template <bool RLA>
+constexpr int max_tpc() { return RLA ? 4 : 16; }
+template <bool RLA>
 __device__ __forceinline__ int32_t plan_tpc(int64_t total_tiles, int32_t grid) {
   int64_t t = (total_tiles + 2 * (int64_t)grid - 1) / (2 * (int64_t)grid);
-  return t < 1 ? 1 : (t > kMaxTpc ? kMaxTpc : (int32_t)t);
+  return t < 1 ? 1 : (t > max_tpc<RLA>() ? max_tpc<RLA>() : (int32_t)t);
 }
 
 template <typename T, int D, int G>
@@ -95,7 +101,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   __shared__ __align__(16) float PhiQ[RLA ? G : 1][RLA ? D : 1];
   __shared__ __align__(16) float Ws[RLA ? G : 1][RLA ? kTile : 1];
   __shared__ int32_t prefix[RMAX + 1];
-  __shared__ uint32_t s_rid[kMaxTpc * kTile];  // pool rows of the item's listed tokens
+  __shared__ uint32_t s_rid[max_tpc<RLA>() * kTile];  // pool rows of the item's listed tokens
   __shared__ int64_t s_tiles;
   __shared__ int32_t s_red[4];
 
@@ -106,7 +112,7 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
   for (int r = tid; r < rows; r += C::NT) my_tiles += (row_count(count, r, cap) + kTile - 1) / kTile;
   atomicAdd((unsigned long long*)&s_tiles, (unsigned long long)my_tiles);
   __syncthreads();
-  const int32_t tpc = plan_tpc(s_tiles, gridDim.x);
+  const int32_t tpc = plan_tpc<RLA>(s_tiles, gridDim.x);
   const int32_t csize = kTile * tpc;
   // prefix[r] = items before row r (sequential scan by wave 0, rows <= RMAX)
   if (wave == 0) {
@@ -413,7 +419,7 @@ k_decode_combine(const float* __restrict__ part_ml, const float* __restrict__ pa
   for (int r = tid; r < rows; r += kCombThreads) my_tiles += (row_count(count, r, cap) + kTile - 1) / kTile;
   atomicAdd((unsigned long long*)&s_tiles, (unsigned long long)my_tiles);
   __syncthreads();
-  const int32_t csize = kTile * plan_tpc(s_tiles, split_grid);
+  const int32_t csize = kTile * plan_tpc<RLA>(s_tiles, split_grid);
   const int32_t n = row_count(count, row, cap);
   const int32_t nch = (n + csize - 1) / csize;
   const int64_t base = ((int64_t)b * s.Hq + h) * nchunk_max;
