@@ -48,7 +48,7 @@ def parse():
                     help="reuse one input replica every step (cache-warm)")
     ap.add_argument("--rla", action="store_true",
                     help="decode workloads: the step also forms the residual linear attention "
-                         "over the unselected tokens (sa_sparse_decode_rla; state built first)")
+                         "over the unselected tokens (sa_decode_step_rla; state built first)")
     ap.add_argument("--policy", default="indexer", choices=["indexer", "oracle"],
                     help="token-level decode workloads: take the support from the low-rank "
                          "indexer (default) or from the dense head-averaged attention mass "
@@ -274,7 +274,7 @@ def bench_decode(args, name):
             ops.sa_select_topp(shape, pages, x, sel["p"], n_sink, n_window, idx, count, ws_sel)
 
     # the whole-step call (token-level indexer or page-level Taylor scores)
-    use_step = not args.rla and not oracle_policy
+    use_step = not oracle_policy and not (args.rla and page_mode)
     if args.rla:  # state of every sequence's cache (maintenance, outside the timed steps)
         rla_state = torch.zeros((B, Hkv, d + 1, d), dtype=torch.float32, device=dev)
         ops.sa_rla_state(shape, pages, inp.k_pool, inp.v_pool, 0, rla_state)
@@ -284,15 +284,23 @@ def bench_decode(args, name):
         state_bytes = rla_state.numel() * 4
     if use_step:
         ws_step = ops.alloc_workspace(ops.workspace_size(
-            L.SA_OP_DECODE_STEP_PAGES if page_mode else L.SA_OP_DECODE_STEP, shape, cap))
+            L.SA_OP_DECODE_STEP_PAGES if page_mode else
+            (L.SA_OP_DECODE_STEP_RLA if args.rla else L.SA_OP_DECODE_STEP), shape, cap))
     fused = use_step and rows <= 16 and inp.G >= 4
     if page_mode:
         fused = fused and k_pages <= 32 and inp.dtype == torch.bfloat16
+    if args.rla:
+        fused = fused and inp.dtype == torch.bfloat16
 
     def run_step(rep):
         if use_step and page_mode:
             ops.sa_decode_step_pages(shape, pages, inp.q, rep[0], rep[1], rep[2], inp.s_att,
                                      k_pages, x, idx, count, out, lse, ws_step)
+            return
+        if use_step and args.rla:
+            ops.sa_decode_step_rla(shape, pages, inp.q, inp.w_q, rep[0], rep[1], rep[2],
+                                   inp.s_idx, inp.s_att, sel.get("p", 0.0), 0, n_sink, n_window,
+                                   x, idx, count, out, lse, rla_state, rla_num, rla_den, ws_step)
             return
         if use_step:
             ops.sa_decode_step(shape, pages, inp.q, inp.w_q, rep[0], rep[1], rep[2], inp.s_idx,
@@ -330,10 +338,14 @@ def bench_decode(args, name):
     # the graph replays must reproduce an eager step bit for bit
     torch.cuda.synchronize()
     g_out, g_idx, g_cnt = out.clone(), idx.clone(), count.clone()
+    g_rla = (rla_num.clone(), rla_den.clone()) if args.rla else None
     run_step(reps[R - 1])
     torch.cuda.synchronize()
     assert torch.equal(g_cnt, count) and torch.equal(g_idx, idx) and torch.equal(g_out, out), \
         "graph replay differs from the eager step"
+    if args.rla:
+        assert torch.equal(g_rla[0], rla_num) and torch.equal(g_rla[1], rla_den), \
+            "graph replay differs from the eager step (residual terms)"
     # per-component times (same rotation), for the breakdown and the roofline
     if page_mode:
         t_index = time_loop(lambda i: ops.sa_page_scores(shape, pages, inp.q, reps[i][0],
@@ -393,7 +405,8 @@ def bench_decode(args, name):
         "index_bytes": index_bytes,
         "kv_bytes": kv_bytes,
         "budget_fraction": round(float(counts.sum()) / float(sum(inp.seq_lens) * Hkv), 5),
-        "step_call": (("sa_decode_step_pages" if page_mode else "sa_decode_step") +
+        "step_call": (("sa_decode_step_pages" if page_mode else
+                       ("sa_decode_step_rla" if args.rla else "sa_decode_step")) +
                       (" (fused)" if fused else "")) if use_step else
                      ((("sa_page_scores + sa_select_topk") if page_mode else
                        ("sa_attention_mass" if oracle_policy else "sa_index_scores") +

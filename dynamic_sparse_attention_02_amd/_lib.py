@@ -35,6 +35,7 @@ SA_OP_PBS_IMPORTANCE = 8
 SA_OP_PBS_SELECT = 9
 SA_OP_PREFILL_ORACLE = 10
 SA_OP_DECODE_STEP_PAGES = 11
+SA_OP_DECODE_STEP_RLA = 12
 
 
 class SaShape(ctypes.Structure):
@@ -83,6 +84,9 @@ SIGNATURES = {
     "sa_decode_step": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F, _F, _I32,
                                       _I32, _I32, _P, _I64, _P, _P, _I32, _P, ctypes.c_int, _P, _P,
                                       _SZ, _P]),
+    "sa_decode_step_rla": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F, _F,
+                                          _I32, _I32, _I32, _P, _I64, _P, _P, _I32, _P,
+                                          ctypes.c_int, _P, _P, _P, _P, _P, _SZ, _P]),
     "sa_decode_step_noalloc": (ctypes.c_int, [_SH, _PG, _P, _P, _P, _P, _P, ctypes.c_int, _F, _F,
                                               _F, _I32, _I32, _I32, _P, _I64, _P, _P, _I32, _P,
                                               ctypes.c_int, _P, _P]),

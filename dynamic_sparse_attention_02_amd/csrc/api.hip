@@ -136,6 +136,20 @@ size_t step_ws(const sa_shape* s, int64_t cap) {
   return index_ws(s) + select_ws(s, s->max_len) + decode_ws(s, cap) + fused_region(s);
 }
 
+// The residual linear attention's sums in a decode step, after step_ws:
+// room for either path's (per chunk, or per row, workgroup and head).
+size_t step_rla_ws(const sa_shape* s, int64_t cap) {
+  if (cap < 1) cap = 1;
+  const sa::Shape sh = to_shape(s);
+  size_t b = sa::decode_rla_part_bytes(sh, (int32_t)cap);
+  if (fused_region(s)) {
+    const size_t f = sa::fused_rla_bytes(s->batch * s->n_kv_heads, 256, s->n_q_heads / s->n_kv_heads,
+                                         s->head_dim);
+    if (f > b) b = f;
+  }
+  return sa::align_up(b, 256);
+}
+
 // Page-level step workspace: select | decode | fused step.
 size_t step_pages_ws(const sa_shape* s, int64_t cap) {
   const int64_t n_cand = (s->max_len + s->page_size - 1) / s->page_size;
@@ -184,6 +198,8 @@ size_t sa_workspace_size(sa_op op, const sa_shape* s, int64_t param) {
       return step_ws(s, param);
     case SA_OP_DECODE_STEP_PAGES:
       return step_pages_ws(s, param);
+    case SA_OP_DECODE_STEP_RLA:
+      return step_ws(s, param) + step_rla_ws(s, param);
     case SA_OP_SPARSE_DECODE_RLA:
       return decode_ws(s, param, true);
     case SA_OP_ATTENTION_MASS:
@@ -361,7 +377,7 @@ sa_status sa_sparse_decode_rla(const sa_shape* s, const sa_pages* pg, const void
   SA_TRY(check_ws(ws, ws_bytes, decode_ws(s, cap, true), fn));
   return hip_status(sa::launch_sparse_decode_rla(to_shape(s), *pg, q, k_pool, v_pool, dt, idx,
                                                  count, cap, s_att, out, out_dt, lse, rla_state,
-                                                 rla_num, rla_den, ws, st), fn);
+                                                 rla_num, rla_den, ws, nullptr, st), fn);
 }
 
 sa_status sa_rla_state(const sa_shape* s, const sa_pages* pg, const void* k_pool,
@@ -466,11 +482,14 @@ sa_status decode_step_impl(const char* fn, const sa_shape* s, const sa_pages* pg
                            const void* v_pool, sa_dtype dt, float s_idx, float s_att, float p,
                            int32_t top_k, int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
                            int32_t* idx, int32_t* count, int32_t cap, void* out, sa_dtype out_dt,
-                           float* lse, void* ws, size_t ws_bytes, bool use_scratch, hipStream_t st) {
+                           float* lse, void* ws, size_t ws_bytes, bool use_scratch,
+                           const float* rla_state, float* rla_num, float* rla_den, hipStream_t st) {
+  const bool rla = rla_state != nullptr;
   SA_TRY(check_shape(s, fn));
   SA_TRY(check_pages(pg, true, fn));
   if (!valid_dtype(dt) || !valid_dtype(out_dt)) return fail(SA_ERR_INVALID_ARGUMENT, "%s: bad dtype", fn);
-  if (!q || !w_q || !kidx_pool || !k_pool || !v_pool || !x || !idx || !count || !out)
+  if (!q || !w_q || !kidx_pool || !k_pool || !v_pool || !x || !idx || !count || !out ||
+      (rla && (!rla_num || !rla_den)))
     return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
   if (ldx < s->max_len) return fail(SA_ERR_INVALID_ARGUMENT, "%s: ldx < max_len", fn);
   if (top_k < 0) return fail(SA_ERR_INVALID_ARGUMENT, "%s: top_k=%d < 0", fn, top_k);
@@ -498,15 +517,18 @@ sa_status decode_step_impl(const char* fn, const sa_shape* s, const sa_pages* pg
     ws = sc + zb;
     ws_bytes = kScratchBytes - zb;
   }
-  SA_TRY(check_ws(ws, ws_bytes, step_ws(s, cap), fn));
+  SA_TRY(check_ws(ws, ws_bytes, step_ws(s, cap) + (rla ? step_rla_ws(s, cap) : 0), fn));
   char* base = (char*)ws;
+  char* rla_part = base + step_ws(s, cap);
   const sa::Shape sh = to_shape(s);
   int32_t nb = 0, tpb = 0;
-  if (sa::fused_plan(sh, n_sink, n_window, dt, 0, &nb, &tpb))
+  if ((!rla || dt == SA_BF16) && sa::fused_plan(sh, n_sink, n_window, dt, rla ? 3 : 0, &nb, &tpb)) {
+    const sa::FusedRla fr{rla_state, rla_num, rla_den, rla_part};
     return hip_status(sa::launch_decode_fused(sh, *pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
                                               s_att, p, top_k, n_sink, n_window, x, ldx, idx, count,
                                               cap, out, out_dt, lse, base + w_i + w_s + w_d, zero, nb,
-                                              tpb, st), fn);
+                                              tpb, rla ? &fr : nullptr, st), fn);
+  }
   hipError_t e = sa::launch_index_scores(sh, *pg, q, w_q, kidx_pool, dt, s_idx, x, ldx, (float*)base, st);
   if (e != hipSuccess) return hip_status(e, fn);
   sa::SelectArgs a{};
@@ -529,8 +551,13 @@ sa_status decode_step_impl(const char* fn, const sa_shape* s, const sa_pages* pg
   a.fused_zero = zero;
   e = sa::launch_select(a, base + w_i, st);
   if (e != hipSuccess) return hip_status(e, fn);
-  e = sa::launch_sparse_decode(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
-                               lse, base + w_i + w_s, st);
+  if (rla)
+    e = sa::launch_sparse_decode_rla(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out,
+                                     out_dt, lse, rla_state, rla_num, rla_den, base + w_i + w_s,
+                                     rla_part, st);
+  else
+    e = sa::launch_sparse_decode(sh, *pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out,
+                                 out_dt, lse, base + w_i + w_s, st);
   return hip_status(e, fn);
 }
 
@@ -546,7 +573,21 @@ sa_status sa_decode_step(const sa_shape* s, const sa_pages* pg, const void* q, c
                          void* ws, size_t ws_bytes, hipStream_t st) {
   return decode_step_impl("sa_decode_step", s, pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx,
                           s_att, p, top_k, n_sink, n_window, x, ldx, idx, count, cap, out, out_dt,
-                          lse, ws, ws_bytes, false, st);
+                          lse, ws, ws_bytes, false, nullptr, nullptr, nullptr, st);
+}
+
+sa_status sa_decode_step_rla(const sa_shape* s, const sa_pages* pg, const void* q,
+                             const void* w_q, const void* kidx_pool, const void* k_pool,
+                             const void* v_pool, sa_dtype dt, float s_idx, float s_att, float p,
+                             int32_t top_k, int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
+                             int32_t* idx, int32_t* count, int32_t cap, void* out, sa_dtype out_dt,
+                             float* lse, const float* rla_state, float* rla_num, float* rla_den,
+                             void* ws, size_t ws_bytes, hipStream_t st) {
+  const char* fn = "sa_decode_step_rla";
+  if (!rla_state) return fail(SA_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+  return decode_step_impl(fn, s, pg, q, w_q, kidx_pool, k_pool, v_pool, dt, s_idx, s_att, p,
+                          top_k, n_sink, n_window, x, ldx, idx, count, cap, out, out_dt, lse, ws,
+                          ws_bytes, false, rla_state, rla_num, rla_den, st);
 }
 
 sa_status sa_decode_step_noalloc(const sa_shape* s, const sa_pages* pg, const void* q,
@@ -557,7 +598,7 @@ sa_status sa_decode_step_noalloc(const sa_shape* s, const sa_pages* pg, const vo
                                  sa_dtype out_dt, float* lse, hipStream_t st) {
   return decode_step_impl("sa_decode_step_noalloc", s, pg, q, w_q, kidx_pool, k_pool, v_pool, dt,
                           s_idx, s_att, p, top_k, n_sink, n_window, x, ldx, idx, count, cap, out,
-                          out_dt, lse, nullptr, 0, true, st);
+                          out_dt, lse, nullptr, 0, true, nullptr, nullptr, nullptr, st);
 }
 
 sa_status sa_decode_step_pages(const sa_shape* s, const sa_pages* pg, const void* q,

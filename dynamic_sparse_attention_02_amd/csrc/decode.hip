@@ -632,6 +632,7 @@ struct RlaArgs {
   const float* state;  // [B][Hkv][D + 1][D]
   float* num;          // [B][Hq][D]
   float* den;          // [B][Hq]
+  void* part;          // per-chunk sums, or NULL: after the other partials
 };
 
 template <typename T, int D, bool RLA>
@@ -643,7 +644,7 @@ hipError_t launch_t(const Shape& s, const sa_pages& pg, const void* q, const voi
   const size_t n_part = (size_t)s.B * s.Hq * nchunk_max;
   float* part_ml = (float*)ws;
   float* part_o = part_ml + align_up(n_part * 2, 64);
-  float* part_rnum = part_o + align_up(n_part * D, 64);
+  float* part_rnum = rla.part ? (float*)rla.part : part_o + align_up(n_part * D, 64);
   float* part_rden = part_rnum + align_up(n_part * D, 64);
   const int G = s.Hq / s.Hkv;
   // few rows: the small row prefix leaves more LDS per workgroup free; the
@@ -706,11 +707,15 @@ hipError_t launch_decode(const Shape& s, const sa_pages& pg, const void* q, cons
 
 }  // namespace
 
+size_t decode_rla_part_bytes(const Shape& s, int32_t cap) {
+  const size_t n_part = (size_t)s.B * s.Hq * (size_t)((cap + kTile - 1) / kTile);
+  return (align_up(n_part * s.D, 64) + align_up(n_part, 64)) * sizeof(float);
+}
+
 size_t decode_workspace_bytes(const Shape& s, int32_t cap, bool rla) {
   const size_t n_part = (size_t)s.B * s.Hq * (size_t)((cap + kTile - 1) / kTile);
-  size_t n = align_up(n_part * 2, 64) + align_up(n_part * s.D, 64);
-  if (rla) n += align_up(n_part * s.D, 64) + align_up(n_part, 64);
-  return n * sizeof(float);
+  const size_t n = align_up(n_part * 2, 64) + align_up(n_part * s.D, 64);
+  return n * sizeof(float) + (rla ? decode_rla_part_bytes(s, cap) : 0);
 }
 
 hipError_t launch_sparse_decode(const Shape& s, const sa_pages& pg, const void* q,
@@ -719,7 +724,7 @@ hipError_t launch_sparse_decode(const Shape& s, const sa_pages& pg, const void* 
                                 float s_att, void* out, sa_dtype out_dt, float* lse,
                                 void* ws, hipStream_t st) {
   return launch_decode<false>(s, pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
-                              lse, ws, RlaArgs{nullptr, nullptr, nullptr}, st);
+                              lse, ws, RlaArgs{nullptr, nullptr, nullptr, nullptr}, st);
 }
 
 hipError_t launch_sparse_decode_rla(const Shape& s, const sa_pages& pg, const void* q,
@@ -727,9 +732,9 @@ hipError_t launch_sparse_decode_rla(const Shape& s, const sa_pages& pg, const vo
                                     const int32_t* idx, const int32_t* count, int32_t cap,
                                     float s_att, void* out, sa_dtype out_dt, float* lse,
                                     const float* rla_state, float* rla_num, float* rla_den,
-                                    void* ws, hipStream_t st) {
+                                    void* ws, void* rla_part, hipStream_t st) {
   return launch_decode<true>(s, pg, q, k_pool, v_pool, dt, idx, count, cap, s_att, out, out_dt,
-                             lse, ws, RlaArgs{rla_state, rla_num, rla_den}, st);
+                             lse, ws, RlaArgs{rla_state, rla_num, rla_den, rla_part}, st);
 }
 
 hipError_t launch_rla_state(const Shape& s, const sa_pages& pg, const void* k_pool,

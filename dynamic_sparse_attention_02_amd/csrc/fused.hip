@@ -96,6 +96,14 @@ struct FusedArgs {
   uint32_t* blk_eq;       // [rows][nb] threshold ties of each workgroup
   float* part_ml;         // [rows][nb][G][2]
   float* part_o;          // [rows][nb][G][D]
+  // residual linear attention over the tokens left out (token mode, bf16):
+  // state [B][Hkv][D + 1][D] (S rows, then z), outputs [B][Hq][D] and [B][Hq],
+  // per-workgroup sums over the own listed tokens
+  const float* rla_state;
+  float* rla_num;
+  float* rla_den;
+  float* part_rnum;       // [rows][nb][G][D]
+  float* part_rden;       // [rows][nb][G]
   uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
   uint64_t* mflag;        // [rows][kMaxNB] marker bit 32 | own maximum score key
   int32_t* plist;         // page mode: [rows][nb][kFusedMaxPages][2] own pages (sequence, pool)
@@ -213,7 +221,7 @@ __device__ __forceinline__ U blk_scan(U v, U* lds, U& total) {  // exclusive, kN
 // PAGES: the candidates are the sequence's pages, scored by the Taylor page
 // score; the top-k pages' tokens are attended and listed.  SEL: selection
 // only, over scores given in x (no attention, no outputs).
-template <typename T, int D, int G, int TPT, bool PAGES, bool SEL>
+template <typename T, int D, int G, int TPT, bool PAGES, bool SEL, bool RLA = false>
 __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   constexpr int HPW = G / 4 > 0 ? G / 4 : 1;   // heads per wave (G >= 4)
   constexpr int DPL = D / 64;
@@ -240,8 +248,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   __shared__ float red_f[4][kRank];
   __shared__ uint32_t red_u[4];
   __shared__ uint64_t red_u64[4];
-  __shared__ uint32_t hcnt_l[kBinsF];
-  __shared__ uint64_t hmass_l[kBinsF];
+  __shared__ __align__(16) uint32_t hcnt_l[kBinsF];
+  __shared__ __align__(16) uint64_t hmass_l[kBinsF];
   __shared__ __align__(16) char Ks[kTileF * PITCH];
   __shared__ __align__(16) char Vs[kTileF * PITCH];
   __shared__ __align__(16) T Qs[G][D];
@@ -877,6 +885,36 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
+    // Residual linear attention over the tokens left out ("SPLA", section
+    // 2.2, subtraction form), with RLA: this workgroup's sums over its own
+    // listed tokens, num_h = sum_j w_hj v_j and den_h = sum_j w_hj, where
+    // w_hj = phi(q_h) . phi(k_j) and phi = exp elementwise, on the matrix
+    // cores beside the attention: W^T = phi(K) phi(Q)^T takes the A operand's
+    // key registers of S^T (exponentiated) and phi(Q) in place of Q, each
+    // fp32 factor split into a bf16 high part and the bf16 rounding of the
+    // remainder (three products: hi.hi, hi.lo, lo.hi; the dropped lo.lo term
+    // and the roundings stay below 2^-16 of each product); W^T has the lane
+    // layout of P^T, so num^T += V^T W^T reuses the V^T operand, again with
+    // W split into high and low parts.
+    typedef __attribute__((ext_vector_type(8))) float f32x8_t;
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+    typedef __attribute__((ext_vector_type(4))) float f32x4v_t;
+    bf16x8_t qH[RLA ? KS : 1], qL[RLA ? KS : 1];
+    f32x4_t racc[RLA ? MB : 1];
+    float rden = 0.f;  // lane (head hq): its tokens' weights
+    if constexpr (RLA) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        f32x8_t f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          f[e] = hq < G ? __expf(bf16_to_f32(Qs[hq < G ? hq : 0][32 * ks + 8 * lg + e])) : 0.f;
+        qH[ks] = __builtin_convertvector(f, bf16x8_t);
+        qL[ks] = __builtin_convertvector(f - __builtin_convertvector(qH[ks], f32x8_t), bf16x8_t);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) racc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
     // K and V rows: 16 lanes per row (contiguous loads), staged row-major;
     // the V^T operand is gathered from four rows by 2-byte LDS reads.  Tiles
     // go in pairs through two register buffers: while a tile is computed the
@@ -916,11 +954,23 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     auto compute = [&](int32_t ts) __attribute__((always_inline)) {
       const int32_t nt = min(kTileF, n_att - ts);
       f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      f32x4_t W = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const uint4 kv = *reinterpret_cast<const uint4*>(krow + 64 * ks);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qB[ks], S, 0, 0, 0);
+        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kv);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qB[ks], S, 0, 0, 0);
+        if constexpr (RLA) {
+          f32x8_t f = __builtin_convertvector(kb, f32x8_t);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = __expf(f[e]);
+          const bf16x8_t kh = __builtin_convertvector(f, bf16x8_t);
+          const bf16x8_t kl = __builtin_convertvector(f - __builtin_convertvector(kh, f32x8_t), bf16x8_t);
+          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qH[ks], W, 0, 0, 0);
+          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qL[ks], W, 0, 0, 0);
+          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qH[ks], W, 0, 0, 0);
+        }
       }
       float sv[4], mt = -INFINITY;
 #pragma unroll
@@ -952,6 +1002,19 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
       const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(hi[0], hi[1]));
       const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(lo[0], lo[1]));
+      s16x4_t wh = s16x4_t{0, 0, 0, 0}, wl = s16x4_t{0, 0, 0, 0};
+      if constexpr (RLA) {  // tokens past the list weigh nothing
+        f32x4v_t wv;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          wv[v] = 16 * wave + 4 * lg + v < nt ? W[v] : 0.f;
+          rden += wv[v];
+        }
+        const bf16x4_t bh = __builtin_convertvector(wv, bf16x4_t);
+        const bf16x4_t bl = __builtin_convertvector(wv - __builtin_convertvector(bh, f32x4v_t), bf16x4_t);
+        wh = __builtin_bit_cast(s16x4_t, bh);
+        wl = __builtin_bit_cast(s16x4_t, bl);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         oacc[mb] *= alpha;
@@ -963,6 +1026,10 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         const s16x4_t av = __builtin_bit_cast(s16x4_t, make_uint2(v0 | (v1 << 16), v2 | (v3 << 16)));
         oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
         oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
+        if constexpr (RLA) {
+          racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wh, racc[mb], 0, 0, 0);
+          racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wl, racc[mb], 0, 0, 0);
+        }
       }
     };
     int32_t ts = 0;
@@ -997,6 +1064,22 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       s_wm[wave][lane] = m_run;
       s_wl[wave][lane] = lw;
     }
+    // the residual sums of the four waves: numerators in the histogram
+    // masses' LDS (free by now), denominators summed over the lane rows
+    __shared__ float s_rd[4][16];
+    float* rbuf = reinterpret_cast<float*>(hmass_l);
+    if constexpr (RLA) {
+      static_assert(4 * D * 16 * 4 <= (int)sizeof(hmass_l), "four waves' residual sums fit");
+      float* rb = rbuf + wave * D * 16;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) rb[(16 * mb + 4 * lg + v) * 16 + hq] = racc[mb][v];
+      float rd = rden;
+      rd += __shfl_xor(rd, 16, 64);
+      rd += __shfl_xor(rd, 32, 64);
+      if (lane < 16) s_rd[wave][lane] = rd;
+    }
     __syncthreads();
     for (int e = tid; e < G * D; e += kNT) {
       const int hl = e / D, d = e % D;
@@ -1016,6 +1099,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       if (d == 0) {
         st_dev(&a.part_ml[pi * 2], M);
         st_dev(&a.part_ml[pi * 2 + 1], lsum);
+      }
+      if constexpr (RLA) {
+        float rn = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) rn += rbuf[w * D * 16 + d * 16 + hl];
+        st_dev(&a.part_rnum[pi * D + d], rn);
+        if (d == 0) st_dev(&a.part_rden[pi], (s_rd[0][hl] + s_rd[1][hl]) + (s_rd[2][hl] + s_rd[3][hl]));
       }
     }
     } else {
@@ -1207,6 +1297,20 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
           po[t] = ld_dev(&a.part_o[pi * D + d]);
         }
       }
+      // residual linear attention (subtraction form): phi(q_h) . S[:, d]
+      // over the state rows sub, sub + 16, ... minus the workgroups' sums
+      constexpr int KR = D / 16;
+      float pr[KP], sv[KR];
+      if constexpr (RLA) {
+        const float* st = a.rla_state + (int64_t)row * (D + 1) * D;
+#pragma unroll
+        for (int t = 0; t < KP; ++t) {
+          const int k = sub + 16 * t;
+          pr[t] = k < NB ? ld_dev(&a.part_rnum[(((int64_t)row * NB + k) * G + hl) * D + d]) : 0.f;
+        }
+#pragma unroll
+        for (int t = 0; t < KR; ++t) sv[t] = st[(int64_t)(sub + 16 * t) * D + d];
+      }
       float M2 = -INFINITY;
 #pragma unroll
       for (int t = 0; t < KP; ++t) M2 = fmaxf(M2, pm[t]);
@@ -1227,6 +1331,31 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         if (a.out_bf16) ((bf16_raw*)a.out)[((int64_t)b * s.Hq + h) * D + d] = f32_to_bf16(v);
         else ((float*)a.out)[((int64_t)b * s.Hq + h) * D + d] = v;
         if (d == 0 && a.lse) a.lse[(int64_t)b * s.Hq + h] = lsum > 0.f ? M2 + logf(lsum) : -INFINITY;
+      }
+      if constexpr (RLA) {
+        const int h = g * G + hl;
+        float lin = 0.f, sel = 0.f;
+#pragma unroll
+        for (int t = 0; t < KR; ++t) lin = fmaf(__expf(to_f32<T>(Qs[hl][sub + 16 * t])), sv[t], lin);
+#pragma unroll
+        for (int t = 0; t < KP; ++t) sel += pr[t];
+        lin = row16_sum(lin);
+        sel = row16_sum(sel);
+        if (sub == 0) a.rla_num[((int64_t)b * s.Hq + h) * D + d] = lin - sel;
+        if (d == 0) {  // the denominator: phi(q_h) . z (state row D) minus the sums
+          const float* z = a.rla_state + ((int64_t)row * (D + 1) + D) * D;
+          float lz = 0.f, sz = 0.f;
+#pragma unroll
+          for (int t = 0; t < KR; ++t) lz = fmaf(__expf(to_f32<T>(Qs[hl][sub + 16 * t])), z[sub + 16 * t], lz);
+#pragma unroll
+          for (int t = 0; t < KP; ++t) {
+            const int k = sub + 16 * t;
+            if (k < NB) sz += ld_dev(&a.part_rden[((int64_t)row * NB + k) * G + hl]);
+          }
+          lz = row16_sum(lz);
+          sz = row16_sum(sz);
+          if (sub == 0) a.rla_den[(int64_t)b * s.Hq + h] = lz - sz;
+        }
       }
     }
     }
@@ -1349,32 +1478,38 @@ size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   return fused_zero_bytes(rows) + fused_data_bytes(rows, nb, G, D);
 }
 
+size_t fused_rla_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
+  return align_up(sizeof(float) * rows * nb * G * D, 256) + align_up(sizeof(float) * rows * nb * G, 256);
+}
+
 namespace {
 
 // The kernel instance a plan launches (mode 0: token step, 1: page step,
-// 2: selection only).
-template <typename T, int D, int G, bool PAGES, bool SEL>
+// 2: selection only, 3: token step with the residual linear attention).
+template <typename T, int D, int G, bool PAGES, bool SEL, bool RLA = false>
 const void* fused_instance(int tpt) {
   switch (tpt) {
-    case 1: return (const void*)k_decode_fused<T, D, G, 1, PAGES, SEL>;
-    case 2: return (const void*)k_decode_fused<T, D, G, 2, PAGES, SEL>;
-    case 4: return (const void*)k_decode_fused<T, D, G, 4, PAGES, SEL>;
-    case 8: return (const void*)k_decode_fused<T, D, G, 8, PAGES, SEL>;
-    default: return (const void*)k_decode_fused<T, D, G, 16, PAGES, SEL>;
+    case 1: return (const void*)k_decode_fused<T, D, G, 1, PAGES, SEL, RLA>;
+    case 2: return (const void*)k_decode_fused<T, D, G, 2, PAGES, SEL, RLA>;
+    case 4: return (const void*)k_decode_fused<T, D, G, 4, PAGES, SEL, RLA>;
+    case 8: return (const void*)k_decode_fused<T, D, G, 8, PAGES, SEL, RLA>;
+    default: return (const void*)k_decode_fused<T, D, G, 16, PAGES, SEL, RLA>;
   }
 }
 
-template <typename T, int D, bool PAGES>
+template <typename T, int D, bool PAGES, bool RLA = false>
 const void* fused_instance_g(int G, int tpt) {
   switch (G) {
-    case 4: return fused_instance<T, D, 4, PAGES, false>(tpt);
-    case 8: return fused_instance<T, D, 8, PAGES, false>(tpt);
-    default: return fused_instance<T, D, 16, PAGES, false>(tpt);
+    case 4: return fused_instance<T, D, 4, PAGES, false, RLA>(tpt);
+    case 8: return fused_instance<T, D, 8, PAGES, false, RLA>(tpt);
+    default: return fused_instance<T, D, 16, PAGES, false, RLA>(tpt);
   }
 }
 
 const void* fused_kernel_for(sa_dtype dt, int D, int G, int tpt, int mode) {
   if (mode == 2) return fused_instance<float, 64, 4, false, true>(tpt);
+  if (mode == 3) return D == 128 ? fused_instance_g<bf16_raw, 128, false, true>(G, tpt)
+                                 : fused_instance_g<bf16_raw, 64, false, true>(G, tpt);
   if (mode == 1) return D == 128 ? fused_instance_g<bf16_raw, 128, true>(G, tpt)
                                  : fused_instance_g<bf16_raw, 64, true>(G, tpt);
   if (dt == SA_BF16) return D == 128 ? fused_instance_g<bf16_raw, 128, false>(G, tpt)
@@ -1558,9 +1693,11 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
                                int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
                                int32_t* idx, int32_t* count, int32_t cap, void* out,
                                sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
-                               int32_t tpb, hipStream_t st) {
+                               int32_t tpb, const FusedRla* rla, hipStream_t st) {
   const int rows = s.B * s.Hkv;
   const int G = s.Hq / s.Hkv;
+  // the residual linear attention rides on the matrix-core attention (bf16)
+  if (rla && dt != SA_BF16) return hipErrorNotSupported;
   FusedArgs a{};
   a.q = q; a.w_q = w_q; a.kidx = kidx_pool; a.k_pool = k_pool; a.v_pool = v_pool;
   a.page_table = pg.page_table; a.seq_lens = pg.seq_lens; a.s = s;
@@ -1568,9 +1705,20 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
   a.n_window = n_window; a.x = x; a.ldx = ldx; a.idx = idx; a.count = count; a.cap = cap;
   a.out = out; a.out_bf16 = out_dt == SA_BF16; a.lse = lse; a.nb = nb; a.tpb = tpb;
   fused_ws(a, ws, zero, rows, nb, G, s.D);
+  if (rla) {
+    a.rla_state = rla->state;
+    a.rla_num = rla->num;
+    a.rla_den = rla->den;
+    a.part_rnum = (float*)rla->part;
+    a.part_rden = (float*)((char*)rla->part + align_up(sizeof(float) * rows * nb * G * s.D, 256));
+  }
   const int tpt = tpb / kNT;  // 1, 2, 4, 8 or 16 (fused_plan)
   dim3 grid(rows * nb);
-#define SA_FZ(TT, DD, GG, PP) k_decode_fused<TT, DD, GG, PP, false, false><<<grid, kNT, 0, st>>>(a)
+#define SA_FZ(TT, DD, GG, PP)                                                         \
+  do {                                                                                \
+    if (rla) k_decode_fused<bf16_raw, DD, GG, PP, false, false, true><<<grid, kNT, 0, st>>>(a); \
+    else k_decode_fused<TT, DD, GG, PP, false, false><<<grid, kNT, 0, st>>>(a);      \
+  } while (0)
 #define SA_FZ_T(TT, DD, GG)              \
   switch (tpt) {                         \
     case 1: SA_FZ(TT, DD, GG, 1); break;  \
@@ -1587,7 +1735,7 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
   }
   if (dt == SA_BF16) {
     if (s.D == 128) { SA_FZ_G(bf16_raw, 128); } else { SA_FZ_G(bf16_raw, 64); }
-  } else {
+  } else {  // (no residual terms: checked above)
     if (s.D == 128) { SA_FZ_G(float, 128); } else { SA_FZ_G(float, 64); }
   }
 #undef SA_FZ_G

@@ -364,12 +364,17 @@ size_t select_workspace_bytes(int32_t rows, int32_t max_cand);
 hipError_t launch_select(const SelectArgs& a, void* ws, hipStream_t st);
 
 size_t decode_workspace_bytes(const Shape& s, int32_t cap, bool rla = false);
+// the residual linear attention's per-chunk sums, the part of
+// decode_workspace_bytes(rla = true) beyond decode_workspace_bytes(rla = false)
+size_t decode_rla_part_bytes(const Shape& s, int32_t cap);
+// rla_part: where the per-chunk sums go, or NULL for their place after the
+// other partials in ws
 hipError_t launch_sparse_decode_rla(const Shape& s, const sa_pages& pg, const void* q,
                                     const void* k_pool, const void* v_pool, sa_dtype dt,
                                     const int32_t* idx, const int32_t* count, int32_t cap,
                                     float s_att, void* out, sa_dtype out_dt, float* lse,
                                     const float* rla_state, float* rla_num, float* rla_den,
-                                    void* ws, hipStream_t st);
+                                    void* ws, void* rla_part, hipStream_t st);
 hipError_t launch_rla_state(const Shape& s, const sa_pages& pg, const void* k_pool,
                             const void* v_pool, sa_dtype dt, int32_t first, float* state,
                             hipStream_t st);
@@ -400,7 +405,18 @@ hipError_t launch_sparse_prefill(const Shape& s, const sa_pages& pg, int32_t n_t
 
 constexpr int kFusedMaxRows = 16;  // rows a persistent launch serves at most
 size_t fused_workspace_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D);
+// the persistent step's residual linear attention sums (per row, workgroup
+// and head), a region of their own
+size_t fused_rla_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D);
+struct FusedRla {
+  const float* state;  // [B][Hkv][D + 1][D]
+  float* num;          // [B][Hq][D]
+  float* den;          // [B][Hq]
+  void* part;          // fused_rla_bytes
+};
 size_t fused_zero_bytes(int32_t rows_cap);
+// mode 0: token step, 1: page step, 2: selection only, 3: token step with
+// the residual linear attention (bf16)
 bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, int mode,
                 int32_t* nb, int32_t* tpb);
 bool fused_plan_pages(const Shape& s, int32_t top_k, int32_t* nb, int32_t* tpb);
@@ -419,7 +435,7 @@ hipError_t launch_decode_fused(const Shape& s, const sa_pages& pg, const void* q
                                int32_t n_sink, int32_t n_window, float* x, int64_t ldx,
                                int32_t* idx, int32_t* count, int32_t cap, void* out,
                                sa_dtype out_dt, float* lse, void* ws, void* zero, int32_t nb,
-                               int32_t tpb, hipStream_t st);
+                               int32_t tpb, const FusedRla* rla, hipStream_t st);
 
 size_t mass_workspace_bytes(const Shape& s);
 hipError_t launch_attention_mass(const Shape& s, const sa_pages& pg, const void* q,

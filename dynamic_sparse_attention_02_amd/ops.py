@@ -32,6 +32,7 @@ __all__ = [
     "sa_attention_mass",
     "sa_support_coverage",
     "sa_decode_step",
+    "sa_decode_step_rla",
     "sa_decode_step_pages",
     "sa_select_prefill_topk",
     "sa_sparse_prefill",
@@ -202,6 +203,20 @@ def sa_decode_step(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att
                                  int(idx.shape[-1]), _dev(out), _dt(out), _dev(lse), wp, wn,
                                  _stream(stream))
     L.check(st, "sa_decode_step")
+
+
+def sa_decode_step_rla(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att, p, top_k,
+                       n_sink, n_window, x, idx, count, out, lse, rla_state, rla_num, rla_den, ws,
+                       stream=None):
+    wp, wn = _ws(ws)
+    st = L.load().sa_decode_step_rla(ctypes.byref(shape), ctypes.byref(pages), _dev(q), _dev(w_q),
+                                     _dev(kidx_pool), _dev(k_pool), _dev(v_pool), _dt(q),
+                                     float(s_idx), float(s_att), float(p), int(top_k), int(n_sink),
+                                     int(n_window), _dev(x), int(x.stride(0)), _dev(idx),
+                                     _dev(count), int(idx.shape[-1]), _dev(out), _dt(out),
+                                     _dev(lse), _dev(rla_state), _dev(rla_num), _dev(rla_den), wp,
+                                     wn, _stream(stream))
+    L.check(st, "sa_decode_step_rla")
 
 
 def sa_decode_step_noalloc(shape, pages, q, w_q, kidx_pool, k_pool, v_pool, s_idx, s_att, p,

@@ -115,7 +115,8 @@ typedef enum {
   SA_OP_PBS_IMPORTANCE = 8,    /* param = n_rows                                 */
   SA_OP_PBS_SELECT = 9,        /* param = k_blocks                               */
   SA_OP_PREFILL_ORACLE = 10,   /* param unused                                   */
-  SA_OP_DECODE_STEP_PAGES = 11 /* param = cap                                    */
+  SA_OP_DECODE_STEP_PAGES = 11, /* param = cap                                   */
+  SA_OP_DECODE_STEP_RLA = 12    /* param = cap                                   */
 } sa_op;
 
 /* Bytes of workspace the operation needs for this shape (0 if none).  A
@@ -305,6 +306,26 @@ sa_status sa_decode_step_noalloc(const sa_shape* shape, const sa_pages* pages, c
                                  float p, int32_t top_k, int32_t n_sink, int32_t n_window,
                                  float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
                                  void* out, sa_dtype out_dtype, float* lse, hipStream_t stream);
+
+/* sa_decode_step plus the residual linear attention over the tokens left out
+ * of the support ("SPLA", section 2.2, subtraction form), as
+ * sa_sparse_decode_rla computes it: the same scores, lists, counts and
+ * outputs as sa_decode_step, and rla_num [batch][n_q_heads][head_dim],
+ * rla_den [batch][n_q_heads] (fp32) from rla_state as written by
+ * sa_rla_state over the whole sequence.  The persistent launch (few rows,
+ * bf16) forms the listed tokens' terms from the K/V tiles its attention
+ * already holds in LDS; otherwise the step ends with sa_sparse_decode_rla.
+ * Workspace from SA_OP_DECODE_STEP_RLA (param = cap): the SA_OP_DECODE_STEP
+ * layout followed by the residual terms' partial sums, so one workspace of
+ * this size also serves sa_decode_step calls. */
+sa_status sa_decode_step_rla(const sa_shape* shape, const sa_pages* pages, const void* q,
+                             const void* w_q, const void* kidx_pool, const void* k_pool,
+                             const void* v_pool, sa_dtype dtype, float s_idx, float s_att,
+                             float p, int32_t top_k, int32_t n_sink, int32_t n_window,
+                             float* x, int64_t ldx, int32_t* idx, int32_t* count, int32_t cap,
+                             void* out, sa_dtype out_dtype, float* lse, const float* rla_state,
+                             float* rla_num, float* rla_den, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /* One whole page-level decode step ("SPLA", section 2.1: pages ranked by the
  * Taylor score, the top_k pages attended exactly): sa_page_scores, then

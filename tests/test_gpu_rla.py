@@ -1,7 +1,7 @@
 """GPU parity of the residual linear attention tail ("SPLA", section 2.2)
 against the float64 oracle: the global state built by sa_rla_state, and the
-unselected-token terms sa_sparse_decode_rla forms by subtraction while it
-computes the exact attention over the support."""
+unselected-token terms sa_sparse_decode_rla and sa_decode_step_rla form by
+subtraction while they compute the exact attention over the support."""
 
 import numpy as np
 import pytest
@@ -182,3 +182,127 @@ def test_rla_decode64k_full_size():
         o_ref, _ = O.attend(q, K[sup], V[sup], inp.s_att)
         assert S.max_abs(S.to_np(out[0, hs]), o_ref) <= 2e-2, g
     print(f"rla decode64k: worst denominator error {worst:.2e} of the summed weights")
+
+
+def _check_unselected(inp, idx, count, num, den, tol=3e-5):
+    """Every group's unselected-token terms against the oracle's direct sums
+    over the tokens outside the GPU's support; returns the worst denominator
+    error relative to the summed weights."""
+    worst = 0.0
+    for b in range(inp.B):
+        for g in range(inp.H_kv):
+            hs = inp.heads(g)
+            gn, gd = S.to_np(num[b, hs]), S.to_np(den[b, hs])
+            if inp.seq_lens[b] == 0:
+                assert np.all(gn == 0) and np.all(gd == 0), (b, g)
+                continue
+            q = S.to_np(inp.q[b, hs])
+            K = S.to_np(inp.seq_keys(b, g))
+            V = S.to_np(inp.seq_values(b, g))
+            sup = S.gpu_support(idx, count, b * inp.H_kv + g)
+            rn, rd = O.rla_unselected(q, K, V, sup)
+            wsum, wabs = _unselected_scale(q, K, V)
+            assert np.all(np.abs(gd - rd) <= tol * wsum), (b, g, gd, rd)
+            assert np.all(np.abs(gn - rn) <= tol * wabs.max(axis=1, keepdims=True)), (b, g)
+            worst = max(worst, float((np.abs(gd - rd) / wsum).max()))
+    return worst
+
+
+def _same(a, b):
+    """Bit-for-bit equal, NaN (never written) matching NaN."""
+    torch.testing.assert_close(a, b, rtol=0, atol=0, equal_nan=True)
+
+
+def _step(o, inp, kidx, ws, p, top_k, n_sink, n_window, state=None, out_dtype=None):
+    """sa_decode_step (state None) or sa_decode_step_rla; returns x, idx,
+    count, out, lse (and num, den)."""
+    shape = S.shape_of(inp)
+    pages = o.make_pages(inp.page_table, inp.seq_lens_tensor())
+    cap = max(inp.seq_lens)
+    x, idx, count, out, lse = S.empty_like_outputs(inp, cap)
+    if out_dtype is not None:
+        out = out.to(out_dtype)
+    if state is None:
+        o.sa_decode_step(shape, pages, inp.q, inp.w_q, kidx, inp.k_pool, inp.v_pool, inp.s_idx,
+                         inp.s_att, p, top_k, n_sink, n_window, x, idx, count, out, lse, ws)
+        torch.cuda.synchronize()
+        return x, idx, count, out, lse
+    num = torch.full((inp.B, inp.H_q, inp.d), float("nan"), dtype=torch.float32, device="cuda")
+    den = torch.full((inp.B, inp.H_q), float("nan"), dtype=torch.float32, device="cuda")
+    o.sa_decode_step_rla(shape, pages, inp.q, inp.w_q, kidx, inp.k_pool, inp.v_pool, inp.s_idx,
+                         inp.s_att, p, top_k, n_sink, n_window, x, idx, count, out, lse, state,
+                         num, den, ws)
+    torch.cuda.synchronize()
+    return x, idx, count, out, lse, num, den
+
+
+# (lengths, kv heads, group size, dtype, head dim): the first four take the
+# persistent single launch (few rows, bf16: G = 4, 8, 16 and d = 64), the
+# last two the separate calls (fp32; more than 16 rows)
+_STEP_CASES = [([3000, 0, 777], 2, 4, torch.bfloat16, 128),
+               ([2500, 64], 2, 8, torch.bfloat16, 128),
+               ([1900], 1, 16, torch.bfloat16, 128),
+               ([1200, 333], 4, 4, torch.bfloat16, 64),
+               ([1500, 0, 640], 2, 4, torch.float32, 64),
+               ([900, 1300, 70], 6, 4, torch.bfloat16, 128)]
+
+
+@pytest.mark.parametrize("case", range(len(_STEP_CASES)))
+def test_decode_step_rla_matches_step_and_oracle(case):
+    """sa_decode_step_rla: the scores, lists, counts, outputs and lse of
+    sa_decode_step (identical where both run the same launches), and the
+    unselected-token terms against the oracle; one workspace of the RLA op's
+    size serves both entry points, called alternately."""
+    o = ops()
+    from dynamic_sparse_attention_02_amd import _lib as L
+    lens, H_kv, G, dtype, d = _STEP_CASES[case]
+    inp = _inputs(lens, dtype, d, G=G, H_kv=H_kv, seed=40 + case)
+    kidx = S.oracle_kidx_pool(inp)
+    shape = S.shape_of(inp)
+    cap = max(inp.seq_lens)
+    state = torch.from_numpy(oracle_state(inp)).float().cuda()
+    ws = o.alloc_workspace(o.workspace_size(L.SA_OP_DECODE_STEP_RLA, shape, cap))
+    assert o.workspace_size(L.SA_OP_DECODE_STEP_RLA, shape, cap) > \
+        o.workspace_size(L.SA_OP_DECODE_STEP, shape, cap)
+    p = S.f32(0.9)
+    ref = _step(o, inp, kidx, ws, p, 0, 4, 16)
+    got = _step(o, inp, kidx, ws, p, 0, 4, 16, state=state)
+    again = _step(o, inp, kidx, ws, p, 0, 4, 16)
+    fused_both = dtype == torch.bfloat16 and inp.B * H_kv <= 16
+    for r, a_ in zip(ref, again):
+        _same(r, a_)  # the shared workspace leaves the plain step unchanged
+    # same scores and lists whichever path runs (same arithmetic)
+    assert torch.equal(ref[1], got[1]) and torch.equal(ref[2], got[2])
+    for b in range(inp.B):
+        rs = slice(b * H_kv, (b + 1) * H_kv)
+        assert torch.equal(ref[0][rs, :lens[b]], got[0][rs, :lens[b]])
+    if fused_both:
+        _same(ref[3], got[3])
+        _same(ref[4], got[4])
+    else:  # attention split differently: equal within rounding
+        torch.testing.assert_close(ref[3], got[3], rtol=0, atol=1e-5)
+        torch.testing.assert_close(ref[4], got[4], rtol=0, atol=1e-4)  # -inf for empty rows
+    _check_unselected(inp, got[1], got[2], got[5], got[6])
+
+
+def test_decode_step_rla_decode64k_full_size():
+    """The 64K decode workload through sa_decode_step_rla as the bench times
+    it (persistent launch with the residual tail): lists and outputs equal to
+    sa_decode_step's, unselected-token terms of every group against the
+    oracle given the GPU-built state."""
+    o = ops()
+    from dynamic_sparse_attention_02_amd import _lib as L
+    inp = synth.make_decode64k(device="cpu").to("cuda")
+    kidx = S.oracle_kidx_pool(inp)
+    shape = S.shape_of(inp)
+    cap = max(inp.seq_lens)
+    state = gpu_state(inp)
+    ws = o.alloc_workspace(o.workspace_size(L.SA_OP_DECODE_STEP_RLA, shape, cap))
+    p = S.f32(0.9)
+    ref = _step(o, inp, kidx, ws, p, 0, 4, 512, out_dtype=torch.bfloat16)
+    got = _step(o, inp, kidx, ws, p, 0, 4, 512, state=state, out_dtype=torch.bfloat16)
+    for r, g_ in zip(ref, got[:5]):
+        _same(r, g_)
+    assert np.all(S.to_np(got[2]) > 0)
+    worst = _check_unselected(inp, got[1], got[2], got[5], got[6])
+    print(f"decode step rla 64k: worst denominator error {worst:.2e} of the summed weights")
