@@ -228,7 +228,8 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   constexpr int ROWB = D * (int)sizeof(T);
   constexpr int CPR = ROWB / 16;
   constexpr int PITCH = ROWB + 16;
-  constexpr int LPT = kTileF * CPR / kNT;
+  constexpr int TM = kTileF;  // attention tile (tokens)
+  constexpr int LPT = TM * CPR / kNT;
   const Shape& s = a.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NB = a.nb;
@@ -248,10 +249,16 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   __shared__ float red_f[4][kRank];
   __shared__ uint32_t red_u[4];
   __shared__ uint64_t red_u64[4];
-  __shared__ __align__(16) uint32_t hcnt_l[kBinsF];
-  __shared__ __align__(16) uint64_t hmass_l[kBinsF];
-  __shared__ __align__(16) char Ks[kTileF * PITCH];
-  __shared__ __align__(16) char Vs[kTileF * PITCH];
+  // the level histograms (selection) and the K/V tiles (attention, after
+  // the last level) share one LDS region, so that two workgroups fit a
+  // compute unit
+  constexpr int kHistBytes = kBinsF * (4 + 8);
+  constexpr int kTileBytes = 2 * TM * PITCH;
+  __shared__ __align__(16) char lds_big[kHistBytes > kTileBytes ? kHistBytes : kTileBytes];
+  uint32_t(&hcnt_l)[kBinsF] = *reinterpret_cast<uint32_t(*)[kBinsF]>(lds_big);
+  uint64_t(&hmass_l)[kBinsF] = *reinterpret_cast<uint64_t(*)[kBinsF]>(lds_big + kBinsF * 4);
+  char* const Ks = lds_big;
+  char* const Vs = lds_big + TM * PITCH;
   __shared__ __align__(16) T Qs[G][D];
   __shared__ __align__(16) float Ps[G][kTileF];
   // pool token rows ((page * Hkv + g) * 64 + slot) of the tokens to attend
@@ -871,7 +878,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     typedef __attribute__((ext_vector_type(4))) short s16x4_t;
     typedef __attribute__((ext_vector_type(4))) float f32x4_t;
     constexpr int KS = D / 32, MB = D / 16;
-    static_assert(2 * D * 16 * 4 <= kTileF * PITCH, "two waves' outputs fit one tile buffer");
+    static_assert(2 * D * 16 * 4 <= TM * PITCH, "two waves' outputs fit one tile buffer");
     __shared__ float s_wm[4][16], s_wl[4][16];
     const int hq = lane & 15, lg = lane >> 4;
     bf16x8_t qB[KS];
@@ -925,13 +932,21 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     // (each buffer is one vector value, so it stays in registers)
     typedef uint32_t kvv_t __attribute__((ext_vector_type(4 * LPT)));
     kvv_t kA, vA, kB, vB;
-    auto gather = [&](int32_t ts, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
+    // the pool rows of a tile's gather, read from the list one staging
+    // ahead, so a gather waits for no LDS read
+    typedef uint32_t ids_t __attribute__((ext_vector_type(LPT)));
+    auto read_ids = [&](int32_t ts) __attribute__((always_inline)) {
+      ids_t r;
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) r[i] = my_list[min(ts + (i * kNT + tid) / CPR, n_att - 1)];
+      return r;
+    };
+    auto gather = [&](const ids_t& ids, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int pc = i * kNT + tid;
-        const int rk = pc / CPR, ck = pc % CPR;
-        const int32_t e = min(ts + rk, n_att - 1);
-        const int64_t off = (int64_t)my_list[e] * D + ck * 8;
+        const int ck = pc % CPR;
+        const int64_t off = (int64_t)ids[i] * D + ck * 8;
         const uint4 k4 = *reinterpret_cast<const uint4*>(k_pool + off);
         const uint4 v4 = *reinterpret_cast<const uint4*>(v_pool + off);
         kr[4 * i] = k4.x; kr[4 * i + 1] = k4.y; kr[4 * i + 2] = k4.z; kr[4 * i + 3] = k4.w;
@@ -952,7 +967,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       __syncthreads();
     };
     auto compute = [&](int32_t ts) __attribute__((always_inline)) {
-      const int32_t nt = min(kTileF, n_att - ts);
+      const int32_t nt = min(TM, n_att - ts);
       f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
       f32x4_t W = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
@@ -978,8 +993,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         sv[v] = 16 * wave + 4 * lg + v < nt ? S[v] * a.s_att : -INFINITY;
         mt = fmaxf(mt, sv[v]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = row4_max(mt);
       const float m_new = fmaxf(m_run, mt);
       const float mu = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = __expf(m_run - mu);  // 0 before the first valid token
@@ -991,17 +1005,15 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
       l_run = l_run * alpha + ls;
       m_run = m_new;
-      uint32_t hi[2], lo[2];
-#pragma unroll
-      for (int v = 0; v < 2; ++v) {
-        const bf16_raw h0 = f32_to_bf16(pv[2 * v]), h1 = f32_to_bf16(pv[2 * v + 1]);
-        const bf16_raw l0 = f32_to_bf16(pv[2 * v] - bf16_to_f32(h0));
-        const bf16_raw l1 = f32_to_bf16(pv[2 * v + 1] - bf16_to_f32(h1));
-        hi[v] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        lo[v] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-      }
-      const s16x4_t ph = __builtin_bit_cast(s16x4_t, make_uint2(hi[0], hi[1]));
-      const s16x4_t pl = __builtin_bit_cast(s16x4_t, make_uint2(lo[0], lo[1]));
+      // high part: round to nearest even (v_cvt_pk_bf16_f32); low part: the
+      // remainder, exact in fp32, rounded the same way
+      const f32x4v_t pvv = f32x4v_t{pv[0], pv[1], pv[2], pv[3]};
+      const bf16x4_t phb = __builtin_convertvector(pvv, bf16x4_t);
+      const bf16x4_t plb = __builtin_convertvector(pvv - __builtin_convertvector(phb, f32x4v_t), bf16x4_t);
+      const s16x4_t ph = __builtin_bit_cast(s16x4_t, phb);
+      const s16x4_t pl = __builtin_bit_cast(s16x4_t, plb);
+      // the running maximum moved for no lane: the accumulators keep their scale
+      const bool rescale = __any(alpha != 1.f);
       s16x4_t wh = s16x4_t{0, 0, 0, 0}, wl = s16x4_t{0, 0, 0, 0};
       if constexpr (RLA) {  // tokens past the list weigh nothing
         f32x4v_t wv;
@@ -1017,7 +1029,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        oacc[mb] *= alpha;
+        if (rescale) oacc[mb] *= alpha;
         const char* vcol = Vs + (16 * wave + 4 * lg) * PITCH + (16 * mb + hq) * 2;
         const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
         const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + PITCH);
@@ -1034,15 +1046,18 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     };
     int32_t ts = 0;
     if (n_att > 0) {
-      gather(0, kA, vA);
-      gather(kTileF, kB, vB);
-      for (; ts + kTileF < n_att; ts += 2 * kTileF) {  // both tiles of the pair hold tokens
+      gather(read_ids(0), kA, vA);
+      gather(read_ids(TM), kB, vB);
+      ids_t nx = read_ids(2 * TM);
+      for (; ts + TM < n_att; ts += 2 * TM) {  // both tiles of the pair hold tokens
         stage(kA, vA);
-        gather(ts + 2 * kTileF, kA, vA);
+        gather(nx, kA, vA);
+        nx = read_ids(ts + 3 * TM);
         compute(ts);
         stage(kB, vB);
-        gather(ts + 3 * kTileF, kB, vB);
-        compute(ts + kTileF);
+        gather(nx, kB, vB);
+        nx = read_ids(ts + 4 * TM);
+        compute(ts + TM);
       }
       if (ts < n_att) {  // an odd last tile
         stage(kA, vA);
@@ -1064,22 +1079,6 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       s_wm[wave][lane] = m_run;
       s_wl[wave][lane] = lw;
     }
-    // the residual sums of the four waves: numerators in the histogram
-    // masses' LDS (free by now), denominators summed over the lane rows
-    __shared__ float s_rd[4][16];
-    float* rbuf = reinterpret_cast<float*>(hmass_l);
-    if constexpr (RLA) {
-      static_assert(4 * D * 16 * 4 <= (int)sizeof(hmass_l), "four waves' residual sums fit");
-      float* rb = rbuf + wave * D * 16;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) rb[(16 * mb + 4 * lg + v) * 16 + hq] = racc[mb][v];
-      float rd = rden;
-      rd += __shfl_xor(rd, 16, 64);
-      rd += __shfl_xor(rd, 32, 64);
-      if (lane < 16) s_rd[wave][lane] = rd;
-    }
     __syncthreads();
     for (int e = tid; e < G * D; e += kNT) {
       const int hl = e / D, d = e % D;
@@ -1100,7 +1099,27 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         st_dev(&a.part_ml[pi * 2], M);
         st_dev(&a.part_ml[pi * 2 + 1], lsum);
       }
-      if constexpr (RLA) {
+    }
+    if constexpr (RLA) {
+      // the residual sums of the four waves, once the outputs are merged:
+      // numerators through the same LDS, denominators summed over the lane rows
+      __shared__ float s_rd[4][16];
+      static_assert(4 * D * 16 * 4 <= (int)sizeof(lds_big), "four waves' residual sums fit");
+      float* rbuf = reinterpret_cast<float*>(lds_big);
+      float rd = rden;
+      rd += __shfl_xor(rd, 16, 64);
+      rd += __shfl_xor(rd, 32, 64);
+      __syncthreads();  // the outputs' merge is done with the buffer
+      float* rb = rbuf + wave * D * 16;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) rb[(16 * mb + 4 * lg + v) * 16 + hq] = racc[mb][v];
+      if (lane < 16) s_rd[wave][lane] = rd;
+      __syncthreads();
+      for (int e = tid; e < G * D; e += kNT) {
+        const int hl = e / D, d = e % D;
+        const int64_t pi = ((int64_t)row * NB + bi) * G + hl;
         float rn = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; ++w) rn += rbuf[w * D * 16 + d * 16 + hl];
@@ -1517,20 +1536,20 @@ const void* fused_kernel_for(sa_dtype dt, int D, int G, int tpt, int mode) {
   return D == 128 ? fused_instance_g<float, 128, false>(G, tpt) : fused_instance_g<float, 64, false>(G, tpt);
 }
 
-// Whether a workgroup of the kernel fits a compute unit (registers and LDS):
-// the persistent launch places one workgroup per compute unit and every one
-// must be resident at once.  Cached per kernel instance and device.
-bool fused_resident(const void* fn, int dev) {
+// How many workgroups of the kernel fit a compute unit at once (registers
+// and LDS): every workgroup of a persistent launch must be resident at the
+// same time.  Cached per kernel instance and device.
+int fused_resident(const void* fn, int dev) {
   static std::mutex mu;
-  static std::map<std::pair<const void*, int>, bool> cache;
+  static std::map<std::pair<const void*, int>, int> cache;
   std::lock_guard<std::mutex> lk(mu);
   const auto key = std::make_pair(fn, dev);
   auto it = cache.find(key);
   if (it != cache.end()) return it->second;
   int nblk = 0;
-  const bool ok = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, fn, kNT, 0) == hipSuccess && nblk >= 1;
-  cache[key] = ok;
-  return ok;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nblk, fn, kNT, 0) != hipSuccess) nblk = 0;
+  cache[key] = nblk;
+  return nblk;
 }
 
 }  // namespace
@@ -1549,7 +1568,10 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, i
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     return false;
-  int n_b = cus / rows;  // one workgroup per compute unit
+  // one workgroup per compute unit (two per unit hide the gathers' latency
+  // better but make every barrier of the row slower by more than the
+  // attention gains); every workgroup of the launch must be resident at once
+  int n_b = cus / rows;
   if (n_b > kMaxNB) n_b = kMaxNB;
   if (n_b < 1) return false;
   // tokens per workgroup: a power-of-two number of kNT rounds, at most 16
@@ -1560,7 +1582,7 @@ bool fused_plan(const Shape& s, int32_t n_sink, int32_t n_window, sa_dtype dt, i
   // each workgroup's share of the sink/window tokens must fit its list
   const int64_t forced = (int64_t)n_sink + n_window;
   if ((forced + n_b - 1) / n_b > 64) return false;
-  if (!fused_resident(fused_kernel_for(dt, s.D, G, rounds, mode), dev)) return false;
+  if (fused_resident(fused_kernel_for(dt, s.D, G, rounds, mode), dev) < 1) return false;
   *nb = n_b;
   *tpb = rounds * kNT;
   return true;

@@ -113,6 +113,16 @@ __device__ __forceinline__ uint32_t wave_excl_scan_u32(uint32_t v) {
   return wave_incl_scan(v) - v;
 }
 
+// Maximum over the four lanes i, i ^ 16, i ^ 32, i ^ 48 (the same position
+// in each 16-lane row), by the gfx950 row swaps (no LDS round trip); every
+// lane receives the result.
+__device__ __forceinline__ float row4_max(float v) {
+  const auto r16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r16[0]), __uint_as_float(r16[1]));
+  const auto r32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r32[0]), __uint_as_float(r32[1]));
+}
+
 // Sum / maximum over each aligned group of 16 lanes (a DPP row); every lane
 // of the row receives its row's value.
 __device__ __forceinline__ float row16_sum(float v) {

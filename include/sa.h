@@ -309,8 +309,10 @@ sa_status sa_decode_step_noalloc(const sa_shape* shape, const sa_pages* pages, c
 
 /* sa_decode_step plus the residual linear attention over the tokens left out
  * of the support ("SPLA", section 2.2, subtraction form), as
- * sa_sparse_decode_rla computes it: the same scores, lists, counts and
- * outputs as sa_decode_step, and rla_num [batch][n_q_heads][head_dim],
+ * sa_sparse_decode_rla computes it: the same scores, lists and counts as
+ * sa_decode_step and outputs equal within rounding (the attention may be
+ * split over a different number of workgroups), and rla_num
+ * [batch][n_q_heads][head_dim],
  * rla_den [batch][n_q_heads] (fp32) from rla_state as written by
  * sa_rla_state over the whole sequence.  The persistent launch (few rows,
  * bf16) forms the listed tokens' terms from the K/V tiles its attention

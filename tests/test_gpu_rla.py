@@ -268,7 +268,6 @@ def test_decode_step_rla_matches_step_and_oracle(case):
     ref = _step(o, inp, kidx, ws, p, 0, 4, 16)
     got = _step(o, inp, kidx, ws, p, 0, 4, 16, state=state)
     again = _step(o, inp, kidx, ws, p, 0, 4, 16)
-    fused_both = dtype == torch.bfloat16 and inp.B * H_kv <= 16
     for r, a_ in zip(ref, again):
         _same(r, a_)  # the shared workspace leaves the plain step unchanged
     # same scores and lists whichever path runs (same arithmetic)
@@ -276,12 +275,10 @@ def test_decode_step_rla_matches_step_and_oracle(case):
     for b in range(inp.B):
         rs = slice(b * H_kv, (b + 1) * H_kv)
         assert torch.equal(ref[0][rs, :lens[b]], got[0][rs, :lens[b]])
-    if fused_both:
-        _same(ref[3], got[3])
-        _same(ref[4], got[4])
-    else:  # attention split differently: equal within rounding
-        torch.testing.assert_close(ref[3], got[3], rtol=0, atol=1e-5)
-        torch.testing.assert_close(ref[4], got[4], rtol=0, atol=1e-4)  # -inf for empty rows
+    # the attention may be split over a different number of workgroups:
+    # equal within rounding
+    torch.testing.assert_close(ref[3], got[3], rtol=0, atol=1e-5)
+    torch.testing.assert_close(ref[4], got[4], rtol=0, atol=1e-4)  # -inf for empty rows
     _check_unselected(inp, got[1], got[2], got[5], got[6])
 
 
@@ -301,8 +298,11 @@ def test_decode_step_rla_decode64k_full_size():
     p = S.f32(0.9)
     ref = _step(o, inp, kidx, ws, p, 0, 4, 512, out_dtype=torch.bfloat16)
     got = _step(o, inp, kidx, ws, p, 0, 4, 512, state=state, out_dtype=torch.bfloat16)
-    for r, g_ in zip(ref, got[:5]):
+    for r, g_ in zip(ref[:3], got[:3]):  # scores, lists, counts
         _same(r, g_)
+    # outputs equal within rounding (bf16: a unit in the last place)
+    torch.testing.assert_close(ref[3].float(), got[3].float(), rtol=8e-3, atol=1e-5)
+    torch.testing.assert_close(ref[4], got[4], rtol=0, atol=1e-4)
     assert np.all(S.to_np(got[2]) > 0)
     worst = _check_unselected(inp, got[1], got[2], got[5], got[6])
     print(f"decode step rla 64k: worst denominator error {worst:.2e} of the summed weights")
