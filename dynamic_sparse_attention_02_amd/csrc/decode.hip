@@ -10,14 +10,18 @@
 // (16-byte loads, 16 lanes per 256-byte row, staged in LDS), computes the
 // logits of the group's heads with one lane per token (bf16 pairs through
 // v_dot2_f32_bf16, fp32 accumulate), keeps an online softmax per head, and
-// accumulates P.V with one lane per head dimension.  The next tile's rows are
+// accumulates P.V with one lane per head dimension; for bf16 and groups of 4
+// to 16 heads the tile runs on the matrix cores instead (each wave takes 16
+// of its tokens for all the group's heads, padded to 16: S^T = K Q^T and
+// O^T += V^T P^T, P split into a bf16 high part and the rounding of the
+// rest, the four waves' softmax states merged per chunk), which leaves the
+// VALU most of the issue slots the gathers need.  The next tile's rows are
 // loaded into registers, and the pool addresses of the tile after it resolved
 // (list entry -> page table -> row), while the current tile is processed.  A second kernel
 // merges the per-chunk (max, sum, output) partials in chunk order.
 //
 // Bound: HBM bandwidth of the gathered rows (512 B per listed token for
-// d = 128 bf16).  No matrix cores: the per-token work is a G x d by d x 1
-// product, too thin to fill an MFMA tile.
+// d = 128 bf16).
 #include <map>
 #include <mutex>
 #include <utility>
@@ -228,7 +232,80 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
       }
       __syncthreads();
     };
+    // matrix-core tile (bf16, G in [4, 16], no residual terms): wave w takes
+    // tokens [16 w, 16 w + 16); lane (hq, lg) holds tokens 16 w + 4 lg + v of
+    // head hq (heads past G carry zero queries)
+    constexpr bool MF = sizeof(T) == 2 && !RLA && G >= 4 && G <= 16 && C::NW == 4;
+    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+    typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+    typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+    constexpr int KS = D / 32, MB = D / 16;
+    const int hq = lane & 15, lg = lane >> 4;
+    bf16x8_t qB[MF ? KS : 1];
+    f32x4_t oacc[MF ? MB : 1];
+    float m_mf = -INFINITY, l_mf = 0.f;
+    if constexpr (MF) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        uint4 w = make_uint4(0, 0, 0, 0);
+        if (hq < G) w = *reinterpret_cast<const uint4*>(&Qs[hq < G ? hq : 0][32 * ks + 8 * lg]);
+        qB[ks] = __builtin_bit_cast(bf16x8_t, w);
+      }
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    auto compute_mf = [&](int32_t ts) __attribute__((always_inline)) {
+      const int32_t nt = min(kTile, t1 - ts);
+      f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const char* krow = Ks + (16 * wave + hq) * C::PITCH + 16 * lg;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kv), qB[ks], S, 0, 0, 0);
+      }
+      float sv[4], mt = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        sv[v] = 16 * wave + 4 * lg + v < nt ? S[v] * s_att : -INFINITY;
+        mt = fmaxf(mt, sv[v]);
+      }
+      mt = row4_max(mt);
+      const float m_new = fmaxf(m_mf, mt);
+      const float mu = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __expf(m_mf - mu);  // 0 before the first valid token
+      float pv[4], ls = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pv[v] = __expf(sv[v] - mu);
+        ls += pv[v];
+      }
+      l_mf = l_mf * alpha + ls;
+      m_mf = m_new;
+      const f32x4_t pvv = f32x4_t{pv[0], pv[1], pv[2], pv[3]};
+      const bf16x4_t phb = __builtin_convertvector(pvv, bf16x4_t);
+      const bf16x4_t plb = __builtin_convertvector(pvv - __builtin_convertvector(phb, f32x4_t), bf16x4_t);
+      const s16x4_t ph = __builtin_bit_cast(s16x4_t, phb);
+      const s16x4_t pl = __builtin_bit_cast(s16x4_t, plb);
+      const bool rescale = __any(alpha != 1.f);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        if (rescale) oacc[mb] *= alpha;
+        const char* vcol = Vs + (16 * wave + 4 * lg) * C::PITCH + (16 * mb + hq) * 2;
+        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
+        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + C::PITCH);
+        const uint32_t v2 = *reinterpret_cast<const uint16_t*>(vcol + 2 * C::PITCH);
+        const uint32_t v3 = *reinterpret_cast<const uint16_t*>(vcol + 3 * C::PITCH);
+        const s16x4_t av = __builtin_bit_cast(s16x4_t, make_uint2(v0 | (v1 << 16), v2 | (v3 << 16)));
+        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
+        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
+      }
+    };
     auto compute = [&](int32_t ts) __attribute__((always_inline)) {
+      if constexpr (MF) {
+        compute_mf(ts);
+        return;
+      }
       const int32_t nt = min(kTile, t1 - ts);
         // logits: lane = token of the tile
         float sc[C::HPW];
@@ -369,6 +446,47 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
         if (ts + kTile < t1) gather(ts + kTile, kA, vA);
         compute(ts);
       }
+    }
+    if constexpr (MF) {
+      // merge the waves (lane (hq, lg) holds O^T[16 mb + 4 lg + v][hq]) and
+      // store the chunk's partials
+      static_assert(2 * D * 16 * 4 <= kTile * C::PITCH, "two waves' outputs fit one tile buffer");
+      __shared__ float s_wm[4][16], s_wl[4][16];
+      float lw = l_mf;
+      lw += __shfl_xor(lw, 16, 64);
+      lw += __shfl_xor(lw, 32, 64);
+      __syncthreads();  // the tile buffers are free
+      float* ob = reinterpret_cast<float*>(wave < 2 ? Ks : Vs) + (wave & 1) * D * 16;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ob[(16 * mb + 4 * lg + v) * 16 + hq] = oacc[mb][v];
+      if (lane < 16) {
+        s_wm[wave][lane] = m_mf;
+        s_wl[wave][lane] = lw;
+      }
+      __syncthreads();
+      for (int e = tid; e < G * D; e += C::NT) {
+        const int hl = e / D, d = e % D;
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) M = fmaxf(M, s_wm[w][hl]);
+        float lsum = 0.f, osum = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float wt = s_wm[w][hl] == -INFINITY ? 0.f : __expf(s_wm[w][hl] - M);
+          const float* obw = reinterpret_cast<const float*>(w < 2 ? Ks : Vs) + (w & 1) * D * 16;
+          lsum += s_wl[w][hl] * wt;
+          osum += obw[d * 16 + hl] * wt;
+        }
+        const int64_t pi = ((int64_t)b * s.Hq + g * G + hl) * nchunk_max + c;
+        part_o[pi * D + d] = osum;
+        if (d == 0) {
+          part_ml[pi * 2] = M;
+          part_ml[pi * 2 + 1] = lsum;
+        }
+      }
+      continue;
     }
     // partials of this chunk
 #pragma unroll

@@ -80,7 +80,7 @@ def _unselected_scale(q, K, V):
 @pytest.mark.parametrize("rule,dtype,d", [({"p": 0.9}, torch.bfloat16, 128), ({"k": 50}, torch.float32, 64),
                                           ({"p": 1.0}, torch.bfloat16, 128)])
 def test_decode_rla_matches_oracle(rule, dtype, d):
-    """Exact attention identical to sa_sparse_decode; unselected-token terms
+    """Exact attention equal to sa_sparse_decode's; unselected-token terms
     (numerator and denominator) against the oracle's direct sums over the
     tokens outside the GPU's support, given the oracle's state."""
     o = ops()
@@ -110,7 +110,10 @@ def test_decode_rla_matches_oracle(rule, dtype, d):
     o.sa_sparse_decode_rla(shape, pages, inp.q, inp.k_pool, inp.v_pool, idx, count, inp.s_att,
                            out2, lse2, state, num, den, ws_r)
     torch.cuda.synchronize()
-    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    # same attention as sa_sparse_decode (which may run it on the matrix cores:
+    # equal within rounding)
+    torch.testing.assert_close(out, out2, rtol=1e-4, atol=1e-5)
+    torch.testing.assert_close(lse, lse2, rtol=0, atol=1e-4)
     for b in range(inp.B):
         for g in range(inp.H_kv):
             hs = inp.heads(g)
