@@ -40,11 +40,12 @@ CFLAGS = [
 ]
 
 
-# Per-source extra flags.  prefill.hip, fused.hip: keep MFMA results and
+# Per-source extra flags.  prefill.hip, fused.hip, decode.hip: keep MFMA results and
 # accumulators in arch VGPRs (the softmax reads every score and rescales the
 # output accumulator; in AGPRs each such access costs a copy).
 EXTRA = {"prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "fused.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:

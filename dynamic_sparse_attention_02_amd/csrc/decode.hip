@@ -288,9 +288,12 @@ k_decode_split(const T* __restrict__ q, const T* __restrict__ k_pool, const T* _
       const s16x4_t ph = __builtin_bit_cast(s16x4_t, phb);
       const s16x4_t pl = __builtin_bit_cast(s16x4_t, plb);
       const bool rescale = __any(alpha != 1.f);
+      if (rescale) {  // (wave-uniform: a branch, not a select per accumulator)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        if (rescale) oacc[mb] *= alpha;
         const char* vcol = Vs + (16 * wave + 4 * lg) * C::PITCH + (16 * mb + hq) * 2;
         const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
         const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + C::PITCH);

@@ -1027,9 +1027,12 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         wh = __builtin_bit_cast(s16x4_t, bh);
         wl = __builtin_bit_cast(s16x4_t, bl);
       }
+      if (rescale) {  // (wave-uniform: a branch, not a select per accumulator)
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        if (rescale) oacc[mb] *= alpha;
         const char* vcol = Vs + (16 * wave + 4 * lg) * PITCH + (16 * mb + hq) * 2;
         const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
         const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + PITCH);
