@@ -152,6 +152,34 @@ __device__ __forceinline__ void row_barrier(uint32_t* flags, int nb, int bi, uin
   __syncthreads();
 }
 
+// row_barrier in two halves: arrive (this workgroup's memory operations
+// completed, its flag raised), later wait for the row's flags; between them
+// the workgroup works on what it already holds.
+__device__ __forceinline__ void row_arrive(uint32_t* flags, int bi, uint32_t epoch) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(&flags[bi], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void row_wait(uint32_t* flags, int nb, uint32_t epoch, uint32_t* err) {
+  if (threadIdx.x < kWave) {
+    uint32_t spins = 0;
+    for (;;) {
+      bool ok = true;
+      for (int k = (int)threadIdx.x; k < nb; k += kWave)
+        ok = ok && __hip_atomic_load(&flags[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= epoch;
+      if (__all(ok)) break;
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins > kSpinLimit) {
+        if (threadIdx.x == 0) atomicOr(err, 1u);
+        break;
+      }
+    }
+  }
+  __syncthreads();
+}
+
 // The first barrier of a top-p row also yields the row's maximum score key:
 // each workgroup stores its own maximum under a marker bit in one 64-bit
 // word (written once per launch, so a word never changes while another
@@ -481,6 +509,250 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   }
   stamp(a, 2);
 
+  // ---- attention machinery (the matrix-core tiles of phase 3; in token
+  // mode it also runs during the level-2 barrier) ----
+  const T* k_pool = (const T*)a.k_pool;
+  const T* v_pool = (const T*)a.v_pool;
+  int32_t n_cur = 0;  // tokens of the current attention job in my_list
+  // Matrix-core attention: in each 64-token tile wave w takes tokens
+  // [16w, 16w + 16).  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves a lane
+  // with 4 tokens of one head (head = lane % 16, the group's heads padded
+  // to 16 with zero queries), which is the lane layout of the P^T operand
+  // of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, so each wave runs its own
+  // online softmax without exchanging scores.  P enters the product as a
+  // bf16 high part plus the bf16 rounding of the remainder (16 significant
+  // bits); K and V are staged row-major.  The four waves' softmax states
+  // are merged once at the end.
+  typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+  typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+  typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+  constexpr int KS = D / 32, MB = D / 16;
+  static_assert(2 * D * 16 * 4 <= TM * PITCH, "two waves' outputs fit one tile buffer");
+  __shared__ float s_wm[4][16], s_wl[4][16];
+  const int hq = lane & 15, lg = lane >> 4;
+  bf16x8_t qB[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (hq < G) w = *reinterpret_cast<const uint4*>(&Qs[hq < G ? hq : 0][32 * ks + 8 * lg]);
+    qB[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  f32x4_t oacc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+  // Residual linear attention over the tokens left out ("SPLA", section
+  // 2.2, subtraction form), with RLA: this workgroup's sums over its own
+  // listed tokens, num_h = sum_j w_hj v_j and den_h = sum_j w_hj, where
+  // w_hj = phi(q_h) . phi(k_j) and phi = exp elementwise, on the matrix
+  // cores beside the attention: W^T = phi(K) phi(Q)^T takes the A operand's
+  // key registers of S^T (exponentiated) and phi(Q) in place of Q, each
+  // fp32 factor split into a bf16 high part and the bf16 rounding of the
+  // remainder (three products: hi.hi, hi.lo, lo.hi; the dropped lo.lo term
+  // and the roundings stay below 2^-16 of each product); W^T has the lane
+  // layout of P^T, so num^T += V^T W^T reuses the V^T operand, again with
+  // W split into high and low parts.
+  typedef __attribute__((ext_vector_type(8))) float f32x8_t;
+  typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+  typedef __attribute__((ext_vector_type(4))) float f32x4v_t;
+  bf16x8_t qH[RLA ? KS : 1], qL[RLA ? KS : 1];
+  f32x4_t racc[RLA ? MB : 1];
+  float rden = 0.f;  // lane (head hq): its tokens' weights
+  if constexpr (RLA) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      f32x8_t f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        f[e] = hq < G ? __expf(to_f32<T>(Qs[hq < G ? hq : 0][32 * ks + 8 * lg + e])) : 0.f;
+      qH[ks] = __builtin_convertvector(f, bf16x8_t);
+      qL[ks] = __builtin_convertvector(f - __builtin_convertvector(qH[ks], f32x8_t), bf16x8_t);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) racc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  // K and V rows: 16 lanes per row (contiguous loads), staged row-major;
+  // the V^T operand is gathered from four rows by 2-byte LDS reads.  Tiles
+  // go in pairs through two register buffers: while a tile is computed the
+  // next tile's rows and the following pair's are in flight.  The gathers
+  // are branch-free (rows past the list re-read its last token, whose
+  // scores are masked), so the compiler waits for one buffer's loads at a
+  // staging, not for every load in flight.
+  // (each buffer is one vector value, so it stays in registers)
+  typedef uint32_t kvv_t __attribute__((ext_vector_type(4 * LPT)));
+  kvv_t kA, vA, kB, vB;
+  // the pool rows of a tile's gather, read from the list one staging
+  // ahead, so a gather waits for no LDS read
+  typedef uint32_t ids_t __attribute__((ext_vector_type(LPT)));
+  auto read_ids = [&](int32_t ts) __attribute__((always_inline)) {
+    ids_t r;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) r[i] = my_list[min(ts + (i * kNT + tid) / CPR, n_cur - 1)];
+    return r;
+  };
+  auto gather = [&](const ids_t& ids, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int pc = i * kNT + tid;
+      const int ck = pc % CPR;
+      const int64_t off = (int64_t)ids[i] * D + ck * 8;
+      const uint4 k4 = *reinterpret_cast<const uint4*>(k_pool + off);
+      const uint4 v4 = *reinterpret_cast<const uint4*>(v_pool + off);
+      kr[4 * i] = k4.x; kr[4 * i + 1] = k4.y; kr[4 * i + 2] = k4.z; kr[4 * i + 3] = k4.w;
+      vr[4 * i] = v4.x; vr[4 * i + 1] = v4.y; vr[4 * i + 2] = v4.z; vr[4 * i + 3] = v4.w;
+    }
+  };
+  auto stage = [&](const kvv_t& kr, const kvv_t& vr) __attribute__((always_inline)) {
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int pc = i * kNT + tid;
+      const int rk = pc / CPR, ck = pc % CPR;
+      *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) =
+          make_uint4(kr[4 * i], kr[4 * i + 1], kr[4 * i + 2], kr[4 * i + 3]);
+      *reinterpret_cast<uint4*>(Vs + rk * PITCH + ck * 16) =
+          make_uint4(vr[4 * i], vr[4 * i + 1], vr[4 * i + 2], vr[4 * i + 3]);
+    }
+    __syncthreads();
+  };
+  auto compute = [&](int32_t ts) __attribute__((always_inline)) {
+    const int32_t nt = min(TM, n_cur - ts);
+    f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t W = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(krow + 64 * ks);
+      const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kv);
+      S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qB[ks], S, 0, 0, 0);
+      if constexpr (RLA) {
+        f32x8_t f = __builtin_convertvector(kb, f32x8_t);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = __expf(f[e]);
+        const bf16x8_t kh = __builtin_convertvector(f, bf16x8_t);
+        const bf16x8_t kl = __builtin_convertvector(f - __builtin_convertvector(kh, f32x8_t), bf16x8_t);
+        W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qH[ks], W, 0, 0, 0);
+        W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qL[ks], W, 0, 0, 0);
+        W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qH[ks], W, 0, 0, 0);
+      }
+    }
+    float sv[4], mt = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = 16 * wave + 4 * lg + v < nt ? S[v] * a.s_att : -INFINITY;
+      mt = fmaxf(mt, sv[v]);
+    }
+    mt = row4_max(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float mu = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __expf(m_run - mu);  // 0 before the first valid token
+    float pv[4], ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      pv[v] = __expf(sv[v] - mu);
+      ls += pv[v];
+    }
+    l_run = l_run * alpha + ls;
+    m_run = m_new;
+    // high part: round to nearest even (v_cvt_pk_bf16_f32); low part: the
+    // remainder, exact in fp32, rounded the same way
+    const f32x4v_t pvv = f32x4v_t{pv[0], pv[1], pv[2], pv[3]};
+    const bf16x4_t phb = __builtin_convertvector(pvv, bf16x4_t);
+    const bf16x4_t plb = __builtin_convertvector(pvv - __builtin_convertvector(phb, f32x4v_t), bf16x4_t);
+    const s16x4_t ph = __builtin_bit_cast(s16x4_t, phb);
+    const s16x4_t pl = __builtin_bit_cast(s16x4_t, plb);
+    // the running maximum moved for no lane: the accumulators keep their scale
+    const bool rescale = __any(alpha != 1.f);
+    s16x4_t wh = s16x4_t{0, 0, 0, 0}, wl = s16x4_t{0, 0, 0, 0};
+    if constexpr (RLA) {  // tokens past the list weigh nothing
+      f32x4v_t wv;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        wv[v] = 16 * wave + 4 * lg + v < nt ? W[v] : 0.f;
+        rden += wv[v];
+      }
+      const bf16x4_t bh = __builtin_convertvector(wv, bf16x4_t);
+      const bf16x4_t bl = __builtin_convertvector(wv - __builtin_convertvector(bh, f32x4v_t), bf16x4_t);
+      wh = __builtin_bit_cast(s16x4_t, bh);
+      wl = __builtin_bit_cast(s16x4_t, bl);
+    }
+    if (rescale) {  // (wave-uniform: a branch, not a select per accumulator)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const char* vcol = Vs + (16 * wave + 4 * lg) * PITCH + (16 * mb + hq) * 2;
+      const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
+      const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + PITCH);
+      const uint32_t v2 = *reinterpret_cast<const uint16_t*>(vcol + 2 * PITCH);
+      const uint32_t v3 = *reinterpret_cast<const uint16_t*>(vcol + 3 * PITCH);
+      const s16x4_t av = __builtin_bit_cast(s16x4_t, make_uint2(v0 | (v1 << 16), v2 | (v3 << 16)));
+      oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
+      oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
+      if constexpr (RLA) {
+        racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wh, racc[mb], 0, 0, 0);
+        racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wl, racc[mb], 0, 0, 0);
+      }
+    }
+  };
+  // the tiles of my_list[0, n_cur), continuing the running softmax state
+  auto run_tiles = [&]() __attribute__((always_inline)) {
+    int32_t ts = 0;
+    if (n_cur > 0) {
+      gather(read_ids(0), kA, vA);
+      gather(read_ids(TM), kB, vB);
+      ids_t nx = read_ids(2 * TM);
+      for (; ts + TM < n_cur; ts += 2 * TM) {  // both tiles of the pair hold tokens
+        stage(kA, vA);
+        gather(nx, kA, vA);
+        nx = read_ids(ts + 3 * TM);
+        compute(ts);
+        stage(kB, vB);
+        gather(nx, kB, vB);
+        nx = read_ids(ts + 4 * TM);
+        compute(ts + TM);
+      }
+      if (ts < n_cur) {  // an odd last tile
+        stage(kA, vA);
+        compute(ts);
+      }
+    }
+  };
+  // Token mode on the matrix cores: the tokens above the level-1 crossing
+  // bin are in the support whatever the later levels decide, so a
+  // workgroup attends the first kEarlyTiles tiles of its own (sink/window
+  // tokens aside) between arriving at the level-2 barrier and waiting on it
+  // (about the barrier's latency; more would delay the row's resolve);
+  // phase 3 then attends the rest.  Which tokens go early depends on the
+  // scores only, so the result stays deterministic.
+  constexpr bool kEarly = sizeof(T) == 2 && !PAGES && !SEL;
+  constexpr int kEarlyTiles = 3;
+  uint32_t early_bits = 0;  // bit u: token u of this thread was attended early
+  auto early_attend = [&](uint32_t pre1) __attribute__((always_inline)) {
+    uint32_t cnt = 0, sure = 0;
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+      const int32_t j = j0 + u * kNT + tid;
+      const bool b = j < n && !(j < a.n_sink || j >= n - a.n_window) && (key[u] >> 20) > pre1;
+      sure |= b ? (1u << u) : 0u;
+      cnt += b ? 1u : 0u;
+    }
+    uint32_t tot;
+    uint32_t o = blk_scan<uint32_t>(cnt, red_u, tot);
+    const uint32_t cap = (uint32_t)(kEarlyTiles * TM);
+#pragma unroll
+    for (int u = 0; u < TPT; ++u)
+      if (((sure >> u) & 1u) && o < cap) {
+        const int32_t jl = u * kNT + tid;  // j - j0
+        my_list[o++] = (uint32_t)(((int64_t)s_pt[jl >> 6] * s.Hkv + g) * kPage + (jl & 63));
+        early_bits |= 1u << u;
+      }
+    __syncthreads();
+    n_cur = (int32_t)min(tot, cap);
+    run_tiles();
+  };
+
   // ---- 2. threshold by radix levels ----
   const bool topk = a.top_k > 0;
   const float mx = key_score(M);
@@ -595,7 +867,13 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     stamp(a, 3 * level);
-    row_barrier(flags, NB, bi, ++epoch, err);
+    if (kEarly && level == 2) {
+      row_arrive(flags, bi, ++epoch);
+      early_attend(pre);
+      row_wait(flags, NB, epoch, err);
+    } else {
+      row_barrier(flags, NB, bi, ++epoch, err);
+    }
     stamp(a, 3 * level + 1);
     // resolve (wave 0): coarse groups, then the 64 bins of the crossing group
     if (wave == 0) {
@@ -828,14 +1106,14 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       my_sel += selmask[u] & 1u;
-      cnt_nf += (selmask[u] == 1u) ? 1u : 0u;
+      cnt_nf += (selmask[u] == 1u && !((early_bits >> u) & 1u)) ? 1u : 0u;  // (not attended early)
     }
     uint32_t tot_nf;
     const uint32_t off = blk_scan<uint32_t>(cnt_nf, red_u, tot_nf);
     uint32_t o = off;
 #pragma unroll
     for (int u = 0; u < TPT; ++u)
-      if (selmask[u] == 1u) {
+      if (selmask[u] == 1u && !((early_bits >> u) & 1u)) {
         const int32_t jl = u * kNT + tid;  // j - j0
         my_list[o++] = (uint32_t)(((int64_t)s_pt[jl >> 6] * s.Hkv + g) * kPage + (jl & 63));
       }
@@ -862,211 +1140,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   stamp(a, 5);
   if constexpr (!SEL) {
   const int32_t n_att = (int32_t)s_cnt;
-    const T* k_pool = (const T*)a.k_pool;
-    const T* v_pool = (const T*)a.v_pool;
     if constexpr (sizeof(T) == 2) {
-    // Matrix-core attention: in each 64-token tile wave w takes tokens
-    // [16w, 16w + 16).  S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves a lane
-    // with 4 tokens of one head (head = lane % 16, the group's heads padded
-    // to 16 with zero queries), which is the lane layout of the P^T operand
-    // of O^T += V^T P^T on v_mfma_f32_16x16x16_bf16, so each wave runs its own
-    // online softmax without exchanging scores.  P enters the product as a
-    // bf16 high part plus the bf16 rounding of the remainder (16 significant
-    // bits); K and V are staged row-major.  The four waves' softmax states
-    // are merged once at the end.
-    typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
-    typedef __attribute__((ext_vector_type(4))) short s16x4_t;
-    typedef __attribute__((ext_vector_type(4))) float f32x4_t;
-    constexpr int KS = D / 32, MB = D / 16;
-    static_assert(2 * D * 16 * 4 <= TM * PITCH, "two waves' outputs fit one tile buffer");
-    __shared__ float s_wm[4][16], s_wl[4][16];
-    const int hq = lane & 15, lg = lane >> 4;
-    bf16x8_t qB[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      uint4 w = make_uint4(0, 0, 0, 0);
-      if (hq < G) w = *reinterpret_cast<const uint4*>(&Qs[hq < G ? hq : 0][32 * ks + 8 * lg]);
-      qB[ks] = __builtin_bit_cast(bf16x8_t, w);
-    }
-    f32x4_t oacc[MB];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) oacc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
-    // Residual linear attention over the tokens left out ("SPLA", section
-    // 2.2, subtraction form), with RLA: this workgroup's sums over its own
-    // listed tokens, num_h = sum_j w_hj v_j and den_h = sum_j w_hj, where
-    // w_hj = phi(q_h) . phi(k_j) and phi = exp elementwise, on the matrix
-    // cores beside the attention: W^T = phi(K) phi(Q)^T takes the A operand's
-    // key registers of S^T (exponentiated) and phi(Q) in place of Q, each
-    // fp32 factor split into a bf16 high part and the bf16 rounding of the
-    // remainder (three products: hi.hi, hi.lo, lo.hi; the dropped lo.lo term
-    // and the roundings stay below 2^-16 of each product); W^T has the lane
-    // layout of P^T, so num^T += V^T W^T reuses the V^T operand, again with
-    // W split into high and low parts.
-    typedef __attribute__((ext_vector_type(8))) float f32x8_t;
-    typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
-    typedef __attribute__((ext_vector_type(4))) float f32x4v_t;
-    bf16x8_t qH[RLA ? KS : 1], qL[RLA ? KS : 1];
-    f32x4_t racc[RLA ? MB : 1];
-    float rden = 0.f;  // lane (head hq): its tokens' weights
-    if constexpr (RLA) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        f32x8_t f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          f[e] = hq < G ? __expf(bf16_to_f32(Qs[hq < G ? hq : 0][32 * ks + 8 * lg + e])) : 0.f;
-        qH[ks] = __builtin_convertvector(f, bf16x8_t);
-        qL[ks] = __builtin_convertvector(f - __builtin_convertvector(qH[ks], f32x8_t), bf16x8_t);
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) racc[mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    }
-    // K and V rows: 16 lanes per row (contiguous loads), staged row-major;
-    // the V^T operand is gathered from four rows by 2-byte LDS reads.  Tiles
-    // go in pairs through two register buffers: while a tile is computed the
-    // next tile's rows and the following pair's are in flight.  The gathers
-    // are branch-free (rows past the list re-read its last token, whose
-    // scores are masked), so the compiler waits for one buffer's loads at a
-    // staging, not for every load in flight.
-    // (each buffer is one vector value, so it stays in registers)
-    typedef uint32_t kvv_t __attribute__((ext_vector_type(4 * LPT)));
-    kvv_t kA, vA, kB, vB;
-    // the pool rows of a tile's gather, read from the list one staging
-    // ahead, so a gather waits for no LDS read
-    typedef uint32_t ids_t __attribute__((ext_vector_type(LPT)));
-    auto read_ids = [&](int32_t ts) __attribute__((always_inline)) {
-      ids_t r;
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) r[i] = my_list[min(ts + (i * kNT + tid) / CPR, n_att - 1)];
-      return r;
-    };
-    auto gather = [&](const ids_t& ids, kvv_t& kr, kvv_t& vr) __attribute__((always_inline)) {
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int pc = i * kNT + tid;
-        const int ck = pc % CPR;
-        const int64_t off = (int64_t)ids[i] * D + ck * 8;
-        const uint4 k4 = *reinterpret_cast<const uint4*>(k_pool + off);
-        const uint4 v4 = *reinterpret_cast<const uint4*>(v_pool + off);
-        kr[4 * i] = k4.x; kr[4 * i + 1] = k4.y; kr[4 * i + 2] = k4.z; kr[4 * i + 3] = k4.w;
-        vr[4 * i] = v4.x; vr[4 * i + 1] = v4.y; vr[4 * i + 2] = v4.z; vr[4 * i + 3] = v4.w;
-      }
-    };
-    auto stage = [&](const kvv_t& kr, const kvv_t& vr) __attribute__((always_inline)) {
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int pc = i * kNT + tid;
-        const int rk = pc / CPR, ck = pc % CPR;
-        *reinterpret_cast<uint4*>(Ks + rk * PITCH + ck * 16) =
-            make_uint4(kr[4 * i], kr[4 * i + 1], kr[4 * i + 2], kr[4 * i + 3]);
-        *reinterpret_cast<uint4*>(Vs + rk * PITCH + ck * 16) =
-            make_uint4(vr[4 * i], vr[4 * i + 1], vr[4 * i + 2], vr[4 * i + 3]);
-      }
-      __syncthreads();
-    };
-    auto compute = [&](int32_t ts) __attribute__((always_inline)) {
-      const int32_t nt = min(TM, n_att - ts);
-      f32x4_t S = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      f32x4_t W = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const char* krow = Ks + (16 * wave + hq) * PITCH + 16 * lg;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kv = *reinterpret_cast<const uint4*>(krow + 64 * ks);
-        const bf16x8_t kb = __builtin_bit_cast(bf16x8_t, kv);
-        S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qB[ks], S, 0, 0, 0);
-        if constexpr (RLA) {
-          f32x8_t f = __builtin_convertvector(kb, f32x8_t);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = __expf(f[e]);
-          const bf16x8_t kh = __builtin_convertvector(f, bf16x8_t);
-          const bf16x8_t kl = __builtin_convertvector(f - __builtin_convertvector(kh, f32x8_t), bf16x8_t);
-          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qH[ks], W, 0, 0, 0);
-          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qL[ks], W, 0, 0, 0);
-          W = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qH[ks], W, 0, 0, 0);
-        }
-      }
-      float sv[4], mt = -INFINITY;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        sv[v] = 16 * wave + 4 * lg + v < nt ? S[v] * a.s_att : -INFINITY;
-        mt = fmaxf(mt, sv[v]);
-      }
-      mt = row4_max(mt);
-      const float m_new = fmaxf(m_run, mt);
-      const float mu = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __expf(m_run - mu);  // 0 before the first valid token
-      float pv[4], ls = 0.f;
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        pv[v] = __expf(sv[v] - mu);
-        ls += pv[v];
-      }
-      l_run = l_run * alpha + ls;
-      m_run = m_new;
-      // high part: round to nearest even (v_cvt_pk_bf16_f32); low part: the
-      // remainder, exact in fp32, rounded the same way
-      const f32x4v_t pvv = f32x4v_t{pv[0], pv[1], pv[2], pv[3]};
-      const bf16x4_t phb = __builtin_convertvector(pvv, bf16x4_t);
-      const bf16x4_t plb = __builtin_convertvector(pvv - __builtin_convertvector(phb, f32x4v_t), bf16x4_t);
-      const s16x4_t ph = __builtin_bit_cast(s16x4_t, phb);
-      const s16x4_t pl = __builtin_bit_cast(s16x4_t, plb);
-      // the running maximum moved for no lane: the accumulators keep their scale
-      const bool rescale = __any(alpha != 1.f);
-      s16x4_t wh = s16x4_t{0, 0, 0, 0}, wl = s16x4_t{0, 0, 0, 0};
-      if constexpr (RLA) {  // tokens past the list weigh nothing
-        f32x4v_t wv;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          wv[v] = 16 * wave + 4 * lg + v < nt ? W[v] : 0.f;
-          rden += wv[v];
-        }
-        const bf16x4_t bh = __builtin_convertvector(wv, bf16x4_t);
-        const bf16x4_t bl = __builtin_convertvector(wv - __builtin_convertvector(bh, f32x4v_t), bf16x4_t);
-        wh = __builtin_bit_cast(s16x4_t, bh);
-        wl = __builtin_bit_cast(s16x4_t, bl);
-      }
-      if (rescale) {  // (wave-uniform: a branch, not a select per accumulator)
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) oacc[mb] *= alpha;
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const char* vcol = Vs + (16 * wave + 4 * lg) * PITCH + (16 * mb + hq) * 2;
-        const uint32_t v0 = *reinterpret_cast<const uint16_t*>(vcol);
-        const uint32_t v1 = *reinterpret_cast<const uint16_t*>(vcol + PITCH);
-        const uint32_t v2 = *reinterpret_cast<const uint16_t*>(vcol + 2 * PITCH);
-        const uint32_t v3 = *reinterpret_cast<const uint16_t*>(vcol + 3 * PITCH);
-        const s16x4_t av = __builtin_bit_cast(s16x4_t, make_uint2(v0 | (v1 << 16), v2 | (v3 << 16)));
-        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, ph, oacc[mb], 0, 0, 0);
-        oacc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, pl, oacc[mb], 0, 0, 0);
-        if constexpr (RLA) {
-          racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wh, racc[mb], 0, 0, 0);
-          racc[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(av, wl, racc[mb], 0, 0, 0);
-        }
-      }
-    };
-    int32_t ts = 0;
-    if (n_att > 0) {
-      gather(read_ids(0), kA, vA);
-      gather(read_ids(TM), kB, vB);
-      ids_t nx = read_ids(2 * TM);
-      for (; ts + TM < n_att; ts += 2 * TM) {  // both tiles of the pair hold tokens
-        stage(kA, vA);
-        gather(nx, kA, vA);
-        nx = read_ids(ts + 3 * TM);
-        compute(ts);
-        stage(kB, vB);
-        gather(nx, kB, vB);
-        nx = read_ids(ts + 4 * TM);
-        compute(ts + TM);
-      }
-      if (ts < n_att) {  // an odd last tile
-        stage(kA, vA);
-        compute(ts);
-      }
-    }
+    n_cur = n_att;
+    run_tiles();
     stamp(a, 8);
     // merge the waves: lane (lg, hq) holds O^T[16 mb + 4 lg + v][hq]
     float lw = l_run;
