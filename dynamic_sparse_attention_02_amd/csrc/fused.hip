@@ -27,9 +27,11 @@
 // Page mode runs the same phases over a sequence's 64-token pages: Taylor
 // page scores from the mean and diagonal variance of each page's keys
 // ("SPLA", section 2.1) in phase 1, a top-k of pages in phase 2, and in
-// phase 3 every workgroup publishes its selected pages, meets the others and
-// reads the row's page list, then attends an even slice of the row's tokens
-// (the selected pages are few and may sit in one workgroup's range).
+// phase 3 every workgroup attends the tokens of its own selected pages (a
+// row's selected pages are few; exchanging them to split the tokens evenly
+// cost a barrier more than the imbalance costs).  In both modes the first
+// tiles of a workgroup's surely selected candidates (above the level-1
+// crossing bin) are attended while the level-2 barrier completes.
 // Selection-only mode takes the scores from memory in phase 1 and stops
 // after the index list.
 #include <map>
@@ -106,7 +108,6 @@ struct FusedArgs {
   float* part_rden;       // [rows][nb][G]
   uint64_t* trace;        // [rows * nb][kTraceSlots] phase timestamps (diagnostics)
   uint64_t* mflag;        // [rows][kMaxNB] marker bit 32 | own maximum score key
-  int32_t* plist;         // page mode: [rows][nb][kFusedMaxPages][2] own pages (sequence, pool)
   uint32_t* flags;        // [rows][kMaxNB] barrier arrival flags (barriers passed)
 };
 
@@ -300,6 +301,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   // page mode: the own selected pages in index order (sequence page, pool page)
   __shared__ int32_t s_spj[kFusedMaxPages], s_spp[kFusedMaxPages];
   __shared__ uint32_t s_np;
+  // page mode: which own pages were attended early; the pool pages left
+  __shared__ uint32_t s_spe[kFusedMaxPages];
+  __shared__ int32_t s_spa[kFusedMaxPages];
 
   stamp(a, 0);
   const int32_t* pt = a.page_table + (int64_t)b * s.max_pages;
@@ -726,30 +730,54 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   // (about the barrier's latency; more would delay the row's resolve);
   // phase 3 then attends the rest.  Which tokens go early depends on the
   // scores only, so the result stays deterministic.
-  constexpr bool kEarly = sizeof(T) == 2 && !PAGES && !SEL;
+  // Page mode likewise, a candidate being a page: the first kEarlyTiles
+  // surely selected pages go early.
+  constexpr bool kEarly = sizeof(T) == 2 && !SEL;
   constexpr int kEarlyTiles = 3;
-  uint32_t early_bits = 0;  // bit u: token u of this thread was attended early
+  uint32_t early_bits = 0;  // bit u: candidate u of this thread was attended early
+  __shared__ int32_t s_epp[kEarlyTiles], s_epl[kEarlyTiles];  // page mode: early pages (pool page, tokens)
   auto early_attend = [&](uint32_t pre1) __attribute__((always_inline)) {
     uint32_t cnt = 0, sure = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
       const int32_t j = j0 + u * kNT + tid;
-      const bool b = j < n && !(j < a.n_sink || j >= n - a.n_window) && (key[u] >> 20) > pre1;
+      const bool b = j < n && (PAGES || !(j < a.n_sink || j >= n - a.n_window)) && (key[u] >> 20) > pre1;
       sure |= b ? (1u << u) : 0u;
       cnt += b ? 1u : 0u;
     }
     uint32_t tot;
     uint32_t o = blk_scan<uint32_t>(cnt, red_u, tot);
-    const uint32_t cap = (uint32_t)(kEarlyTiles * TM);
+    if constexpr (PAGES) {
+      // pages in index order; only the sequence's last page (the last of
+      // them) may be partial, so page k's tokens start at 64 k
 #pragma unroll
-    for (int u = 0; u < TPT; ++u)
-      if (((sure >> u) & 1u) && o < cap) {
-        const int32_t jl = u * kNT + tid;  // j - j0
-        my_list[o++] = (uint32_t)(((int64_t)s_pt[jl >> 6] * s.Hkv + g) * kPage + (jl & 63));
-        early_bits |= 1u << u;
-      }
-    __syncthreads();
-    n_cur = (int32_t)min(tot, cap);
+      for (int u = 0; u < TPT; ++u)
+        if (((sure >> u) & 1u) && o < (uint32_t)kEarlyTiles) {
+          const int32_t j = j0 + u * kNT + tid;
+          s_epp[o] = (int32_t)clamp_page(pt[j], s.n_pool_pages);
+          s_epl[o] = min(kPage, L - j * kPage);
+          ++o;
+          early_bits |= 1u << u;
+        }
+      __syncthreads();
+      const uint32_t ne = min(tot, (uint32_t)kEarlyTiles);
+      const int32_t ntok = ne == 0 ? 0 : (int32_t)(ne - 1) * kPage + s_epl[ne - 1];
+      for (int32_t e = tid; e < ntok; e += kNT)
+        my_list[e] = (uint32_t)(((int64_t)s_epp[e / kPage] * s.Hkv + g) * kPage + (e % kPage));
+      __syncthreads();
+      n_cur = ntok;
+    } else {
+      const uint32_t cap = (uint32_t)(kEarlyTiles * TM);
+#pragma unroll
+      for (int u = 0; u < TPT; ++u)
+        if (((sure >> u) & 1u) && o < cap) {
+          const int32_t jl = u * kNT + tid;  // j - j0
+          my_list[o++] = (uint32_t)(((int64_t)s_pt[jl >> 6] * s.Hkv + g) * kPage + (jl & 63));
+          early_bits |= 1u << u;
+        }
+      __syncthreads();
+      n_cur = (int32_t)min(tot, cap);
+    }
     run_tiles();
   };
 
@@ -1022,7 +1050,9 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
   }
   if constexpr (PAGES) {
     // own selected pages in index order; each expands to its tokens (all 64
-    // but the sequence's last page, which is also the last in this order)
+    // but the sequence's last page, which is also the last in this order).
+    // A workgroup attends its own pages (those not attended early) and
+    // publishes its token count for the ordered list.
     uint32_t run = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
@@ -1040,55 +1070,27 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
         if (k < (uint32_t)kFusedMaxPages) {  // at most top_k <= kFusedMaxPages pages per row
           s_spj[k] = j;
           s_spp[k] = (int32_t)clamp_page(pt[j], s.n_pool_pages);
+          s_spe[k] = (early_bits >> u) & 1u;
         }
       }
       run += round_tot;
       __syncthreads();
     }
-    // publish the own pages, meet, and gather the row's page list in index
-    // order (workgroups own ascending page ranges); the row's tokens are
-    // then split evenly over its workgroups for the attention
     const uint32_t np = run < (uint32_t)kFusedMaxPages ? run : (uint32_t)kFusedMaxPages;
-    int32_t* pl = a.plist + ((int64_t)row * NB + bi) * 2 * kFusedMaxPages;
-    if (tid < np) {
-      __hip_atomic_store(&pl[2 * tid], s_spj[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&pl[2 * tid + 1], s_spp[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      // tokens of the own pages (output) and of those left to attend
+      uint32_t na = 0;
+      for (uint32_t k = 0; k < np; ++k)
+        if (!s_spe[k]) s_spa[na++] = s_spp[k];
+      const uint32_t last = np == 0 ? 0u : (uint32_t)min(kPage, L - s_spj[np - 1] * kPage);
+      const uint32_t tok_out = np == 0 ? 0u : (np - 1) * kPage + last;
+      s_np = np;
+      s_cnt = na == 0 ? 0u : (na - 1) * kPage + (s_spe[np - 1] ? (uint32_t)kPage : last);
+      __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], tok_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid == 0) __hip_atomic_store(&a.blk_sel[(int64_t)row * NB + bi], np, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    row_barrier(flags, NB, bi, ++epoch, err);
-    {
-      // each workgroup's count and first page in one round trip (most
-      // workgroups hold at most one selected page)
-      const int32_t* src = a.plist + ((int64_t)row * NB + tid) * 2 * kFusedMaxPages;
-      uint32_t c = 0;
-      int32_t pj = 0, pp = 0;
-      if (tid < NB) {
-        c = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pj = __hip_atomic_load(&src[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        pp = __hip_atomic_load(&src[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      uint32_t tot;
-      const uint32_t off = blk_scan<uint32_t>(c, red_u, tot);
-      if (c > 0 && off < (uint32_t)kFusedMaxPages) {
-        s_spj[off] = pj;
-        s_spp[off] = pp;
-      }
-      for (uint32_t i2 = 1; i2 < c && off + i2 < (uint32_t)kFusedMaxPages; ++i2) {
-        s_spj[off + i2] = __hip_atomic_load(&src[2 * i2], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_spp[off + i2] = __hip_atomic_load(&src[2 * i2 + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      if (tid == 0) s_np = tot < (uint32_t)kFusedMaxPages ? tot : (uint32_t)kFusedMaxPages;
-      __syncthreads();
-    }
-    const uint32_t npr = s_np;
-    // every listed page holds 64 tokens but the sequence's last page
-    const uint32_t tot_tok = npr == 0 ? 0u
-        : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
-    const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
-    const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
-    for (uint32_t e = t0 + tid; e < t1; e += kNT)
-      my_list[e - t0] = (uint32_t)(((int64_t)s_spp[e / kPage] * s.Hkv + g) * kPage + (e % kPage));
-    if (tid == 0) s_cnt = t1 - t0;
+    __syncthreads();
+    for (uint32_t e = tid; e < s_cnt; e += kNT)
+      my_list[e] = (uint32_t)(((int64_t)s_spa[e / kPage] * s.Hkv + g) * kPage + (e % kPage));
     __syncthreads();
   } else if constexpr (SEL) {
     // the own selected count, for the ordered list
@@ -1365,8 +1367,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     // the workgroups' selected counts, loaded now and used after the merge
     // (so their round trip overlaps the partials')
     uint32_t bsel = 0;
-    if constexpr (!PAGES)
-      if (tid < NB) bsel = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid < NB) bsel = __hip_atomic_load(&a.blk_sel[(int64_t)row * NB + tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if constexpr (!SEL) {
     // outputs [bi * opb, (bi + 1) * opb) of the row's G * D values
     const int n_out = G * D;
@@ -1457,7 +1458,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
       }
     }
     }
-    if constexpr (!PAGES) {
+    {
       const uint32_t vt = bsel, vb = tid < bi ? bsel : 0u;
       uint32_t tb, tt;
       blk_scan<uint32_t>(vb, red_u, tb);
@@ -1470,16 +1471,14 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
     }
     int32_t* outl = a.idx + (int64_t)row * a.cap;
     if constexpr (PAGES) {
-      // the own token slice of the row's list (the attention's slice)
-      const uint32_t npr = s_np;
-      const uint32_t tot_tok = npr == 0 ? 0u
-          : npr * kPage - (uint32_t)(kPage - min(kPage, L - s_spj[npr - 1] * kPage));
-      const uint32_t t0 = (uint32_t)(((uint64_t)tot_tok * bi) / NB);
-      const uint32_t t1 = (uint32_t)(((uint64_t)tot_tok * (bi + 1)) / NB);
-      for (uint32_t e = t0 + tid; e < t1 && e < (uint32_t)a.cap; e += kNT)
-        outl[e] = s_spj[e / kPage] * kPage + (int32_t)(e % kPage);
-      if (tid == 0) s_total = tot_tok;
-      __syncthreads();
+      // the own pages' tokens, in index order, after the lower workgroups'
+      const uint32_t np = s_np;
+      const uint32_t tok_out = np == 0 ? 0u
+          : (np - 1) * kPage + (uint32_t)min(kPage, L - s_spj[np - 1] * kPage);
+      for (uint32_t e = tid; e < tok_out; e += kNT) {
+        const uint32_t pos = s_base + e;
+        if (pos < (uint32_t)a.cap) outl[pos] = s_spj[e / kPage] * kPage + (int32_t)(e % kPage);
+      }
     } else {
     // every round's per-wave counts first, so one barrier serves all rounds
     uint64_t msk[TPT];
@@ -1542,7 +1541,7 @@ __global__ void __launch_bounds__(kNT) k_decode_fused(FusedArgs a) {
 // be zero when a launch starts and is zero again when it ends (row control
 // words, level histograms, barrier flags); it is laid out for rows_cap rows
 // and a launch uses the first rows of it, so its offsets do not depend on
-// the launch's shape.  The data part (counts, partial outputs, page lists,
+// the launch's shape.  The data part (counts, partial outputs,
 // phase stamps) is written before it is read.
 size_t fused_zero_bytes(int32_t rows_cap) {
   size_t b = 0;
@@ -1564,7 +1563,6 @@ size_t fused_data_bytes(int32_t rows, int32_t nb, int32_t G, int32_t D) {
   b += align_up(sizeof(float) * rows * nb * G * 2, 256);
   b += align_up(sizeof(float) * rows * nb * G * D, 256);
   b += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
-  b += align_up(sizeof(int32_t) * 2 * rows * nb * kFusedMaxPages, 256);
   return b;
 }
 
@@ -1696,8 +1694,7 @@ void fused_ws(FusedArgs& a, void* ws, void* zero, int rows, int nb, int G, int D
   a.blk_eq = (uint32_t*)w;      w += align_up(sizeof(uint32_t) * rows * nb, 256);
   a.part_ml = (float*)w;        w += align_up(sizeof(float) * rows * nb * G * 2, 256);
   a.part_o = (float*)w;         w += align_up(sizeof(float) * rows * nb * G * D, 256);
-  a.trace = (uint64_t*)w;       w += align_up(sizeof(uint64_t) * rows * nb * kTraceSlots, 256);
-  a.plist = (int32_t*)w;
+  a.trace = (uint64_t*)w;
 }
 
 }  // namespace
