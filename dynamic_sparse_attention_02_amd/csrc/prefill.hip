@@ -4,9 +4,12 @@
 // section 2.2: one head-collapsed indexer channel).
 //
 // Selection: per (query block, group) the block-collapsed indexer query is
-// formed (sum of the block's queries per head, then projected), scores over
-// the keys of all earlier blocks are written for a slab of query blocks, and
-// the row-resident radix select keeps the top k of each row.
+// formed (sum of the block's queries per head, then projected).  With bf16
+// indexer keys the scores over the keys of all earlier blocks are formed on
+// the matrix cores against a sampled per-row threshold, and only the hits
+// (a few thousand per row) reach the exact top-k; otherwise the scores of a
+// slab of query blocks are written and the row-resident radix select keeps
+// the top k of each row.
 //
 // Attention: one workgroup per (query block, group); each wave owns one query
 // head and 32 of the block's 64 queries (two waves per head, so a wave needs
@@ -601,6 +604,573 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   }
 }
 
+// ---------------------------------------------------------------------------
+// Top-k rows with bf16 indexer keys (k <= kHitMaxK): three launches per slab
+// instead of one fp32 score per candidate written and read back.
+//   k_pf_thresh: per row, a threshold lo from a sample of the row (the scores
+//     of every stride-th 16-candidate tile): the 24-bit key floor at which ks
+//     sampled keys are reached from the top, ks set so that the whole row
+//     holds between k and kHitCap keys >= lo except with negligible
+//     probability.  Rows of at most kHitCap candidates take lo = 0.
+//   k_pf_hits: the scores of 64 rows x 256 candidates per workgroup on the
+//     matrix cores, written as a hit bitmap (key >= lo) plus the keys of the
+//     first kSlotCap hits of each (row, 256-candidate tile).
+//   k_pf_select: per row, the exact top k among the hits: the hit list from
+//     the bitmap and the stored keys (a tile with more hits has its keys
+//     recomputed), then the radix levels over the list.  A row whose hits do
+//     not bracket k (fewer than k, or more than kHitCap) is resolved over all
+//     its candidates, the keys recomputed tile by tile.
+// A score is one matrix-core product (v_mfma_f32_16x16x32_bf16, fp32
+// accumulate) wherever it is formed: the block's indexer query, split into a
+// bf16 high part and the bf16 rounding of the remainder (16 significant
+// bits), sits in row (blk - blk0) mod 16 of the A operand and the candidate's
+// key in column c mod 16 of the B operand, with the same k order (high part
+// against the 16 key values, then low part), in both k_pf_hits and
+// k_pf_select, so both see the same float for every candidate.
+// ---------------------------------------------------------------------------
+constexpr int kHitCap = 4096;      // hits a row's exact selection holds in LDS
+constexpr int kSlotCap = 64;       // keys stored per (row, 256-candidate tile)
+constexpr int kHitSample = 16384;  // sampled candidates per row at most
+constexpr int kSelNT = 512;        // threads of k_pf_thresh and k_pf_select
+constexpr int kHitMaxK = 2048;     // largest k the hit path takes
+typedef __attribute__((ext_vector_type(8))) float f32x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// A operand of the score product: lane l holds row l % 16's k-slice
+// 8 (l / 16) .. + 8, i.e. q[0..8) and q[8..16) of the high part for slices 0
+// and 1, of the low part for slices 2 and 3 (zero when !valid).
+__device__ __forceinline__ bf16x8_t split_query(const float* __restrict__ q16, int lane, bool valid) {
+  const int lg = lane >> 4;
+  f32x8_t f = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const float4 a = *reinterpret_cast<const float4*>(q16 + 8 * (lg & 1));
+    const float4 b = *reinterpret_cast<const float4*>(q16 + 8 * (lg & 1) + 4);
+    f = f32x8_t{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  }
+  const bf16x8_t hi = __builtin_convertvector(f, bf16x8_t);
+  if (lg < 2) return hi;
+  return __builtin_convertvector(f - __builtin_convertvector(hi, f32x8_t), bf16x8_t);
+}
+
+// The U 16-candidate tiles from cb (a multiple of 16) against the A
+// operand: acc[u] holds the products of candidate cb + 16 u + (lane % 16)
+// with rows 4 (lane / 16) + i.  A tile's 16 candidates share one page, so
+// its page id is one uniform load; the key loads are branch-free (a tile
+// past lim reads the last valid page, a candidate past lim its page's row)
+// and zeroed afterwards, so all U of them are in flight together.
+template <int U>
+__device__ __forceinline__ void score_tiles(const bf16_raw* __restrict__ kidx,
+                                            const int32_t* __restrict__ pt, const Shape& s, int g,
+                                            int32_t cb, int32_t lim, bf16x8_t qa, int lane,
+                                            f32x4_t (&acc)[U]) {
+  const int col = lane & 15;
+  const int32_t plast = lim > 0 ? (lim - 1) >> 6 : 0;
+  int64_t page[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t pi = (cb + 16 * u) >> 6;
+    page[u] = clamp_page(pt[pi < plast ? pi : plast], s.n_pool_pages);
+  }
+  uint4 kv[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t c = cb + 16 * u + col;
+    kv[u] = *reinterpret_cast<const uint4*>(kidx + ((page[u] * s.Hkv + g) * kPage + (c & 63)) * kRank +
+                                            8 * ((lane >> 4) & 1));
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const bool ok = cb + 16 * u + col < lim;
+    const uint4 w = ok ? kv[u] : make_uint4(0u, 0u, 0u, 0u);
+    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, __builtin_bit_cast(bf16x8_t, w),
+                                                     f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+}
+
+// Exclusive scan over the kSelNT threads.
+__device__ __forceinline__ uint32_t sel_scan(uint32_t v, uint32_t* red, uint32_t& total) {
+  constexpr int NW = kSelNT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  uint32_t off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t x = red[i];
+    off += i < w ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  total = tot;
+  return off + inc - v;
+}
+
+// The bin of hc[0, nb) where the count from the top bin down reaches need
+// (1 <= need): *bin (0xffffffff if the bins hold fewer) and *before, the
+// count of the bins above it.
+__device__ __forceinline__ void top_bin(const uint32_t* hc, int nb, uint32_t need, uint32_t* red,
+                                        uint32_t* bin, uint32_t* before) {
+  const int t = threadIdx.x;
+  const int per = nb / kSelNT > 0 ? nb / kSelNT : 1;
+  const bool owns = t * per < nb;
+  uint32_t c = 0;
+  if (owns)
+    for (int e = 0; e < per; ++e) c += hc[nb - 1 - (t * per + e)];
+  if (t == 0) *bin = 0xffffffffu;
+  uint32_t tot;
+  uint32_t cb = sel_scan(c, red, tot);
+  if (owns)
+    for (int e = 0; e < per; ++e) {
+      const int b = nb - 1 - (t * per + e);
+      const uint32_t v = hc[b];
+      if (cb < need && cb + v >= need) {
+        *bin = (uint32_t)b;
+        *before = cb;
+      }
+      cb += v;
+    }
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(kSelNT)
+k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
+            const float* __restrict__ qcb, int32_t blk0, int32_t bsel, int32_t self, Shape s,
+            int32_t k, int32_t stride, uint32_t* __restrict__ lo_out) {
+  constexpr int kPer = kHitSample / kSelNT;
+  const int row = blockIdx.x, t = threadIdx.x;
+  const int g = row % s.Hkv;
+  const int32_t blk = blk0 + row / s.Hkv;
+  const int32_t n = bsel * blk + self;
+  if (n <= kHitCap) {
+    if (t == 0) lo_out[row] = 0u;
+    return;
+  }
+  const int32_t ntl = (n + 15) >> 4;               // 16-candidate tiles
+  const int32_t nst = (ntl + stride - 1) / stride;  // sampled tiles: 16 nst <= kHitSample
+  const int32_t last = (nst - 1) * stride;
+  const int32_t m = nst * 16 - (last == ntl - 1 ? ntl * 16 - n : 0);  // sampled candidates
+  const float kf = (float)k * (float)m / (float)n;
+  const uint32_t ks = (uint32_t)ceilf(kf + 5.5f * sqrtf(kf) + 6.f);
+  if (ks >= (uint32_t)m) {
+    if (t == 0) lo_out[row] = 0u;
+    return;
+  }
+  __shared__ float qs[kRank];
+  __shared__ uint32_t hc[4096];
+  __shared__ uint32_t red[kSelNT / 64];
+  __shared__ uint32_t s_bin, s_bef;
+  if (t < kRank) qs[t] = qcb[((int64_t)blk * s.Hkv + g) * kRank + t];
+  for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
+  __syncthreads();
+  uint32_t key[kPer];
+  uint32_t valid = 0u;
+#pragma unroll
+  for (int e0 = 0; e0 < kPer; e0 += 8) {
+    // branch-free loads (a position past the sample reads candidate n - 1)
+    int32_t cc[8];
+    int64_t page[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int32_t i = (e0 + e) * kSelNT + t;  // sample position
+      const int32_t c = (((i >> 4) * stride) << 4) + (i & 15);
+      const bool ok = i < nst * 16 && c < n;
+      valid |= ok ? 1u << (e0 + e) : 0u;
+      cc[e] = ok ? c : n - 1;
+      page[e] = clamp_page(pt[cc[e] >> 6], s.n_pool_pages);
+    }
+    uint4 va[8], vb[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint4* v = reinterpret_cast<const uint4*>(kidx + ((page[e] * s.Hkv + g) * kPage + (cc[e] & 63)) * kRank);
+      va[e] = v[0];
+      vb[e] = v[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u[8] = {va[e].x, va[e].y, va[e].z, va[e].w, vb[e].x, vb[e].y, vb[e].z, vb[e].w};
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        a = fmaf(qs[2 * j], __uint_as_float(u[j] << 16), a);
+        a = fmaf(qs[2 * j + 1], __uint_as_float(u[j] & 0xffff0000u), a);
+      }
+      key[e0 + e] = score_key(a);
+      if ((valid >> (e0 + e)) & 1u) atomicAdd(&hc[key[e0 + e] >> 20], 1u);
+    }
+  }
+  __syncthreads();
+  top_bin(hc, 4096, ks, red, &s_bin, &s_bef);
+  const uint32_t b1 = s_bin, bef1 = s_bef;
+  if (b1 == 0xffffffffu) {  // not reached (ks < m): take every candidate
+    if (t == 0) lo_out[row] = 0u;
+    return;
+  }
+  for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (((valid >> e) & 1u) && (key[e] >> 20) == b1) atomicAdd(&hc[(key[e] >> 8) & 0xfffu], 1u);
+  __syncthreads();
+  top_bin(hc, 4096, ks - bef1, red, &s_bin, &s_bef);
+  if (t == 0) lo_out[row] = (b1 << 20) | ((s_bin == 0xffffffffu ? 0u : s_bin) << 8);
+}
+
+__global__ void __launch_bounds__(256)
+k_pf_hits(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
+          const float* __restrict__ qcb, const uint32_t* __restrict__ lo_in, int32_t blk0,
+          int32_t blk1, int32_t bsel, int32_t self, Shape s, int32_t tpr,
+          uint32_t* __restrict__ bits, uint32_t* __restrict__ slots) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, lg = lane >> 4;
+  const int g = blockIdx.z, x = blockIdx.x;
+  const int32_t bfirst = blk0 + (int32_t)blockIdx.y * 64 + wave * 16;  // this wave's 16 rows
+  if (bfirst >= blk1) return;
+  const int32_t blast = min(blk1, bfirst + 16) - 1;
+  const int32_t cb = 256 * x;
+  if (cb >= bsel * blast + self) return;  // no row of the wave has candidates here
+  __shared__ uint32_t stage[4][16][256];  // the keys, [row][candidate - cb]
+  __shared__ uint64_t msk[4][16][4];      // hit ballots, [tile][i]: bit 16 q + col = row 4 q + i
+  const int32_t bq = bfirst + col;
+  const bf16x8_t qa = split_query(qcb + ((int64_t)(bq < blk1 ? bq : bfirst) * s.Hkv + g) * kRank, lane, bq < blk1);
+  f32x4_t acc[16];
+  score_tiles<16>(kidx, pt, s, g, cb, bsel * blast + self, qa, lane, acc);
+  int32_t n_i[4];
+  uint32_t lo_i[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int32_t bb = bfirst + 4 * lg + i;
+    const uint32_t lv = lo_in[(int64_t)((bb < blk1 ? bb : blast) - blk0) * s.Hkv + g];
+    n_i[i] = bb < blk1 ? bsel * bb + self : 0;
+    lo_i[i] = bb < blk1 ? lv : 0xffffffffu;
+  }
+  // every lane stores the same (uniform) ballot; when every row of the wave
+  // holds all 256 candidates the bound check drops out
+  if (cb + 256 <= bsel * bfirst + self) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t key = score_key(acc[u][i]);
+        stage[wave][4 * lg + i][16 * u + col] = key;
+        msk[wave][u][i] = __builtin_amdgcn_ballot_w64(key >= lo_i[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t key = score_key(acc[u][i]);
+        stage[wave][4 * lg + i][16 * u + col] = key;
+        msk[wave][u][i] = __builtin_amdgcn_ballot_w64(cb + 16 * u + col < n_i[i] && key >= lo_i[i]);
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // lane L holds bitmap word p = L % 8 of rows L / 8 (wv0) and 8 + L / 8
+  // (wv1): tiles 2p (low half) and 2p + 1 (high half)
+  const int p = lane & 7;
+  uint32_t wv0, wv1;
+  {
+    const int R0 = lane >> 3, R1 = 8 + (lane >> 3);
+    const uint64_t a0 = msk[wave][2 * p][R0 & 3], b0 = msk[wave][2 * p + 1][R0 & 3];
+    const uint64_t a1 = msk[wave][2 * p][R1 & 3], b1 = msk[wave][2 * p + 1][R1 & 3];
+    const int s0 = 16 * (R0 >> 2), s1 = 16 * (R1 >> 2);
+    wv0 = (uint32_t)((a0 >> s0) & 0xffffu) | ((uint32_t)((b0 >> s0) & 0xffffu) << 16);
+    wv1 = (uint32_t)((a1 >> s1) & 0xffffu) | ((uint32_t)((b1 >> s1) & 0xffffu) << 16);
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int R = 8 * h + (lane >> 3);
+    const uint32_t w = h ? wv1 : wv0;
+    // hits of this row in the words before this one (the row's 8 lanes)
+    const uint32_t pc = (uint32_t)__popc(w);
+    uint32_t inc = pc;
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_up((int)inc, d, 8);
+      if (p >= d) inc += v;
+    }
+    const int32_t bb = bfirst + R;
+    if (bb < blk1 && cb < bsel * bb + self) {
+      const int64_t r = (int64_t)(bb - blk0) * s.Hkv + g;
+      bits[(r * tpr + x) * 8 + p] = w;
+      uint32_t e = inc - pc, ww = w;
+      uint32_t* sl = slots + (r * tpr + x) * kSlotCap;
+      while (ww != 0u && e < (uint32_t)kSlotCap) {
+        const int b = __ffs(ww) - 1;
+        ww &= ww - 1u;
+        sl[e++] = stage[wave][R][32 * p + b];
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kSelNT)
+k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
+            const float* __restrict__ qcb, const uint32_t* __restrict__ bits,
+            const uint32_t* __restrict__ slots, int32_t blk0, int32_t bsel, int32_t self, Shape s,
+            int32_t tpr, int32_t k, int32_t n_window, int32_t* __restrict__ idx_out,
+            int32_t* __restrict__ count_out, int32_t cap) {
+  constexpr int NT = kSelNT, NW = NT / 64;
+  constexpr uint32_t kSearchM = 0, kGEM = 1, kTiesM = 2;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int col = lane & 15, lg = lane >> 4;
+  const int g = row % s.Hkv;
+  const int32_t blk = blk0 + row / s.Hkv;
+  const int32_t n = bsel * blk + self;  // <= 256 kSelNT (host-checked)
+  const int pr = (blk - blk0) & 15;     // the block's row in the score product
+  const int32_t ntr = (n + 255) >> 8;   // 256-candidate tiles of the row: thread t owns tile t
+  __shared__ uint32_t l_idx[kHitCap], l_key[kHitCap];
+  __shared__ uint32_t hc[4096];
+  __shared__ uint32_t sel[NT * 8];  // selection bitmap, words [8 t, 8 t + 8) = tile t
+  __shared__ uint32_t toff[NT], ovf[NT];
+  __shared__ uint32_t red[NW];
+  __shared__ uint32_t s_novf, s_mode, s_pre, s_need, s_thr, s_neq, s_bin, s_bef;
+  uint32_t* const tie = l_key;  // all-candidate path: tie bitmap over the list arrays
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sel[8 * t + e] = 0u;
+  if (t == 0) {
+    s_novf = 0u;
+    s_mode = kSearchM;
+    s_pre = 0u;
+    s_need = (uint32_t)k;
+    s_thr = 0u;
+    s_neq = 0u;
+  }
+  uint32_t w[8];
+  uint32_t cnt = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = 0u;
+  if (t < ntr) {
+    const uint4* bp = reinterpret_cast<const uint4*>(bits + ((int64_t)row * tpr + t) * 8);
+    const uint4 a = bp[0], b = bp[1];
+    w[0] = a.x; w[1] = a.y; w[2] = a.z; w[3] = a.w;
+    w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) cnt += (uint32_t)__popc(w[e]);
+  }
+  uint32_t H;
+  const uint32_t off = sel_scan(cnt, red, H);  // (its barriers publish the set-up above)
+  const bool take_all = k >= n;
+  const bool fast = !take_all && H >= (uint32_t)k && H <= (uint32_t)kHitCap;
+  const bf16x8_t qa = split_query(qcb + ((int64_t)blk * s.Hkv + g) * kRank, lane, col == pr);
+  // keys of the row's candidates recomputed, tile by tile over the waves:
+  // fn(candidate, key) in the lanes that hold the block's row
+  auto for_all_keys = [&](auto&& fn) {
+    for (int32_t th = wave; th < 2 * ntr; th += NW) {  // half tiles of 128 candidates
+      f32x4_t acc[8];
+      score_tiles<8>(kidx, pt, s, g, 128 * th, n, qa, lane, acc);
+      if (lg == (pr >> 2)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int32_t c = 128 * th + 16 * u + col;
+          const float v = (pr & 3) == 0 ? acc[u][0] : ((pr & 3) == 1 ? acc[u][1] : ((pr & 3) == 2 ? acc[u][2] : acc[u][3]));
+          if (c < n) fn(c, score_key(v));
+        }
+      }
+    }
+  };
+  if (fast) {
+    // ---- the hit list, in candidate order ----
+    if (t < ntr) {
+      toff[t] = off;
+      const bool stored = cnt <= (uint32_t)kSlotCap;
+      if (stored) {  // the stored keys, 32 at a time with all loads in flight
+        const uint4* sl = reinterpret_cast<const uint4*>(slots + ((int64_t)row * tpr + t) * kSlotCap);
+#pragma unroll
+        for (int h = 0; h < kSlotCap / 32; ++h) {
+          if (cnt > 32u * h) {
+            uint4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = sl[8 * h + j];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const uint32_t e = 32u * h + 4u * j;
+              if (e < cnt) l_key[off + e] = v[j].x;
+              if (e + 1 < cnt) l_key[off + e + 1] = v[j].y;
+              if (e + 2 < cnt) l_key[off + e + 2] = v[j].z;
+              if (e + 3 < cnt) l_key[off + e + 3] = v[j].w;
+            }
+          }
+        }
+      }
+      uint32_t e = 0u;
+#pragma unroll
+      for (int wi = 0; wi < 8; ++wi) {
+        uint32_t ww = w[wi];
+        while (ww != 0u) {
+          const int b = __ffs(ww) - 1;
+          ww &= ww - 1u;
+          l_idx[off + e] = (uint32_t)(256 * t + 32 * wi + b);
+          ++e;
+        }
+      }
+      if (!stored) ovf[atomicAdd(&s_novf, 1u)] = (uint32_t)t;
+    }
+    __syncthreads();
+    // tiles with more hits than stored keys: recompute their keys
+    for (uint32_t o = (uint32_t)wave; o < s_novf; o += NW) {
+      const int32_t tt = (int32_t)ovf[o];
+      const uint4* bp = reinterpret_cast<const uint4*>(bits + ((int64_t)row * tpr + tt) * 8);
+      const uint4 a = bp[0], b = bp[1];
+      const uint32_t tw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      for (int hf = 0; hf < 2; ++hf) {
+      f32x4_t acc[8];
+      score_tiles<8>(kidx, pt, s, g, 256 * tt + 128 * hf, n, qa, lane, acc);
+      if (lg == (pr >> 2)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int q = 128 * hf + 16 * u + col;  // candidate within the tile
+          if ((tw[q >> 5] >> (q & 31)) & 1u) {
+            uint32_t rank = (uint32_t)__popc(tw[q >> 5] & ((1u << (q & 31)) - 1u));
+#pragma unroll
+            for (int wi = 0; wi < 8; ++wi) rank += wi < (q >> 5) ? (uint32_t)__popc(tw[wi]) : 0u;
+            const float v = (pr & 3) == 0 ? acc[u][0] : ((pr & 3) == 1 ? acc[u][1] : ((pr & 3) == 2 ? acc[u][2] : acc[u][3]));
+            l_key[toff[tt] + rank] = score_key(v);
+          }
+        }
+      }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- radix levels (12 + 12 + 8 bits, counts from the top) ----
+  if (!take_all) {
+    for (int level = 1; level <= 3; ++level) {
+      if (s_mode != kSearchM) break;  // block-uniform (read after a barrier)
+      const int NB = level == 3 ? 256 : 4096;
+      const uint32_t pre = s_pre;
+      for (int i = t; i < NB; i += NT) hc[i] = 0u;
+      __syncthreads();
+      auto add = [&](int32_t, uint32_t key) {
+        if (level == 1) atomicAdd(&hc[key >> 20], 1u);
+        else if (level == 2) { if ((key >> 20) == pre) atomicAdd(&hc[(key >> 8) & 0xfffu], 1u); }
+        else if ((key >> 8) == pre) atomicAdd(&hc[key & 0xffu], 1u);
+      };
+      if (fast) {
+        for (uint32_t j = (uint32_t)t; j < H; j += NT) add(0, l_key[j]);
+      } else {
+        for_all_keys(add);
+      }
+      __syncthreads();
+      top_bin(hc, NB, s_need, red, &s_bin, &s_bef);
+      if (t == 0) {
+        const uint32_t bin = s_bin;
+        if (bin == 0xffffffffu) {  // fewer candidates than k: cannot happen (k < n), take all
+          s_mode = kGEM;
+          s_thr = 0u;
+        } else {
+          const uint32_t np = level == 1 ? bin : (level == 2 ? ((pre << 12) | bin) : ((pre << 8) | bin));
+          const uint32_t floor_key = level == 1 ? (np << 20) : (level == 2 ? (np << 8) : np);
+          const uint32_t nd = s_need - s_bef;
+          if (nd == hc[bin]) {
+            s_mode = kGEM;
+            s_thr = floor_key;
+          } else if (level < 3) {
+            s_pre = np;
+            s_need = nd;
+          } else {
+            s_mode = kTiesM;
+            s_thr = floor_key;
+            s_neq = nd;
+          }
+        }
+      }
+      __syncthreads();
+    }
+    // ---- marking ----
+    const uint32_t mode = s_mode, thr = s_thr, neq = s_neq;
+    if (fast) {
+      for (uint32_t j = (uint32_t)t; j < H; j += NT) {
+        const uint32_t key = l_key[j];
+        if (key > thr || (mode == kGEM && key == thr)) atomicOr(&sel[l_idx[j] >> 5], 1u << (l_idx[j] & 31));
+      }
+      if (mode == kTiesM) {  // the neq lowest-index keys equal to thr: list order is candidate order
+        const uint32_t E = (H + NT - 1) / NT;
+        uint32_t c = 0u;
+        for (uint32_t j = E * t; j < E * t + E && j < H; ++j) c += l_key[j] == thr ? 1u : 0u;
+        uint32_t tot;
+        const uint32_t before = sel_scan(c, red, tot);
+        uint32_t left = before < neq ? neq - before : 0u;
+        for (uint32_t j = E * t; j < E * t + E && j < H && left; ++j)
+          if (l_key[j] == thr) {
+            atomicOr(&sel[l_idx[j] >> 5], 1u << (l_idx[j] & 31));
+            --left;
+          }
+      }
+    } else {
+      if (mode == kTiesM) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) tie[8 * t + e] = 0u;
+      }
+      __syncthreads();
+      for_all_keys([&](int32_t c, uint32_t key) {
+        if (key > thr || (mode == kGEM && key == thr)) atomicOr(&sel[c >> 5], 1u << (c & 31));
+        else if (mode == kTiesM && key == thr) atomicOr(&tie[c >> 5], 1u << (c & 31));
+      });
+      __syncthreads();
+      if (mode == kTiesM) {
+        uint32_t tw[8], c = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          tw[e] = tie[8 * t + e];
+          c += (uint32_t)__popc(tw[e]);
+        }
+        uint32_t tot;
+        const uint32_t before = sel_scan(c, red, tot);
+        uint32_t left = before < neq ? neq - before : 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          uint32_t b = tw[e], keep = 0u;
+          while (b != 0u && left != 0u) {
+            keep |= b & (0u - b);
+            b &= b - 1u;
+            --left;
+          }
+          sel[8 * t + e] |= keep;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- ordered compaction: thread t owns candidates [256 t, 256 t + 256) ----
+  uint32_t sw[8], c = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int32_t lo = 256 * t + 32 * e;
+    uint32_t m = 0u;
+    if (lo < n) {
+      const uint32_t vm = n - lo >= 32 ? ~0u : ((1u << (n - lo)) - 1u);
+      const int32_t ws = n - n_window;  // always-kept window [n - n_window, n)
+      uint32_t fm = 0u;
+      if (ws < lo + 32) fm = ws <= lo ? ~0u : (~0u << (ws - lo));
+      m = ((take_all ? ~0u : sel[8 * t + e]) | fm) & vm;
+    }
+    sw[e] = m;
+    c += (uint32_t)__popc(m);
+  }
+  uint32_t total;
+  uint32_t rank = sel_scan(c, red, total);
+  int32_t* out = idx_out + (int64_t)row * cap;
+  const uint32_t T = total < (uint32_t)cap ? total : (uint32_t)cap;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t b = sw[e];
+    while (b != 0u) {
+      const int j = __ffs(b) - 1;
+      b &= b - 1u;
+      if (rank < (uint32_t)cap) out[rank] = 256 * t + 32 * e + j;
+      ++rank;
+    }
+  }
+  for (int64_t o = (int64_t)T + t; o < cap; o += NT) out[o] = -1;
+  if (t == 0) count_out[row] = (int32_t)T;
+}
+
 // Selection plan: rows of query blocks (bsel = 64) or of queries (bsel = 1)
 // are scored and selected a slab at a time.
 struct PrefillSelPlan {
@@ -686,6 +1256,26 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     // logit scores go to the selection as 16-bit keys (exact scores of the
     // threshold bin are recomputed there) when its one-block rows take them
     const bool key16 = !probs && ldx <= kSelectRowMax;
+    // block rows, bf16 indexer keys and k <= kHitMaxK: sampled thresholds,
+    // hit bitmaps from the matrix cores and the exact top k over the hits
+    if (key16 && bf && b_sel > 1 && k <= kHitMaxK && ldx >= 256) {
+      const int64_t rows = (int64_t)(b1 - b0) * s.Hkv;
+      const int32_t tpr = (int32_t)((ldx + 255) / 256);
+      uint32_t* lo = (uint32_t*)xs;
+      uint32_t* bits = lo + align_up((size_t)rows, 64);
+      uint32_t* slots = bits + (size_t)rows * tpr * 8;
+      const int32_t stride = k <= 1024 ? 16 : 8;
+      k_pf_thresh<<<(unsigned)rows, kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, b0,
+                                                     b_sel, P.self, s, k, stride, lo);
+      dim3 gh((unsigned)tpr, (unsigned)((b1 - b0 + 63) / 64), (unsigned)s.Hkv);
+      k_pf_hits<<<gh, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, lo, b0, b1, b_sel,
+                                    P.self, s, tpr, bits, slots);
+      k_pf_select<<<(unsigned)rows, kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, bits,
+                                                     slots, b0, b_sel, P.self, s, tpr, k, P.self,
+                                                     idx + (int64_t)b0 * s.Hkv * cap,
+                                                     count + (int64_t)b0 * s.Hkv, cap);
+      continue;
+    }
     if (probs) {
       const int ntile = (int)((cand_hi + 255) / 256);
       dim3 g2(ntile > 0 ? ntile : 1, (b1 - b0 + kRowsQ - 1) / kRowsQ, s.Hkv);

@@ -182,3 +182,35 @@ def test_prefill_select_long_tie_groups():
         qc = O.prefill_block_query(S.to_np(inp.q[rows.start:rows.stop][:, inp.heads(0)]), wq, inp.s_idx)
         core = O.prefill_block_support(qc, kt_rows[0], blk, B_SEL, k)
         assert S.gpu_support(idx, count, blk).tolist() == core.tolist(), blk
+
+
+def periodic_kidx(inp, seed, on_high):
+    """Indexer keys s_j * v plus small noise, with s_j near +3 on the keys of
+    every eighth 16-key tile and near -3 elsewhere (on_high), or the other
+    way round: the scores of a row are bimodal with a mode that only every
+    eighth tile holds."""
+    rng = np.random.default_rng(seed)
+    v = rng.standard_normal(16)
+    on = (np.arange(inp.N) // 16) % 8 == 0
+    sj = np.where(on == on_high, 3.0, -3.0) + rng.uniform(-0.5, 0.5, inp.N)
+    kt = S.store_round(sj[:, None] * v[None, :] + 0.05 * rng.standard_normal((inp.N, 16)), inp.dtype)
+    pool = torch.zeros((inp.k_pool.shape[0], inp.H_kv, 64, 16), dtype=inp.dtype)
+    full = torch.zeros((pool.shape[0] * 64, 16), dtype=inp.dtype)
+    full[: inp.N] = torch.from_numpy(kt).to(inp.dtype)
+    for g in range(inp.H_kv):
+        pool[:, g] = full.view(pool.shape[0], 64, 16)
+    return pool.to(inp.device), {g: kt for g in range(inp.H_kv)}
+
+
+@pytest.mark.parametrize("on_high", [True, False])
+def test_prefill_select_periodic_keys(on_high):
+    """Top-2048 over rows of 4K-40K candidates whose scores follow a pattern
+    with period 128 keys (a threshold estimated from a regular sample of the
+    row can be far off); the supports must still be the oracle's."""
+    inp = synth.make_prefill_custom(N=40000, H_q=4, H_kv=1, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=23, n_hh=0)
+    kidx, kt_rows = periodic_kidx(inp, 5, on_high)
+    k = 2048
+    idx, count, out, lse = run_prefill(inp, kidx, k)
+    blocks = [2, 40, 64, 65, 70, 200, 400, inp.n_blocks - 1]
+    check_blocks(inp, kt_rows, idx, count, out, lse, k, blocks, [0])
