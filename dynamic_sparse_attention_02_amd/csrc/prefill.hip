@@ -629,7 +629,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 // k_pf_select, so both see the same float for every candidate.
 // ---------------------------------------------------------------------------
 constexpr int kHitCap = 4096;      // hits a row's exact selection holds in LDS
-constexpr int kSlotCap = 64;       // keys stored per (row, 256-candidate tile)
+constexpr int kSlotCap = 128;      // keys stored per (row, 256-candidate tile)
 constexpr int kHitSample = 16384;  // sampled candidates per row at most
 constexpr int kSelNT = 512;        // threads of k_pf_thresh and k_pf_select
 constexpr int kHitMaxK = 2048;     // largest k the hit path takes
@@ -659,10 +659,9 @@ __device__ __forceinline__ bf16x8_t split_query(const float* __restrict__ q16, i
 // past lim reads the last valid page, a candidate past lim its page's row)
 // and zeroed afterwards, so all U of them are in flight together.
 template <int U>
-__device__ __forceinline__ void score_tiles(const bf16_raw* __restrict__ kidx,
-                                            const int32_t* __restrict__ pt, const Shape& s, int g,
-                                            int32_t cb, int32_t lim, bf16x8_t qa, int lane,
-                                            f32x4_t (&acc)[U]) {
+__device__ __forceinline__ void load_tiles(const bf16_raw* __restrict__ kidx,
+                                           const int32_t* __restrict__ pt, const Shape& s, int g,
+                                           int32_t cb, int32_t lim, int lane, uint4 (&kv)[U]) {
   const int col = lane & 15;
   const int32_t plast = lim > 0 ? (lim - 1) >> 6 : 0;
   int64_t page[U];
@@ -671,13 +670,17 @@ __device__ __forceinline__ void score_tiles(const bf16_raw* __restrict__ kidx,
     const int32_t pi = (cb + 16 * u) >> 6;
     page[u] = clamp_page(pt[pi < plast ? pi : plast], s.n_pool_pages);
   }
-  uint4 kv[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int32_t c = cb + 16 * u + col;
     kv[u] = *reinterpret_cast<const uint4*>(kidx + ((page[u] * s.Hkv + g) * kPage + (c & 63)) * kRank +
                                             8 * ((lane >> 4) & 1));
   }
+}
+template <int U>
+__device__ __forceinline__ void product_tiles(int32_t cb, int32_t lim, bf16x8_t qa, int lane,
+                                              const uint4 (&kv)[U], f32x4_t (&acc)[U]) {
+  const int col = lane & 15;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const bool ok = cb + 16 * u + col < lim;
@@ -685,6 +688,15 @@ __device__ __forceinline__ void score_tiles(const bf16_raw* __restrict__ kidx,
     acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, __builtin_bit_cast(bf16x8_t, w),
                                                      f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
   }
+}
+template <int U>
+__device__ __forceinline__ void score_tiles(const bf16_raw* __restrict__ kidx,
+                                            const int32_t* __restrict__ pt, const Shape& s, int g,
+                                            int32_t cb, int32_t lim, bf16x8_t qa, int lane,
+                                            f32x4_t (&acc)[U]) {
+  uint4 kv[U];
+  load_tiles<U>(kidx, pt, s, g, cb, lim, lane, kv);
+  product_tiles<U>(cb, lim, qa, lane, kv, acc);
 }
 
 // Exclusive scan over the kSelNT threads.
@@ -758,31 +770,31 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   }
   __shared__ float qs[kRank];
   __shared__ uint32_t hc[4096];
+  __shared__ int32_t s_pg[kHitSample / 16];  // pool page of each sampled tile
   __shared__ uint32_t red[kSelNT / 64];
   __shared__ uint32_t s_bin, s_bef;
   if (t < kRank) qs[t] = qcb[((int64_t)blk * s.Hkv + g) * kRank + t];
+  for (int j = t; j < nst; j += kSelNT) s_pg[j] = (int32_t)clamp_page(pt[(j * stride) >> 2], s.n_pool_pages);
   for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
   __syncthreads();
   uint32_t key[kPer];
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) key[e] = 0u;
   uint32_t valid = 0u;
 #pragma unroll
   for (int e0 = 0; e0 < kPer; e0 += 8) {
-    // branch-free loads (a position past the sample reads candidate n - 1)
-    int32_t cc[8];
-    int64_t page[8];
+    if (e0 * kSelNT >= nst * 16) break;  // (uniform) past the sample
+    // branch-free loads (a position past the sample reads the first
+    // sampled candidate); a sampled tile's 16 candidates share a page
+    uint4 va[8], vb[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int32_t i = (e0 + e) * kSelNT + t;  // sample position
       const int32_t c = (((i >> 4) * stride) << 4) + (i & 15);
       const bool ok = i < nst * 16 && c < n;
       valid |= ok ? 1u << (e0 + e) : 0u;
-      cc[e] = ok ? c : n - 1;
-      page[e] = clamp_page(pt[cc[e] >> 6], s.n_pool_pages);
-    }
-    uint4 va[8], vb[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint4* v = reinterpret_cast<const uint4*>(kidx + ((page[e] * s.Hkv + g) * kPage + (cc[e] & 63)) * kRank);
+      const int64_t page = s_pg[ok ? i >> 4 : 0];
+      const uint4* v = reinterpret_cast<const uint4*>(kidx + ((page * s.Hkv + g) * kPage + ((ok ? c : 0) & 63)) * kRank);
       va[e] = v[0];
       vb[e] = v[1];
     }
@@ -821,95 +833,107 @@ k_pf_hits(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
           const float* __restrict__ qcb, const uint32_t* __restrict__ lo_in, int32_t blk0,
           int32_t blk1, int32_t bsel, int32_t self, Shape s, int32_t tpr,
           uint32_t* __restrict__ bits, uint32_t* __restrict__ slots) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row and page arithmetic
   const int col = lane & 15, lg = lane >> 4;
-  const int g = blockIdx.z, x = blockIdx.x;
+  const int g = blockIdx.z;
   const int32_t bfirst = blk0 + (int32_t)blockIdx.y * 64 + wave * 16;  // this wave's 16 rows
   if (bfirst >= blk1) return;
   const int32_t blast = min(blk1, bfirst + 16) - 1;
-  const int32_t cb = 256 * x;
-  if (cb >= bsel * blast + self) return;  // no row of the wave has candidates here
-  __shared__ uint32_t stage[4][16][256];  // the keys, [row][candidate - cb]
-  __shared__ uint64_t msk[4][16][4];      // hit ballots, [tile][i]: bit 16 q + col = row 4 q + i
+  const int32_t nmax = bsel * blast + self;  // candidates of the wave's last row
+  const int32_t x = (int32_t)blockIdx.x;  // the 256-candidate tile
+  const int32_t cb0 = 256 * x;
+  if (cb0 >= nmax) return;  // no row of the wave has candidates here
+  __shared__ uint32_t stage[4][16][128];  // the keys of one half tile, [row][candidate - cb]
+  __shared__ uint64_t msk[4][8][4];       // hit ballots, [16-candidate tile][i]: bit 16 q + col = row 4 q + i
   const int32_t bq = bfirst + col;
   const bf16x8_t qa = split_query(qcb + ((int64_t)(bq < blk1 ? bq : bfirst) * s.Hkv + g) * kRank, lane, bq < blk1);
-  f32x4_t acc[16];
-  score_tiles<16>(kidx, pt, s, g, cb, bsel * blast + self, qa, lane, acc);
+  // the rows' thresholds as floats: for a finite score f, key(f) >= lo
+  // exactly when f >= key_score(lo), and every finite f passes when lo is at
+  // most the key of -inf
   int32_t n_i[4];
-  uint32_t lo_i[4];
+  float lof[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int32_t bb = bfirst + 4 * lg + i;
     const uint32_t lv = lo_in[(int64_t)((bb < blk1 ? bb : blast) - blk0) * s.Hkv + g];
     n_i[i] = bb < blk1 ? bsel * bb + self : 0;
-    lo_i[i] = bb < blk1 ? lv : 0xffffffffu;
+    lof[i] = bb >= blk1 ? INFINITY : (lv <= 0x007fffffu ? -INFINITY : key_score(lv));
   }
-  // every lane stores the same (uniform) ballot; when every row of the wave
-  // holds all 256 candidates the bound check drops out
-  if (cb + 256 <= bsel * bfirst + self) {
+  // lane L finishes bitmap word 4 hf + (L % 4) of row L / 4
+  const int R = lane >> 2, q = lane & 3;
+  const int32_t bR = bfirst + R;
+  const bool rowok = bR < blk1 && cb0 < bsel * bR + self;
+  const int64_t r = (int64_t)(bR - blk0) * s.Hkv + g;
+  uint32_t carry = 0u;  // hits of this row in the first half
+  uint4 kv[16];  // both halves' key rows in flight together
+  load_tiles<16>(kidx, pt, s, g, cb0, nmax, lane, kv);
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+  for (int hf = 0; hf < 2; ++hf) {
+    const int32_t cb = cb0 + 128 * hf;
+    f32x4_t acc[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t key = score_key(acc[u][i]);
-        stage[wave][4 * lg + i][16 * u + col] = key;
-        msk[wave][u][i] = __builtin_amdgcn_ballot_w64(key >= lo_i[i]);
+    for (int u = 0; u < 8; ++u) {
+      const uint4 w = cb + 16 * u + col < nmax ? kv[8 * hf + u] : make_uint4(0u, 0u, 0u, 0u);
+      acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa, __builtin_bit_cast(bf16x8_t, w),
+                                                       f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+    }
+    // the scores are staged as floats (keys only for the hits, below);
+    // every lane stores the same (uniform) ballot, and when every row of
+    // the wave holds all of these candidates the bound check drops out
+    if (cb + 128 <= bsel * bfirst + self) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          stage[wave][4 * lg + i][16 * u + col] = __float_as_uint(acc[u][i]);
+          msk[wave][u][i] = __builtin_amdgcn_ballot_w64(acc[u][i] >= lof[i]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          stage[wave][4 * lg + i][16 * u + col] = __float_as_uint(acc[u][i]);
+          msk[wave][u][i] = __builtin_amdgcn_ballot_w64(cb + 16 * u + col < n_i[i] && acc[u][i] >= lof[i]);
+        }
       }
     }
-  } else {
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t key = score_key(acc[u][i]);
-        stage[wave][4 * lg + i][16 * u + col] = key;
-        msk[wave][u][i] = __builtin_amdgcn_ballot_w64(cb + 16 * u + col < n_i[i] && key >= lo_i[i]);
-      }
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // lane L holds bitmap word p = L % 8 of rows L / 8 (wv0) and 8 + L / 8
-  // (wv1): tiles 2p (low half) and 2p + 1 (high half)
-  const int p = lane & 7;
-  uint32_t wv0, wv1;
-  {
-    const int R0 = lane >> 3, R1 = 8 + (lane >> 3);
-    const uint64_t a0 = msk[wave][2 * p][R0 & 3], b0 = msk[wave][2 * p + 1][R0 & 3];
-    const uint64_t a1 = msk[wave][2 * p][R1 & 3], b1 = msk[wave][2 * p + 1][R1 & 3];
-    const int s0 = 16 * (R0 >> 2), s1 = 16 * (R1 >> 2);
-    wv0 = (uint32_t)((a0 >> s0) & 0xffffu) | ((uint32_t)((b0 >> s0) & 0xffffu) << 16);
-    wv1 = (uint32_t)((a1 >> s1) & 0xffffu) | ((uint32_t)((b1 >> s1) & 0xffffu) << 16);
-  }
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int R = 8 * h + (lane >> 3);
-    const uint32_t w = h ? wv1 : wv0;
-    // hits of this row in the words before this one (the row's 8 lanes)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // word 4 hf + q of row R: 16-candidate tiles 2q (low half) and 2q + 1
+    const uint64_t a = msk[wave][2 * q][R & 3], b = msk[wave][2 * q + 1][R & 3];
+    const int sh = 16 * (R >> 2);
+    const uint32_t w = (uint32_t)((a >> sh) & 0xffffu) | ((uint32_t)((b >> sh) & 0xffffu) << 16);
+    // hits of this row before this word: the first half plus the row's earlier lanes
     const uint32_t pc = (uint32_t)__popc(w);
     uint32_t inc = pc;
 #pragma unroll
-    for (int d = 1; d < 8; d <<= 1) {
-      const uint32_t v = (uint32_t)__shfl_up((int)inc, d, 8);
-      if (p >= d) inc += v;
+    for (int d = 1; d < 4; d <<= 1) {
+      const uint32_t v = (uint32_t)__shfl_up((int)inc, d, 4);
+      if (q >= d) inc += v;
     }
-    const int32_t bb = bfirst + R;
-    if (bb < blk1 && cb < bsel * bb + self) {
-      const int64_t r = (int64_t)(bb - blk0) * s.Hkv + g;
-      bits[(r * tpr + x) * 8 + p] = w;
-      uint32_t e = inc - pc, ww = w;
+    if (rowok) {
+      bits[(r * tpr + x) * 8 + 4 * hf + q] = w;
+      uint32_t e = carry + inc - pc, ww = w;
       uint32_t* sl = slots + (r * tpr + x) * kSlotCap;
       while (ww != 0u && e < (uint32_t)kSlotCap) {
-        const int b = __ffs(ww) - 1;
+        const int bt = __ffs(ww) - 1;
         ww &= ww - 1u;
-        sl[e++] = stage[wave][R][32 * p + b];
+        sl[e++] = score_key(__uint_as_float(stage[wave][R][32 * q + bt]));
       }
     }
+    carry += (uint32_t)__shfl((int)inc, (lane & ~3) + 3);  // the row's total in this half
+    // the next half rewrites stage and msk: this wave's reads come first
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-__global__ void __launch_bounds__(kSelNT)
+__global__ void __launch_bounds__(kSelNT, 6)
 k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
             const float* __restrict__ qcb, const uint32_t* __restrict__ bits,
             const uint32_t* __restrict__ slots, int32_t blk0, int32_t bsel, int32_t self, Shape s,
@@ -917,14 +941,15 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
             int32_t* __restrict__ count_out, int32_t cap) {
   constexpr int NT = kSelNT, NW = NT / 64;
   constexpr uint32_t kSearchM = 0, kGEM = 1, kTiesM = 2;
-  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x, t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int col = lane & 15, lg = lane >> 4;
   const int g = row % s.Hkv;
   const int32_t blk = blk0 + row / s.Hkv;
   const int32_t n = bsel * blk + self;  // <= 256 kSelNT (host-checked)
   const int pr = (blk - blk0) & 15;     // the block's row in the score product
   const int32_t ntr = (n + 255) >> 8;   // 256-candidate tiles of the row: thread t owns tile t
-  __shared__ uint32_t l_idx[kHitCap], l_key[kHitCap];
+  __shared__ uint32_t l_key[kHitCap];  // hit keys in candidate order (tile t's at toff[t])
   __shared__ uint32_t hc[4096];
   __shared__ uint32_t sel[NT * 8];  // selection bitmap, words [8 t, 8 t + 8) = tile t
   __shared__ uint32_t toff[NT], ovf[NT];
@@ -941,6 +966,7 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     s_thr = 0u;
     s_neq = 0u;
   }
+  for (int i = t; i < 4096; i += NT) hc[i] = 0u;  // level-1 counts, added while the list is built
   uint32_t w[8];
   uint32_t cnt = 0u;
 #pragma unroll
@@ -952,6 +978,15 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     w[4] = b.x; w[5] = b.y; w[6] = b.z; w[7] = b.w;
 #pragma unroll
     for (int e = 0; e < 8; ++e) cnt += (uint32_t)__popc(w[e]);
+  }
+  // the first 32 stored keys of the tile, in flight across the scan
+  uint4 sv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sv[j] = make_uint4(0u, 0u, 0u, 0u);
+  const uint4* slp = reinterpret_cast<const uint4*>(slots + ((int64_t)row * tpr + (t < ntr ? t : 0)) * kSlotCap);
+  if (t < ntr && cnt != 0u && cnt <= (uint32_t)kSlotCap) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sv[j] = slp[j];
   }
   uint32_t H;
   const uint32_t off = sel_scan(cnt, red, H);  // (its barriers publish the set-up above)
@@ -979,34 +1014,30 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     if (t < ntr) {
       toff[t] = off;
       const bool stored = cnt <= (uint32_t)kSlotCap;
-      if (stored) {  // the stored keys, 32 at a time with all loads in flight
-        const uint4* sl = reinterpret_cast<const uint4*>(slots + ((int64_t)row * tpr + t) * kSlotCap);
-#pragma unroll
-        for (int h = 0; h < kSlotCap / 32; ++h) {
-          if (cnt > 32u * h) {
-            uint4 v[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = sl[8 * h + j];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const uint32_t e = 32u * h + 4u * j;
-              if (e < cnt) l_key[off + e] = v[j].x;
-              if (e + 1 < cnt) l_key[off + e + 1] = v[j].y;
-              if (e + 2 < cnt) l_key[off + e + 2] = v[j].z;
-              if (e + 3 < cnt) l_key[off + e + 3] = v[j].w;
-            }
+      if (stored) {  // the stored keys (the first 32 already loaded)
+        auto put = [&](uint32_t e, uint32_t key) {
+          if (e < cnt) {
+            l_key[off + e] = key;
+            atomicAdd(&hc[key >> 20], 1u);
           }
-        }
-      }
-      uint32_t e = 0u;
+        };
 #pragma unroll
-      for (int wi = 0; wi < 8; ++wi) {
-        uint32_t ww = w[wi];
-        while (ww != 0u) {
-          const int b = __ffs(ww) - 1;
-          ww &= ww - 1u;
-          l_idx[off + e] = (uint32_t)(256 * t + 32 * wi + b);
-          ++e;
+        for (int j = 0; j < 8; ++j) {
+          put(4u * j, sv[j].x);
+          put(4u * j + 1, sv[j].y);
+          put(4u * j + 2, sv[j].z);
+          put(4u * j + 3, sv[j].w);
+        }
+        for (uint32_t e0 = 32u; e0 < cnt; e0 += 32u) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) sv[j] = slp[e0 / 4u + j];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            put(e0 + 4u * j, sv[j].x);
+            put(e0 + 4u * j + 1, sv[j].y);
+            put(e0 + 4u * j + 2, sv[j].z);
+            put(e0 + 4u * j + 3, sv[j].w);
+          }
         }
       }
       if (!stored) ovf[atomicAdd(&s_novf, 1u)] = (uint32_t)t;
@@ -1030,7 +1061,9 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
 #pragma unroll
             for (int wi = 0; wi < 8; ++wi) rank += wi < (q >> 5) ? (uint32_t)__popc(tw[wi]) : 0u;
             const float v = (pr & 3) == 0 ? acc[u][0] : ((pr & 3) == 1 ? acc[u][1] : ((pr & 3) == 2 ? acc[u][2] : acc[u][3]));
-            l_key[toff[tt] + rank] = score_key(v);
+            const uint32_t key = score_key(v);
+            l_key[toff[tt] + rank] = key;
+            atomicAdd(&hc[key >> 20], 1u);
           }
         }
       }
@@ -1044,19 +1077,24 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
       if (s_mode != kSearchM) break;  // block-uniform (read after a barrier)
       const int NB = level == 3 ? 256 : 4096;
       const uint32_t pre = s_pre;
-      for (int i = t; i < NB; i += NT) hc[i] = 0u;
-      __syncthreads();
+      const bool have = fast && level == 1;  // the list build made the level-1 counts
+      if (!have) {
+        for (int i = t; i < NB; i += NT) hc[i] = 0u;
+        __syncthreads();
+      }
       auto add = [&](int32_t, uint32_t key) {
         if (level == 1) atomicAdd(&hc[key >> 20], 1u);
         else if (level == 2) { if ((key >> 20) == pre) atomicAdd(&hc[(key >> 8) & 0xfffu], 1u); }
         else if ((key >> 8) == pre) atomicAdd(&hc[key & 0xffu], 1u);
       };
-      if (fast) {
-        for (uint32_t j = (uint32_t)t; j < H; j += NT) add(0, l_key[j]);
-      } else {
-        for_all_keys(add);
+      if (!have) {
+        if (fast) {
+          for (uint32_t j = (uint32_t)t; j < H; j += NT) add(0, l_key[j]);
+        } else {
+          for_all_keys(add);
+        }
+        __syncthreads();
       }
-      __syncthreads();
       top_bin(hc, NB, s_need, red, &s_bin, &s_bef);
       if (t == 0) {
         const uint32_t bin = s_bin;
@@ -1085,22 +1123,42 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     // ---- marking ----
     const uint32_t mode = s_mode, thr = s_thr, neq = s_neq;
     if (fast) {
-      for (uint32_t j = (uint32_t)t; j < H; j += NT) {
-        const uint32_t key = l_key[j];
-        if (key > thr || (mode == kGEM && key == thr)) atomicOr(&sel[l_idx[j] >> 5], 1u << (l_idx[j] & 31));
-      }
-      if (mode == kTiesM) {  // the neq lowest-index keys equal to thr: list order is candidate order
-        const uint32_t E = (H + NT - 1) / NT;
-        uint32_t c = 0u;
-        for (uint32_t j = E * t; j < E * t + E && j < H; ++j) c += l_key[j] == thr ? 1u : 0u;
-        uint32_t tot;
-        const uint32_t before = sel_scan(c, red, tot);
-        uint32_t left = before < neq ? neq - before : 0u;
-        for (uint32_t j = E * t; j < E * t + E && j < H && left; ++j)
-          if (l_key[j] == thr) {
-            atomicOr(&sel[l_idx[j] >> 5], 1u << (l_idx[j] & 31));
-            --left;
+      // thread t walks its tile's hits in candidate order (list positions
+      // off, off + 1, ...) and sets its own selection words
+      uint32_t neq_t = 0u;
+      {
+        uint32_t e = off;
+#pragma unroll
+        for (int wi = 0; wi < 8; ++wi) {
+          uint32_t ww = w[wi], m = 0u;
+          while (ww != 0u) {
+            const uint32_t bit = ww & (0u - ww);
+            ww &= ww - 1u;
+            const uint32_t key = l_key[e++];
+            if (key > thr || (mode == kGEM && key == thr)) m |= bit;
+            neq_t += key == thr ? 1u : 0u;
           }
+          sel[8 * t + wi] |= m;
+        }
+      }
+      if (mode == kTiesM) {  // the neq lowest-index keys equal to thr
+        uint32_t tot;
+        const uint32_t before = sel_scan(neq_t, red, tot);
+        uint32_t left = before < neq ? neq - before : 0u;
+        uint32_t e = off;
+#pragma unroll
+        for (int wi = 0; wi < 8; ++wi) {
+          uint32_t ww = w[wi], m = 0u;
+          while (ww != 0u) {
+            const uint32_t bit = ww & (0u - ww);
+            ww &= ww - 1u;
+            if (l_key[e++] == thr && left != 0u) {
+              m |= bit;
+              --left;
+            }
+          }
+          sel[8 * t + wi] |= m;
+        }
       }
     } else {
       if (mode == kTiesM) {
@@ -1155,16 +1213,25 @@ k_pf_select(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   }
   uint32_t total;
   uint32_t rank = sel_scan(c, red, total);
-  int32_t* out = idx_out + (int64_t)row * cap;
-  const uint32_t T = total < (uint32_t)cap ? total : (uint32_t)cap;
+  // every word's mask and output offset to LDS (the offsets over hc), then
+  // word j written by thread j mod NT: a short dense row spreads over all
+  // threads instead of the few that own its words
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    uint32_t b = sw[e];
+    sel[8 * t + e] = sw[e];
+    hc[8 * t + e] = rank;
+    rank += (uint32_t)__popc(sw[e]);
+  }
+  __syncthreads();
+  int32_t* out = idx_out + (int64_t)row * cap;
+  const uint32_t T = total < (uint32_t)cap ? total : (uint32_t)cap;
+  for (int32_t j = t; j < ((n + 31) >> 5); j += NT) {
+    uint32_t b = sel[j], o = hc[j];
     while (b != 0u) {
-      const int j = __ffs(b) - 1;
+      const int jj = __ffs(b) - 1;
       b &= b - 1u;
-      if (rank < (uint32_t)cap) out[rank] = 256 * t + 32 * e + j;
-      ++rank;
+      if (o < (uint32_t)cap) out[o] = 32 * j + jj;
+      ++o;
     }
   }
   for (int64_t o = (int64_t)T + t; o < cap; o += NT) out[o] = -1;
@@ -1261,10 +1328,12 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     if (key16 && bf && b_sel > 1 && k <= kHitMaxK && ldx >= 256) {
       const int64_t rows = (int64_t)(b1 - b0) * s.Hkv;
       const int32_t tpr = (int32_t)((ldx + 255) / 256);
+      const size_t need = align_up((size_t)rows * 4, 256) + (size_t)rows * tpr * (8 + kSlotCap) * 4;
+      if (need > (size_t)P.slab * s.Hkv * (size_t)P.ldx * sizeof(float)) return hipErrorInvalidValue;
       uint32_t* lo = (uint32_t*)xs;
       uint32_t* bits = lo + align_up((size_t)rows, 64);
       uint32_t* slots = bits + (size_t)rows * tpr * 8;
-      const int32_t stride = k <= 1024 ? 16 : 8;
+      const int32_t stride = k <= 1024 ? 16 : 12;  // sampled: every stride-th 16-candidate tile
       k_pf_thresh<<<(unsigned)rows, kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, b0,
                                                      b_sel, P.self, s, k, stride, lo);
       dim3 gh((unsigned)tpr, (unsigned)((b1 - b0 + 63) / 64), (unsigned)s.Hkv);
