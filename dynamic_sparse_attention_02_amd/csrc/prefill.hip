@@ -1323,9 +1323,9 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     // logit scores go to the selection as 16-bit keys (exact scores of the
     // threshold bin are recomputed there) when its one-block rows take them
     const bool key16 = !probs && ldx <= kSelectRowMax;
-    // block rows, bf16 indexer keys and k <= kHitMaxK: sampled thresholds,
-    // hit bitmaps from the matrix cores and the exact top k over the hits
-    if (key16 && bf && b_sel > 1 && k <= kHitMaxK && ldx >= 256) {
+    // bf16 indexer keys and k <= kHitMaxK: sampled thresholds, hit bitmaps
+    // from the matrix cores and the exact top k over the hits
+    if (key16 && bf && k <= kHitMaxK && ldx >= 256) {
       const int64_t rows = (int64_t)(b1 - b0) * s.Hkv;
       const int32_t tpr = (int32_t)((ldx + 255) / 256);
       const size_t need = align_up((size_t)rows * 4, 256) + (size_t)rows * tpr * (8 + kSlotCap) * 4;
