@@ -49,8 +49,9 @@ __global__ void k_iota1(int32_t* __restrict__ v, int32_t n) {
 // thread projects its (head, dims) chunk and the block reduces the rank-16
 // result.
 // ---------------------------------------------------------------------------
+constexpr int kQcNT = 256;  // threads of k_prefill_qc
 template <typename T>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kQcNT)
 k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int32_t Hq,
              int32_t Hkv, int32_t D, int32_t bsel, float s_idx, float* __restrict__ qcb) {
   const int blk = blockIdx.x, g = blockIdx.y;
@@ -59,25 +60,37 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
   const int nr = min(bsel, N - r0);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunks = G * D / 8;              // (head, 8 dims) chunks: <= 256
-  const int parts = 256 / chunks;            // row shares per chunk
+  const int parts = kQcNT / chunks;          // row shares per chunk
   const int ch = threadIdx.x % chunks, part = threadIdx.x / chunks;
   const int h = g * G + (ch * 8) / D, d0 = (ch * 8) % D;
-  __shared__ float qs[256][8];               // each thread's partial sums
+  __shared__ float qs[kQcNT][8];             // each thread's partial sums
   float acc8[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
   if (part < parts) {
-    for (int i = part; i < nr; i += parts) {
-      const T* src = q + ((int64_t)(r0 + i) * Hq + h) * D + d0;
-      if constexpr (sizeof(T) == 2) {
-        const uint4 v = *reinterpret_cast<const uint4*>(src);
+    int i = part;
+    if constexpr (sizeof(T) == 2) {
+      auto add = [&](const uint4& v) {
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           acc8[2 * e] += __uint_as_float(w[e] << 16);
           acc8[2 * e + 1] += __uint_as_float(w[e] & 0xffff0000u);
         }
-      } else {
+      };
+      // eight rows' loads in flight at a time (the sum order is the same)
+      for (; i + 7 * parts < nr; i += 8 * parts) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = *reinterpret_cast<const uint4*>(q + ((int64_t)(r0 + i + u * parts) * Hq + h) * D + d0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) add(v[u]);
+      }
+      for (; i < nr; i += parts) add(*reinterpret_cast<const uint4*>(q + ((int64_t)(r0 + i) * Hq + h) * D + d0));
+    } else {
+      for (; i < nr; i += parts) {
+        const T* src = q + ((int64_t)(r0 + i) * Hq + h) * D + d0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc8[e] += to_f32<T>(src[e]);
       }
@@ -100,7 +113,7 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
       for (int c = 0; c < kRank; ++c) acc[c] = fmaf(to_f32<T>(wr[c]), v, acc[c]);
     }
   }
-  __shared__ float red[4][kRank];
+  __shared__ float red[kQcNT / 64][kRank];
 #pragma unroll
   for (int c = 0; c < kRank; ++c) {
     const float v = wave_sum(acc[c]);
@@ -109,6 +122,7 @@ k_prefill_qc(const T* __restrict__ q, const T* __restrict__ w_q, int32_t N, int3
   __syncthreads();
   if (threadIdx.x < kRank) {
     const int c = threadIdx.x;
+    static_assert(kQcNT == 256, "four waves' sums");
     const float v = (red[0][c] + red[1][c]) + (red[2][c] + red[3][c]);
     qcb[((int64_t)blk * Hkv + g) * kRank + c] = v * (s_idx / (float)(nr * G));
   }
@@ -607,7 +621,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 // ---------------------------------------------------------------------------
 // Top-k rows with bf16 indexer keys (k <= kHitMaxK): three launches per slab
 // instead of one fp32 score per candidate written and read back.
-//   k_pf_thresh: per row, a threshold lo from a sample of the row (the scores
+//   k_pf_thresh (one launch for every row): per row, a threshold lo from a sample of the row (the scores
 //     of every stride-th 16-candidate tile): the 24-bit key floor at which ks
 //     sampled keys are reached from the top, ks set so that the whole row
 //     holds between k and kHitCap keys >= lo except with negligible
@@ -745,17 +759,29 @@ __device__ __forceinline__ void top_bin(const uint32_t* hc, int nb, uint32_t nee
   __syncthreads();
 }
 
+// The sampled threshold of row (blk, g) = blockIdx.x, blk = blockIdx.x /
+// Hkv over all query blocks (or queries): lo such that the row holds
+// between k and kHitCap keys >= lo except with negligible probability; rows
+// of at most kHitCap candidates take 0.
 __global__ void __launch_bounds__(kSelNT)
 k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
-            const float* __restrict__ qcb, int32_t blk0, int32_t bsel, int32_t self, Shape s,
-            int32_t k, int32_t stride, uint32_t* __restrict__ lo_out) {
+            const float* __restrict__ qcb, int32_t bsel, int32_t self, Shape s, int32_t k,
+            int32_t stride, uint32_t* __restrict__ lo_all) {
   constexpr int kPer = kHitSample / kSelNT;
-  const int row = blockIdx.x, t = threadIdx.x;
-  const int g = row % s.Hkv;
-  const int32_t blk = blk0 + row / s.Hkv;
+  const int t = threadIdx.x;
+  const int g = blockIdx.x % s.Hkv;
+  const int32_t blk = blockIdx.x / s.Hkv;
   const int32_t n = bsel * blk + self;
+  uint32_t* const lo_out = lo_all + blockIdx.x;
+  __shared__ float qs[kRank];
+  __shared__ uint32_t hc[4096];
+  __shared__ int32_t s_pg[kHitSample / 16];  // pool page of each sampled tile
+  __shared__ uint32_t red[kSelNT / 64];
+  __shared__ uint32_t s_binv, s_befv;
+  uint32_t* const s_bin = &s_binv;
+  uint32_t* const s_bef = &s_befv;
   if (n <= kHitCap) {
-    if (t == 0) lo_out[row] = 0u;
+    if (t == 0) *lo_out = 0u;
     return;
   }
   const int32_t ntl = (n + 15) >> 4;               // 16-candidate tiles
@@ -765,30 +791,25 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   const float kf = (float)k * (float)m / (float)n;
   const uint32_t ks = (uint32_t)ceilf(kf + 5.5f * sqrtf(kf) + 6.f);
   if (ks >= (uint32_t)m) {
-    if (t == 0) lo_out[row] = 0u;
+    if (t == 0) *lo_out = 0u;
     return;
   }
-  __shared__ float qs[kRank];
-  __shared__ uint32_t hc[4096];
-  __shared__ int32_t s_pg[kHitSample / 16];  // pool page of each sampled tile
-  __shared__ uint32_t red[kSelNT / 64];
-  __shared__ uint32_t s_bin, s_bef;
-  if (t < kRank) qs[t] = qcb[((int64_t)blk * s.Hkv + g) * kRank + t];
   for (int j = t; j < nst; j += kSelNT) s_pg[j] = (int32_t)clamp_page(pt[(j * stride) >> 2], s.n_pool_pages);
   for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
+  if (t < kRank) qs[t] = qcb[((int64_t)blk * s.Hkv + g) * kRank + t];
   __syncthreads();
   uint32_t key[kPer];
 #pragma unroll
   for (int e = 0; e < kPer; ++e) key[e] = 0u;
   uint32_t valid = 0u;
 #pragma unroll
-  for (int e0 = 0; e0 < kPer; e0 += 8) {
+  for (int e0 = 0; e0 < kPer; e0 += 4) {
     if (e0 * kSelNT >= nst * 16) break;  // (uniform) past the sample
     // branch-free loads (a position past the sample reads the first
     // sampled candidate); a sampled tile's 16 candidates share a page
-    uint4 va[8], vb[8];
+    uint4 va[4], vb[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const int32_t i = (e0 + e) * kSelNT + t;  // sample position
       const int32_t c = (((i >> 4) * stride) << 4) + (i & 15);
       const bool ok = i < nst * 16 && c < n;
@@ -799,7 +820,7 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
       vb[e] = v[1];
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
       const uint32_t u[8] = {va[e].x, va[e].y, va[e].z, va[e].w, vb[e].x, vb[e].y, vb[e].z, vb[e].w};
       float a = 0.f;
 #pragma unroll
@@ -812,10 +833,10 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     }
   }
   __syncthreads();
-  top_bin(hc, 4096, ks, red, &s_bin, &s_bef);
-  const uint32_t b1 = s_bin, bef1 = s_bef;
+  top_bin(hc, 4096, ks, red, s_bin, s_bef);
+  const uint32_t b1 = *s_bin, bef1 = *s_bef;
   if (b1 == 0xffffffffu) {  // not reached (ks < m): take every candidate
-    if (t == 0) lo_out[row] = 0u;
+    if (t == 0) *lo_out = 0u;
     return;
   }
   for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
@@ -824,8 +845,8 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   for (int e = 0; e < kPer; ++e)
     if (((valid >> e) & 1u) && (key[e] >> 20) == b1) atomicAdd(&hc[(key[e] >> 8) & 0xfffu], 1u);
   __syncthreads();
-  top_bin(hc, 4096, ks - bef1, red, &s_bin, &s_bef);
-  if (t == 0) lo_out[row] = (b1 << 20) | ((s_bin == 0xffffffffu ? 0u : s_bin) << 8);
+  top_bin(hc, 4096, ks - bef1, red, s_bin, s_bef);
+  if (t == 0) *lo_out = (b1 << 20) | ((*s_bin == 0xffffffffu ? 0u : *s_bin) << 8);
 }
 
 __global__ void __launch_bounds__(256)
@@ -1246,7 +1267,7 @@ struct PrefillSelPlan {
   int32_t self;      // the own token is a candidate (per query)
   int64_t ldx;       // score row stride (candidates of the last row)
   int32_t nparts;    // per-head passes: wave partials per row
-  size_t off_x, off_part, off_lse, off_sel, total;
+  size_t off_lo, off_x, off_part, off_lse, off_sel, total;
 };
 
 PrefillSelPlan prefill_sel_plan(const Shape& s, int32_t n_tokens, int32_t bsel, bool probs) {
@@ -1265,6 +1286,8 @@ PrefillSelPlan prefill_sel_plan(const Shape& s, int32_t n_tokens, int32_t bsel, 
   const int G = s.Hq / s.Hkv;
   size_t off = probs ? align_up((size_t)n_tokens * s.Hq * kRank * sizeof(float), 256)
                      : align_up((size_t)p.nblk * s.Hkv * kRank * sizeof(float), 256);
+  p.off_lo = off;  // sampled top-k thresholds of every row
+  if (!probs) off += align_up((size_t)p.nblk * s.Hkv * sizeof(uint32_t), 256);
   p.off_x = off;
   off += align_up((size_t)p.slab * s.Hkv * (size_t)p.ldx * sizeof(float), 256);
   p.off_part = off;
@@ -1303,6 +1326,8 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
   float* lse2 = (float*)(base + P.off_lse);
   void* sel_ws = base + P.off_sel;
   const bool bf = dt == SA_BF16;
+  // every row's sampled threshold when the slabs may take the hit path
+  uint32_t* hit_lo = (bf && !probs && k <= kHitMaxK) ? (uint32_t*)(base + P.off_lo) : nullptr;
   if (probs) {
     dim3 g1(n_tokens, s.Hkv);
     if (bf) k_prefill_qh<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q,
@@ -1311,10 +1336,15 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
                                                  s.D, s_idx, qv);
   } else {
     dim3 g1(P.nblk, s.Hkv);
-    if (bf) k_prefill_qc<bf16_raw><<<g1, 256, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q,
-                                                      n_tokens, s.Hq, s.Hkv, s.D, b_sel, s_idx, qv);
-    else k_prefill_qc<float><<<g1, 256, 0, st>>>((const float*)q, (const float*)w_q, n_tokens, s.Hq,
-                                                 s.Hkv, s.D, b_sel, s_idx, qv);
+    if (bf) k_prefill_qc<bf16_raw><<<g1, kQcNT, 0, st>>>((const bf16_raw*)q, (const bf16_raw*)w_q,
+                                                        n_tokens, s.Hq, s.Hkv, s.D, b_sel, s_idx, qv);
+    else k_prefill_qc<float><<<g1, kQcNT, 0, st>>>((const float*)q, (const float*)w_q, n_tokens, s.Hq,
+                                                   s.Hkv, s.D, b_sel, s_idx, qv);
+    // sampled thresholds of every row (every stride-th 16-candidate tile)
+    if (hit_lo != nullptr)
+      k_pf_thresh<<<(unsigned)(P.nblk * s.Hkv), kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table,
+                                                                 qv, b_sel, P.self, s, k,
+                                                                 k <= 1024 ? 16 : 12, hit_lo);
   }
   for (int b0 = 0; b0 < P.nblk; b0 += (int)P.slab) {
     const int b1 = b0 + (int)P.slab < P.nblk ? b0 + (int)P.slab : P.nblk;
@@ -1325,17 +1355,14 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
     const bool key16 = !probs && ldx <= kSelectRowMax;
     // bf16 indexer keys and k <= kHitMaxK: sampled thresholds, hit bitmaps
     // from the matrix cores and the exact top k over the hits
-    if (key16 && bf && k <= kHitMaxK && ldx >= 256) {
+    if (key16 && hit_lo != nullptr && ldx >= 256) {
       const int64_t rows = (int64_t)(b1 - b0) * s.Hkv;
       const int32_t tpr = (int32_t)((ldx + 255) / 256);
-      const size_t need = align_up((size_t)rows * 4, 256) + (size_t)rows * tpr * (8 + kSlotCap) * 4;
+      const size_t need = (size_t)rows * tpr * (8 + kSlotCap) * 4;
       if (need > (size_t)P.slab * s.Hkv * (size_t)P.ldx * sizeof(float)) return hipErrorInvalidValue;
-      uint32_t* lo = (uint32_t*)xs;
-      uint32_t* bits = lo + align_up((size_t)rows, 64);
+      const uint32_t* lo = hit_lo + (int64_t)b0 * s.Hkv;
+      uint32_t* bits = (uint32_t*)xs;
       uint32_t* slots = bits + (size_t)rows * tpr * 8;
-      const int32_t stride = k <= 1024 ? 16 : 12;  // sampled: every stride-th 16-candidate tile
-      k_pf_thresh<<<(unsigned)rows, kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, b0,
-                                                     b_sel, P.self, s, k, stride, lo);
       dim3 gh((unsigned)tpr, (unsigned)((b1 - b0 + 63) / 64), (unsigned)s.Hkv);
       k_pf_hits<<<gh, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, lo, b0, b1, b_sel,
                                     P.self, s, tpr, bits, slots);
