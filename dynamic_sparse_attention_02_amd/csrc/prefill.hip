@@ -849,7 +849,8 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   if (t == 0) *lo_out = (b1 << 20) | ((*s_bin == 0xffffffffu ? 0u : *s_bin) << 8);
 }
 
-__global__ void __launch_bounds__(256)
+constexpr int kHitWaves = 2;  // waves (16 rows each) per k_pf_hits workgroup
+__global__ void __launch_bounds__(64 * kHitWaves)
 k_pf_hits(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
           const float* __restrict__ qcb, const uint32_t* __restrict__ lo_in, int32_t blk0,
           int32_t blk1, int32_t bsel, int32_t self, Shape s, int32_t tpr,
@@ -858,15 +859,15 @@ k_pf_hits(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar row and page arithmetic
   const int col = lane & 15, lg = lane >> 4;
   const int g = blockIdx.z;
-  const int32_t bfirst = blk0 + (int32_t)blockIdx.y * 64 + wave * 16;  // this wave's 16 rows
+  const int32_t bfirst = blk0 + (int32_t)blockIdx.y * (16 * kHitWaves) + wave * 16;  // this wave's 16 rows
   if (bfirst >= blk1) return;
   const int32_t blast = min(blk1, bfirst + 16) - 1;
   const int32_t nmax = bsel * blast + self;  // candidates of the wave's last row
   const int32_t x = (int32_t)blockIdx.x;  // the 256-candidate tile
   const int32_t cb0 = 256 * x;
   if (cb0 >= nmax) return;  // no row of the wave has candidates here
-  __shared__ uint32_t stage[4][16][128];  // the keys of one half tile, [row][candidate - cb]
-  __shared__ uint64_t msk[4][8][4];       // hit ballots, [16-candidate tile][i]: bit 16 q + col = row 4 q + i
+  __shared__ uint32_t stage[kHitWaves][16][128];  // the keys of one half tile, [row][candidate - cb]
+  __shared__ uint64_t msk[kHitWaves][8][4];       // hit ballots, [16-candidate tile][i]: bit 16 q + col = row 4 q + i
   const int32_t bq = bfirst + col;
   const bf16x8_t qa = split_query(qcb + ((int64_t)(bq < blk1 ? bq : bfirst) * s.Hkv + g) * kRank, lane, bq < blk1);
   // the rows' thresholds as floats: for a finite score f, key(f) >= lo
@@ -1363,8 +1364,8 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
       const uint32_t* lo = hit_lo + (int64_t)b0 * s.Hkv;
       uint32_t* bits = (uint32_t*)xs;
       uint32_t* slots = bits + (size_t)rows * tpr * 8;
-      dim3 gh((unsigned)tpr, (unsigned)((b1 - b0 + 63) / 64), (unsigned)s.Hkv);
-      k_pf_hits<<<gh, 256, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, lo, b0, b1, b_sel,
+      dim3 gh((unsigned)tpr, (unsigned)((b1 - b0 + 16 * kHitWaves - 1) / (16 * kHitWaves)), (unsigned)s.Hkv);
+      k_pf_hits<<<gh, 64 * kHitWaves, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, lo, b0, b1, b_sel,
                                     P.self, s, tpr, bits, slots);
       k_pf_select<<<(unsigned)rows, kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table, qv, bits,
                                                      slots, b0, b_sel, P.self, s, tpr, k, P.self,
