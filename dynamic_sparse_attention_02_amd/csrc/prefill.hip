@@ -759,52 +759,63 @@ __device__ __forceinline__ void top_bin(const uint32_t* hc, int nb, uint32_t nee
   __syncthreads();
 }
 
-// The sampled threshold of row (blk, g) = blockIdx.x, blk = blockIdx.x /
-// Hkv over all query blocks (or queries): lo such that the row holds
-// between k and kHitCap keys >= lo except with negligible probability; rows
-// of at most kHitCap candidates take 0.
-__global__ void __launch_bounds__(kSelNT)
+// The sampled thresholds of rows (blk, g) and (blk + 1, g), blk = 2 (w /
+// Hkv), g = w % Hkv for workgroup w, over all query blocks (or queries): lo
+// such that the row holds between k and kHitCap keys >= lo except with
+// negligible probability; rows of at most kHitCap candidates take 0.  The
+// two rows share the sampled key rows (one load scores both queries).
+constexpr int kThrPer = 24;  // sampled candidates per thread (stride >= 11)
+__global__ void __launch_bounds__(kSelNT, 4)
 k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
-            const float* __restrict__ qcb, int32_t bsel, int32_t self, Shape s, int32_t k,
-            int32_t stride, uint32_t* __restrict__ lo_all) {
-  constexpr int kPer = kHitSample / kSelNT;
+            const float* __restrict__ qcb, int32_t nblk, int32_t bsel, int32_t self, Shape s,
+            int32_t k, int32_t stride, uint32_t* __restrict__ lo_all) {
   const int t = threadIdx.x;
   const int g = blockIdx.x % s.Hkv;
-  const int32_t blk = blockIdx.x / s.Hkv;
-  const int32_t n = bsel * blk + self;
-  uint32_t* const lo_out = lo_all + blockIdx.x;
-  __shared__ float qs[kRank];
-  __shared__ uint32_t hc[4096];
-  __shared__ int32_t s_pg[kHitSample / 16];  // pool page of each sampled tile
+  const int32_t blk0 = 2 * (int32_t)(blockIdx.x / s.Hkv);
+  __shared__ float qs[2][kRank];
+  __shared__ uint32_t hc[2][4096];
+  __shared__ int32_t s_pg[kThrPer * kSelNT / 16];  // pool page of each sampled tile
   __shared__ uint32_t red[kSelNT / 64];
-  __shared__ uint32_t s_binv, s_befv;
-  uint32_t* const s_bin = &s_binv;
-  uint32_t* const s_bef = &s_befv;
-  if (n <= kHitCap) {
-    if (t == 0) *lo_out = 0u;
+  __shared__ uint32_t s_bin, s_bef;
+  // per row: candidates, sampled tiles and candidates, the sample count ks
+  // the threshold must reach (0: the row takes lo = 0)
+  int32_t n[2], nst[2];
+  uint32_t ks[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int32_t blk = blk0 + r;
+    n[r] = blk < nblk ? bsel * blk + self : 0;
+    nst[r] = 0;
+    ks[r] = 0u;
+    if (n[r] > kHitCap) {
+      const int32_t ntl = (n[r] + 15) >> 4;  // 16-candidate tiles
+      nst[r] = (ntl + stride - 1) / stride;   // sampled tiles: 16 nst <= kThrPer kSelNT
+      const int32_t last = (nst[r] - 1) * stride;
+      const int32_t m = nst[r] * 16 - (last == ntl - 1 ? ntl * 16 - n[r] : 0);
+      const float kf = (float)k * (float)m / (float)n[r];
+      const uint32_t kk = (uint32_t)ceilf(kf + 5.5f * sqrtf(kf) + 6.f);
+      ks[r] = kk < (uint32_t)m ? kk : 0u;
+    }
+  }
+  if (ks[0] == 0u && ks[1] == 0u) {
+    if (t < 2 && blk0 + t < nblk) lo_all[(int64_t)(blk0 + t) * s.Hkv + g] = 0u;
     return;
   }
-  const int32_t ntl = (n + 15) >> 4;               // 16-candidate tiles
-  const int32_t nst = (ntl + stride - 1) / stride;  // sampled tiles: 16 nst <= kHitSample
-  const int32_t last = (nst - 1) * stride;
-  const int32_t m = nst * 16 - (last == ntl - 1 ? ntl * 16 - n : 0);  // sampled candidates
-  const float kf = (float)k * (float)m / (float)n;
-  const uint32_t ks = (uint32_t)ceilf(kf + 5.5f * sqrtf(kf) + 6.f);
-  if (ks >= (uint32_t)m) {
-    if (t == 0) *lo_out = 0u;
-    return;
+  const int32_t nsa = nst[0] > nst[1] ? nst[0] : nst[1];  // the sample of the longer row
+  for (int j = t; j < nsa; j += kSelNT) s_pg[j] = (int32_t)clamp_page(pt[(j * stride) >> 2], s.n_pool_pages);
+  for (int i = t; i < 2 * 4096; i += kSelNT) (&hc[0][0])[i] = 0u;
+  if (t < 2 * kRank) {
+    const int r = t / kRank;
+    qs[r][t % kRank] = blk0 + r < nblk ? qcb[((int64_t)(blk0 + r) * s.Hkv + g) * kRank + t % kRank] : 0.f;
   }
-  for (int j = t; j < nst; j += kSelNT) s_pg[j] = (int32_t)clamp_page(pt[(j * stride) >> 2], s.n_pool_pages);
-  for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
-  if (t < kRank) qs[t] = qcb[((int64_t)blk * s.Hkv + g) * kRank + t];
   __syncthreads();
-  uint32_t key[kPer];
+  uint32_t key0[kThrPer], key1[kThrPer];
+  uint32_t v0 = 0u, v1 = 0u;  // bit e: sample e is a candidate of row 0 / 1 with ks != 0
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) key[e] = 0u;
-  uint32_t valid = 0u;
+  for (int e = 0; e < kThrPer; ++e) key0[e] = key1[e] = 0u;
 #pragma unroll
-  for (int e0 = 0; e0 < kPer; e0 += 4) {
-    if (e0 * kSelNT >= nst * 16) break;  // (uniform) past the sample
+  for (int e0 = 0; e0 < kThrPer; e0 += 4) {
+    if (e0 * kSelNT >= nsa * 16) break;  // (uniform) past the sample
     // branch-free loads (a position past the sample reads the first
     // sampled candidate); a sampled tile's 16 candidates share a page
     uint4 va[4], vb[4];
@@ -812,8 +823,9 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
     for (int e = 0; e < 4; ++e) {
       const int32_t i = (e0 + e) * kSelNT + t;  // sample position
       const int32_t c = (((i >> 4) * stride) << 4) + (i & 15);
-      const bool ok = i < nst * 16 && c < n;
-      valid |= ok ? 1u << (e0 + e) : 0u;
+      const bool ok = i < nsa * 16;
+      v0 |= (ok && ks[0] != 0u && i < nst[0] * 16 && c < n[0]) ? 1u << (e0 + e) : 0u;
+      v1 |= (ok && ks[1] != 0u && i < nst[1] * 16 && c < n[1]) ? 1u << (e0 + e) : 0u;
       const int64_t page = s_pg[ok ? i >> 4 : 0];
       const uint4* v = reinterpret_cast<const uint4*>(kidx + ((page * s.Hkv + g) * kPage + ((ok ? c : 0) & 63)) * kRank);
       va[e] = v[0];
@@ -822,31 +834,48 @@ k_pf_thresh(const bf16_raw* __restrict__ kidx, const int32_t* __restrict__ pt,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t u[8] = {va[e].x, va[e].y, va[e].z, va[e].w, vb[e].x, vb[e].y, vb[e].z, vb[e].w};
-      float a = 0.f;
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        a = fmaf(qs[2 * j], __uint_as_float(u[j] << 16), a);
-        a = fmaf(qs[2 * j + 1], __uint_as_float(u[j] & 0xffff0000u), a);
+        const float lo16 = __uint_as_float(u[j] << 16), hi16 = __uint_as_float(u[j] & 0xffff0000u);
+        a0 = fmaf(qs[0][2 * j], lo16, a0);
+        a0 = fmaf(qs[0][2 * j + 1], hi16, a0);
+        a1 = fmaf(qs[1][2 * j], lo16, a1);
+        a1 = fmaf(qs[1][2 * j + 1], hi16, a1);
       }
-      key[e0 + e] = score_key(a);
-      if ((valid >> (e0 + e)) & 1u) atomicAdd(&hc[key[e0 + e] >> 20], 1u);
+      key0[e0 + e] = score_key(a0);
+      key1[e0 + e] = score_key(a1);
+      if ((v0 >> (e0 + e)) & 1u) atomicAdd(&hc[0][key0[e0 + e] >> 20], 1u);
+      if ((v1 >> (e0 + e)) & 1u) atomicAdd(&hc[1][key1[e0 + e] >> 20], 1u);
     }
   }
   __syncthreads();
-  top_bin(hc, 4096, ks, red, s_bin, s_bef);
-  const uint32_t b1 = *s_bin, bef1 = *s_bef;
-  if (b1 == 0xffffffffu) {  // not reached (ks < m): take every candidate
-    if (t == 0) *lo_out = 0u;
-    return;
+  // level 1 of both rows, then level 2 inside each row's crossing bin
+  uint32_t b1[2] = {0xffffffffu, 0xffffffffu}, bef[2] = {0u, 0u};
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    if (ks[r] == 0u) continue;  // (uniform)
+    top_bin(hc[r], 4096, ks[r], red, &s_bin, &s_bef);
+    b1[r] = s_bin;
+    bef[r] = s_bef;
   }
-  for (int i = t; i < 4096; i += kSelNT) hc[i] = 0u;
+  for (int i = t; i < 2 * 4096; i += kSelNT) (&hc[0][0])[i] = 0u;
   __syncthreads();
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (((valid >> e) & 1u) && (key[e] >> 20) == b1) atomicAdd(&hc[(key[e] >> 8) & 0xfffu], 1u);
+  for (int e = 0; e < kThrPer; ++e) {
+    if (((v0 >> e) & 1u) && (key0[e] >> 20) == b1[0]) atomicAdd(&hc[0][(key0[e] >> 8) & 0xfffu], 1u);
+    if (((v1 >> e) & 1u) && (key1[e] >> 20) == b1[1]) atomicAdd(&hc[1][(key1[e] >> 8) & 0xfffu], 1u);
+  }
   __syncthreads();
-  top_bin(hc, 4096, ks - bef1, red, s_bin, s_bef);
-  if (t == 0) *lo_out = (b1 << 20) | ((*s_bin == 0xffffffffu ? 0u : *s_bin) << 8);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    uint32_t lo = 0u;
+    if (ks[r] != 0u && b1[r] != 0xffffffffu) {  // (uniform)
+      top_bin(hc[r], 4096, ks[r] - bef[r], red, &s_bin, &s_bef);
+      lo = (b1[r] << 20) | ((s_bin == 0xffffffffu ? 0u : s_bin) << 8);
+    }
+    if (t == 0 && blk0 + r < nblk) lo_all[(int64_t)(blk0 + r) * s.Hkv + g] = lo;
+  }
 }
 
 constexpr int kHitWaves = 2;  // waves (16 rows each) per k_pf_hits workgroup
@@ -1343,9 +1372,10 @@ hipError_t launch_prefill_select(const Shape& s, const sa_pages& pg, int32_t n_t
                                                    s.Hkv, s.D, b_sel, s_idx, qv);
     // sampled thresholds of every row (every stride-th 16-candidate tile)
     if (hit_lo != nullptr)
-      k_pf_thresh<<<(unsigned)(P.nblk * s.Hkv), kSelNT, 0, st>>>((const bf16_raw*)kidx_pool, pg.page_table,
-                                                                 qv, b_sel, P.self, s, k,
-                                                                 k <= 1024 ? 16 : 12, hit_lo);
+      k_pf_thresh<<<(unsigned)(((P.nblk + 1) / 2) * s.Hkv), kSelNT, 0, st>>>((const bf16_raw*)kidx_pool,
+                                                                            pg.page_table, qv, P.nblk, b_sel,
+                                                                            P.self, s, k, k <= 1024 ? 16 : 12,
+                                                                            hit_lo);
   }
   for (int b0 = 0; b0 < P.nblk; b0 += (int)P.slab) {
     const int b1 = b0 + (int)P.slab < P.nblk ? b0 + (int)P.slab : P.nblk;
