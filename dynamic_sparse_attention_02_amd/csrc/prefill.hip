@@ -327,17 +327,24 @@ k_prefill_hnorm(const float2* __restrict__ part, int32_t nparts, int32_t q0, int
 // Block-sparse causal attention.
 // ---------------------------------------------------------------------------
 constexpr int kKT = 64;                 // keys per tile
-constexpr int kKPitch = 128 * 2 + 16;   // K tile row pitch in bytes (d = 128 bf16)
-constexpr int kVPitch = kKT * 2 + 8;    // V^T row pitch in bytes (64 keys bf16; 34 dwords)
+constexpr int kTileBytes = kKT * 128 * 2;  // one 64-key tile of K or V (d = 128 bf16)
 constexpr int kMaxListed = 2048;        // listed keys per block the attention kernel takes
 constexpr float kLazy = 8.f;            // log2 headroom of the lazily raised softmax maximum
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 
 // Two fp32 -> packed bf16 (round to nearest even; one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const bf16x2_t v = {(__bf16)a, (__bf16)b};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+// a.x * b.x + a.y * b.y + c over bf16 pairs, fp32 accumulate (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // HB query heads of one group per workgroup (two waves each, 32 queries per
@@ -375,14 +382,21 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   const int n_tiles = n_list_tiles + 1;  // + the diagonal tile
   const int32_t* list = idx + (int64_t)row * cap;
 
-  __shared__ __align__(16) char Ks[2][kKT * kKPitch];
-  __shared__ __align__(16) char Vt[2][D * kVPitch];
+  // K and V tiles, three of each (tile t in buffer t mod 3).  A tile is
+  // chunk-major: chunk c (dims 8c .. 8c + 7, 16 bytes per key) of the 64
+  // keys fills 1 KB, key r at slot r ^ (4 (c & 1)), so that the K operand
+  // reads and the transposing V reads below are free of bank conflicts.
+  __shared__ __align__(16) char K0[kTileBytes], K1[kTileBytes], K2[kTileBytes];
+  __shared__ __align__(16) char V0[kTileBytes], V1[kTileBytes], V2[kTileBytes];
   // pool row (page * Hkv + g) * 64 + slot of every key the item visits, in
   // tile order (listed keys, then the diagonal block); -1 marks padding
   __shared__ int32_t rows_lds[kMaxListed + kKT];
 
   // Q as the B operand of S^T = K Q^T: Qb[nb][ks] holds query nb*32 + l32,
   // dims ks*16 + 8*half .. +7
+  // The query is stored pre-scaled by s_att * log2(e) (rounded once to
+  // bf16), so the products are the logits in log2 units.
+  const float sl2 = s_att * 1.4426950408889634f;
   bf16x8_t Qb[NBQ][8];
 #pragma unroll
   for (int nb = 0; nb < NBQ; ++nb) {
@@ -392,11 +406,35 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
       uint4 v = make_uint4(0, 0, 0, 0);
       if (qi < N)
         v = *reinterpret_cast<const uint4*>(q + ((int64_t)qi * s.Hq + h) * D + ks * 16 + 8 * half);
-      Qb[nb][ks] = __builtin_bit_cast(bf16x8_t, v);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = pack_bf16x2(__uint_as_float(w[e] << 16) * sl2, __uint_as_float(w[e] & 0xffff0000u) * sl2);
+      Qb[nb][ks] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   }
 
   // resolve every key's pool row once (list entry -> page table -> row)
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const kb0 = (lds_char*)K0;
+  lds_char* const kb1 = (lds_char*)K1;
+  lds_char* const kb2 = (lds_char*)K2;
+  lds_char* const vb0 = (lds_char*)V0;
+  lds_char* const vb1 = (lds_char*)V1;
+  lds_char* const vb2 = (lds_char*)V2;
+  // every slot starts at zero: a slot that no key fills keeps finite values
+  // (zero, or an earlier tile's key), which the mask turns into P = 0
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  for (int o = tid * 16; o < kTileBytes; o += NT * 16) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    *(lds_u32x4*)(kb0 + o) = z;
+    *(lds_u32x4*)(kb1 + o) = z;
+    *(lds_u32x4*)(kb2 + o) = z;
+    *(lds_u32x4*)(vb0 + o) = z;
+    *(lds_u32x4*)(vb1 + o) = z;
+    *(lds_u32x4*)(vb2 + o) = z;
+  }
   const int n_rows_total = n_list_tiles * kKT + kKT;
   for (int t = tid; t < n_rows_total; t += NT) {
     int32_t j = -1;
@@ -414,39 +452,28 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     rows_lds[t] = rw;
   }
   __syncthreads();
-  // Gather: piece pc moves 16 bytes (8 head dims, chunk col = pc / 64) of
-  // key row r = pc % 64, so the 64 lanes of a wave hold one chunk of all 64
-  // keys: the transposed V^T stores of a wave then fill one LDS row.
-  uint4 kr[LPT], vr[LPT];
-  auto gather = [&](int tile) {
+  // Gather straight into LDS (global_load_lds_dwordx4): instruction i of a
+  // wave moves chunk c = i * NT / 64 + wave of the tile's 64 keys, lane p
+  // loading key p ^ (4 (c & 1)) into slot p.  No registers hold the tile and
+  // no LDS stores are issued; the barrier that precedes a tile's first use
+  // waits for its loads.
+  typedef __attribute__((address_space(3))) void lds_void;
+  // s_waitcnt vmcnt(0): this wave's loads into LDS have landed.  Issued
+  // before every barrier that publishes a tile, so that after the barrier
+  // every wave's part of it is there (the compiler's own waits are not
+  // relied on for this).
+  auto wait_loads = []() { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  auto gather = [&](int tile, lds_char* dk, lds_char* dv) {
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
-      const int pc = i * NT + tid;
-      const int r = pc & 63, col = pc >> 6;
-      kr[i] = make_uint4(0, 0, 0, 0);
-      vr[i] = make_uint4(0, 0, 0, 0);
-      if (pc < PIECES) {
+      const int c = (i * NT + tid) >> 6;
+      if (c < 16) {
+        const int r = lane ^ (4 * (c & 1));
         const int32_t rw = rows_lds[tile * kKT + r];
         if (rw >= 0) {
-          const int64_t off = (int64_t)rw * D + col * 8;
-          kr[i] = *reinterpret_cast<const uint4*>(k_pool + off);
-          vr[i] = *reinterpret_cast<const uint4*>(v_pool + off);
-        }
-      }
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int pc = i * NT + tid;
-      if (pc < PIECES) {
-        const int r = pc & 63, col = pc >> 6;
-        *reinterpret_cast<uint4*>(Ks[buf] + r * kKPitch + col * 16) = kr[i];
-        const uint32_t w[4] = {vr[i].x, vr[i].y, vr[i].z, vr[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          *reinterpret_cast<uint16_t*>(Vt[buf] + (col * 8 + 2 * e) * kVPitch + r * 2) = (uint16_t)(w[e] & 0xffffu);
-          *reinterpret_cast<uint16_t*>(Vt[buf] + (col * 8 + 2 * e + 1) * kVPitch + r * 2) = (uint16_t)(w[e] >> 16);
+          const int64_t off = (int64_t)rw * D + c * 8;
+          __builtin_amdgcn_global_load_lds((const void*)(k_pool + off), (lds_void*)(dk + c * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(v_pool + off), (lds_void*)(dv + c * 1024), 16, 0, 0);
         }
       }
     }
@@ -459,47 +486,97 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[mb][nb][v] = 0.f;
+  // m_run: running maximum (log2 units, -inf before the first key);
+  // negm: -m_run (0 before the first key) in every accumulator slot, the
+  // C operand of each tile's first product, so the products come out as
+  // logit - m_run and feed the exponential directly.
   float m_run[NBQ], l_run[NBQ];
+  f32x16_t negm[NBQ];
 #pragma unroll
   for (int nb = 0; nb < NBQ; ++nb) {
     m_run[nb] = -INFINITY;
     l_run[nb] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) negm[nb][v] = 0.f;
   }
-  const float sl2 = s_att * 1.4426950408889634f;  // scores in log2 units
+  const uint32_t ones2 = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  gather(0);
-  stage(0);
+  // K Q^T of a tile: S^T[key][query] for the 64 keys x 32 queries of this
+  // wave, minus the running maximum.  ka: this lane's K operand address in
+  // the tile (key mk * 32 + l32, chunk 2 ks + half, in its swizzled slot).
+  f32x16_t S[2][NBQ];
+  const int klane = half * 1024 + (l32 ^ (4 * half)) * 16;
+  auto score_mfma = [&](lds_char* ka, int ks, int mk) {
+    const u32x4_t a = *(const lds_u32x4*)(ka + (ks * 2048 + mk * 512));
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb)
+      S[mk][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Qb[nb][ks], ks == 0 ? negm[nb] : S[mk][nb], 0, 0, 0);
+  };
+  // O^T[d][query] += V^T[d][key] P^T[key][query] for one 16-key step st of
+  // a tile and one 32-row block mb of d (keys in the score accumulator's
+  // order).  The V^T operand comes through the transposing LDS read
+  // (ds_read_b64_tr_b16): in each 16-lane group, lane 4k + t points at dims
+  // 4t .. 4t + 3 of key k, and lane j then receives dim j of the four keys.
+  // Group g = lane / 16 takes dims (g & 1) * 16 .. + 15 of the block and
+  // keys 4 (g >> 1) + 0..3 (then + 8), which is the operand's layout: lane
+  // (l32, half) holds d = l32 of keys 4 half + 0..3 and 8 + 4 half + 0..3
+  // of the step.  va: this lane's address in the tile for st = mb = 0.
+  bf16x8_t Pb[4][NBQ];
+  const int vg = lane >> 4, vs = lane & 15;
+  const int vlane = ((vg & 1) * 2 + ((vs >> 1) & 1)) * 1024 +
+                    ((4 * (vg >> 1) + (vs >> 2)) ^ (4 * ((vs >> 1) & 1))) * 16 + (vs & 1) * 8;
+  typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
+  auto pv_mfma = [&](lds_char* va, int st, int mb) {
+    const int kb = (st >> 1) * 32 + (st & 1) * 16;
+    lds_char* vp = va + (mb * 4096 + kb * 16);
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 128));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
+#pragma unroll
+    for (int nb = 0; nb < NBQ; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Pb[st][nb], acc[mb][nb], 0, 0, 0);
+  };
+  // a lane offset made opaque to the optimiser (per use), so that the reads
+  // of a tile add their constant offsets to one register instead of each
+  // keeping its own precomputed address; the buffer itself stays visible,
+  // so the compiler knows that these reads do not touch the buffers whose
+  // loads are in flight
+  auto opaque = [](int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+
+  // Tiles cycle through the three buffers, loaded two tiles ahead of their
+  // products, so after the single barrier of iteration t the products of
+  // tile t (P V) and the scores of tile t + 1 (K Q^T) are independent and
+  // interleave.  The buffers loaded in iteration t last held tile t - 1,
+  // which every wave finished before that barrier.  The loop is unrolled by
+  // three so that each buffer is a distinct LDS object in every iteration
+  // (the compiler then need not wait for the loads in flight before each
+  // read).  The last iteration scores a stale buffer (in bounds, result
+  // unused) so that its body has no branch between the two product chains.
+  gather(0, kb0, vb0);
+  if (n_tiles > 1) gather(1, kb1, vb1);
+  wait_loads();
   __syncthreads();
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) gather(tile + 1);
+  {
+    lds_char* ka = kb0 + opaque(klane);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int mk = 0; mk < 2; ++mk) score_mfma(ka, ks, mk);
+  }
+  auto body = [&](lds_char* vcur, lds_char* knext, lds_char* dk, lds_char* dv, int tile) {
     const bool diag = tile == n_list_tiles;
     const int nt = diag ? nq : min(kKT, nl - tile * kKT);
 
-    // S^T[key][query] for the 64 keys x 64 queries of this wave's head
-    f32x16_t S[2][NBQ];
-#pragma unroll
-    for (int mk = 0; mk < 2; ++mk)
-#pragma unroll
-      for (int nb = 0; nb < NBQ; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) S[mk][nb][v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-      for (int mk = 0; mk < 2; ++mk) {
-        const uint4 a = *reinterpret_cast<const uint4*>(Ks[buf] + (mk * 32 + l32) * kKPitch + ks * 32 + half * 16);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
-#pragma unroll
-        for (int nb = 0; nb < NBQ; ++nb)
-          S[mk][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Qb[nb][ks], S[mk][nb], 0, 0, 0);
-      }
-    }
     // online softmax per query (lane's query nb*32 + l32; keys spread over
-    // this lane's 32 accumulator values and the partner lane's), in log2
-    // units.  The running maximum is raised only when a tile's maximum
-    // exceeds it by more than kLazy (so P stays below 2^kLazy): the output
-    // accumulator is rescaled on those tiles only.
+    // this lane's 32 accumulator values and the partner lane's); S holds
+    // logit - m_run in log2 units.  The running maximum is raised only when
+    // a tile's maximum exceeds it by more than kLazy (so P stays below
+    // 2^kLazy): the output accumulator is rescaled on those tiles only.
     const bool masked = diag || nt < kKT;
     float mt[NBQ];
 #pragma unroll
@@ -519,12 +596,12 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
       for (int mk = 0; mk < 2; ++mk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) m = fmaxf(m, S[mk][nb][v]);
-      mt[nb] = fmaxf(m, __shfl_xor(m, 32, 64)) * sl2;
+      mt[nb] = fmaxf(m, __shfl_xor(m, 32, 64));
     }
     bool raise[NBQ], any_raise = false;
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
-      raise[nb] = mt[nb] > m_run[nb] + kLazy;
+      raise[nb] = m_run[nb] == -INFINITY ? mt[nb] > -INFINITY : mt[nb] > kLazy;
       any_raise = any_raise || raise[nb];
     }
     if (__ballot(any_raise)) {
@@ -532,10 +609,18 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 #pragma unroll
       for (int nb = 0; nb < NBQ; ++nb) {
         const bool r = raise[nb];
-        const float m_new = r ? mt[nb] : m_run[nb];
+        const float shift = r ? mt[nb] : 0.f;
+        const float m_new = r ? (m_run[nb] == -INFINITY ? 0.f : m_run[nb]) + mt[nb] : m_run[nb];
         alpha[nb] = r ? __builtin_amdgcn_exp2f(m_run[nb] - m_new) : 1.f;  // 0 on the first raise
         l_run[nb] *= alpha[nb];
         m_run[nb] = m_new;
+#pragma unroll
+        for (int mk = 0; mk < 2; ++mk)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) S[mk][nb][v] -= shift;
+        const float nm = m_new == -INFINITY ? 0.f : -m_new;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) negm[nb][v] = nm;
       }
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
@@ -544,50 +629,43 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[mb][nb][v] *= alpha[nb];
     }
+    // P = 2^S as bf16 (the B operand of the P V products, keys in the
+    // accumulator's order) and its row sum from the same bf16 values
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
-      const float m_use = m_run[nb] == -INFINITY ? 0.f : m_run[nb];
       float lt = 0.f;
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk)
+      for (int st = 0; st < 4; ++st) {
+        const int mk = st >> 1, hv = (st & 1) * 8;
+        uint32_t w[4];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(S[mk][nb][v], sl2, -m_use));
-          S[mk][nb][v] = p;
-          lt += p;
+        for (int e = 0; e < 4; ++e) {
+          w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(S[mk][nb][hv + 2 * e]),
+                             __builtin_amdgcn_exp2f(S[mk][nb][hv + 2 * e + 1]));
+          lt = dot2_bf16(w[e], ones2, lt);
         }
+        Pb[st][nb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+      }
       l_run[nb] += lt + __shfl_xor(lt, 32, 64);
     }
-    // O^T[d][query] += V^T[d][key] P^T[key][query], 16 keys per step in the
-    // accumulator's key order
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      const int mk = st >> 1, hv = (st & 1) * 8;
-      bf16x8_t Pb[NBQ];
-#pragma unroll
-      for (int nb = 0; nb < NBQ; ++nb) {
-        uint4 pw;
-        pw.x = pack_bf16x2(S[mk][nb][hv + 0], S[mk][nb][hv + 1]);
-        pw.y = pack_bf16x2(S[mk][nb][hv + 2], S[mk][nb][hv + 3]);
-        pw.z = pack_bf16x2(S[mk][nb][hv + 4], S[mk][nb][hv + 5]);
-        pw.w = pack_bf16x2(S[mk][nb][hv + 6], S[mk][nb][hv + 7]);
-        Pb[nb] = __builtin_bit_cast(bf16x8_t, pw);
-      }
-      const int kbase = mk * 32 + (st & 1) * 16 + 4 * half;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const char* vrow = Vt[buf] + (mb * 32 + l32) * kVPitch;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + kbase * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (kbase + 8) * 2);
-        const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-#pragma unroll
-        for (int nb = 0; nb < NBQ; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, Pb[nb], acc[mb][nb], 0, 0, 0);
-      }
-    }
-    // the other buffer was released by the barrier that ended the previous tile
-    if (tile + 1 < n_tiles) stage(buf ^ 1);
+    wait_loads();
     __syncthreads();
+    if (tile + 2 < n_tiles) gather(tile + 2, dk, dv);
+    lds_char* va = vcur + opaque(vlane);
+    lds_char* ka = knext + opaque(klane);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      pv_mfma(va, i >> 2, i & 3);
+      score_mfma(ka, i >> 1, i & 1);
+    }
+  };
+  for (int t0 = 0;; t0 += 3) {
+    body(vb0, kb1, kb2, vb2, t0);
+    if (t0 + 1 >= n_tiles) break;
+    body(vb1, kb2, kb0, vb0, t0 + 1);
+    if (t0 + 2 >= n_tiles) break;
+    body(vb2, kb0, kb1, vb1, t0 + 2);
+    if (t0 + 3 >= n_tiles) break;
   }
   // normalise and store: lane holds d = mb*32 + 8*(v/4) + 4*half + v%4 of
   // query nb*32 + l32
