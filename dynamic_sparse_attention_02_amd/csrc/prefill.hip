@@ -34,7 +34,12 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kQB = 64;     // queries per selection block
-constexpr int kSlab = 256;  // query blocks per score slab
+// Query blocks per score slab.  One slab holds the whole 128K prefill (2048
+// blocks): a single launch of each selection kernel balances the rows'
+// uneven work over the chip, where eight slabs paid eight launch tails
+// (1.52 -> 1.38 ms).  The slab's fp32 score rows (8.6 GB at 128K, used only
+// when a row leaves the hit path) are sized for a GPU with hundreds of GB.
+constexpr int kSlab = 2048;
 
 __global__ void k_iota1(int32_t* __restrict__ v, int32_t n) {
   const int32_t i = blockIdx.x * 256 + threadIdx.x;
