@@ -389,8 +389,10 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 
   // K and V tiles, three of each (tile t in buffer t mod 3).  A tile is
   // chunk-major: chunk c (dims 8c .. 8c + 7, 16 bytes per key) of the 64
-  // keys fills 1 KB, key r at slot r ^ (4 (c & 1)), so that the K operand
-  // reads and the transposing V reads below are free of bank conflicts.
+  // keys fills 1 KB, key r at slot r ^ 4 (c & 1) ^ 8 ((c >> 1) & 1), so
+  // that the K operand reads and the transposing V reads below are free of
+  // conflicts on the 64 LDS banks (each 256-byte access phase covers every
+  // bank once).
   __shared__ __align__(16) char K0[kTileBytes], K1[kTileBytes], K2[kTileBytes];
   __shared__ __align__(16) char V0[kTileBytes], V1[kTileBytes], V2[kTileBytes];
   // pool row (page * Hkv + g) * 64 + slot of every key the item visits, in
@@ -459,7 +461,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   __syncthreads();
   // Gather straight into LDS (global_load_lds_dwordx4): instruction i of a
   // wave moves chunk c = i * NT / 64 + wave of the tile's 64 keys, lane p
-  // loading key p ^ (4 (c & 1)) into slot p.  No registers hold the tile and
+  // loading the key of slot p.  No registers hold the tile and
   // no LDS stores are issued; the barrier that precedes a tile's first use
   // waits for its loads.
   typedef __attribute__((address_space(3))) void lds_void;
@@ -473,7 +475,7 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     for (int i = 0; i < LPT; ++i) {
       const int c = (i * NT + tid) >> 6;
       if (c < 16) {
-        const int r = lane ^ (4 * (c & 1));
+        const int r = lane ^ (4 * (c & 1)) ^ (8 * ((c >> 1) & 1));
         const int32_t rw = rows_lds[tile * kKT + r];
         if (rw >= 0) {
           const int64_t off = (int64_t)rw * D + c * 8;
@@ -508,11 +510,12 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
 
   // K Q^T of a tile: S^T[key][query] for the 64 keys x 32 queries of this
   // wave, minus the running maximum.  ka: this lane's K operand address in
-  // the tile (key mk * 32 + l32, chunk 2 ks + half, in its swizzled slot).
+  // the tile (key mk * 32 + l32, chunk 2 ks + half, in its swizzled slot)
+  // for even ks; odd ks flip the slot's bit 3 (ka1 = address ^ 128).
   f32x16_t S[2][NBQ];
   const int klane = half * 1024 + (l32 ^ (4 * half)) * 16;
-  auto score_mfma = [&](lds_char* ka, int ks, int mk) {
-    const u32x4_t a = *(const lds_u32x4*)(ka + (ks * 2048 + mk * 512));
+  auto score_mfma = [&](lds_char* ka, lds_char* ka1, int ks, int mk) {
+    const u32x4_t a = *(const lds_u32x4*)(((ks & 1) ? ka1 : ka) + (ks * 2048 + mk * 512));
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, a);
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb)
@@ -526,17 +529,17 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   // Group g = lane / 16 takes dims (g & 1) * 16 .. + 15 of the block and
   // keys 4 (g >> 1) + 0..3 (then + 8), which is the operand's layout: lane
   // (l32, half) holds d = l32 of keys 4 half + 0..3 and 8 + 4 half + 0..3
-  // of the step.  va: this lane's address in the tile for st = mb = 0.
+  // of the step.  va: this lane's address in the tile for st = mb = 0 (its
+  // first four keys); va1 = va ^ 128, the next four (slot bit 3 flipped).
   bf16x8_t Pb[4][NBQ];
   const int vg = lane >> 4, vs = lane & 15;
   const int vlane = ((vg & 1) * 2 + ((vs >> 1) & 1)) * 1024 +
-                    ((4 * (vg >> 1) + (vs >> 2)) ^ (4 * ((vs >> 1) & 1))) * 16 + (vs & 1) * 8;
+                    ((4 * (vg >> 1) + (vs >> 2)) ^ (4 * ((vs >> 1) & 1)) ^ (8 * (vg & 1))) * 16 + (vs & 1) * 8;
   typedef __attribute__((address_space(3))) v4i16_t lds_v4i16;
-  auto pv_mfma = [&](lds_char* va, int st, int mb) {
+  auto pv_mfma = [&](lds_char* va, lds_char* va1, int st, int mb) {
     const int kb = (st >> 1) * 32 + (st & 1) * 16;
-    lds_char* vp = va + (mb * 4096 + kb * 16);
-    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp);
-    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 128));
+    const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va + (mb * 4096 + kb * 16)));
+    const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(va1 + (mb * 4096 + kb * 16)));
     const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
     const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(l2.x, l2.y, h2.x, h2.y));
 #pragma unroll
@@ -568,10 +571,11 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
   __syncthreads();
   {
     lds_char* ka = kb0 + opaque(klane);
+    lds_char* ka1 = kb0 + opaque(klane ^ 128);
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int mk = 0; mk < 2; ++mk) score_mfma(ka, ks, mk);
+      for (int mk = 0; mk < 2; ++mk) score_mfma(ka, ka1, ks, mk);
   }
   auto body = [&](lds_char* vcur, lds_char* knext, lds_char* dk, lds_char* dv, int tile) {
     const bool diag = tile == n_list_tiles;
@@ -657,11 +661,13 @@ k_prefill_attn(const bf16_raw* __restrict__ q, const bf16_raw* __restrict__ k_po
     __syncthreads();
     if (tile + 2 < n_tiles) gather(tile + 2, dk, dv);
     lds_char* va = vcur + opaque(vlane);
+    lds_char* va1 = vcur + opaque(vlane ^ 128);
     lds_char* ka = knext + opaque(klane);
+    lds_char* ka1 = knext + opaque(klane ^ 128);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      pv_mfma(va, i >> 2, i & 3);
-      score_mfma(ka, i >> 1, i & 1);
+      pv_mfma(va, va1, i >> 2, i & 3);
+      score_mfma(ka, ka1, i >> 1, i & 1);
     }
   };
   for (int t0 = 0;; t0 += 3) {
