@@ -419,6 +419,12 @@ def bench_decode(args, name):
                      "traffic": recorded_traffic(res_workload, dom),
                      "bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 5)},
     }
+    # the cold protocol: every step after a 1 GiB scrub, timed alone
+    c_med, c_min, c_max, c_n = time_cold(lambda: run_step(base), min(args.steps, 20))
+    res["cold"] = {"us_per_step_median": round(c_med * 1e3, 2), "us_min": round(c_min * 1e3, 2),
+                   "us_max": round(c_max * 1e3, 2), "steps": c_n,
+                   "gb_s_median": round(step_bytes / (c_med * 1e-3) / 1e9, 2),
+                   "protocol": "1 GiB written then read before each step; HIP events around the step"}
     if not page_mode:
         res["coverage"] = support_coverage(ops, shape, pages, inp, base, x.shape[1], idx, count,
                                            sel["p"], ws_mass, ws_sel, run_step)
@@ -746,6 +752,31 @@ def prefill_coverage(inp, idx, count):
     return {"dense_mass_kept_mean": round(float(kept.mean()), 4),
             "dense_mass_kept_min": round(float(kept.min()), 4),
             "sample": "8 query rows of each of 4 query blocks x 2 groups"}
+
+
+def time_cold(fn, n, scrub_bytes=1 << 30):
+    """Per-step milliseconds of fn() with the caches cold: before each step a
+    scrub writes and then reads scrub_bytes (four times the 256 MB last-level
+    cache), and HIP events on the current stream bracket the step alone.  The
+    scrub is still running on the GPU while the host enqueues the step, so
+    the events see no host launch gap.  Returns (median, min, max, n)."""
+    import torch
+    scrub = torch.empty(scrub_bytes, dtype=torch.uint8, device="cuda")
+    fn()
+    torch.cuda.synchronize()
+    times = []
+    for i in range(n):
+        scrub.fill_(i & 0xFF)
+        scrub.view(torch.int64).sum()
+        a, b = _events()
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del scrub
+    times.sort()
+    return times[len(times) // 2], times[0], times[-1], n
 
 
 def time_events(fn, n):
