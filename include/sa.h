@@ -407,7 +407,9 @@ sa_status sa_support_coverage(const sa_shape* shape, const sa_pages* pages, cons
  * feed sa_sparse_prefill_query.
  * q [n_tokens][n_q_heads][head_dim], w_q, kidx_pool of dtype; page_table row 0
  * of pages maps the single sequence; workspace from SA_OP_PREFILL_SELECT
- * (param = n_tokens). */
+ * (param = n_tokens): for 64-query blocks it holds fp32 score rows for up to
+ * 2048 blocks at once (one slab for a 128K prefill, about 8.6 GB with 8
+ * key/value heads), so that each selection kernel runs as one launch. */
 sa_status sa_select_prefill_topk(const sa_shape* shape, const sa_pages* pages,
                                  int32_t n_tokens, const void* q, const void* w_q,
                                  const void* kidx_pool, sa_dtype dtype, float s_idx,
