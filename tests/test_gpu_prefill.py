@@ -103,6 +103,19 @@ def test_prefill_small(N, k):
     check_blocks(inp, kt_rows, idx, count, out, lse, k, range(inp.n_blocks), range(inp.H_kv))
 
 
+def test_prefill_late_maximum_raises():
+    """Planted keys with logits about 13 log2 units above the rest (q += 4u,
+    k += 25u): in many (block, query) rows a later tile of the list, or the
+    diagonal tile, holds a key far above the running maximum, so the
+    attention's lazily raised maximum moves after the first tile (147 such
+    raises in this input, counted on the CPU from the oracle's supports)."""
+    inp = synth.make_prefill_custom(N=1200, H_q=8, H_kv=2, d=128, dtype=torch.bfloat16,
+                                    device="cuda", seed=5, n_hh=6, q_shift=4.0, k_shift=25.0)
+    kidx, kt_rows = oracle_kidx(inp)
+    idx, count, out, lse = run_prefill(inp, kidx, 96)
+    check_blocks(inp, kt_rows, idx, count, out, lse, 96, range(inp.n_blocks), range(inp.H_kv))
+
+
 @pytest.mark.parametrize("H_q,H_kv", [(4, 4), (4, 2), (8, 1), (16, 1)])
 def test_prefill_group_sizes(H_q, H_kv):
     """G = 1, 2, 8, 16 (a group of more than 4 heads is split over several
